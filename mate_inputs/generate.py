@@ -1,0 +1,165 @@
+"""Seeded input generator.
+
+Every tensor is drawn from its own stream, ``SeedSequence([seed, cfg_id,
+tensor_id, head])``, so one head of a large configuration can be regenerated on
+its own (the full-size parity tests check sampled heads against the oracle).
+
+Distributions (the same for every configuration):
+  x ~ N(0,1); dt = softplus(z), z ~ N(-3,1); A = -exp(u), u ~ U(0, ln 16) per
+  head; B, C ~ N(0, sd = 1/sqrt(N)); D ~ N(0,1) per head; q, k, v ~ N(0,1).
+
+bf16 configurations round x, B, C, q, k, v to bfloat16 (round to nearest even)
+here, on the host; dt, A and D stay fp32.  The arrays are stored as raw bf16 bit
+patterns (uint16) or float32, and ``f64`` gives the exact values as float64.
+"""
+from __future__ import annotations
+
+import concurrent.futures as _fut
+import math
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+from .configs import MateShape
+
+TENSOR_IDS = {"x": 0, "dt": 1, "A": 2, "B": 3, "C": 4, "D": 5, "q": 6, "k": 7, "v": 8}
+DEFAULT_SEED = 20241212
+
+
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit pattern, round to nearest, ties to even.
+
+    NaN/Inf do not occur in generated data; they are not special-cased.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(seed: int, cfg_id: int, tensor: str, head: int) -> np.random.Generator:
+    ss = np.random.SeedSequence([seed, cfg_id, TENSOR_IDS[tensor], head])
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def _normal(seed, cfg_id, tensor, head, n, scale=1.0) -> np.ndarray:
+    z = _rng(seed, cfg_id, tensor, head).standard_normal(n, dtype=np.float32)
+    if scale != 1.0:
+        z *= np.float32(scale)
+    return z
+
+
+@dataclass
+class MateInputs:
+    """Inputs of one batch element in storage form.
+
+    ``store[name]`` is uint16 (bf16 bits) for x, B, C, q, k, v in bf16
+    configurations and float32 otherwise.  Layouts: x [L, Hs', P], dt [L, Hs'],
+    A [Hs'], B and C [L, N], D [Hs'], q, k, v [L, Ha', d]; Hs' and Ha' count
+    only the generated heads (``heads``), which default to all.
+    """
+
+    shape: MateShape
+    cfg_id: int
+    seed: int
+    heads: Sequence[int]
+    store: Dict[str, np.ndarray] = field(default_factory=dict)
+
+    def is_bf16(self, name: str) -> bool:
+        return self.store[name].dtype == np.uint16
+
+    def f32(self, name: str) -> np.ndarray:
+        a = self.store[name]
+        return f32_from_bf16_bits(a) if a.dtype == np.uint16 else a
+
+    def f64(self, name: str) -> np.ndarray:
+        return self.f32(name).astype(np.float64)
+
+    def torch(self, name: str, device="cuda"):
+        import torch  # local import: the oracle tests do not need torch
+
+        a = self.store[name]
+        if a.dtype == np.uint16:
+            t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(a)
+        return t.to(device)
+
+
+def make_inputs(shape: MateShape, cfg_id: int, seed: int = DEFAULT_SEED,
+                heads: Optional[Sequence[int]] = None, threads: int = 8,
+                tensors: Optional[Sequence[str]] = None) -> MateInputs:
+    """Generate the inputs of one batch element.
+
+    ``heads`` restricts x, dt, A, D (SSD heads) and q, k, v (attention heads)
+    to the listed head indices; values for a head do not depend on which other
+    heads are generated.  ``tensors`` restricts which tensors are produced.
+    """
+    L, P, N, d = shape.L, shape.headdim, shape.d_state, shape.attn_headdim
+    Hs, Ha = shape.ssd_heads, shape.attn_heads
+    if heads is None:
+        hs_list = list(range(Hs))
+        ha_list = list(range(Ha))
+    else:
+        hs_list = [h for h in heads if h < Hs]
+        ha_list = [h for h in heads if h < Ha]
+    want = set(tensors) if tensors is not None else set(TENSOR_IDS)
+    bf16 = shape.dtype == "bf16"
+    sdt = np.uint16 if bf16 else np.float32
+
+    def finish(a32: np.ndarray) -> np.ndarray:
+        return bf16_bits_from_f32(a32) if bf16 else a32
+
+    out = MateInputs(shape=shape, cfg_id=cfg_id, seed=seed, heads=list(heads) if heads is not None else list(range(max(Hs, Ha))))
+    jobs = []
+
+    def per_head(name, hl, width):
+        arr = np.empty((L, len(hl), width), dtype=sdt)
+        out.store[name] = arr
+
+        def fill(j, h):
+            arr[:, j, :] = finish(_normal(seed, cfg_id, name, h, L * width).reshape(L, width))
+
+        for j, h in enumerate(hl):
+            jobs.append((fill, j, h))
+
+    if "x" in want:
+        per_head("x", hs_list, P)
+    for name in ("q", "k", "v"):
+        if name in want:
+            per_head(name, ha_list, d)
+
+    if "dt" in want:
+        dt = np.empty((L, len(hs_list)), dtype=np.float32)
+        out.store["dt"] = dt
+
+        def fill_dt(j, h):
+            z = _rng(seed, cfg_id, "dt", h).standard_normal(L).astype(np.float64) - 3.0
+            # softplus(z) = log(1 + e^z), evaluated stably
+            sp = np.where(z > 20.0, z, np.log1p(np.exp(np.minimum(z, 20.0))))
+            dt[:, j] = sp.astype(np.float32)
+
+        for j, h in enumerate(hs_list):
+            jobs.append((fill_dt, j, h))
+
+    if "A" in want:
+        u = _rng(seed, cfg_id, "A", 0).uniform(0.0, math.log(16.0), Hs)
+        out.store["A"] = (-np.exp(u)).astype(np.float32)[hs_list]
+    if "D" in want:
+        out.store["D"] = _rng(seed, cfg_id, "D", 0).standard_normal(Hs).astype(np.float32)[hs_list]
+    for name in ("B", "C"):
+        if name in want:
+            out.store[name] = finish(_normal(seed, cfg_id, name, 0, L * N, 1.0 / math.sqrt(N)).reshape(L, N))
+
+    if threads > 1 and len(jobs) > 1:
+        with _fut.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(lambda j: j[0](j[1], j[2]), jobs))
+    else:
+        for f, j, h in jobs:
+            f(j, h)
+    return out

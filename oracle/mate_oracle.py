@@ -1,0 +1,331 @@
+"""fp64 reference implementation of the MATE token mixer.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring for the source legend
+[ABS], [ART], [ZH], [SSD] and for who may use this module).
+
+Tensor conventions (one batch element; canonical token order is (t, h, w)
+row-major, token index c = (t*H + h)*W + w):
+  x  [L, Hs, P]   SSD input, one P-vector per (token, head)
+  dt [L, Hs]      positive step sizes (already passed through softplus)
+  A  [Hs]         negative scalar decay rate per head
+  B, C [L, N]     input / output projections, shared by all heads (one group)
+  D  [Hs]         skip weight per head
+  q, k, v [L, Ha, d]
+All arithmetic is float64.  Inputs may be any float dtype; they are upcast.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Layer schedule: which scan order and which window phase a layer uses.
+# --------------------------------------------------------------------------
+
+
+def rms_mode(layer_idx: int) -> int:
+    """Scan mode of a layer.
+
+    [ART] 要领 and [ZH] 关键算法创新 (Rotary Major Scan): four scan orders are
+    used in turn on adjacent layers.  Reading taken: mode = layer_idx mod 4,
+    in the order the four modes are listed on [ZH].
+    """
+    if layer_idx < 0:
+        raise ValueError("layer_idx must be >= 0")
+    return layer_idx % 4
+
+
+def tesa_shift(layer_idx: int, win: Tuple[int, int, int]) -> Tuple[int, int, int]:
+    """Window-grid offset of a layer.
+
+    [ZH] 技术细节 / 关键算法创新 (TEmporal Swin Attention): plain and shifted
+    window partitions alternate between adjacent layers.  Reading taken:
+    odd layers are shifted, by half a window (floored) along each axis, as in
+    Swin attention; even layers are not shifted.
+    """
+    if layer_idx < 0:
+        raise ValueError("layer_idx must be >= 0")
+    if layer_idx % 2 == 1:
+        return tuple(w // 2 for w in win)
+    return (0, 0, 0)
+
+
+# --------------------------------------------------------------------------
+# Rotary Major Scan: the four token orders.
+# --------------------------------------------------------------------------
+
+# For each mode, the order of the (T, H, W) axes from slowest to fastest.
+# "First priority" in the pages is the axis unfolded first, i.e. the one that
+# varies fastest along the scan.
+#   mode 0  spatial row-major:     W fastest, then H, then T
+#   mode 1  spatial column-major:  H fastest, then W, then T
+#   mode 2  temporal row-major:    T fastest, then W, then H
+#   mode 3  temporal column-major: T fastest, then H, then W
+_RMS_AXES = {0: (0, 1, 2), 1: (0, 2, 1), 2: (1, 2, 0), 3: (2, 1, 0)}
+
+
+def rms_scan_order(mode: int, T: int, H: int, W: int) -> np.ndarray:
+    """perm[s] = canonical index of the token visited at scan position s.
+
+    [ART] 要领: W, H and T carry the first, second and third unfolding
+    priority in the default order, and swapping the priorities gives the other
+    scans, which need nothing beyond reshaping the token tensor.  [ZH]
+    关键算法创新 names the four modes (spatial row-major with W highest,
+    spatial column-major with H highest, temporal row-major and temporal
+    column-major with T highest).  Written, as the pages say, as a reshape and
+    an axis permutation of the (T, H, W) index grid.
+    """
+    if mode not in _RMS_AXES:
+        raise ValueError(f"RMS mode must be 0..3, got {mode}")
+    grid = np.arange(T * H * W, dtype=np.int64).reshape(T, H, W)
+    return grid.transpose(_RMS_AXES[mode]).ravel()
+
+
+def rms_inverse(perm: np.ndarray) -> np.ndarray:
+    """inv[c] = scan position of canonical token c."""
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size, dtype=perm.dtype)
+    return inv
+
+
+# --------------------------------------------------------------------------
+# Selective SSM scan (MA branch).
+# --------------------------------------------------------------------------
+
+
+def ssd_scan(x, dt, A, B, C, D, order: Sequence[int], h0=None,
+             record_after: Iterable[int] = (), stats: Optional[Dict] = None):
+    """Run the scalar-A selective SSM recurrence over tokens in ``order``.
+
+    [SSD]: per head, with state h in R^{P x N} (h = h0, zero by default),
+    for each visited token c:
+        h <- exp(dt_c * A) * h + dt_c * (x_c outer B_c)
+        y_c = h C_c + D * x_c
+    The decay applied when a token is absorbed uses that token's own dt.
+
+    Returns (y, h_final, recorded) where y[c] is set for every visited c (zero
+    elsewhere) and recorded[k] is the state after the first k visited tokens,
+    for each k in ``record_after``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dt = np.asarray(dt, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    D = np.asarray(D, dtype=np.float64)
+    Hs, P = x.shape[1], x.shape[2]
+    N = B.shape[1]
+    h = np.zeros((Hs, P, N)) if h0 is None else np.array(h0, dtype=np.float64, copy=True)
+    y = np.zeros(x.shape, dtype=np.float64)
+    want = set(int(k) for k in record_after)
+    recorded = {}
+    if 0 in want:
+        recorded[0] = h.copy()
+    step = 0
+    for c in order:
+        decay = np.exp(dt[c] * A)                         # [Hs]
+        u = dt[c][:, None] * x[c]                         # [Hs, P]
+        h = decay[:, None, None] * h + u[:, :, None] * B[c][None, None, :]
+        y[c] = h @ C[c] + D[:, None] * x[c]
+        step += 1
+        if step in want:
+            recorded[step] = h.copy()
+    if stats is not None:
+        stats["ssd_steps"] = stats.get("ssd_steps", 0) + step
+    return y, h, recorded
+
+
+def ssd_bidir(x, dt, A, B, C, D, perm: np.ndarray, h0=None, stats=None):
+    """Bidirectional scan: the forward scan along ``perm`` plus the same scan
+    along the reversed order, summed per token in canonical order.
+
+    [ABS]: the MA branch is a bidirectional Mamba2 block.  Readings taken:
+    both directions share x, dt, A, B, C, D; the backward direction is the
+    plain scan over the reversed sequence ("flip, run, flip back"); each
+    direction carries its own D skip, so the sum holds 2*D*x; a review-token
+    state h0, when present, is the initial state of both directions.
+    """
+    perm = np.asarray(perm)
+    y_f, _, _ = ssd_scan(x, dt, A, B, C, D, perm, h0=h0, stats=stats)
+    y_b, _, _ = ssd_scan(x, dt, A, B, C, D, perm[::-1], h0=h0, stats=stats)
+    return y_f + y_b
+
+
+# --------------------------------------------------------------------------
+# Review tokens.
+# --------------------------------------------------------------------------
+
+
+def review_tokens(x, dt, B, C, T: int, H: int, W: int,
+                  rpool: Tuple[int, int, int], rgrid: Tuple[int, int, int]):
+    """Build the review tokens from the token tensor.
+
+    [ART] 要领 / [ZH] 功能特色: review tokens give the Mamba hidden state an
+    overview of the whole video tensor before the scan starts.  The pages do
+    not say how the overview is formed.  Reading taken: mean-pool x, dt, B and
+    C over non-overlapping rpool blocks, giving a (T/pt, H/ph, W/pw) grid, then
+    keep rgrid points per axis at a regular stride starting from 0, listed in
+    canonical (t, h, w) order.
+    """
+    pt, ph, pw = rpool
+    gt, gh, gw = T // pt, H // ph, W // pw
+    rt, rh, rw = rgrid
+    st, sh, sw = gt // rt, gh // rh, gw // rw
+
+    def pool(a):
+        a = np.asarray(a, dtype=np.float64)
+        feat = a.shape[1:]
+        g = a.reshape((gt, pt, gh, ph, gw, pw) + feat).mean(axis=(1, 3, 5))
+        s = g[::st, ::sh, ::sw][:rt, :rh, :rw]
+        return s.reshape((rt * rh * rw,) + feat)
+
+    return pool(x), pool(dt), pool(B), pool(C)
+
+
+def review_state(x, dt, A, B, C, T, H, W, rpool, rgrid):
+    """State after scanning the review tokens from a zero state, [Hs, P, N].
+
+    Reading taken: the review tokens are scanned once, in canonical order, and
+    their outputs are discarded; only the state they leave is kept and handed
+    to both scan directions of the main sequence.
+    """
+    xr, dtr, Br, Cr = review_tokens(x, dt, B, C, T, H, W, rpool, rgrid)
+    R = xr.shape[0]
+    zeroD = np.zeros(np.asarray(A).shape)
+    _, h, _ = ssd_scan(xr, dtr, A, Br, Cr, zeroD, np.arange(R))
+    return h
+
+
+# --------------------------------------------------------------------------
+# TEmporal Swin Attention (TE branch).
+# --------------------------------------------------------------------------
+
+
+def tesa_window_keys(T: int, H: int, W: int, win, shift) -> np.ndarray:
+    """Window key of every token, [L, 3] (canonical order).
+
+    [ART] 要领 / [ZH] 关键算法创新: TESA attends inside small 3D windows whose
+    size is fixed regardless of resolution and length, and whose placement
+    moves between layers.  Reading taken (Swin's shifted windows): the window
+    grid is offset by ``shift``; a token (t, h, w) belongs to window
+    (floor((t-st)/wt), floor((h-sh)/wh), floor((w-sw)/ww)).  Tokens cut off at
+    the borders form smaller windows of their own; nothing wraps around.
+    """
+    wt, wh, ww = win
+    st, sh, sw = shift
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    keys = np.stack([(t - st) // wt, (h - sh) // wh, (w - sw) // ww], axis=-1)
+    return keys.reshape(-1, 3)
+
+
+def _attend(qg, kg, vg):
+    """Softmax attention of one token set, all heads: [n, Ha, d] each."""
+    d = qg.shape[-1]
+    qh = qg.transpose(1, 0, 2)
+    kh = kg.transpose(1, 0, 2)
+    vh = vg.transpose(1, 0, 2)
+    s = (qh @ kh.transpose(0, 2, 1)) / math.sqrt(d)      # [Ha, n, n]
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    return (p @ vh).transpose(1, 0, 2)
+
+
+def _groups(keys: np.ndarray):
+    _, gid = np.unique(keys, axis=0, return_inverse=True)
+    gid = np.asarray(gid).ravel()
+    order = np.argsort(gid, kind="stable")
+    counts = np.bincount(gid)
+    return gid, order, counts
+
+
+def tesa(q, k, v, T: int, H: int, W: int, win, shift, stats: Optional[Dict] = None):
+    """o_i = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j over the tokens j in the
+    same window as token i, per head; returns [L, Ha, d].
+
+    Readings taken: scale 1/sqrt(d); no positional bias, no causal mask; the
+    window partition is ``tesa_window_keys``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    keys = tesa_window_keys(T, H, W, win, shift)
+    _, order, counts = _groups(keys)
+    o = np.empty(q.shape, dtype=np.float64)
+    start = 0
+    pairs = 0
+    for n in counts:
+        idx = order[start:start + n]
+        start += n
+        o[idx] = _attend(q[idx], k[idx], v[idx])
+        pairs += int(n) * int(n)
+    if stats is not None:
+        stats["tesa_pairs"] = stats.get("tesa_pairs", 0) + pairs * q.shape[1]
+    return o
+
+
+def tesa_for_queries(q, k, v, T: int, H: int, W: int, win, shift,
+                     query_idx: Sequence[int]) -> np.ndarray:
+    """TESA output for selected query tokens only, [len(query_idx), Ha, d].
+
+    Same definition as ``tesa``; each query attends over its own window.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    query_idx = np.asarray(query_idx)
+    keys = tesa_window_keys(T, H, W, win, shift)
+    gid, order, counts = _groups(keys)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    out = np.empty((query_idx.size, q.shape[1], q.shape[2]), dtype=np.float64)
+    for g in np.unique(gid[query_idx]):
+        members = order[starts[g]:starts[g + 1]]
+        sel = np.nonzero(gid[query_idx] == g)[0]
+        qi = query_idx[sel]
+        d = q.shape[-1]
+        qh = q[qi].transpose(1, 0, 2)
+        kh = k[members].transpose(1, 0, 2)
+        vh = v[members].transpose(1, 0, 2)
+        s = (qh @ kh.transpose(0, 2, 1)) / math.sqrt(d)
+        s = s - s.max(axis=-1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=-1, keepdims=True)
+        out[sel] = (p @ vh).transpose(1, 0, 2)
+    return out
+
+
+# --------------------------------------------------------------------------
+# The whole mixer.
+# --------------------------------------------------------------------------
+
+
+def ma_fwd(x, dt, A, B, C, D, mode: int, T: int, H: int, W: int,
+           review=None, stats=None):
+    """MA branch: RMS order ``mode``, bidirectional scan, optional review state.
+
+    ``review`` is None or (rpool, rgrid).  Returns y_MA [L, Hs, P].
+    """
+    perm = rms_scan_order(mode, T, H, W)
+    h0 = None
+    if review is not None:
+        rpool, rgrid = review
+        h0 = review_state(x, dt, A, B, C, T, H, W, rpool, rgrid)
+    return ssd_bidir(x, dt, A, B, C, D, perm, h0=h0, stats=stats)
+
+
+def mate_fwd(x, dt, A, B, C, D, q, k, v, layer_idx: int, T: int, H: int, W: int,
+             win, review=None, stats=None):
+    """MATE mixer: y = y_MA + o, both viewed as [L, Hs*P] (= [L, Ha*d]).
+
+    [ABS]: MATE consists of an MA branch and a TE branch.  The pages do not
+    say how the branch outputs are combined; reading taken: a plain sum with
+    no weights, SSD head i and attention head i sharing columns i*P..i*P+P-1.
+    """
+    mode = rms_mode(layer_idx)
+    shift = tesa_shift(layer_idx, win)
+    y_ma = ma_fwd(x, dt, A, B, C, D, mode, T, H, W, review=review, stats=stats)
+    o = tesa(q, k, v, T, H, W, win, shift, stats=stats)
+    L = T * H * W
+    return y_ma.reshape(L, -1) + o.reshape(L, -1)

@@ -1,0 +1,172 @@
+/*
+ * lingen_mate.h -- C ABI of the MI355X (gfx950) MATE token mixer library.
+ *
+ * MATE is LinGen's linear-complexity replacement for DiT self-attention
+ * (page "Towards High-Resolution Minute-Length Text-to-Video Generation with
+ * Linear Computational Complexity", English abstract).  It has two branches
+ * over a T x H x W video-latent token tensor:
+ *
+ *   MA  Rotary Major Scan (four token orders used in turn by layer) followed
+ *       by a bidirectional Mamba2 selective-SSM scan, optionally preceded by
+ *       review tokens that seed the scan state (abstract; page
+ *       "视频生成模子太贵太慢如何办？", section 要领：线性复杂度的 MATE 模块;
+ *       page "LinGen：基于Mamba机制的线性复杂度高清长视频生成框架",
+ *       section 关键算法创新 > Rotary Major Scan).
+ *   TE  TEmporal Swin Attention: softmax attention inside small fixed 3D
+ *       windows, the window grid shifted by half a window on odd layers
+ *       (same pages, sections 要领 and 关键算法创新 > TESA).
+ *
+ * and y = y_MA + y_TE.  The projections around the mixer are the caller's:
+ * this library takes the projected tensors (x, dt, B, C for the scan and
+ * q, k, v for the attention) and returns the mixed tokens.
+ *
+ * The scan uses Mamba2's scalar-A recurrence (Dao & Gu 2024): per head, with
+ * state h in R^{P x N},
+ *     h <- exp(dt_c * A) * h + dt_c * (x_c outer B_c),   y_c = h C_c + D x_c,
+ * run once along the scan order and once along the reversed order, the two
+ * outputs summed (so the skip term appears as 2 D x).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Canonical token order is (t, h, w) row-major: c = (t*H + h)*W + w,
+ *   L = T*H*W tokens per batch element.
+ * - Tensor pointers marked "device" are HIP device pointers owned by the
+ *   caller; the library never allocates, frees or retains them.  Inputs are
+ *   read only.  Outputs must not alias inputs.  All device pointers must be
+ *   16-byte aligned.
+ * - Layouts (contiguous, row-major, batch outermost):
+ *     x        [batch, L, Hs, P]   dtype
+ *     dt       [batch, L, Hs]      fp32, > 0 (already through softplus)
+ *     A        [Hs]                fp32, <= 0
+ *     B, C     [batch, L, N]       dtype (one group shared by all heads)
+ *     D        [Hs]                fp32
+ *     q, k, v  [batch, L, Ha, d]   dtype
+ *     y        [batch, L, Hs*P]    dtype  (head i owns columns i*P..i*P+P-1)
+ *   "dtype" is shape->dtype: LINGEN_F32 or LINGEN_BF16.
+ * - Every call validates its arguments on the host before it touches the GPU
+ *   and returns a negative lingen_status on failure, with nothing enqueued.
+ *   Device work is enqueued on `stream` and the call returns without waiting;
+ *   a launch failure is reported as LINGEN_ERR_HIP.  The library keeps no
+ *   mutable global state; concurrent calls on different streams are safe if
+ *   they use different outputs and workspaces.
+ */
+#ifndef LINGEN_MATE_H
+#define LINGEN_MATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LINGEN_OK = 0,
+  LINGEN_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  LINGEN_ERR_SHAPE = -2,       /* sizes inconsistent or out of range               */
+  LINGEN_ERR_DTYPE = -3,       /* dtype code unknown                               */
+  LINGEN_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned          */
+  LINGEN_ERR_WORKSPACE = -5,   /* workspace smaller than lingen_mate_workspace_bytes */
+  LINGEN_ERR_HIP = -6,         /* a HIP call or kernel launch failed               */
+  LINGEN_ERR_UNSUPPORTED = -7  /* valid shape, but no compiled kernel for it       */
+} lingen_status;
+
+typedef enum { LINGEN_F32 = 0, LINGEN_BF16 = 1 } lingen_dtype;
+
+typedef struct {
+  int32_t batch, T, H, W;          /* token grid; L = T*H*W                        */
+  int32_t ssd_heads, headdim;      /* Hs, P                                        */
+  int32_t d_state, ngroups, chunk; /* N, G (must be 1), Q (must divide L)          */
+  int32_t attn_heads, attn_headdim;/* Ha, d; Ha*d must equal Hs*P                  */
+  int32_t win_t, win_h, win_w;     /* TESA window; must divide T, H, W             */
+  int32_t dtype;                   /* lingen_dtype of x, B, C, q, k, v, y          */
+  int32_t n_review;                /* 0 (no review tokens) or rgrid_t*rgrid_h*rgrid_w */
+  int32_t rpool_t, rpool_h, rpool_w;  /* review pooling block; divides T, H, W     */
+  int32_t rgrid_t, rgrid_h, rgrid_w;  /* review points per axis; divides the pooled grid */
+} lingen_mate_shape;
+
+/* Compiled kernel families (anything else returns LINGEN_ERR_UNSUPPORTED):
+ *   scan:      (dtype, P, N, Q) in { (F32, 32, 16, 16), (BF16, 64, 64, 64),
+ *                                    (BF16, 64, 128, 128) }
+ *   attention: (dtype, d, win_t*win_h*win_w) in { (F32, 32, 32), (BF16, 64, 256) }
+ */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* lingen_status_str(int status);
+
+/* Host-only check of a shape against every rule above.  Touches no GPU. */
+int lingen_mate_validate(const lingen_mate_shape* shape);
+
+/* Bytes of device workspace that lingen_mate_fwd, lingen_ma_fwd and
+ * lingen_ssd_chunk_states need for `shape` (written to *bytes).  Host only.
+ * The workspace holds the per-chunk scan states of both directions, the
+ * chunk decays and, with review tokens, the pooled review tokens and their
+ * state.  Its contents on entry are ignored. */
+int lingen_mate_workspace_bytes(const lingen_mate_shape* shape, size_t* bytes);
+
+/* Rotary Major Scan index maps on the host (page "LinGen：基于Mamba机制的
+ * 线性复杂度高清长视频生成框架", section 关键算法创新 > Rotary Major Scan).
+ * mode 0: W fastest, then H, then T   (spatial row-major)
+ * mode 1: H fastest, then W, then T   (spatial column-major)
+ * mode 2: T fastest, then W, then H   (temporal row-major)
+ * mode 3: T fastest, then H, then W   (temporal column-major)
+ * perm_host[s] = canonical index of scan position s; inv_host[c] = scan
+ * position of canonical token c.  Both arrays are caller-owned host memory of
+ * T*H*W int32; either may be NULL to skip it.  Errors: LINGEN_ERR_SHAPE for a
+ * mode outside 0..3 or a non-positive or too large (>= 2^31 tokens) grid. */
+int lingen_rms_index(int32_t mode, int32_t T, int32_t H, int32_t W,
+                     int32_t* perm_host, int32_t* inv_host);
+
+/* The same map computed on the GPU by the device function the scan kernels
+ * use for their loads and stores: perm_dev[s] = canonical index (device,
+ * T*H*W int32). */
+int lingen_rms_index_device(int32_t mode, int32_t T, int32_t H, int32_t W,
+                            int32_t* perm_dev, hipStream_t stream);
+
+/* Scan-order copy of a token tensor: dst row s = src row perm[s], rows of
+ * row_bytes bytes (a multiple of 16), batch 1.  The scan kernels never make
+ * this copy (they address src through the map directly); it exists to
+ * measure and test the gather on its own.  src, dst: device, T*H*W*row_bytes. */
+int lingen_rms_gather(const void* src, int64_t row_bytes, int32_t mode,
+                      int32_t T, int32_t H, int32_t W, void* dst, hipStream_t stream);
+
+/* Scan states at chunk boundaries for RMS mode `mode` (both directions,
+ * including the review-token state when shape->n_review > 0):
+ *   h_fwd[b, c, i, p, n] = forward state before the first token of chunk c,
+ *   h_bwd[b, c, i, p, n] = backward state before the last token of chunk c
+ *                          (i.e. after absorbing every later chunk),
+ * chunks counted along the scan order, fp32, [batch, L/Q, Hs, P, N], device.
+ * Needs the workspace of lingen_mate_workspace_bytes. */
+int lingen_ssd_chunk_states(const void* x, const float* dt, const float* A, const void* B,
+                            int32_t mode, const lingen_mate_shape* shape,
+                            float* h_fwd, float* h_bwd,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* MA branch alone: y_ma = bidirectional scan along RMS order `mode` (0..3),
+ * with review tokens if shape->n_review > 0.  y_ma: device, layout of y. */
+int lingen_ma_fwd(const void* x, const float* dt, const float* A, const void* B,
+                  const void* C, const float* D, int32_t mode,
+                  const lingen_mate_shape* shape, void* y_ma,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* TE branch alone: y_te = windowed softmax attention with the window grid
+ * shifted by (win_t/2, win_h/2, win_w/2) if `shifted` != 0; border windows are
+ * cut, not wrapped.  Scale 1/sqrt(d).  y_te: device, layout of y. */
+int lingen_te_fwd(const void* q, const void* k, const void* v, int32_t shifted,
+                  const lingen_mate_shape* shape, void* y_te, hipStream_t stream);
+
+/* The mixer: y = MA(mode = layer_idx mod 4) + TE(shifted = layer_idx odd).
+ * layer_idx >= 0.  y: device, [batch, L, Hs*P] dtype; it is also used as the
+ * staging buffer of the MA branch, so its contents on entry are ignored. */
+int lingen_mate_fwd(const void* x, const float* dt, const float* A, const void* B,
+                    const void* C, const float* D,
+                    const void* q, const void* k, const void* v,
+                    int32_t layer_idx, const lingen_mate_shape* shape, void* y,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINGEN_MATE_H */

@@ -1,0 +1,291 @@
+"""ctypes binding of liblingen_mate.so (include/lingen_mate.h).
+
+Argument marshalling only: these functions check tensor dtypes, devices and
+sizes, allocate outputs and workspaces with torch when the caller passes
+none, and call the C entry point of the same name on torch's current HIP
+stream.  Every step of the mixer runs in the library's HIP kernels; if the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblingen_mate.so")
+
+LINGEN_OK = 0
+STATUS_NAMES = {
+    0: "LINGEN_OK",
+    -1: "LINGEN_ERR_NULL",
+    -2: "LINGEN_ERR_SHAPE",
+    -3: "LINGEN_ERR_DTYPE",
+    -4: "LINGEN_ERR_ALIGN",
+    -5: "LINGEN_ERR_WORKSPACE",
+    -6: "LINGEN_ERR_HIP",
+    -7: "LINGEN_ERR_UNSUPPORTED",
+}
+LINGEN_F32, LINGEN_BF16 = 0, 1
+
+EXPORTS = (
+    "lingen_status_str",
+    "lingen_mate_validate",
+    "lingen_mate_workspace_bytes",
+    "lingen_rms_index",
+    "lingen_rms_index_device",
+    "lingen_rms_gather",
+    "lingen_ssd_chunk_states",
+    "lingen_ma_fwd",
+    "lingen_te_fwd",
+    "lingen_mate_fwd",
+)
+
+
+class LingenError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(code, code)} ({status_str(code)})")
+
+
+class lingen_mate_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "T", "H", "W", "ssd_heads", "headdim", "d_state", "ngroups", "chunk",
+        "attn_heads", "attn_headdim", "win_t", "win_h", "win_w", "dtype", "n_review",
+        "rpool_t", "rpool_h", "rpool_w", "rgrid_t", "rgrid_h", "rgrid_w")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m linear_complexity_video_mate_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    SP = ctypes.POINTER(lingen_mate_shape)
+    sig = {
+        "lingen_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        "lingen_mate_validate": ([SP], ctypes.c_int),
+        "lingen_mate_workspace_bytes": ([SP, ctypes.POINTER(SZ)], ctypes.c_int),
+        "lingen_rms_index": ([I32, I32, I32, I32, P, P], ctypes.c_int),
+        "lingen_rms_index_device": ([I32, I32, I32, I32, P, P], ctypes.c_int),
+        "lingen_rms_gather": ([P, I64, I32, I32, I32, I32, P, P], ctypes.c_int),
+        "lingen_ssd_chunk_states": ([P, P, P, P, I32, SP, P, P, P, SZ, P], ctypes.c_int),
+        "lingen_ma_fwd": ([P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
+        "lingen_te_fwd": ([P, P, P, I32, SP, P, P], ctypes.c_int),
+        "lingen_mate_fwd": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def status_str(code: int) -> str:
+    return lib().lingen_status_str(int(code)).decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != LINGEN_OK:
+        raise LingenError(fn, rc)
+
+
+def to_c_shape(s) -> lingen_mate_shape:
+    """Build the C struct from any object with the MateShape attribute names."""
+    dtype = s.dtype
+    if isinstance(dtype, str):
+        dtype = {"f32": LINGEN_F32, "bf16": LINGEN_BF16}.get(dtype, 99)
+    rpool = getattr(s, "rpool", (1, 1, 1))
+    rgrid = getattr(s, "rgrid", (1, 1, 1))
+    return lingen_mate_shape(
+        s.batch, s.T, s.H, s.W, s.ssd_heads, s.headdim, s.d_state, s.ngroups, s.chunk,
+        s.attn_heads, s.attn_headdim, s.win[0], s.win[1], s.win[2], dtype,
+        getattr(s, "n_review", 0), rpool[0], rpool[1], rpool[2], rgrid[0], rgrid[1], rgrid[2])
+
+
+def lingen_mate_validate(shape) -> int:
+    """Status code of the host-side shape check (no exception)."""
+    cs = to_c_shape(shape)
+    return lib().lingen_mate_validate(ctypes.byref(cs))
+
+
+def lingen_mate_workspace_bytes(shape) -> int:
+    cs = to_c_shape(shape)
+    n = ctypes.c_size_t(0)
+    _check("lingen_mate_workspace_bytes", lib().lingen_mate_workspace_bytes(ctypes.byref(cs), ctypes.byref(n)))
+    return int(n.value)
+
+
+def lingen_rms_index(mode: int, T: int, H: int, W: int) -> Tuple[np.ndarray, np.ndarray]:
+    L = T * H * W
+    perm = np.empty(L, dtype=np.int32)
+    inv = np.empty(L, dtype=np.int32)
+    _check("lingen_rms_index", lib().lingen_rms_index(mode, T, H, W, perm.ctypes.data, inv.ctypes.data))
+    return perm, inv
+
+
+# ---------------------------------------------------------------------------
+# Device entry points (torch tensors on the GPU)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _tdtype(shape):
+    torch = _torch()
+    return torch.bfloat16 if shape.dtype in ("bf16", LINGEN_BF16) else torch.float32
+
+
+def _need(t, name: str, dtype, numel: int):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _sizes(s):
+    L = s.T * s.H * s.W
+    return dict(
+        x=s.batch * L * s.ssd_heads * s.headdim,
+        dt=s.batch * L * s.ssd_heads,
+        A=s.ssd_heads,
+        B=s.batch * L * s.d_state,
+        D=s.ssd_heads,
+        q=s.batch * L * s.attn_heads * s.attn_headdim,
+        y=s.batch * L * s.ssd_heads * s.headdim,
+        states=s.batch * (L // s.chunk) * s.ssd_heads * s.headdim * s.d_state,
+    )
+
+
+def _workspace(shape, workspace):
+    torch = _torch()
+    need = lingen_mate_workspace_bytes(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    return workspace, ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(nbytes)
+
+
+def lingen_rms_index_device(mode: int, T: int, H: int, W: int, out=None):
+    torch = _torch()
+    L = T * H * W
+    if out is None:
+        out = torch.empty(L, dtype=torch.int32, device="cuda")
+    p = _need(out, "out", torch.int32, L)
+    _check("lingen_rms_index_device", lib().lingen_rms_index_device(mode, T, H, W, p, _stream()))
+    return out
+
+
+def lingen_rms_gather(src, mode: int, T: int, H: int, W: int, out=None):
+    """Scan-order copy of a [T*H*W, ...] GPU tensor (rows = leading dim)."""
+    torch = _torch()
+    L = T * H * W
+    if src.shape[0] != L or not src.is_contiguous() or src.device.type != "cuda":
+        raise ValueError("src must be a contiguous GPU tensor with T*H*W rows")
+    row_bytes = src.numel() // L * src.element_size()
+    if out is None:
+        out = torch.empty_like(src)
+    _need(out, "out", src.dtype, src.numel())
+    _check("lingen_rms_gather", lib().lingen_rms_gather(
+        ctypes.c_void_p(src.data_ptr()), row_bytes, mode, T, H, W, ctypes.c_void_p(out.data_ptr()), _stream()))
+    return out
+
+
+def lingen_ssd_chunk_states(x, dt, A, B, mode: int, shape, workspace=None):
+    """(h_fwd, h_bwd): scan states entering every chunk, [batch, L/Q, Hs, P, N] fp32."""
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    px = _need(x, "x", td, n["x"])
+    pdt = _need(dt, "dt", torch.float32, n["dt"])
+    pA = _need(A, "A", torch.float32, n["A"])
+    pB = _need(B, "B", td, n["B"])
+    L = shape.T * shape.H * shape.W
+    hshape = (shape.batch, L // shape.chunk, shape.ssd_heads, shape.headdim, shape.d_state)
+    hf = torch.empty(hshape, dtype=torch.float32, device="cuda")
+    hb = torch.empty(hshape, dtype=torch.float32, device="cuda")
+    workspace, pw, nw = _workspace(shape, workspace)
+    _check("lingen_ssd_chunk_states", lib().lingen_ssd_chunk_states(
+        px, pdt, pA, pB, mode, ctypes.byref(cs), ctypes.c_void_p(hf.data_ptr()), ctypes.c_void_p(hb.data_ptr()),
+        pw, nw, _stream()))
+    return hf, hb
+
+
+def lingen_ma_fwd(x, dt, A, B, C, D, mode: int, shape, out=None, workspace=None):
+    """MA branch alone; returns y_ma [batch, L, Hs*P]."""
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    L = shape.T * shape.H * shape.W
+    if out is None:
+        out = torch.empty((shape.batch, L, shape.ssd_heads * shape.headdim), dtype=td, device="cuda")
+    args = [_need(x, "x", td, n["x"]), _need(dt, "dt", torch.float32, n["dt"]),
+            _need(A, "A", torch.float32, n["A"]), _need(B, "B", td, n["B"]), _need(C, "C", td, n["B"]),
+            _need(D, "D", torch.float32, n["D"])]
+    py = _need(out, "out", td, n["y"])
+    workspace, pw, nw = _workspace(shape, workspace)
+    _check("lingen_ma_fwd", lib().lingen_ma_fwd(*args, mode, ctypes.byref(cs), py, pw, nw, _stream()))
+    return out
+
+
+def lingen_te_fwd(q, k, v, shifted: int, shape, out=None):
+    """TE branch alone; returns y_te [batch, L, Ha*d]."""
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    torch = _torch()
+    L = shape.T * shape.H * shape.W
+    if out is None:
+        out = torch.empty((shape.batch, L, shape.attn_heads * shape.attn_headdim), dtype=td, device="cuda")
+    args = [_need(q, "q", td, n["q"]), _need(k, "k", td, n["q"]), _need(v, "v", td, n["q"])]
+    py = _need(out, "out", td, n["y"])
+    _check("lingen_te_fwd", lib().lingen_te_fwd(*args, int(shifted), ctypes.byref(cs), py, _stream()))
+    return out
+
+
+def lingen_mate_fwd(x, dt, A, B, C, D, q, k, v, layer_idx: int, shape, out=None, workspace=None):
+    """The MATE mixer; returns y [batch, L, Hs*P]."""
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    L = shape.T * shape.H * shape.W
+    if out is None:
+        out = torch.empty((shape.batch, L, shape.ssd_heads * shape.headdim), dtype=td, device="cuda")
+    args = [_need(x, "x", td, n["x"]), _need(dt, "dt", torch.float32, n["dt"]),
+            _need(A, "A", torch.float32, n["A"]), _need(B, "B", td, n["B"]), _need(C, "C", td, n["B"]),
+            _need(D, "D", torch.float32, n["D"]), _need(q, "q", td, n["q"]), _need(k, "k", td, n["q"]),
+            _need(v, "v", td, n["q"])]
+    py = _need(out, "out", td, n["y"])
+    workspace, pw, nw = _workspace(shape, workspace)
+    _check("lingen_mate_fwd", lib().lingen_mate_fwd(*args, int(layer_idx), ctypes.byref(cs), py, pw, nw, _stream()))
+    return out

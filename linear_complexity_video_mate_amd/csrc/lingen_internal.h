@@ -1,0 +1,36 @@
+// Internal declarations shared by the host validation code and the kernel
+// launchers of the MATE mixer library.  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "lingen_mate.h"
+
+namespace lingen {
+
+// Byte offsets of the sub-buffers inside the caller's workspace, for one
+// batch element (batch elements are processed one after another and reuse
+// the same workspace).
+struct WsLayout {
+  size_t states;   // fp32 [2][n_chunks][Hs][P][N]: chunk states, then scan states
+  size_t logdec;   // fp32 [n_chunks][Hs]: sum of dt*A over each chunk
+  size_t review_h; // fp32 [Hs][P][N]: state left by the review tokens
+  size_t review_x; // fp32 [R][Hs][P]: pooled review x
+  size_t review_dt;// fp32 [R][Hs]
+  size_t review_b; // fp32 [R][N]
+  size_t total;
+};
+
+// Which compiled kernel families a shape uses.
+enum ScanFamily { SCAN_F32_P32_N16_Q16 = 0, SCAN_BF16_P64_N64_Q64 = 1, SCAN_BF16_P64_N128_Q128 = 2, SCAN_NONE = -1 };
+enum AttnFamily { ATTN_F32_D32_W32 = 0, ATTN_BF16_D64_W256 = 1, ATTN_NONE = -1 };
+
+int validate_shape(const lingen_mate_shape* s);   // lingen_status
+int64_t tokens(const lingen_mate_shape* s);       // T*H*W
+WsLayout ws_layout(const lingen_mate_shape* s);
+ScanFamily scan_family(const lingen_mate_shape* s);
+AttnFamily attn_family(const lingen_mate_shape* s);
+int check_ptr(const void* p);                      // NULL / alignment check
+
+}  // namespace lingen

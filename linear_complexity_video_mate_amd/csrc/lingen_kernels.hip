@@ -1,0 +1,1060 @@
+// HIP kernels (gfx950 / CDNA4) of the MATE token mixer and the C-ABI entry
+// points that launch them.
+//
+// Pipeline of one forward call (per batch element, all on the caller's
+// stream):
+//   review_pool, review_state  (only with review tokens)
+//   ssd_chunk_state            phase A: per (chunk, head) the decay-weighted
+//                              chunk states of both scan directions, on MFMA
+//   ssd_state_pass             inter-chunk recurrence, forward and backward
+//                              (the backward walk is the same loop with the
+//                              chunk index reflected)
+//   ssd_chunk_out              phase B: per (chunk, head) the in-chunk
+//                              quadratic form plus both inter-chunk terms plus
+//                              the skip, scattered to canonical token order
+//   tesa_window                per (window, head) masked softmax attention on
+//                              MFMA with an online softmax, adding the MA
+//                              output (fused branch sum)
+//
+// The Rotary Major Scan never materialises a permuted copy: every scan-order
+// access goes through RmsMap::canon, which turns a scan position into the
+// canonical token index with mixed-radix arithmetic.
+//
+// Chunked form of the bidirectional scan used by phases A and B (Mamba2's SSD
+// chunking, extended to the reversed direction).  Inside a chunk of Q scan
+// positions, with a_s = dt_s*A, cum_t = sum_{tau<=t} a_tau and
+// exc_t = cum_t - a_t (both taken within the chunk):
+//   forward  state out of the chunk   = e^{cum_end} h_in + sum_s e^{cum_end-cum_s} dt_s x_s B_s^T
+//   backward state out of the chunk   = e^{cum_end} h_in + sum_s e^{exc_s} dt_s x_s B_s^T
+//   y_t = sum_s Lambda[t,s] (C_t.B_s) dt_s x_s + e^{cum_t} C_t.h_fwd_in
+//         + e^{cum_end-exc_t} C_t.h_bwd_in + 2 D x_t,
+//   Lambda[t,s] = e^{cum_t-cum_s} (s<t), e^{exc_s-exc_t} (s>t), 2 (s=t).
+// Only differences of partial sums that are <= 0 are exponentiated.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "lingen_internal.h"
+
+namespace lingen {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Small device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(__bf16 v) { return static_cast<float>(v); }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return static_cast<__bf16>(v); }
+
+// MFMA 16x16 tiles.  Output layout (both variants): lane l holds
+// D[4*(l/16) + r][l%16] in element r.  Operand layout: lane l supplies row
+// l%16 of A and column l%16 of B, for the k values of its lane group l/16.
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Operand fragment of one MFMA from a k-contiguous row: 8 bf16 (k = 8*g ..
+// 8*g+7) or one float (k = g), g = lane/16.
+template <typename MT> struct Frag;
+template <> struct Frag<__bf16> {
+  using type = bf16x8;
+  static constexpr int K = 32;
+  __device__ static type load(const __bf16* row, int lane) {
+    return *reinterpret_cast<const bf16x8*>(row + (lane >> 4) * 8);
+  }
+};
+template <> struct Frag<float> {
+  using type = float;
+  static constexpr int K = 4;
+  __device__ static type load(const float* row, int lane) { return row[lane >> 4]; }
+};
+
+// Element padding of k-contiguous LDS rows (keeps 16-byte alignment and
+// spreads the 16 rows one fragment load touches over different banks).
+template <typename MT> struct LdsPad { static constexpr int v = 8; };
+template <> struct LdsPad<float> { static constexpr int v = 4; };
+
+// 16-byte global vector, viewed as elements.
+template <typename T> struct Vec16 {
+  static constexpr int n = 16 / sizeof(T);
+  union { uint4 u; T e[16 / sizeof(T)]; };
+};
+
+// Scan position -> canonical token index for the four Rotary Major Scan
+// orders (page "LinGen：基于Mamba机制的线性复杂度高清长视频生成框架", section
+// 关键算法创新 > Rotary Major Scan):
+//   mode 0: s = (t*H + h)*W + w   W first, then H, then T
+//   mode 1: s = (t*W + w)*H + h   H first, then W, then T
+//   mode 2: s = (h*W + w)*T + t   T first, then W, then H
+//   mode 3: s = (w*H + h)*T + t   T first, then H, then W
+struct RmsMap {
+  int mode, T, H, W;
+  __device__ __forceinline__ int canon(int s) const {
+    int t, h, w;
+    switch (mode) {
+      case 0: return s;
+      case 1: { h = s % H; const int r = s / H; w = r % W; t = r / W; break; }
+      case 2: { t = s % T; const int r = s / T; w = r % W; h = r / W; break; }
+      default: { t = s % T; const int r = s / T; h = r % H; w = r / H; break; }
+    }
+    return (t * H + h) * W + w;
+  }
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs of the chip.  Give
+// every XCD a contiguous range of work ids so that the workgroups of all
+// heads of one chunk share one L2 (B, C and dt rows are shared by heads).
+__device__ __forceinline__ int xcd_work_id(int bid, int nblocks) {
+  if (nblocks % 8) return bid;
+  return (bid % 8) * (nblocks / 8) + bid / 8;
+}
+
+// Inclusive and exclusive prefix sums of a_s = dt_s * A over one chunk (Q <=
+// 256 positions), computed by wave 0 and left in LDS.  Ends with a barrier.
+template <int Q>
+__device__ __forceinline__ void chunk_prefix(const float* sdt, float Ah, float* scum, float* sexc) {
+  constexpr int E = (Q + 63) / 64;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    float v[E];
+    float run = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = tid * E + e;
+      v[e] = idx < Q ? sdt[idx] * Ah : 0.f;
+      run += v[e];
+    }
+    float incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(incl, off, 64);
+      if (tid >= off) incl += o;
+    }
+    float base = incl - run;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = tid * E + e;
+      if (idx < Q) {
+        sexc[idx] = base;
+        base += v[e];
+        scum[idx] = base;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// RMS probe kernels: the index map and a scan-order copy.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void rms_index_kernel(RmsMap m, int L, int* __restrict__ perm) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s < L) perm[s] = m.canon(s);
+}
+
+__global__ __launch_bounds__(256) void rms_gather_kernel(const uint4* __restrict__ src, int64_t row16, RmsMap m,
+                                                         int64_t units, uint4* __restrict__ dst) {
+  const int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int s = int(u / row16);
+  const int64_t off = u - int64_t(s) * row16;
+  dst[u] = src[int64_t(m.canon(s)) * row16 + off];
+}
+
+// ---------------------------------------------------------------------------
+// Review tokens: block means at the sampled block positions, then the state
+// the review tokens leave behind.
+// ---------------------------------------------------------------------------
+
+struct ReviewGeom {
+  int pt, ph, pw;   // pooling block
+  int rt, rh, rw;   // points per axis
+  int st, sh, sw;   // stride between sampled blocks, in blocks
+};
+
+template <typename TS>
+__global__ __launch_bounds__(256) void review_pool_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
+                                                          const TS* __restrict__ B, int T, int H, int W, int Hs,
+                                                          int P, int N, ReviewGeom g, float* __restrict__ rx,
+                                                          float* __restrict__ rdt, float* __restrict__ rb) {
+  __shared__ float red[256];
+  const int r = blockIdx.x;
+  const int y = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int i = r / (g.rh * g.rw), j = (r / g.rw) % g.rh, k = r % g.rw;
+  const int t0 = i * g.st * g.pt, h0 = j * g.sh * g.ph, w0 = k * g.sw * g.pw;
+  const int cnt = g.pt * g.ph * g.pw;
+  const float inv = 1.f / float(cnt);
+  auto token = [&](int tl) {
+    const int a = tl / (g.ph * g.pw), b = (tl / g.pw) % g.ph, c = tl % g.pw;
+    return ((t0 + a) * H + (h0 + b)) * W + (w0 + c);
+  };
+  const int width = (y < Hs) ? P : N;   // P and N divide 256 (checked on the host)
+  const int col = tid % width, grp = tid / width, ngrp = 256 / width;
+  float acc = 0.f;
+  for (int tl = grp; tl < cnt; tl += ngrp) {
+    const int64_t tok = token(tl);
+    acc += (y < Hs) ? to_f32(x[(tok * Hs + y) * P + col]) : to_f32(B[tok * N + col]);
+  }
+  red[tid] = acc;
+  __syncthreads();
+  if (tid < width) {
+    float s = 0.f;
+    for (int q = 0; q < ngrp; ++q) s += red[q * width + tid];
+    if (y < Hs) rx[(int64_t(r) * Hs + y) * P + tid] = s * inv;
+    else rb[int64_t(r) * N + tid] = s * inv;
+  }
+  if (y < Hs) {
+    __syncthreads();
+    float d = 0.f;
+    for (int tl = tid; tl < cnt; tl += 256) d += dt[int64_t(token(tl)) * Hs + y];
+    red[tid] = d;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+      if (tid < off) red[tid] += red[tid + off];
+      __syncthreads();
+    }
+    if (tid == 0) rdt[int64_t(r) * Hs + y] = red[0] * inv;
+  }
+}
+
+// h_R[h][p][n] = sum_r exp(sum_{tau>r} a_tau) dt_r x_r[p] B_r[n], from zero.
+__global__ __launch_bounds__(256) void review_state_kernel(const float* __restrict__ rx, const float* __restrict__ rdt,
+                                                           const float* __restrict__ rb, const float* __restrict__ A,
+                                                           int R, int Hs, int P, int N, float* __restrict__ hR) {
+  __shared__ float w[256];
+  const int h = blockIdx.x;
+  if (threadIdx.x == 0) {
+    float suf = 0.f;
+    for (int r = R - 1; r >= 0; --r) {
+      const float d = rdt[r * Hs + h];
+      w[r] = expf(suf) * d;
+      suf += d * A[h];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < P * N; e += 256) {
+    const int p = e / N, n = e % N;
+    float acc = 0.f;
+    for (int r = 0; r < R; ++r) acc += w[r] * rx[(r * Hs + h) * P + p] * rb[r * N + n];
+    hR[int64_t(h) * P * N + e] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase A: chunk states of both directions.
+//   S_f^T[p][n] = sum_s (x_s[p] wf_s) B_s[n],  wf_s = e^{cum_end - cum_s} dt_s
+//   S_b^T[p][n] = sum_s (x_s[p] wb_s) B_s[n],  wb_s = e^{exc_s} dt_s
+// Stored as states[dir][chunk][head][p][n] (fp32), plus logdec = cum_end.
+// ---------------------------------------------------------------------------
+
+template <typename TS, int P, int N, int Q>
+__global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
+                                                              const float* __restrict__ A, const TS* __restrict__ B,
+                                                              RmsMap rms, int Hs, int n_chunks,
+                                                              float* __restrict__ states, float* __restrict__ logdec) {
+  using MT = TS;
+  using F = Frag<MT>;
+  constexpr int KI = F::K;
+  constexpr int QP = Q + LdsPad<MT>::v;
+  constexpr int VEC = Vec16<TS>::n;
+  static_assert(Q % KI == 0 && P % 16 == 0 && N % 16 == 0 && P % VEC == 0 && N % VEC == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) MT sXf[P * QP];
+  __shared__ __attribute__((aligned(16))) MT sXb[P * QP];
+  __shared__ __attribute__((aligned(16))) MT sB[N * QP];
+  __shared__ float sDt[Q], sCum[Q], sExc[Q], sWf[Q], sWb[Q];
+  __shared__ int sTok[Q];
+
+  const int work = xcd_work_id(blockIdx.x, gridDim.x);
+  const int c = work / Hs, h = work % Hs;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int i = tid; i < Q; i += 256) {
+    const int tok = rms.canon(c * Q + i);
+    sTok[i] = tok;
+    sDt[i] = dt[int64_t(tok) * Hs + h];
+  }
+  __syncthreads();
+  const float Ah = A[h];
+  chunk_prefix<Q>(sDt, Ah, sCum, sExc);
+  const float cum_end = sCum[Q - 1];
+  for (int i = tid; i < Q; i += 256) {
+    sWf[i] = expf(cum_end - sCum[i]) * sDt[i];
+    sWb[i] = expf(sExc[i]) * sDt[i];
+  }
+  if (tid == 0) logdec[int64_t(c) * Hs + h] = cum_end;
+  __syncthreads();
+
+  // Stage x (scaled, transposed) and B (transposed).  Unit = 16 bytes of one
+  // token row; consecutive threads take consecutive tokens.
+  for (int u = tid; u < Q * (P / VEC); u += 256) {
+    const int s = u % Q, p0 = (u / Q) * VEC;
+    Vec16<TS> v;
+    v.u = *reinterpret_cast<const uint4*>(x + (int64_t(sTok[s]) * Hs + h) * P + p0);
+    const float wf = sWf[s], wb = sWb[s];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float xv = to_f32(v.e[e]);
+      sXf[(p0 + e) * QP + s] = from_f32<MT>(xv * wf);
+      sXb[(p0 + e) * QP + s] = from_f32<MT>(xv * wb);
+    }
+  }
+  for (int u = tid; u < Q * (N / VEC); u += 256) {
+    const int s = u % Q, n0 = (u / Q) * VEC;
+    Vec16<TS> v;
+    v.u = *reinterpret_cast<const uint4*>(B + int64_t(sTok[s]) * N + n0);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) sB[(n0 + e) * QP + s] = v.e[e];
+  }
+  __syncthreads();
+
+  // Wave tiling of the P x N outputs (16x16 tiles, both directions).
+  constexpr int PT = P / 16, NT = N / 16;
+  constexpr int WP = PT >= 4 ? 4 : PT;
+  constexpr int WN = 4 / WP;
+  constexpr int PT_PER = PT / WP;
+  constexpr int NT_PER = (NT + WN - 1) / WN;
+  const int wp = wave % WP, wn = wave / WP;
+  f32x4 accf[PT_PER][NT_PER], accb[PT_PER][NT_PER];
+#pragma unroll
+  for (int i = 0; i < PT_PER; ++i)
+#pragma unroll
+    for (int j = 0; j < NT_PER; ++j) {
+      accf[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accb[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  const int r16 = lane & 15;
+#pragma unroll
+  for (int ks = 0; ks < Q / KI; ++ks) {
+    typename F::type af[PT_PER], ab[PT_PER];
+#pragma unroll
+    for (int i = 0; i < PT_PER; ++i) {
+      const int pt = wp + i * WP;
+      af[i] = F::load(&sXf[(pt * 16 + r16) * QP + ks * KI], lane);
+      ab[i] = F::load(&sXb[(pt * 16 + r16) * QP + ks * KI], lane);
+    }
+#pragma unroll
+    for (int j = 0; j < NT_PER; ++j) {
+      const int nt = wn + j * WN;
+      if (nt < NT) {
+        const typename F::type bf = F::load(&sB[(nt * 16 + r16) * QP + ks * KI], lane);
+#pragma unroll
+        for (int i = 0; i < PT_PER; ++i) {
+          accf[i][j] = mma(af[i], bf, accf[i][j]);
+          accb[i][j] = mma(ab[i], bf, accb[i][j]);
+        }
+      }
+    }
+  }
+  const int64_t per = int64_t(P) * N;
+  float* outf = states + (int64_t(c) * Hs + h) * per;
+  float* outb = states + ((int64_t(n_chunks) + c) * Hs + h) * per;
+  const int g4 = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < PT_PER; ++i)
+#pragma unroll
+    for (int j = 0; j < NT_PER; ++j) {
+      const int nt = wn + j * WN;
+      if (nt < NT) {
+        const int pbase = (wp + i * WP) * 16 + g4, n = nt * 16 + r16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          outf[(pbase + r) * N + n] = accf[i][j][r];
+          outb[(pbase + r) * N + n] = accb[i][j][r];
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// State pass: turns chunk states into the state entering each chunk, in
+// place.  dir 0 walks chunks upward, dir 1 downward; h0 (review state or
+// zero) starts both walks.  Each thread owns 4 consecutive floats of one
+// head's P x N state.
+// ---------------------------------------------------------------------------
+
+template <int U>
+__global__ __launch_bounds__(256) void ssd_state_pass_kernel(float* __restrict__ states, const float* __restrict__ logdec,
+                                                             const float* __restrict__ h0, int Hs, int PN, int n_chunks) {
+  const int dir = blockIdx.y;
+  const int64_t per4 = PN / 4;
+  const int64_t e4 = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e4 >= int64_t(Hs) * per4) return;
+  const int h = int(e4 / per4);
+  float4 hv = h0 ? reinterpret_cast<const float4*>(h0)[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  const int64_t cstride = int64_t(Hs) * per4;
+  float4* base = reinterpret_cast<float4*>(states) + int64_t(dir) * n_chunks * cstride + e4;
+  for (int step = 0; step < n_chunks; step += U) {
+    float4 buf[U];
+    float g[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = step + u;
+      if (k < n_chunks) {
+        const int c = dir ? n_chunks - 1 - k : k;
+        buf[u] = base[int64_t(c) * cstride];
+        g[u] = logdec[int64_t(c) * Hs + h];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = step + u;
+      if (k < n_chunks) {
+        const int c = dir ? n_chunks - 1 - k : k;
+        base[int64_t(c) * cstride] = hv;
+        const float d = expf(g[u]);
+        hv.x = d * hv.x + buf[u].x;
+        hv.y = d * hv.y + buf[u].y;
+        hv.z = d * hv.z + buf[u].z;
+        hv.w = d * hv.w + buf[u].w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase B: chunk outputs.  Per (chunk, head), with t the output position:
+//   G^T[s][t] = B_s . C_t                         (MFMA, k = n)
+//   M^T[s][t] = G^T[s][t] Lambda[t,s] dt_s        (registers)
+//   Y^T[p][t] = sum_s x_s[p] M^T[s][t]            (MFMA, k = s, M^T from registers)
+//             + e^{cum_t}       sum_n Hf[p][n] C_t[n]
+//             + e^{cum_end-exc_t} sum_n Hb[p][n] C_t[n]
+//             + 2 D x_t[p]
+// and y[canon(t)][h*P + p] = Y^T[p][t] (or the MA output is stored there for
+// the attention kernel to add to).
+// ---------------------------------------------------------------------------
+
+template <typename TS, int P, int N, int Q>
+struct OutCfg {
+  static constexpr int QT = Q / 16, PT = P / 16;
+  static constexpr int NW = QT >= 8 ? 8 : 4;               // waves per workgroup
+  static constexpr int WT = NW < QT ? NW : QT;              // waves along t
+  static constexpr int WPW = NW / WT;                       // waves along p
+  static constexpr int T_PER = QT / WT;
+  static constexpr int P_PER = (PT + WPW - 1) / WPW;
+};
+
+template <typename TS, int P, int N, int Q>
+__global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_kernel(
+    const TS* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const TS* __restrict__ B,
+    const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int n_chunks,
+    const float* __restrict__ states, TS* __restrict__ y) {
+  using MT = TS;
+  using F = Frag<MT>;
+  using Cfg = OutCfg<TS, P, N, Q>;
+  constexpr int NTHR = Cfg::NW * 64;
+  constexpr int KI = F::K;
+  constexpr int NP = N + LdsPad<MT>::v;
+  constexpr int QP = Q + LdsPad<MT>::v;
+  constexpr int VEC = Vec16<TS>::n;
+  constexpr bool kBf16 = std::is_same<MT, __bf16>::value;
+  static_assert((N % KI == 0 && Q % 32 == 0) || !kBf16, "bf16 tiles need Q multiple of 32");
+  __shared__ __attribute__((aligned(16))) MT sB[Q * NP];
+  __shared__ __attribute__((aligned(16))) MT sC[Q * NP];
+  __shared__ __attribute__((aligned(16))) MT sXt[P * QP];
+  __shared__ __attribute__((aligned(16))) MT sHf[P * NP];
+  __shared__ __attribute__((aligned(16))) MT sHb[P * NP];
+  __shared__ float sDt[Q], sCum[Q], sExc[Q];
+  __shared__ int sTok[Q];
+
+  const int work = xcd_work_id(blockIdx.x, gridDim.x);
+  const int c = work / Hs, h = work % Hs;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int i = tid; i < Q; i += NTHR) {
+    const int tok = rms.canon(c * Q + i);
+    sTok[i] = tok;
+    sDt[i] = dt[int64_t(tok) * Hs + h];
+  }
+  __syncthreads();
+  const float Ah = A[h];
+  chunk_prefix<Q>(sDt, Ah, sCum, sExc);
+  const float cum_end = sCum[Q - 1];
+
+  // Stage B, C (row-major), x (transposed), and the two entering states.
+  for (int u = tid; u < Q * (N / VEC); u += NTHR) {
+    const int s = u / (N / VEC), n0 = (u % (N / VEC)) * VEC;
+    const int64_t src = int64_t(sTok[s]) * N + n0;
+    const uint4 vb = *reinterpret_cast<const uint4*>(B + src);
+    const uint4 vc = *reinterpret_cast<const uint4*>(C + src);
+    *reinterpret_cast<uint4*>(&sB[s * NP + n0]) = vb;
+    *reinterpret_cast<uint4*>(&sC[s * NP + n0]) = vc;
+  }
+  for (int u = tid; u < Q * (P / VEC); u += NTHR) {
+    const int s = u % Q, p0 = (u / Q) * VEC;
+    Vec16<TS> v;
+    v.u = *reinterpret_cast<const uint4*>(x + (int64_t(sTok[s]) * Hs + h) * P + p0);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) sXt[(p0 + e) * QP + s] = v.e[e];
+  }
+  {
+    const int64_t per = int64_t(P) * N;
+    const float* hf = states + (int64_t(c) * Hs + h) * per;
+    const float* hb = states + ((int64_t(n_chunks) + c) * Hs + h) * per;
+    for (int u = tid; u < P * N / 4; u += NTHR) {
+      const int p = (u * 4) / N, n0 = (u * 4) % N;
+      const float4 a = reinterpret_cast<const float4*>(hf)[u];
+      const float4 b = reinterpret_cast<const float4*>(hb)[u];
+      MT* df = &sHf[p * NP + n0];
+      MT* db = &sHb[p * NP + n0];
+      df[0] = from_f32<MT>(a.x); df[1] = from_f32<MT>(a.y); df[2] = from_f32<MT>(a.z); df[3] = from_f32<MT>(a.w);
+      db[0] = from_f32<MT>(b.x); db[1] = from_f32<MT>(b.y); db[2] = from_f32<MT>(b.z); db[3] = from_f32<MT>(b.w);
+    }
+  }
+  __syncthreads();
+
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int wt = wave % Cfg::WT, wpw = wave / Cfg::WT;
+  const float twoD = 2.f * D[h];
+
+#pragma unroll 1
+  for (int ti = 0; ti < Cfg::T_PER; ++ti) {
+    const int tt = wt + ti * Cfg::WT;
+    const int t = tt * 16 + r16;            // this lane's output position
+    // G^T tiles over all s for this t-tile.
+    f32x4 g[Cfg::QT];
+#pragma unroll
+    for (int st = 0; st < Cfg::QT; ++st) g[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < N / KI; ++ks) {
+      const typename F::type bc = F::load(&sC[t * NP + ks * KI], lane);
+#pragma unroll
+      for (int st = 0; st < Cfg::QT; ++st) {
+        const typename F::type ab = F::load(&sB[(st * 16 + r16) * NP + ks * KI], lane);
+        g[st] = mma(ab, bc, g[st]);
+      }
+    }
+    // Lambda, dt and the diagonal.
+    const float cum_t = sCum[t], exc_t = sExc[t];
+#pragma unroll
+    for (int st = 0; st < Cfg::QT; ++st) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = st * 16 + grp * 4 + r;
+        float lam;
+        if (s < t) lam = expf(cum_t - sCum[s]);
+        else if (s > t) lam = expf(sExc[s] - exc_t);
+        else lam = 2.f;
+        g[st][r] *= lam * sDt[s];
+      }
+    }
+    const float ef = expf(cum_t), eb = expf(cum_end - exc_t);
+#pragma unroll 1
+    for (int pj = 0; pj < Cfg::P_PER; ++pj) {
+      const int pt = wpw + pj * Cfg::WPW;
+      if (pt >= Cfg::PT) break;
+      const int prow = pt * 16 + r16;      // A-operand row of this lane
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kBf16) {
+        // k = s in pairs of s-tiles: lane group g covers s = 32k + 4g + {0..3}
+        // and 32k + 16 + 4g + {0..3}, matching the M^T values it holds.
+#pragma unroll
+        for (int k2 = 0; k2 < Cfg::QT / 2; ++k2) {
+          bf16x8 bm;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bm[r] = static_cast<__bf16>(g[2 * k2][r]);
+            bm[4 + r] = static_cast<__bf16>(g[2 * k2 + 1][r]);
+          }
+          const __bf16* xr = &sXt[prow * QP + k2 * 32 + grp * 4];
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
+          const bf16x8 ax = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc = mma(ax, bm, acc);
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < Cfg::QT; ++st)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float ax = to_f32(sXt[prow * QP + st * 16 + grp * 4 + r]);
+            acc = mma(ax, g[st][r], acc);
+          }
+      }
+      // Inter-chunk terms.
+      f32x4 zf = f32x4{0.f, 0.f, 0.f, 0.f}, zb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < N / KI; ++ks) {
+        const typename F::type bc = F::load(&sC[t * NP + ks * KI], lane);
+        const typename F::type hf = F::load(&sHf[prow * NP + ks * KI], lane);
+        const typename F::type hb = F::load(&sHb[prow * NP + ks * KI], lane);
+        zf = mma(hf, bc, zf);
+        zb = mma(hb, bc, zb);
+      }
+      // Lane holds Y^T[p][t] for p = pt*16 + 4*grp + r.
+      const int p0 = pt * 16 + grp * 4;
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        o[r] = acc[r] + ef * zf[r] + eb * zb[r] + twoD * to_f32(sXt[(p0 + r) * QP + t]);
+      TS* dst = y + int64_t(sTok[t]) * (int64_t(Hs) * P) + int64_t(h) * P + p0;
+      if constexpr (kBf16) {
+        bf16x4 ov;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[r] = static_cast<__bf16>(o[r]);
+        *reinterpret_cast<bf16x4*>(dst) = ov;
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// TESA: one workgroup per (window, head).  Windows are enumerated on the
+// rolled grid (offset by the shift, wrapping), so every window has n_w
+// tokens; a token that wrapped along an axis belongs to a different window
+// of the unrolled partition than one that did not, which the kernel enforces
+// by masking scores between tokens of different wrap classes.  This is the
+// border-cut partition of page "LinGen：基于Mamba机制的线性复杂度高清长视频
+// 生成框架", section 关键算法创新 > TESA (plain and shifted windows alternate),
+// in Swin's roll-and-mask form.
+//   S^T[j][i] = K_j . Q_i           (MFMA, A = K from LDS, B = Q in registers)
+//   online softmax over j per query i (each lane owns one query per tile)
+//   O^T[e][i] += V^T[e][j] P^T[j][i] (MFMA, A = V^T from LDS, B = P^T in registers)
+// ---------------------------------------------------------------------------
+
+struct WinGeom {
+  int T, H, W;
+  int wt, wh, ww;
+  int st, sh, sw;   // shift (0 on unshifted layers)
+  int nwt, nwh, nww;  // windows per axis (T/wt, ...)
+};
+
+template <typename TS, int DH, int NWIN>
+struct AttnCfg {
+  static constexpr int QTILES = NWIN / 16;
+  static constexpr int NWAVE = QTILES >= 4 ? 4 : QTILES;
+  static constexpr int QT_PER = QTILES / NWAVE;       // query tiles per wave
+  static constexpr int KB = 32;                        // keys per block
+};
+
+template <typename TS, int DH, int NWIN>
+__global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_window_kernel(
+    const TS* __restrict__ q, const TS* __restrict__ k, const TS* __restrict__ v, WinGeom wg, int Ha,
+    int accumulate, TS* __restrict__ y) {
+  using MT = TS;
+  using F = Frag<MT>;
+  using Cfg = AttnCfg<TS, DH, NWIN>;
+  constexpr int NTHR = Cfg::NWAVE * 64;
+  constexpr int KI = F::K;
+  constexpr int DP = DH + LdsPad<MT>::v;
+  constexpr int WP = NWIN + LdsPad<MT>::v;
+  constexpr int VEC = Vec16<TS>::n;
+  constexpr bool kBf16 = std::is_same<MT, __bf16>::value;
+  static_assert(NWIN % Cfg::KB == 0 && DH % 16 == 0 && DH % KI == 0, "attention tile shape");
+  __shared__ __attribute__((aligned(16))) MT sK[NWIN * DP];
+  __shared__ __attribute__((aligned(16))) MT sVt[DH * WP];
+  __shared__ int sTok[NWIN];
+  __shared__ int sCls[NWIN];
+
+  const int win = blockIdx.x / Ha, h = blockIdx.x % Ha;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = win / (wg.nwh * wg.nww), wj = (win / wg.nww) % wg.nwh, wk = win % wg.nww;
+  const int64_t rowstride = int64_t(Ha) * DH;
+
+  for (int i = tid; i < NWIN; i += NTHR) {
+    const int a = i / (wg.wh * wg.ww), b = (i / wg.ww) % wg.wh, cc = i % wg.ww;
+    int t = wi * wg.wt + a + wg.st, hh = wj * wg.wh + b + wg.sh, w = wk * wg.ww + cc + wg.sw;
+    int cls = 0;
+    if (t >= wg.T) { t -= wg.T; cls |= 4; }
+    if (hh >= wg.H) { hh -= wg.H; cls |= 2; }
+    if (w >= wg.W) { w -= wg.W; cls |= 1; }
+    sTok[i] = (t * wg.H + hh) * wg.W + w;
+    sCls[i] = cls;
+  }
+  __syncthreads();
+  for (int u = tid; u < NWIN * (DH / VEC); u += NTHR) {
+    const int j = u / (DH / VEC), e0 = (u % (DH / VEC)) * VEC;
+    const int64_t off = int64_t(sTok[j]) * rowstride + int64_t(h) * DH + e0;
+    *reinterpret_cast<uint4*>(&sK[j * DP + e0]) = *reinterpret_cast<const uint4*>(k + off);
+  }
+  for (int u = tid; u < NWIN * (DH / VEC); u += NTHR) {
+    const int j = u % NWIN, e0 = (u / NWIN) * VEC;
+    Vec16<TS> vv;
+    vv.u = *reinterpret_cast<const uint4*>(v + int64_t(sTok[j]) * rowstride + int64_t(h) * DH + e0);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) sVt[(e0 + e) * WP + j] = vv.e[e];
+  }
+  __syncthreads();
+
+  const int r16 = lane & 15, grp = lane >> 4;
+  const float sc = kLog2e * rsqrtf(float(DH));
+  constexpr int ET = DH / 16;
+  constexpr int NKS = DH / KI;
+
+#pragma unroll 1
+  for (int qi = 0; qi < Cfg::QT_PER; ++qi) {
+    const int qtile = wave + qi * Cfg::NWAVE;
+    const int iq = qtile * 16 + r16;          // this lane's query (window-local)
+    const int qcls = sCls[iq];
+    // Q fragments for this query, straight from global memory.
+    typename F::type qf[NKS];
+    {
+      const TS* qrow = q + int64_t(sTok[iq]) * rowstride + int64_t(h) * DH;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = F::load(qrow + ks * KI, lane);
+    }
+    f32x4 o[ET];
+#pragma unroll
+    for (int et = 0; et < ET; ++et) o[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+#pragma unroll 1
+    for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
+      f32x4 s[2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int jrow = jb + jt * 16 + r16;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(F::load(&sK[jrow * DP + ks * KI], lane), qf[ks], s[jt]);
+      }
+      // Lane holds scores for query iq and keys j = jb + 16*jt + 4*grp + r.
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = jb + jt * 16 + grp * 4 + r;
+          const float val = (sCls[j] == qcls) ? s[jt][r] * sc : -INFINITY;
+          s[jt][r] = val;
+          bmax = fmaxf(bmax, val);
+        }
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+      const float mnew = fmaxf(m, bmax);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = exp2f(m - muse);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int et = 0; et < ET; ++et) o[et] *= alpha;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = exp2f(s[jt][r] - muse);
+          s[jt][r] = p;
+          l += p;
+        }
+      if constexpr (kBf16) {
+        bf16x8 pb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pb[r] = static_cast<__bf16>(s[0][r]);
+          pb[4 + r] = static_cast<__bf16>(s[1][r]);
+        }
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+          const __bf16* vr = &sVt[(et * 16 + r16) * WP + jb + grp * 4];
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+          o[et] = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[et]);
+        }
+      } else {
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int et = 0; et < ET; ++et) {
+              const float av = to_f32(sVt[(et * 16 + r16) * WP + jb + jt * 16 + grp * 4 + r]);
+              o[et] = mma(av, s[jt][r], o[et]);
+            }
+      }
+    }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.f / l;
+    TS* yrow = y + int64_t(sTok[iq]) * rowstride + int64_t(h) * DH;
+#pragma unroll
+    for (int et = 0; et < ET; ++et) {
+      const int e0 = et * 16 + grp * 4;
+      float ov[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ov[r] = o[et][r] * inv;
+      if constexpr (kBf16) {
+        bf16x4* dst = reinterpret_cast<bf16x4*>(yrow + e0);
+        bf16x4 res;
+        if (accumulate) {
+          const bf16x4 prev = *dst;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) res[r] = static_cast<__bf16>(static_cast<float>(prev[r]) + ov[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) res[r] = static_cast<__bf16>(ov[r]);
+        }
+        *dst = res;
+      } else {
+        float4* dst = reinterpret_cast<float4*>(yrow + e0);
+        float4 res = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        if (accumulate) {
+          const float4 prev = *dst;
+          res.x += prev.x; res.y += prev.y; res.z += prev.z; res.w += prev.w;
+        }
+        *dst = res;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct Args {
+  const void* x; const float* dt; const float* A; const void* B; const void* C; const float* D;
+  const void* q; const void* k; const void* v;
+};
+
+int64_t elem_bytes(const lingen_mate_shape* s) { return s->dtype == LINGEN_BF16 ? 2 : 4; }
+
+int hip_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
+}
+
+RmsMap make_rms(const lingen_mate_shape* s, int mode) { return RmsMap{mode, s->T, s->H, s->W}; }
+
+template <typename TS>
+int launch_review(const lingen_mate_shape* s, const TS* x, const float* dt, const float* A, const TS* B,
+                  char* ws, const WsLayout& lay, hipStream_t st) {
+  ReviewGeom g;
+  g.pt = s->rpool_t; g.ph = s->rpool_h; g.pw = s->rpool_w;
+  g.rt = s->rgrid_t; g.rh = s->rgrid_h; g.rw = s->rgrid_w;
+  g.st = (s->T / g.pt) / g.rt; g.sh = (s->H / g.ph) / g.rh; g.sw = (s->W / g.pw) / g.rw;
+  float* rx = reinterpret_cast<float*>(ws + lay.review_x);
+  float* rdt = reinterpret_cast<float*>(ws + lay.review_dt);
+  float* rb = reinterpret_cast<float*>(ws + lay.review_b);
+  float* hR = reinterpret_cast<float*>(ws + lay.review_h);
+  review_pool_kernel<TS><<<dim3(s->n_review, s->ssd_heads + 1), 256, 0, st>>>(
+      x, dt, B, s->T, s->H, s->W, s->ssd_heads, s->headdim, s->d_state, g, rx, rdt, rb);
+  if (hip_status()) return LINGEN_ERR_HIP;
+  review_state_kernel<<<s->ssd_heads, 256, 0, st>>>(rx, rdt, rb, A, s->n_review, s->ssd_heads, s->headdim,
+                                                    s->d_state, hR);
+  return hip_status();
+}
+
+// Phase A + state pass (+ review state) for one batch element.
+template <typename TS, int P, int N, int Q>
+int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float* dt, const float* A, const TS* B,
+                  char* ws, hipStream_t st) {
+  const WsLayout lay = ws_layout(s);
+  const int L = int(tokens(s));
+  const int nc = L / Q;
+  const int Hs = s->ssd_heads;
+  float* states = reinterpret_cast<float*>(ws + lay.states);
+  float* logdec = reinterpret_cast<float*>(ws + lay.logdec);
+  const float* h0 = nullptr;
+  if (s->n_review > 0) {
+    if (int rc = launch_review<TS>(s, x, dt, A, B, ws, lay, st)) return rc;
+    h0 = reinterpret_cast<const float*>(ws + lay.review_h);
+  }
+  ssd_chunk_state_kernel<TS, P, N, Q><<<nc * Hs, 256, 0, st>>>(x, dt, A, B, make_rms(s, mode), Hs, nc, states, logdec);
+  if (hip_status()) return LINGEN_ERR_HIP;
+  const int64_t thr = int64_t(Hs) * P * N / 4;
+  ssd_state_pass_kernel<8><<<dim3(unsigned((thr + 255) / 256), 2), 256, 0, st>>>(states, logdec, h0, Hs, P * N, nc);
+  return hip_status();
+}
+
+template <typename TS, int P, int N, int Q>
+int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char* ws, hipStream_t st) {
+  const int L = int(tokens(s));
+  const int nc = L / Q;
+  const int Hs = s->ssd_heads;
+  const WsLayout lay = ws_layout(s);
+  const int64_t eb = elem_bytes(s);
+  for (int b = 0; b < s->batch; ++b) {
+    const TS* x = reinterpret_cast<const TS*>(static_cast<const char*>(a.x) + int64_t(b) * L * Hs * P * eb);
+    const float* dt = a.dt + int64_t(b) * L * Hs;
+    const TS* B = reinterpret_cast<const TS*>(static_cast<const char*>(a.B) + int64_t(b) * L * N * eb);
+    const TS* C = reinterpret_cast<const TS*>(static_cast<const char*>(a.C) + int64_t(b) * L * N * eb);
+    TS* yb = reinterpret_cast<TS*>(static_cast<char*>(y) + int64_t(b) * L * Hs * P * eb);
+    if (int rc = launch_states<TS, P, N, Q>(s, mode, x, dt, a.A, B, ws, st)) return rc;
+    using Cfg = OutCfg<TS, P, N, Q>;
+    ssd_chunk_out_kernel<TS, P, N, Q><<<nc * Hs, Cfg::NW * 64, 0, st>>>(
+        x, dt, a.A, B, C, a.D, make_rms(s, mode), Hs, nc, reinterpret_cast<const float*>(ws + lay.states), yb);
+    if (hip_status()) return LINGEN_ERR_HIP;
+  }
+  return LINGEN_OK;
+}
+
+int dispatch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char* ws, hipStream_t st) {
+  switch (scan_family(s)) {
+    case SCAN_F32_P32_N16_Q16: return launch_ma<float, 32, 16, 16>(s, mode, a, y, ws, st);
+    case SCAN_BF16_P64_N64_Q64: return launch_ma<__bf16, 64, 64, 64>(s, mode, a, y, ws, st);
+    case SCAN_BF16_P64_N128_Q128: return launch_ma<__bf16, 64, 128, 128>(s, mode, a, y, ws, st);
+    default: return LINGEN_ERR_UNSUPPORTED;
+  }
+}
+
+template <typename TS, int DH, int NWIN>
+int launch_te(const lingen_mate_shape* s, int shifted, const void* q, const void* k, const void* v, void* y,
+              int accumulate, hipStream_t st) {
+  WinGeom g;
+  g.T = s->T; g.H = s->H; g.W = s->W;
+  g.wt = s->win_t; g.wh = s->win_h; g.ww = s->win_w;
+  g.st = shifted ? s->win_t / 2 : 0; g.sh = shifted ? s->win_h / 2 : 0; g.sw = shifted ? s->win_w / 2 : 0;
+  g.nwt = s->T / s->win_t; g.nwh = s->H / s->win_h; g.nww = s->W / s->win_w;
+  const int64_t L = tokens(s);
+  const int nwin = g.nwt * g.nwh * g.nww;
+  const int64_t per = L * s->attn_heads * DH * elem_bytes(s);
+  using Cfg = AttnCfg<TS, DH, NWIN>;
+  for (int b = 0; b < s->batch; ++b) {
+    const int64_t off = int64_t(b) * per;
+    tesa_window_kernel<TS, DH, NWIN><<<nwin * s->attn_heads, Cfg::NWAVE * 64, 0, st>>>(
+        reinterpret_cast<const TS*>(static_cast<const char*>(q) + off),
+        reinterpret_cast<const TS*>(static_cast<const char*>(k) + off),
+        reinterpret_cast<const TS*>(static_cast<const char*>(v) + off), g, s->attn_heads, accumulate,
+        reinterpret_cast<TS*>(static_cast<char*>(y) + off));
+    if (hip_status()) return LINGEN_ERR_HIP;
+  }
+  return LINGEN_OK;
+}
+
+int dispatch_te(const lingen_mate_shape* s, int shifted, const void* q, const void* k, const void* v, void* y,
+                int accumulate, hipStream_t st) {
+  switch (attn_family(s)) {
+    case ATTN_F32_D32_W32: return launch_te<float, 32, 32>(s, shifted, q, k, v, y, accumulate, st);
+    case ATTN_BF16_D64_W256: return launch_te<__bf16, 64, 256>(s, shifted, q, k, v, y, accumulate, st);
+    default: return LINGEN_ERR_UNSUPPORTED;
+  }
+}
+
+int check_all(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (int rc = check_ptr(p)) return rc;
+  return LINGEN_OK;
+}
+
+int check_ws(const lingen_mate_shape* s, const void* ws, size_t ws_bytes) {
+  if (int rc = check_ptr(ws)) return rc;
+  if (ws_bytes < ws_layout(s).total) return LINGEN_ERR_WORKSPACE;
+  return LINGEN_OK;
+}
+
+}  // namespace
+}  // namespace lingen
+
+using namespace lingen;
+
+extern "C" {
+
+int lingen_rms_index_device(int32_t mode, int32_t T, int32_t H, int32_t W, int32_t* perm_dev, hipStream_t stream) {
+  if (mode < 0 || mode > 3 || T < 1 || H < 1 || W < 1) return LINGEN_ERR_SHAPE;
+  const int64_t L = int64_t(T) * H * W;
+  if (L > (int64_t(1) << 31) - 1) return LINGEN_ERR_SHAPE;
+  if (int rc = check_ptr(perm_dev)) return rc;
+  rms_index_kernel<<<unsigned((L + 255) / 256), 256, 0, stream>>>(RmsMap{mode, T, H, W}, int(L), perm_dev);
+  return hip_status();
+}
+
+int lingen_rms_gather(const void* src, int64_t row_bytes, int32_t mode, int32_t T, int32_t H, int32_t W, void* dst,
+                      hipStream_t stream) {
+  if (mode < 0 || mode > 3 || T < 1 || H < 1 || W < 1) return LINGEN_ERR_SHAPE;
+  const int64_t L = int64_t(T) * H * W;
+  if (L > (int64_t(1) << 31) - 1) return LINGEN_ERR_SHAPE;
+  if (row_bytes < 16 || row_bytes % 16) return LINGEN_ERR_SHAPE;
+  if (int rc = check_all({src, dst})) return rc;
+  const int64_t row16 = row_bytes / 16;
+  const int64_t units = L * row16;
+  if ((units + 255) / 256 > int64_t(0x7fffffff)) return LINGEN_ERR_SHAPE;
+  rms_gather_kernel<<<unsigned((units + 255) / 256), 256, 0, stream>>>(
+      static_cast<const uint4*>(src), row16, RmsMap{mode, T, H, W}, units, static_cast<uint4*>(dst));
+  return hip_status();
+}
+
+int lingen_ssd_chunk_states(const void* x, const float* dt, const float* A, const void* B, int32_t mode,
+                            const lingen_mate_shape* shape, float* h_fwd, float* h_bwd, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (int rc = validate_shape(shape)) return rc;
+  if (mode < 0 || mode > 3) return LINGEN_ERR_SHAPE;
+  if (int rc = check_all({x, dt, A, B, h_fwd, h_bwd})) return rc;
+  if (int rc = check_ws(shape, workspace, workspace_bytes)) return rc;
+  const lingen_mate_shape* s = shape;
+  const int64_t L = tokens(s);
+  const int64_t Hs = s->ssd_heads, P = s->headdim, N = s->d_state, nc = L / s->chunk;
+  const int64_t eb = elem_bytes(s);
+  const int64_t per = nc * Hs * P * N;       // floats per direction per batch element
+  char* ws = static_cast<char*>(workspace);
+  const WsLayout lay = ws_layout(s);
+  for (int b = 0; b < s->batch; ++b) {
+    const char* xb = static_cast<const char*>(x) + b * L * Hs * P * eb;
+    const float* dtb = dt + b * L * Hs;
+    const char* Bb = static_cast<const char*>(B) + b * L * N * eb;
+    int rc = LINGEN_ERR_UNSUPPORTED;
+    switch (scan_family(s)) {
+      case SCAN_F32_P32_N16_Q16:
+        rc = launch_states<float, 32, 16, 16>(s, mode, reinterpret_cast<const float*>(xb), dtb, A,
+                                              reinterpret_cast<const float*>(Bb), ws, stream);
+        break;
+      case SCAN_BF16_P64_N64_Q64:
+        rc = launch_states<__bf16, 64, 64, 64>(s, mode, reinterpret_cast<const __bf16*>(xb), dtb, A,
+                                               reinterpret_cast<const __bf16*>(Bb), ws, stream);
+        break;
+      case SCAN_BF16_P64_N128_Q128:
+        rc = launch_states<__bf16, 64, 128, 128>(s, mode, reinterpret_cast<const __bf16*>(xb), dtb, A,
+                                                 reinterpret_cast<const __bf16*>(Bb), ws, stream);
+        break;
+      default: break;
+    }
+    if (rc) return rc;
+    const float* st = reinterpret_cast<const float*>(ws + lay.states);
+    if (hipMemcpyAsync(h_fwd + b * per, st, per * sizeof(float), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return LINGEN_ERR_HIP;
+    if (hipMemcpyAsync(h_bwd + b * per, st + per, per * sizeof(float), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return LINGEN_ERR_HIP;
+  }
+  return LINGEN_OK;
+}
+
+int lingen_ma_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                  int32_t mode, const lingen_mate_shape* shape, void* y_ma, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  if (int rc = validate_shape(shape)) return rc;
+  if (mode < 0 || mode > 3) return LINGEN_ERR_SHAPE;
+  if (int rc = check_all({x, dt, A, B, C, D, y_ma})) return rc;
+  if (int rc = check_ws(shape, workspace, workspace_bytes)) return rc;
+  Args a{x, dt, A, B, C, D, nullptr, nullptr, nullptr};
+  return dispatch_ma(shape, mode, a, y_ma, static_cast<char*>(workspace), stream);
+}
+
+int lingen_te_fwd(const void* q, const void* k, const void* v, int32_t shifted, const lingen_mate_shape* shape,
+                  void* y_te, hipStream_t stream) {
+  if (int rc = validate_shape(shape)) return rc;
+  if (int rc = check_all({q, k, v, y_te})) return rc;
+  return dispatch_te(shape, shifted ? 1 : 0, q, k, v, y_te, 0, stream);
+}
+
+int lingen_mate_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                    const void* q, const void* k, const void* v, int32_t layer_idx, const lingen_mate_shape* shape,
+                    void* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int rc = validate_shape(shape)) return rc;
+  if (layer_idx < 0) return LINGEN_ERR_SHAPE;
+  if (int rc = check_all({x, dt, A, B, C, D, q, k, v, y})) return rc;
+  if (int rc = check_ws(shape, workspace, workspace_bytes)) return rc;
+  const int mode = layer_idx % 4;
+  const int shifted = layer_idx % 2;
+  Args a{x, dt, A, B, C, D, q, k, v};
+  if (int rc = dispatch_ma(shape, mode, a, y, static_cast<char*>(workspace), stream)) return rc;
+  return dispatch_te(shape, shifted, q, k, v, y, 1, stream);
+}
+
+}  // extern "C"

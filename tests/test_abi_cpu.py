@@ -1,0 +1,171 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-side checks return the documented status codes before any GPU work.
+No call in this file reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from mate_inputs import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lingen_mate.h")
+
+mate = pytest.importorskip("linear_complexity_video_mate_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mate.LIB_PATH):
+        pytest.fail("liblingen_mate.so is not built (run __graft_entry__.build())")
+    return mate.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lingen_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 10
+    assert sorted(mate.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(-7, 1):
+        assert mate.status_str(code) and mate.status_str(code) != "unknown status"
+    assert mate.status_str(5) == "unknown status"
+
+
+@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+def test_configs_validate(L, cfg):
+    assert mate.lingen_mate_validate(CONFIGS[cfg]) == 0
+
+
+BAD = [
+    ("batch", dict(batch=0), -2),
+    ("T", dict(T=0), -2),
+    ("chunk_not_dividing", dict(chunk=48), -2),
+    ("groups", dict(ngroups=2), -2),
+    ("heads_mismatch", dict(attn_heads=8), -2),
+    ("window_not_dividing", dict(win=(3, 8, 8)), -2),
+    ("dtype", dict(dtype="f16"), -3),
+    ("unsupported_state", dict(d_state=32, chunk=64), -7),
+    ("unsupported_window", dict(win=(2, 8, 8)), -7),
+    ("review_count", dict(n_review=63, rpool=(2, 8, 8), rgrid=(4, 4, 4)), -2),
+    ("review_pool", dict(n_review=64, rpool=(3, 8, 8), rgrid=(4, 4, 4)), -2),
+    ("review_grid", dict(n_review=27, rpool=(2, 8, 8), rgrid=(3, 3, 3)), -2),
+    ("negative_review", dict(n_review=-1), -2),
+    ("huge", dict(T=2 ** 20, H=2 ** 10, W=2 ** 10), -2),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD, ids=[b[0] for b in BAD])
+def test_invalid_shapes(L, name, kw, code):
+    s = CONFIGS[1].with_(**kw)
+    assert mate.lingen_mate_validate(s) == code
+    with pytest.raises(mate.LingenError) as e:
+        mate.lingen_mate_workspace_bytes(s)
+    assert e.value.code == code
+
+
+def test_review_shape_valid(L):
+    s = CONFIGS[1].with_(n_review=64, rpool=(2, 4, 4), rgrid=(4, 4, 4))   # pooled 8x8x8
+    assert mate.lingen_mate_validate(s) == 0
+
+
+@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+def test_workspace_formula(L, cfg):
+    s = CONFIGS[cfg]
+    al = lambda v: (v + 255) // 256 * 256
+    nc = s.L // s.chunk
+    want = al(2 * nc * s.ssd_heads * s.headdim * s.d_state * 4) + al(nc * s.ssd_heads * 4)
+    R = s.n_review
+    if R:
+        want += al(s.ssd_heads * s.headdim * s.d_state * 4) + al(R * s.ssd_heads * s.headdim * 4) \
+            + al(R * s.ssd_heads * 4) + al(R * s.d_state * 4)
+    assert mate.lingen_mate_workspace_bytes(s) == want
+
+
+@pytest.mark.parametrize("mode", range(4))
+@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+def test_host_rms_index_bitexact(L, mode, cfg):
+    s = CONFIGS[cfg]
+    perm, inv = mate.lingen_rms_index(mode, s.T, s.H, s.W)
+    ref = oracle.rms_scan_order(mode, s.T, s.H, s.W)
+    np.testing.assert_array_equal(perm, ref.astype(np.int32))
+    np.testing.assert_array_equal(inv, oracle.rms_inverse(ref).astype(np.int32))
+
+
+def test_host_rms_index_errors(L):
+    buf = np.empty(8, dtype=np.int32)
+    assert L.lingen_rms_index(4, 2, 2, 2, buf.ctypes.data, None) == -2
+    assert L.lingen_rms_index(0, 0, 2, 2, buf.ctypes.data, None) == -2
+    assert L.lingen_rms_index(0, 2 ** 12, 2 ** 12, 2 ** 8, None, None) == -2
+
+
+# -- entry points reject bad arguments before touching the GPU ---------------
+
+FAKE = 0x1000          # 16-byte aligned, never dereferenced
+MISALIGNED = 0x1008
+
+
+def _mate_call(L, shape, ptrs=None, layer=0, ws=FAKE, ws_bytes=None):
+    cs = mate.to_c_shape(shape)
+    if ws_bytes is None:
+        ws_bytes = mate.lingen_mate_workspace_bytes(shape) if mate.lingen_mate_validate(shape) == 0 else 0
+    p = [FAKE] * 10 if ptrs is None else ptrs
+    return L.lingen_mate_fwd(*[ctypes.c_void_p(v) for v in p[:9]], layer, ctypes.byref(cs), ctypes.c_void_p(p[9]),
+                             ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_mate_fwd_rejects_before_launch(L):
+    s = CONFIGS[1]
+    for i in range(10):
+        p = [FAKE] * 10
+        p[i] = 0
+        assert _mate_call(L, s, p) == -1, i
+        p[i] = MISALIGNED
+        assert _mate_call(L, s, p) == -4, i
+    assert _mate_call(L, s, layer=-1) == -2
+    assert _mate_call(L, s, ws=0) == -1
+    need = mate.lingen_mate_workspace_bytes(s)
+    assert _mate_call(L, s, ws_bytes=need - 1) == -5
+    assert _mate_call(L, s.with_(T=3)) == -2
+    cs = None
+    assert L.lingen_mate_fwd(*[ctypes.c_void_p(FAKE)] * 9, 0, cs, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                             need, None) == -1
+
+
+def test_branch_entry_points_reject_before_launch(L):
+    s = CONFIGS[0]
+    cs = mate.to_c_shape(s)
+    F = ctypes.c_void_p(FAKE)
+    Z = ctypes.c_void_p(0)
+    need = mate.lingen_mate_workspace_bytes(s)
+    assert L.lingen_ma_fwd(F, F, F, F, F, F, 4, ctypes.byref(cs), F, F, need, None) == -2
+    assert L.lingen_ma_fwd(F, F, F, F, F, Z, 0, ctypes.byref(cs), F, F, need, None) == -1
+    assert L.lingen_ma_fwd(F, F, F, F, F, F, 0, ctypes.byref(cs), F, F, need - 256, None) == -5
+    assert L.lingen_te_fwd(F, Z, F, 0, ctypes.byref(cs), F, None) == -1
+    assert L.lingen_te_fwd(F, F, F, 0, None, F, None) == -1
+    assert L.lingen_ssd_chunk_states(F, F, F, F, -1, ctypes.byref(cs), F, F, F, need, None) == -2
+    assert L.lingen_ssd_chunk_states(F, F, F, F, 0, ctypes.byref(cs), F, Z, F, need, None) == -1
+    assert L.lingen_rms_gather(F, 24, 0, 2, 2, 2, F, None) == -2
+    assert L.lingen_rms_gather(F, 32, 0, 2, 2, 2, Z, None) == -1
+    assert L.lingen_rms_index_device(5, 2, 2, 2, F, None) == -2
+    assert L.lingen_rms_index_device(0, 2, 2, 2, ctypes.c_void_p(MISALIGNED), None) == -4
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    import linear_complexity_video_mate_amd.binding as b
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "LIB_PATH", "/nonexistent/liblingen_mate.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        b.lib()

@@ -1,0 +1,302 @@
+"""Benchmark of the MATE mixer forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+
+One step = one lingen_mate_fwd call over the whole token tensor: both MA
+stages (chunk states, inter-chunk state pass, chunk outputs), windowed
+attention and the branch sum.  Step k uses layer index k mod 4, so the four
+scan orders and both window phases are timed in equal measure.  Inputs are
+the seeded synthetic tensors of the workload, resident in GPU memory before
+timing starts.
+
+Prints one JSON line: whole-job tokens/s, per-stage times from HIP events
+recorded on the launch stream (lingen_mate_fwd_events), the roofline of the
+dominant kernel against MI355X's peak HBM bandwidth, and the fp64 oracle
+timed on host cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MATE fwd tokens/s (bidir SSD + TESA) at 1 GPU; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+STAGES = ("review", "ssd_chunk_state", "ssd_state_pass", "ssd_chunk_out", "tesa_window")
+KERNEL_SRC = os.path.join(ROOT, "linear_complexity_video_mate_amd", "csrc", "lingen_kernels.hip")
+
+
+# ---------------------------------------------------------------------------
+# HIP events through the HIP runtime's C API
+# ---------------------------------------------------------------------------
+
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.made.append(e.value)
+        return e.value
+
+    def record(self, e: int, stream: int) -> None:
+        if self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def sync(self, e: int) -> None:
+        self.hip.hipEventSynchronize(ctypes.c_void_p(e))
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.made = []
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work per kernel launch (each input read once, each output
+# written once, by that kernel), for one batch element.
+# ---------------------------------------------------------------------------
+
+def kernel_work(s):
+    e = s.elem_bytes
+    L, Hs, P, N, Q = s.L, s.ssd_heads, s.headdim, s.d_state, s.chunk
+    Ha, d, nw = s.attn_heads, s.attn_headdim, s.n_w
+    nc = L // Q
+    states = 2 * nc * Hs * P * N * 4
+    x, y, bc, dt = L * Hs * P * e, L * Hs * P * e, L * N * e, L * Hs * 4
+    qkv = 3 * L * Ha * d * e
+    work = {
+        "ssd_chunk_state": dict(bytes=x + dt + bc + states + nc * Hs * 4,
+                                flops=2 * 2 * nc * Hs * Q * N * P),
+        "ssd_state_pass": dict(bytes=2 * states + nc * Hs * 4, flops=2 * states // 4),
+        "ssd_chunk_out": dict(bytes=x + dt + 2 * bc + states + y,
+                              flops=nc * Hs * (2 * Q * Q * N + 2 * Q * Q * P + 2 * 2 * Q * N * P)),
+        "tesa_window": dict(bytes=qkv + 2 * y, flops=4 * L * nw * d * Ha),
+    }
+    if s.n_review:
+        R = s.n_review
+        blk = s.rpool[0] * s.rpool[1] * s.rpool[2]
+        work["review"] = dict(bytes=R * blk * (Hs * P * e + Hs * 4 + N * e), flops=2 * R * Hs * P * N)
+    return work
+
+
+def compulsory_bytes(s):
+    e = s.elem_bytes
+    L = s.L
+    return L * (2 * s.ssd_heads * s.headdim * e + s.ssd_heads * 4 + 2 * s.d_state * e
+                + 3 * s.attn_heads * s.attn_headdim * e)
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` measured with rocprofv3 counters, if a
+    committed measurement exists for the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != src_hash or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle, as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(s, inp):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from mate_inputs import f32_from_bf16_bits
+
+    def head(name, h):
+        a = inp.store[name]
+        sl = a[[h]] if name in ("A", "D") else a[:, [h]]
+        return (f32_from_bf16_bits(sl) if sl.dtype == np.uint16 else sl).astype(np.float64)
+
+    B, C = inp.f64("B"), inp.f64("C")
+    hx = {n: head(n, 0) for n in ("x", "dt", "A", "D", "q", "k", "v")}
+    review = (s.rpool, s.rgrid) if s.n_review else None
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.ma_fwd(hx["x"], hx["dt"], hx["A"], B, C, hx["D"], 0, s.T, s.H, s.W, review=review)
+        t1 = time.perf_counter()
+        oracle.tesa(hx["q"], hx["k"], hx["v"], s.T, s.H, s.W, s.win, (0, 0, 0))
+        t2 = time.perf_counter()
+    est = (t1 - t0) * s.ssd_heads + (t2 - t1) * s.attn_heads
+    return {
+        "value": s.L / est,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle, single thread: SSD head 0 (both directions, layer 0) "
+                   f"{t1 - t0:.2f} s and attention head 0 {t2 - t1:.2f} s over all {s.L} tokens; "
+                   f"scaled by {s.ssd_heads} SSD heads and {s.attn_heads} attention heads"),
+    }
+
+
+# ---------------------------------------------------------------------------
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the mixer is built and measured on a single MI355X "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import linear_complexity_video_mate_amd as mate
+    from mate_inputs import CONFIGS, CONFIG_NOTES, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    mate.lib()
+    s = CONFIGS[args.config]
+    workload = CONFIG_NOTES[args.config]
+    print(f"[bench] generating inputs: {workload}, {s.L} tokens", file=sys.stderr, flush=True)
+    inp = make_inputs(s, args.config, threads=16)
+    d = {n: inp.torch(n, "cuda") for n in ("x", "dt", "A", "B", "C", "D", "q", "k", "v")}
+    args_t = [d[n] for n in ("x", "dt", "A", "B", "C", "D", "q", "k", "v")]
+    ws = torch.empty(mate.lingen_mate_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    y = torch.empty((1, s.L, s.d_inner), dtype=torch.bfloat16 if s.dtype == "bf16" else torch.float32,
+                    device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+    K, W = args.steps, args.warmup
+    step_events = [[ev.create() for _ in range(6)] for _ in range(K)]
+    warm_events = [ev.create() for _ in range(6)]
+    t_start, t_end = ev.create(), ev.create()
+
+    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    for i in range(W):
+        mate.lingen_mate_fwd_events(*args_t, i % 4, s, warm_events, out=y, workspace=ws)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    wall0 = time.perf_counter()
+    ev.record(t_start, stream)
+    for k in range(K):
+        mate.lingen_mate_fwd_events(*args_t, k % 4, s, step_events[k], out=y, workspace=ws)
+    ev.record(t_end, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev.ms(t_start, t_end)
+    ms_step = total_ms / K
+
+    stage_ms = {name: 0.0 for name in STAGES}
+    per_layer = [0.0] * 4
+    for k in range(K):
+        e = step_events[k]
+        for i, name in enumerate(STAGES):
+            stage_ms[name] += ev.ms(e[i], e[i + 1]) / K
+        per_layer[k % 4] += ev.ms(e[0], e[5]) / (K / 4)
+    ev.close()
+
+    work = kernel_work(s)
+    stages = {}
+    for name in STAGES:
+        if name not in work:
+            continue
+        t = stage_ms[name] / 1e3
+        stages[name] = {
+            "ms": round(stage_ms[name], 4),
+            "GB/s": round(work[name]["bytes"] / t / 1e9, 1),
+            "hbm_frac": round(work[name]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOP/s": round(work[name]["flops"] / t / 1e12, 2),
+            "mfma_frac": round(work[name]["flops"] / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+        }
+    dom = max((n for n in stages), key=lambda n: stage_ms[n])
+    dom_t = stage_ms[dom] / 1e3
+    achieved = work[dom]["bytes"] / dom_t / 1e9
+    roofline = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic_for(dom, workload),
+        "algorithmic_bytes_per_launch": work[dom]["bytes"],
+        "avg_launch_ms": round(stage_ms[dom], 4),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(s, inp)
+
+    comp = compulsory_bytes(s)
+    out = {
+        "metric": METRIC,
+        "value": round(s.L / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": workload,
+            "tokens": s.L,
+            "grid_THW": [s.T, s.H, s.W],
+            "ssd": {"heads": s.ssd_heads, "P": s.headdim, "N": s.d_state, "chunk": s.chunk},
+            "attention": {"heads": s.attn_heads, "d": s.attn_headdim, "window": list(s.win)},
+            "review_tokens": s.n_review,
+            "layer_idx": "step k uses k mod 4",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "per_layer_ms": [round(v, 4) for v in per_layer],
+        "path_vs_compulsory_hbm": round(comp / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "wall_s_timed_region": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

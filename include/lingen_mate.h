@@ -165,6 +165,22 @@ int lingen_mate_fwd(const void* x, const float* dt, const float* A, const void* 
                     int32_t layer_idx, const lingen_mate_shape* shape, void* y,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* lingen_mate_fwd that also records six caller-created HIP events on
+ * `stream` at the stage boundaries of the call, for timing each stage:
+ *   events[0] start                     events[3] after the inter-chunk state pass
+ *   events[1] after review tokens       events[4] after the chunk outputs (MA done)
+ *   events[2] after the chunk states    events[5] after windowed attention (y done)
+ * (events[1] follows events[0] at once when there are no review tokens).
+ * Same arguments, results and errors as lingen_mate_fwd, plus LINGEN_ERR_NULL
+ * for a NULL array or event and LINGEN_ERR_SHAPE for batch != 1.  The events
+ * stay owned by the caller. */
+int lingen_mate_fwd_events(const void* x, const float* dt, const float* A, const void* B,
+                           const void* C, const float* D,
+                           const void* q, const void* k, const void* v,
+                           int32_t layer_idx, const lingen_mate_shape* shape, void* y,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipEvent_t* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,7 @@ from .binding import (
     lib,
     lingen_ma_fwd,
     lingen_mate_fwd,
+    lingen_mate_fwd_events,
     lingen_mate_validate,
     lingen_mate_workspace_bytes,
     lingen_rms_gather,
@@ -36,6 +37,7 @@ __all__ = [
     "lib",
     "lingen_ma_fwd",
     "lingen_mate_fwd",
+    "lingen_mate_fwd_events",
     "lingen_mate_validate",
     "lingen_mate_workspace_bytes",
     "lingen_rms_gather",

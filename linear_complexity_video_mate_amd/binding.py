@@ -41,6 +41,7 @@ EXPORTS = (
     "lingen_ma_fwd",
     "lingen_te_fwd",
     "lingen_mate_fwd",
+    "lingen_mate_fwd_events",
 )
 
 
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
         "lingen_ma_fwd": ([P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_te_fwd": ([P, P, P, I32, SP, P, P], ctypes.c_int),
         "lingen_mate_fwd": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
+        "lingen_mate_fwd_events": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -288,4 +290,28 @@ def lingen_mate_fwd(x, dt, A, B, C, D, q, k, v, layer_idx: int, shape, out=None,
     py = _need(out, "out", td, n["y"])
     workspace, pw, nw = _workspace(shape, workspace)
     _check("lingen_mate_fwd", lib().lingen_mate_fwd(*args, int(layer_idx), ctypes.byref(cs), py, pw, nw, _stream()))
+    return out
+
+
+def lingen_mate_fwd_events(x, dt, A, B, C, D, q, k, v, layer_idx: int, shape, events, out=None, workspace=None):
+    """lingen_mate_fwd plus six caller-created HIP events (raw hipEvent_t
+    handles as ints) recorded at the stage boundaries; returns y."""
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    L = shape.T * shape.H * shape.W
+    if len(events) != 6:
+        raise ValueError("events must hold 6 hipEvent_t handles")
+    if out is None:
+        out = torch.empty((shape.batch, L, shape.ssd_heads * shape.headdim), dtype=td, device="cuda")
+    args = [_need(x, "x", td, n["x"]), _need(dt, "dt", torch.float32, n["dt"]),
+            _need(A, "A", torch.float32, n["A"]), _need(B, "B", td, n["B"]), _need(C, "C", td, n["B"]),
+            _need(D, "D", torch.float32, n["D"]), _need(q, "q", td, n["q"]), _need(k, "k", td, n["q"]),
+            _need(v, "v", td, n["q"])]
+    py = _need(out, "out", td, n["y"])
+    workspace, pw, nw = _workspace(shape, workspace)
+    ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(int(e)) for e in events])
+    _check("lingen_mate_fwd_events", lib().lingen_mate_fwd_events(
+        *args, int(layer_idx), ctypes.byref(cs), py, pw, nw, _stream(), ctypes.cast(ev, ctypes.c_void_p)))
     return out

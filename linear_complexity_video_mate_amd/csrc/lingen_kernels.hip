@@ -833,6 +833,13 @@ int hip_status() {
 
 RmsMap make_rms(const lingen_mate_shape* s, int mode) { return RmsMap{mode, s->T, s->H, s->W}; }
 
+// Optional stage markers (lingen_mate_fwd_events): ev[i] is recorded on the
+// stream when stage boundary i is reached.
+int mark(const hipEvent_t* ev, int i, hipStream_t st) {
+  if (ev == nullptr) return LINGEN_OK;
+  return hipEventRecord(ev[i], st) == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
+}
+
 template <typename TS>
 int launch_review(const lingen_mate_shape* s, const TS* x, const float* dt, const float* A, const TS* B,
                   char* ws, const WsLayout& lay, hipStream_t st) {
@@ -855,7 +862,7 @@ int launch_review(const lingen_mate_shape* s, const TS* x, const float* dt, cons
 // Phase A + state pass (+ review state) for one batch element.
 template <typename TS, int P, int N, int Q>
 int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float* dt, const float* A, const TS* B,
-                  char* ws, hipStream_t st) {
+                  char* ws, hipStream_t st, const hipEvent_t* ev = nullptr) {
   const WsLayout lay = ws_layout(s);
   const int L = int(tokens(s));
   const int nc = L / Q;
@@ -867,15 +874,19 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
     if (int rc = launch_review<TS>(s, x, dt, A, B, ws, lay, st)) return rc;
     h0 = reinterpret_cast<const float*>(ws + lay.review_h);
   }
+  if (int rc = mark(ev, 1, st)) return rc;
   ssd_chunk_state_kernel<TS, P, N, Q><<<nc * Hs, 256, 0, st>>>(x, dt, A, B, make_rms(s, mode), Hs, nc, states, logdec);
   if (hip_status()) return LINGEN_ERR_HIP;
+  if (int rc = mark(ev, 2, st)) return rc;
   const int64_t thr = int64_t(Hs) * P * N / 4;
   ssd_state_pass_kernel<8><<<dim3(unsigned((thr + 255) / 256), 2), 256, 0, st>>>(states, logdec, h0, Hs, P * N, nc);
-  return hip_status();
+  if (hip_status()) return LINGEN_ERR_HIP;
+  return mark(ev, 3, st);
 }
 
 template <typename TS, int P, int N, int Q>
-int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char* ws, hipStream_t st) {
+int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char* ws, hipStream_t st,
+              const hipEvent_t* ev) {
   const int L = int(tokens(s));
   const int nc = L / Q;
   const int Hs = s->ssd_heads;
@@ -887,20 +898,22 @@ int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char
     const TS* B = reinterpret_cast<const TS*>(static_cast<const char*>(a.B) + int64_t(b) * L * N * eb);
     const TS* C = reinterpret_cast<const TS*>(static_cast<const char*>(a.C) + int64_t(b) * L * N * eb);
     TS* yb = reinterpret_cast<TS*>(static_cast<char*>(y) + int64_t(b) * L * Hs * P * eb);
-    if (int rc = launch_states<TS, P, N, Q>(s, mode, x, dt, a.A, B, ws, st)) return rc;
+    if (int rc = launch_states<TS, P, N, Q>(s, mode, x, dt, a.A, B, ws, st, ev)) return rc;
     using Cfg = OutCfg<TS, P, N, Q>;
     ssd_chunk_out_kernel<TS, P, N, Q><<<nc * Hs, Cfg::NW * 64, 0, st>>>(
         x, dt, a.A, B, C, a.D, make_rms(s, mode), Hs, nc, reinterpret_cast<const float*>(ws + lay.states), yb);
     if (hip_status()) return LINGEN_ERR_HIP;
+    if (int rc = mark(ev, 4, st)) return rc;
   }
   return LINGEN_OK;
 }
 
-int dispatch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char* ws, hipStream_t st) {
+int dispatch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char* ws, hipStream_t st,
+                const hipEvent_t* ev = nullptr) {
   switch (scan_family(s)) {
-    case SCAN_F32_P32_N16_Q16: return launch_ma<float, 32, 16, 16>(s, mode, a, y, ws, st);
-    case SCAN_BF16_P64_N64_Q64: return launch_ma<__bf16, 64, 64, 64>(s, mode, a, y, ws, st);
-    case SCAN_BF16_P64_N128_Q128: return launch_ma<__bf16, 64, 128, 128>(s, mode, a, y, ws, st);
+    case SCAN_F32_P32_N16_Q16: return launch_ma<float, 32, 16, 16>(s, mode, a, y, ws, st, ev);
+    case SCAN_BF16_P64_N64_Q64: return launch_ma<__bf16, 64, 64, 64>(s, mode, a, y, ws, st, ev);
+    case SCAN_BF16_P64_N128_Q128: return launch_ma<__bf16, 64, 128, 128>(s, mode, a, y, ws, st, ev);
     default: return LINGEN_ERR_UNSUPPORTED;
   }
 }
@@ -1043,9 +1056,10 @@ int lingen_te_fwd(const void* q, const void* k, const void* v, int32_t shifted, 
   return dispatch_te(shape, shifted ? 1 : 0, q, k, v, y_te, 0, stream);
 }
 
-int lingen_mate_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
-                    const void* q, const void* k, const void* v, int32_t layer_idx, const lingen_mate_shape* shape,
-                    void* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static int mate_fwd_impl(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                         const float* D, const void* q, const void* k, const void* v, int32_t layer_idx,
+                         const lingen_mate_shape* shape, void* y, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream, const hipEvent_t* ev) {
   if (int rc = validate_shape(shape)) return rc;
   if (layer_idx < 0) return LINGEN_ERR_SHAPE;
   if (int rc = check_all({x, dt, A, B, C, D, q, k, v, y})) return rc;
@@ -1053,8 +1067,27 @@ int lingen_mate_fwd(const void* x, const float* dt, const float* A, const void* 
   const int mode = layer_idx % 4;
   const int shifted = layer_idx % 2;
   Args a{x, dt, A, B, C, D, q, k, v};
-  if (int rc = dispatch_ma(shape, mode, a, y, static_cast<char*>(workspace), stream)) return rc;
-  return dispatch_te(shape, shifted, q, k, v, y, 1, stream);
+  if (int rc = mark(ev, 0, stream)) return rc;
+  if (int rc = dispatch_ma(shape, mode, a, y, static_cast<char*>(workspace), stream, ev)) return rc;
+  if (int rc = dispatch_te(shape, shifted, q, k, v, y, 1, stream)) return rc;
+  return mark(ev, 5, stream);
+}
+
+int lingen_mate_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                    const void* q, const void* k, const void* v, int32_t layer_idx, const lingen_mate_shape* shape,
+                    void* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mate_fwd_impl(x, dt, A, B, C, D, q, k, v, layer_idx, shape, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+int lingen_mate_fwd_events(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                           const float* D, const void* q, const void* k, const void* v, int32_t layer_idx,
+                           const lingen_mate_shape* shape, void* y, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, hipEvent_t* events) {
+  if (events == nullptr) return LINGEN_ERR_NULL;
+  if (shape != nullptr && shape->batch != 1) return LINGEN_ERR_SHAPE;
+  for (int i = 0; i < 6; ++i)
+    if (events[i] == nullptr) return LINGEN_ERR_NULL;
+  return mate_fwd_impl(x, dt, A, B, C, D, q, k, v, layer_idx, shape, y, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -85,7 +85,7 @@ def kernel_work(s):
     L, Hs, P, N, Q = s.L, s.ssd_heads, s.headdim, s.d_state, s.chunk
     Ha, d, nw = s.attn_heads, s.attn_headdim, s.n_w
     nc = L // Q
-    states = 2 * nc * Hs * P * N * 4
+    states = 2 * nc * Hs * P * N * e          # chunk states are stored in the input dtype
     x, y, bc, dt = L * Hs * P * e, L * Hs * P * e, L * N * e, L * Hs * 4
     qkv = 3 * L * Ha * d * e
     work = {

@@ -80,7 +80,9 @@ WsLayout ws_layout(const lingen_mate_shape* s) {
   const size_t R = size_t(s->n_review);
   size_t off = 0;
   w.states = off;
-  off = align_up(off + 2 * nc * hs * P * N * sizeof(float));
+  // chunk states are kept in the element type of the inputs (fp32 or bf16)
+  const size_t se = s->dtype == LINGEN_BF16 ? 2 : 4;
+  off = align_up(off + 2 * nc * hs * P * N * se);
   w.logdec = off;
   off = align_up(off + nc * hs * sizeof(float));
   w.review_h = off;

@@ -13,7 +13,7 @@ namespace lingen {
 // batch element (batch elements are processed one after another and reuse
 // the same workspace).
 struct WsLayout {
-  size_t states;   // fp32 [2][n_chunks][Hs][P][N]: chunk states, then scan states
+  size_t states;   // [2][n_chunks][Hs][P][N] in the input dtype: chunk states, then scan states
   size_t logdec;   // fp32 [n_chunks][Hs]: sum of dt*A over each chunk
   size_t review_h; // fp32 [Hs][P][N]: state left by the review tokens
   size_t review_x; // fp32 [R][Hs][P]: pooled review x

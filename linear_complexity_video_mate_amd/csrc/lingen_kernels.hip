@@ -122,38 +122,66 @@ __device__ __forceinline__ int xcd_work_id(int bid, int nblocks) {
   return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
-// Inclusive and exclusive prefix sums of a_s = dt_s * A over one chunk (Q <=
-// 256 positions), computed by wave 0 and left in LDS.  Ends with a barrier.
+// Inclusive and exclusive prefix sums of a_s = dt_s * A over one chunk of Q
+// scan positions (Q <= 256), computed by the calling wave alone (all 64
+// lanes call it; no block barrier inside).
 template <int Q>
-__device__ __forceinline__ void chunk_prefix(const float* sdt, float Ah, float* scum, float* sexc) {
+__device__ __forceinline__ void wave_chunk_prefix(const float* sdt, float Ah, float* scum, float* sexc) {
   constexpr int E = (Q + 63) / 64;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    float v[E];
-    float run = 0.f;
+  const int lane = threadIdx.x & 63;
+  float v[E];
+  float run = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int idx = tid * E + e;
-      v[e] = idx < Q ? sdt[idx] * Ah : 0.f;
-      run += v[e];
-    }
-    float incl = run;
+  for (int e = 0; e < E; ++e) {
+    const int idx = lane * E + e;
+    v[e] = idx < Q ? sdt[idx] * Ah : 0.f;
+    run += v[e];
+  }
+  float incl = run;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(incl, off, 64);
-      if (tid >= off) incl += o;
-    }
-    float base = incl - run;
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  float base = incl - run;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int idx = tid * E + e;
-      if (idx < Q) {
-        sexc[idx] = base;
-        base += v[e];
-        scum[idx] = base;
-      }
+  for (int e = 0; e < E; ++e) {
+    const int idx = lane * E + e;
+    if (idx < Q) {
+      sexc[idx] = base;
+      base += v[e];
+      scum[idx] = base;
     }
   }
+}
+
+// Heads handled by one chunk workgroup (the largest divisor of Hs up to 8).
+constexpr int kHeadGroupMax = 8;
+
+// Per-chunk schedule shared by the heads of one workgroup: the canonical
+// token of every scan position, and per head the step sizes and their
+// inclusive / exclusive prefix sums of dt*A.
+template <int Q>
+struct ChunkSched {
+  int tok[Q];
+  float dt[kHeadGroupMax][Q];
+  float cum[kHeadGroupMax][Q];
+  float exc[kHeadGroupMax][Q];
+};
+
+template <int Q>
+__device__ __forceinline__ void load_chunk_schedule(ChunkSched<Q>& cs, const float* __restrict__ dt,
+                                                    const float* __restrict__ A, RmsMap rms, int c, int Hs, int h0,
+                                                    int hg) {
+  const int tid = threadIdx.x, nthr = blockDim.x, wave = tid >> 6, nwave = nthr >> 6;
+  for (int i = tid; i < Q; i += nthr) cs.tok[i] = rms.canon(c * Q + i);
+  __syncthreads();
+  for (int u = tid; u < Q * hg; u += nthr) {
+    const int i = u / hg, j = u % hg;
+    cs.dt[j][i] = dt[int64_t(cs.tok[i]) * Hs + h0 + j];
+  }
+  __syncthreads();
+  for (int j = wave; j < hg; j += nwave) wave_chunk_prefix<Q>(cs.dt[j], A[h0 + j], cs.cum[j], cs.exc[j]);
   __syncthreads();
 }
 
@@ -256,150 +284,171 @@ __global__ __launch_bounds__(256) void review_state_kernel(const float* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Phase A: chunk states of both directions.
+// Phase A: chunk states of both directions.  One workgroup per (chunk, group
+// of heads); B^T is staged once and reused by every head of the group.
 //   S_f^T[p][n] = sum_s (x_s[p] wf_s) B_s[n],  wf_s = e^{cum_end - cum_s} dt_s
 //   S_b^T[p][n] = sum_s (x_s[p] wb_s) B_s[n],  wb_s = e^{exc_s} dt_s
-// Stored as states[dir][chunk][head][p][n] (fp32), plus logdec = cum_end.
+// Stored in the input element type as states[dir][chunk][head][p][n], plus
+// logdec[chunk][head] = cum_end.
 // ---------------------------------------------------------------------------
 
+template <int P, int N>
+struct StateCfg {
+  static constexpr int PT = P / 16, NT = N / 16;
+  static constexpr int NWAVE = PT * NT >= 16 ? 8 : 4;
+  static constexpr int WP = PT >= 4 ? 4 : PT;       // waves along p
+  static constexpr int WN = NWAVE / WP;               // waves along n
+  static constexpr int PT_PER = PT / WP;
+  static constexpr int NT_PER = (NT + WN - 1) / WN;
+};
+
 template <typename TS, int P, int N, int Q>
-__global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
+__global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
                                                               const float* __restrict__ A, const TS* __restrict__ B,
-                                                              RmsMap rms, int Hs, int n_chunks,
-                                                              float* __restrict__ states, float* __restrict__ logdec) {
+                                                              RmsMap rms, int Hs, int hg, int n_chunks,
+                                                              TS* __restrict__ states, float* __restrict__ logdec) {
   using MT = TS;
   using F = Frag<MT>;
   constexpr int KI = F::K;
   constexpr int QP = Q + LdsPad<MT>::v;
   constexpr int VEC = Vec16<TS>::n;
   static_assert(Q % KI == 0 && P % 16 == 0 && N % 16 == 0 && P % VEC == 0 && N % VEC == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) MT sXf[P * QP];
-  __shared__ __attribute__((aligned(16))) MT sXb[P * QP];
-  __shared__ __attribute__((aligned(16))) MT sB[N * QP];
-  __shared__ float sDt[Q], sCum[Q], sExc[Q], sWf[Q], sWb[Q];
-  __shared__ int sTok[Q];
+  constexpr int XBYTES = 2 * P * QP * int(sizeof(MT));
+  constexpr int OBYTES = 2 * P * N * int(sizeof(TS));
+  constexpr int UBYTES = XBYTES > OBYTES ? XBYTES : OBYTES;
+  __shared__ __attribute__((aligned(16))) MT sBt[N * QP];
+  __shared__ __attribute__((aligned(16))) char sU[UBYTES];   // x staging, then output staging
+  __shared__ ChunkSched<Q> cs;
+  __shared__ float sW[2][Q];
+  MT* sXf = reinterpret_cast<MT*>(sU);
+  MT* sXb = sXf + P * QP;
+  TS* sOut = reinterpret_cast<TS*>(sU);
+  using SC = StateCfg<P, N>;
+  constexpr int NTHR = SC::NWAVE * 64;
 
+  const int ngrp = Hs / hg;
   const int work = xcd_work_id(blockIdx.x, gridDim.x);
-  const int c = work / Hs, h = work % Hs;
+  const int c = work / ngrp, h0 = (work % ngrp) * hg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  for (int i = tid; i < Q; i += 256) {
-    const int tok = rms.canon(c * Q + i);
-    sTok[i] = tok;
-    sDt[i] = dt[int64_t(tok) * Hs + h];
-  }
-  __syncthreads();
-  const float Ah = A[h];
-  chunk_prefix<Q>(sDt, Ah, sCum, sExc);
-  const float cum_end = sCum[Q - 1];
-  for (int i = tid; i < Q; i += 256) {
-    sWf[i] = expf(cum_end - sCum[i]) * sDt[i];
-    sWb[i] = expf(sExc[i]) * sDt[i];
-  }
-  if (tid == 0) logdec[int64_t(c) * Hs + h] = cum_end;
-  __syncthreads();
-
-  // Stage x (scaled, transposed) and B (transposed).  Unit = 16 bytes of one
-  // token row; consecutive threads take consecutive tokens.
-  for (int u = tid; u < Q * (P / VEC); u += 256) {
-    const int s = u % Q, p0 = (u / Q) * VEC;
-    Vec16<TS> v;
-    v.u = *reinterpret_cast<const uint4*>(x + (int64_t(sTok[s]) * Hs + h) * P + p0);
-    const float wf = sWf[s], wb = sWb[s];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const float xv = to_f32(v.e[e]);
-      sXf[(p0 + e) * QP + s] = from_f32<MT>(xv * wf);
-      sXb[(p0 + e) * QP + s] = from_f32<MT>(xv * wb);
-    }
-  }
-  for (int u = tid; u < Q * (N / VEC); u += 256) {
+  load_chunk_schedule<Q>(cs, dt, A, rms, c, Hs, h0, hg);
+  for (int u = tid; u < Q * (N / VEC); u += NTHR) {
     const int s = u % Q, n0 = (u / Q) * VEC;
     Vec16<TS> v;
-    v.u = *reinterpret_cast<const uint4*>(B + int64_t(sTok[s]) * N + n0);
+    v.u = *reinterpret_cast<const uint4*>(B + int64_t(cs.tok[s]) * N + n0);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) sB[(n0 + e) * QP + s] = v.e[e];
+    for (int e = 0; e < VEC; ++e) sBt[(n0 + e) * QP + s] = v.e[e];
   }
-  __syncthreads();
 
-  // Wave tiling of the P x N outputs (16x16 tiles, both directions).
-  constexpr int PT = P / 16, NT = N / 16;
-  constexpr int WP = PT >= 4 ? 4 : PT;
-  constexpr int WN = 4 / WP;
-  constexpr int PT_PER = PT / WP;
-  constexpr int NT_PER = (NT + WN - 1) / WN;
+  constexpr int NT = SC::NT, WP = SC::WP, WN = SC::WN, PT_PER = SC::PT_PER, NT_PER = SC::NT_PER;
   const int wp = wave % WP, wn = wave / WP;
-  f32x4 accf[PT_PER][NT_PER], accb[PT_PER][NT_PER];
-#pragma unroll
-  for (int i = 0; i < PT_PER; ++i)
-#pragma unroll
-    for (int j = 0; j < NT_PER; ++j) {
-      accf[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accb[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int r16 = lane & 15, g4 = (lane >> 4) * 4;
+  const int64_t per = int64_t(P) * N;
+
+#pragma unroll 1
+  for (int hh = 0; hh < hg; ++hh) {
+    const int h = h0 + hh;
+    const float cum_end = cs.cum[hh][Q - 1];
+    for (int i = tid; i < Q; i += NTHR) {
+      const float d = cs.dt[hh][i];
+      sW[0][i] = expf(cum_end - cs.cum[hh][i]) * d;
+      sW[1][i] = expf(cs.exc[hh][i]) * d;
     }
-  const int r16 = lane & 15;
+    if (tid == 0) logdec[int64_t(c) * Hs + h] = cum_end;
+    __syncthreads();
+    for (int u = tid; u < Q * (P / VEC); u += NTHR) {
+      const int s = u % Q, p0 = (u / Q) * VEC;
+      Vec16<TS> v;
+      v.u = *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[s]) * Hs + h) * P + p0);
+      const float wf = sW[0][s], wb = sW[1][s];
 #pragma unroll
-  for (int ks = 0; ks < Q / KI; ++ks) {
-    typename F::type af[PT_PER], ab[PT_PER];
-#pragma unroll
-    for (int i = 0; i < PT_PER; ++i) {
-      const int pt = wp + i * WP;
-      af[i] = F::load(&sXf[(pt * 16 + r16) * QP + ks * KI], lane);
-      ab[i] = F::load(&sXb[(pt * 16 + r16) * QP + ks * KI], lane);
+      for (int e = 0; e < VEC; ++e) {
+        const float xv = to_f32(v.e[e]);
+        sXf[(p0 + e) * QP + s] = from_f32<MT>(xv * wf);
+        sXb[(p0 + e) * QP + s] = from_f32<MT>(xv * wb);
+      }
     }
+    __syncthreads();
+    f32x4 accf[PT_PER][NT_PER], accb[PT_PER][NT_PER];
 #pragma unroll
-    for (int j = 0; j < NT_PER; ++j) {
-      const int nt = wn + j * WN;
-      if (nt < NT) {
-        const typename F::type bf = F::load(&sB[(nt * 16 + r16) * QP + ks * KI], lane);
+    for (int i = 0; i < PT_PER; ++i)
 #pragma unroll
-        for (int i = 0; i < PT_PER; ++i) {
-          accf[i][j] = mma(af[i], bf, accf[i][j]);
-          accb[i][j] = mma(ab[i], bf, accb[i][j]);
+      for (int j = 0; j < NT_PER; ++j) {
+        accf[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accb[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int ks = 0; ks < Q / KI; ++ks) {
+      typename F::type af[PT_PER], ab[PT_PER];
+#pragma unroll
+      for (int i = 0; i < PT_PER; ++i) {
+        const int pt = wp + i * WP;
+        af[i] = F::load(&sXf[(pt * 16 + r16) * QP + ks * KI], lane);
+        ab[i] = F::load(&sXb[(pt * 16 + r16) * QP + ks * KI], lane);
+      }
+#pragma unroll
+      for (int j = 0; j < NT_PER; ++j) {
+        const int nt = wn + j * WN;
+        if (nt < NT) {
+          const typename F::type bf = F::load(&sBt[(nt * 16 + r16) * QP + ks * KI], lane);
+#pragma unroll
+          for (int i = 0; i < PT_PER; ++i) {
+            accf[i][j] = mma(af[i], bf, accf[i][j]);
+            accb[i][j] = mma(ab[i], bf, accb[i][j]);
+          }
         }
       }
+    }
+    __syncthreads();   // x staging (aliased by the output staging) fully read
+#pragma unroll
+    for (int i = 0; i < PT_PER; ++i)
+#pragma unroll
+      for (int j = 0; j < NT_PER; ++j) {
+        const int nt = wn + j * WN;
+        if (nt < NT) {
+          const int pbase = (wp + i * WP) * 16 + g4, n = nt * 16 + r16;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sOut[(pbase + r) * N + n] = from_f32<TS>(accf[i][j][r]);
+            sOut[per + (pbase + r) * N + n] = from_f32<TS>(accb[i][j][r]);
+          }
+        }
+      }
+    __syncthreads();
+    constexpr int VPD = P * N / VEC;   // 16-byte vectors per direction
+    for (int u = tid; u < 2 * VPD; u += NTHR) {
+      const int dir = u / VPD, off = u % VPD;
+      uint4* dst = reinterpret_cast<uint4*>(states + ((int64_t(dir) * n_chunks + c) * Hs + h) * per);
+      dst[off] = reinterpret_cast<const uint4*>(sOut)[u];
     }
   }
-  const int64_t per = int64_t(P) * N;
-  float* outf = states + (int64_t(c) * Hs + h) * per;
-  float* outb = states + ((int64_t(n_chunks) + c) * Hs + h) * per;
-  const int g4 = (lane >> 4) * 4;
-#pragma unroll
-  for (int i = 0; i < PT_PER; ++i)
-#pragma unroll
-    for (int j = 0; j < NT_PER; ++j) {
-      const int nt = wn + j * WN;
-      if (nt < NT) {
-        const int pbase = (wp + i * WP) * 16 + g4, n = nt * 16 + r16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          outf[(pbase + r) * N + n] = accf[i][j][r];
-          outb[(pbase + r) * N + n] = accb[i][j][r];
-        }
-      }
-    }
 }
 
 // ---------------------------------------------------------------------------
 // State pass: turns chunk states into the state entering each chunk, in
-// place.  dir 0 walks chunks upward, dir 1 downward; h0 (review state or
-// zero) starts both walks.  Each thread owns 4 consecutive floats of one
-// head's P x N state.
+// place.  dir 0 walks chunks upward, dir 1 downward; h0 (review state, fp32,
+// or zero) starts both walks.  Each thread owns 16 bytes of one head's
+// P x N state and carries it in fp32.
 // ---------------------------------------------------------------------------
 
-template <int U>
-__global__ __launch_bounds__(256) void ssd_state_pass_kernel(float* __restrict__ states, const float* __restrict__ logdec,
-                                                             const float* __restrict__ h0, int Hs, int PN, int n_chunks) {
+template <typename TS, int U>
+__global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ states, const float* __restrict__ logdec,
+                                                             const float* __restrict__ h0, int Hs, int PN,
+                                                             int n_chunks) {
+  // 4 elements per thread: 8-byte bf16 or 16-byte fp32 accesses.
+  using VT = typename std::conditional<std::is_same<TS, __bf16>::value, bf16x4, f32x4>::type;
   const int dir = blockIdx.y;
-  const int64_t per4 = PN / 4;
-  const int64_t e4 = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (e4 >= int64_t(Hs) * per4) return;
-  const int h = int(e4 / per4);
-  float4 hv = h0 ? reinterpret_cast<const float4*>(h0)[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  const int64_t cstride = int64_t(Hs) * per4;
-  float4* base = reinterpret_cast<float4*>(states) + int64_t(dir) * n_chunks * cstride + e4;
+  const int64_t per_v = PN / 4;
+  const int64_t ev = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (ev >= int64_t(Hs) * per_v) return;
+  const int h = int(ev / per_v);
+  float hv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hv[e] = h0 ? h0[ev * 4 + e] : 0.f;
+  const int64_t cstride = int64_t(Hs) * per_v;
+  VT* base = reinterpret_cast<VT*>(states) + int64_t(dir) * n_chunks * cstride + ev;
   for (int step = 0; step < n_chunks; step += U) {
-    float4 buf[U];
+    VT buf[U];
     float g[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -415,27 +464,37 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(float* __restrict__
       const int k = step + u;
       if (k < n_chunks) {
         const int c = dir ? n_chunks - 1 - k : k;
-        base[int64_t(c) * cstride] = hv;
+        VT o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = from_f32<TS>(hv[e]);
+        base[int64_t(c) * cstride] = o;
         const float d = expf(g[u]);
-        hv.x = d * hv.x + buf[u].x;
-        hv.y = d * hv.y + buf[u].y;
-        hv.z = d * hv.z + buf[u].z;
-        hv.w = d * hv.w + buf[u].w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] = d * hv[e] + to_f32(buf[u][e]);
       }
     }
   }
 }
 
+// Scan states in the workspace -> fp32 output (lingen_ssd_chunk_states).
+template <typename TS>
+__global__ __launch_bounds__(256) void states_to_f32_kernel(const TS* __restrict__ src, float* __restrict__ dst,
+                                                            int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) dst[i] = to_f32(src[i]);
+}
+
 // ---------------------------------------------------------------------------
-// Phase B: chunk outputs.  Per (chunk, head), with t the output position:
-//   G^T[s][t] = B_s . C_t                         (MFMA, k = n)
+// Phase B: chunk outputs.  One workgroup per (chunk, group of heads); wave w
+// owns output positions t of t-tile w.  Per chunk (head independent):
+//   G^T[s][t] = B_s . C_t   (MFMA, fragments straight from global memory)
+// and the C_t fragments are kept in registers.  Per head:
 //   M^T[s][t] = G^T[s][t] Lambda[t,s] dt_s        (registers)
-//   Y^T[p][t] = sum_s x_s[p] M^T[s][t]            (MFMA, k = s, M^T from registers)
-//             + e^{cum_t}       sum_n Hf[p][n] C_t[n]
+//   Y^T[p][t] = sum_s x_s[p] M^T[s][t]             (MFMA, k = s)
+//             + e^{cum_t}         sum_n Hf[p][n] C_t[n]
 //             + e^{cum_end-exc_t} sum_n Hb[p][n] C_t[n]
 //             + 2 D x_t[p]
-// and y[canon(t)][h*P + p] = Y^T[p][t] (or the MA output is stored there for
-// the attention kernel to add to).
+// and y[canon(t)][h*P + p] = Y^T[p][t].
 // ---------------------------------------------------------------------------
 
 template <typename TS, int P, int N, int Q>
@@ -444,15 +503,16 @@ struct OutCfg {
   static constexpr int NW = QT >= 8 ? 8 : 4;               // waves per workgroup
   static constexpr int WT = NW < QT ? NW : QT;              // waves along t
   static constexpr int WPW = NW / WT;                       // waves along p
-  static constexpr int T_PER = QT / WT;
   static constexpr int P_PER = (PT + WPW - 1) / WPW;
+  static_assert(QT <= NW, "one t-tile per wave");
 };
 
 template <typename TS, int P, int N, int Q>
-__global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_kernel(
+__global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) __attribute__((amdgpu_waves_per_eu(4)))
+void ssd_chunk_out_kernel(
     const TS* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const TS* __restrict__ B,
-    const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int n_chunks,
-    const float* __restrict__ states, TS* __restrict__ y) {
+    const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int hg, int n_chunks,
+    const TS* __restrict__ states, TS* __restrict__ y) {
   using MT = TS;
   using F = Frag<MT>;
   using Cfg = OutCfg<TS, P, N, Q>;
@@ -463,96 +523,83 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   constexpr int VEC = Vec16<TS>::n;
   constexpr bool kBf16 = std::is_same<MT, __bf16>::value;
   static_assert((N % KI == 0 && Q % 32 == 0) || !kBf16, "bf16 tiles need Q multiple of 32");
-  __shared__ __attribute__((aligned(16))) MT sB[Q * NP];
-  __shared__ __attribute__((aligned(16))) MT sC[Q * NP];
   __shared__ __attribute__((aligned(16))) MT sXt[P * QP];
   __shared__ __attribute__((aligned(16))) MT sHf[P * NP];
   __shared__ __attribute__((aligned(16))) MT sHb[P * NP];
-  __shared__ float sDt[Q], sCum[Q], sExc[Q];
-  __shared__ int sTok[Q];
+  __shared__ ChunkSched<Q> cs;
 
+  const int ngrp = Hs / hg;
   const int work = xcd_work_id(blockIdx.x, gridDim.x);
-  const int c = work / Hs, h = work % Hs;
+  const int c = work / ngrp, h0 = (work % ngrp) * hg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  for (int i = tid; i < Q; i += NTHR) {
-    const int tok = rms.canon(c * Q + i);
-    sTok[i] = tok;
-    sDt[i] = dt[int64_t(tok) * Hs + h];
-  }
-  __syncthreads();
-  const float Ah = A[h];
-  chunk_prefix<Q>(sDt, Ah, sCum, sExc);
-  const float cum_end = sCum[Q - 1];
-
-  // Stage B, C (row-major), x (transposed), and the two entering states.
-  for (int u = tid; u < Q * (N / VEC); u += NTHR) {
-    const int s = u / (N / VEC), n0 = (u % (N / VEC)) * VEC;
-    const int64_t src = int64_t(sTok[s]) * N + n0;
-    const uint4 vb = *reinterpret_cast<const uint4*>(B + src);
-    const uint4 vc = *reinterpret_cast<const uint4*>(C + src);
-    *reinterpret_cast<uint4*>(&sB[s * NP + n0]) = vb;
-    *reinterpret_cast<uint4*>(&sC[s * NP + n0]) = vc;
-  }
-  for (int u = tid; u < Q * (P / VEC); u += NTHR) {
-    const int s = u % Q, p0 = (u / Q) * VEC;
-    Vec16<TS> v;
-    v.u = *reinterpret_cast<const uint4*>(x + (int64_t(sTok[s]) * Hs + h) * P + p0);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) sXt[(p0 + e) * QP + s] = v.e[e];
-  }
-  {
-    const int64_t per = int64_t(P) * N;
-    const float* hf = states + (int64_t(c) * Hs + h) * per;
-    const float* hb = states + ((int64_t(n_chunks) + c) * Hs + h) * per;
-    for (int u = tid; u < P * N / 4; u += NTHR) {
-      const int p = (u * 4) / N, n0 = (u * 4) % N;
-      const float4 a = reinterpret_cast<const float4*>(hf)[u];
-      const float4 b = reinterpret_cast<const float4*>(hb)[u];
-      MT* df = &sHf[p * NP + n0];
-      MT* db = &sHb[p * NP + n0];
-      df[0] = from_f32<MT>(a.x); df[1] = from_f32<MT>(a.y); df[2] = from_f32<MT>(a.z); df[3] = from_f32<MT>(a.w);
-      db[0] = from_f32<MT>(b.x); db[1] = from_f32<MT>(b.y); db[2] = from_f32<MT>(b.z); db[3] = from_f32<MT>(b.w);
-    }
-  }
-  __syncthreads();
-
   const int r16 = lane & 15, grp = lane >> 4;
-  const int wt = wave % Cfg::WT, wpw = wave / Cfg::WT;
-  const float twoD = 2.f * D[h];
 
+  load_chunk_schedule<Q>(cs, dt, A, rms, c, Hs, h0, hg);
+
+  const int wt = wave % Cfg::WT, wpw = wave / Cfg::WT;
+  const int t = wt * 16 + r16;            // this lane's output position
+  const int64_t tok_t = cs.tok[t];
+  // C_t fragments (B operand, k = n) for the inter-chunk terms, and G^T.
+  typename F::type cfr[N / KI];
+#pragma unroll
+  for (int ks = 0; ks < N / KI; ++ks) cfr[ks] = F::load(C + tok_t * N + ks * KI, lane);
+  f32x4 g[Cfg::QT];
+#pragma unroll
+  for (int st = 0; st < Cfg::QT; ++st) g[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < Cfg::QT; ++st) {
+    const TS* brow = B + int64_t(cs.tok[st * 16 + r16]) * N;
+#pragma unroll
+    for (int ks = 0; ks < N / KI; ++ks) g[st] = mma(F::load(brow + ks * KI, lane), cfr[ks], g[st]);
+  }
+
+  const int64_t per = int64_t(P) * N;
 #pragma unroll 1
-  for (int ti = 0; ti < Cfg::T_PER; ++ti) {
-    const int tt = wt + ti * Cfg::WT;
-    const int t = tt * 16 + r16;            // this lane's output position
-    // G^T tiles over all s for this t-tile.
-    f32x4 g[Cfg::QT];
+  for (int hh = 0; hh < hg; ++hh) {
+    const int h = h0 + hh;
+    // Stage x_h (transposed) and the two entering states of this head.
+    for (int u = tid; u < Q * (P / VEC); u += NTHR) {
+      const int s = u % Q, p0 = (u / Q) * VEC;
+      Vec16<TS> v;
+      v.u = *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[s]) * Hs + h) * P + p0);
 #pragma unroll
-    for (int st = 0; st < Cfg::QT; ++st) g[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < N / KI; ++ks) {
-      const typename F::type bc = F::load(&sC[t * NP + ks * KI], lane);
-#pragma unroll
-      for (int st = 0; st < Cfg::QT; ++st) {
-        const typename F::type ab = F::load(&sB[(st * 16 + r16) * NP + ks * KI], lane);
-        g[st] = mma(ab, bc, g[st]);
+      for (int e = 0; e < VEC; ++e) sXt[(p0 + e) * QP + s] = v.e[e];
+    }
+    {
+      const TS* hf = states + (int64_t(c) * Hs + h) * per;
+      const TS* hb = states + ((int64_t(n_chunks) + c) * Hs + h) * per;
+      for (int u = tid; u < P * (N / VEC); u += NTHR) {
+        const int p = u / (N / VEC), n0 = (u % (N / VEC)) * VEC;
+        *reinterpret_cast<uint4*>(&sHf[p * NP + n0]) = reinterpret_cast<const uint4*>(hf)[u];
+        *reinterpret_cast<uint4*>(&sHb[p * NP + n0]) = reinterpret_cast<const uint4*>(hb)[u];
       }
     }
-    // Lambda, dt and the diagonal.
-    const float cum_t = sCum[t], exc_t = sExc[t];
+    __syncthreads();
+
+    const float* cum = cs.cum[hh];
+    const float* exc = cs.exc[hh];
+    const float* dth = cs.dt[hh];
+    const float cum_t = cum[t], exc_t = exc[t];
+    // M^T values of this lane (s = 16*st + 4*grp + r), packed for the MFMA
+    // B operand as soon as they are formed: bf16 pairs of s-tiles, or fp32.
+    constexpr int MREG = kBf16 ? Cfg::QT / 2 : Cfg::QT;
+    typename std::conditional<kBf16, bf16x8, f32x4>::type m[MREG];
 #pragma unroll
     for (int st = 0; st < Cfg::QT; ++st) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = st * 16 + grp * 4 + r;
         float lam;
-        if (s < t) lam = expf(cum_t - sCum[s]);
-        else if (s > t) lam = expf(sExc[s] - exc_t);
+        if (s < t) lam = expf(cum_t - cum[s]);
+        else if (s > t) lam = expf(exc[s] - exc_t);
         else lam = 2.f;
-        g[st][r] *= lam * sDt[s];
+        const float mv = g[st][r] * lam * dth[s];
+        if constexpr (kBf16) m[st / 2][(st % 2) * 4 + r] = static_cast<__bf16>(mv);
+        else m[st][r] = mv;
       }
     }
-    const float ef = expf(cum_t), eb = expf(cum_end - exc_t);
+    const float ef = expf(cum_t), eb = expf(cum[Q - 1] - exc_t);
+    const float twoD = 2.f * D[h];
 #pragma unroll 1
     for (int pj = 0; pj < Cfg::P_PER; ++pj) {
       const int pt = wpw + pj * Cfg::WPW;
@@ -564,36 +611,23 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
         // and 32k + 16 + 4g + {0..3}, matching the M^T values it holds.
 #pragma unroll
         for (int k2 = 0; k2 < Cfg::QT / 2; ++k2) {
-          bf16x8 bm;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            bm[r] = static_cast<__bf16>(g[2 * k2][r]);
-            bm[4 + r] = static_cast<__bf16>(g[2 * k2 + 1][r]);
-          }
           const __bf16* xr = &sXt[prow * QP + k2 * 32 + grp * 4];
           const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
           const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
-          const bf16x8 ax = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc = mma(ax, bm, acc);
+          acc = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), m[k2], acc);
         }
       } else {
 #pragma unroll
         for (int st = 0; st < Cfg::QT; ++st)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float ax = to_f32(sXt[prow * QP + st * 16 + grp * 4 + r]);
-            acc = mma(ax, g[st][r], acc);
-          }
+          for (int r = 0; r < 4; ++r)
+            acc = mma(to_f32(sXt[prow * QP + st * 16 + grp * 4 + r]), m[st][r], acc);
       }
-      // Inter-chunk terms.
       f32x4 zf = f32x4{0.f, 0.f, 0.f, 0.f}, zb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < N / KI; ++ks) {
-        const typename F::type bc = F::load(&sC[t * NP + ks * KI], lane);
-        const typename F::type hf = F::load(&sHf[prow * NP + ks * KI], lane);
-        const typename F::type hb = F::load(&sHb[prow * NP + ks * KI], lane);
-        zf = mma(hf, bc, zf);
-        zb = mma(hb, bc, zb);
+        zf = mma(F::load(&sHf[prow * NP + ks * KI], lane), cfr[ks], zf);
+        zb = mma(F::load(&sHb[prow * NP + ks * KI], lane), cfr[ks], zb);
       }
       // Lane holds Y^T[p][t] for p = pt*16 + 4*grp + r.
       const int p0 = pt * 16 + grp * 4;
@@ -601,7 +635,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         o[r] = acc[r] + ef * zf[r] + eb * zb[r] + twoD * to_f32(sXt[(p0 + r) * QP + t]);
-      TS* dst = y + int64_t(sTok[t]) * (int64_t(Hs) * P) + int64_t(h) * P + p0;
+      TS* dst = y + tok_t * (int64_t(Hs) * P) + int64_t(h) * P + p0;
       if constexpr (kBf16) {
         bf16x4 ov;
 #pragma unroll
@@ -611,6 +645,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
         *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
       }
     }
+    __syncthreads();   // staging buffers free for the next head
   }
 }
 
@@ -622,10 +657,12 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 // by masking scores between tokens of different wrap classes.  This is the
 // border-cut partition of page "LinGen：基于Mamba机制的线性复杂度高清长视频
 // 生成框架", section 关键算法创新 > TESA (plain and shifted windows alternate),
-// in Swin's roll-and-mask form.
-//   S^T[j][i] = K_j . Q_i           (MFMA, A = K from LDS, B = Q in registers)
+// in Swin's roll-and-mask form.  Windows with no wrapped token skip the mask.
+//   S^T[j][i] = K_j . Q_i            (MFMA, A = K from LDS, B = Q in registers)
 //   online softmax over j per query i (each lane owns one query per tile)
-//   O^T[e][i] += V^T[e][j] P^T[j][i] (MFMA, A = V^T from LDS, B = P^T in registers)
+//   O^T[e][i] += V^T[e][j] P^T[j][i]  (MFMA, A = V^T from LDS, B = P^T in registers)
+// The key loop is outermost so every K / V^T fragment read from LDS serves
+// all query tiles of the wave.
 // ---------------------------------------------------------------------------
 
 struct WinGeom {
@@ -638,7 +675,7 @@ struct WinGeom {
 template <typename TS, int DH, int NWIN>
 struct AttnCfg {
   static constexpr int QTILES = NWIN / 16;
-  static constexpr int NWAVE = QTILES >= 4 ? 4 : QTILES;
+  static constexpr int NWAVE = QTILES >= 8 ? 8 : QTILES;
   static constexpr int QT_PER = QTILES / NWAVE;       // query tiles per wave
   static constexpr int KB = 32;                        // keys per block
 };
@@ -651,6 +688,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   using F = Frag<MT>;
   using Cfg = AttnCfg<TS, DH, NWIN>;
   constexpr int NTHR = Cfg::NWAVE * 64;
+  constexpr int QTP = Cfg::QT_PER;
   constexpr int KI = F::K;
   constexpr int DP = DH + LdsPad<MT>::v;
   constexpr int WP = NWIN + LdsPad<MT>::v;
@@ -661,12 +699,15 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   __shared__ __attribute__((aligned(16))) MT sVt[DH * WP];
   __shared__ int sTok[NWIN];
   __shared__ int sCls[NWIN];
+  __shared__ int sWrapped;
 
   const int win = blockIdx.x / Ha, h = blockIdx.x % Ha;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = win / (wg.nwh * wg.nww), wj = (win / wg.nww) % wg.nwh, wk = win % wg.nww;
   const int64_t rowstride = int64_t(Ha) * DH;
 
+  if (tid == 0) sWrapped = 0;
+  __syncthreads();
   for (int i = tid; i < NWIN; i += NTHR) {
     const int a = i / (wg.wh * wg.ww), b = (i / wg.ww) % wg.wh, cc = i % wg.ww;
     int t = wi * wg.wt + a + wg.st, hh = wj * wg.wh + b + wg.sh, w = wk * wg.ww + cc + wg.sw;
@@ -676,6 +717,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
     if (w >= wg.W) { w -= wg.W; cls |= 1; }
     sTok[i] = (t * wg.H + hh) * wg.W + w;
     sCls[i] = cls;
+    if (cls) sWrapped = 1;
   }
   __syncthreads();
   for (int u = tid; u < NWIN * (DH / VEC); u += NTHR) {
@@ -690,68 +732,87 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
 #pragma unroll
     for (int e = 0; e < VEC; ++e) sVt[(e0 + e) * WP + j] = vv.e[e];
   }
-  __syncthreads();
 
   const int r16 = lane & 15, grp = lane >> 4;
-  const float sc = kLog2e * rsqrtf(float(DH));
   constexpr int ET = DH / 16;
   constexpr int NKS = DH / KI;
+  // Q fragments of this lane's queries, straight from global memory.
+  typename F::type qf[QTP][NKS];
+  int qcls[QTP];
+#pragma unroll
+  for (int qi = 0; qi < QTP; ++qi) {
+    const int iq = (wave + qi * Cfg::NWAVE) * 16 + r16;
+    const TS* qrow = q + int64_t(sTok[iq]) * rowstride + int64_t(h) * DH;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[qi][ks] = F::load(qrow + ks * KI, lane);
+    qcls[qi] = sCls[iq];
+  }
+  __syncthreads();
+  const bool wrapped = sWrapped != 0;
+  // scores are kept in raw units; exp2((s - m) * sc) with sc = log2(e)/sqrt(d)
+  const float sc = kLog2e * rsqrtf(float(DH));
+
+  f32x4 o[QTP][ET];
+  float m[QTP], l[QTP];
+#pragma unroll
+  for (int qi = 0; qi < QTP; ++qi) {
+    m[qi] = -INFINITY;
+    l[qi] = 0.f;
+#pragma unroll
+    for (int et = 0; et < ET; ++et) o[qi][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
 #pragma unroll 1
-  for (int qi = 0; qi < Cfg::QT_PER; ++qi) {
-    const int qtile = wave + qi * Cfg::NWAVE;
-    const int iq = qtile * 16 + r16;          // this lane's query (window-local)
-    const int qcls = sCls[iq];
-    // Q fragments for this query, straight from global memory.
-    typename F::type qf[NKS];
-    {
-      const TS* qrow = q + int64_t(sTok[iq]) * rowstride + int64_t(h) * DH;
+  for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
+    typename F::type kf[2][NKS];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[ks] = F::load(qrow + ks * KI, lane);
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) kf[jt][ks] = F::load(&sK[(jb + jt * 16 + r16) * DP + ks * KI], lane);
+    int kcls[2][4];
+    if (wrapped) {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kcls[jt][r] = sCls[jb + jt * 16 + grp * 4 + r];
     }
-    f32x4 o[ET];
 #pragma unroll
-    for (int et = 0; et < ET; ++et) o[et] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.f;
-
-#pragma unroll 1
-    for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
+    for (int qi = 0; qi < QTP; ++qi) {
       f32x4 s[2];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
         s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int jrow = jb + jt * 16 + r16;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(F::load(&sK[jrow * DP + ks * KI], lane), qf[ks], s[jt]);
+        for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(kf[jt][ks], qf[qi][ks], s[jt]);
       }
-      // Lane holds scores for query iq and keys j = jb + 16*jt + 4*grp + r.
-      float bmax = -INFINITY;
+      // Lane holds raw scores for query qi and keys j = jb + 16*jt + 4*grp + r.
+      if (wrapped) {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = jb + jt * 16 + grp * 4 + r;
-          const float val = (sCls[j] == qcls) ? s[jt][r] * sc : -INFINITY;
-          s[jt][r] = val;
-          bmax = fmaxf(bmax, val);
-        }
+          for (int r = 0; r < 4; ++r)
+            if (kcls[jt][r] != qcls[qi]) s[jt][r] = -INFINITY;
+      }
+      float bmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-      const float mnew = fmaxf(m, bmax);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2f(m - muse);
-      m = mnew;
-      l *= alpha;
-#pragma unroll
-      for (int et = 0; et < ET; ++et) o[et] *= alpha;
+      const float mnew = fmaxf(m[qi], bmax);
+      const float msc = (mnew == -INFINITY) ? 0.f : mnew * sc;
+      const float alpha = exp2f(m[qi] * sc - msc);
+      m[qi] = mnew;
+      float lsum = 0.f;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(s[jt][r] - muse);
+          const float p = exp2f(fmaf(s[jt][r], sc, -msc));
           s[jt][r] = p;
-          l += p;
+          lsum += p;
         }
+      l[qi] = l[qi] * alpha + lsum;
+#pragma unroll
+      for (int et = 0; et < ET; ++et) o[qi][et] *= alpha;
       if constexpr (kBf16) {
         bf16x8 pb;
 #pragma unroll
@@ -764,7 +825,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
           const __bf16* vr = &sVt[(et * 16 + r16) * WP + jb + grp * 4];
           const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
           const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-          o[et] = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[et]);
+          o[qi][et] = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[qi][et]);
         }
       } else {
 #pragma unroll
@@ -774,20 +835,26 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
 #pragma unroll
             for (int et = 0; et < ET; ++et) {
               const float av = to_f32(sVt[(et * 16 + r16) * WP + jb + jt * 16 + grp * 4 + r]);
-              o[et] = mma(av, s[jt][r], o[et]);
+              o[qi][et] = mma(av, s[jt][r], o[qi][et]);
             }
       }
     }
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float inv = 1.f / l;
+  }
+
+#pragma unroll
+  for (int qi = 0; qi < QTP; ++qi) {
+    float lt = l[qi];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const float inv = 1.f / lt;
+    const int iq = (wave + qi * Cfg::NWAVE) * 16 + r16;
     TS* yrow = y + int64_t(sTok[iq]) * rowstride + int64_t(h) * DH;
 #pragma unroll
     for (int et = 0; et < ET; ++et) {
       const int e0 = et * 16 + grp * 4;
       float ov[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ov[r] = o[et][r] * inv;
+      for (int r = 0; r < 4; ++r) ov[r] = o[qi][et][r] * inv;
       if constexpr (kBf16) {
         bf16x4* dst = reinterpret_cast<bf16x4*>(yrow + e0);
         bf16x4 res;
@@ -833,6 +900,13 @@ int hip_status() {
 
 RmsMap make_rms(const lingen_mate_shape* s, int mode) { return RmsMap{mode, s->T, s->H, s->W}; }
 
+// Heads per chunk workgroup: the largest divisor of Hs not above 8.
+int head_group(int Hs) {
+  for (int g = kHeadGroupMax; g > 1; --g)
+    if (Hs % g == 0) return g;
+  return 1;
+}
+
 // Optional stage markers (lingen_mate_fwd_events): ev[i] is recorded on the
 // stream when stage boundary i is reached.
 int mark(const hipEvent_t* ev, int i, hipStream_t st) {
@@ -867,19 +941,22 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
   const int L = int(tokens(s));
   const int nc = L / Q;
   const int Hs = s->ssd_heads;
-  float* states = reinterpret_cast<float*>(ws + lay.states);
+  TS* states = reinterpret_cast<TS*>(ws + lay.states);
   float* logdec = reinterpret_cast<float*>(ws + lay.logdec);
+  const int hg = head_group(Hs);
   const float* h0 = nullptr;
   if (s->n_review > 0) {
     if (int rc = launch_review<TS>(s, x, dt, A, B, ws, lay, st)) return rc;
     h0 = reinterpret_cast<const float*>(ws + lay.review_h);
   }
   if (int rc = mark(ev, 1, st)) return rc;
-  ssd_chunk_state_kernel<TS, P, N, Q><<<nc * Hs, 256, 0, st>>>(x, dt, A, B, make_rms(s, mode), Hs, nc, states, logdec);
+  ssd_chunk_state_kernel<TS, P, N, Q><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(x, dt, A, B, make_rms(s, mode), Hs, hg, nc,
+                                                                       states, logdec);
   if (hip_status()) return LINGEN_ERR_HIP;
   if (int rc = mark(ev, 2, st)) return rc;
   const int64_t thr = int64_t(Hs) * P * N / 4;
-  ssd_state_pass_kernel<8><<<dim3(unsigned((thr + 255) / 256), 2), 256, 0, st>>>(states, logdec, h0, Hs, P * N, nc);
+  ssd_state_pass_kernel<TS, 16><<<dim3(unsigned((thr + 255) / 256), 2), 256, 0, st>>>(states, logdec, h0, Hs, P * N,
+                                                                                      nc);
   if (hip_status()) return LINGEN_ERR_HIP;
   return mark(ev, 3, st);
 }
@@ -900,8 +977,9 @@ int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char
     TS* yb = reinterpret_cast<TS*>(static_cast<char*>(y) + int64_t(b) * L * Hs * P * eb);
     if (int rc = launch_states<TS, P, N, Q>(s, mode, x, dt, a.A, B, ws, st, ev)) return rc;
     using Cfg = OutCfg<TS, P, N, Q>;
-    ssd_chunk_out_kernel<TS, P, N, Q><<<nc * Hs, Cfg::NW * 64, 0, st>>>(
-        x, dt, a.A, B, C, a.D, make_rms(s, mode), Hs, nc, reinterpret_cast<const float*>(ws + lay.states), yb);
+    const int hg = head_group(Hs);
+    ssd_chunk_out_kernel<TS, P, N, Q><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
+        x, dt, a.A, B, C, a.D, make_rms(s, mode), Hs, hg, nc, reinterpret_cast<const TS*>(ws + lay.states), yb);
     if (hip_status()) return LINGEN_ERR_HIP;
     if (int rc = mark(ev, 4, st)) return rc;
   }
@@ -1029,11 +1107,17 @@ int lingen_ssd_chunk_states(const void* x, const float* dt, const float* A, cons
       default: break;
     }
     if (rc) return rc;
-    const float* st = reinterpret_cast<const float*>(ws + lay.states);
-    if (hipMemcpyAsync(h_fwd + b * per, st, per * sizeof(float), hipMemcpyDeviceToDevice, stream) != hipSuccess)
-      return LINGEN_ERR_HIP;
-    if (hipMemcpyAsync(h_bwd + b * per, st + per, per * sizeof(float), hipMemcpyDeviceToDevice, stream) != hipSuccess)
-      return LINGEN_ERR_HIP;
+    const unsigned blocks = unsigned((per + 255) / 256);
+    if (s->dtype == LINGEN_BF16) {
+      const __bf16* st = reinterpret_cast<const __bf16*>(ws + lay.states);
+      states_to_f32_kernel<__bf16><<<blocks, 256, 0, stream>>>(st, h_fwd + b * per, per);
+      states_to_f32_kernel<__bf16><<<blocks, 256, 0, stream>>>(st + per, h_bwd + b * per, per);
+    } else {
+      const float* st = reinterpret_cast<const float*>(ws + lay.states);
+      states_to_f32_kernel<float><<<blocks, 256, 0, stream>>>(st, h_fwd + b * per, per);
+      states_to_f32_kernel<float><<<blocks, 256, 0, stream>>>(st + per, h_bwd + b * per, per);
+    }
+    if (hip_status()) return LINGEN_ERR_HIP;
   }
   return LINGEN_OK;
 }

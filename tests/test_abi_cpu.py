@@ -86,7 +86,8 @@ def test_workspace_formula(L, cfg):
     s = CONFIGS[cfg]
     al = lambda v: (v + 255) // 256 * 256
     nc = s.L // s.chunk
-    want = al(2 * nc * s.ssd_heads * s.headdim * s.d_state * 4) + al(nc * s.ssd_heads * 4)
+    # chunk states in the input element type, then fp32 chunk decays
+    want = al(2 * nc * s.ssd_heads * s.headdim * s.d_state * s.elem_bytes) + al(nc * s.ssd_heads * 4)
     R = s.n_review
     if R:
         want += al(s.ssd_heads * s.headdim * s.d_state * 4) + al(R * s.ssd_heads * s.headdim * 4) \

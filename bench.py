@@ -164,6 +164,30 @@ def cpu_baseline(s, inp):
     }
 
 
+def copy_calibration(args, mate, torch):
+    """Plain copy of rows of 4 KiB through lingen_rms_gather (mode 0 is the
+    identity order): reads and writes exactly copy_gib GiB each per launch."""
+    rows = int(args.copy_gib * 2 ** 30) // 4096
+    T, H, W = rows // 4096, 64, 64
+    src = torch.empty((T * H * W, 2048), dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    nbytes = src.numel() * 2
+    for _ in range(args.warmup):
+        mate.lingen_rms_gather(src, 0, T, H, W, out=dst)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        mate.lingen_rms_gather(src, 0, T, H, W, out=dst)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    assert torch.equal(dst.view(torch.int16), src.view(torch.int16))
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": round(ms, 4),
+                      "GB/s_read+write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------------------
 
 def main(argv=None):
@@ -173,6 +197,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="instead of the mixer, time a plain device copy of this many GiB (the RMS gather "
+                         "kernel in scan mode 0) and print its bandwidth: the HBM calibration point")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -190,6 +217,8 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     mate.lib()
+    if args.copy_gib > 0:
+        return copy_calibration(args, mate, torch)
     s = CONFIGS[args.config]
     workload = CONFIG_NOTES[args.config]
     print(f"[bench] generating inputs: {workload}, {s.L} tokens", file=sys.stderr, flush=True)

@@ -83,7 +83,7 @@ WsLayout ws_layout(const lingen_mate_shape* s) {
   // chunk states are kept in the element type of the inputs (fp32 or bf16)
   const size_t se = s->dtype == LINGEN_BF16 ? 2 : 4;
   off = align_up(off + 2 * nc * hs * P * N * se);
-  w.logdec = off;
+  w.decay = off;
   off = align_up(off + nc * hs * sizeof(float));
   w.review_h = off;
   off = align_up(off + (R ? hs * P * N * sizeof(float) : 0));

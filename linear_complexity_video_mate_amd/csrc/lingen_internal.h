@@ -14,7 +14,7 @@ namespace lingen {
 // the same workspace).
 struct WsLayout {
   size_t states;   // [2][n_chunks][Hs][P][N] in the input dtype: chunk states, then scan states
-  size_t logdec;   // fp32 [n_chunks][Hs]: sum of dt*A over each chunk
+  size_t decay;    // fp32 [n_chunks][Hs]: exp of the sum of dt*A over each chunk
   size_t review_h; // fp32 [Hs][P][N]: state left by the review tokens
   size_t review_x; // fp32 [R][Hs][P]: pooled review x
   size_t review_dt;// fp32 [R][Hs]

@@ -23,7 +23,8 @@
 // Chunked form of the bidirectional scan used by phases A and B (Mamba2's SSD
 // chunking, extended to the reversed direction).  Inside a chunk of Q scan
 // positions, with a_s = dt_s*A, cum_t = sum_{tau<=t} a_tau and
-// exc_t = cum_t - a_t (both taken within the chunk):
+// exc_t = cum_t - a_t (both taken within the chunk; the kernels keep them in
+// log2 units, i.e. multiplied by log2(e), and exponentiate with v_exp_f32):
 //   forward  state out of the chunk   = e^{cum_end} h_in + sum_s e^{cum_end-cum_s} dt_s x_s B_s^T
 //   backward state out of the chunk   = e^{cum_end} h_in + sum_s e^{exc_s} dt_s x_s B_s^T
 //   y_t = sum_s Lambda[t,s] (C_t.B_s) dt_s x_s + e^{cum_t} C_t.h_fwd_in
@@ -45,6 +46,11 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x with the hardware instruction alone (no range reduction wrapper):
+// exp2(-inf) = 0, and results below the normal range come out as zero or
+// denormal, which is far below every tolerance the callers work to.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
 // Small device helpers
@@ -93,6 +99,32 @@ template <typename T> struct Vec16 {
   union { uint4 u; T e[16 / sizeof(T)]; };
 };
 
+// Staging of TOTAL 16-byte units by NTHR threads (unit u -> thread u % NTHR)
+// in two steps, so that all of a thread's global loads are in flight before
+// the first one is consumed: load() issues them into registers, use() hands
+// each to the caller (typically to be written to LDS).
+template <int TOTAL, int NTHR>
+struct Stage16 {
+  static constexpr int IT = (TOTAL + NTHR - 1) / NTHR;
+  uint4 v[IT];
+  template <typename Load>
+  __device__ __forceinline__ void load(Load f) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int u = int(threadIdx.x) + it * NTHR;
+      if (TOTAL % NTHR == 0 || u < TOTAL) v[it] = f(u);
+    }
+  }
+  template <typename Use>
+  __device__ __forceinline__ void use(Use f) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int u = int(threadIdx.x) + it * NTHR;
+      if (TOTAL % NTHR == 0 || u < TOTAL) f(u, v[it]);
+    }
+  }
+};
+
 // Scan position -> canonical token index for the four Rotary Major Scan
 // orders (page "LinGen：基于Mamba机制的线性复杂度高清长视频生成框架", section
 // 关键算法创新 > Rotary Major Scan):
@@ -122,19 +154,20 @@ __device__ __forceinline__ int xcd_work_id(int bid, int nblocks) {
   return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
-// Inclusive and exclusive prefix sums of a_s = dt_s * A over one chunk of Q
-// scan positions (Q <= 256), computed by the calling wave alone (all 64
-// lanes call it; no block barrier inside).
+// Inclusive and exclusive prefix sums of a_s = dt_s * A * log2(e) over one
+// chunk of Q scan positions (Q <= 256), computed by the calling wave alone
+// (all 64 lanes call it; no block barrier inside).
 template <int Q>
 __device__ __forceinline__ void wave_chunk_prefix(const float* sdt, float Ah, float* scum, float* sexc) {
   constexpr int E = (Q + 63) / 64;
   const int lane = threadIdx.x & 63;
+  const float a2 = Ah * kLog2e;
   float v[E];
   float run = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int idx = lane * E + e;
-    v[e] = idx < Q ? sdt[idx] * Ah : 0.f;
+    v[e] = idx < Q ? sdt[idx] * a2 : 0.f;
     run += v[e];
   }
   float incl = run;
@@ -155,30 +188,42 @@ __device__ __forceinline__ void wave_chunk_prefix(const float* sdt, float Ah, fl
   }
 }
 
-// Heads handled by one chunk workgroup (the largest divisor of Hs up to 8).
+// Heads handled by one chunk workgroup (the largest divisor of Hs up to 8;
+// up to 4 for the chunk-state kernel, whose LDS then fits twice per CU).
 constexpr int kHeadGroupMax = 8;
+constexpr int kStateHeadGroup = 4;
 
 // Per-chunk schedule shared by the heads of one workgroup: the canonical
 // token of every scan position, and per head the step sizes and their
-// inclusive / exclusive prefix sums of dt*A.
-template <int Q>
-struct ChunkSched {
+// inclusive / exclusive prefix sums of dt*A in log2 units.
+template <int Q, int HGM = kHeadGroupMax>
+struct __attribute__((aligned(16))) ChunkSched {
+  static_assert(Q % 4 == 0, "rows are read as float4");
   int tok[Q];
-  float dt[kHeadGroupMax][Q];
-  float cum[kHeadGroupMax][Q];
-  float exc[kHeadGroupMax][Q];
+  float dt[HGM][Q];
+  float cum[HGM][Q];
+  float exc[HGM][Q];
 };
 
-template <int Q>
-__device__ __forceinline__ void load_chunk_schedule(ChunkSched<Q>& cs, const float* __restrict__ dt,
+template <int Q, int NTHR, int HGM>
+__device__ __forceinline__ void load_chunk_schedule(ChunkSched<Q, HGM>& cs, const float* __restrict__ dt,
                                                     const float* __restrict__ A, RmsMap rms, int c, int Hs, int h0,
                                                     int hg) {
-  const int tid = threadIdx.x, nthr = blockDim.x, wave = tid >> 6, nwave = nthr >> 6;
-  for (int i = tid; i < Q; i += nthr) cs.tok[i] = rms.canon(c * Q + i);
+  const int tid = threadIdx.x, wave = tid >> 6;
+  constexpr int nwave = NTHR / 64;
+  for (int i = tid; i < Q; i += NTHR) cs.tok[i] = rms.canon(c * Q + i);
   __syncthreads();
-  for (int u = tid; u < Q * hg; u += nthr) {
-    const int i = u / hg, j = u % hg;
-    cs.dt[j][i] = dt[int64_t(cs.tok[i]) * Hs + h0 + j];
+  constexpr int IT = (Q * HGM + NTHR - 1) / NTHR;
+  float v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int u = tid + it * NTHR;
+    if (u < Q * hg) v[it] = dt[int64_t(cs.tok[u / hg]) * Hs + h0 + u % hg];
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int u = tid + it * NTHR;
+    if (u < Q * hg) cs.dt[u % hg][u / hg] = v[it];
   }
   __syncthreads();
   for (int j = wave; j < hg; j += nwave) wave_chunk_prefix<Q>(cs.dt[j], A[h0 + j], cs.cum[j], cs.exc[j]);
@@ -289,7 +334,7 @@ __global__ __launch_bounds__(256) void review_state_kernel(const float* __restri
 //   S_f^T[p][n] = sum_s (x_s[p] wf_s) B_s[n],  wf_s = e^{cum_end - cum_s} dt_s
 //   S_b^T[p][n] = sum_s (x_s[p] wb_s) B_s[n],  wb_s = e^{exc_s} dt_s
 // Stored in the input element type as states[dir][chunk][head][p][n], plus
-// logdec[chunk][head] = cum_end.
+// decay[chunk][head] = e^{cum_end}.
 // ---------------------------------------------------------------------------
 
 template <int P, int N>
@@ -306,7 +351,7 @@ template <typename TS, int P, int N, int Q>
 __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
                                                               const float* __restrict__ A, const TS* __restrict__ B,
                                                               RmsMap rms, int Hs, int hg, int n_chunks,
-                                                              TS* __restrict__ states, float* __restrict__ logdec) {
+                                                              TS* __restrict__ states, float* __restrict__ decay) {
   using MT = TS;
   using F = Frag<MT>;
   constexpr int KI = F::K;
@@ -318,7 +363,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
   constexpr int UBYTES = XBYTES > OBYTES ? XBYTES : OBYTES;
   __shared__ __attribute__((aligned(16))) MT sBt[N * QP];
   __shared__ __attribute__((aligned(16))) char sU[UBYTES];   // x staging, then output staging
-  __shared__ ChunkSched<Q> cs;
+  __shared__ ChunkSched<Q, kStateHeadGroup> cs;
   __shared__ float sW[2][Q];
   MT* sXf = reinterpret_cast<MT*>(sU);
   MT* sXb = sXf + P * QP;
@@ -331,14 +376,26 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
   const int c = work / ngrp, h0 = (work % ngrp) * hg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  load_chunk_schedule<Q>(cs, dt, A, rms, c, Hs, h0, hg);
-  for (int u = tid; u < Q * (N / VEC); u += NTHR) {
-    const int s = u % Q, n0 = (u / Q) * VEC;
-    Vec16<TS> v;
-    v.u = *reinterpret_cast<const uint4*>(B + int64_t(cs.tok[s]) * N + n0);
+  load_chunk_schedule<Q, NTHR>(cs, dt, A, rms, c, Hs, h0, hg);
+  {
+    Stage16<Q * (N / VEC), NTHR> bs;
+    bs.load([&](int u) { return *reinterpret_cast<const uint4*>(B + int64_t(cs.tok[u % Q]) * N + (u / Q) * VEC); });
+    bs.use([&](int u, uint4 raw) {
+      const int s = u % Q, n0 = (u / Q) * VEC;
+      Vec16<TS> v;
+      v.u = raw;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) sBt[(n0 + e) * QP + s] = v.e[e];
+      for (int e = 0; e < VEC; ++e) sBt[(n0 + e) * QP + s] = v.e[e];
+    });
   }
+  // x of the next head is loaded while the current head is computed.
+  Stage16<Q * (P / VEC), NTHR> xs;
+  auto load_x = [&](int h) {
+    xs.load([&](int u) {
+      return *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[u % Q]) * Hs + h) * P + (u / Q) * VEC);
+    });
+  };
+  load_x(h0);
 
   constexpr int NT = SC::NT, WP = SC::WP, WN = SC::WN, PT_PER = SC::PT_PER, NT_PER = SC::NT_PER;
   const int wp = wave % WP, wn = wave / WP;
@@ -351,15 +408,15 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
     const float cum_end = cs.cum[hh][Q - 1];
     for (int i = tid; i < Q; i += NTHR) {
       const float d = cs.dt[hh][i];
-      sW[0][i] = expf(cum_end - cs.cum[hh][i]) * d;
-      sW[1][i] = expf(cs.exc[hh][i]) * d;
+      sW[0][i] = fast_exp2(cum_end - cs.cum[hh][i]) * d;
+      sW[1][i] = fast_exp2(cs.exc[hh][i]) * d;
     }
-    if (tid == 0) logdec[int64_t(c) * Hs + h] = cum_end;
+    if (tid == 0) decay[int64_t(c) * Hs + h] = fast_exp2(cum_end);
     __syncthreads();
-    for (int u = tid; u < Q * (P / VEC); u += NTHR) {
+    xs.use([&](int u, uint4 raw) {
       const int s = u % Q, p0 = (u / Q) * VEC;
       Vec16<TS> v;
-      v.u = *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[s]) * Hs + h) * P + p0);
+      v.u = raw;
       const float wf = sW[0][s], wb = sW[1][s];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
@@ -367,8 +424,9 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
         sXf[(p0 + e) * QP + s] = from_f32<MT>(xv * wf);
         sXb[(p0 + e) * QP + s] = from_f32<MT>(xv * wb);
       }
-    }
+    });
     __syncthreads();
+    if (hh + 1 < hg) load_x(h + 1);
     f32x4 accf[PT_PER][NT_PER], accb[PT_PER][NT_PER];
 #pragma unroll
     for (int i = 0; i < PT_PER; ++i)
@@ -432,21 +490,23 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
 // ---------------------------------------------------------------------------
 
 template <typename TS, int U>
-__global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ states, const float* __restrict__ logdec,
+__global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ states, const float* __restrict__ decay,
                                                              const float* __restrict__ h0, int Hs, int PN,
                                                              int n_chunks) {
-  // 4 elements per thread: 8-byte bf16 or 16-byte fp32 accesses.
+  // 4 elements per thread: 8-byte bf16 or 16-byte fp32 accesses.  A block
+  // (blockDim.x threads, dividing PN/4) covers consecutive elements of one
+  // head, so the head index and its chunk decays are wave-uniform.
   using VT = typename std::conditional<std::is_same<TS, __bf16>::value, bf16x4, f32x4>::type;
   const int dir = blockIdx.y;
-  const int64_t per_v = PN / 4;
-  const int64_t ev = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (ev >= int64_t(Hs) * per_v) return;
-  const int h = int(ev / per_v);
+  const int blocks_per_head = (PN / 4) / int(blockDim.x);
+  const int h = __builtin_amdgcn_readfirstlane(int(blockIdx.x) / blocks_per_head);
+  const int64_t ev = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   float hv[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) hv[e] = h0 ? h0[ev * 4 + e] : 0.f;
-  const int64_t cstride = int64_t(Hs) * per_v;
+  const int64_t cstride = int64_t(Hs) * PN / 4;
   VT* base = reinterpret_cast<VT*>(states) + int64_t(dir) * n_chunks * cstride + ev;
+  const float* dec = decay + h;
   for (int step = 0; step < n_chunks; step += U) {
     VT buf[U];
     float g[U];
@@ -456,7 +516,7 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ st
       if (k < n_chunks) {
         const int c = dir ? n_chunks - 1 - k : k;
         buf[u] = base[int64_t(c) * cstride];
-        g[u] = logdec[int64_t(c) * Hs + h];
+        g[u] = dec[int64_t(c) * Hs];
       }
     }
 #pragma unroll
@@ -468,9 +528,8 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ st
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = from_f32<TS>(hv[e]);
         base[int64_t(c) * cstride] = o;
-        const float d = expf(g[u]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hv[e] = d * hv[e] + to_f32(buf[u][e]);
+        for (int e = 0; e < 4; ++e) hv[e] = g[u] * hv[e] + to_f32(buf[u][e]);
       }
     }
   }
@@ -508,8 +567,7 @@ struct OutCfg {
 };
 
 template <typename TS, int P, int N, int Q>
-__global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) __attribute__((amdgpu_waves_per_eu(4)))
-void ssd_chunk_out_kernel(
+__global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_kernel(
     const TS* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const TS* __restrict__ B,
     const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int hg, int n_chunks,
     const TS* __restrict__ states, TS* __restrict__ y) {
@@ -534,7 +592,23 @@ void ssd_chunk_out_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, grp = lane >> 4;
 
-  load_chunk_schedule<Q>(cs, dt, A, rms, c, Hs, h0, hg);
+  load_chunk_schedule<Q, NTHR>(cs, dt, A, rms, c, Hs, h0, hg);
+
+  // x and the two entering states of the next head are loaded while the
+  // current head is computed.
+  const int64_t per = int64_t(P) * N;
+  Stage16<Q * (P / VEC), NTHR> xs;
+  Stage16<P * (N / VEC), NTHR> hfs, hbs;
+  auto load_head = [&](int h) {
+    xs.load([&](int u) {
+      return *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[u % Q]) * Hs + h) * P + (u / Q) * VEC);
+    });
+    const uint4* hf = reinterpret_cast<const uint4*>(states + (int64_t(c) * Hs + h) * per);
+    const uint4* hb = reinterpret_cast<const uint4*>(states + ((int64_t(n_chunks) + c) * Hs + h) * per);
+    hfs.load([&](int u) { return hf[u]; });
+    hbs.load([&](int u) { return hb[u]; });
+  };
+  load_head(h0);
 
   const int wt = wave % Cfg::WT, wpw = wave / Cfg::WT;
   const int t = wt * 16 + r16;            // this lane's output position
@@ -543,86 +617,118 @@ void ssd_chunk_out_kernel(
   typename F::type cfr[N / KI];
 #pragma unroll
   for (int ks = 0; ks < N / KI; ++ks) cfr[ks] = F::load(C + tok_t * N + ks * KI, lane);
-  f32x4 g[Cfg::QT];
-#pragma unroll
-  for (int st = 0; st < Cfg::QT; ++st) g[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // G^T is accumulated in fp32 and kept in the operand type (bf16 for bf16
+  // data: the M^T values built from it are rounded to bf16 anyway).
+  using GT = typename std::conditional<kBf16, bf16x4, f32x4>::type;
+  GT g[Cfg::QT];
 #pragma unroll
   for (int st = 0; st < Cfg::QT; ++st) {
     const TS* brow = B + int64_t(cs.tok[st * 16 + r16]) * N;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < N / KI; ++ks) g[st] = mma(F::load(brow + ks * KI, lane), cfr[ks], g[st]);
+    for (int ks = 0; ks < N / KI; ++ks) acc = mma(F::load(brow + ks * KI, lane), cfr[ks], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) g[st][r] = from_f32<MT>(acc[r]);
   }
 
-  const int64_t per = int64_t(P) * N;
 #pragma unroll 1
   for (int hh = 0; hh < hg; ++hh) {
     const int h = h0 + hh;
     // Stage x_h (transposed) and the two entering states of this head.
-    for (int u = tid; u < Q * (P / VEC); u += NTHR) {
+    xs.use([&](int u, uint4 raw) {
       const int s = u % Q, p0 = (u / Q) * VEC;
       Vec16<TS> v;
-      v.u = *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[s]) * Hs + h) * P + p0);
+      v.u = raw;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) sXt[(p0 + e) * QP + s] = v.e[e];
-    }
-    {
-      const TS* hf = states + (int64_t(c) * Hs + h) * per;
-      const TS* hb = states + ((int64_t(n_chunks) + c) * Hs + h) * per;
-      for (int u = tid; u < P * (N / VEC); u += NTHR) {
-        const int p = u / (N / VEC), n0 = (u % (N / VEC)) * VEC;
-        *reinterpret_cast<uint4*>(&sHf[p * NP + n0]) = reinterpret_cast<const uint4*>(hf)[u];
-        *reinterpret_cast<uint4*>(&sHb[p * NP + n0]) = reinterpret_cast<const uint4*>(hb)[u];
-      }
-    }
+    });
+    hfs.use([&](int u, uint4 raw) {
+      *reinterpret_cast<uint4*>(&sHf[(u / (N / VEC)) * NP + (u % (N / VEC)) * VEC]) = raw;
+    });
+    hbs.use([&](int u, uint4 raw) {
+      *reinterpret_cast<uint4*>(&sHb[(u / (N / VEC)) * NP + (u % (N / VEC)) * VEC]) = raw;
+    });
     __syncthreads();
+    if (hh + 1 < hg) load_head(h + 1);
 
     const float* cum = cs.cum[hh];
     const float* exc = cs.exc[hh];
     const float* dth = cs.dt[hh];
     const float cum_t = cum[t], exc_t = exc[t];
-    // M^T values of this lane (s = 16*st + 4*grp + r), packed for the MFMA
-    // B operand as soon as they are formed: bf16 pairs of s-tiles, or fp32.
-    constexpr int MREG = kBf16 ? Cfg::QT / 2 : Cfg::QT;
-    typename std::conditional<kBf16, bf16x8, f32x4>::type m[MREG];
-#pragma unroll
-    for (int st = 0; st < Cfg::QT; ++st) {
+
+    // M^T values of this lane for s-tile st (s = 16*st + 4*grp + r):
+    // s < t: forward decay e^{cum_t - cum_s}; s > t: backward decay
+    // e^{exc_s - exc_t}; s = t: both directions see the token, weight 2.
+    auto m_tile = [&](int st, float (&mv)[4]) {
+      const int sb = st * 16 + grp * 4;
+      const float4 cum4 = *reinterpret_cast<const float4*>(&cum[sb]);
+      const float4 exc4 = *reinterpret_cast<const float4*>(&exc[sb]);
+      const float4 dt4 = *reinterpret_cast<const float4*>(&dth[sb]);
+      const float cv[4] = {cum4.x, cum4.y, cum4.z, cum4.w};
+      const float xv[4] = {exc4.x, exc4.y, exc4.z, exc4.w};
+      const float dv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int s = st * 16 + grp * 4 + r;
-        float lam;
-        if (s < t) lam = expf(cum_t - cum[s]);
-        else if (s > t) lam = expf(exc[s] - exc_t);
-        else lam = 2.f;
-        const float mv = g[st][r] * lam * dth[s];
-        if constexpr (kBf16) m[st / 2][(st % 2) * 4 + r] = static_cast<__bf16>(mv);
-        else m[st][r] = mv;
+        const int s = sb + r;
+        const float arg = s < t ? cum_t - cv[r] : xv[r] - exc_t;
+        const float lam = s == t ? 2.f : fast_exp2(arg);
+        mv[r] = to_f32(g[st][r]) * lam * dv[r];
+      }
+    };
+
+    // Intra-chunk term, s-tiles outermost so one M^T pair is live at a time.
+    f32x4 acc[Cfg::P_PER];
+#pragma unroll
+    for (int pj = 0; pj < Cfg::P_PER; ++pj) acc[pj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kBf16) {
+      // k = s in pairs of s-tiles: lane group g covers s = 32k + 4g + {0..3}
+      // and 32k + 16 + 4g + {0..3}, matching the M^T values it holds.
+#pragma unroll
+      for (int k2 = 0; k2 < Cfg::QT / 2; ++k2) {
+        float m0[4], m1[4];
+        m_tile(2 * k2, m0);
+        m_tile(2 * k2 + 1, m1);
+        bf16x8 bm;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bm[r] = static_cast<__bf16>(m0[r]);
+          bm[4 + r] = static_cast<__bf16>(m1[r]);
+        }
+#pragma unroll
+        for (int pj = 0; pj < Cfg::P_PER; ++pj) {
+          const int pt = wpw + pj * Cfg::WPW;
+          if (pt < Cfg::PT) {
+            const __bf16* xr = &sXt[(pt * 16 + r16) * QP + k2 * 32 + grp * 4];
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
+            acc[pj] = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), bm, acc[pj]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < Cfg::QT; ++st) {
+        float mv[4];
+        m_tile(st, mv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int pj = 0; pj < Cfg::P_PER; ++pj) {
+            const int pt = wpw + pj * Cfg::WPW;
+            if (pt < Cfg::PT)
+              acc[pj] = mma(to_f32(sXt[(pt * 16 + r16) * QP + st * 16 + grp * 4 + r]), mv[r], acc[pj]);
+          }
       }
     }
-    const float ef = expf(cum_t), eb = expf(cum[Q - 1] - exc_t);
+
+    // Inter-chunk terms, the skip, and the store.
+    const float ef = fast_exp2(cum_t), eb = fast_exp2(cum[Q - 1] - exc_t);
     const float twoD = 2.f * D[h];
-#pragma unroll 1
+#pragma unroll
     for (int pj = 0; pj < Cfg::P_PER; ++pj) {
       const int pt = wpw + pj * Cfg::WPW;
       if (pt >= Cfg::PT) break;
       const int prow = pt * 16 + r16;      // A-operand row of this lane
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (kBf16) {
-        // k = s in pairs of s-tiles: lane group g covers s = 32k + 4g + {0..3}
-        // and 32k + 16 + 4g + {0..3}, matching the M^T values it holds.
-#pragma unroll
-        for (int k2 = 0; k2 < Cfg::QT / 2; ++k2) {
-          const __bf16* xr = &sXt[prow * QP + k2 * 32 + grp * 4];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
-          acc = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), m[k2], acc);
-        }
-      } else {
-#pragma unroll
-        for (int st = 0; st < Cfg::QT; ++st)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc = mma(to_f32(sXt[prow * QP + st * 16 + grp * 4 + r]), m[st][r], acc);
-      }
       f32x4 zf = f32x4{0.f, 0.f, 0.f, 0.f}, zb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < N / KI; ++ks) {
@@ -634,7 +740,7 @@ void ssd_chunk_out_kernel(
       float o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        o[r] = acc[r] + ef * zf[r] + eb * zb[r] + twoD * to_f32(sXt[(p0 + r) * QP + t]);
+        o[r] = acc[pj][r] + ef * zf[r] + eb * zb[r] + twoD * to_f32(sXt[(p0 + r) * QP + t]);
       TS* dst = y + tok_t * (int64_t(Hs) * P) + int64_t(h) * P + p0;
       if constexpr (kBf16) {
         bf16x4 ov;
@@ -659,10 +765,13 @@ void ssd_chunk_out_kernel(
 // 生成框架", section 关键算法创新 > TESA (plain and shifted windows alternate),
 // in Swin's roll-and-mask form.  Windows with no wrapped token skip the mask.
 //   S^T[j][i] = K_j . Q_i            (MFMA, A = K from LDS, B = Q in registers)
-//   online softmax over j per query i (each lane owns one query per tile)
-//   O^T[e][i] += V^T[e][j] P^T[j][i]  (MFMA, A = V^T from LDS, B = P^T in registers)
-// The key loop is outermost so every K / V^T fragment read from LDS serves
-// all query tiles of the wave.
+//   pass 1: row maxima of S over the window (each lane owns one query per tile)
+//   pass 2: P^T = 2^((S^T - max) log2(e)/sqrt(d)), row sums, and
+//           O^T[e][i] += V^T[e][j] P^T[j][i]  (MFMA, A = V^T from LDS, B = P^T in registers)
+// Recomputing S in pass 2 costs MFMA time, which this kernel has to spare,
+// and removes the rescaling of the running output that an online softmax
+// needs.  The key loops are outermost so every K / V^T fragment read from
+// LDS serves all query tiles of the wave.
 // ---------------------------------------------------------------------------
 
 struct WinGeom {
@@ -698,7 +807,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   __shared__ __attribute__((aligned(16))) MT sK[NWIN * DP];
   __shared__ __attribute__((aligned(16))) MT sVt[DH * WP];
   __shared__ int sTok[NWIN];
-  __shared__ int sCls[NWIN];
+  __shared__ __attribute__((aligned(16))) int sCls[NWIN];
   __shared__ int sWrapped;
 
   const int win = blockIdx.x / Ha, h = blockIdx.x % Ha;
@@ -720,17 +829,26 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
     if (cls) sWrapped = 1;
   }
   __syncthreads();
-  for (int u = tid; u < NWIN * (DH / VEC); u += NTHR) {
-    const int j = u / (DH / VEC), e0 = (u % (DH / VEC)) * VEC;
-    const int64_t off = int64_t(sTok[j]) * rowstride + int64_t(h) * DH + e0;
-    *reinterpret_cast<uint4*>(&sK[j * DP + e0]) = *reinterpret_cast<const uint4*>(k + off);
-  }
-  for (int u = tid; u < NWIN * (DH / VEC); u += NTHR) {
-    const int j = u % NWIN, e0 = (u / NWIN) * VEC;
-    Vec16<TS> vv;
-    vv.u = *reinterpret_cast<const uint4*>(v + int64_t(sTok[j]) * rowstride + int64_t(h) * DH + e0);
+  {
+    Stage16<NWIN * (DH / VEC), NTHR> ks, vs;
+    ks.load([&](int u) {
+      return *reinterpret_cast<const uint4*>(k + int64_t(sTok[u / (DH / VEC)]) * rowstride + int64_t(h) * DH +
+                                             (u % (DH / VEC)) * VEC);
+    });
+    vs.load([&](int u) {
+      return *reinterpret_cast<const uint4*>(v + int64_t(sTok[u % NWIN]) * rowstride + int64_t(h) * DH +
+                                             (u / NWIN) * VEC);
+    });
+    ks.use([&](int u, uint4 raw) {
+      *reinterpret_cast<uint4*>(&sK[(u / (DH / VEC)) * DP + (u % (DH / VEC)) * VEC]) = raw;
+    });
+    vs.use([&](int u, uint4 raw) {
+      const int j = u % NWIN, e0 = (u / NWIN) * VEC;
+      Vec16<TS> vv;
+      vv.u = raw;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) sVt[(e0 + e) * WP + j] = vv.e[e];
+      for (int e = 0; e < VEC; ++e) sVt[(e0 + e) * WP + j] = vv.e[e];
+    });
   }
 
   const int r16 = lane & 15, grp = lane >> 4;
@@ -749,19 +867,14 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   }
   __syncthreads();
   const bool wrapped = sWrapped != 0;
-  // scores are kept in raw units; exp2((s - m) * sc) with sc = log2(e)/sqrt(d)
+  // scores stay in raw units; p = 2^((s - max) * sc) with sc = log2(e)/sqrt(d)
   const float sc = kLog2e * rsqrtf(float(DH));
 
-  f32x4 o[QTP][ET];
-  float m[QTP], l[QTP];
+  // Pass 1: the row maximum of every query over the keys of its own window
+  // (the query itself is always one of them, so the maximum is finite).
+  float msc[QTP];
 #pragma unroll
-  for (int qi = 0; qi < QTP; ++qi) {
-    m[qi] = -INFINITY;
-    l[qi] = 0.f;
-#pragma unroll
-    for (int et = 0; et < ET; ++et) o[qi][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
+  for (int qi = 0; qi < QTP; ++qi) msc[qi] = -INFINITY;
 #pragma unroll 1
   for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
     typename F::type kf[2][NKS];
@@ -769,12 +882,73 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) kf[jt][ks] = F::load(&sK[(jb + jt * 16 + r16) * DP + ks * KI], lane);
-    int kcls[2][4];
-    if (wrapped) {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
+    for (int qi = 0; qi < QTP; ++qi) {
+      f32x4 s[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) kcls[jt][r] = sCls[jb + jt * 16 + grp * 4 + r];
+      for (int jt = 0; jt < 2; ++jt) {
+        s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(kf[jt][ks], qf[qi][ks], s[jt]);
+      }
+      if (wrapped) {
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          const int4 kc = *reinterpret_cast<const int4*>(&sCls[jb + jt * 16 + grp * 4]);
+          const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[jt][r] = kcv[r] != qcls[qi] ? -INFINITY : s[jt][r];
+        }
+      }
+      msc[qi] = fmaxf(msc[qi], fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))));
+    }
+  }
+#pragma unroll
+  for (int qi = 0; qi < QTP; ++qi) {
+    float mq = fmaxf(msc[qi], __shfl_xor(msc[qi], 16, 64));
+    mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
+    msc[qi] = mq * sc;
+  }
+
+  // The MA output this kernel adds to (fused branch sum) is fetched now so
+  // its latency is hidden behind pass 2.
+  using YV = typename std::conditional<kBf16, bf16x4, f32x4>::type;
+  YV yprev[QTP][ET];
+  if (accumulate) {
+#pragma unroll
+    for (int qi = 0; qi < QTP; ++qi) {
+      const TS* yrow = y + int64_t(sTok[(wave + qi * Cfg::NWAVE) * 16 + r16]) * rowstride + int64_t(h) * DH;
+#pragma unroll
+      for (int et = 0; et < ET; ++et) yprev[qi][et] = *reinterpret_cast<const YV*>(yrow + et * 16 + grp * 4);
+    }
+  }
+
+  // Pass 2: probabilities against the fixed maximum, their sums, and P V.
+  f32x4 o[QTP][ET];
+  float l[QTP];
+#pragma unroll
+  for (int qi = 0; qi < QTP; ++qi) {
+    l[qi] = 0.f;
+#pragma unroll
+    for (int et = 0; et < ET; ++et) o[qi][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll 1
+  for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
+    typename F::type kf[2][NKS];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) kf[jt][ks] = F::load(&sK[(jb + jt * 16 + r16) * DP + ks * KI], lane);
+    bf16x8 vf[kBf16 ? ET : 1];
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        const __bf16* vr = reinterpret_cast<const __bf16*>(&sVt[(et * 16 + r16) * WP + jb + grp * 4]);
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+        vf[et] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
     }
 #pragma unroll
     for (int qi = 0; qi < QTP; ++qi) {
@@ -785,34 +959,25 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(kf[jt][ks], qf[qi][ks], s[jt]);
       }
-      // Lane holds raw scores for query qi and keys j = jb + 16*jt + 4*grp + r.
       if (wrapped) {
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < 2; ++jt) {
+          const int4 kc = *reinterpret_cast<const int4*>(&sCls[jb + jt * 16 + grp * 4]);
+          const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kcls[jt][r] != qcls[qi]) s[jt][r] = -INFINITY;
+          for (int r = 0; r < 4; ++r) s[jt][r] = kcv[r] != qcls[qi] ? -INFINITY : s[jt][r];
+        }
       }
-      float bmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-      const float mnew = fmaxf(m[qi], bmax);
-      const float msc = (mnew == -INFINITY) ? 0.f : mnew * sc;
-      const float alpha = exp2f(m[qi] * sc - msc);
-      m[qi] = mnew;
       float lsum = 0.f;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(fmaf(s[jt][r], sc, -msc));
+          const float p = fast_exp2(fmaf(s[jt][r], sc, -msc[qi]));
           s[jt][r] = p;
           lsum += p;
         }
-      l[qi] = l[qi] * alpha + lsum;
-#pragma unroll
-      for (int et = 0; et < ET; ++et) o[qi][et] *= alpha;
+      l[qi] += lsum;
       if constexpr (kBf16) {
         bf16x8 pb;
 #pragma unroll
@@ -821,12 +986,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
           pb[4 + r] = static_cast<__bf16>(s[1][r]);
         }
 #pragma unroll
-        for (int et = 0; et < ET; ++et) {
-          const __bf16* vr = &sVt[(et * 16 + r16) * WP + jb + grp * 4];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-          o[qi][et] = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[qi][et]);
-        }
+        for (int et = 0; et < ET; ++et) o[qi][et] = mma(vf[et], pb, o[qi][et]);
       } else {
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
@@ -855,27 +1015,11 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
       float ov[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ov[r] = o[qi][et][r] * inv;
-      if constexpr (kBf16) {
-        bf16x4* dst = reinterpret_cast<bf16x4*>(yrow + e0);
-        bf16x4 res;
-        if (accumulate) {
-          const bf16x4 prev = *dst;
+      YV res;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) res[r] = static_cast<__bf16>(static_cast<float>(prev[r]) + ov[r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) res[r] = static_cast<__bf16>(ov[r]);
-        }
-        *dst = res;
-      } else {
-        float4* dst = reinterpret_cast<float4*>(yrow + e0);
-        float4 res = make_float4(ov[0], ov[1], ov[2], ov[3]);
-        if (accumulate) {
-          const float4 prev = *dst;
-          res.x += prev.x; res.y += prev.y; res.z += prev.z; res.w += prev.w;
-        }
-        *dst = res;
-      }
+      for (int r = 0; r < 4; ++r)
+        res[r] = from_f32<TS>(accumulate ? to_f32(yprev[qi][et][r]) + ov[r] : ov[r]);
+      *reinterpret_cast<YV*>(yrow + e0) = res;
     }
   }
 }
@@ -900,9 +1044,9 @@ int hip_status() {
 
 RmsMap make_rms(const lingen_mate_shape* s, int mode) { return RmsMap{mode, s->T, s->H, s->W}; }
 
-// Heads per chunk workgroup: the largest divisor of Hs not above 8.
-int head_group(int Hs) {
-  for (int g = kHeadGroupMax; g > 1; --g)
+// Heads per chunk workgroup: the largest divisor of Hs not above `cap`.
+int head_group(int Hs, int cap = kHeadGroupMax) {
+  for (int g = cap; g > 1; --g)
     if (Hs % g == 0) return g;
   return 1;
 }
@@ -942,8 +1086,8 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
   const int nc = L / Q;
   const int Hs = s->ssd_heads;
   TS* states = reinterpret_cast<TS*>(ws + lay.states);
-  float* logdec = reinterpret_cast<float*>(ws + lay.logdec);
-  const int hg = head_group(Hs);
+  float* decay = reinterpret_cast<float*>(ws + lay.decay);
+  const int hg = head_group(Hs, kStateHeadGroup);
   const float* h0 = nullptr;
   if (s->n_review > 0) {
     if (int rc = launch_review<TS>(s, x, dt, A, B, ws, lay, st)) return rc;
@@ -951,11 +1095,14 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
   }
   if (int rc = mark(ev, 1, st)) return rc;
   ssd_chunk_state_kernel<TS, P, N, Q><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(x, dt, A, B, make_rms(s, mode), Hs, hg, nc,
-                                                                       states, logdec);
+                                                                       states, decay);
   if (hip_status()) return LINGEN_ERR_HIP;
   if (int rc = mark(ev, 2, st)) return rc;
+  // P*N/4 threads per head; P*N is a multiple of 256 in every compiled family
+  const int bs = (P * N / 4) < 256 ? (P * N / 4) : 256;
+  static_assert((P * N / 4) % 64 == 0 && ((P * N / 4) < 256 || (P * N / 4) % 256 == 0), "state pass blocking");
   const int64_t thr = int64_t(Hs) * P * N / 4;
-  ssd_state_pass_kernel<TS, 16><<<dim3(unsigned((thr + 255) / 256), 2), 256, 0, st>>>(states, logdec, h0, Hs, P * N,
+  ssd_state_pass_kernel<TS, 16><<<dim3(unsigned(thr / bs), 2), bs, 0, st>>>(states, decay, h0, Hs, P * N,
                                                                                       nc);
   if (hip_status()) return LINGEN_ERR_HIP;
   return mark(ev, 3, st);

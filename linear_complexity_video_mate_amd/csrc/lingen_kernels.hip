@@ -125,6 +125,59 @@ struct Stage16 {
   }
 };
 
+// Transposing stage of a [ROWS tokens][COLS] block of T into an LDS block
+// laid out [COLS][ld]: unit u covers the token pair (2i, 2i+1) and VEC
+// consecutive columns; both rows are loaded before any is consumed, and the
+// consumer writes each column's pair of values with one store (for bf16 one
+// 32-bit LDS word, so no two lanes touch the same word).
+template <typename T, int ROWS, int COLS, int NTHR>
+struct StageT {
+  static constexpr int VEC = Vec16<T>::n;
+  static constexpr int UNITS = (ROWS / 2) * (COLS / VEC);
+  static constexpr int IT = (UNITS + NTHR - 1) / NTHR;
+  static_assert(ROWS % 2 == 0 && COLS % VEC == 0, "token pairs and 16-byte columns");
+  uint4 a[IT], b[IT];
+  template <typename RowPtr>   // RowPtr(token) -> const T* to the start of that token's row
+  __device__ __forceinline__ void load(RowPtr row) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int u = int(threadIdx.x) + it * NTHR;
+      if (UNITS % NTHR == 0 || u < UNITS) {
+        const int i = u % (ROWS / 2), c0 = (u / (ROWS / 2)) * VEC;
+        a[it] = *reinterpret_cast<const uint4*>(row(2 * i) + c0);
+        b[it] = *reinterpret_cast<const uint4*>(row(2 * i + 1) + c0);
+      }
+    }
+  }
+  template <typename Use>      // Use(s0 = even token, c0 = first column, values of s0, values of s0 + 1)
+  __device__ __forceinline__ void use(Use f) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int u = int(threadIdx.x) + it * NTHR;
+      if (UNITS % NTHR == 0 || u < UNITS) {
+        Vec16<T> va, vb;
+        va.u = a[it];
+        vb.u = b[it];
+        f(2 * (u % (ROWS / 2)), (u / (ROWS / 2)) * VEC, va, vb);
+      }
+    }
+  }
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two consecutive elements of one LDS row (4-byte aligned for bf16, 8 for
+// fp32): from values already in the element type, or rounded from fp32.
+__device__ __forceinline__ void st_pair(__bf16* dst, __bf16 lo, __bf16 hi) {
+  *reinterpret_cast<bf16x2*>(dst) = bf16x2{lo, hi};
+}
+__device__ __forceinline__ void st_pair_f32(__bf16* dst, float lo, float hi) {
+  *reinterpret_cast<bf16x2*>(dst) = bf16x2{static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+}
+__device__ __forceinline__ void st_pair(float* dst, float lo, float hi) {
+  *reinterpret_cast<float2*>(dst) = make_float2(lo, hi);
+}
+__device__ __forceinline__ void st_pair_f32(float* dst, float lo, float hi) { st_pair(dst, lo, hi); }
+
 // Scan position -> canonical token index for the four Rotary Major Scan
 // orders (page "LinGen：基于Mamba机制的线性复杂度高清长视频生成框架", section
 // 关键算法创新 > Rotary Major Scan):
@@ -378,23 +431,16 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
 
   load_chunk_schedule<Q, NTHR>(cs, dt, A, rms, c, Hs, h0, hg);
   {
-    Stage16<Q * (N / VEC), NTHR> bs;
-    bs.load([&](int u) { return *reinterpret_cast<const uint4*>(B + int64_t(cs.tok[u % Q]) * N + (u / Q) * VEC); });
-    bs.use([&](int u, uint4 raw) {
-      const int s = u % Q, n0 = (u / Q) * VEC;
-      Vec16<TS> v;
-      v.u = raw;
+    StageT<TS, Q, N, NTHR> bs;
+    bs.load([&](int s) { return B + int64_t(cs.tok[s]) * N; });
+    bs.use([&](int s0, int n0, const Vec16<TS>& va, const Vec16<TS>& vb) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) sBt[(n0 + e) * QP + s] = v.e[e];
+      for (int e = 0; e < VEC; ++e) st_pair(&sBt[(n0 + e) * QP + s0], va.e[e], vb.e[e]);
     });
   }
   // x of the next head is loaded while the current head is computed.
-  Stage16<Q * (P / VEC), NTHR> xs;
-  auto load_x = [&](int h) {
-    xs.load([&](int u) {
-      return *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[u % Q]) * Hs + h) * P + (u / Q) * VEC);
-    });
-  };
+  StageT<TS, Q, P, NTHR> xs;
+  auto load_x = [&](int h) { xs.load([&](int s) { return x + (int64_t(cs.tok[s]) * Hs + h) * P; }); };
   load_x(h0);
 
   constexpr int NT = SC::NT, WP = SC::WP, WN = SC::WN, PT_PER = SC::PT_PER, NT_PER = SC::NT_PER;
@@ -413,16 +459,13 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
     }
     if (tid == 0) decay[int64_t(c) * Hs + h] = fast_exp2(cum_end);
     __syncthreads();
-    xs.use([&](int u, uint4 raw) {
-      const int s = u % Q, p0 = (u / Q) * VEC;
-      Vec16<TS> v;
-      v.u = raw;
-      const float wf = sW[0][s], wb = sW[1][s];
+    xs.use([&](int s0, int p0, const Vec16<TS>& va, const Vec16<TS>& vb) {
+      const float wf0 = sW[0][s0], wf1 = sW[0][s0 + 1], wb0 = sW[1][s0], wb1 = sW[1][s0 + 1];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float xv = to_f32(v.e[e]);
-        sXf[(p0 + e) * QP + s] = from_f32<MT>(xv * wf);
-        sXb[(p0 + e) * QP + s] = from_f32<MT>(xv * wb);
+        const float x0 = to_f32(va.e[e]), x1 = to_f32(vb.e[e]);
+        st_pair_f32(&sXf[(p0 + e) * QP + s0], x0 * wf0, x1 * wf1);
+        st_pair_f32(&sXb[(p0 + e) * QP + s0], x0 * wb0, x1 * wb1);
       }
     });
     __syncthreads();

@@ -164,6 +164,49 @@ def cpu_baseline(s, inp):
     }
 
 
+def _pmc_means(path):
+    """Mean counter value per kernel (short name) from a rocprofv3 counter CSV."""
+    import csv
+    import re
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        m = re.search(r"lingen(?:::|\d+)?([a-z_]+?)_kernel", r["Kernel_Name"])
+        if not m:
+            continue
+        name = re.sub(r"^\d+", "", m.group(1))
+        acc.setdefault(name, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def record_traffic(mix_fetch, mix_write, copy_fetch, copy_write, config=2):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the plain copy kernel,
+    whose true traffic is known (--copy-gib 1: 1 GiB read, 1 GiB written)."""
+    from mate_inputs import CONFIG_NOTES
+
+    true_kib = 2 ** 20
+    fcal = true_kib / _pmc_means(copy_fetch)["rms_gather"]
+    wcal = true_kib / _pmc_means(copy_write)["rms_gather"]
+    fetch, write = _pmc_means(mix_fetch), _pmc_means(mix_write)
+    kernels = {}
+    for name in sorted(set(fetch) & set(write)):
+        rd, wr = fetch[name] * fcal * 1024, write[name] * wcal * 1024
+        kernels[name] = {"read_bytes": round(rd), "write_bytes": round(wr), "bytes_per_launch": round(rd + wr)}
+    rec = {
+        "workload": CONFIG_NOTES[config],
+        "kernel_source_sha256": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest(),
+        "calibration": {"FETCH_SIZE_scale": round(fcal, 4), "WRITE_SIZE_scale": round(wcal, 4),
+                        "copy": "bench.py --copy-gib 1 (1 GiB read + 1 GiB written per launch)"},
+        "counters": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, each its own run",
+        "kernels": kernels,
+    }
+    out = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
 def copy_calibration(args, mate, torch):
     """Plain copy of rows of 4 KiB through lingen_rms_gather (mode 0 is the
     identity order): reads and writes exactly copy_gib GiB each per launch."""
@@ -197,10 +240,16 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("MIX_FETCH", "MIX_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write profiles/hbm_traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs of "
+                         "this benchmark and of the --copy-gib calibration run, then exit")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="instead of the mixer, time a plain device copy of this many GiB (the RMS gather "
                          "kernel in scan mode 0) and print its bandwidth: the HBM calibration point")
     args = ap.parse_args(argv)
+
+    if args.record_traffic:
+        return record_traffic(*args.record_traffic, config=args.config)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -624,10 +624,17 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   constexpr int VEC = Vec16<TS>::n;
   constexpr bool kBf16 = std::is_same<MT, __bf16>::value;
   static_assert((N % KI == 0 && Q % 32 == 0) || !kBf16, "bf16 tiles need Q multiple of 32");
-  __shared__ __attribute__((aligned(16))) MT sXt[P * QP];
-  __shared__ __attribute__((aligned(16))) MT sHf[P * NP];
-  __shared__ __attribute__((aligned(16))) MT sHb[P * NP];
+  // One LDS region, used first for the B rows of the chunk (to form G^T)
+  // and then, per head, for x^T and the two entering states.
+  constexpr int HEAD_ELEMS = P * QP + 2 * P * NP;
+  constexpr int U_ELEMS = HEAD_ELEMS > Q * NP ? HEAD_ELEMS : Q * NP;
+  __shared__ __attribute__((aligned(16))) MT sU[U_ELEMS];
+  MT* sXt = sU;
+  MT* sHf = sXt + P * QP;
+  MT* sHb = sHf + P * NP;
+  MT* sBr = sU;
   __shared__ ChunkSched<Q> cs;
+  __shared__ __attribute__((aligned(16))) float sV[Cfg::NW][Q];   // per-wave decay factors of s
 
   const int ngrp = Hs / hg;
   const int work = xcd_work_id(blockIdx.x, gridDim.x);
@@ -640,18 +647,21 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   // x and the two entering states of the next head are loaded while the
   // current head is computed.
   const int64_t per = int64_t(P) * N;
-  Stage16<Q * (P / VEC), NTHR> xs;
-  Stage16<P * (N / VEC), NTHR> hfs, hbs;
-  auto load_head = [&](int h) {
-    xs.load([&](int u) {
+  struct HeadBuf {
+    Stage16<Q * (P / VEC), NTHR> xs;
+    Stage16<P * (N / VEC), NTHR> hfs, hbs;
+  };
+  HeadBuf buf0;
+  auto load_head = [&](HeadBuf& hb_, int h) {
+    hb_.xs.load([&](int u) {
       return *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[u % Q]) * Hs + h) * P + (u / Q) * VEC);
     });
     const uint4* hf = reinterpret_cast<const uint4*>(states + (int64_t(c) * Hs + h) * per);
     const uint4* hb = reinterpret_cast<const uint4*>(states + ((int64_t(n_chunks) + c) * Hs + h) * per);
-    hfs.load([&](int u) { return hf[u]; });
-    hbs.load([&](int u) { return hb[u]; });
+    hb_.hfs.load([&](int u) { return hf[u]; });
+    hb_.hbs.load([&](int u) { return hb[u]; });
   };
-  load_head(h0);
+  load_head(buf0, h0);
 
   const int wt = wave % Cfg::WT, wpw = wave / Cfg::WT;
   const int t = wt * 16 + r16;            // this lane's output position
@@ -663,59 +673,98 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   // G^T is accumulated in fp32 and kept in the operand type (bf16 for bf16
   // data: the M^T values built from it are rounded to bf16 anyway).
   using GT = typename std::conditional<kBf16, bf16x4, f32x4>::type;
+  // The B rows of the chunk are staged once (coalesced, row-major) and every
+  // wave reads its MFMA fragments from LDS.
+  {
+    Stage16<Q * (N / VEC), NTHR> bs;
+    bs.load([&](int u) {
+      return *reinterpret_cast<const uint4*>(B + int64_t(cs.tok[u / (N / VEC)]) * N + (u % (N / VEC)) * VEC);
+    });
+    bs.use([&](int u, uint4 raw) {
+      *reinterpret_cast<uint4*>(&sBr[(u / (N / VEC)) * NP + (u % (N / VEC)) * VEC]) = raw;
+    });
+  }
+  __syncthreads();
   GT g[Cfg::QT];
 #pragma unroll
   for (int st = 0; st < Cfg::QT; ++st) {
-    const TS* brow = B + int64_t(cs.tok[st * 16 + r16]) * N;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < N / KI; ++ks) acc = mma(F::load(brow + ks * KI, lane), cfr[ks], acc);
+    for (int ks = 0; ks < N / KI; ++ks) acc = mma(F::load(&sBr[(st * 16 + r16) * NP + ks * KI], lane), cfr[ks], acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) g[st][r] = from_f32<MT>(acc[r]);
   }
+  __syncthreads();   // the region now takes the per-head staging
 
-#pragma unroll 1
-  for (int hh = 0; hh < hg; ++hh) {
+  auto do_head = [&](int hh, HeadBuf& buf) {
     const int h = h0 + hh;
     // Stage x_h (transposed) and the two entering states of this head.
-    xs.use([&](int u, uint4 raw) {
+    buf.xs.use([&](int u, uint4 raw) {
       const int s = u % Q, p0 = (u / Q) * VEC;
       Vec16<TS> v;
       v.u = raw;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) sXt[(p0 + e) * QP + s] = v.e[e];
     });
-    hfs.use([&](int u, uint4 raw) {
+    buf.hfs.use([&](int u, uint4 raw) {
       *reinterpret_cast<uint4*>(&sHf[(u / (N / VEC)) * NP + (u % (N / VEC)) * VEC]) = raw;
     });
-    hbs.use([&](int u, uint4 raw) {
+    buf.hbs.use([&](int u, uint4 raw) {
       *reinterpret_cast<uint4*>(&sHb[(u / (N / VEC)) * NP + (u % (N / VEC)) * VEC]) = raw;
     });
+    // Off the wave's own t-tile [ts, te] the decay splits at the tile edge
+    // into two factors that are both <= 1:
+    //   s < ts: e^{cum_t - cum_s}  = e^{cum_t - exc_ts} * e^{exc_ts - cum_s}
+    //   s > te: e^{exc_s - exc_t}  = e^{cum_te - exc_t} * e^{exc_s - cum_te}
+    // The s-side factor (times dt_s) goes to sV; the t-side one stays in a
+    // register, so each off-diagonal element costs two multiplies.
+    {
+      const float* cum = cs.cum[hh];
+      const float* exc = cs.exc[hh];
+      const int ts = wt * 16, te = ts + 15;
+      const float ref_lo = exc[ts], ref_hi = cum[te];
+      for (int s = lane; s < Q; s += 64) {
+        float vs = 0.f;
+        if (s < ts) vs = fast_exp2(ref_lo - cum[s]) * cs.dt[hh][s];
+        else if (s > te) vs = fast_exp2(exc[s] - ref_hi) * cs.dt[hh][s];
+        sV[wave][s] = vs;
+      }
+    }
     __syncthreads();
-    if (hh + 1 < hg) load_head(h + 1);
+    if (hh + 1 < hg) load_head(buf, h + 1);
 
     const float* cum = cs.cum[hh];
     const float* exc = cs.exc[hh];
     const float* dth = cs.dt[hh];
     const float cum_t = cum[t], exc_t = exc[t];
+    const float fac_lo = fast_exp2(cum_t - exc[wt * 16]);          // t-side factor, s before the tile
+    const float fac_hi = fast_exp2(cum[wt * 16 + 15] - exc_t);     // t-side factor, s after the tile
 
-    // M^T values of this lane for s-tile st (s = 16*st + 4*grp + r):
-    // s < t: forward decay e^{cum_t - cum_s}; s > t: backward decay
-    // e^{exc_s - exc_t}; s = t: both directions see the token, weight 2.
+    // M^T values of this lane for s-tile st (s = 16*st + 4*grp + r).  On the
+    // diagonal tile: s < t forward decay e^{cum_t - cum_s}, s > t backward
+    // decay e^{exc_s - exc_t}, s = t both directions see the token (weight 2).
     auto m_tile = [&](int st, float (&mv)[4]) {
       const int sb = st * 16 + grp * 4;
-      const float4 cum4 = *reinterpret_cast<const float4*>(&cum[sb]);
-      const float4 exc4 = *reinterpret_cast<const float4*>(&exc[sb]);
-      const float4 dt4 = *reinterpret_cast<const float4*>(&dth[sb]);
-      const float cv[4] = {cum4.x, cum4.y, cum4.z, cum4.w};
-      const float xv[4] = {exc4.x, exc4.y, exc4.z, exc4.w};
-      const float dv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
+      if (st == wt) {
+        const float4 cum4 = *reinterpret_cast<const float4*>(&cum[sb]);
+        const float4 exc4 = *reinterpret_cast<const float4*>(&exc[sb]);
+        const float4 dt4 = *reinterpret_cast<const float4*>(&dth[sb]);
+        const float cv[4] = {cum4.x, cum4.y, cum4.z, cum4.w};
+        const float xv[4] = {exc4.x, exc4.y, exc4.z, exc4.w};
+        const float dv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = sb + r;
-        const float arg = s < t ? cum_t - cv[r] : xv[r] - exc_t;
-        const float lam = s == t ? 2.f : fast_exp2(arg);
-        mv[r] = to_f32(g[st][r]) * lam * dv[r];
+        for (int r = 0; r < 4; ++r) {
+          const int s = sb + r;
+          const float arg = s < t ? cum_t - cv[r] : xv[r] - exc_t;
+          const float lam = s == t ? 2.f : fast_exp2(arg);
+          mv[r] = to_f32(g[st][r]) * lam * dv[r];
+        }
+      } else {
+        const float4 v4 = *reinterpret_cast<const float4*>(&sV[wave][sb]);
+        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+        const float fac = st < wt ? fac_lo : fac_hi;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mv[r] = to_f32(g[st][r]) * vv[r] * fac;
       }
     };
 
@@ -795,7 +844,9 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       }
     }
     __syncthreads();   // staging buffers free for the next head
-  }
+  };
+#pragma unroll 1
+  for (int hh = 0; hh < hg; ++hh) do_head(hh, buf0);
 }
 
 // ---------------------------------------------------------------------------

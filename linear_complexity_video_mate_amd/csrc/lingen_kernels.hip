@@ -210,7 +210,7 @@ __device__ __forceinline__ int xcd_work_id(int bid, int nblocks) {
 // Inclusive and exclusive prefix sums of a_s = dt_s * A * log2(e) over one
 // chunk of Q scan positions (Q <= 256), computed by the calling wave alone
 // (all 64 lanes call it; no block barrier inside).
-template <int Q>
+template <int Q, bool WITH_EXC = true>
 __device__ __forceinline__ void wave_chunk_prefix(const float* sdt, float Ah, float* scum, float* sexc) {
   constexpr int E = (Q + 63) / 64;
   const int lane = threadIdx.x & 63;
@@ -234,32 +234,33 @@ __device__ __forceinline__ void wave_chunk_prefix(const float* sdt, float Ah, fl
   for (int e = 0; e < E; ++e) {
     const int idx = lane * E + e;
     if (idx < Q) {
-      sexc[idx] = base;
+      if (WITH_EXC) sexc[idx] = base;
       base += v[e];
       scum[idx] = base;
     }
   }
 }
 
-// Heads handled by one chunk workgroup (the largest divisor of Hs up to 8;
-// up to 4 for the chunk-state kernel, whose LDS then fits twice per CU).
-constexpr int kHeadGroupMax = 8;
-constexpr int kStateHeadGroup = 4;
+// Heads handled by one chunk workgroup (the largest divisor of Hs up to 16
+// for the output kernel; up to 8 for the chunk-state kernel, whose LDS then
+// still fits twice per CU).
+constexpr int kHeadGroupMax = 16;
+constexpr int kStateHeadGroup = 8;
 
 // Per-chunk schedule shared by the heads of one workgroup: the canonical
 // token of every scan position, and per head the step sizes and their
 // inclusive / exclusive prefix sums of dt*A in log2 units.
-template <int Q, int HGM = kHeadGroupMax>
+template <int Q, int HGM = kHeadGroupMax, bool WITH_EXC = true>
 struct __attribute__((aligned(16))) ChunkSched {
   static_assert(Q % 4 == 0, "rows are read as float4");
   int tok[Q];
   float dt[HGM][Q];
   float cum[HGM][Q];
-  float exc[HGM][Q];
+  float exc[WITH_EXC ? HGM : 1][WITH_EXC ? Q : 4];   // exc = cum - a when not kept
 };
 
-template <int Q, int NTHR, int HGM>
-__device__ __forceinline__ void load_chunk_schedule(ChunkSched<Q, HGM>& cs, const float* __restrict__ dt,
+template <int Q, int NTHR, int HGM, bool WITH_EXC>
+__device__ __forceinline__ void load_chunk_schedule(ChunkSched<Q, HGM, WITH_EXC>& cs, const float* __restrict__ dt,
                                                     const float* __restrict__ A, RmsMap rms, int c, int Hs, int h0,
                                                     int hg) {
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -279,7 +280,7 @@ __device__ __forceinline__ void load_chunk_schedule(ChunkSched<Q, HGM>& cs, cons
     if (u < Q * hg) cs.dt[u % hg][u / hg] = v[it];
   }
   __syncthreads();
-  for (int j = wave; j < hg; j += nwave) wave_chunk_prefix<Q>(cs.dt[j], A[h0 + j], cs.cum[j], cs.exc[j]);
+  for (int j = wave; j < hg; j += nwave) wave_chunk_prefix<Q, WITH_EXC>(cs.dt[j], A[h0 + j], cs.cum[j], cs.exc[WITH_EXC ? j : 0]);
   __syncthreads();
 }
 
@@ -416,7 +417,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
   constexpr int UBYTES = XBYTES > OBYTES ? XBYTES : OBYTES;
   __shared__ __attribute__((aligned(16))) MT sBt[N * QP];
   __shared__ __attribute__((aligned(16))) char sU[UBYTES];   // x staging, then output staging
-  __shared__ ChunkSched<Q, kStateHeadGroup> cs;
+  __shared__ ChunkSched<Q, kStateHeadGroup, false> cs;
   __shared__ float sW[2][Q];
   MT* sXf = reinterpret_cast<MT*>(sU);
   MT* sXb = sXf + P * QP;
@@ -452,10 +453,12 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
   for (int hh = 0; hh < hg; ++hh) {
     const int h = h0 + hh;
     const float cum_end = cs.cum[hh][Q - 1];
+    const float a2 = A[h] * kLog2e;
     for (int i = tid; i < Q; i += NTHR) {
       const float d = cs.dt[hh][i];
-      sW[0][i] = fast_exp2(cum_end - cs.cum[hh][i]) * d;
-      sW[1][i] = fast_exp2(cs.exc[hh][i]) * d;
+      const float cum_i = cs.cum[hh][i];
+      sW[0][i] = fast_exp2(cum_end - cum_i) * d;
+      sW[1][i] = fast_exp2(cum_i - d * a2) * d;     // exc_i = cum_i - a_i
     }
     if (tid == 0) decay[int64_t(c) * Hs + h] = fast_exp2(cum_end);
     __syncthreads();

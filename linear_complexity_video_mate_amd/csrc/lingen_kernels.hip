@@ -93,6 +93,28 @@ template <> struct Frag<float> {
 template <typename MT> struct LdsPad { static constexpr int v = 8; };
 template <> struct LdsPad<float> { static constexpr int v = 4; };
 
+// LDS tile with COLS elements per row, read by MFMA fragment loads (16 rows
+// x one 16-byte chunk per lane group).  bf16 rows that are a whole number of
+// 128-byte lines are stored unpadded with the 16-byte chunks of row r
+// permuted as chunk ^ (r mod 16) (mod 8 for 128-byte rows): fragment loads,
+// row-contiguous stores and the 16-row column stores of MFMA results then
+// all touch distinct banks.  Other tiles are padded by LdsPad.
+template <typename MT, int COLS>
+struct Tile {
+  static constexpr bool kSwz = sizeof(MT) == 2 && COLS % 64 == 0;
+  static constexpr int LD = kSwz ? COLS : COLS + LdsPad<MT>::v;
+  static constexpr int kMask = (COLS / 8 >= 16 ? 16 : COLS / 8) - 1;
+  __device__ static __forceinline__ int at(int row, int col) {
+    if constexpr (kSwz) return row * COLS + ((((col >> 3) ^ (row & kMask)) << 3) | (col & 7));
+    else return row * LD + col;
+  }
+  // Operand fragment of row `row` for k = k0 + the lane group's k values.
+  __device__ static __forceinline__ typename Frag<MT>::type frag(const MT* base, int row, int k0, int lane) {
+    if constexpr (sizeof(MT) == 2) return *reinterpret_cast<const bf16x8*>(base + at(row, k0 + (lane >> 4) * 8));
+    else return base[at(row, k0 + (lane >> 4))];
+  }
+};
+
 // 16-byte global vector, viewed as elements.
 template <typename T> struct Vec16 {
   static constexpr int n = 16 / sizeof(T);
@@ -409,7 +431,9 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
   using MT = TS;
   using F = Frag<MT>;
   constexpr int KI = F::K;
-  constexpr int QP = Q + LdsPad<MT>::v;
+  using TQ = Tile<MT, Q>;     // rows of Q tokens: B^T and the weighted x^T
+  using TO = Tile<TS, N>;     // output staging, rows of N
+  constexpr int QP = TQ::LD;
   constexpr int VEC = Vec16<TS>::n;
   static_assert(Q % KI == 0 && P % 16 == 0 && N % 16 == 0 && P % VEC == 0 && N % VEC == 0, "tile shape");
   constexpr int XBYTES = 2 * P * QP * int(sizeof(MT));
@@ -436,7 +460,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
     bs.load([&](int s) { return B + int64_t(cs.tok[s]) * N; });
     bs.use([&](int s0, int n0, const Vec16<TS>& va, const Vec16<TS>& vb) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) st_pair(&sBt[(n0 + e) * QP + s0], va.e[e], vb.e[e]);
+      for (int e = 0; e < VEC; ++e) st_pair(&sBt[TQ::at(n0 + e, s0)], va.e[e], vb.e[e]);
     });
   }
   // x of the next head is loaded while the current head is computed.
@@ -448,6 +472,8 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
   const int wp = wave % WP, wn = wave / WP;
   const int r16 = lane & 15, g4 = (lane >> 4) * 4;
   const int64_t per = int64_t(P) * N;
+  // Output staging is unpadded [P][N] per direction (chunk-permuted for bf16).
+  auto out_at = [](int row, int col) { return TO::kSwz ? TO::at(row, col) : row * N + col; };
 
 #pragma unroll 1
   for (int hh = 0; hh < hg; ++hh) {
@@ -467,8 +493,8 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float x0 = to_f32(va.e[e]), x1 = to_f32(vb.e[e]);
-        st_pair_f32(&sXf[(p0 + e) * QP + s0], x0 * wf0, x1 * wf1);
-        st_pair_f32(&sXb[(p0 + e) * QP + s0], x0 * wb0, x1 * wb1);
+        st_pair_f32(&sXf[TQ::at(p0 + e, s0)], x0 * wf0, x1 * wf1);
+        st_pair_f32(&sXb[TQ::at(p0 + e, s0)], x0 * wb0, x1 * wb1);
       }
     });
     __syncthreads();
@@ -487,14 +513,14 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
 #pragma unroll
       for (int i = 0; i < PT_PER; ++i) {
         const int pt = wp + i * WP;
-        af[i] = F::load(&sXf[(pt * 16 + r16) * QP + ks * KI], lane);
-        ab[i] = F::load(&sXb[(pt * 16 + r16) * QP + ks * KI], lane);
+        af[i] = TQ::frag(sXf, pt * 16 + r16, ks * KI, lane);
+        ab[i] = TQ::frag(sXb, pt * 16 + r16, ks * KI, lane);
       }
 #pragma unroll
       for (int j = 0; j < NT_PER; ++j) {
         const int nt = wn + j * WN;
         if (nt < NT) {
-          const typename F::type bf = F::load(&sBt[(nt * 16 + r16) * QP + ks * KI], lane);
+          const typename F::type bf = TQ::frag(sBt, nt * 16 + r16, ks * KI, lane);
 #pragma unroll
           for (int i = 0; i < PT_PER; ++i) {
             accf[i][j] = mma(af[i], bf, accf[i][j]);
@@ -513,8 +539,8 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
           const int pbase = (wp + i * WP) * 16 + g4, n = nt * 16 + r16;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            sOut[(pbase + r) * N + n] = from_f32<TS>(accf[i][j][r]);
-            sOut[per + (pbase + r) * N + n] = from_f32<TS>(accb[i][j][r]);
+            sOut[out_at(pbase + r, n)] = from_f32<TS>(accf[i][j][r]);
+            sOut[per + out_at(pbase + r, n)] = from_f32<TS>(accb[i][j][r]);
           }
         }
       }
@@ -523,7 +549,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
     for (int u = tid; u < 2 * VPD; u += NTHR) {
       const int dir = u / VPD, off = u % VPD;
       uint4* dst = reinterpret_cast<uint4*>(states + ((int64_t(dir) * n_chunks + c) * Hs + h) * per);
-      dst[off] = reinterpret_cast<const uint4*>(sOut)[u];
+      dst[off] = reinterpret_cast<const uint4*>(sOut)[dir * VPD + out_at(off / (N / VEC), (off % (N / VEC)) * VEC) / VEC];
     }
   }
 }
@@ -622,7 +648,8 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   using Cfg = OutCfg<TS, P, N, Q>;
   constexpr int NTHR = Cfg::NW * 64;
   constexpr int KI = F::K;
-  constexpr int NP = N + LdsPad<MT>::v;
+  using TN = Tile<MT, N>;     // rows of N: B rows and the entering states
+  constexpr int NP = TN::LD;
   constexpr int QP = Q + LdsPad<MT>::v;
   constexpr int VEC = Vec16<TS>::n;
   constexpr bool kBf16 = std::is_same<MT, __bf16>::value;
@@ -684,7 +711,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       return *reinterpret_cast<const uint4*>(B + int64_t(cs.tok[u / (N / VEC)]) * N + (u % (N / VEC)) * VEC);
     });
     bs.use([&](int u, uint4 raw) {
-      *reinterpret_cast<uint4*>(&sBr[(u / (N / VEC)) * NP + (u % (N / VEC)) * VEC]) = raw;
+      *reinterpret_cast<uint4*>(&sBr[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
     });
   }
   __syncthreads();
@@ -693,7 +720,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   for (int st = 0; st < Cfg::QT; ++st) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < N / KI; ++ks) acc = mma(F::load(&sBr[(st * 16 + r16) * NP + ks * KI], lane), cfr[ks], acc);
+    for (int ks = 0; ks < N / KI; ++ks) acc = mma(TN::frag(sBr, st * 16 + r16, ks * KI, lane), cfr[ks], acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) g[st][r] = from_f32<MT>(acc[r]);
   }
@@ -710,10 +737,10 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       for (int e = 0; e < VEC; ++e) sXt[(p0 + e) * QP + s] = v.e[e];
     });
     buf.hfs.use([&](int u, uint4 raw) {
-      *reinterpret_cast<uint4*>(&sHf[(u / (N / VEC)) * NP + (u % (N / VEC)) * VEC]) = raw;
+      *reinterpret_cast<uint4*>(&sHf[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
     });
     buf.hbs.use([&](int u, uint4 raw) {
-      *reinterpret_cast<uint4*>(&sHb[(u / (N / VEC)) * NP + (u % (N / VEC)) * VEC]) = raw;
+      *reinterpret_cast<uint4*>(&sHb[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
     });
     // Off the wave's own t-tile [ts, te] the decay splits at the tile edge
     // into two factors that are both <= 1:
@@ -827,8 +854,8 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       f32x4 zf = f32x4{0.f, 0.f, 0.f, 0.f}, zb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < N / KI; ++ks) {
-        zf = mma(F::load(&sHf[prow * NP + ks * KI], lane), cfr[ks], zf);
-        zb = mma(F::load(&sHb[prow * NP + ks * KI], lane), cfr[ks], zb);
+        zf = mma(TN::frag(sHf, prow, ks * KI, lane), cfr[ks], zf);
+        zb = mma(TN::frag(sHb, prow, ks * KI, lane), cfr[ks], zb);
       }
       // Lane holds Y^T[p][t] for p = pt*16 + 4*grp + r.
       const int p0 = pt * 16 + grp * 4;
@@ -896,7 +923,8 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   constexpr int NTHR = Cfg::NWAVE * 64;
   constexpr int QTP = Cfg::QT_PER;
   constexpr int KI = F::K;
-  constexpr int DP = DH + LdsPad<MT>::v;
+  using TK = Tile<MT, DH>;    // key rows
+  constexpr int DP = TK::LD;
   constexpr int WP = NWIN + LdsPad<MT>::v;
   constexpr int VEC = Vec16<TS>::n;
   constexpr bool kBf16 = std::is_same<MT, __bf16>::value;
@@ -937,7 +965,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
                                              (u / NWIN) * VEC);
     });
     ks.use([&](int u, uint4 raw) {
-      *reinterpret_cast<uint4*>(&sK[(u / (DH / VEC)) * DP + (u % (DH / VEC)) * VEC]) = raw;
+      *reinterpret_cast<uint4*>(&sK[TK::at(u / (DH / VEC), (u % (DH / VEC)) * VEC)]) = raw;
     });
     vs.use([&](int u, uint4 raw) {
       const int j = u % NWIN, e0 = (u / NWIN) * VEC;
@@ -978,7 +1006,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) kf[jt][ks] = F::load(&sK[(jb + jt * 16 + r16) * DP + ks * KI], lane);
+      for (int ks = 0; ks < NKS; ++ks) kf[jt][ks] = TK::frag(sK, jb + jt * 16 + r16, ks * KI, lane);
 #pragma unroll
     for (int qi = 0; qi < QTP; ++qi) {
       f32x4 s[2];
@@ -1036,7 +1064,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) kf[jt][ks] = F::load(&sK[(jb + jt * 16 + r16) * DP + ks * KI], lane);
+      for (int ks = 0; ks < NKS; ++ks) kf[jt][ks] = TK::frag(sK, jb + jt * 16 + r16, ks * KI, lane);
     bf16x8 vf[kBf16 ? ET : 1];
     if constexpr (kBf16) {
 #pragma unroll

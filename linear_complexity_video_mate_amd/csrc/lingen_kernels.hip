@@ -52,6 +52,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 // denormal, which is far below every tolerance the callers work to.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier for LDS traffic only.  The waves of a workgroup exchange
+// data through LDS alone (never through global memory), so the barrier waits
+// for this wave's LDS accesses but leaves its global loads and stores in
+// flight: prefetches issued before a barrier keep streaming across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------
 // Small device helpers
 // ---------------------------------------------------------------------------
@@ -288,7 +298,7 @@ __device__ __forceinline__ void load_chunk_schedule(ChunkSched<Q, HGM, WITH_EXC>
   const int tid = threadIdx.x, wave = tid >> 6;
   constexpr int nwave = NTHR / 64;
   for (int i = tid; i < Q; i += NTHR) cs.tok[i] = rms.canon(c * Q + i);
-  __syncthreads();
+  lds_barrier();
   constexpr int IT = (Q * HGM + NTHR - 1) / NTHR;
   float v[IT];
 #pragma unroll
@@ -301,9 +311,9 @@ __device__ __forceinline__ void load_chunk_schedule(ChunkSched<Q, HGM, WITH_EXC>
     const int u = tid + it * NTHR;
     if (u < Q * hg) cs.dt[u % hg][u / hg] = v[it];
   }
-  __syncthreads();
+  lds_barrier();
   for (int j = wave; j < hg; j += nwave) wave_chunk_prefix<Q, WITH_EXC>(cs.dt[j], A[h0 + j], cs.cum[j], cs.exc[WITH_EXC ? j : 0]);
-  __syncthreads();
+  lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -360,7 +370,7 @@ __global__ __launch_bounds__(256) void review_pool_kernel(const TS* __restrict__
     acc += (y < Hs) ? to_f32(x[(tok * Hs + y) * P + col]) : to_f32(B[tok * N + col]);
   }
   red[tid] = acc;
-  __syncthreads();
+  lds_barrier();
   if (tid < width) {
     float s = 0.f;
     for (int q = 0; q < ngrp; ++q) s += red[q * width + tid];
@@ -368,14 +378,14 @@ __global__ __launch_bounds__(256) void review_pool_kernel(const TS* __restrict__
     else rb[int64_t(r) * N + tid] = s * inv;
   }
   if (y < Hs) {
-    __syncthreads();
+    lds_barrier();
     float d = 0.f;
     for (int tl = tid; tl < cnt; tl += 256) d += dt[int64_t(token(tl)) * Hs + y];
     red[tid] = d;
-    __syncthreads();
+    lds_barrier();
     for (int off = 128; off > 0; off >>= 1) {
       if (tid < off) red[tid] += red[tid + off];
-      __syncthreads();
+      lds_barrier();
     }
     if (tid == 0) rdt[int64_t(r) * Hs + y] = red[0] * inv;
   }
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(256) void review_state_kernel(const float* __restri
       suf += d * A[h];
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int e = threadIdx.x; e < P * N; e += 256) {
     const int p = e / N, n = e % N;
     float acc = 0.f;
@@ -487,7 +497,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
       sW[1][i] = fast_exp2(cum_i - d * a2) * d;     // exc_i = cum_i - a_i
     }
     if (tid == 0) decay[int64_t(c) * Hs + h] = fast_exp2(cum_end);
-    __syncthreads();
+    lds_barrier();
     xs.use([&](int s0, int p0, const Vec16<TS>& va, const Vec16<TS>& vb) {
       const float wf0 = sW[0][s0], wf1 = sW[0][s0 + 1], wb0 = sW[1][s0], wb1 = sW[1][s0 + 1];
 #pragma unroll
@@ -497,7 +507,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
         st_pair_f32(&sXb[TQ::at(p0 + e, s0)], x0 * wb0, x1 * wb1);
       }
     });
-    __syncthreads();
+    lds_barrier();
     if (hh + 1 < hg) load_x(h + 1);
     f32x4 accf[PT_PER][NT_PER], accb[PT_PER][NT_PER];
 #pragma unroll
@@ -529,7 +539,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
         }
       }
     }
-    __syncthreads();   // x staging (aliased by the output staging) fully read
+    lds_barrier();   // x staging (aliased by the output staging) fully read
 #pragma unroll
     for (int i = 0; i < PT_PER; ++i)
 #pragma unroll
@@ -544,7 +554,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
           }
         }
       }
-    __syncthreads();
+    lds_barrier();
     constexpr int VPD = P * N / VEC;   // 16-byte vectors per direction
     for (int u = tid; u < 2 * VPD; u += NTHR) {
       const int dir = u / VPD, off = u % VPD;
@@ -714,7 +724,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       *reinterpret_cast<uint4*>(&sBr[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
     });
   }
-  __syncthreads();
+  lds_barrier();
   GT g[Cfg::QT];
 #pragma unroll
   for (int st = 0; st < Cfg::QT; ++st) {
@@ -724,7 +734,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 #pragma unroll
     for (int r = 0; r < 4; ++r) g[st][r] = from_f32<MT>(acc[r]);
   }
-  __syncthreads();   // the region now takes the per-head staging
+  lds_barrier();   // the region now takes the per-head staging
 
   auto do_head = [&](int hh, HeadBuf& buf) {
     const int h = h0 + hh;
@@ -760,7 +770,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
         sV[wave][s] = vs;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (hh + 1 < hg) load_head(buf, h + 1);
 
     const float* cum = cs.cum[hh];
@@ -873,7 +883,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
         *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
       }
     }
-    __syncthreads();   // staging buffers free for the next head
+    lds_barrier();   // staging buffers free for the next head
   };
 #pragma unroll 1
   for (int hh = 0; hh < hg; ++hh) do_head(hh, buf0);
@@ -941,7 +951,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   const int64_t rowstride = int64_t(Ha) * DH;
 
   if (tid == 0) sWrapped = 0;
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < NWIN; i += NTHR) {
     const int a = i / (wg.wh * wg.ww), b = (i / wg.ww) % wg.wh, cc = i % wg.ww;
     int t = wi * wg.wt + a + wg.st, hh = wj * wg.wh + b + wg.sh, w = wk * wg.ww + cc + wg.sw;
@@ -953,7 +963,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
     sCls[i] = cls;
     if (cls) sWrapped = 1;
   }
-  __syncthreads();
+  lds_barrier();
   {
     Stage16<NWIN * (DH / VEC), NTHR> ks, vs;
     ks.load([&](int u) {
@@ -990,7 +1000,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
     for (int ks = 0; ks < NKS; ++ks) qf[qi][ks] = F::load(qrow + ks * KI, lane);
     qcls[qi] = sCls[iq];
   }
-  __syncthreads();
+  lds_barrier();
   const bool wrapped = sWrapped != 0;
   // scores stay in raw units; p = 2^((s - max) * sc) with sc = log2(e)/sqrt(d)
   const float sc = kLog2e * rsqrtf(float(DH));

@@ -923,10 +923,10 @@ struct AttnCfg {
   static constexpr int KB = 32;                        // keys per block
 };
 
-template <typename TS, int DH, int NWIN>
+template <typename TS, int DH, int NWIN, bool ACCUMULATE>
 __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_window_kernel(
     const TS* __restrict__ q, const TS* __restrict__ k, const TS* __restrict__ v, WinGeom wg, int Ha,
-    int accumulate, TS* __restrict__ y) {
+    TS* __restrict__ y) {
   using MT = TS;
   using F = Frag<MT>;
   using Cfg = AttnCfg<TS, DH, NWIN>;
@@ -1050,7 +1050,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   // its latency is hidden behind pass 2.
   using YV = typename std::conditional<kBf16, bf16x4, f32x4>::type;
   YV yprev[QTP][ET];
-  if (accumulate) {
+  if constexpr (ACCUMULATE) {
 #pragma unroll
     for (int qi = 0; qi < QTP; ++qi) {
       const TS* yrow = y + int64_t(sTok[(wave + qi * Cfg::NWAVE) * 16 + r16]) * rowstride + int64_t(h) * DH;
@@ -1141,7 +1141,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
     float lt = l[qi];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    const float inv = 1.f / lt;
+    const float inv = __builtin_amdgcn_rcpf(lt);
     const int iq = (wave + qi * Cfg::NWAVE) * 16 + r16;
     TS* yrow = y + int64_t(sTok[iq]) * rowstride + int64_t(h) * DH;
 #pragma unroll
@@ -1153,7 +1153,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
       YV res;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        res[r] = from_f32<TS>(accumulate ? to_f32(yprev[qi][et][r]) + ov[r] : ov[r]);
+        res[r] = from_f32<TS>(ACCUMULATE ? to_f32(yprev[qi][et][r]) + ov[r] : ov[r]);
       *reinterpret_cast<YV*>(yrow + e0) = res;
     }
   }
@@ -1292,11 +1292,14 @@ int launch_te(const lingen_mate_shape* s, int shifted, const void* q, const void
   using Cfg = AttnCfg<TS, DH, NWIN>;
   for (int b = 0; b < s->batch; ++b) {
     const int64_t off = int64_t(b) * per;
-    tesa_window_kernel<TS, DH, NWIN><<<nwin * s->attn_heads, Cfg::NWAVE * 64, 0, st>>>(
-        reinterpret_cast<const TS*>(static_cast<const char*>(q) + off),
-        reinterpret_cast<const TS*>(static_cast<const char*>(k) + off),
-        reinterpret_cast<const TS*>(static_cast<const char*>(v) + off), g, s->attn_heads, accumulate,
-        reinterpret_cast<TS*>(static_cast<char*>(y) + off));
+    const TS* qb = reinterpret_cast<const TS*>(static_cast<const char*>(q) + off);
+    const TS* kb = reinterpret_cast<const TS*>(static_cast<const char*>(k) + off);
+    const TS* vb = reinterpret_cast<const TS*>(static_cast<const char*>(v) + off);
+    TS* yb = reinterpret_cast<TS*>(static_cast<char*>(y) + off);
+    if (accumulate)
+      tesa_window_kernel<TS, DH, NWIN, true><<<nwin * s->attn_heads, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, yb);
+    else
+      tesa_window_kernel<TS, DH, NWIN, false><<<nwin * s->attn_heads, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, yb);
     if (hip_status()) return LINGEN_ERR_HIP;
   }
   return LINGEN_OK;

@@ -890,22 +890,28 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 }
 
 // ---------------------------------------------------------------------------
-// TESA: one workgroup per (window, head).  Windows are enumerated on the
-// rolled grid (offset by the shift, wrapping), so every window has n_w
-// tokens; a token that wrapped along an axis belongs to a different window
-// of the unrolled partition than one that did not, which the kernel enforces
-// by masking scores between tokens of different wrap classes.  This is the
-// border-cut partition of page "LinGen：基于Mamba机制的线性复杂度高清长视频
-// 生成框架", section 关键算法创新 > TESA (plain and shifted windows alternate),
-// in Swin's roll-and-mask form.  Windows with no wrapped token skip the mask.
+// TESA.  Windows are enumerated on the rolled grid (offset by the shift,
+// wrapping), so every window has n_w tokens; a token that wrapped along an
+// axis belongs to a different window of the unrolled partition than one
+// that did not, which the kernel enforces by masking scores between tokens
+// of different wrap classes.  This is the border-cut partition of page
+// "LinGen：基于Mamba机制的线性复杂度高清长视频生成框架", section 关键算法创新 >
+// TESA (plain and shifted windows alternate), in Swin's roll-and-mask form.
+// Windows with no wrapped token skip the mask.
+//
+// Work item = (window, head).  The grid is persistent (one workgroup per
+// CU); a workgroup walks its items in sequence with the K and V tiles of the
+// next item streaming into the second of two LDS buffers (direct
+// global-to-LDS loads, no registers) while the current one is computed, and
+// the next item's Q fragments and MA output held in registers.  Per item:
 //   S^T[j][i] = K_j . Q_i            (MFMA, A = K from LDS, B = Q in registers)
 //   pass 1: row maxima of S over the window (each lane owns one query per tile)
 //   pass 2: P^T = 2^((S^T - max) log2(e)/sqrt(d)), row sums, and
-//           O^T[e][i] += V^T[e][j] P^T[j][i]  (MFMA, A = V^T from LDS, B = P^T in registers)
+//           O^T[e][i] += V^T[e][j] P^T[j][i]  (MFMA, B = P^T in registers;
+//           A = V^T read from the row-major V tile with LDS transpose loads)
 // Recomputing S in pass 2 costs MFMA time, which this kernel has to spare,
 // and removes the rescaling of the running output that an online softmax
-// needs.  The key loops are outermost so every K / V^T fragment read from
-// LDS serves all query tiles of the wave.
+// needs.
 // ---------------------------------------------------------------------------
 
 struct WinGeom {
@@ -918,244 +924,358 @@ struct WinGeom {
 template <typename TS, int DH, int NWIN>
 struct AttnCfg {
   static constexpr int QTILES = NWIN / 16;
-  static constexpr int NWAVE = QTILES >= 8 ? 8 : QTILES;
+  static constexpr int NWAVE = QTILES >= 16 ? 16 : QTILES;
   static constexpr int QT_PER = QTILES / NWAVE;       // query tiles per wave
   static constexpr int KB = 32;                        // keys per block
+  static constexpr int VEC = 16 / int(sizeof(TS));     // elements per 16-byte chunk
+  static constexpr int CPR = DH / VEC;                 // chunks per K / V row
+  static constexpr int UNITS = NWIN * CPR;             // 16-byte chunks per tile
+  static constexpr int DMA_PER_WAVE = UNITS / (NWAVE * 64);
+  static_assert(CPR == 8, "K / V rows of 128 bytes");
+  static_assert(UNITS % (NWAVE * 64) == 0, "whole wave-wide LDS loads per tile");
 };
+
+// K and V tiles in LDS: row-major [NWIN][DH] with the 16-byte chunks of row r
+// permuted as chunk ^ (r mod 8).  One direct global-to-LDS load instruction
+// fills 64 consecutive chunks (8 rows), each lane fetching the source chunk
+// that lands in its slot.
+template <typename TS, int DH>
+struct KvTile {
+  static constexpr int VEC = 16 / int(sizeof(TS));
+  __device__ static __forceinline__ int at(int row, int col) {
+    return row * DH + ((((col / VEC) ^ (row & 7)) * VEC) | (col % VEC));
+  }
+};
+
+// 16-byte direct global-to-LDS load: lane l's chunk lands at lds_wave_base +
+// 16*l (the base must be the same for all lanes of the wave).  Kept out of
+// the kernel templates, whose host-side stubs are not emitted otherwise.
+__device__ __forceinline__ void lds_load16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// Transposing LDS load (16-bit elements): within each group of 16 lanes,
+// lane i receives element (i mod 4) of the 8-byte chunk read by lane
+// 4r + i/4, in slot r.
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
 
 template <typename TS, int DH, int NWIN, bool ACCUMULATE>
 __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_window_kernel(
     const TS* __restrict__ q, const TS* __restrict__ k, const TS* __restrict__ v, WinGeom wg, int Ha,
-    TS* __restrict__ y) {
+    int n_items, TS* __restrict__ y) {
   using MT = TS;
   using F = Frag<MT>;
   using Cfg = AttnCfg<TS, DH, NWIN>;
+  using KT = KvTile<TS, DH>;
   constexpr int NTHR = Cfg::NWAVE * 64;
   constexpr int QTP = Cfg::QT_PER;
   constexpr int KI = F::K;
-  using TK = Tile<MT, DH>;    // key rows
-  constexpr int DP = TK::LD;
-  constexpr int WP = NWIN + LdsPad<MT>::v;
-  constexpr int VEC = Vec16<TS>::n;
+  constexpr int VEC = Cfg::VEC;
   constexpr bool kBf16 = std::is_same<MT, __bf16>::value;
-  static_assert(NWIN % Cfg::KB == 0 && DH % 16 == 0 && DH % KI == 0, "attention tile shape");
-  __shared__ __attribute__((aligned(16))) MT sK[NWIN * DP];
-  __shared__ __attribute__((aligned(16))) MT sVt[DH * WP];
-  __shared__ int sTok[NWIN];
-  __shared__ __attribute__((aligned(16))) int sCls[NWIN];
-  __shared__ int sWrapped;
-
-  const int win = blockIdx.x / Ha, h = blockIdx.x % Ha;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wi = win / (wg.nwh * wg.nww), wj = (win / wg.nww) % wg.nwh, wk = win % wg.nww;
-  const int64_t rowstride = int64_t(Ha) * DH;
-
-  if (tid == 0) sWrapped = 0;
-  lds_barrier();
-  for (int i = tid; i < NWIN; i += NTHR) {
-    const int a = i / (wg.wh * wg.ww), b = (i / wg.ww) % wg.wh, cc = i % wg.ww;
-    int t = wi * wg.wt + a + wg.st, hh = wj * wg.wh + b + wg.sh, w = wk * wg.ww + cc + wg.sw;
-    int cls = 0;
-    if (t >= wg.T) { t -= wg.T; cls |= 4; }
-    if (hh >= wg.H) { hh -= wg.H; cls |= 2; }
-    if (w >= wg.W) { w -= wg.W; cls |= 1; }
-    sTok[i] = (t * wg.H + hh) * wg.W + w;
-    sCls[i] = cls;
-    if (cls) sWrapped = 1;
-  }
-  lds_barrier();
-  {
-    Stage16<NWIN * (DH / VEC), NTHR> ks, vs;
-    ks.load([&](int u) {
-      return *reinterpret_cast<const uint4*>(k + int64_t(sTok[u / (DH / VEC)]) * rowstride + int64_t(h) * DH +
-                                             (u % (DH / VEC)) * VEC);
-    });
-    vs.load([&](int u) {
-      return *reinterpret_cast<const uint4*>(v + int64_t(sTok[u % NWIN]) * rowstride + int64_t(h) * DH +
-                                             (u / NWIN) * VEC);
-    });
-    ks.use([&](int u, uint4 raw) {
-      *reinterpret_cast<uint4*>(&sK[TK::at(u / (DH / VEC), (u % (DH / VEC)) * VEC)]) = raw;
-    });
-    vs.use([&](int u, uint4 raw) {
-      const int j = u % NWIN, e0 = (u / NWIN) * VEC;
-      Vec16<TS> vv;
-      vv.u = raw;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) sVt[(e0 + e) * WP + j] = vv.e[e];
-    });
-  }
-
-  const int r16 = lane & 15, grp = lane >> 4;
   constexpr int ET = DH / 16;
   constexpr int NKS = DH / KI;
-  // Q fragments of this lane's queries, straight from global memory.
-  typename F::type qf[QTP][NKS];
-  int qcls[QTP];
-#pragma unroll
-  for (int qi = 0; qi < QTP; ++qi) {
-    const int iq = (wave + qi * Cfg::NWAVE) * 16 + r16;
-    const TS* qrow = q + int64_t(sTok[iq]) * rowstride + int64_t(h) * DH;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[qi][ks] = F::load(qrow + ks * KI, lane);
-    qcls[qi] = sCls[iq];
-  }
-  lds_barrier();
-  const bool wrapped = sWrapped != 0;
+  static_assert(NWIN % Cfg::KB == 0 && DH % 16 == 0 && DH % KI == 0, "attention tile shape");
+  // Two buffers per tile, as separate arrays so that reads of the current
+  // buffer need not wait for the loads streaming into the other one.
+  __shared__ __attribute__((aligned(16))) MT sK0[NWIN * DH];
+  __shared__ __attribute__((aligned(16))) MT sK1[NWIN * DH];
+  __shared__ __attribute__((aligned(16))) MT sV0[NWIN * DH];
+  __shared__ __attribute__((aligned(16))) MT sV1[NWIN * DH];
+  __shared__ int sTok[2][NWIN];   // token index of each window slot (item parity)
+  __shared__ int sCls[3][NWIN];   // wrap class of each window slot (item mod 3)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int64_t rowstride = int64_t(Ha) * DH;
+  const int nwin_hw = wg.nwh * wg.nww;
   // scores stay in raw units; p = 2^((s - max) * sc) with sc = log2(e)/sqrt(d)
   const float sc = kLog2e * rsqrtf(float(DH));
 
-  // Pass 1: the row maximum of every query over the keys of its own window
-  // (the query itself is always one of them, so the maximum is finite).
-  float msc[QTP];
-#pragma unroll
-  for (int qi = 0; qi < QTP; ++qi) msc[qi] = -INFINITY;
-#pragma unroll 1
-  for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
-    typename F::type kf[2][NKS];
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) kf[jt][ks] = TK::frag(sK, jb + jt * 16 + r16, ks * KI, lane);
-#pragma unroll
-    for (int qi = 0; qi < QTP; ++qi) {
-      f32x4 s[2];
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(kf[jt][ks], qf[qi][ks], s[jt]);
-      }
-      if (wrapped) {
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          const int4 kc = *reinterpret_cast<const int4*>(&sCls[jb + jt * 16 + grp * 4]);
-          const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) s[jt][r] = kcv[r] != qcls[qi] ? -INFINITY : s[jt][r];
-        }
-      }
-      msc[qi] = fmaxf(msc[qi], fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))));
+  // Position of an item: head and window coordinates.  Items advance by the
+  // grid size, which is added in mixed radix (no divisions per item).
+  struct ItemPos { int item, h, wi, wj, wk; };
+  auto decompose = [&](int it) {
+    const int win = it / Ha;
+    return ItemPos{it, it % Ha, win / nwin_hw, (win / wg.nww) % wg.nwh, win % wg.nww};
+  };
+  const ItemPos step_pos = decompose(int(gridDim.x));   // item offset of one step, as (h, wi, wj, wk)
+  auto advance = [&](ItemPos p) {
+    p.item += int(gridDim.x);
+    p.h += step_pos.h;
+    int c = p.h >= Ha;
+    if (c) p.h -= Ha;
+    p.wk += step_pos.wk + c;
+    c = p.wk >= wg.nww;
+    if (c) p.wk -= wg.nww;
+    p.wj += step_pos.wj + c;
+    c = p.wj >= wg.nwh;
+    if (c) p.wj -= wg.nwh;
+    p.wi += step_pos.wi + c;
+    return p;
+  };
+  // Offsets of this thread's window slot (tid < NWIN) inside the window.
+  static_assert(NWIN <= NTHR, "one window slot per thread");
+  const int slot_a = tid / (wg.wh * wg.ww), slot_b = (tid / wg.ww) % wg.wh, slot_c = tid % wg.ww;
+  // Token index and wrap class of every slot of an item's window.
+  auto item_tokens = [&](const ItemPos& p, int* tok, int* cls) {
+    if (tid < NWIN) {
+      int t = p.wi * wg.wt + slot_a + wg.st, hh = p.wj * wg.wh + slot_b + wg.sh, w = p.wk * wg.ww + slot_c + wg.sw;
+      int cl = 0;
+      if (t >= wg.T) { t -= wg.T; cl |= 4; }
+      if (hh >= wg.H) { hh -= wg.H; cl |= 2; }
+      if (w >= wg.W) { w -= wg.W; cl |= 1; }
+      tok[tid] = (t * wg.H + hh) * wg.W + w;
+      cls[tid] = cl;
     }
-  }
+  };
+  // The window holds wrapped tokens iff it is the last one along a shifted axis.
+  auto item_wrapped = [&](const ItemPos& p) {
+    return (wg.st > 0 && p.wi == wg.nwt - 1) || (wg.sh > 0 && p.wj == wg.nwh - 1) || (wg.sw > 0 && p.wk == wg.nww - 1);
+  };
+  // Direct global-to-LDS loads of an item's K and V tiles.
+  auto issue_kv = [&](MT* dK, MT* dV, const int* tok, int h) {
 #pragma unroll
-  for (int qi = 0; qi < QTP; ++qi) {
-    float mq = fmaxf(msc[qi], __shfl_xor(msc[qi], 16, 64));
-    mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
-    msc[qi] = mq * sc;
-  }
-
-  // The MA output this kernel adds to (fused branch sum) is fetched now so
-  // its latency is hidden behind pass 2.
+    for (int d = 0; d < Cfg::DMA_PER_WAVE; ++d) {
+      const int base = (wave * Cfg::DMA_PER_WAVE + d) * 64;    // first chunk of this instruction
+      const int u = base + lane, row = u / Cfg::CPR, ch = (u % Cfg::CPR) ^ (row & 7);
+      const int64_t goff = int64_t(tok[row]) * rowstride + int64_t(h) * DH + ch * VEC;
+      lds_load16(k + goff, dK + base * VEC);
+      lds_load16(v + goff, dV + base * VEC);
+    }
+  };
   using YV = typename std::conditional<kBf16, bf16x4, f32x4>::type;
-  YV yprev[QTP][ET];
-  if constexpr (ACCUMULATE) {
+  // Per-lane registers of an item, loaded one item ahead: Q fragments and
+  // the query tokens.
+  struct QState {
+    typename F::type qf[QTP][NKS];
+    int tokq[QTP];
+  };
+  auto load_q = [&](QState& qs, const int* tok, int h) {
 #pragma unroll
     for (int qi = 0; qi < QTP; ++qi) {
-      const TS* yrow = y + int64_t(sTok[(wave + qi * Cfg::NWAVE) * 16 + r16]) * rowstride + int64_t(h) * DH;
+      const int iq = (wave + qi * Cfg::NWAVE) * 16 + r16;
+      qs.tokq[qi] = tok[iq];
+      const TS* qrow = q + int64_t(qs.tokq[qi]) * rowstride + int64_t(h) * DH;
 #pragma unroll
-      for (int et = 0; et < ET; ++et) yprev[qi][et] = *reinterpret_cast<const YV*>(yrow + et * 16 + grp * 4);
+      for (int ks = 0; ks < NKS; ++ks) qs.qf[qi][ks] = F::load(qrow + ks * KI, lane);
     }
+  };
+
+  if (int(blockIdx.x) >= n_items) return;
+  ItemPos pos = decompose(int(blockIdx.x));
+  item_tokens(pos, sTok[0], sCls[0]);
+  lds_barrier();
+  QState nxt;
+  issue_kv(sK0, sV0, sTok[0], pos.h);
+  load_q(nxt, sTok[0], pos.h);
+
+  // Per-lane LDS offsets of the operand fragments for key block 0 (block jb
+  // adds jb rows; jb is a multiple of 8, so the chunk permutation is the same).
+  int offk[2][NKS];
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) offk[jt][ks] = KT::at(jt * 16 + r16, ks * KI + grp * (kBf16 ? 8 : 1));
+  int offv[kBf16 ? ET : 1][2];
+  if constexpr (kBf16) {
+#pragma unroll
+    for (int et = 0; et < ET; ++et)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) offv[et][hf] = KT::at(4 * grp + (r16 >> 2) + 16 * hf, et * 16 + 4 * (r16 & 3));
   }
 
-  // Pass 2: probabilities against the fixed maximum, their sums, and P V.
-  f32x4 o[QTP][ET];
-  float l[QTP];
+  // One item whose K / V tiles are in (cK, cV); the next item's go to (nK, nV).
+  auto step = [&](int n, const MT* cK, const MT* cV, MT* nK, MT* nV) -> bool {
+    const int h = pos.h;
+    const ItemPos npos = advance(pos);
+    const bool has_next = npos.item < n_items;
+    if (has_next) item_tokens(npos, sTok[(n + 1) & 1], sCls[(n + 1) % 3]);
+    wait_vmem();        // this wave's loads for the item (and earlier stores) are done
+    lds_barrier();      // ... and every wave's; the other buffers are free
+    const QState cur = nxt;
+    if (has_next) {
+      issue_kv(nK, nV, sTok[(n + 1) & 1], npos.h);
+      load_q(nxt, sTok[(n + 1) & 1], npos.h);
+    }
+    // The MA output this item adds to (fused branch sum) arrives while the
+    // two passes run.
+    YV yp[QTP][ET];
+    if constexpr (ACCUMULATE) {
 #pragma unroll
-  for (int qi = 0; qi < QTP; ++qi) {
-    l[qi] = 0.f;
+      for (int qi = 0; qi < QTP; ++qi) {
+        const TS* yrow = y + int64_t(cur.tokq[qi]) * rowstride + int64_t(h) * DH;
 #pragma unroll
-    for (int et = 0; et < ET; ++et) o[qi][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll 1
-  for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
-    typename F::type kf[2][NKS];
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) kf[jt][ks] = TK::frag(sK, jb + jt * 16 + r16, ks * KI, lane);
-    bf16x8 vf[kBf16 ? ET : 1];
-    if constexpr (kBf16) {
-#pragma unroll
-      for (int et = 0; et < ET; ++et) {
-        const __bf16* vr = reinterpret_cast<const __bf16*>(&sVt[(et * 16 + r16) * WP + jb + grp * 4]);
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-        vf[et] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int et = 0; et < ET; ++et) yp[qi][et] = *reinterpret_cast<const YV*>(yrow + et * 16 + grp * 4);
       }
     }
+    const bool wrapped = item_wrapped(pos);
+    const int* cls = sCls[n % 3];
+    int qcls[QTP];
 #pragma unroll
-    for (int qi = 0; qi < QTP; ++qi) {
-      f32x4 s[2];
+    for (int qi = 0; qi < QTP; ++qi) qcls[qi] = cls[(wave + qi * Cfg::NWAVE) * 16 + r16];
+
+    // Pass 1: the row maximum of every query over the keys of its own window
+    // (the query itself is always one of them, so the maximum is finite).
+    float msc[QTP];
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(kf[jt][ks], qf[qi][ks], s[jt]);
-      }
-      if (wrapped) {
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          const int4 kc = *reinterpret_cast<const int4*>(&sCls[jb + jt * 16 + grp * 4]);
-          const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) s[jt][r] = kcv[r] != qcls[qi] ? -INFINITY : s[jt][r];
-        }
-      }
-      float lsum = 0.f;
+    for (int qi = 0; qi < QTP; ++qi) msc[qi] = -INFINITY;
+#pragma unroll 1
+    for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
+      typename F::type kf[2][NKS];
+      const MT* kb = cK + jb * DH;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(fmaf(s[jt][r], sc, -msc[qi]));
-          s[jt][r] = p;
-          lsum += p;
+        for (int ks = 0; ks < NKS; ++ks) {
+          if constexpr (kBf16) kf[jt][ks] = *reinterpret_cast<const bf16x8*>(kb + offk[jt][ks]);
+          else kf[jt][ks] = kb[offk[jt][ks]];
         }
-      l[qi] += lsum;
+#pragma unroll
+      for (int qi = 0; qi < QTP; ++qi) {
+        f32x4 s[2];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(kf[jt][ks], cur.qf[qi][ks], s[jt]);
+        }
+        if (wrapped) {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const int4 kc = *reinterpret_cast<const int4*>(&cls[jb + jt * 16 + grp * 4]);
+            const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[jt][r] = kcv[r] != qcls[qi] ? -INFINITY : s[jt][r];
+          }
+        }
+        msc[qi] = fmaxf(msc[qi], fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))));
+      }
+    }
+#pragma unroll
+    for (int qi = 0; qi < QTP; ++qi) {
+      float mq = fmaxf(msc[qi], __shfl_xor(msc[qi], 16, 64));
+      mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
+      msc[qi] = mq * sc;
+    }
+
+    // Pass 2: probabilities against the fixed maximum, their sums, and P V.
+    f32x4 o[QTP][ET];
+    float l[QTP];
+#pragma unroll
+    for (int qi = 0; qi < QTP; ++qi) {
+      l[qi] = 0.f;
+#pragma unroll
+      for (int et = 0; et < ET; ++et) o[qi][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll 1
+    for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
+      typename F::type kf[2][NKS];
+      const MT* kb = cK + jb * DH;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          if constexpr (kBf16) kf[jt][ks] = *reinterpret_cast<const bf16x8*>(kb + offk[jt][ks]);
+          else kf[jt][ks] = kb[offk[jt][ks]];
+        }
+      // V^T fragments (A operand, k = key): lane group g covers keys
+      // jb + 4g + {0..3} and jb + 16 + 4g + {0..3}, matching P^T below.
+      bf16x8 vf[kBf16 ? ET : 1];
       if constexpr (kBf16) {
-        bf16x8 pb;
+        const MT* vb = cV + jb * DH;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pb[r] = static_cast<__bf16>(s[0][r]);
-          pb[4 + r] = static_cast<__bf16>(s[1][r]);
+        for (int et = 0; et < ET; ++et) {
+          const bf16x4 lo = lds_read_tr(vb + offv[et][0]);
+          const bf16x4 hi = lds_read_tr(vb + offv[et][1]);
+          vf[et] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+      }
 #pragma unroll
-        for (int et = 0; et < ET; ++et) o[qi][et] = mma(vf[et], pb, o[qi][et]);
-      } else {
+      for (int qi = 0; qi < QTP; ++qi) {
+        f32x4 s[2];
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(kf[jt][ks], cur.qf[qi][ks], s[jt]);
+        }
+        if (wrapped) {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const int4 kc = *reinterpret_cast<const int4*>(&cls[jb + jt * 16 + grp * 4]);
+            const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[jt][r] = kcv[r] != qcls[qi] ? -INFINITY : s[jt][r];
+          }
+        }
+        float lsum = 0.f;
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(fmaf(s[jt][r], sc, -msc[qi]));
+            s[jt][r] = p;
+            lsum += p;
+          }
+        l[qi] += lsum;
+        if constexpr (kBf16) {
+          bf16x8 pb;
 #pragma unroll
-            for (int et = 0; et < ET; ++et) {
-              const float av = to_f32(sVt[(et * 16 + r16) * WP + jb + jt * 16 + grp * 4 + r]);
-              o[qi][et] = mma(av, s[jt][r], o[qi][et]);
-            }
+          for (int r = 0; r < 4; ++r) {
+            pb[r] = static_cast<__bf16>(s[0][r]);
+            pb[4 + r] = static_cast<__bf16>(s[1][r]);
+          }
+#pragma unroll
+          for (int et = 0; et < ET; ++et) o[qi][et] = mma(vf[et], pb, o[qi][et]);
+        } else {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int et = 0; et < ET; ++et) {
+                const float av = to_f32(cV[KT::at(jb + jt * 16 + grp * 4 + r, et * 16 + r16)]);
+                o[qi][et] = mma(av, s[jt][r], o[qi][et]);
+              }
+        }
       }
     }
-  }
 
 #pragma unroll
-  for (int qi = 0; qi < QTP; ++qi) {
-    float lt = l[qi];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    const float inv = __builtin_amdgcn_rcpf(lt);
-    const int iq = (wave + qi * Cfg::NWAVE) * 16 + r16;
-    TS* yrow = y + int64_t(sTok[iq]) * rowstride + int64_t(h) * DH;
+    for (int qi = 0; qi < QTP; ++qi) {
+      float lt = l[qi];
+      lt += __shfl_xor(lt, 16, 64);
+      lt += __shfl_xor(lt, 32, 64);
+      const float inv = __builtin_amdgcn_rcpf(lt);
+      TS* yrow = y + int64_t(cur.tokq[qi]) * rowstride + int64_t(h) * DH;
 #pragma unroll
-    for (int et = 0; et < ET; ++et) {
-      const int e0 = et * 16 + grp * 4;
-      float ov[4];
+      for (int et = 0; et < ET; ++et) {
+        YV res;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ov[r] = o[qi][et][r] * inv;
-      YV res;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        res[r] = from_f32<TS>(ACCUMULATE ? to_f32(yprev[qi][et][r]) + ov[r] : ov[r]);
-      *reinterpret_cast<YV*>(yrow + e0) = res;
+        for (int r = 0; r < 4; ++r) {
+          const float ov = o[qi][et][r] * inv;
+          res[r] = from_f32<TS>(ACCUMULATE ? to_f32(yp[qi][et][r]) + ov : ov);
+        }
+        *reinterpret_cast<YV*>(yrow + et * 16 + grp * 4) = res;
+      }
     }
+    pos = npos;
+    return has_next;
+  };
+
+#pragma unroll 1
+  for (int n = 0;; n += 2) {
+    if (!step(n, sK0, sV0, sK1, sV1)) break;
+    if (!step(n + 1, sK1, sV1, sK0, sV0)) break;
   }
 }
 
@@ -1178,6 +1298,18 @@ int hip_status() {
 }
 
 RmsMap make_rms(const lingen_mate_shape* s, int mode) { return RmsMap{mode, s->T, s->H, s->W}; }
+
+// Compute units of the current device (cached per device).
+int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
 
 // Heads per chunk workgroup: the largest divisor of Hs not above `cap`.
 int head_group(int Hs, int cap = kHeadGroupMax) {
@@ -1290,16 +1422,21 @@ int launch_te(const lingen_mate_shape* s, int shifted, const void* q, const void
   const int nwin = g.nwt * g.nwh * g.nww;
   const int64_t per = L * s->attn_heads * DH * elem_bytes(s);
   using Cfg = AttnCfg<TS, DH, NWIN>;
+  // Persistent grid: one workgroup per compute unit.
+  const int ncu = compute_units();
+  if (ncu < 1) return LINGEN_ERR_HIP;
   for (int b = 0; b < s->batch; ++b) {
     const int64_t off = int64_t(b) * per;
     const TS* qb = reinterpret_cast<const TS*>(static_cast<const char*>(q) + off);
     const TS* kb = reinterpret_cast<const TS*>(static_cast<const char*>(k) + off);
     const TS* vb = reinterpret_cast<const TS*>(static_cast<const char*>(v) + off);
     TS* yb = reinterpret_cast<TS*>(static_cast<char*>(y) + off);
+    const int items = nwin * s->attn_heads;
+    const int grid = items < ncu ? items : ncu;
     if (accumulate)
-      tesa_window_kernel<TS, DH, NWIN, true><<<nwin * s->attn_heads, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, yb);
+      tesa_window_kernel<TS, DH, NWIN, true><<<grid, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, items, yb);
     else
-      tesa_window_kernel<TS, DH, NWIN, false><<<nwin * s->attn_heads, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, yb);
+      tesa_window_kernel<TS, DH, NWIN, false><<<grid, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, items, yb);
     if (hip_status()) return LINGEN_ERR_HIP;
   }
   return LINGEN_OK;

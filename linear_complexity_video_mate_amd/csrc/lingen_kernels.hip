@@ -903,15 +903,13 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 // CU); a workgroup walks its items in sequence with the K and V tiles of the
 // next item streaming into the second of two LDS buffers (direct
 // global-to-LDS loads, no registers) while the current one is computed, and
-// the next item's Q fragments and MA output held in registers.  Per item:
+// the next item's Q fragments in registers.  Per item and block of 32 keys:
 //   S^T[j][i] = K_j . Q_i            (MFMA, A = K from LDS, B = Q in registers)
-//   pass 1: row maxima of S over the window (each lane owns one query per tile)
-//   pass 2: P^T = 2^((S^T - max) log2(e)/sqrt(d)), row sums, and
-//           O^T[e][i] += V^T[e][j] P^T[j][i]  (MFMA, B = P^T in registers;
-//           A = V^T read from the row-major V tile with LDS transpose loads)
-// Recomputing S in pass 2 costs MFMA time, which this kernel has to spare,
-// and removes the rescaling of the running output that an online softmax
-// needs.
+//   m_i <- max(m_i, max_j S[i][j])   (running maximum; each lane owns one query)
+//   P^T = 2^((S^T - m) log2(e)/sqrt(d)); output and row sums rescaled by
+//         2^(m_old - m_new) and accumulated:
+//   O^T[e][i] += V^T[e][j] P^T[j][i] (MFMA, B = P^T in registers; A = V^T
+//         read from the row-major V tile with LDS transpose loads)
 // ---------------------------------------------------------------------------
 
 struct WinGeom {
@@ -1122,56 +1120,15 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
 #pragma unroll
     for (int qi = 0; qi < QTP; ++qi) qcls[qi] = cls[(wave + qi * Cfg::NWAVE) * 16 + r16];
 
-    // Pass 1: the row maximum of every query over the keys of its own window
-    // (the query itself is always one of them, so the maximum is finite).
+    // One pass over the key blocks with a running maximum per query: the
+    // block's scores are exponentiated against max(running, block) and the
+    // earlier output and sums are rescaled when the maximum grows.
     float msc[QTP];
-#pragma unroll
-    for (int qi = 0; qi < QTP; ++qi) msc[qi] = -INFINITY;
-#pragma unroll 1
-    for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
-      typename F::type kf[2][NKS];
-      const MT* kb = cK + jb * DH;
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          if constexpr (kBf16) kf[jt][ks] = *reinterpret_cast<const bf16x8*>(kb + offk[jt][ks]);
-          else kf[jt][ks] = kb[offk[jt][ks]];
-        }
-#pragma unroll
-      for (int qi = 0; qi < QTP; ++qi) {
-        f32x4 s[2];
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(kf[jt][ks], cur.qf[qi][ks], s[jt]);
-        }
-        if (wrapped) {
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            const int4 kc = *reinterpret_cast<const int4*>(&cls[jb + jt * 16 + grp * 4]);
-            const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[jt][r] = kcv[r] != qcls[qi] ? -INFINITY : s[jt][r];
-          }
-        }
-        msc[qi] = fmaxf(msc[qi], fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))));
-      }
-    }
-#pragma unroll
-    for (int qi = 0; qi < QTP; ++qi) {
-      float mq = fmaxf(msc[qi], __shfl_xor(msc[qi], 16, 64));
-      mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
-      msc[qi] = mq * sc;
-    }
-
-    // Pass 2: probabilities against the fixed maximum, their sums, and P V.
     f32x4 o[QTP][ET];
     float l[QTP];
 #pragma unroll
     for (int qi = 0; qi < QTP; ++qi) {
+      msc[qi] = -INFINITY;
       l[qi] = 0.f;
 #pragma unroll
       for (int et = 0; et < ET; ++et) o[qi][et] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1187,8 +1144,6 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
           if constexpr (kBf16) kf[jt][ks] = *reinterpret_cast<const bf16x8*>(kb + offk[jt][ks]);
           else kf[jt][ks] = kb[offk[jt][ks]];
         }
-      // V^T fragments (A operand, k = key): lane group g covers keys
-      // jb + 4g + {0..3} and jb + 16 + 4g + {0..3}, matching P^T below.
       bf16x8 vf[kBf16 ? ET : 1];
       if constexpr (kBf16) {
         const MT* vb = cV + jb * DH;
@@ -1217,16 +1172,29 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
             for (int r = 0; r < 4; ++r) s[jt][r] = kcv[r] != qcls[qi] ? -INFINITY : s[jt][r];
           }
         }
+        float bm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        const float mnew = fmaxf(msc[qi], bm * sc);
+        // A query with every key so far masked keeps a zero output.
+        const float mref = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = fast_exp2(msc[qi] - mref);
+        msc[qi] = mnew;
         float lsum = 0.f;
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(fmaf(s[jt][r], sc, -msc[qi]));
+            const float p = fast_exp2(fmaf(s[jt][r], sc, -mref));
             s[jt][r] = p;
             lsum += p;
           }
-        l[qi] += lsum;
+        l[qi] = fmaf(l[qi], alpha, lsum);
+#pragma unroll
+        for (int et = 0; et < ET; ++et)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[qi][et][r] *= alpha;
         if constexpr (kBf16) {
           bf16x8 pb;
 #pragma unroll

@@ -903,7 +903,8 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 // CU); a workgroup walks its items in sequence with the K and V tiles of the
 // next item streaming into the second of two LDS buffers (direct
 // global-to-LDS loads, no registers) while the current one is computed, and
-// the next item's Q fragments in registers.  Per item and block of 32 keys:
+// the next item's Q fragments in registers.  Per item and block of 64 keys
+// (32 for fp32):
 //   S^T[j][i] = K_j . Q_i            (MFMA, A = K from LDS, B = Q in registers)
 //   m_i <- max(m_i, max_j S[i][j])   (running maximum; each lane owns one query)
 //   P^T = 2^((S^T - m) log2(e)/sqrt(d)); output and row sums rescaled by
@@ -924,7 +925,6 @@ struct AttnCfg {
   static constexpr int QTILES = NWIN / 16;
   static constexpr int NWAVE = QTILES >= 16 ? 16 : QTILES;
   static constexpr int QT_PER = QTILES / NWAVE;       // query tiles per wave
-  static constexpr int KB = 32;                        // keys per block
   static constexpr int VEC = 16 / int(sizeof(TS));     // elements per 16-byte chunk
   static constexpr int CPR = DH / VEC;                 // chunks per K / V row
   static constexpr int UNITS = NWIN * CPR;             // 16-byte chunks per tile
@@ -980,7 +980,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   constexpr bool kBf16 = std::is_same<MT, __bf16>::value;
   constexpr int ET = DH / 16;
   constexpr int NKS = DH / KI;
-  static_assert(NWIN % Cfg::KB == 0 && DH % 16 == 0 && DH % KI == 0, "attention tile shape");
+  static_assert(NWIN % 32 == 0 && DH % 16 == 0 && DH % KI == 0, "attention tile shape");
   // Two buffers per tile, as separate arrays so that reads of the current
   // buffer need not wait for the loads streaming into the other one.
   __shared__ __attribute__((aligned(16))) MT sK0[NWIN * DH];
@@ -1133,87 +1133,91 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
 #pragma unroll
       for (int et = 0; et < ET; ++et) o[qi][et] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    static_assert(NWIN % 64 == 0 || !kBf16, "64-key blocks");
+    constexpr int SB = kBf16 ? 2 : 1;     // 32-key sub-blocks per block
 #pragma unroll 1
-    for (int jb = 0; jb < NWIN; jb += Cfg::KB) {
-      typename F::type kf[2][NKS];
-      const MT* kb = cK + jb * DH;
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          if constexpr (kBf16) kf[jt][ks] = *reinterpret_cast<const bf16x8*>(kb + offk[jt][ks]);
-          else kf[jt][ks] = kb[offk[jt][ks]];
-        }
-      bf16x8 vf[kBf16 ? ET : 1];
-      if constexpr (kBf16) {
-        const MT* vb = cV + jb * DH;
-#pragma unroll
-        for (int et = 0; et < ET; ++et) {
-          const bf16x4 lo = lds_read_tr(vb + offv[et][0]);
-          const bf16x4 hi = lds_read_tr(vb + offv[et][1]);
-          vf[et] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      }
+    for (int jb = 0; jb < NWIN; jb += 32 * SB) {
 #pragma unroll
       for (int qi = 0; qi < QTP; ++qi) {
-        f32x4 s[2];
+        f32x4 s[SB][2];
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) s[jt] = mma(kf[jt][ks], cur.qf[qi][ks], s[jt]);
-        }
-        if (wrapped) {
+        for (int sb = 0; sb < SB; ++sb) {
+          const MT* kb = cK + (jb + 32 * sb) * DH;
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
-            const int4 kc = *reinterpret_cast<const int4*>(&cls[jb + jt * 16 + grp * 4]);
-            const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
+            s[sb][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s[jt][r] = kcv[r] != qcls[qi] ? -INFINITY : s[jt][r];
+            for (int ks = 0; ks < NKS; ++ks) {
+              typename F::type kf;
+              if constexpr (kBf16) kf = *reinterpret_cast<const bf16x8*>(kb + offk[jt][ks]);
+              else kf = kb[offk[jt][ks]];
+              s[sb][jt] = mma(kf, cur.qf[qi][ks], s[sb][jt]);
+            }
+          }
+          if (wrapped) {
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+              const int4 kc = *reinterpret_cast<const int4*>(&cls[jb + 32 * sb + jt * 16 + grp * 4]);
+              const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+              for (int r = 0; r < 4; ++r) s[sb][jt][r] = kcv[r] != qcls[qi] ? -INFINITY : s[sb][jt][r];
+            }
           }
         }
-        float bm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        float bm = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb)
+          bm = fmaxf(bm, fmaxf(fmaxf(fmaxf(s[sb][0][0], s[sb][0][1]), fmaxf(s[sb][0][2], s[sb][0][3])),
+                               fmaxf(fmaxf(s[sb][1][0], s[sb][1][1]), fmaxf(s[sb][1][2], s[sb][1][3]))));
         bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
         bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
         const float mnew = fmaxf(msc[qi], bm * sc);
-        // A query with every key so far masked keeps a zero output.
         const float mref = mnew == -INFINITY ? 0.f : mnew;
         const float alpha = fast_exp2(msc[qi] - mref);
         msc[qi] = mnew;
         float lsum = 0.f;
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+        for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(fmaf(s[jt][r], sc, -mref));
-            s[jt][r] = p;
-            lsum += p;
-          }
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float p = fast_exp2(fmaf(s[sb][jt][r], sc, -mref));
+              s[sb][jt][r] = p;
+              lsum += p;
+            }
         l[qi] = fmaf(l[qi], alpha, lsum);
 #pragma unroll
         for (int et = 0; et < ET; ++et)
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[qi][et][r] *= alpha;
-        if constexpr (kBf16) {
-          bf16x8 pb;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pb[r] = static_cast<__bf16>(s[0][r]);
-            pb[4 + r] = static_cast<__bf16>(s[1][r]);
+        for (int sb = 0; sb < SB; ++sb) {
+          if constexpr (kBf16) {
+            bf16x8 pb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              pb[r] = static_cast<__bf16>(s[sb][0][r]);
+              pb[4 + r] = static_cast<__bf16>(s[sb][1][r]);
+            }
+            const MT* vb = cV + (jb + 32 * sb) * DH;
+#pragma unroll
+            for (int et = 0; et < ET; ++et) {
+              const bf16x4 lo = lds_read_tr(vb + offv[et][0]);
+              const bf16x4 hi = lds_read_tr(vb + offv[et][1]);
+              o[qi][et] = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[qi][et]);
+            }
+          } else {
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int et = 0; et < ET; ++et) {
+                  const float av = to_f32(cV[KT::at(jb + jt * 16 + grp * 4 + r, et * 16 + r16)]);
+                  o[qi][et] = mma(av, s[sb][jt][r], o[qi][et]);
+                }
           }
-#pragma unroll
-          for (int et = 0; et < ET; ++et) o[qi][et] = mma(vf[et], pb, o[qi][et]);
-        } else {
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-              for (int et = 0; et < ET; ++et) {
-                const float av = to_f32(cV[KT::at(jb + jt * 16 + grp * 4 + r, et * 16 + r16)]);
-                o[qi][et] = mma(av, s[jt][r], o[qi][et]);
-              }
         }
       }
     }

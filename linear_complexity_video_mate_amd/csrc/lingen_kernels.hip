@@ -956,12 +956,13 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) const __bf16 lds_bf16;
 // Transposing LDS load (16-bit elements): within each group of 16 lanes,
 // lane i receives element (i mod 4) of the 8-byte chunk read by lane
-// 4r + i/4, in slot r.
-__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
+// 4r + i/4, in slot r.  Takes an LDS-space pointer so that constant parts
+// of the address fold into the instruction's offset field.
+__device__ __forceinline__ bf16x4 lds_read_tr(lds_bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(bf16x4, v);
 }
 
@@ -1075,19 +1076,16 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   issue_kv(sK0, sV0, sTok[0], pos.h);
   load_q(nxt, sTok[0], pos.h);
 
-  // Per-lane LDS offsets of the operand fragments for key block 0 (block jb
-  // adds jb rows; jb is a multiple of 8, so the chunk permutation is the same).
-  int offk[2][NKS];
+  // Per-lane LDS offsets of the operand fragments in rows 0..15 of a tile.
+  // A fragment 8m rows further down is m*8*DH elements further on (the
+  // chunk permutation repeats every 8 rows), a compile-time offset.
+  int offk[NKS];
 #pragma unroll
-  for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) offk[jt][ks] = KT::at(jt * 16 + r16, ks * KI + grp * (kBf16 ? 8 : 1));
-  int offv[kBf16 ? ET : 1][2];
+  for (int ks = 0; ks < NKS; ++ks) offk[ks] = KT::at(r16, ks * KI + grp * (kBf16 ? 8 : 1));
+  int offv[kBf16 ? ET : 1];
   if constexpr (kBf16) {
 #pragma unroll
-    for (int et = 0; et < ET; ++et)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) offv[et][hf] = KT::at(4 * grp + (r16 >> 2) + 16 * hf, et * 16 + 4 * (r16 & 3));
+    for (int et = 0; et < ET; ++et) offv[et] = KT::at(4 * grp + (r16 >> 2), et * 16 + 4 * (r16 & 3));
   }
 
   // One item whose K / V tiles are in (cK, cV); the next item's go to (nK, nV).
@@ -1142,15 +1140,16 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
         f32x4 s[SB][2];
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
-          const MT* kb = cK + (jb + 32 * sb) * DH;
+          const MT* kb = cK + jb * DH;
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
             s[sb][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
               typename F::type kf;
-              if constexpr (kBf16) kf = *reinterpret_cast<const bf16x8*>(kb + offk[jt][ks]);
-              else kf = kb[offk[jt][ks]];
+              const MT* kp = kb + offk[ks] + (32 * sb + 16 * jt) * DH;
+              if constexpr (kBf16) kf = *reinterpret_cast<const bf16x8*>(kp);
+              else kf = *kp;
               s[sb][jt] = mma(kf, cur.qf[qi][ks], s[sb][jt]);
             }
           }
@@ -1200,11 +1199,11 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
               pb[r] = static_cast<__bf16>(s[sb][0][r]);
               pb[4 + r] = static_cast<__bf16>(s[sb][1][r]);
             }
-            const MT* vb = cV + (jb + 32 * sb) * DH;
+            lds_bf16* vb = (lds_bf16*)(cV) + jb * DH;
 #pragma unroll
             for (int et = 0; et < ET; ++et) {
-              const bf16x4 lo = lds_read_tr(vb + offv[et][0]);
-              const bf16x4 hi = lds_read_tr(vb + offv[et][1]);
+              const bf16x4 lo = lds_read_tr(vb + offv[et] + (32 * sb) * DH);
+              const bf16x4 hi = lds_read_tr(vb + offv[et] + (32 * sb + 16) * DH);
               o[qi][et] = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[qi][et]);
             }
           } else {

@@ -345,12 +345,18 @@ struct ReviewGeom {
   int st, sh, sw;   // stride between sampled blocks, in blocks
 };
 
+// Block (r, y): the mean over review block r of head y's x row slice (and
+// of dt for that head) for y < Hs, of the B rows for y == Hs.  Each thread
+// sums the 16-byte chunk c of every RP-th token row, with several rows'
+// loads in flight, and the RP partial sums are reduced through LDS.
 template <typename TS>
 __global__ __launch_bounds__(256) void review_pool_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
                                                           const TS* __restrict__ B, int T, int H, int W, int Hs,
                                                           int P, int N, ReviewGeom g, float* __restrict__ rx,
                                                           float* __restrict__ rdt, float* __restrict__ rb) {
-  __shared__ float red[256];
+  constexpr int VEC = Vec16<TS>::n;
+  constexpr int UNROLL = 4;
+  __shared__ float red[256 * VEC];
   const int r = blockIdx.x;
   const int y = blockIdx.y;
   const int tid = threadIdx.x;
@@ -362,20 +368,38 @@ __global__ __launch_bounds__(256) void review_pool_kernel(const TS* __restrict__
     const int a = tl / (g.ph * g.pw), b = (tl / g.pw) % g.ph, c = tl % g.pw;
     return ((t0 + a) * H + (h0 + b)) * W + (w0 + c);
   };
-  const int width = (y < Hs) ? P : N;   // P and N divide 256 (checked on the host)
-  const int col = tid % width, grp = tid / width, ngrp = 256 / width;
-  float acc = 0.f;
-  for (int tl = grp; tl < cnt; tl += ngrp) {
-    const int64_t tok = token(tl);
-    acc += (y < Hs) ? to_f32(x[(tok * Hs + y) * P + col]) : to_f32(B[tok * N + col]);
+  const int width = (y < Hs) ? P : N;   // P, N in {16, 32, 64, 128} in every compiled family, so
+                                        // width / VEC divides 256
+  const int cpr = width / VEC, rp = 256 / cpr;
+  const int c = tid % cpr, ro = tid / cpr;
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  for (int tl0 = ro; tl0 < cnt; tl0 += rp * UNROLL) {
+    Vec16<TS> v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int tl = tl0 + u * rp;
+      v[u].u = make_uint4(0, 0, 0, 0);
+      if (tl < cnt) {
+        const int64_t tok = token(tl);
+        const TS* src = (y < Hs) ? x + (tok * Hs + y) * P : B + tok * N;
+        v[u].u = *reinterpret_cast<const uint4*>(src + c * VEC);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += to_f32(v[u].e[e]);
   }
-  red[tid] = acc;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) red[ro * width + c * VEC + e] = acc[e];
   lds_barrier();
   if (tid < width) {
-    float s = 0.f;
-    for (int q = 0; q < ngrp; ++q) s += red[q * width + tid];
-    if (y < Hs) rx[(int64_t(r) * Hs + y) * P + tid] = s * inv;
-    else rb[int64_t(r) * N + tid] = s * inv;
+    float sum = 0.f;
+    for (int q = 0; q < rp; ++q) sum += red[q * width + tid];
+    if (y < Hs) rx[(int64_t(r) * Hs + y) * P + tid] = sum * inv;
+    else rb[int64_t(r) * N + tid] = sum * inv;
   }
   if (y < Hs) {
     lds_barrier();
@@ -395,23 +419,50 @@ __global__ __launch_bounds__(256) void review_pool_kernel(const TS* __restrict__
 __global__ __launch_bounds__(256) void review_state_kernel(const float* __restrict__ rx, const float* __restrict__ rdt,
                                                            const float* __restrict__ rb, const float* __restrict__ A,
                                                            int R, int Hs, int P, int N, float* __restrict__ hR) {
+  // Block (h, slice) computes elements slice*1024 .. +1023 of head h's P x N
+  // state, four per thread.  Review tokens are taken RT at a time: their
+  // weighted x rows and B rows are staged in LDS, then every thread
+  // accumulates its elements.
+  constexpr int RT = 64, MAXP = 128, MAXN = 128, MAXE = 4;
   __shared__ float w[256];
-  const int h = blockIdx.x;
-  if (threadIdx.x == 0) {
+  __shared__ float sx[RT * MAXP];
+  __shared__ float sb[RT * MAXN];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  for (int r = tid; r < R; r += 256) w[r] = rdt[r * Hs + h];
+  lds_barrier();
+  if (tid == 0) {   // w_r = e^{sum_{tau > r} a_tau} dt_r, from the last review token back
     float suf = 0.f;
     for (int r = R - 1; r >= 0; --r) {
-      const float d = rdt[r * Hs + h];
+      const float d = w[r];
       w[r] = expf(suf) * d;
       suf += d * A[h];
     }
   }
   lds_barrier();
-  for (int e = threadIdx.x; e < P * N; e += 256) {
-    const int p = e / N, n = e % N;
-    float acc = 0.f;
-    for (int r = 0; r < R; ++r) acc += w[r] * rx[(r * Hs + h) * P + p] * rb[r * N + n];
-    hR[int64_t(h) * P * N + e] = acc;
+  const int e0 = int(blockIdx.y) * 1024 + tid;
+  float acc[MAXE];
+#pragma unroll
+  for (int k = 0; k < MAXE; ++k) acc[k] = 0.f;
+  for (int r0 = 0; r0 < R; r0 += RT) {
+    const int rn = R - r0 < RT ? R - r0 : RT;
+    for (int u = tid; u < rn * P; u += 256) sx[u] = rx[((r0 + u / P) * Hs + h) * P + u % P] * w[r0 + u / P];
+    for (int u = tid; u < rn * N; u += 256) sb[u] = rb[(r0 + u / N) * N + u % N];
+    lds_barrier();
+    int pk[MAXE], nk[MAXE];
+#pragma unroll
+    for (int k = 0; k < MAXE; ++k) {
+      const int e = e0 + k * 256 < P * N ? e0 + k * 256 : 0;
+      pk[k] = e / N;
+      nk[k] = e % N;
+    }
+    for (int rr = 0; rr < rn; ++rr)
+#pragma unroll
+      for (int k = 0; k < MAXE; ++k) acc[k] += sx[rr * P + pk[k]] * sb[rr * N + nk[k]];
+    lds_barrier();
   }
+#pragma unroll
+  for (int k = 0; k < MAXE; ++k)
+    if (e0 + k * 256 < P * N) hR[int64_t(h) * P * N + e0 + k * 256] = acc[k];
 }
 
 // ---------------------------------------------------------------------------
@@ -1310,7 +1361,7 @@ int launch_review(const lingen_mate_shape* s, const TS* x, const float* dt, cons
   review_pool_kernel<TS><<<dim3(s->n_review, s->ssd_heads + 1), 256, 0, st>>>(
       x, dt, B, s->T, s->H, s->W, s->ssd_heads, s->headdim, s->d_state, g, rx, rdt, rb);
   if (hip_status()) return LINGEN_ERR_HIP;
-  review_state_kernel<<<s->ssd_heads, 256, 0, st>>>(rx, rdt, rb, A, s->n_review, s->ssd_heads, s->headdim,
+  review_state_kernel<<<dim3(s->ssd_heads, (s->headdim * s->d_state + 1023) / 1024), 256, 0, st>>>(rx, rdt, rb, A, s->n_review, s->ssd_heads, s->headdim,
                                                     s->d_state, hR);
   return hip_status();
 }

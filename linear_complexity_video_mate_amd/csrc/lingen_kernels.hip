@@ -161,13 +161,17 @@ struct Stage16 {
 // laid out [COLS][ld]: unit u covers the token pair (2i, 2i+1) and VEC
 // consecutive columns; both rows are loaded before any is consumed, and the
 // consumer writes each column's pair of values with one store (for bf16 one
-// 32-bit LDS word, so no two lanes touch the same word).
-template <typename T, int ROWS, int COLS, int NTHR>
+// 32-bit LDS word, so no two lanes touch the same word).  LPT consecutive
+// units take consecutive 16-byte pieces of the same pair of rows.
+template <typename T, int ROWS, int COLS, int NTHR, int LPT = 1>
 struct StageT {
   static constexpr int VEC = Vec16<T>::n;
   static constexpr int UNITS = (ROWS / 2) * (COLS / VEC);
   static constexpr int IT = (UNITS + NTHR - 1) / NTHR;
   static_assert(ROWS % 2 == 0 && COLS % VEC == 0, "token pairs and 16-byte columns");
+  static_assert((COLS / VEC) % LPT == 0, "whole groups of pieces per row");
+  __device__ static __forceinline__ int pair_of(int u) { return (u / LPT) % (ROWS / 2); }
+  __device__ static __forceinline__ int col_of(int u) { return ((u / LPT) / (ROWS / 2) * LPT + u % LPT) * VEC; }
   uint4 a[IT], b[IT];
   template <typename RowPtr>   // RowPtr(token) -> const T* to the start of that token's row
   __device__ __forceinline__ void load(RowPtr row) {
@@ -175,7 +179,7 @@ struct StageT {
     for (int it = 0; it < IT; ++it) {
       const int u = int(threadIdx.x) + it * NTHR;
       if (UNITS % NTHR == 0 || u < UNITS) {
-        const int i = u % (ROWS / 2), c0 = (u / (ROWS / 2)) * VEC;
+        const int i = pair_of(u), c0 = col_of(u);
         a[it] = *reinterpret_cast<const uint4*>(row(2 * i) + c0);
         b[it] = *reinterpret_cast<const uint4*>(row(2 * i + 1) + c0);
       }
@@ -190,7 +194,7 @@ struct StageT {
         Vec16<T> va, vb;
         va.u = a[it];
         vb.u = b[it];
-        f(2 * (u % (ROWS / 2)), (u / (ROWS / 2)) * VEC, va, vb);
+        f(2 * pair_of(u), col_of(u), va, vb);
       }
     }
   }
@@ -484,6 +488,12 @@ struct StateCfg {
   static constexpr int NT_PER = (NT + WN - 1) / WN;
 };
 
+// Pieces of one token-pair row taken by consecutive lanes when staging x
+// and B: one load instruction then touches 32 token rows instead of 64,
+// which halves its address translations when the scan order puts
+// consecutive tokens far apart, while the transposed LDS stores stay
+// spread over the banks.
+constexpr int kLptX = 2, kLptB = 2;
 template <typename TS, int P, int N, int Q>
 __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
                                                               const float* __restrict__ A, const TS* __restrict__ B,
@@ -517,7 +527,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
 
   load_chunk_schedule<Q, NTHR>(cs, dt, A, rms, c, Hs, h0, hg);
   {
-    StageT<TS, Q, N, NTHR> bs;
+    StageT<TS, Q, N, NTHR, kLptB> bs;
     bs.load([&](int s) { return B + int64_t(cs.tok[s]) * N; });
     bs.use([&](int s0, int n0, const Vec16<TS>& va, const Vec16<TS>& vb) {
 #pragma unroll
@@ -525,7 +535,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
     });
   }
   // x of the next head is loaded while the current head is computed.
-  StageT<TS, Q, P, NTHR> xs;
+  StageT<TS, Q, P, NTHR, kLptX> xs;
   auto load_x = [&](int h) { xs.load([&](int s) { return x + (int64_t(cs.tok[s]) * Hs + h) * P; }); };
   load_x(h0);
 
@@ -744,8 +754,11 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   };
   HeadBuf buf0;
   auto load_head = [&](HeadBuf& hb_, int h) {
+    // Consecutive lanes take consecutive 16-byte pieces of one token row, so
+    // one load instruction touches few rows (and pages) even when the scan
+    // order puts consecutive tokens far apart.
     hb_.xs.load([&](int u) {
-      return *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[u % Q]) * Hs + h) * P + (u / Q) * VEC);
+      return *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[u / (P / VEC)]) * Hs + h) * P + (u % (P / VEC)) * VEC);
     });
     const uint4* hf = reinterpret_cast<const uint4*>(states + (int64_t(c) * Hs + h) * per);
     const uint4* hb = reinterpret_cast<const uint4*>(states + ((int64_t(n_chunks) + c) * Hs + h) * per);
@@ -791,7 +804,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
     const int h = h0 + hh;
     // Stage x_h (transposed) and the two entering states of this head.
     buf.xs.use([&](int u, uint4 raw) {
-      const int s = u % Q, p0 = (u / Q) * VEC;
+      const int s = u / (P / VEC), p0 = (u % (P / VEC)) * VEC;
       Vec16<TS> v;
       v.u = raw;
 #pragma unroll

@@ -628,26 +628,27 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
 // ---------------------------------------------------------------------------
 // State pass: turns chunk states into the state entering each chunk, in
 // place.  dir 0 walks chunks upward, dir 1 downward; h0 (review state, fp32,
-// or zero) starts both walks.  Each thread owns 16 bytes of one head's
-// P x N state and carries it in fp32.
+// or zero) starts both walks.  Each thread owns 8 elements of one head's
+// P x N state and carries them in fp32.
 // ---------------------------------------------------------------------------
 
-template <typename TS, int U>
+template <typename TS, int U, int E>
 __global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ states, const float* __restrict__ decay,
                                                              const float* __restrict__ h0, int Hs, int PN,
                                                              int n_chunks) {
-  // 4 elements per thread: 8-byte bf16 or 16-byte fp32 accesses.  A block
-  // (blockDim.x threads, dividing PN/4) covers consecutive elements of one
-  // head, so the head index and its chunk decays are wave-uniform.
-  using VT = typename std::conditional<std::is_same<TS, __bf16>::value, bf16x4, f32x4>::type;
+  // E elements per thread (16-byte accesses for bf16 at E = 8), U chunks'
+  // loads in flight.  A block (blockDim.x threads, dividing PN/E) covers
+  // consecutive elements of one head, so the head index and its chunk
+  // decays are wave-uniform.
+  using VT = TS __attribute__((ext_vector_type(E)));
   const int dir = blockIdx.y;
-  const int blocks_per_head = (PN / 4) / int(blockDim.x);
+  const int blocks_per_head = (PN / E) / int(blockDim.x);
   const int h = __builtin_amdgcn_readfirstlane(int(blockIdx.x) / blocks_per_head);
   const int64_t ev = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  float hv[4];
+  float hv[E];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) hv[e] = h0 ? h0[ev * 4 + e] : 0.f;
-  const int64_t cstride = int64_t(Hs) * PN / 4;
+  for (int e = 0; e < E; ++e) hv[e] = h0 ? h0[ev * E + e] : 0.f;
+  const int64_t cstride = int64_t(Hs) * PN / E;
   VT* base = reinterpret_cast<VT*>(states) + int64_t(dir) * n_chunks * cstride + ev;
   const float* dec = decay + h;
   for (int step = 0; step < n_chunks; step += U) {
@@ -669,10 +670,10 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ st
         const int c = dir ? n_chunks - 1 - k : k;
         VT o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = from_f32<TS>(hv[e]);
+        for (int e = 0; e < E; ++e) o[e] = from_f32<TS>(hv[e]);
         base[int64_t(c) * cstride] = o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hv[e] = g[u] * hv[e] + to_f32(buf[u][e]);
+        for (int e = 0; e < E; ++e) hv[e] = g[u] * hv[e] + to_f32(buf[u][e]);
       }
     }
   }
@@ -1400,11 +1401,13 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
                                                                        states, decay);
   if (hip_status()) return LINGEN_ERR_HIP;
   if (int rc = mark(ev, 2, st)) return rc;
-  // P*N/4 threads per head; P*N is a multiple of 256 in every compiled family
-  const int bs = (P * N / 4) < 256 ? (P * N / 4) : 256;
-  static_assert((P * N / 4) % 64 == 0 && ((P * N / 4) < 256 || (P * N / 4) % 256 == 0), "state pass blocking");
-  const int64_t thr = int64_t(Hs) * P * N / 4;
-  ssd_state_pass_kernel<TS, 16><<<dim3(unsigned(thr / bs), 2), bs, 0, st>>>(states, decay, h0, Hs, P * N,
+  // P*N/8 threads per head, in blocks of up to 256 (P*N/8 is 64, 512 or
+  // 1024 in the compiled families).
+  constexpr int E = 8, BS = 256;
+  static_assert((P * N / E) % 64 == 0 && ((P * N / E) < BS || (P * N / E) % BS == 0), "state pass blocking");
+  const int bs = (P * N / E) < BS ? (P * N / E) : BS;
+  const int64_t thr = int64_t(Hs) * P * N / E;
+  ssd_state_pass_kernel<TS, 8, E><<<dim3(unsigned(thr / bs), 2), bs, 0, st>>>(states, decay, h0, Hs, P * N,
                                                                                       nc);
   if (hip_status()) return LINGEN_ERR_HIP;
   return mark(ev, 3, st);

@@ -231,6 +231,35 @@ def copy_calibration(args, mate, torch):
     return 0
 
 
+def gather_modes(args, mate, torch):
+    """The scan-order gather (lingen_rms_gather) on the workload's grid with
+    rows of one token's x (Hs*P elements): reads and writes L rows per launch,
+    in each of the four scan orders."""
+    from mate_inputs import CONFIGS, CONFIG_NOTES
+
+    s = CONFIGS[args.config]
+    src = torch.empty((s.L, s.d_inner), dtype=torch.bfloat16 if s.dtype == "bf16" else torch.float32,
+                      device="cuda").normal_()
+    dst = torch.empty_like(src)
+    nbytes = src.numel() * src.element_size()
+    out = {"workload": CONFIG_NOTES[args.config], "row_bytes": s.d_inner * src.element_size(), "modes": {}}
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for mode in range(4):
+        for _ in range(args.warmup):
+            mate.lingen_rms_gather(src, mode, s.T, s.H, s.W, out=dst)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            mate.lingen_rms_gather(src, mode, s.T, s.H, s.W, out=dst)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        out["modes"][mode] = {"ms": round(ms, 4), "GB/s_read+write": round(2 * nbytes / ms / 1e6, 1),
+                              "hbm_frac": round(2 * nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------------------
 
 def main(argv=None):
@@ -246,6 +275,9 @@ def main(argv=None):
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="instead of the mixer, time a plain device copy of this many GiB (the RMS gather "
                          "kernel in scan mode 0) and print its bandwidth: the HBM calibration point")
+    ap.add_argument("--gather", action="store_true",
+                    help="instead of the mixer, time the scan-order gather of x-sized rows in each of the "
+                         "four scan orders on the workload's grid")
     args = ap.parse_args(argv)
 
     if args.record_traffic:
@@ -268,6 +300,8 @@ def main(argv=None):
     mate.lib()
     if args.copy_gib > 0:
         return copy_calibration(args, mate, torch)
+    if args.gather:
+        return gather_modes(args, mate, torch)
     s = CONFIGS[args.config]
     workload = CONFIG_NOTES[args.config]
     print(f"[bench] generating inputs: {workload}, {s.L} tokens", file=sys.stderr, flush=True)

@@ -639,7 +639,8 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ st
   // E elements per thread (16-byte accesses for bf16 at E = 8), U chunks'
   // loads in flight.  A block (blockDim.x threads, dividing PN/E) covers
   // consecutive elements of one head, so the head index and its chunk
-  // decays are wave-uniform.
+  // decays are wave-uniform.  Every state is read and written exactly once,
+  // so the accesses are marked non-temporal (they need not stay in cache).
   using VT = TS __attribute__((ext_vector_type(E)));
   const int dir = blockIdx.y;
   const int blocks_per_head = (PN / E) / int(blockDim.x);
@@ -659,7 +660,7 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ st
       const int k = step + u;
       if (k < n_chunks) {
         const int c = dir ? n_chunks - 1 - k : k;
-        buf[u] = base[int64_t(c) * cstride];
+        buf[u] = __builtin_nontemporal_load(&base[int64_t(c) * cstride]);
         g[u] = dec[int64_t(c) * Hs];
       }
     }
@@ -671,7 +672,7 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ st
         VT o;
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = from_f32<TS>(hv[e]);
-        base[int64_t(c) * cstride] = o;
+        __builtin_nontemporal_store(o, &base[int64_t(c) * cstride]);
 #pragma unroll
         for (int e = 0; e < E; ++e) hv[e] = g[u] * hv[e] + to_f32(buf[u][e]);
       }

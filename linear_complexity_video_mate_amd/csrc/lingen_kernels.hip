@@ -200,6 +200,32 @@ struct StageT {
   }
 };
 
+// Row-major LDS tile of 128-byte rows (ROWLEN elements) with the 16-byte
+// chunks of row r permuted as chunk ^ (r mod 8): row-contiguous 16-byte
+// stores, 16-byte row reads and the transposing reads below all touch
+// distinct banks.  Direct global-to-LDS loads fill it 64 chunks (8 rows) per
+// instruction, each lane fetching the source chunk that lands in its slot.
+template <typename TS, int ROWLEN>
+struct KvTile {
+  static constexpr int VEC = 16 / int(sizeof(TS));
+  static_assert(ROWLEN / VEC == 8, "rows of eight 16-byte chunks");
+  __device__ static __forceinline__ int at(int row, int col) {
+    return row * ROWLEN + ((((col / VEC) ^ (row & 7)) * VEC) | (col % VEC));
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) const __bf16 lds_bf16;
+// Transposing LDS load (16-bit elements): within each group of 16 lanes,
+// lane i receives element (i mod 4) of the 8-byte chunk read by lane
+// 4r + i/4, in slot r.  Takes an LDS-space pointer so that constant parts
+// of the address fold into the instruction's offset field.
+__device__ __forceinline__ bf16x4 lds_read_tr(lds_bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Two consecutive elements of one LDS row (4-byte aligned for bf16, 8 for
 // fp32): from values already in the element type, or rounded from fp32.
@@ -723,17 +749,18 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   constexpr int KI = F::K;
   using TN = Tile<MT, N>;     // rows of N: B rows and the entering states
   constexpr int NP = TN::LD;
-  constexpr int QP = Q + LdsPad<MT>::v;
   constexpr int VEC = Vec16<TS>::n;
   constexpr bool kBf16 = std::is_same<MT, __bf16>::value;
   static_assert((N % KI == 0 && Q % 32 == 0) || !kBf16, "bf16 tiles need Q multiple of 32");
   // One LDS region, used first for the B rows of the chunk (to form G^T)
-  // and then, per head, for x^T and the two entering states.
-  constexpr int HEAD_ELEMS = P * QP + 2 * P * NP;
+  // and then, per head, for x (row-major [Q][P], read transposed for the
+  // MFMA A operand) and the two entering states.
+  using TX = KvTile<MT, P>;
+  constexpr int HEAD_ELEMS = Q * P + 2 * P * NP;
   constexpr int U_ELEMS = HEAD_ELEMS > Q * NP ? HEAD_ELEMS : Q * NP;
   __shared__ __attribute__((aligned(16))) MT sU[U_ELEMS];
-  MT* sXt = sU;
-  MT* sHf = sXt + P * QP;
+  MT* sX = sU;
+  MT* sHf = sX + Q * P;
   MT* sHb = sHf + P * NP;
   MT* sBr = sU;
   __shared__ ChunkSched<Q> cs;
@@ -804,13 +831,9 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 
   auto do_head = [&](int hh, HeadBuf& buf) {
     const int h = h0 + hh;
-    // Stage x_h (transposed) and the two entering states of this head.
+    // Stage x_h and the two entering states of this head.
     buf.xs.use([&](int u, uint4 raw) {
-      const int s = u / (P / VEC), p0 = (u % (P / VEC)) * VEC;
-      Vec16<TS> v;
-      v.u = raw;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) sXt[(p0 + e) * QP + s] = v.e[e];
+      *reinterpret_cast<uint4*>(&sX[TX::at(u / (P / VEC), (u % (P / VEC)) * VEC)]) = raw;
     });
     buf.hfs.use([&](int u, uint4 raw) {
       *reinterpret_cast<uint4*>(&sHf[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
@@ -896,9 +919,12 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
         for (int pj = 0; pj < Cfg::P_PER; ++pj) {
           const int pt = wpw + pj * Cfg::WPW;
           if (pt < Cfg::PT) {
-            const __bf16* xr = &sXt[(pt * 16 + r16) * QP + k2 * 32 + grp * 4];
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
+            // x^T fragment (row p = pt*16 + r16) by transposing reads of the
+            // row-major tile: lane group g gets s = 32k + 4g + {0..3} and
+            // 32k + 16 + 4g + {0..3}.
+            lds_bf16* xr = (lds_bf16*)(sX) + TX::at(k2 * 32 + 4 * grp + (r16 >> 2), pt * 16 + 4 * (r16 & 3));
+            const bf16x4 lo = lds_read_tr(xr);
+            const bf16x4 hi = lds_read_tr(xr + 16 * P);
             acc[pj] = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), bm, acc[pj]);
           }
         }
@@ -914,7 +940,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
           for (int pj = 0; pj < Cfg::P_PER; ++pj) {
             const int pt = wpw + pj * Cfg::WPW;
             if (pt < Cfg::PT)
-              acc[pj] = mma(to_f32(sXt[(pt * 16 + r16) * QP + st * 16 + grp * 4 + r]), mv[r], acc[pj]);
+              acc[pj] = mma(to_f32(sX[TX::at(st * 16 + grp * 4 + r, pt * 16 + r16)]), mv[r], acc[pj]);
           }
       }
     }
@@ -936,9 +962,10 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       // Lane holds Y^T[p][t] for p = pt*16 + 4*grp + r.
       const int p0 = pt * 16 + grp * 4;
       float o[4];
+      const MT* xt = &sX[TX::at(t, p0)];    // x_t[p0 .. p0+3]
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        o[r] = acc[pj][r] + ef * zf[r] + eb * zb[r] + twoD * to_f32(sXt[(p0 + r) * QP + t]);
+        o[r] = acc[pj][r] + ef * zf[r] + eb * zb[r] + twoD * to_f32(xt[r]);
       TS* dst = y + tok_t * (int64_t(Hs) * P) + int64_t(h) * P + p0;
       if constexpr (kBf16) {
         bf16x4 ov;
@@ -999,17 +1026,6 @@ struct AttnCfg {
   static_assert(UNITS % (NWAVE * 64) == 0, "whole wave-wide LDS loads per tile");
 };
 
-// K and V tiles in LDS: row-major [NWIN][DH] with the 16-byte chunks of row r
-// permuted as chunk ^ (r mod 8).  One direct global-to-LDS load instruction
-// fills 64 consecutive chunks (8 rows), each lane fetching the source chunk
-// that lands in its slot.
-template <typename TS, int DH>
-struct KvTile {
-  static constexpr int VEC = 16 / int(sizeof(TS));
-  __device__ static __forceinline__ int at(int row, int col) {
-    return row * DH + ((((col / VEC) ^ (row & 7)) * VEC) | (col % VEC));
-  }
-};
 
 // 16-byte direct global-to-LDS load: lane l's chunk lands at lds_wave_base +
 // 16*l (the base must be the same for all lanes of the wave).  Kept out of
@@ -1020,17 +1036,6 @@ __device__ __forceinline__ void lds_load16(const void* src, void* lds_wave_base)
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) const __bf16 lds_bf16;
-// Transposing LDS load (16-bit elements): within each group of 16 lanes,
-// lane i receives element (i mod 4) of the 8-byte chunk read by lane
-// 4r + i/4, in slot r.  Takes an LDS-space pointer so that constant parts
-// of the address fold into the instruction's offset field.
-__device__ __forceinline__ bf16x4 lds_read_tr(lds_bf16* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
 
 template <typename TS, int DH, int NWIN, bool ACCUMULATE>
 __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_window_kernel(

@@ -179,6 +179,18 @@ def test_mate_single_frame(layer):
     _mate_case(CONFIGS[0].with_(T=1, H=8, W=8, win=(1, 4, 8)), 22, layer)
 
 
+@pytest.mark.parametrize("heads,layer", [(3, 1), (5, 2)])
+def test_mate_odd_head_groups_fp32(heads, layer):
+    # 3 and 5 heads: chunk workgroups take all heads at once (an odd group)
+    _mate_case(CONFIGS[0].with_(ssd_heads=heads, attn_heads=heads), 23, layer)
+
+
+@pytest.mark.parametrize("heads,layer", [(10, 3), (12, 0)])
+def test_mate_other_head_groups_bf16(heads, layer):
+    # 10 heads: groups of 10 (output) and 5 (states); 12 heads: 12 and 6
+    _mate_case(CONFIGS[1].with_(ssd_heads=heads, attn_heads=heads), 24, layer)
+
+
 @pytest.mark.parametrize("A_value", [0.0, -1.0e4])
 def test_mate_decay_extremes(A_value):
     # A = 0: no decay at all (plain cumulative sums); A = -1e4: every decay

@@ -92,8 +92,10 @@ def kernel_work(s):
         "ssd_chunk_state": dict(bytes=x + dt + bc + states + nc * Hs * 4,
                                 flops=2 * 2 * nc * Hs * Q * N * P),
         "ssd_state_pass": dict(bytes=2 * states + nc * Hs * 4, flops=2 * states // 4),
+        # C.B^T once per chunk (shared by the heads), then per head the masked
+        # in-chunk product and the two inter-chunk read-outs
         "ssd_chunk_out": dict(bytes=x + dt + 2 * bc + states + y,
-                              flops=nc * Hs * (2 * Q * Q * N + 2 * Q * Q * P + 2 * 2 * Q * N * P)),
+                              flops=nc * 2 * Q * Q * N + nc * Hs * (2 * Q * Q * P + 2 * 2 * Q * N * P)),
         "tesa_window": dict(bytes=qkv + 2 * y, flops=4 * L * nw * d * Ha),
     }
     if s.n_review:

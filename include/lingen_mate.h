@@ -46,9 +46,10 @@
  * - Every call validates its arguments on the host before it touches the GPU
  *   and returns a negative lingen_status on failure, with nothing enqueued.
  *   Device work is enqueued on `stream` and the call returns without waiting;
- *   a launch failure is reported as LINGEN_ERR_HIP.  The library keeps no
- *   mutable global state; concurrent calls on different streams are safe if
- *   they use different outputs and workspaces.
+ *   a launch failure is reported as LINGEN_ERR_HIP.  The only state the
+ *   library keeps is a per-device cache of the compute-unit count (it sizes
+ *   the persistent attention grid); concurrent calls on different streams
+ *   are safe if they use different outputs and workspaces.
  */
 #ifndef LINGEN_MATE_H
 #define LINGEN_MATE_H

@@ -34,6 +34,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -1341,15 +1342,19 @@ int hip_status() {
 
 RmsMap make_rms(const lingen_mate_shape* s, int mode) { return RmsMap{mode, s->T, s->H, s->W}; }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device (the only state
+// the library keeps; concurrent first calls store the same value).
 int compute_units() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

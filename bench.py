@@ -32,7 +32,17 @@ METRIC = "MATE fwd tokens/s (bidir SSD + TESA) at 1 GPU; % MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 STAGES = ("review", "ssd_chunk_state", "ssd_state_pass", "ssd_chunk_out", "tesa_window")
-KERNEL_SRC = os.path.join(ROOT, "linear_complexity_video_mate_amd", "csrc", "lingen_kernels.hip")
+# Sources that define the mixer's kernels (a traffic record is valid only for them as they stand).
+KERNEL_SRCS = [os.path.join(ROOT, "linear_complexity_video_mate_amd", "csrc", n)
+               for n in ("lingen_kernels.hip", "lingen_device.h")]
+
+
+def kernel_source_sha256() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 # ---------------------------------------------------------------------------
@@ -122,8 +132,7 @@ def traffic_for(kernel: str, workload: str):
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != src_hash or rec.get("workload") != workload:
+    if rec.get("kernel_source_sha256") != kernel_source_sha256() or rec.get("workload") != workload:
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
@@ -202,7 +211,7 @@ def record_traffic(mix_fetch, mix_write, copy_fetch, copy_write, config=2):
         kernels[name] = {"read_bytes": round(rd), "write_bytes": round(wr), "bytes_per_launch": round(rd + wr)}
     rec = {
         "workload": CONFIG_NOTES[config],
-        "kernel_source_sha256": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest(),
+        "kernel_source_sha256": kernel_source_sha256(),
         "calibration": {"FETCH_SIZE_scale": round(fcal, 4), "WRITE_SIZE_scale": round(wcal, 4),
                         "copy": "bench.py --copy-gib 1 (1 GiB read + 1 GiB written per launch)"},
         "counters": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, each its own run",
@@ -268,6 +277,91 @@ def gather_modes(args, mate, torch):
     return 0
 
 
+def library_attention(torch, qkv, steps, flops, timed):
+    """Context for the dense kernel: torch's fused scaled_dot_product_attention
+    on the same tensors, restricted to its flash / memory-efficient backends
+    (never the unfused math path).  Returns its latency, or why it could not
+    run."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    q, k, v = (t.transpose(1, 2).contiguous() for t in qkv)      # [batch, heads, L, d]
+    for backend in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            with sdpa_kernel([backend]):
+                ms = timed(lambda i: F.scaled_dot_product_attention(q, k, v), steps, 1)
+        except RuntimeError as err:
+            last = f"{backend.name}: {str(err).splitlines()[0][:200]}"
+            continue
+        tflops = flops / (ms / 1e3) / 1e12
+        return {"op": "torch.nn.functional.scaled_dot_product_attention", "backend": backend.name,
+                "ms": round(ms, 3), "TFLOP/s": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    return {"op": "torch.nn.functional.scaled_dot_product_attention", "unavailable": last}
+
+
+def dense_compare(args, mate, torch):
+    """The quadratic mixer MATE replaces, at the workload's L, heads and head
+    size: dense softmax attention over all tokens (lingen_dense_attn_fwd)
+    against the MATE forward (lingen_mate_fwd, layer_idx cycling 0..3), both
+    timed with events on the launch stream in one run; prints their
+    latencies, the dense kernel's MFMA rate and the latency and FLOP ratios."""
+    from mate_inputs import CONFIGS, CONFIG_NOTES, make_inputs
+
+    s = CONFIGS[args.config]
+    if s.dtype != "bf16" or s.attn_headdim != 64:
+        print("--dense needs a bf16 workload with 64-wide attention heads", file=sys.stderr)
+        return 2
+    print(f"[bench] dense comparison: generating inputs, {s.L} tokens", file=sys.stderr, flush=True)
+    inp = make_inputs(s, args.config, threads=16)
+    d = {n: inp.torch(n, "cuda") for n in ("x", "dt", "A", "B", "C", "D", "q", "k", "v")}
+    del inp
+    mate_args = [d[n] for n in ("x", "dt", "A", "B", "C", "D", "q", "k", "v")]
+    ws = torch.empty(mate.lingen_mate_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    y = torch.empty((1, s.L, s.d_inner), dtype=torch.bfloat16, device="cuda")
+    qkv = [d[n].view(1, s.L, s.attn_heads, s.attn_headdim) for n in ("q", "k", "v")]
+    o = torch.empty_like(qkv[0])
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    dense_steps = max(1, min(args.steps, 10))
+    print(f"[bench] dense attention: {dense_steps} launches", file=sys.stderr, flush=True)
+    dense_ms = timed(lambda i: mate.lingen_dense_attn_fwd(*qkv, out=o), dense_steps, 1)
+    print(f"[bench] MATE forward: {args.steps} steps", file=sys.stderr, flush=True)
+    mate_ms = timed(lambda i: mate.lingen_mate_fwd(*mate_args, i % 4, s, out=y, workspace=ws), args.steps,
+                    args.warmup)
+    dense_flops = 4 * s.L * s.L * s.attn_headdim * s.attn_heads
+    library = None
+    if args.sdpa:
+        library = library_attention(torch, qkv, dense_steps, dense_flops, timed)
+    work = kernel_work(s)
+    mate_flops = sum(w["flops"] for w in work.values())
+    tflops = dense_flops / (dense_ms / 1e3) / 1e12
+    out = {
+        "comparison": "dense softmax attention vs MATE forward, same tokens / heads / head size",
+        "workload": CONFIG_NOTES[args.config],
+        "tokens": s.L,
+        "attention": {"heads": s.attn_heads, "d": s.attn_headdim},
+        "dense_attn": {"ms": round(dense_ms, 3), "launches": dense_steps, "flops": dense_flops,
+                       "TFLOP/s": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
+        "mate_fwd": {"ms": round(mate_ms, 4), "steps": args.steps, "flops": mate_flops},
+        "library_dense_attn": library,
+        "latency_ratio_dense_over_mate": round(dense_ms / mate_ms, 2),
+        "flop_ratio_dense_over_mate": round(dense_flops / mate_flops, 2),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------------------
 
 def main(argv=None):
@@ -286,6 +380,12 @@ def main(argv=None):
     ap.add_argument("--gather", action="store_true",
                     help="instead of the mixer, time the scan-order gather of x-sized rows in each of the "
                          "four scan orders on the workload's grid")
+    ap.add_argument("--sdpa", action="store_true",
+                    help="with --dense, also time torch's fused scaled_dot_product_attention on the same "
+                         "tensors, as context for the dense kernel")
+    ap.add_argument("--dense", action="store_true",
+                    help="instead of the benchmark line, time dense softmax attention over all tokens (the "
+                         "quadratic mixer MATE replaces) against the MATE forward on the workload")
     args = ap.parse_args(argv)
 
     if args.record_traffic:
@@ -310,6 +410,8 @@ def main(argv=None):
         return copy_calibration(args, mate, torch)
     if args.gather:
         return gather_modes(args, mate, torch)
+    if args.dense:
+        return dense_compare(args, mate, torch)
     s = CONFIGS[args.config]
     workload = CONFIG_NOTES[args.config]
     print(f"[bench] generating inputs: {workload}, {s.L} tokens", file=sys.stderr, flush=True)

@@ -182,6 +182,26 @@ int lingen_mate_fwd_events(const void* x, const float* dt, const float* A, const
                            void* workspace, size_t workspace_bytes, hipStream_t stream,
                            hipEvent_t* events);
 
+/* Dense softmax attention over all L tokens of each sequence, per head:
+ *     o_i = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j,   j = 0 .. L-1,
+ * with no mask and no bias.  This is the quadratic self-attention of the DiT
+ * baseline that MATE replaces (abstract of the first page above: linear
+ * complexity in place of DiT self-attention; page "视频生成模子太贵太慢如何办？",
+ * section 评估: latency and FLOPs against the attention model), provided so
+ * that the two mixers can be timed at the same L, heads and head size.  It is
+ * not used by lingen_mate_fwd.
+ *   q, k, v, o: device, [batch, L, heads, head_dim], dtype; o must not alias
+ *               the inputs.
+ *   dtype:      LINGEN_F32 or LINGEN_BF16 (LINGEN_ERR_DTYPE otherwise).
+ * Compiled for LINGEN_BF16 with head_dim 64 (fp32 accumulation and softmax);
+ * other valid combinations return LINGEN_ERR_UNSUPPORTED.  batch, L or heads
+ * equal to 0 is a no-op that does not look at the pointers; negative sizes,
+ * batch or heads above 65535 and more than 2^40 elements per tensor give
+ * LINGEN_ERR_SHAPE. */
+int lingen_dense_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                          int32_t batch, int32_t L, int32_t heads, int32_t head_dim,
+                          int32_t dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,7 @@ from .binding import (
     LingenError,
     STATUS_NAMES,
     lib,
+    lingen_dense_attn_fwd,
     lingen_ma_fwd,
     lingen_mate_fwd,
     lingen_mate_fwd_events,
@@ -35,6 +36,7 @@ __all__ = [
     "LingenError",
     "STATUS_NAMES",
     "lib",
+    "lingen_dense_attn_fwd",
     "lingen_ma_fwd",
     "lingen_mate_fwd",
     "lingen_mate_fwd_events",

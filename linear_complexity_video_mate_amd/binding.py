@@ -42,6 +42,7 @@ EXPORTS = (
     "lingen_te_fwd",
     "lingen_mate_fwd",
     "lingen_mate_fwd_events",
+    "lingen_dense_attn_fwd",
 )
 
 
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
         "lingen_te_fwd": ([P, P, P, I32, SP, P, P], ctypes.c_int),
         "lingen_mate_fwd": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_mate_fwd_events": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P, P], ctypes.c_int),
+        "lingen_dense_attn_fwd": ([P, P, P, P, I32, I32, I32, I32, I32, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -314,4 +316,21 @@ def lingen_mate_fwd_events(x, dt, A, B, C, D, q, k, v, layer_idx: int, shape, ev
     ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(int(e)) for e in events])
     _check("lingen_mate_fwd_events", lib().lingen_mate_fwd_events(
         *args, int(layer_idx), ctypes.byref(cs), py, pw, nw, _stream(), ctypes.cast(ev, ctypes.c_void_p)))
+    return out
+
+
+def lingen_dense_attn_fwd(q, k, v, out=None):
+    """Dense softmax attention over all tokens; q, k, v [batch, L, heads, d]
+    GPU tensors (bf16 or fp32); returns o of the same shape."""
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must be [batch, L, heads, d] tensors of one shape")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"q must be bfloat16 or float32 (got {q.dtype})")
+    batch, L, heads, d = (int(n) for n in q.shape)
+    code = LINGEN_BF16 if q.dtype == torch.bfloat16 else LINGEN_F32
+    if out is None:
+        out = torch.empty_like(q)
+    args = [_need(t, name, q.dtype, q.numel()) for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+    _check("lingen_dense_attn_fwd", lib().lingen_dense_attn_fwd(*args, batch, L, heads, d, code, _stream()))
     return out

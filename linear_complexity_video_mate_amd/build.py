@@ -22,7 +22,7 @@ LIB_NAME = "liblingen_mate.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = os.environ.get("LINGEN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["lingen_host.cpp", "lingen_kernels.hip"]
+SOURCES = ["lingen_host.cpp", "lingen_kernels.hip", "dense_attn.hip"]
 
 COMMON_FLAGS = [
     "-O3",
@@ -45,9 +45,16 @@ def _hipcc() -> str:
     return path
 
 
+# Per-source additions.  The dense attention kernel never produces or
+# consumes NaN (masked scores are -inf, exp2(-inf) = 0), so it is built
+# without NaN semantics: its running maxima then need no NaN-quieting
+# instructions around v_max.
+SOURCE_FLAGS = {"dense_attn.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:

@@ -38,66 +38,14 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "lingen_device.h"
 #include "lingen_internal.h"
 
 namespace lingen {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-// 2^x with the hardware instruction alone (no range reduction wrapper):
-// exp2(-inf) = 0, and results below the normal range come out as zero or
-// denormal, which is far below every tolerance the callers work to.
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Workgroup barrier for LDS traffic only.  The waves of a workgroup exchange
-// data through LDS alone (never through global memory), so the barrier waits
-// for this wave's LDS accesses but leaves its global loads and stores in
-// flight: prefetches issued before a barrier keep streaming across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // ---------------------------------------------------------------------------
 // Small device helpers
 // ---------------------------------------------------------------------------
-
-__device__ __forceinline__ float to_f32(float v) { return v; }
-__device__ __forceinline__ float to_f32(__bf16 v) { return static_cast<float>(v); }
-template <typename T> __device__ __forceinline__ T from_f32(float v);
-template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
-template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return static_cast<__bf16>(v); }
-
-// MFMA 16x16 tiles.  Output layout (both variants): lane l holds
-// D[4*(l/16) + r][l%16] in element r.  Operand layout: lane l supplies row
-// l%16 of A and column l%16 of B, for the k values of its lane group l/16.
-__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Operand fragment of one MFMA from a k-contiguous row: 8 bf16 (k = 8*g ..
-// 8*g+7) or one float (k = g), g = lane/16.
-template <typename MT> struct Frag;
-template <> struct Frag<__bf16> {
-  using type = bf16x8;
-  static constexpr int K = 32;
-  __device__ static type load(const __bf16* row, int lane) {
-    return *reinterpret_cast<const bf16x8*>(row + (lane >> 4) * 8);
-  }
-};
-template <> struct Frag<float> {
-  using type = float;
-  static constexpr int K = 4;
-  __device__ static type load(const float* row, int lane) { return row[lane >> 4]; }
-};
 
 // Element padding of k-contiguous LDS rows (keeps 16-byte alignment and
 // spreads the 16 rows one fragment load touches over different banks).
@@ -200,32 +148,6 @@ struct StageT {
     }
   }
 };
-
-// Row-major LDS tile of 128-byte rows (ROWLEN elements) with the 16-byte
-// chunks of row r permuted as chunk ^ (r mod 8): row-contiguous 16-byte
-// stores, 16-byte row reads and the transposing reads below all touch
-// distinct banks.  Direct global-to-LDS loads fill it 64 chunks (8 rows) per
-// instruction, each lane fetching the source chunk that lands in its slot.
-template <typename TS, int ROWLEN>
-struct KvTile {
-  static constexpr int VEC = 16 / int(sizeof(TS));
-  static_assert(ROWLEN / VEC == 8, "rows of eight 16-byte chunks");
-  __device__ static __forceinline__ int at(int row, int col) {
-    return row * ROWLEN + ((((col / VEC) ^ (row & 7)) * VEC) | (col % VEC));
-  }
-};
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) const __bf16 lds_bf16;
-// Transposing LDS load (16-bit elements): within each group of 16 lanes,
-// lane i receives element (i mod 4) of the 8-byte chunk read by lane
-// 4r + i/4, in slot r.  Takes an LDS-space pointer so that constant parts
-// of the address fold into the instruction's offset field.
-__device__ __forceinline__ bf16x4 lds_read_tr(lds_bf16* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Two consecutive elements of one LDS row (4-byte aligned for bf16, 8 for
@@ -1026,17 +948,6 @@ struct AttnCfg {
   static_assert(CPR == 8, "K / V rows of 128 bytes");
   static_assert(UNITS % (NWAVE * 64) == 0, "whole wave-wide LDS loads per tile");
 };
-
-
-// 16-byte direct global-to-LDS load: lane l's chunk lands at lds_wave_base +
-// 16*l (the base must be the same for all lanes of the wave).  Kept out of
-// the kernel templates, whose host-side stubs are not emitted otherwise.
-__device__ __forceinline__ void lds_load16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
-
 
 template <typename TS, int DH, int NWIN, bool ACCUMULATE>
 __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_window_kernel(

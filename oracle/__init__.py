@@ -35,6 +35,8 @@ from .mate_oracle import (
     tesa_window_keys,
     tesa,
     tesa_for_queries,
+    dense_attention,
+    dense_attention_for_queries,
     mate_fwd,
     ma_fwd,
 )
@@ -51,6 +53,8 @@ __all__ = [
     "tesa_window_keys",
     "tesa",
     "tesa_for_queries",
+    "dense_attention",
+    "dense_attention_for_queries",
     "mate_fwd",
     "ma_fwd",
 ]

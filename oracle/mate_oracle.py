@@ -297,6 +297,51 @@ def tesa_for_queries(q, k, v, T: int, H: int, W: int, win, shift,
 
 
 # --------------------------------------------------------------------------
+# Dense attention: the quadratic mixer MATE replaces.
+# --------------------------------------------------------------------------
+
+
+def dense_attention_for_queries(q, k, v, query_idx: Sequence[int],
+                                head_block: int = 4) -> np.ndarray:
+    """Softmax attention of the selected queries over ALL L tokens, per head:
+    o_i = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j, j = 0..L-1; returns
+    [len(query_idx), Ha, d].
+
+    [ABS] (MATE replaces DiT's self-attention, whose cost is quadratic in the
+    token count) and [ART] 评估 (latency and FLOPs measured against the
+    attention model).  Readings taken: the same scale, no mask and no bias as
+    TESA, i.e. TESA with one window holding every token.  Heads are processed
+    ``head_block`` at a time to bound memory.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    query_idx = np.asarray(query_idx, dtype=np.int64)
+    d = q.shape[-1]
+    Ha = q.shape[1]
+    out = np.empty((query_idx.size, Ha, d), dtype=np.float64)
+    for h0 in range(0, Ha, head_block):
+        hs = slice(h0, min(Ha, h0 + head_block))
+        qh = q[query_idx, hs].transpose(1, 0, 2)           # [hb, nq, d]
+        kh = k[:, hs].transpose(1, 2, 0)                   # [hb, d, L]
+        vh = v[:, hs].transpose(1, 0, 2)                   # [hb, L, d]
+        s = (qh @ kh) / math.sqrt(d)                        # [hb, nq, L]
+        s -= s.max(axis=-1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=-1, keepdims=True)
+        out[:, hs] = (p @ vh).transpose(1, 0, 2)
+    return out
+
+
+def dense_attention(q, k, v) -> np.ndarray:
+    """Dense softmax attention of every token over every token, per head,
+    [L, Ha, d]; the definition of ``dense_attention_for_queries`` applied to
+    all queries."""
+    L = np.asarray(q).shape[0]
+    return dense_attention_for_queries(q, k, v, np.arange(L))
+
+
+# --------------------------------------------------------------------------
 # The whole mixer.
 # --------------------------------------------------------------------------
 

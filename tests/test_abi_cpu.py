@@ -164,6 +164,31 @@ def test_branch_entry_points_reject_before_launch(L):
     assert L.lingen_rms_index_device(0, 2, 2, 2, ctypes.c_void_p(MISALIGNED), None) == -4
 
 
+def test_dense_attention_rejects_before_launch(L):
+    F = ctypes.c_void_p(FAKE)
+    Z = ctypes.c_void_p(0)
+    M = ctypes.c_void_p(MISALIGNED)
+    call = L.lingen_dense_attn_fwd
+    assert call(F, F, F, F, 1, 64, 2, 64, 7, None) == -3
+    assert call(F, F, F, F, 1, -1, 2, 64, 1, None) == -2
+    assert call(F, F, F, F, 1, 64, 2, 0, 1, None) == -2
+    assert call(F, F, F, F, 1, 64, 70000, 64, 1, None) == -2
+    assert call(F, F, F, F, 1 << 20, 1 << 20, 2, 64, 1, None) == -2
+    assert call(F, F, F, F, 1, 64, 2, 32, 1, None) == -7
+    assert call(F, F, F, F, 1, 64, 2, 64, 0, None) == -7
+    for i in range(4):
+        p = [F] * 4
+        p[i] = Z
+        assert call(*p, 1, 64, 2, 64, 1, None) == -1, i
+        p[i] = M
+        assert call(*p, 1, 64, 2, 64, 1, None) == -4, i
+    # empty problems are valid no-ops (nothing is launched, pointers unused)
+    assert call(F, F, F, F, 1, 0, 2, 64, 1, None) == 0
+    assert call(Z, Z, Z, Z, 1, 0, 2, 64, 1, None) == 0
+    assert call(F, F, F, F, 0, 64, 2, 64, 1, None) == 0
+    assert call(F, F, F, F, 1, 64, 0, 64, 1, None) == 0
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     import linear_complexity_video_mate_amd.binding as b
     monkeypatch.setattr(b, "_lib", None)

@@ -90,7 +90,11 @@ typedef struct {
 /* Compiled kernel families (anything else returns LINGEN_ERR_UNSUPPORTED):
  *   scan:      (dtype, P, N, Q) in { (F32, 32, 16, 16), (BF16, 64, 64, 64),
  *                                    (BF16, 64, 128, 128) }
- *   attention: (dtype, d, win_t*win_h*win_w) in { (F32, 32, 32), (BF16, 64, 256) }
+ *   attention: (dtype, d, win_t*win_h*win_w) in { (F32, 32, 32), (BF16, 64, 256),
+ *                                                 (BF16, 64, 27) }
+ * Odd window sizes (the 3x3x3 example of the TESA section) shift by the
+ * floored half window, 1 per axis of 3, the grid offset moving forward:
+ * along an axis of length n the shifted cut points are s, s+w, s+2w, ...
  */
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -156,6 +160,23 @@ int lingen_ma_fwd(const void* x, const float* dt, const float* A, const void* B,
  * cut, not wrapped.  Scale 1/sqrt(d).  y_te: device, layout of y. */
 int lingen_te_fwd(const void* q, const void* k, const void* v, int32_t shifted,
                   const lingen_mate_shape* shape, void* y_te, hipStream_t stream);
+
+/* TE branch with an explicit window-grid offset and either reading of a
+ * shifted partition (page "LinGen：基于Mamba机制的线性复杂度高清长视频生成框架",
+ * section 关键算法创新 > TESA says only that plain and shifted windows alternate):
+ *   shift_t, shift_h, shift_w  grid offset per axis, 0 <= shift < window
+ *                              (lingen_te_fwd uses window/2 or 0);
+ *   masked = 1                 the border pieces cut off by the offset are
+ *                              windows of their own (Swin's masked roll; what
+ *                              lingen_te_fwd and lingen_mate_fwd compute);
+ *   masked = 0                 cyclic windows: the tokens that roll past the
+ *                              end join the last window of that axis, so every
+ *                              window holds win_t*win_h*win_w tokens.
+ * Other arguments and errors as lingen_te_fwd, plus LINGEN_ERR_SHAPE for an
+ * offset outside [0, window) or masked not 0 or 1. */
+int lingen_te_fwd_shift(const void* q, const void* k, const void* v,
+                        int32_t shift_t, int32_t shift_h, int32_t shift_w, int32_t masked,
+                        const lingen_mate_shape* shape, void* y_te, hipStream_t stream);
 
 /* The mixer: y = MA(mode = layer_idx mod 4) + TE(shifted = layer_idx odd).
  * layer_idx >= 0.  y: device, [batch, L, Hs*P] dtype; it is also used as the

@@ -40,6 +40,7 @@ EXPORTS = (
     "lingen_ssd_chunk_states",
     "lingen_ma_fwd",
     "lingen_te_fwd",
+    "lingen_te_fwd_shift",
     "lingen_mate_fwd",
     "lingen_mate_fwd_events",
     "lingen_dense_attn_fwd",
@@ -83,6 +84,7 @@ def lib() -> ctypes.CDLL:
         "lingen_ssd_chunk_states": ([P, P, P, P, I32, SP, P, P, P, SZ, P], ctypes.c_int),
         "lingen_ma_fwd": ([P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_te_fwd": ([P, P, P, I32, SP, P, P], ctypes.c_int),
+        "lingen_te_fwd_shift": ([P, P, P, I32, I32, I32, I32, SP, P, P], ctypes.c_int),
         "lingen_mate_fwd": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_mate_fwd_events": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P, P], ctypes.c_int),
         "lingen_dense_attn_fwd": ([P, P, P, P, I32, I32, I32, I32, I32, P], ctypes.c_int),
@@ -273,6 +275,25 @@ def lingen_te_fwd(q, k, v, shifted: int, shape, out=None):
     args = [_need(q, "q", td, n["q"]), _need(k, "k", td, n["q"]), _need(v, "v", td, n["q"])]
     py = _need(out, "out", td, n["y"])
     _check("lingen_te_fwd", lib().lingen_te_fwd(*args, int(shifted), ctypes.byref(cs), py, _stream()))
+    return out
+
+
+def lingen_te_fwd_shift(q, k, v, shift, masked: int, shape, out=None):
+    """TE branch with window-grid offset ``shift`` = (st, sh, sw) and
+    ``masked`` = 1 (border pieces are windows of their own) or 0 (cyclic
+    windows); returns y_te [batch, L, Ha*d]."""
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    torch = _torch()
+    L = shape.T * shape.H * shape.W
+    if out is None:
+        out = torch.empty((shape.batch, L, shape.attn_heads * shape.attn_headdim), dtype=td, device="cuda")
+    args = [_need(q, "q", td, n["q"]), _need(k, "k", td, n["q"]), _need(v, "v", td, n["q"])]
+    py = _need(out, "out", td, n["y"])
+    st, sh, sw = (int(a) for a in shift)
+    _check("lingen_te_fwd_shift", lib().lingen_te_fwd_shift(*args, st, sh, sw, int(masked), ctypes.byref(cs), py,
+                                                            _stream()))
     return out
 
 

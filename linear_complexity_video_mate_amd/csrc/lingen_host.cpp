@@ -31,6 +31,7 @@ AttnFamily attn_family(const lingen_mate_shape* s) {
   const int64_t nw = int64_t(s->win_t) * s->win_h * s->win_w;
   if (s->dtype == LINGEN_F32 && s->attn_headdim == 32 && nw == 32) return ATTN_F32_D32_W32;
   if (s->dtype == LINGEN_BF16 && s->attn_headdim == 64 && nw == 256) return ATTN_BF16_D64_W256;
+  if (s->dtype == LINGEN_BF16 && s->attn_headdim == 64 && nw == 27) return ATTN_BF16_D64_W27;
   return ATTN_NONE;
 }
 

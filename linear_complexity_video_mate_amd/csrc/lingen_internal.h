@@ -24,7 +24,7 @@ struct WsLayout {
 
 // Which compiled kernel families a shape uses.
 enum ScanFamily { SCAN_F32_P32_N16_Q16 = 0, SCAN_BF16_P64_N64_Q64 = 1, SCAN_BF16_P64_N128_Q128 = 2, SCAN_NONE = -1 };
-enum AttnFamily { ATTN_F32_D32_W32 = 0, ATTN_BF16_D64_W256 = 1, ATTN_NONE = -1 };
+enum AttnFamily { ATTN_F32_D32_W32 = 0, ATTN_BF16_D64_W256 = 1, ATTN_BF16_D64_W27 = 2, ATTN_NONE = -1 };
 
 int validate_shape(const lingen_mate_shape* s);   // lingen_status
 int64_t tokens(const lingen_mate_shape* s);       // T*H*W

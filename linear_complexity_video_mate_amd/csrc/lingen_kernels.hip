@@ -913,10 +913,13 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 // of different wrap classes.  This is the border-cut partition of page
 // "LinGen：基于Mamba机制的线性复杂度高清长视频生成框架", section 关键算法创新 >
 // TESA (plain and shifted windows alternate), in Swin's roll-and-mask form.
-// Windows with no wrapped token skip the mask.
+// Windows with no wrapped token skip the mask.  With masking off the same
+// enumeration gives the cyclic reading of shifted windows (wrapped tokens
+// join the window they rolled into).  Window sizes that are not a multiple
+// of 32 tokens (3x3x3 on the same page) are padded to the next 32 slots.
 //
 // Work item = (window, head).  The grid is persistent (one workgroup per
-// CU); a workgroup walks its items in sequence with the K and V tiles of the
+// CU for 256-token windows); a workgroup walks its items in sequence with the K and V tiles of the
 // next item streaming into the second of two LDS buffers (direct
 // global-to-LDS loads, no registers) while the current one is computed, and
 // the next item's Q fragments in registers.  Per item and block of 64 keys
@@ -932,8 +935,9 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 struct WinGeom {
   int T, H, W;
   int wt, wh, ww;
-  int st, sh, sw;   // shift (0 on unshifted layers)
+  int st, sh, sw;   // grid offset per axis, 0 <= shift < window (0 on unshifted layers)
   int nwt, nwh, nww;  // windows per axis (T/wt, ...)
+  int masked;         // 1: wrapped tokens form windows of their own (Swin); 0: cyclic windows
 };
 
 template <typename TS, int DH, int NWIN>
@@ -949,7 +953,10 @@ struct AttnCfg {
   static_assert(UNITS % (NWAVE * 64) == 0, "whole wave-wide LDS loads per tile");
 };
 
-template <typename TS, int DH, int NWIN, bool ACCUMULATE>
+// NVALID = wt*wh*ww tokens of a window occupy the first NVALID of NWIN slots;
+// the remaining slots (odd window sizes) repeat the window's first token, and
+// their keys are masked and their query rows not stored.
+template <typename TS, int DH, int NWIN, int NVALID, bool ACCUMULATE>
 __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_window_kernel(
     const TS* __restrict__ q, const TS* __restrict__ k, const TS* __restrict__ v, WinGeom wg, int Ha,
     int n_items, TS* __restrict__ y) {
@@ -1005,7 +1012,10 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   };
   // Offsets of this thread's window slot (tid < NWIN) inside the window.
   static_assert(NWIN <= NTHR, "one window slot per thread");
-  const int slot_a = tid / (wg.wh * wg.ww), slot_b = (tid / wg.ww) % wg.wh, slot_c = tid % wg.ww;
+  static_assert(NVALID <= NWIN && NVALID > NWIN - 32, "padding below one 32-key block");
+  constexpr bool kPadded = NVALID < NWIN;
+  const int slot = tid < NVALID ? tid : 0;
+  const int slot_a = slot / (wg.wh * wg.ww), slot_b = (slot / wg.ww) % wg.wh, slot_c = slot % wg.ww;
   // Token index and wrap class of every slot of an item's window.
   auto item_tokens = [&](const ItemPos& p, int* tok, int* cls) {
     if (tid < NWIN) {
@@ -1015,7 +1025,9 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
       if (hh >= wg.H) { hh -= wg.H; cl |= 2; }
       if (w >= wg.W) { w -= wg.W; cl |= 1; }
       tok[tid] = (t * wg.H + hh) * wg.W + w;
-      cls[tid] = cl;
+      // Class 8 (padding) matches no query of the window; cyclic windows
+      // (masking off) put every real slot in class 0.
+      cls[tid] = (kPadded && tid >= NVALID) ? 8 : (wg.masked ? cl : 0);
     }
   };
   // The window holds wrapped tokens iff it is the last one along a shifted axis.
@@ -1095,7 +1107,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
         for (int et = 0; et < ET; ++et) yp[qi][et] = *reinterpret_cast<const YV*>(yrow + et * 16 + grp * 4);
       }
     }
-    const bool wrapped = item_wrapped(pos);
+    const bool wrapped = kPadded || (wg.masked && item_wrapped(pos));
     const int* cls = sCls[n % 3];
     int qcls[QTP];
 #pragma unroll
@@ -1114,8 +1126,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
 #pragma unroll
       for (int et = 0; et < ET; ++et) o[qi][et] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    static_assert(NWIN % 64 == 0 || !kBf16, "64-key blocks");
-    constexpr int SB = kBf16 ? 2 : 1;     // 32-key sub-blocks per block
+    constexpr int SB = (kBf16 && NWIN % 64 == 0) ? 2 : 1;     // 32-key sub-blocks per block
 #pragma unroll 1
     for (int jb = 0; jb < NWIN; jb += 32 * SB) {
 #pragma unroll
@@ -1210,6 +1221,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
       lt += __shfl_xor(lt, 16, 64);
       lt += __shfl_xor(lt, 32, 64);
       const float inv = __builtin_amdgcn_rcpf(lt);
+      if (kPadded && (wave + qi * Cfg::NWAVE) * 16 + r16 >= NVALID) continue;   // padding slot
       TS* yrow = y + int64_t(cur.tokq[qi]) * rowstride + int64_t(h) * DH;
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
@@ -1370,21 +1382,24 @@ int dispatch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, ch
   }
 }
 
-template <typename TS, int DH, int NWIN>
-int launch_te(const lingen_mate_shape* s, int shifted, const void* q, const void* k, const void* v, void* y,
-              int accumulate, hipStream_t st) {
+template <typename TS, int DH, int NWIN, int NVALID>
+int launch_te(const lingen_mate_shape* s, const int shift[3], int masked, const void* q, const void* k,
+              const void* v, void* y, int accumulate, hipStream_t st) {
   WinGeom g;
   g.T = s->T; g.H = s->H; g.W = s->W;
   g.wt = s->win_t; g.wh = s->win_h; g.ww = s->win_w;
-  g.st = shifted ? s->win_t / 2 : 0; g.sh = shifted ? s->win_h / 2 : 0; g.sw = shifted ? s->win_w / 2 : 0;
+  g.st = shift[0]; g.sh = shift[1]; g.sw = shift[2];
   g.nwt = s->T / s->win_t; g.nwh = s->H / s->win_h; g.nww = s->W / s->win_w;
+  g.masked = masked;
   const int64_t L = tokens(s);
   const int nwin = g.nwt * g.nwh * g.nww;
   const int64_t per = L * s->attn_heads * DH * elem_bytes(s);
   using Cfg = AttnCfg<TS, DH, NWIN>;
-  // Persistent grid: one workgroup per compute unit.
+  // Persistent grid: 16 waves per compute unit (one workgroup of the
+  // 256-slot windows, several of the small ones).
   const int ncu = compute_units();
   if (ncu < 1) return LINGEN_ERR_HIP;
+  const int64_t slots = int64_t(ncu) * (Cfg::NWAVE >= 16 ? 1 : 16 / Cfg::NWAVE);
   for (int b = 0; b < s->batch; ++b) {
     const int64_t off = int64_t(b) * per;
     const TS* qb = reinterpret_cast<const TS*>(static_cast<const char*>(q) + off);
@@ -1392,23 +1407,35 @@ int launch_te(const lingen_mate_shape* s, int shifted, const void* q, const void
     const TS* vb = reinterpret_cast<const TS*>(static_cast<const char*>(v) + off);
     TS* yb = reinterpret_cast<TS*>(static_cast<char*>(y) + off);
     const int items = nwin * s->attn_heads;
-    const int grid = items < ncu ? items : ncu;
+    const int grid = int(items < slots ? items : slots);
     if (accumulate)
-      tesa_window_kernel<TS, DH, NWIN, true><<<grid, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, items, yb);
+      tesa_window_kernel<TS, DH, NWIN, NVALID, true><<<grid, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads,
+                                                                                      items, yb);
     else
-      tesa_window_kernel<TS, DH, NWIN, false><<<grid, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, items, yb);
+      tesa_window_kernel<TS, DH, NWIN, NVALID, false><<<grid, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads,
+                                                                                       items, yb);
     if (hip_status()) return LINGEN_ERR_HIP;
   }
   return LINGEN_OK;
 }
 
-int dispatch_te(const lingen_mate_shape* s, int shifted, const void* q, const void* k, const void* v, void* y,
-                int accumulate, hipStream_t st) {
+// shift: grid offset per axis (0 <= shift < window); masked: 1 for Swin's
+// cut border windows, 0 for cyclic windows.
+int dispatch_te(const lingen_mate_shape* s, const int shift[3], int masked, const void* q, const void* k,
+                const void* v, void* y, int accumulate, hipStream_t st) {
   switch (attn_family(s)) {
-    case ATTN_F32_D32_W32: return launch_te<float, 32, 32>(s, shifted, q, k, v, y, accumulate, st);
-    case ATTN_BF16_D64_W256: return launch_te<__bf16, 64, 256>(s, shifted, q, k, v, y, accumulate, st);
+    case ATTN_F32_D32_W32: return launch_te<float, 32, 32, 32>(s, shift, masked, q, k, v, y, accumulate, st);
+    case ATTN_BF16_D64_W256: return launch_te<__bf16, 64, 256, 256>(s, shift, masked, q, k, v, y, accumulate, st);
+    case ATTN_BF16_D64_W27: return launch_te<__bf16, 64, 32, 27>(s, shift, masked, q, k, v, y, accumulate, st);
     default: return LINGEN_ERR_UNSUPPORTED;
   }
+}
+
+// Half-window offsets (floored) on shifted layers, none otherwise.
+void layer_shift(const lingen_mate_shape* s, int shifted, int shift[3]) {
+  shift[0] = shifted ? s->win_t / 2 : 0;
+  shift[1] = shifted ? s->win_h / 2 : 0;
+  shift[2] = shifted ? s->win_w / 2 : 0;
 }
 
 int check_all(std::initializer_list<const void*> ptrs) {
@@ -1519,7 +1546,21 @@ int lingen_te_fwd(const void* q, const void* k, const void* v, int32_t shifted, 
                   void* y_te, hipStream_t stream) {
   if (int rc = validate_shape(shape)) return rc;
   if (int rc = check_all({q, k, v, y_te})) return rc;
-  return dispatch_te(shape, shifted ? 1 : 0, q, k, v, y_te, 0, stream);
+  int shift[3];
+  layer_shift(shape, shifted ? 1 : 0, shift);
+  return dispatch_te(shape, shift, 1, q, k, v, y_te, 0, stream);
+}
+
+int lingen_te_fwd_shift(const void* q, const void* k, const void* v, int32_t shift_t, int32_t shift_h,
+                        int32_t shift_w, int32_t masked, const lingen_mate_shape* shape, void* y_te,
+                        hipStream_t stream) {
+  if (int rc = validate_shape(shape)) return rc;
+  if (shift_t < 0 || shift_t >= shape->win_t || shift_h < 0 || shift_h >= shape->win_h || shift_w < 0 ||
+      shift_w >= shape->win_w || (masked != 0 && masked != 1))
+    return LINGEN_ERR_SHAPE;
+  if (int rc = check_all({q, k, v, y_te})) return rc;
+  const int shift[3] = {shift_t, shift_h, shift_w};
+  return dispatch_te(shape, shift, masked, q, k, v, y_te, 0, stream);
 }
 
 static int mate_fwd_impl(const void* x, const float* dt, const float* A, const void* B, const void* C,
@@ -1531,11 +1572,12 @@ static int mate_fwd_impl(const void* x, const float* dt, const float* A, const v
   if (int rc = check_all({x, dt, A, B, C, D, q, k, v, y})) return rc;
   if (int rc = check_ws(shape, workspace, workspace_bytes)) return rc;
   const int mode = layer_idx % 4;
-  const int shifted = layer_idx % 2;
+  int shift[3];
+  layer_shift(shape, layer_idx % 2, shift);
   Args a{x, dt, A, B, C, D, q, k, v};
   if (int rc = mark(ev, 0, stream)) return rc;
   if (int rc = dispatch_ma(shape, mode, a, y, static_cast<char*>(workspace), stream, ev)) return rc;
-  if (int rc = dispatch_te(shape, shifted, q, k, v, y, 1, stream)) return rc;
+  if (int rc = dispatch_te(shape, shift, 1, q, k, v, y, 1, stream)) return rc;
   return mark(ev, 5, stream);
 }
 

@@ -203,7 +203,7 @@ def review_state(x, dt, A, B, C, T, H, W, rpool, rgrid):
 # --------------------------------------------------------------------------
 
 
-def tesa_window_keys(T: int, H: int, W: int, win, shift) -> np.ndarray:
+def tesa_window_keys(T: int, H: int, W: int, win, shift, cyclic: bool = False) -> np.ndarray:
     """Window key of every token, [L, 3] (canonical order).
 
     [ART] 要领 / [ZH] 关键算法创新: TESA attends inside small 3D windows whose
@@ -212,11 +212,21 @@ def tesa_window_keys(T: int, H: int, W: int, win, shift) -> np.ndarray:
     grid is offset by ``shift``; a token (t, h, w) belongs to window
     (floor((t-st)/wt), floor((h-sh)/wh), floor((w-sw)/ww)).  Tokens cut off at
     the borders form smaller windows of their own; nothing wraps around.
+
+    ``cyclic=True`` is the other reading of a shifted partition, not the one
+    the mixer uses: the offset grid wraps around each axis, window
+    (floor(((t-st) mod T)/wt), ...), so every window is whole (the axis
+    lengths must be multiples of the window).
     """
     wt, wh, ww = win
     st, sh, sw = shift
     t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
-    keys = np.stack([(t - st) // wt, (h - sh) // wh, (w - sw) // ww], axis=-1)
+    if cyclic:
+        if T % wt or H % wh or W % ww:
+            raise ValueError("cyclic windows need axis lengths that are multiples of the window")
+        keys = np.stack([((t - st) % T) // wt, ((h - sh) % H) // wh, ((w - sw) % W) // ww], axis=-1)
+    else:
+        keys = np.stack([(t - st) // wt, (h - sh) // wh, (w - sw) // ww], axis=-1)
     return keys.reshape(-1, 3)
 
 
@@ -241,17 +251,17 @@ def _groups(keys: np.ndarray):
     return gid, order, counts
 
 
-def tesa(q, k, v, T: int, H: int, W: int, win, shift, stats: Optional[Dict] = None):
+def tesa(q, k, v, T: int, H: int, W: int, win, shift, stats: Optional[Dict] = None, cyclic: bool = False):
     """o_i = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j over the tokens j in the
     same window as token i, per head; returns [L, Ha, d].
 
     Readings taken: scale 1/sqrt(d); no positional bias, no causal mask; the
-    window partition is ``tesa_window_keys``.
+    window partition is ``tesa_window_keys`` (with ``cyclic`` passed on).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    keys = tesa_window_keys(T, H, W, win, shift)
+    keys = tesa_window_keys(T, H, W, win, shift, cyclic)
     _, order, counts = _groups(keys)
     o = np.empty(q.shape, dtype=np.float64)
     start = 0
@@ -267,7 +277,7 @@ def tesa(q, k, v, T: int, H: int, W: int, win, shift, stats: Optional[Dict] = No
 
 
 def tesa_for_queries(q, k, v, T: int, H: int, W: int, win, shift,
-                     query_idx: Sequence[int]) -> np.ndarray:
+                     query_idx: Sequence[int], cyclic: bool = False) -> np.ndarray:
     """TESA output for selected query tokens only, [len(query_idx), Ha, d].
 
     Same definition as ``tesa``; each query attends over its own window.
@@ -276,7 +286,7 @@ def tesa_for_queries(q, k, v, T: int, H: int, W: int, win, shift,
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     query_idx = np.asarray(query_idx)
-    keys = tesa_window_keys(T, H, W, win, shift)
+    keys = tesa_window_keys(T, H, W, win, shift, cyclic)
     gid, order, counts = _groups(keys)
     starts = np.concatenate([[0], np.cumsum(counts)])
     out = np.empty((query_idx.size, q.shape[1], q.shape[2]), dtype=np.float64)

@@ -164,6 +164,26 @@ def test_branch_entry_points_reject_before_launch(L):
     assert L.lingen_rms_index_device(0, 2, 2, 2, ctypes.c_void_p(MISALIGNED), None) == -4
 
 
+def test_te_shift_rejects_before_launch(L):
+    s = CONFIGS[0]
+    cs = mate.to_c_shape(s)
+    F = ctypes.c_void_p(FAKE)
+    call = L.lingen_te_fwd_shift
+    for st, sh, sw, masked in ((2, 0, 0, 1), (-1, 0, 0, 1), (0, 4, 0, 0), (0, 0, 4, 1), (0, 0, 0, 2), (0, 0, 0, -1)):
+        assert call(F, F, F, st, sh, sw, masked, ctypes.byref(cs), F, None) == -2
+    assert call(F, F, F, 1, 3, 3, 1, None, F, None) == -1
+    assert call(F, F, F, 1, 3, 3, 1, ctypes.byref(cs), ctypes.c_void_p(0), None) == -1
+    assert call(F, F, F, 1, 3, 3, 0, ctypes.byref(cs), ctypes.c_void_p(MISALIGNED), None) == -4
+
+
+def test_odd_window_shapes_validate(L):
+    for T in (12, 24):
+        s = CONFIGS[1].with_(T=T, H=T, W=T, win=(3, 3, 3))
+        assert mate.lingen_mate_validate(s) == 0
+    # 27-token windows are compiled for bf16 with d = 64 only
+    assert mate.lingen_mate_validate(CONFIGS[0].with_(T=6, H=6, W=12, win=(3, 3, 3))) == -7
+
+
 def test_dense_attention_rejects_before_launch(L):
     F = ctypes.c_void_p(FAKE)
     Z = ctypes.c_void_p(0)

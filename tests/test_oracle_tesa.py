@@ -185,3 +185,52 @@ def test_oracle_time_grows_linearly_in_T():
 
     t1, t4 = run(16), run(64)
     assert 2.0 < t4 / t1 < 8.0, (t1, t4)
+
+
+def _load_cyclic():
+    rows = []
+    with open(os.path.join(GOLDEN, "tesa_cyclic_windows.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = line.split(":")
+            n, w, s = (int(t) for t in lhs.split())
+            rows.append((n, w, s, [int(t) for t in rhs.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("row", _load_cyclic())
+def test_cyclic_windows_fixture(row):
+    n, w, s, want = row
+    keys = oracle.tesa_window_keys(n, 1, 1, (w, 1, 1), (s, 0, 0), cyclic=True)[:, 0]
+    assert keys.tolist() == want
+    assert np.all(np.bincount(keys) == w)      # every cyclic window is whole
+
+
+@pytest.mark.parametrize("win,shift", [((2, 4, 4), (1, 2, 2)), ((3, 3, 3), (1, 1, 1)), ((2, 4, 4), (1, 3, 1))])
+def test_cyclic_equals_roll_then_plain_windows(win, shift):
+    # Cyclic shifted windows = roll the grid back by the offset, attend in the
+    # plain (unshifted) windows, roll the result forward again.
+    rng = np.random.default_rng(6)
+    T, H, W, Ha, d = 6 if win[0] == 3 else 4, 6 if win[1] == 3 else 8, 6 if win[2] == 3 else 8, 2, 4
+    L = T * H * W
+    q, k, v = _qkv(rng, L, Ha, d)
+    roll = lambda a, sgn: np.roll(a.reshape(T, H, W, Ha, d), tuple(sgn * s for s in shift), axis=(0, 1, 2))
+    plain = oracle.tesa(roll(q, -1).reshape(L, Ha, d), roll(k, -1).reshape(L, Ha, d), roll(v, -1).reshape(L, Ha, d),
+                        T, H, W, win, (0, 0, 0))
+    want = roll(plain, 1).reshape(L, Ha, d)
+    got = oracle.tesa(q, k, v, T, H, W, win, shift, cyclic=True)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    assert np.allclose(oracle.tesa(q, k, v, T, H, W, win, (0, 0, 0), cyclic=True),
+                       oracle.tesa(q, k, v, T, H, W, win, (0, 0, 0)), rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("win,shift", [((3, 3, 3), (1, 1, 1)), ((2, 4, 4), (1, 3, 1))])
+def test_swin_roll_and_mask_agrees_odd_and_uneven(win, shift):
+    rng = np.random.default_rng(7)
+    T, H, W, Ha, d = (6, 6, 6, 2, 4) if win[0] == 3 else (4, 8, 8, 2, 4)
+    q, k, v = _qkv(rng, T * H * W, Ha, d)
+    got = oracle.tesa(q, k, v, T, H, W, win, shift)
+    want = _swin_roll_mask(q, k, v, T, H, W, win, shift)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)

@@ -96,29 +96,30 @@ def kernel_work(s):
     Ha, d, nw = s.attn_heads, s.attn_headdim, s.n_w
     nc = L // Q
     states = 2 * nc * Hs * P * N * e          # chunk states are stored in the input dtype
-    x, y, bc, dt = L * Hs * P * e, L * Hs * P * e, L * N * e, L * Hs * 4
+    G = s.ngroups
+    x, y, bc, dt = L * Hs * P * e, L * Hs * P * e, L * G * N * e, L * Hs * 4
     qkv = 3 * L * Ha * d * e
     work = {
         "ssd_chunk_state": dict(bytes=x + dt + bc + states + nc * Hs * 4,
                                 flops=2 * 2 * nc * Hs * Q * N * P),
         "ssd_state_pass": dict(bytes=2 * states + nc * Hs * 4, flops=2 * states // 4),
-        # C.B^T once per chunk (shared by the heads), then per head the masked
-        # in-chunk product and the two inter-chunk read-outs
+        # C.B^T once per chunk and group (shared by the group's heads), then per
+        # head the masked in-chunk product and the two inter-chunk read-outs
         "ssd_chunk_out": dict(bytes=x + dt + 2 * bc + states + y,
-                              flops=nc * 2 * Q * Q * N + nc * Hs * (2 * Q * Q * P + 2 * 2 * Q * N * P)),
+                              flops=nc * G * 2 * Q * Q * N + nc * Hs * (2 * Q * Q * P + 2 * 2 * Q * N * P)),
         "tesa_window": dict(bytes=qkv + 2 * y, flops=4 * L * nw * d * Ha),
     }
     if s.n_review:
         R = s.n_review
         blk = s.rpool[0] * s.rpool[1] * s.rpool[2]
-        work["review"] = dict(bytes=R * blk * (Hs * P * e + Hs * 4 + N * e), flops=2 * R * Hs * P * N)
+        work["review"] = dict(bytes=R * blk * (Hs * P * e + Hs * 4 + G * N * e), flops=2 * R * Hs * P * N)
     return work
 
 
 def compulsory_bytes(s):
     e = s.elem_bytes
     L = s.L
-    return L * (2 * s.ssd_heads * s.headdim * e + s.ssd_heads * 4 + 2 * s.d_state * e
+    return L * (2 * s.ssd_heads * s.headdim * e + s.ssd_heads * 4 + 2 * s.ngroups * s.d_state * e
                 + 3 * s.attn_heads * s.attn_headdim * e)
 
 

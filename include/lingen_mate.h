@@ -38,7 +38,8 @@
  *     x        [batch, L, Hs, P]   dtype
  *     dt       [batch, L, Hs]      fp32, > 0 (already through softplus)
  *     A        [Hs]                fp32, <= 0
- *     B, C     [batch, L, N]       dtype (one group shared by all heads)
+ *     B, C     [batch, L, G, N]    dtype (G groups; head h uses group
+ *                                  h / (Hs/G), so G = 1 shares them by all heads)
  *     D        [Hs]                fp32
  *     q, k, v  [batch, L, Ha, d]   dtype
  *     y        [batch, L, Hs*P]    dtype  (head i owns columns i*P..i*P+P-1)
@@ -78,7 +79,7 @@ typedef enum { LINGEN_F32 = 0, LINGEN_BF16 = 1 } lingen_dtype;
 typedef struct {
   int32_t batch, T, H, W;          /* token grid; L = T*H*W                        */
   int32_t ssd_heads, headdim;      /* Hs, P                                        */
-  int32_t d_state, ngroups, chunk; /* N, G (must be 1), Q (must divide L)          */
+  int32_t d_state, ngroups, chunk; /* N, G (must divide Hs), Q (must divide L)    */
   int32_t attn_heads, attn_headdim;/* Ha, d; Ha*d must equal Hs*P                  */
   int32_t win_t, win_h, win_w;     /* TESA window; must divide T, H, W             */
   int32_t dtype;                   /* lingen_dtype of x, B, C, q, k, v, y          */

@@ -180,7 +180,7 @@ def _sizes(s):
         x=s.batch * L * s.ssd_heads * s.headdim,
         dt=s.batch * L * s.ssd_heads,
         A=s.ssd_heads,
-        B=s.batch * L * s.d_state,
+        B=s.batch * L * s.ngroups * s.d_state,
         D=s.ssd_heads,
         q=s.batch * L * s.attn_heads * s.attn_headdim,
         y=s.batch * L * s.ssd_heads * s.headdim,

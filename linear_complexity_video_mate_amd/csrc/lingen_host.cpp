@@ -48,7 +48,7 @@ int validate_shape(const lingen_mate_shape* s) {
   const int64_t L = tokens(s);
   if (L > kMaxTokens) return LINGEN_ERR_SHAPE;
   if (s->ssd_heads < 1 || s->headdim < 1 || s->d_state < 1 || s->chunk < 1) return LINGEN_ERR_SHAPE;
-  if (s->ngroups != 1) return LINGEN_ERR_SHAPE;
+  if (s->ngroups < 1 || s->ssd_heads % s->ngroups) return LINGEN_ERR_SHAPE;
   if (L % s->chunk != 0) return LINGEN_ERR_SHAPE;
   if (s->attn_heads < 1 || s->attn_headdim < 1) return LINGEN_ERR_SHAPE;
   if (int64_t(s->attn_heads) * s->attn_headdim != int64_t(s->ssd_heads) * s->headdim) return LINGEN_ERR_SHAPE;
@@ -93,7 +93,7 @@ WsLayout ws_layout(const lingen_mate_shape* s) {
   w.review_dt = off;
   off = align_up(off + R * hs * sizeof(float));
   w.review_b = off;
-  off = align_up(off + R * N * sizeof(float));
+  off = align_up(off + R * size_t(s->ngroups) * N * sizeof(float));
   w.total = off;
   return w;
 }

@@ -18,7 +18,7 @@ struct WsLayout {
   size_t review_h; // fp32 [Hs][P][N]: state left by the review tokens
   size_t review_x; // fp32 [R][Hs][P]: pooled review x
   size_t review_dt;// fp32 [R][Hs]
-  size_t review_b; // fp32 [R][N]
+  size_t review_b; // fp32 [R][G][N]
   size_t total;
 };
 

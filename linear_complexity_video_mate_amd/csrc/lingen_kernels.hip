@@ -299,13 +299,13 @@ struct ReviewGeom {
 };
 
 // Block (r, y): the mean over review block r of head y's x row slice (and
-// of dt for that head) for y < Hs, of the B rows for y == Hs.  Each thread
+// of dt for that head) for y < Hs, of group y - Hs's B rows for y >= Hs.  Each thread
 // sums the 16-byte chunk c of every RP-th token row, with several rows'
 // loads in flight, and the RP partial sums are reduced through LDS.
 template <typename TS>
 __global__ __launch_bounds__(256) void review_pool_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
                                                           const TS* __restrict__ B, int T, int H, int W, int Hs,
-                                                          int P, int N, ReviewGeom g, float* __restrict__ rx,
+                                                          int P, int N, int G, ReviewGeom g, float* __restrict__ rx,
                                                           float* __restrict__ rdt, float* __restrict__ rb) {
   constexpr int VEC = Vec16<TS>::n;
   constexpr int UNROLL = 4;
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void review_pool_kernel(const TS* __restrict__
       v[u].u = make_uint4(0, 0, 0, 0);
       if (tl < cnt) {
         const int64_t tok = token(tl);
-        const TS* src = (y < Hs) ? x + (tok * Hs + y) * P : B + tok * N;
+        const TS* src = (y < Hs) ? x + (tok * Hs + y) * P : B + (tok * G + (y - Hs)) * N;
         v[u].u = *reinterpret_cast<const uint4*>(src + c * VEC);
       }
     }
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void review_pool_kernel(const TS* __restrict__
     float sum = 0.f;
     for (int q = 0; q < rp; ++q) sum += red[q * width + tid];
     if (y < Hs) rx[(int64_t(r) * Hs + y) * P + tid] = sum * inv;
-    else rb[int64_t(r) * N + tid] = sum * inv;
+    else rb[(int64_t(r) * G + (y - Hs)) * N + tid] = sum * inv;
   }
   if (y < Hs) {
     lds_barrier();
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256) void review_pool_kernel(const TS* __restrict__
 // h_R[h][p][n] = sum_r exp(sum_{tau>r} a_tau) dt_r x_r[p] B_r[n], from zero.
 __global__ __launch_bounds__(256) void review_state_kernel(const float* __restrict__ rx, const float* __restrict__ rdt,
                                                            const float* __restrict__ rb, const float* __restrict__ A,
-                                                           int R, int Hs, int P, int N, float* __restrict__ hR) {
+                                                           int R, int Hs, int P, int N, int G, float* __restrict__ hR) {
   // Block (h, slice) computes elements slice*1024 .. +1023 of head h's P x N
   // state, four per thread.  Review tokens are taken RT at a time: their
   // weighted x rows and B rows are staged in LDS, then every thread
@@ -381,6 +381,7 @@ __global__ __launch_bounds__(256) void review_state_kernel(const float* __restri
   __shared__ float sx[RT * MAXP];
   __shared__ float sb[RT * MAXN];
   const int h = blockIdx.x, tid = threadIdx.x;
+  const int grp = h / (Hs / G);   // B group of head h
   for (int r = tid; r < R; r += 256) w[r] = rdt[r * Hs + h];
   lds_barrier();
   if (tid == 0) {   // w_r = e^{sum_{tau > r} a_tau} dt_r, from the last review token back
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(256) void review_state_kernel(const float* __restri
   for (int r0 = 0; r0 < R; r0 += RT) {
     const int rn = R - r0 < RT ? R - r0 : RT;
     for (int u = tid; u < rn * P; u += 256) sx[u] = rx[((r0 + u / P) * Hs + h) * P + u % P] * w[r0 + u / P];
-    for (int u = tid; u < rn * N; u += 256) sb[u] = rb[(r0 + u / N) * N + u % N];
+    for (int u = tid; u < rn * N; u += 256) sb[u] = rb[((r0 + u / N) * G + grp) * N + u % N];
     lds_barrier();
     int pk[MAXE], nk[MAXE];
 #pragma unroll
@@ -446,7 +447,7 @@ constexpr int kLptX = 2, kLptB = 2;
 template <typename TS, int P, int N, int Q>
 __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
                                                               const float* __restrict__ A, const TS* __restrict__ B,
-                                                              RmsMap rms, int Hs, int hg, int n_chunks,
+                                                              RmsMap rms, int Hs, int G, int hg, int n_chunks,
                                                               TS* __restrict__ states, float* __restrict__ decay) {
   using MT = TS;
   using F = Frag<MT>;
@@ -476,8 +477,10 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
 
   load_chunk_schedule<Q, NTHR>(cs, dt, A, rms, c, Hs, h0, hg);
   {
+    // the hg heads of the workgroup share one B group
+    const TS* Bg = B + int64_t(h0 / (Hs / G)) * N;
     StageT<TS, Q, N, NTHR, kLptB> bs;
-    bs.load([&](int s) { return B + int64_t(cs.tok[s]) * N; });
+    bs.load([&](int s) { return Bg + int64_t(cs.tok[s]) * G * N; });
     bs.use([&](int s0, int n0, const Vec16<TS>& va, const Vec16<TS>& vb) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) st_pair(&sBt[TQ::at(n0 + e, s0)], va.e[e], vb.e[e]);
@@ -663,7 +666,7 @@ struct OutCfg {
 template <typename TS, int P, int N, int Q>
 __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_kernel(
     const TS* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const TS* __restrict__ B,
-    const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int hg, int n_chunks,
+    const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int G, int hg, int n_chunks,
     const TS* __restrict__ states, TS* __restrict__ y) {
   using MT = TS;
   using F = Frag<MT>;
@@ -722,10 +725,13 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   const int wt = wave % Cfg::WT, wpw = wave / Cfg::WT;
   const int t = wt * 16 + r16;            // this lane's output position
   const int64_t tok_t = cs.tok[t];
+  // the hg heads of the workgroup share one B, C group
+  const TS* Bg = B + int64_t(h0 / (Hs / G)) * N;
+  const TS* Cg = C + int64_t(h0 / (Hs / G)) * N;
   // C_t fragments (B operand, k = n) for the inter-chunk terms, and G^T.
   typename F::type cfr[N / KI];
 #pragma unroll
-  for (int ks = 0; ks < N / KI; ++ks) cfr[ks] = F::load(C + tok_t * N + ks * KI, lane);
+  for (int ks = 0; ks < N / KI; ++ks) cfr[ks] = F::load(Cg + tok_t * G * N + ks * KI, lane);
   // G^T is accumulated in fp32 and kept in the operand type (bf16 for bf16
   // data: the M^T values built from it are rounded to bf16 anyway).
   using GT = typename std::conditional<kBf16, bf16x4, f32x4>::type;
@@ -734,7 +740,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   {
     Stage16<Q * (N / VEC), NTHR> bs;
     bs.load([&](int u) {
-      return *reinterpret_cast<const uint4*>(B + int64_t(cs.tok[u / (N / VEC)]) * N + (u % (N / VEC)) * VEC);
+      return *reinterpret_cast<const uint4*>(Bg + int64_t(cs.tok[u / (N / VEC)]) * G * N + (u % (N / VEC)) * VEC);
     });
     bs.use([&](int u, uint4 raw) {
       *reinterpret_cast<uint4*>(&sBr[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
@@ -1306,11 +1312,11 @@ int launch_review(const lingen_mate_shape* s, const TS* x, const float* dt, cons
   float* rdt = reinterpret_cast<float*>(ws + lay.review_dt);
   float* rb = reinterpret_cast<float*>(ws + lay.review_b);
   float* hR = reinterpret_cast<float*>(ws + lay.review_h);
-  review_pool_kernel<TS><<<dim3(s->n_review, s->ssd_heads + 1), 256, 0, st>>>(
-      x, dt, B, s->T, s->H, s->W, s->ssd_heads, s->headdim, s->d_state, g, rx, rdt, rb);
+  review_pool_kernel<TS><<<dim3(s->n_review, s->ssd_heads + s->ngroups), 256, 0, st>>>(
+      x, dt, B, s->T, s->H, s->W, s->ssd_heads, s->headdim, s->d_state, s->ngroups, g, rx, rdt, rb);
   if (hip_status()) return LINGEN_ERR_HIP;
   review_state_kernel<<<dim3(s->ssd_heads, (s->headdim * s->d_state + 1023) / 1024), 256, 0, st>>>(rx, rdt, rb, A, s->n_review, s->ssd_heads, s->headdim,
-                                                    s->d_state, hR);
+                                                    s->d_state, s->ngroups, hR);
   return hip_status();
 }
 
@@ -1324,14 +1330,15 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
   const int Hs = s->ssd_heads;
   TS* states = reinterpret_cast<TS*>(ws + lay.states);
   float* decay = reinterpret_cast<float*>(ws + lay.decay);
-  const int hg = head_group(Hs, kStateHeadGroup);
+  // heads per workgroup: a divisor of the heads per B group
+  const int hg = head_group(Hs / s->ngroups, kStateHeadGroup);
   const float* h0 = nullptr;
   if (s->n_review > 0) {
     if (int rc = launch_review<TS>(s, x, dt, A, B, ws, lay, st)) return rc;
     h0 = reinterpret_cast<const float*>(ws + lay.review_h);
   }
   if (int rc = mark(ev, 1, st)) return rc;
-  ssd_chunk_state_kernel<TS, P, N, Q><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(x, dt, A, B, make_rms(s, mode), Hs, hg, nc,
+  ssd_chunk_state_kernel<TS, P, N, Q><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(x, dt, A, B, make_rms(s, mode), Hs, s->ngroups, hg, nc,
                                                                        states, decay);
   if (hip_status()) return LINGEN_ERR_HIP;
   if (int rc = mark(ev, 2, st)) return rc;
@@ -1358,14 +1365,16 @@ int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char
   for (int b = 0; b < s->batch; ++b) {
     const TS* x = reinterpret_cast<const TS*>(static_cast<const char*>(a.x) + int64_t(b) * L * Hs * P * eb);
     const float* dt = a.dt + int64_t(b) * L * Hs;
-    const TS* B = reinterpret_cast<const TS*>(static_cast<const char*>(a.B) + int64_t(b) * L * N * eb);
-    const TS* C = reinterpret_cast<const TS*>(static_cast<const char*>(a.C) + int64_t(b) * L * N * eb);
+    const int64_t bc = int64_t(b) * L * s->ngroups * N * eb;
+    const TS* B = reinterpret_cast<const TS*>(static_cast<const char*>(a.B) + bc);
+    const TS* C = reinterpret_cast<const TS*>(static_cast<const char*>(a.C) + bc);
     TS* yb = reinterpret_cast<TS*>(static_cast<char*>(y) + int64_t(b) * L * Hs * P * eb);
     if (int rc = launch_states<TS, P, N, Q>(s, mode, x, dt, a.A, B, ws, st, ev)) return rc;
     using Cfg = OutCfg<TS, P, N, Q>;
-    const int hg = head_group(Hs);
+    const int hg = head_group(Hs / s->ngroups);   // a divisor of the heads per B, C group
     ssd_chunk_out_kernel<TS, P, N, Q><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
-        x, dt, a.A, B, C, a.D, make_rms(s, mode), Hs, hg, nc, reinterpret_cast<const TS*>(ws + lay.states), yb);
+        x, dt, a.A, B, C, a.D, make_rms(s, mode), Hs, s->ngroups, hg, nc, reinterpret_cast<const TS*>(ws + lay.states),
+        yb);
     if (hip_status()) return LINGEN_ERR_HIP;
     if (int rc = mark(ev, 4, st)) return rc;
   }
@@ -1498,7 +1507,7 @@ int lingen_ssd_chunk_states(const void* x, const float* dt, const float* A, cons
   for (int b = 0; b < s->batch; ++b) {
     const char* xb = static_cast<const char*>(x) + b * L * Hs * P * eb;
     const float* dtb = dt + b * L * Hs;
-    const char* Bb = static_cast<const char*>(B) + b * L * N * eb;
+    const char* Bb = static_cast<const char*>(B) + b * L * s->ngroups * N * eb;
     int rc = LINGEN_ERR_UNSUPPORTED;
     switch (scan_family(s)) {
       case SCAN_F32_P32_N16_Q16:

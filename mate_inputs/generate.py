@@ -60,7 +60,8 @@ class MateInputs:
 
     ``store[name]`` is uint16 (bf16 bits) for x, B, C, q, k, v in bf16
     configurations and float32 otherwise.  Layouts: x [L, Hs', P], dt [L, Hs'],
-    A [Hs'], B and C [L, N], D [Hs'], q, k, v [L, Ha', d]; Hs' and Ha' count
+    A [Hs'], B and C [L, N] ([L, G, N] with G > 1 groups), D [Hs'],
+    q, k, v [L, Ha', d]; Hs' and Ha' count
     only the generated heads (``heads``), which default to all.
     """
 
@@ -152,9 +153,14 @@ def make_inputs(shape: MateShape, cfg_id: int, seed: int = DEFAULT_SEED,
         out.store["A"] = (-np.exp(u)).astype(np.float32)[hs_list]
     if "D" in want:
         out.store["D"] = _rng(seed, cfg_id, "D", 0).standard_normal(Hs).astype(np.float32)[hs_list]
+    G = shape.ngroups
     for name in ("B", "C"):
         if name in want:
-            out.store[name] = finish(_normal(seed, cfg_id, name, 0, L * N, 1.0 / math.sqrt(N)).reshape(L, N))
+            # group g draws from stream g (the head slot of the seed), so the
+            # single-group tensors are those of group 0; layout [L, N] for one
+            # group, [L, G, N] for several
+            groups = [_normal(seed, cfg_id, name, g, L * N, 1.0 / math.sqrt(N)).reshape(L, N) for g in range(G)]
+            out.store[name] = finish(groups[0] if G == 1 else np.stack(groups, axis=1))
 
     if threads > 1 and len(jobs) > 1:
         with _fut.ThreadPoolExecutor(max_workers=threads) as ex:

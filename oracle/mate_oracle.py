@@ -95,6 +95,19 @@ def rms_inverse(perm: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
+def _per_head(M, Hs: int) -> np.ndarray:
+    """B or C as [L, Hs, N]: from [L, N] (one group, shared by every head) or
+    [L, G, N] (G groups; head h uses group h // (Hs // G), Mamba2's grouping
+    of heads)."""
+    M = np.asarray(M, dtype=np.float64)
+    if M.ndim == 2:
+        return np.broadcast_to(M[:, None, :], (M.shape[0], Hs, M.shape[1]))
+    G = M.shape[1]
+    if Hs % G:
+        raise ValueError("the number of groups must divide the number of heads")
+    return np.repeat(M, Hs // G, axis=1)
+
+
 def ssd_scan(x, dt, A, B, C, D, order: Sequence[int], h0=None,
              record_after: Iterable[int] = (), stats: Optional[Dict] = None):
     """Run the scalar-A selective SSM recurrence over tokens in ``order``.
@@ -104,6 +117,7 @@ def ssd_scan(x, dt, A, B, C, D, order: Sequence[int], h0=None,
         h <- exp(dt_c * A) * h + dt_c * (x_c outer B_c)
         y_c = h C_c + D * x_c
     The decay applied when a token is absorbed uses that token's own dt.
+    B and C are [L, N] (shared by all heads) or [L, G, N] (see ``_per_head``).
 
     Returns (y, h_final, recorded) where y[c] is set for every visited c (zero
     elsewhere) and recorded[k] is the state after the first k visited tokens,
@@ -112,11 +126,11 @@ def ssd_scan(x, dt, A, B, C, D, order: Sequence[int], h0=None,
     x = np.asarray(x, dtype=np.float64)
     dt = np.asarray(dt, dtype=np.float64)
     A = np.asarray(A, dtype=np.float64)
-    B = np.asarray(B, dtype=np.float64)
-    C = np.asarray(C, dtype=np.float64)
+    B = _per_head(B, x.shape[1])
+    C = _per_head(C, x.shape[1])
     D = np.asarray(D, dtype=np.float64)
     Hs, P = x.shape[1], x.shape[2]
-    N = B.shape[1]
+    N = B.shape[2]
     h = np.zeros((Hs, P, N)) if h0 is None else np.array(h0, dtype=np.float64, copy=True)
     y = np.zeros(x.shape, dtype=np.float64)
     want = set(int(k) for k in record_after)
@@ -127,8 +141,8 @@ def ssd_scan(x, dt, A, B, C, D, order: Sequence[int], h0=None,
     for c in order:
         decay = np.exp(dt[c] * A)                         # [Hs]
         u = dt[c][:, None] * x[c]                         # [Hs, P]
-        h = decay[:, None, None] * h + u[:, :, None] * B[c][None, None, :]
-        y[c] = h @ C[c] + D[:, None] * x[c]
+        h = decay[:, None, None] * h + u[:, :, None] * B[c][:, None, :]
+        y[c] = np.matmul(h, C[c][:, :, None])[:, :, 0] + D[:, None] * x[c]
         step += 1
         if step in want:
             recorded[step] = h.copy()

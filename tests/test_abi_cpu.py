@@ -53,7 +53,8 @@ BAD = [
     ("batch", dict(batch=0), -2),
     ("T", dict(T=0), -2),
     ("chunk_not_dividing", dict(chunk=48), -2),
-    ("groups", dict(ngroups=2), -2),
+    ("groups_not_dividing", dict(ngroups=3), -2),
+    ("groups_zero", dict(ngroups=0), -2),
     ("heads_mismatch", dict(attn_heads=8), -2),
     ("window_not_dividing", dict(win=(3, 8, 8)), -2),
     ("dtype", dict(dtype="f16"), -3),
@@ -76,6 +77,11 @@ def test_invalid_shapes(L, name, kw, code):
     assert e.value.code == code
 
 
+def test_grouped_shapes_valid(L):
+    for G in (1, 2, 4, 16):
+        assert mate.lingen_mate_validate(CONFIGS[1].with_(ngroups=G)) == 0
+
+
 def test_review_shape_valid(L):
     s = CONFIGS[1].with_(n_review=64, rpool=(2, 4, 4), rgrid=(4, 4, 4))   # pooled 8x8x8
     assert mate.lingen_mate_validate(s) == 0
@@ -91,8 +97,11 @@ def test_workspace_formula(L, cfg):
     R = s.n_review
     if R:
         want += al(s.ssd_heads * s.headdim * s.d_state * 4) + al(R * s.ssd_heads * s.headdim * 4) \
-            + al(R * s.ssd_heads * 4) + al(R * s.d_state * 4)
+            + al(R * s.ssd_heads * 4) + al(R * s.ngroups * s.d_state * 4)
     assert mate.lingen_mate_workspace_bytes(s) == want
+    if R:   # pooled review B rows are kept per group
+        g4 = s.with_(ngroups=4)
+        assert mate.lingen_mate_workspace_bytes(g4) == want - al(R * s.d_state * 4) + al(R * 4 * s.d_state * 4)
 
 
 @pytest.mark.parametrize("mode", range(4))

@@ -182,3 +182,43 @@ def test_heads_are_independent():
     full = oracle.ssd_bidir(x, dt, A, B, C, D, perm)
     sub = oracle.ssd_bidir(x[:, [1, 3]], dt[:, [1, 3]], A[[1, 3]], B, C, D[[1, 3]], perm)
     np.testing.assert_allclose(sub, full[:, [1, 3]], rtol=0, atol=0)
+
+
+def test_grouped_bc_reduce_to_shared_and_split_by_group():
+    # G groups of B and C: head h reads group h // (Hs // G).  Identical groups
+    # give the shared (one-group) scan; and each group's heads alone, scanned
+    # with that group's B and C shared, give the same outputs.
+    rng = np.random.default_rng(40)
+    L, Hs, P, N, G = 24, 4, 3, 5, 2
+    x = rng.standard_normal((L, Hs, P))
+    dt = rng.uniform(0.05, 0.5, (L, Hs))
+    A = -rng.uniform(0.5, 2.0, Hs)
+    D = rng.standard_normal(Hs)
+    B1, C1 = rng.standard_normal((L, N)), rng.standard_normal((L, N))
+    perm = rng.permutation(L)
+    same = oracle.ssd_bidir(x, dt, A, np.stack([B1] * G, 1), np.stack([C1] * G, 1), D, perm)
+    np.testing.assert_allclose(same, oracle.ssd_bidir(x, dt, A, B1, C1, D, perm), rtol=1e-13, atol=1e-13)
+    Bg, Cg = rng.standard_normal((L, G, N)), rng.standard_normal((L, G, N))
+    got = oracle.ssd_bidir(x, dt, A, Bg, Cg, D, perm)
+    hpg = Hs // G
+    for g in range(G):
+        hs = slice(g * hpg, (g + 1) * hpg)
+        want = oracle.ssd_bidir(x[:, hs], dt[:, hs], A[hs], Bg[:, g], Cg[:, g], D[hs], perm)
+        np.testing.assert_allclose(got[:, hs], want, rtol=1e-13, atol=1e-13)
+    with pytest.raises(ValueError):
+        oracle.ssd_bidir(x, dt, A, rng.standard_normal((L, 3, N)), rng.standard_normal((L, 3, N)), D, perm)
+
+
+def test_grouped_review_state_splits_by_group():
+    rng = np.random.default_rng(41)
+    T, H, W, Hs, P, N, G = 4, 4, 4, 4, 2, 3, 2
+    L = T * H * W
+    x = rng.standard_normal((L, Hs, P))
+    dt = rng.uniform(0.05, 0.5, (L, Hs))
+    A = -rng.uniform(0.5, 2.0, Hs)
+    Bg, Cg = rng.standard_normal((L, G, N)), rng.standard_normal((L, G, N))
+    got = oracle.review_state(x, dt, A, Bg, Cg, T, H, W, (2, 2, 2), (2, 2, 2))
+    for g in range(G):
+        hs = slice(g * 2, g * 2 + 2)
+        want = oracle.review_state(x[:, hs], dt[:, hs], A[hs], Bg[:, g], Cg[:, g], T, H, W, (2, 2, 2), (2, 2, 2))
+        np.testing.assert_allclose(got[hs], want, rtol=1e-13, atol=1e-13)

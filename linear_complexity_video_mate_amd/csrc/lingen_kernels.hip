@@ -877,6 +877,10 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
     // Inter-chunk terms, the skip, and the store.
     const float ef = fast_exp2(cum_t), eb = fast_exp2(cum[Q - 1] - exc_t);
     const float twoD = 2.f * D[h];
+    // bf16 rows of 64 owned by one wave: the four p-tiles are stored together
+    // in 16-byte pieces (see below).
+    constexpr bool kP16 = kBf16 && Cfg::PT == 4 && Cfg::P_PER == 4 && Cfg::WPW == 1;
+    float ob[4][4];
 #pragma unroll
     for (int pj = 0; pj < Cfg::P_PER; ++pj) {
       const int pt = wpw + pj * Cfg::WPW;
@@ -895,6 +899,11 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         o[r] = acc[pj][r] + ef * zf[r] + eb * zb[r] + twoD * to_f32(xt[r]);
+      if constexpr (kP16) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ob[pj][r] = o[r];
+        continue;
+      }
       TS* dst = y + tok_t * (int64_t(Hs) * P) + int64_t(h) * P + p0;
       if constexpr (kBf16) {
         bf16x4 ov;
@@ -903,6 +912,25 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
         *reinterpret_cast<bf16x4*>(dst) = ov;
       } else {
         *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    if constexpr (kP16) {
+      // Exchange the 4-element pieces of p-tiles 2 r1 and 2 r1 + 1 between
+      // lane groups g and g ^ 1 (v_permlane16_swap): the lane then holds
+      // p0 .. p0 + 7, p0 = 32 r1 + 16 (g & 1) + 8 (g >> 1), and a wave's
+      // 16-byte stores cover 64 contiguous bytes of each row.
+      TS* row = y + tok_t * (int64_t(Hs) * P) + int64_t(h) * P + 16 * (grp & 1) + 8 * (grp >> 1);
+#pragma unroll
+      for (int r1 = 0; r1 < 2; ++r1) {
+        bf16x8 res;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(ob[2 * r1][r]),
+                                                           __float_as_uint(ob[2 * r1 + 1][r]), false, false);
+          res[r] = static_cast<__bf16>(__uint_as_float(sw[0]));
+          res[4 + r] = static_cast<__bf16>(__uint_as_float(sw[1]));
+        }
+        *reinterpret_cast<bf16x8*>(row + 32 * r1) = res;
       }
     }
     lds_barrier();   // staging buffers free for the next head
@@ -1052,6 +1080,9 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
     }
   };
   using YV = typename std::conditional<kBf16, bf16x4, f32x4>::type;
+  // bf16 rows of 64: y is read and written in 16-byte pieces (see the epilogue)
+  constexpr bool kY16 = kBf16 && ET == 4;
+  const int y16_off = 16 * (grp & 1) + 8 * (grp >> 1);
   // Per-lane registers of an item, loaded one item ahead: Q fragments and
   // the query tokens.
   struct QState {
@@ -1105,7 +1136,15 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
     // The MA output this item adds to (fused branch sum) arrives while the
     // two passes run.
     YV yp[QTP][ET];
-    if constexpr (ACCUMULATE) {
+    bf16x8 yq[QTP][2];
+    if constexpr (ACCUMULATE && kY16) {
+#pragma unroll
+      for (int qi = 0; qi < QTP; ++qi) {
+        const TS* yrow = y + int64_t(cur.tokq[qi]) * rowstride + int64_t(h) * DH + y16_off;
+#pragma unroll
+        for (int r1 = 0; r1 < 2; ++r1) yq[qi][r1] = *reinterpret_cast<const bf16x8*>(yrow + 32 * r1);
+      }
+    } else if constexpr (ACCUMULATE) {
 #pragma unroll
       for (int qi = 0; qi < QTP; ++qi) {
         const TS* yrow = y + int64_t(cur.tokq[qi]) * rowstride + int64_t(h) * DH;
@@ -1229,6 +1268,31 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
       const float inv = __builtin_amdgcn_rcpf(lt);
       if (kPadded && (wave + qi * Cfg::NWAVE) * 16 + r16 >= NVALID) continue;   // padding slot
       TS* yrow = y + int64_t(cur.tokq[qi]) * rowstride + int64_t(h) * DH;
+      if constexpr (kY16) {
+        // Exchange the 4-element pieces of the d-tiles 2 r1 and 2 r1 + 1
+        // between lane groups g and g ^ 1 (v_permlane16_swap): the lane then
+        // holds d0 .. d0 + 7, d0 = 32 r1 + 16 (g & 1) + 8 (g >> 1), and a
+        // wave's 16-byte stores cover 64 contiguous bytes of each row.
+#pragma unroll
+        for (int r1 = 0; r1 < 2; ++r1) {
+          float ov[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(o[qi][2 * r1][r]),
+                                                             __float_as_uint(o[qi][2 * r1 + 1][r]), false, false);
+            ov[r] = __uint_as_float(sw[0]);
+            ov[4 + r] = __uint_as_float(sw[1]);
+          }
+          bf16x8 res;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float val = ov[e] * inv;
+            res[e] = static_cast<__bf16>(ACCUMULATE ? to_f32(yq[qi][r1][e]) + val : val);
+          }
+          *reinterpret_cast<bf16x8*>(yrow + y16_off + 32 * r1) = res;
+        }
+        continue;
+      }
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
         YV res;

@@ -35,6 +35,7 @@ from .mate_oracle import (
     tesa_window_keys,
     tesa,
     tesa_for_queries,
+    tesa_backward,
     dense_attention,
     dense_attention_for_queries,
     mate_fwd,
@@ -53,6 +54,7 @@ __all__ = [
     "tesa_window_keys",
     "tesa",
     "tesa_for_queries",
+    "tesa_backward",
     "dense_attention",
     "dense_attention_for_queries",
     "mate_fwd",

@@ -290,6 +290,43 @@ def tesa(q, k, v, T: int, H: int, W: int, win, shift, stats: Optional[Dict] = No
     return o
 
 
+def tesa_backward(q, k, v, dO, T: int, H: int, W: int, win, shift, cyclic: bool = False):
+    """Gradients of TESA, (dq, dk, dv), each [L, Ha, d], for an upstream
+    gradient dO of the output: the chain rule through o = softmax(q k^T /
+    sqrt(d)) v inside every window, per head.  With P the softmax weights of
+    a window and s = 1/sqrt(d):
+        dv = P^T dO
+        dP = dO v^T
+        dS = P * (dP - rowsum(dP * P))     (elementwise; the softmax Jacobian)
+        dq = s dS k,   dk = s dS^T q
+    Needed for training the mixer (the pages train LinGen progressively, [ART]
+    要领 and [ZH] 技术细节); the partition is ``tesa_window_keys``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    sc = 1.0 / math.sqrt(q.shape[-1])
+    keys = tesa_window_keys(T, H, W, win, shift, cyclic)
+    _, order, counts = _groups(keys)
+    dq, dk, dv = np.empty(q.shape), np.empty(k.shape), np.empty(v.shape)
+    start = 0
+    for n in counts:
+        idx = order[start:start + n]
+        start += n
+        qh, kh, vh, gh = (a[idx].transpose(1, 0, 2) for a in (q, k, v, dO))      # [Ha, n, d]
+        S = (qh @ kh.transpose(0, 2, 1)) * sc
+        S -= S.max(axis=-1, keepdims=True)
+        P = np.exp(S)
+        P /= P.sum(axis=-1, keepdims=True)
+        dP = gh @ vh.transpose(0, 2, 1)
+        dS = P * (dP - (dP * P).sum(axis=-1, keepdims=True))
+        dq[idx] = ((dS @ kh) * sc).transpose(1, 0, 2)
+        dk[idx] = ((dS.transpose(0, 2, 1) @ qh) * sc).transpose(1, 0, 2)
+        dv[idx] = (P.transpose(0, 2, 1) @ gh).transpose(1, 0, 2)
+    return dq, dk, dv
+
+
 def tesa_for_queries(q, k, v, T: int, H: int, W: int, win, shift,
                      query_idx: Sequence[int], cyclic: bool = False) -> np.ndarray:
     """TESA output for selected query tokens only, [len(query_idx), Ha, d].

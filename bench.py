@@ -34,7 +34,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 STAGES = ("review", "ssd_chunk_state", "ssd_state_pass", "ssd_chunk_out", "tesa_window")
 # Sources that define the mixer's kernels (a traffic record is valid only for them as they stand).
 KERNEL_SRCS = [os.path.join(ROOT, "linear_complexity_video_mate_amd", "csrc", n)
-               for n in ("lingen_kernels.hip", "lingen_device.h")]
+               for n in ("lingen_kernels.hip", "lingen_device.h", "lingen_window.h")]
 
 
 def kernel_source_sha256() -> str:
@@ -300,6 +300,51 @@ def library_attention(torch, qkv, steps, flops, timed):
     return {"op": "torch.nn.functional.scaled_dot_product_attention", "unavailable": last}
 
 
+def te_backward(args, mate, torch):
+    """The TE branch's backward pass (lingen_te_bwd) on the workload against
+    its forward (lingen_te_fwd), both timed with events on the launch stream,
+    plain and shifted windows alternating by step as in the mixer."""
+    from mate_inputs import CONFIGS, CONFIG_NOTES, make_inputs
+
+    s = CONFIGS[args.config]
+    inp = make_inputs(s, args.config, tensors=["q", "k", "v"], threads=16)
+    q, k, v = (inp.torch(n, "cuda") for n in ("q", "k", "v"))
+    g = torch.empty_like(q).normal_()
+    dq, dk, dv, y = (torch.empty_like(q) for _ in range(4))
+    half = tuple(w // 2 for w in s.win)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    bwd_ms = timed(lambda i: mate.lingen_te_bwd(q, k, v, g, half if i % 2 else (0, 0, 0), 1, s, dq=dq, dk=dk, dv=dv))
+    fwd_ms = timed(lambda i: mate.lingen_te_fwd(q, k, v, i % 2, s, out=y))
+    e = s.elem_bytes
+    rows = s.L * s.attn_heads * s.attn_headdim
+    nbytes = 7 * rows * e                                # q, k, v, dO read; dq, dk, dv written
+    flops = 10 * s.n_w * rows                            # S, dP, dq, dk, dv: five products of 2 n_w d
+    issued = 18 * s.n_w * rows                           # S three times, o, dP twice, dq, dk, dv
+    out = {
+        "kernel": "tesa_bwd", "workload": CONFIG_NOTES[args.config], "steps": args.steps,
+        "bwd_ms": round(bwd_ms, 4), "fwd_ms": round(fwd_ms, 4), "bwd_over_fwd": round(bwd_ms / fwd_ms, 2),
+        "algorithmic_bytes": nbytes, "GB/s": round(nbytes / bwd_ms / 1e6, 1),
+        "hbm_frac": round(nbytes / bwd_ms / 1e6 / HBM_PEAK_GBS, 4),
+        "algorithmic_flops": flops, "TFLOP/s": round(flops / bwd_ms / 1e9, 1),
+        "mfma_frac": round(flops / bwd_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "issued_mfma_TFLOP/s": round(issued / bwd_ms / 1e9, 1),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def dense_compare(args, mate, torch):
     """The quadratic mixer MATE replaces, at the workload's L, heads and head
     size: dense softmax attention over all tokens (lingen_dense_attn_fwd)
@@ -384,6 +429,8 @@ def main(argv=None):
     ap.add_argument("--sdpa", action="store_true",
                     help="with --dense, also time torch's fused scaled_dot_product_attention on the same "
                          "tensors, as context for the dense kernel")
+    ap.add_argument("--te-bwd", action="store_true",
+                    help="instead of the benchmark line, time the TE branch's backward pass against its forward")
     ap.add_argument("--dense", action="store_true",
                     help="instead of the benchmark line, time dense softmax attention over all tokens (the "
                          "quadratic mixer MATE replaces) against the MATE forward on the workload")
@@ -413,6 +460,8 @@ def main(argv=None):
         return gather_modes(args, mate, torch)
     if args.dense:
         return dense_compare(args, mate, torch)
+    if args.te_bwd:
+        return te_backward(args, mate, torch)
     s = CONFIGS[args.config]
     workload = CONFIG_NOTES[args.config]
     print(f"[bench] generating inputs: {workload}, {s.L} tokens", file=sys.stderr, flush=True)

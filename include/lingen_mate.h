@@ -179,6 +179,26 @@ int lingen_te_fwd_shift(const void* q, const void* k, const void* v,
                         int32_t shift_t, int32_t shift_h, int32_t shift_w, int32_t masked,
                         const lingen_mate_shape* shape, void* y_te, hipStream_t stream);
 
+/* Backward pass of the TE branch: the gradients of y_te =
+ * lingen_te_fwd_shift(q, k, v, shift, masked) for an upstream gradient d_out,
+ *     dv = P^T d_out,  dS = P * (d_out v^T - rowsum(d_out * y_te)),
+ *     dq = dS k / sqrt(d),  dk = dS^T q / sqrt(d)      (per window and head),
+ * P being the softmax weights of a window (the chain rule through the
+ * attention of page "LinGen：基于Mamba机制的线性复杂度高清长视频生成框架",
+ * section 关键算法创新 > TESA, which training the model needs).  The
+ * forward output is recomputed, not passed in.
+ *   q, k, v, d_out:  device, [batch, L, Ha, d] dtype (the forward's inputs and
+ *                    the gradient of its output);
+ *   dq, dk, dv:      device, [batch, L, Ha, d] dtype, written in full; they
+ *                    must not alias the inputs or each other.
+ * Offsets and masking as lingen_te_fwd_shift.  Compiled for BF16 with d = 64
+ * and 4x8x8-token windows (256 tokens); other valid shapes return
+ * LINGEN_ERR_UNSUPPORTED.  Errors as lingen_te_fwd_shift. */
+int lingen_te_bwd(const void* q, const void* k, const void* v, const void* d_out,
+                  int32_t shift_t, int32_t shift_h, int32_t shift_w, int32_t masked,
+                  const lingen_mate_shape* shape, void* dq, void* dk, void* dv,
+                  hipStream_t stream);
+
 /* The mixer: y = MA(mode = layer_idx mod 4) + TE(shifted = layer_idx odd).
  * layer_idx >= 0.  y: device, [batch, L, Hs*P] dtype; it is also used as the
  * staging buffer of the MA branch, so its contents on entry are ignored. */

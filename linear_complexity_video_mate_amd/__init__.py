@@ -24,6 +24,7 @@ from .binding import (
     lingen_rms_index_device,
     lingen_ssd_chunk_states,
     lingen_te_fwd,
+    lingen_te_bwd,
     lingen_te_fwd_shift,
     status_str,
     to_c_shape,
@@ -48,6 +49,7 @@ __all__ = [
     "lingen_rms_index_device",
     "lingen_ssd_chunk_states",
     "lingen_te_fwd",
+    "lingen_te_bwd",
     "lingen_te_fwd_shift",
     "status_str",
     "to_c_shape",

@@ -41,6 +41,7 @@ EXPORTS = (
     "lingen_ma_fwd",
     "lingen_te_fwd",
     "lingen_te_fwd_shift",
+    "lingen_te_bwd",
     "lingen_mate_fwd",
     "lingen_mate_fwd_events",
     "lingen_dense_attn_fwd",
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
         "lingen_ma_fwd": ([P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_te_fwd": ([P, P, P, I32, SP, P, P], ctypes.c_int),
         "lingen_te_fwd_shift": ([P, P, P, I32, I32, I32, I32, SP, P, P], ctypes.c_int),
+        "lingen_te_bwd": ([P, P, P, P, I32, I32, I32, I32, SP, P, P, P, P], ctypes.c_int),
         "lingen_mate_fwd": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_mate_fwd_events": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P, P], ctypes.c_int),
         "lingen_dense_attn_fwd": ([P, P, P, P, I32, I32, I32, I32, I32, P], ctypes.c_int),
@@ -295,6 +297,23 @@ def lingen_te_fwd_shift(q, k, v, shift, masked: int, shape, out=None):
     _check("lingen_te_fwd_shift", lib().lingen_te_fwd_shift(*args, st, sh, sw, int(masked), ctypes.byref(cs), py,
                                                             _stream()))
     return out
+
+
+def lingen_te_bwd(q, k, v, d_out, shift, masked: int, shape, dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) of the TE branch for the upstream gradient
+    ``d_out`` of its output; window offset ``shift`` and ``masked`` as in
+    lingen_te_fwd_shift."""
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    torch = _torch()
+    outs = [t if t is not None else torch.empty_like(q) for t in (dq, dk, dv)]
+    args = [_need(q, "q", td, n["q"]), _need(k, "k", td, n["q"]), _need(v, "v", td, n["q"]),
+            _need(d_out, "d_out", td, n["q"])]
+    pouts = [_need(t, name, td, n["q"]) for t, name in zip(outs, ("dq", "dk", "dv"))]
+    st, sh, sw = (int(a) for a in shift)
+    _check("lingen_te_bwd", lib().lingen_te_bwd(*args, st, sh, sw, int(masked), ctypes.byref(cs), *pouts, _stream()))
+    return tuple(outs)
 
 
 def lingen_mate_fwd(x, dt, A, B, C, D, q, k, v, layer_idx: int, shape, out=None, workspace=None):

@@ -40,6 +40,7 @@
 
 #include "lingen_device.h"
 #include "lingen_internal.h"
+#include "lingen_window.h"
 
 namespace lingen {
 
@@ -966,14 +967,6 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 //         read from the row-major V tile with LDS transpose loads)
 // ---------------------------------------------------------------------------
 
-struct WinGeom {
-  int T, H, W;
-  int wt, wh, ww;
-  int st, sh, sw;   // grid offset per axis, 0 <= shift < window (0 on unshifted layers)
-  int nwt, nwh, nww;  // windows per axis (T/wt, ...)
-  int masked;         // 1: wrapped tokens form windows of their own (Swin); 0: cyclic windows
-};
-
 template <typename TS, int DH, int NWIN>
 struct AttnCfg {
   static constexpr int QTILES = NWIN / 16;
@@ -1053,21 +1046,14 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
   // Token index and wrap class of every slot of an item's window.
   auto item_tokens = [&](const ItemPos& p, int* tok, int* cls) {
     if (tid < NWIN) {
-      int t = p.wi * wg.wt + slot_a + wg.st, hh = p.wj * wg.wh + slot_b + wg.sh, w = p.wk * wg.ww + slot_c + wg.sw;
-      int cl = 0;
-      if (t >= wg.T) { t -= wg.T; cl |= 4; }
-      if (hh >= wg.H) { hh -= wg.H; cl |= 2; }
-      if (w >= wg.W) { w -= wg.W; cl |= 1; }
-      tok[tid] = (t * wg.H + hh) * wg.W + w;
+      int cl;
+      tok[tid] = window_token(wg, p.wi, p.wj, p.wk, slot_a, slot_b, slot_c, cl);
       // Class 8 (padding) matches no query of the window; cyclic windows
       // (masking off) put every real slot in class 0.
       cls[tid] = (kPadded && tid >= NVALID) ? 8 : (wg.masked ? cl : 0);
     }
   };
-  // The window holds wrapped tokens iff it is the last one along a shifted axis.
-  auto item_wrapped = [&](const ItemPos& p) {
-    return (wg.st > 0 && p.wi == wg.nwt - 1) || (wg.sh > 0 && p.wj == wg.nwh - 1) || (wg.sw > 0 && p.wk == wg.nww - 1);
-  };
+  auto item_wrapped = [&](const ItemPos& p) { return window_wrapped(wg, p.wi, p.wj, p.wk); };
   // Direct global-to-LDS loads of an item's K and V tiles.
   auto issue_kv = [&](MT* dK, MT* dV, const int* tok, int h) {
 #pragma unroll
@@ -1458,12 +1444,7 @@ int dispatch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, ch
 template <typename TS, int DH, int NWIN, int NVALID>
 int launch_te(const lingen_mate_shape* s, const int shift[3], int masked, const void* q, const void* k,
               const void* v, void* y, int accumulate, hipStream_t st) {
-  WinGeom g;
-  g.T = s->T; g.H = s->H; g.W = s->W;
-  g.wt = s->win_t; g.wh = s->win_h; g.ww = s->win_w;
-  g.st = shift[0]; g.sh = shift[1]; g.sw = shift[2];
-  g.nwt = s->T / s->win_t; g.nwh = s->H / s->win_h; g.nww = s->W / s->win_w;
-  g.masked = masked;
+  const WinGeom g = make_wingeom(s, shift, masked);
   const int64_t L = tokens(s);
   const int nwin = g.nwt * g.nwh * g.nww;
   const int64_t per = L * s->attn_heads * DH * elem_bytes(s);

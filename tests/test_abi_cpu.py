@@ -185,6 +185,25 @@ def test_te_shift_rejects_before_launch(L):
     assert call(F, F, F, 1, 3, 3, 0, ctypes.byref(cs), ctypes.c_void_p(MISALIGNED), None) == -4
 
 
+def test_te_bwd_rejects_before_launch(L):
+    F = ctypes.c_void_p(FAKE)
+    Z = ctypes.c_void_p(0)
+    call = L.lingen_te_bwd
+    cs1 = mate.to_c_shape(CONFIGS[1])
+    for st, sh, sw, masked in ((4, 0, 0, 1), (0, -1, 0, 1), (0, 0, 8, 0), (0, 0, 0, 3)):
+        assert call(F, F, F, F, st, sh, sw, masked, ctypes.byref(cs1), F, F, F, None) == -2
+    for i in range(7):
+        p = [F] * 7
+        p[i] = Z
+        assert call(*p[:4], 2, 4, 4, 1, ctypes.byref(cs1), *p[4:], None) == -1, i
+        p[i] = ctypes.c_void_p(MISALIGNED)
+        assert call(*p[:4], 2, 4, 4, 1, ctypes.byref(cs1), *p[4:], None) == -4, i
+    # only the bf16 / d 64 / 256-token window family has a backward kernel
+    cs0 = mate.to_c_shape(CONFIGS[0])
+    assert call(F, F, F, F, 1, 2, 2, 1, ctypes.byref(cs0), F, F, F, None) == -7
+    assert call(F, F, F, F, 1, 2, 2, 1, None, F, F, F, None) == -1
+
+
 def test_odd_window_shapes_validate(L):
     for T in (12, 24):
         s = CONFIGS[1].with_(T=T, H=T, W=T, win=(3, 3, 3))

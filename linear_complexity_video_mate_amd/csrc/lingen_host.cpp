@@ -1,6 +1,7 @@
 // Host-side part of the MATE mixer library: argument validation, workspace
 // planning and the host copy of the Rotary Major Scan index maps.  Nothing in
 // this file calls into HIP, so all of it can be exercised without a GPU.
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 
@@ -33,6 +34,22 @@ AttnFamily attn_family(const lingen_mate_shape* s) {
   if (s->dtype == LINGEN_BF16 && s->attn_headdim == 64 && nw == 256) return ATTN_BF16_D64_W256;
   if (s->dtype == LINGEN_BF16 && s->attn_headdim == 64 && nw == 27) return ATTN_BF16_D64_W27;
   return ATTN_NONE;
+}
+
+// Compute units of the current device, cached per device (the only state
+// the library keeps; concurrent first calls store the same value).
+int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 int check_ptr(const void* p) {

@@ -32,5 +32,6 @@ WsLayout ws_layout(const lingen_mate_shape* s);
 ScanFamily scan_family(const lingen_mate_shape* s);
 AttnFamily attn_family(const lingen_mate_shape* s);
 int check_ptr(const void* p);                      // NULL / alignment check
+int compute_units();                               // of the current device (cached per device), -1 on error
 
 }  // namespace lingen

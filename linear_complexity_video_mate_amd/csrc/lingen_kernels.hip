@@ -34,7 +34,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -1321,21 +1320,6 @@ int hip_status() {
 
 RmsMap make_rms(const lingen_mate_shape* s, int mode) { return RmsMap{mode, s->T, s->H, s->W}; }
 
-// Compute units of the current device, cached per device (the only state
-// the library keeps; concurrent first calls store the same value).
-int compute_units() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-  if (dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
 
 // Heads per chunk workgroup: the largest divisor of Hs not above `cap`.
 int head_group(int Hs, int cap = kHeadGroupMax) {

@@ -6,14 +6,15 @@
 // s = 1/sqrt(d) and D_i = sum_d dO_i[d] o_i[d] = sum_j P_ij dP_ij:
 //   dP = dO v^T,   dS = P * (dP - D),   dq = s dS k,   dk = s dS^T q,   dv = P^T dO.
 //
-// One workgroup of 16 waves per (window, head) item; the item's q, k, v and
+// One workgroup of 8 waves per (window, head) item; the item's q, k, v and
 // dO tiles (256 x 64 bf16 each) sit in LDS, filled by direct global-to-LDS
-// loads.  Phase 1, wave w owning queries 16w..16w+15: an online-softmax sweep
-// over 64-key blocks gives the row maximum and sum and the output o (fp32),
-// hence log-sum-exp and D; a second sweep recomputes P, forms dP^T = V dO^T
-// and dS^T, and accumulates dq^T = K^T dS^T.  Phase 2, wave w owning keys
-// 16w..16w+15, sweeps 32-query blocks: P and dP from Q K^T and dO V^T with
-// the stored per-query statistics, then dv^T = dO^T P and dk^T = Q^T dS.
+// loads.  Phase 1, each wave owning two 16-query tiles: an online-softmax
+// sweep over 32-key blocks gives the row maximum and sum and the output o
+// (fp32), hence log-sum-exp and D; a second sweep recomputes P, forms
+// dP^T = V dO^T and dS^T, and accumulates dq^T = K^T dS^T.  Phase 2, each
+// wave owning two 16-key tiles, sweeps 32-query blocks: P and dP from Q K^T
+// and dO V^T with the stored per-query statistics, then dv^T = dO^T P and
+// dk^T = Q^T dS.  The fragments a block reads from LDS serve both tiles.
 // Every product is a 16x16x32 bf16 MFMA with fp32 accumulation; the
 // k-permuted register operands and the transposing LDS reads are those of
 // the forward window kernel.
@@ -31,6 +32,7 @@ namespace lingen {
 namespace {
 
 constexpr int kBwdWin = 256, kBwdDim = 64;
+constexpr int kBwdTiles = 2;   // 16-row tiles per wave
 
 // 4-element pieces of the 16-wide d-tiles 2 r1 and 2 r1 + 1 exchanged between
 // lane groups g and g ^ 1: the lane then holds d0 .. d0 + 7 of its row,
@@ -53,11 +55,18 @@ __device__ __forceinline__ void store_rows16(__bf16* row, const f32x4 (&acc)[4],
 
 }  // namespace
 
-__global__ __launch_bounds__(1024) void tesa_bwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                                        const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
-                                                        WinGeom wg, int Ha, __bf16* __restrict__ dq,
-                                                        __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
+// QT row tiles of 16 per wave (16 / QT waves): the operand fragments read
+// from LDS for a block are shared by the wave's QT tiles.
+template <int QT>
+__global__ __launch_bounds__(64 * 16 / QT) void tesa_bwd_kernel(const __bf16* __restrict__ q,
+                                                                const __bf16* __restrict__ k,
+                                                                const __bf16* __restrict__ v,
+                                                                const __bf16* __restrict__ dO, WinGeom wg, int Ha,
+                                                                __bf16* __restrict__ dq, __bf16* __restrict__ dk,
+                                                                __bf16* __restrict__ dv) {
   constexpr int NWIN = kBwdWin, DH = kBwdDim, ET = DH / 16, NKS = DH / 32;
+  constexpr int NW = 16 / QT, NTHR = NW * 64;
+  static_assert(NWIN == 16 * QT * NW, "one 16-row tile per wave and QT");
   using KT = KvTile<__bf16, DH>;
   __shared__ __attribute__((aligned(16))) __bf16 sQ[NWIN * DH];
   __shared__ __attribute__((aligned(16))) __bf16 sK[NWIN * DH];
@@ -75,26 +84,25 @@ __global__ __launch_bounds__(1024) void tesa_bwd_kernel(const __bf16* __restrict
   const int nwin_hw = wg.nwh * wg.nww;
   const int wi = win / nwin_hw, wj = (win / wg.nww) % wg.nwh, wk = win % wg.nww;
   const int64_t rowstride = int64_t(Ha) * DH;
+  const int64_t hoff = int64_t(h) * DH;
   const float sc = kLog2e * rsqrtf(float(DH));   // scores in log2 units
   const float snat = rsqrtf(float(DH));          // 1/sqrt(d)
 
-  {
-    const int a = tid / (wg.wh * wg.ww), b = (tid / wg.ww) % wg.wh, c = tid % wg.ww;
-    if (tid < NWIN) {
-      int cl;
-      sTok[tid] = window_token(wg, wi, wj, wk, a, b, c, cl);
-      sCls[tid] = wg.masked ? cl : 0;
-    }
+  for (int u = tid; u < NWIN; u += NTHR) {
+    const int a = u / (wg.wh * wg.ww), b = (u / wg.ww) % wg.wh, c = u % wg.ww;
+    int cl;
+    sTok[u] = window_token(wg, wi, wj, wk, a, b, c, cl);
+    sCls[u] = wg.masked ? cl : 0;
   }
   lds_barrier();
   // Direct loads of the four tiles: 16-byte chunk u of a tile is row u/8,
   // chunk (u%8) ^ (row%8) of that row (the KvTile permutation).
-  constexpr int PER_WAVE = NWIN * 8 / (16 * 64);   // load instructions per wave and tile
+  constexpr int PER_WAVE = NWIN * 8 / (NW * 64);   // load instructions per wave and tile
 #pragma unroll
   for (int d = 0; d < PER_WAVE; ++d) {
     const int base = (wave * PER_WAVE + d) * 64;
     const int u = base + lane, row = u / 8, ch = (u % 8) ^ (row & 7);
-    const int64_t goff = int64_t(sTok[row]) * rowstride + int64_t(h) * DH + ch * 8;
+    const int64_t goff = int64_t(sTok[row]) * rowstride + hoff + ch * 8;
     lds_load16(q + goff, sQ + base * 8);
     lds_load16(k + goff, sK + base * 8);
     lds_load16(v + goff, sV + base * 8);
@@ -133,165 +141,228 @@ __global__ __launch_bounds__(1024) void tesa_bwd_kernel(const __bf16* __restrict
     }
     return p;
   };
+  auto mask = [&](f32x4& s, int j0, int c) {
+    const int4 kc = *reinterpret_cast<const int4*>(&sCls[j0 + 4 * grp]);
+    const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = kcv[r] != c ? -INFINITY : s[r];
+  };
 
-  // ---------------- Phase 1: queries i = 16 wave + r16 --------------------
+  // ---------------- Phase 1: the wave's query tiles -----------------------
   {
-    const int i0 = wave * 16;
-    const int icls = sCls[i0 + r16];
-    bf16x8 qf[NKS], gf[NKS];
+    int icls[QT];
+    bf16x8 qf[QT][NKS], gf[QT][NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      qf[ks] = rowfrag(sQ, i0, ks);
-      gf[ks] = rowfrag(sG, i0, ks);
-    }
-    // S^T tile (16 keys from row j0) for the lane's query column, masked.
-    auto scores = [&](int j0) {
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < QT; ++qt) {
+      const int i0 = (wave * QT + qt) * 16;
+      icls[qt] = sCls[i0 + r16];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) s = mma(rowfrag(sK, j0, ks), qf[ks], s);
-      if (wrapped) {
-        const int4 kc = *reinterpret_cast<const int4*>(&sCls[j0 + 4 * grp]);
-        const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = kcv[r] != icls ? -INFINITY : s[r];
+      for (int ks = 0; ks < NKS; ++ks) {
+        qf[qt][ks] = rowfrag(sQ, i0, ks);
+        gf[qt][ks] = rowfrag(sG, i0, ks);
       }
-      return s;
-    };
-    // Sweep 1: online softmax statistics and the output o.
-    float m = -INFINITY, l = 0.f;
-    f32x4 o[ET];
+    }
+    // Sweep 1: online softmax statistics and the output o, 32 keys a step.
+    float m[QT], l[QT];
+    f32x4 o[QT][ET];
 #pragma unroll
-    for (int et = 0; et < ET; ++et) o[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < QT; ++qt) {
+      m[qt] = -INFINITY;
+      l[qt] = 0.f;
+#pragma unroll
+      for (int et = 0; et < ET; ++et) o[qt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll 1
-    for (int jb = 0; jb < NWIN; jb += 64) {
-      f32x4 s[4];
+    for (int jb = 0; jb < NWIN; jb += 32) {
+      bf16x8 kfr[2][NKS], vtr[ET];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s[t] = scores(jb + 16 * t);
-      float bm = -INFINITY;
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bm = fmaxf(bm, fmaxf(fmaxf(s[t][0], s[t][1]), fmaxf(s[t][2], s[t][3])));
-      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-      const float mnew = fmaxf(m, bm * sc);
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = fast_exp2(m - mref);
-      m = mnew;
-      float ls = 0.f;
+        for (int ks = 0; ks < NKS; ++ks) kfr[t][ks] = rowfrag(sK, jb + 16 * t, ks);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int et = 0; et < ET; ++et) vtr[et] = trfrag(sV, jb, et);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s[t][r] = fast_exp2(fmaf(s[t][r], sc, -mref));
-          ls += s[t][r];
+      for (int qt = 0; qt < QT; ++qt) {
+        f32x4 s[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) s[t] = mma(kfr[t][ks], qf[qt][ks], s[t]);
+          if (wrapped) mask(s[t], jb + 16 * t, icls[qt]);
         }
-      l = fmaf(l, alpha, ls);
+        float bm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        const float mnew = fmaxf(m[qt], bm * sc);
+        const float mref = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = fast_exp2(m[qt] - mref);
+        m[qt] = mnew;
+        float ls = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            s[t][r] = fast_exp2(fmaf(s[t][r], sc, -mref));
+            ls += s[t][r];
+          }
+        l[qt] = fmaf(l[qt], alpha, ls);
+        const bf16x8 pb = pack(s[0], s[1]);
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[qt][et][r] *= alpha;
+          o[qt][et] = mma(vtr[et], pb, o[qt][et]);
+        }
+      }
+    }
+    float lse[QT], dsum[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int i0 = (wave * QT + qt) * 16;
+      float lt = l[qt];
+      lt += __shfl_xor(lt, 16, 64);
+      lt += __shfl_xor(lt, 32, 64);
+      const float inv = 1.f / lt;
+      // D_i = sum_d dO_i[d] o_i[d]: the lane holds o for d = et*16 + 4g + r.
+      float ds_ = 0.f;
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
+        const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(sG + KT::at(i0 + r16, et * 16 + 4 * grp));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[et][r] *= alpha;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-          o[et] = mma(trfrag(sV, jb + 32 * sb, et), pack(s[2 * sb], s[2 * sb + 1]), o[et]);
+        for (int r = 0; r < 4; ++r) ds_ = fmaf(static_cast<float>(g4[r]), o[qt][et][r] * inv, ds_);
+      }
+      ds_ += __shfl_xor(ds_, 16, 64);
+      ds_ += __shfl_xor(ds_, 32, 64);
+      dsum[qt] = ds_;
+      lse[qt] = m[qt] + log2f(lt);
+      if (grp == 0) {
+        sLse[i0 + r16] = lse[qt];
+        sD[i0 + r16] = ds_;
       }
     }
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float inv = 1.f / l;
-    // D_i = sum_d dO_i[d] o_i[d]: the lane holds o for d = et*16 + 4g + r.
-    float dsum = 0.f;
+    // Sweep 2: dS^T and dq^T = K^T dS^T, 32 keys a step.
+    f32x4 gq[QT][ET];
 #pragma unroll
-    for (int et = 0; et < ET; ++et) {
-      const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(sG + KT::at(i0 + r16, et * 16 + 4 * grp));
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dsum = fmaf(static_cast<float>(g4[r]), o[et][r] * inv, dsum);
-    }
-    dsum += __shfl_xor(dsum, 16, 64);
-    dsum += __shfl_xor(dsum, 32, 64);
-    const float lse = m + log2f(l);
-    if (grp == 0) {
-      sLse[i0 + r16] = lse;
-      sD[i0 + r16] = dsum;
-    }
-    // Sweep 2: dS^T and dq^T = K^T dS^T.
-    f32x4 gq[ET];
-#pragma unroll
-    for (int et = 0; et < ET; ++et) gq[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int et = 0; et < ET; ++et) gq[qt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-    for (int jb = 0; jb < NWIN; jb += 64) {
-      f32x4 ds[4];
+    for (int jb = 0; jb < NWIN; jb += 32) {
+      bf16x8 kfr[2][NKS], vfr[2][NKS], ktr[ET];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int j0 = jb + 16 * t;
-        const f32x4 s = scores(j0);
-        f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) dp = mma(rowfrag(sV, j0, ks), gf[ks], dp);
+        for (int ks = 0; ks < NKS; ++ks) {
+          kfr[t][ks] = rowfrag(sK, jb + 16 * t, ks);
+          vfr[t][ks] = rowfrag(sV, jb + 16 * t, ks);
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ds[t][r] = fast_exp2(fmaf(s[r], sc, -lse)) * (dp[r] - dsum);
+      for (int et = 0; et < ET; ++et) ktr[et] = trfrag(sK, jb, et);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        f32x4 ds[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            s = mma(kfr[t][ks], qf[qt][ks], s);
+            dp = mma(vfr[t][ks], gf[qt][ks], dp);
+          }
+          if (wrapped) mask(s, jb + 16 * t, icls[qt]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ds[t][r] = fast_exp2(fmaf(s[r], sc, -lse[qt])) * (dp[r] - dsum[qt]);
+        }
+        const bf16x8 db = pack(ds[0], ds[1]);
+#pragma unroll
+        for (int et = 0; et < ET; ++et) gq[qt][et] = mma(ktr[et], db, gq[qt][et]);
       }
-#pragma unroll
-      for (int et = 0; et < ET; ++et)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-          gq[et] = mma(trfrag(sK, jb + 32 * sb, et), pack(ds[2 * sb], ds[2 * sb + 1]), gq[et]);
     }
-    store_rows16(dq + int64_t(sTok[i0 + r16]) * rowstride + int64_t(h) * DH, gq, snat, grp);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int i = (wave * QT + qt) * 16 + r16;
+      store_rows16(dq + int64_t(sTok[i]) * rowstride + hoff, gq[qt], snat, grp);
+    }
   }
   lds_barrier();   // every query's statistics are in LDS
 
-  // ---------------- Phase 2: keys j = 16 wave + r16 -----------------------
+  // ---------------- Phase 2: the wave's key tiles -------------------------
   {
-    const int j0 = wave * 16;
-    const int jcls = sCls[j0 + r16];
-    bf16x8 kf[NKS], vf[NKS];
+    int jcls[QT];
+    bf16x8 kf[QT][NKS], vf[QT][NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = rowfrag(sK, j0, ks);
-      vf[ks] = rowfrag(sV, j0, ks);
-    }
-    f32x4 gk[ET], gv[ET];
+    for (int kt = 0; kt < QT; ++kt) {
+      const int j0 = (wave * QT + kt) * 16;
+      jcls[kt] = sCls[j0 + r16];
 #pragma unroll
-    for (int et = 0; et < ET; ++et) {
-      gk[et] = f32x4{0.f, 0.f, 0.f, 0.f};
-      gv[et] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll 1
-    for (int ib = 0; ib < NWIN; ib += 32) {
-      f32x4 p[2], ds[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int i0 = ib + 16 * t;   // lane holds rows i0 + 4g + r, column j0 + r16
-        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          s = mma(rowfrag(sQ, i0, ks), kf[ks], s);
-          dp = mma(rowfrag(sG, i0, ks), vf[ks], dp);
-        }
-        const float4 lse = *reinterpret_cast<const float4*>(&sLse[i0 + 4 * grp]);
-        const float4 dd = *reinterpret_cast<const float4*>(&sD[i0 + 4 * grp]);
-        const float lv[4] = {lse.x, lse.y, lse.z, lse.w}, dv4[4] = {dd.x, dd.y, dd.z, dd.w};
-        int qc[4] = {0, 0, 0, 0};
-        if (wrapped) {
-          const int4 c4 = *reinterpret_cast<const int4*>(&sCls[i0 + 4 * grp]);
-          qc[0] = c4.x; qc[1] = c4.y; qc[2] = c4.z; qc[3] = c4.w;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pv = (wrapped && qc[r] != jcls) ? 0.f : fast_exp2(fmaf(s[r], sc, -lv[r]));
-          p[t][r] = pv;
-          ds[t][r] = pv * (dp[r] - dv4[r]);
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        kf[kt][ks] = rowfrag(sK, j0, ks);
+        vf[kt][ks] = rowfrag(sV, j0, ks);
       }
-      const bf16x8 pb = pack(p[0], p[1]), db = pack(ds[0], ds[1]);
+    }
+    f32x4 gk[QT][ET], gv[QT][ET];
+#pragma unroll
+    for (int kt = 0; kt < QT; ++kt)
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
-        gv[et] = mma(trfrag(sG, ib, et), pb, gv[et]);
-        gk[et] = mma(trfrag(sQ, ib, et), db, gk[et]);
+        gk[kt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+        gv[kt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll 1
+    for (int ib = 0; ib < NWIN; ib += 32) {
+      bf16x8 qfr[2][NKS], gfr[2][NKS];
+      float lv[2][4], dv4[2][4];
+      int qc[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int iq = ib + 16 * t;   // score rows iq + 4g + r
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          qfr[t][ks] = rowfrag(sQ, iq, ks);
+          gfr[t][ks] = rowfrag(sG, iq, ks);
+        }
+        const float4 ls4 = *reinterpret_cast<const float4*>(&sLse[iq + 4 * grp]);
+        const float4 dd = *reinterpret_cast<const float4*>(&sD[iq + 4 * grp]);
+        lv[t][0] = ls4.x; lv[t][1] = ls4.y; lv[t][2] = ls4.z; lv[t][3] = ls4.w;
+        dv4[t][0] = dd.x; dv4[t][1] = dd.y; dv4[t][2] = dd.z; dv4[t][3] = dd.w;
+        const int4 c4 = *reinterpret_cast<const int4*>(&sCls[iq + 4 * grp]);
+        qc[t][0] = c4.x; qc[t][1] = c4.y; qc[t][2] = c4.z; qc[t][3] = c4.w;
+      }
+#pragma unroll
+      for (int kt = 0; kt < QT; ++kt) {
+        f32x4 p[2], ds[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            s = mma(qfr[t][ks], kf[kt][ks], s);
+            dp = mma(gfr[t][ks], vf[kt][ks], dp);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pv = (wrapped && qc[t][r] != jcls[kt]) ? 0.f : fast_exp2(fmaf(s[r], sc, -lv[t][r]));
+            p[t][r] = pv;
+            ds[t][r] = pv * (dp[r] - dv4[t][r]);
+          }
+        }
+        const bf16x8 pb = pack(p[0], p[1]), db = pack(ds[0], ds[1]);
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+          gv[kt][et] = mma(trfrag(sG, ib, et), pb, gv[kt][et]);
+          gk[kt][et] = mma(trfrag(sQ, ib, et), db, gk[kt][et]);
+        }
       }
     }
-    const int64_t roff = int64_t(sTok[j0 + r16]) * rowstride + int64_t(h) * DH;
-    store_rows16(dk + roff, gk, snat, grp);
-    store_rows16(dv + roff, gv, 1.f, grp);
+#pragma unroll
+    for (int kt = 0; kt < QT; ++kt) {
+      const int j = (wave * QT + kt) * 16 + r16;
+      const int64_t roff = int64_t(sTok[j]) * rowstride + hoff;
+      store_rows16(dk + roff, gk[kt], snat, grp);
+      store_rows16(dv + roff, gv[kt], 1.f, grp);
+    }
   }
 }
 
@@ -317,7 +388,7 @@ extern "C" int lingen_te_bwd(const void* q, const void* k, const void* v, const 
   const int64_t per = L * shape->attn_heads * kBwdDim;   // elements per batch element
   for (int b = 0; b < shape->batch; ++b) {
     const int64_t off = int64_t(b) * per;
-    tesa_bwd_kernel<<<items, 1024, 0, stream>>>(
+    tesa_bwd_kernel<kBwdTiles><<<items, 64 * 16 / kBwdTiles, 0, stream>>>(
         static_cast<const __bf16*>(q) + off, static_cast<const __bf16*>(k) + off, static_cast<const __bf16*>(v) + off,
         static_cast<const __bf16*>(d_out) + off, g, shape->attn_heads, static_cast<__bf16*>(dq) + off,
         static_cast<__bf16*>(dk) + off, static_cast<__bf16*>(dv) + off);

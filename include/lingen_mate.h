@@ -156,6 +156,23 @@ int lingen_ma_fwd(const void* x, const float* dt, const float* A, const void* B,
                   const lingen_mate_shape* shape, void* y_ma,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* MA branch with a parameter set per scan direction (the reading in which
+ * the two directions of the bidirectional Mamba2 block keep weights of their
+ * own; lingen_ma_fwd and lingen_mate_fwd share one set between them):
+ *   y_ma = scan(x_f, dt_f, A_f, B_f, C_f, D_f along the order of `mode`)
+ *        + scan(x_b, dt_b, A_b, B_b, C_b, D_b along the reversed order),
+ * each scan carrying its own skip D x (so y_ma holds D_f x_f + D_b x_b).
+ * Layouts, dtypes and workspace as lingen_ma_fwd, for both sets.  Review
+ * tokens are not supported here (shape->n_review must be 0, else
+ * LINGEN_ERR_UNSUPPORTED).  The forward scan's result is rounded to the
+ * output dtype before the backward scan's is added. */
+int lingen_ma_fwd_dirs(const void* x_f, const float* dt_f, const float* A_f, const void* B_f,
+                       const void* C_f, const float* D_f,
+                       const void* x_b, const float* dt_b, const float* A_b, const void* B_b,
+                       const void* C_b, const float* D_b,
+                       int32_t mode, const lingen_mate_shape* shape, void* y_ma,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* TE branch alone: y_te = windowed softmax attention with the window grid
  * shifted by (win_t/2, win_h/2, win_w/2) if `shifted` != 0; border windows are
  * cut, not wrapped.  Scale 1/sqrt(d).  y_te: device, layout of y. */

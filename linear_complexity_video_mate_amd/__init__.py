@@ -15,6 +15,7 @@ from .binding import (
     lib,
     lingen_dense_attn_fwd,
     lingen_ma_fwd,
+    lingen_ma_fwd_dirs,
     lingen_mate_fwd,
     lingen_mate_fwd_events,
     lingen_mate_validate,
@@ -40,6 +41,7 @@ __all__ = [
     "lib",
     "lingen_dense_attn_fwd",
     "lingen_ma_fwd",
+    "lingen_ma_fwd_dirs",
     "lingen_mate_fwd",
     "lingen_mate_fwd_events",
     "lingen_mate_validate",

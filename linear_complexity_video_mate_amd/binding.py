@@ -39,6 +39,7 @@ EXPORTS = (
     "lingen_rms_gather",
     "lingen_ssd_chunk_states",
     "lingen_ma_fwd",
+    "lingen_ma_fwd_dirs",
     "lingen_te_fwd",
     "lingen_te_fwd_shift",
     "lingen_te_bwd",
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
         "lingen_rms_gather": ([P, I64, I32, I32, I32, I32, P, P], ctypes.c_int),
         "lingen_ssd_chunk_states": ([P, P, P, P, I32, SP, P, P, P, SZ, P], ctypes.c_int),
         "lingen_ma_fwd": ([P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
+        "lingen_ma_fwd_dirs": ([P] * 12 + [I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_te_fwd": ([P, P, P, I32, SP, P, P], ctypes.c_int),
         "lingen_te_fwd_shift": ([P, P, P, I32, I32, I32, I32, SP, P, P], ctypes.c_int),
         "lingen_te_bwd": ([P, P, P, P, I32, I32, I32, I32, SP, P, P, P, P], ctypes.c_int),
@@ -262,6 +264,27 @@ def lingen_ma_fwd(x, dt, A, B, C, D, mode: int, shape, out=None, workspace=None)
     py = _need(out, "out", td, n["y"])
     workspace, pw, nw = _workspace(shape, workspace)
     _check("lingen_ma_fwd", lib().lingen_ma_fwd(*args, mode, ctypes.byref(cs), py, pw, nw, _stream()))
+    return out
+
+
+def lingen_ma_fwd_dirs(fwd, bwd, mode: int, shape, out=None, workspace=None):
+    """MA branch with a parameter set per direction: ``fwd`` and ``bwd`` are
+    (x, dt, A, B, C, D) tuples; returns y_ma [batch, L, Hs*P]."""
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    L = shape.T * shape.H * shape.W
+    if out is None:
+        out = torch.empty((shape.batch, L, shape.ssd_heads * shape.headdim), dtype=td, device="cuda")
+    args = []
+    for tag, (x, dt, A, B, C, D) in (("f", fwd), ("b", bwd)):
+        args += [_need(x, "x_" + tag, td, n["x"]), _need(dt, "dt_" + tag, torch.float32, n["dt"]),
+                 _need(A, "A_" + tag, torch.float32, n["A"]), _need(B, "B_" + tag, td, n["B"]),
+                 _need(C, "C_" + tag, td, n["B"]), _need(D, "D_" + tag, torch.float32, n["D"])]
+    py = _need(out, "out", td, n["y"])
+    workspace, pw, nw = _workspace(shape, workspace)
+    _check("lingen_ma_fwd_dirs", lib().lingen_ma_fwd_dirs(*args, mode, ctypes.byref(cs), py, pw, nw, _stream()))
     return out
 
 

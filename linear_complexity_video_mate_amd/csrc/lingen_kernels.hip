@@ -170,9 +170,13 @@ __device__ __forceinline__ void st_pair_f32(float* dst, float lo, float hi) { st
 //   mode 1: s = (t*W + w)*H + h   H first, then W, then T
 //   mode 2: s = (h*W + w)*T + t   T first, then W, then H
 //   mode 3: s = (w*H + h)*T + t   T first, then H, then W
+// rev = 1 walks the order backwards (scan position s is position L-1-s of
+// the mode's order): the backward scan of a direction-specific parameter set.
 struct RmsMap {
   int mode, T, H, W;
+  int rev = 0;
   __device__ __forceinline__ int canon(int s) const {
+    if (rev) s = T * H * W - 1 - s;
     int t, h, w;
     switch (mode) {
       case 0: return s;
@@ -444,7 +448,9 @@ struct StateCfg {
 // consecutive tokens far apart, while the transposed LDS stores stay
 // spread over the banks.
 constexpr int kLptX = 2, kLptB = 2;
-template <typename TS, int P, int N, int Q>
+// BIDIR = false: the forward direction's chunk states only (a scan whose
+// backward direction has parameters of its own).
+template <typename TS, int P, int N, int Q, bool BIDIR = true>
 __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
                                                               const float* __restrict__ A, const TS* __restrict__ B,
                                                               RmsMap rms, int Hs, int G, int hg, int n_chunks,
@@ -517,7 +523,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
       for (int e = 0; e < VEC; ++e) {
         const float x0 = to_f32(va.e[e]), x1 = to_f32(vb.e[e]);
         st_pair_f32(&sXf[TQ::at(p0 + e, s0)], x0 * wf0, x1 * wf1);
-        st_pair_f32(&sXb[TQ::at(p0 + e, s0)], x0 * wb0, x1 * wb1);
+        if constexpr (BIDIR) st_pair_f32(&sXb[TQ::at(p0 + e, s0)], x0 * wb0, x1 * wb1);
       }
     });
     lds_barrier();
@@ -537,7 +543,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
       for (int i = 0; i < PT_PER; ++i) {
         const int pt = wp + i * WP;
         af[i] = TQ::frag(sXf, pt * 16 + r16, ks * KI, lane);
-        ab[i] = TQ::frag(sXb, pt * 16 + r16, ks * KI, lane);
+        if constexpr (BIDIR) ab[i] = TQ::frag(sXb, pt * 16 + r16, ks * KI, lane);
       }
 #pragma unroll
       for (int j = 0; j < NT_PER; ++j) {
@@ -547,7 +553,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
 #pragma unroll
           for (int i = 0; i < PT_PER; ++i) {
             accf[i][j] = mma(af[i], bf, accf[i][j]);
-            accb[i][j] = mma(ab[i], bf, accb[i][j]);
+            if constexpr (BIDIR) accb[i][j] = mma(ab[i], bf, accb[i][j]);
           }
         }
       }
@@ -563,13 +569,13 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             sOut[out_at(pbase + r, n)] = from_f32<TS>(accf[i][j][r]);
-            sOut[per + out_at(pbase + r, n)] = from_f32<TS>(accb[i][j][r]);
+            if constexpr (BIDIR) sOut[per + out_at(pbase + r, n)] = from_f32<TS>(accb[i][j][r]);
           }
         }
       }
     lds_barrier();
     constexpr int VPD = P * N / VEC;   // 16-byte vectors per direction
-    for (int u = tid; u < 2 * VPD; u += NTHR) {
+    for (int u = tid; u < (BIDIR ? 2 : 1) * VPD; u += NTHR) {
       const int dir = u / VPD, off = u % VPD;
       uint4* dst = reinterpret_cast<uint4*>(states + ((int64_t(dir) * n_chunks + c) * Hs + h) * per);
       dst[off] = reinterpret_cast<const uint4*>(sOut)[dir * VPD + out_at(off / (N / VEC), (off % (N / VEC)) * VEC) / VEC];
@@ -663,7 +669,10 @@ struct OutCfg {
   static_assert(QT <= NW, "one t-tile per wave");
 };
 
-template <typename TS, int P, int N, int Q>
+// BIDIR = false: the forward direction alone (lower triangle and diagonal
+// weight 1, the forward inter-chunk term, D x once), for a scan whose
+// backward direction has parameters of its own; ACC adds the result to y.
+template <typename TS, int P, int N, int Q, bool BIDIR = true, bool ACC = false>
 __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_kernel(
     const TS* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const TS* __restrict__ B,
     const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int G, int hg, int n_chunks,
@@ -718,7 +727,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
     const uint4* hf = reinterpret_cast<const uint4*>(states + (int64_t(c) * Hs + h) * per);
     const uint4* hb = reinterpret_cast<const uint4*>(states + ((int64_t(n_chunks) + c) * Hs + h) * per);
     hb_.hfs.load([&](int u) { return hf[u]; });
-    hb_.hbs.load([&](int u) { return hb[u]; });
+    if constexpr (BIDIR) hb_.hbs.load([&](int u) { return hb[u]; });
   };
   load_head(buf0, h0);
 
@@ -767,9 +776,10 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
     buf.hfs.use([&](int u, uint4 raw) {
       *reinterpret_cast<uint4*>(&sHf[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
     });
-    buf.hbs.use([&](int u, uint4 raw) {
-      *reinterpret_cast<uint4*>(&sHb[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
-    });
+    if constexpr (BIDIR)
+      buf.hbs.use([&](int u, uint4 raw) {
+        *reinterpret_cast<uint4*>(&sHb[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
+      });
     // Off the wave's own t-tile [ts, te] the decay splits at the tile edge
     // into two factors that are both <= 1:
     //   s < ts: e^{cum_t - cum_s}  = e^{cum_t - exc_ts} * e^{exc_ts - cum_s}
@@ -814,13 +824,13 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
         for (int r = 0; r < 4; ++r) {
           const int s = sb + r;
           const float arg = s < t ? cum_t - cv[r] : xv[r] - exc_t;
-          const float lam = s == t ? 2.f : fast_exp2(arg);
+          const float lam = s == t ? (BIDIR ? 2.f : 1.f) : (BIDIR || s < t ? fast_exp2(arg) : 0.f);
           mv[r] = to_f32(g[st][r]) * lam * dv[r];
         }
       } else {
         const float4 v4 = *reinterpret_cast<const float4*>(&sV[wave][sb]);
         const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-        const float fac = st < wt ? fac_lo : fac_hi;
+        const float fac = st < wt ? fac_lo : (BIDIR ? fac_hi : 0.f);
 #pragma unroll
         for (int r = 0; r < 4; ++r) mv[r] = to_f32(g[st][r]) * vv[r] * fac;
       }
@@ -875,8 +885,8 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
     }
 
     // Inter-chunk terms, the skip, and the store.
-    const float ef = fast_exp2(cum_t), eb = fast_exp2(cum[Q - 1] - exc_t);
-    const float twoD = 2.f * D[h];
+    const float ef = fast_exp2(cum_t), eb = BIDIR ? fast_exp2(cum[Q - 1] - exc_t) : 0.f;
+    const float twoD = (BIDIR ? 2.f : 1.f) * D[h];
     // bf16 rows of 64 owned by one wave: the four p-tiles are stored together
     // in 16-byte pieces (see below).
     constexpr bool kP16 = kBf16 && Cfg::PT == 4 && Cfg::P_PER == 4 && Cfg::WPW == 1;
@@ -890,7 +900,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 #pragma unroll
       for (int ks = 0; ks < N / KI; ++ks) {
         zf = mma(TN::frag(sHf, prow, ks * KI, lane), cfr[ks], zf);
-        zb = mma(TN::frag(sHb, prow, ks * KI, lane), cfr[ks], zb);
+        if constexpr (BIDIR) zb = mma(TN::frag(sHb, prow, ks * KI, lane), cfr[ks], zb);
       }
       // Lane holds Y^T[p][t] for p = pt*16 + 4*grp + r.
       const int p0 = pt * 16 + grp * 4;
@@ -907,10 +917,19 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       TS* dst = y + tok_t * (int64_t(Hs) * P) + int64_t(h) * P + p0;
       if constexpr (kBf16) {
         bf16x4 ov;
+        if constexpr (ACC) {
+          const bf16x4 old = *reinterpret_cast<const bf16x4*>(dst);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] += static_cast<float>(old[r]);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) ov[r] = static_cast<__bf16>(o[r]);
         *reinterpret_cast<bf16x4*>(dst) = ov;
       } else {
+        if constexpr (ACC) {
+          const float4 old = *reinterpret_cast<const float4*>(dst);
+          o[0] += old.x; o[1] += old.y; o[2] += old.z; o[3] += old.w;
+        }
         *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
       }
     }
@@ -922,13 +941,20 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       TS* row = y + tok_t * (int64_t(Hs) * P) + int64_t(h) * P + 16 * (grp & 1) + 8 * (grp >> 1);
 #pragma unroll
       for (int r1 = 0; r1 < 2; ++r1) {
+        bf16x8 old;
+        if constexpr (ACC) old = *reinterpret_cast<const bf16x8*>(row + 32 * r1);
         bf16x8 res;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(ob[2 * r1][r]),
                                                            __float_as_uint(ob[2 * r1 + 1][r]), false, false);
-          res[r] = static_cast<__bf16>(__uint_as_float(sw[0]));
-          res[4 + r] = static_cast<__bf16>(__uint_as_float(sw[1]));
+          float lo = __uint_as_float(sw[0]), hi = __uint_as_float(sw[1]);
+          if constexpr (ACC) {
+            lo += static_cast<float>(old[r]);
+            hi += static_cast<float>(old[4 + r]);
+          }
+          res[r] = static_cast<__bf16>(lo);
+          res[4 + r] = static_cast<__bf16>(hi);
         }
         *reinterpret_cast<bf16x8*>(row + 32 * r1) = res;
       }
@@ -1318,7 +1344,7 @@ int hip_status() {
   return e == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
 }
 
-RmsMap make_rms(const lingen_mate_shape* s, int mode) { return RmsMap{mode, s->T, s->H, s->W}; }
+RmsMap make_rms(const lingen_mate_shape* s, int mode, int rev = 0) { return RmsMap{mode, s->T, s->H, s->W, rev}; }
 
 
 // Heads per chunk workgroup: the largest divisor of Hs not above `cap`.
@@ -1354,10 +1380,11 @@ int launch_review(const lingen_mate_shape* s, const TS* x, const float* dt, cons
   return hip_status();
 }
 
-// Phase A + state pass (+ review state) for one batch element.
-template <typename TS, int P, int N, int Q>
+// Phase A + state pass (+ review state) for one batch element.  BIDIR =
+// false: the forward direction of the (possibly reversed, rev = 1) order only.
+template <typename TS, int P, int N, int Q, bool BIDIR = true>
 int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float* dt, const float* A, const TS* B,
-                  char* ws, hipStream_t st, const hipEvent_t* ev = nullptr) {
+                  char* ws, hipStream_t st, const hipEvent_t* ev = nullptr, int rev = 0) {
   const WsLayout lay = ws_layout(s);
   const int L = int(tokens(s));
   const int nc = L / Q;
@@ -1372,8 +1399,8 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
     h0 = reinterpret_cast<const float*>(ws + lay.review_h);
   }
   if (int rc = mark(ev, 1, st)) return rc;
-  ssd_chunk_state_kernel<TS, P, N, Q><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(x, dt, A, B, make_rms(s, mode), Hs, s->ngroups, hg, nc,
-                                                                       states, decay);
+  ssd_chunk_state_kernel<TS, P, N, Q, BIDIR><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(
+      x, dt, A, B, make_rms(s, mode, rev), Hs, s->ngroups, hg, nc, states, decay);
   if (hip_status()) return LINGEN_ERR_HIP;
   if (int rc = mark(ev, 2, st)) return rc;
   // P*N/8 threads per head, in blocks of up to 256 (P*N/8 is 64, 512 or
@@ -1382,8 +1409,8 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
   static_assert((P * N / E) % 64 == 0 && ((P * N / E) < BS || (P * N / E) % BS == 0), "state pass blocking");
   const int bs = (P * N / E) < BS ? (P * N / E) : BS;
   const int64_t thr = int64_t(Hs) * P * N / E;
-  ssd_state_pass_kernel<TS, 8, E><<<dim3(unsigned(thr / bs), 2), bs, 0, st>>>(states, decay, h0, Hs, P * N,
-                                                                                      nc);
+  ssd_state_pass_kernel<TS, 8, E><<<dim3(unsigned(thr / bs), BIDIR ? 2 : 1), bs, 0, st>>>(states, decay, h0, Hs,
+                                                                                           P * N, nc);
   if (hip_status()) return LINGEN_ERR_HIP;
   return mark(ev, 3, st);
 }
@@ -1413,6 +1440,52 @@ int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char
     if (int rc = mark(ev, 4, st)) return rc;
   }
   return LINGEN_OK;
+}
+
+// MA branch with a parameter set per direction: the forward direction of
+// the scan order with af, then the forward direction of the reversed order
+// (the backward scan) with ab, added to the first result.
+template <typename TS, int P, int N, int Q>
+int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const Args& ab, void* y, char* ws,
+                   hipStream_t st) {
+  const int L = int(tokens(s));
+  const int nc = L / Q;
+  const int Hs = s->ssd_heads;
+  const WsLayout lay = ws_layout(s);
+  const int64_t eb = elem_bytes(s);
+  using Cfg = OutCfg<TS, P, N, Q>;
+  const int hg = head_group(Hs / s->ngroups);
+  for (int b = 0; b < s->batch; ++b) {
+    TS* yb = reinterpret_cast<TS*>(static_cast<char*>(y) + int64_t(b) * L * Hs * P * eb);
+    for (int dir = 0; dir < 2; ++dir) {
+      const Args& a = dir ? ab : af;
+      const TS* x = reinterpret_cast<const TS*>(static_cast<const char*>(a.x) + int64_t(b) * L * Hs * P * eb);
+      const float* dt = a.dt + int64_t(b) * L * Hs;
+      const int64_t bc = int64_t(b) * L * s->ngroups * N * eb;
+      const TS* B = reinterpret_cast<const TS*>(static_cast<const char*>(a.B) + bc);
+      const TS* C = reinterpret_cast<const TS*>(static_cast<const char*>(a.C) + bc);
+      if (int rc = launch_states<TS, P, N, Q, false>(s, mode, x, dt, a.A, B, ws, st, nullptr, dir)) return rc;
+      const TS* states = reinterpret_cast<const TS*>(ws + lay.states);
+      if (dir == 0)
+        ssd_chunk_out_kernel<TS, P, N, Q, false, false><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
+            x, dt, a.A, B, C, a.D, make_rms(s, mode, 0), Hs, s->ngroups, hg, nc, states, yb);
+      else
+        ssd_chunk_out_kernel<TS, P, N, Q, false, true><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
+            x, dt, a.A, B, C, a.D, make_rms(s, mode, 1), Hs, s->ngroups, hg, nc, states, yb);
+      if (hip_status()) return LINGEN_ERR_HIP;
+    }
+  }
+  return LINGEN_OK;
+}
+
+int dispatch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const Args& ab, void* y, char* ws,
+                     hipStream_t st) {
+  switch (scan_family(s)) {
+    case SCAN_F32_P32_N16_Q16: return launch_ma_dirs<float, 32, 16, 16>(s, mode, af, ab, y, ws, st);
+    case SCAN_BF16_P64_N64_Q64: return launch_ma_dirs<__bf16, 64, 64, 64>(s, mode, af, ab, y, ws, st);
+    case SCAN_BF16_P64_N128_Q128: return launch_ma_dirs<__bf16, 64, 128, 128>(s, mode, af, ab, y, ws, st);
+    default: return LINGEN_ERR_UNSUPPORTED;
+  }
 }
 
 int dispatch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char* ws, hipStream_t st,
@@ -1578,6 +1651,20 @@ int lingen_ma_fwd(const void* x, const float* dt, const float* A, const void* B,
   if (int rc = check_ws(shape, workspace, workspace_bytes)) return rc;
   Args a{x, dt, A, B, C, D, nullptr, nullptr, nullptr};
   return dispatch_ma(shape, mode, a, y_ma, static_cast<char*>(workspace), stream);
+}
+
+int lingen_ma_fwd_dirs(const void* x_f, const float* dt_f, const float* A_f, const void* B_f, const void* C_f,
+                       const float* D_f, const void* x_b, const float* dt_b, const float* A_b, const void* B_b,
+                       const void* C_b, const float* D_b, int32_t mode, const lingen_mate_shape* shape, void* y_ma,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int rc = validate_shape(shape)) return rc;
+  if (mode < 0 || mode > 3) return LINGEN_ERR_SHAPE;
+  if (int rc = check_all({x_f, dt_f, A_f, B_f, C_f, D_f, x_b, dt_b, A_b, B_b, C_b, D_b, y_ma})) return rc;
+  if (int rc = check_ws(shape, workspace, workspace_bytes)) return rc;
+  if (shape->n_review != 0) return LINGEN_ERR_UNSUPPORTED;
+  Args af{x_f, dt_f, A_f, B_f, C_f, D_f, nullptr, nullptr, nullptr};
+  Args ab{x_b, dt_b, A_b, B_b, C_b, D_b, nullptr, nullptr, nullptr};
+  return dispatch_ma_dirs(shape, mode, af, ab, y_ma, static_cast<char*>(workspace), stream);
 }
 
 int lingen_te_fwd(const void* q, const void* k, const void* v, int32_t shifted, const lingen_mate_shape* shape,

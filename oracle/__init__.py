@@ -30,6 +30,7 @@ from .mate_oracle import (
     rms_inverse,
     ssd_scan,
     ssd_bidir,
+    ssd_dirs,
     review_tokens,
     review_state,
     tesa_window_keys,
@@ -49,6 +50,7 @@ __all__ = [
     "rms_inverse",
     "ssd_scan",
     "ssd_bidir",
+    "ssd_dirs",
     "review_tokens",
     "review_state",
     "tesa_window_keys",

@@ -167,6 +167,22 @@ def ssd_bidir(x, dt, A, B, C, D, perm: np.ndarray, h0=None, stats=None):
     return y_f + y_b
 
 
+def ssd_dirs(fwd, bwd, perm: np.ndarray):
+    """Bidirectional scan with a parameter set per direction: the scan of
+    ``fwd`` = (x, dt, A, B, C, D) along ``perm`` plus the scan of ``bwd`` along
+    the reversed order, summed per token; each direction carries its own D
+    skip.
+
+    [ABS] names a bidirectional Mamba2 block without saying whether the two
+    directions share weights; this is the reading in which they do not (the
+    mixer's default, ``ssd_bidir``, shares them).
+    """
+    perm = np.asarray(perm)
+    y_f, _, _ = ssd_scan(*fwd, perm)
+    y_b, _, _ = ssd_scan(*bwd, perm[::-1])
+    return y_f + y_b
+
+
 # --------------------------------------------------------------------------
 # Review tokens.
 # --------------------------------------------------------------------------

@@ -222,3 +222,40 @@ def test_grouped_review_state_splits_by_group():
         hs = slice(g * 2, g * 2 + 2)
         want = oracle.review_state(x[:, hs], dt[:, hs], A[hs], Bg[:, g], Cg[:, g], T, H, W, (2, 2, 2), (2, 2, 2))
         np.testing.assert_allclose(got[hs], want, rtol=1e-13, atol=1e-13)
+
+
+def _brute_dirs(fwd, bwd, perm):
+    """Explicit sums with a parameter set per direction: the lower triangle
+    (s <= t) from the forward set, the upper (s >= t) from the backward set,
+    and D x per direction."""
+    xf, dtf, Af, Bf, Cf, Df = fwd
+    xb, dtb, Ab, Bb, Cb, Db = bwd
+    L, Hs, P = xf.shape
+    y = np.zeros_like(xf)
+    for hd in range(Hs):
+        af = np.array([dtf[perm[s], hd] * Af[hd] for s in range(L)])
+        ab = np.array([dtb[perm[s], hd] * Ab[hd] for s in range(L)])
+        for t in range(L):
+            ct = perm[t]
+            acc = Df[hd] * xf[ct, hd] + Db[hd] * xb[ct, hd]
+            for s in range(L):
+                cs = perm[s]
+                if s <= t:
+                    acc = acc + math.exp(af[s + 1:t + 1].sum()) * dtf[cs, hd] * float(Cf[ct] @ Bf[cs]) * xf[cs, hd]
+                if s >= t:
+                    acc = acc + math.exp(ab[t:s].sum()) * dtb[cs, hd] * float(Cb[ct] @ Bb[cs]) * xb[cs, hd]
+            y[ct, hd] = acc
+    return y
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+def test_direction_specific_parameters_match_bruteforce(mode):
+    rng = np.random.default_rng(60 + mode)
+    T, H, W = 2, 2, 3
+    fwd = _rand_case(rng, T, H, W, 2, 3, 4)
+    bwd = _rand_case(rng, T, H, W, 2, 3, 4)
+    perm = oracle.rms_scan_order(mode, T, H, W)
+    got = oracle.ssd_dirs(fwd, bwd, perm)
+    assert _rel(got, _brute_dirs(fwd, bwd, perm)) < 1e-12
+    # one set for both directions is the shared-weight scan
+    assert _rel(oracle.ssd_dirs(fwd, fwd, perm), oracle.ssd_bidir(*fwd, perm)) < 1e-13

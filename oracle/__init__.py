@@ -38,6 +38,11 @@ from .mate_oracle import (
     tesa_for_queries,
     tesa_backward,
     dense_attention,
+    scan_conv_silu,
+    ma_prep,
+    gated_rmsnorm,
+    silu,
+    softplus,
     dense_attention_for_queries,
     mate_fwd,
     ma_fwd,
@@ -58,6 +63,11 @@ __all__ = [
     "tesa_for_queries",
     "tesa_backward",
     "dense_attention",
+    "scan_conv_silu",
+    "ma_prep",
+    "gated_rmsnorm",
+    "silu",
+    "softplus",
     "dense_attention_for_queries",
     "mate_fwd",
     "ma_fwd",

@@ -419,6 +419,78 @@ def dense_attention(q, k, v) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Steps either side of the scan (Mamba2 block conventions).
+# --------------------------------------------------------------------------
+
+
+def silu(a):
+    a = np.asarray(a, dtype=np.float64)
+    return a / (1.0 + np.exp(-a))
+
+
+def softplus(a):
+    a = np.asarray(a, dtype=np.float64)
+    return np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a)))
+
+
+def scan_conv_silu(u, w, b, order: Sequence[int]):
+    """Depthwise causal convolution along a scan order, then SiLU.
+
+    [SSD] (Mamba2 block): the x, B, C channels pass a short depthwise causal
+    convolution and SiLU before the scan.  Reading taken for a scanned video
+    tensor: causal along the order the scan visits the tokens.  u [L, Ch]
+    (canonical rows), w [Ch, K], b [Ch]; for the token at scan position s,
+        out[order[s], c] = silu(b[c] + sum_k w[c, k] u[order[s - K + 1 + k], c]),
+    with u taken as 0 before the first position.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    order = np.asarray(order)
+    L, K = u.shape[0], w.shape[1]
+    us = np.concatenate([np.zeros((K - 1, u.shape[1])), u[order]], axis=0)   # scan order, zero padded
+    acc = np.broadcast_to(b, (L, u.shape[1])).copy()
+    for k in range(K):
+        acc += w[:, k] * us[k:k + L]
+    out = np.empty_like(u)
+    out[order] = silu(acc)
+    return out
+
+
+def ma_prep(xbc, dt_raw, w_f, b_f, w_b, b_b, dt_bias, order: Sequence[int], Hs: int, P: int, G: int, N: int):
+    """The steps between the input projection and the scan, for a parameter
+    set per scan direction: the xBC channels (x: Hs*P, then B: G*N, then C:
+    G*N, Mamba2's split) convolved along the scan order (forward direction)
+    and along the reversed order (backward direction), each with its own
+    kernel and bias, then SiLU; and dt = softplus(dt_raw + dt_bias), shared.
+
+    Returns (x_f, B_f, C_f, x_b, B_b, C_b, dt) with x [L, Hs, P], B and C
+    [L, G, N], dt [L, Hs].
+    """
+    order = np.asarray(order)
+    L = np.asarray(xbc).shape[0]
+    outs = []
+    for w, b, o in ((w_f, b_f, order), (w_b, b_b, order[::-1])):
+        c = scan_conv_silu(xbc, w, b, o)
+        d = Hs * P
+        outs += [c[:, :d].reshape(L, Hs, P), c[:, d:d + G * N].reshape(L, G, N), c[:, d + G * N:].reshape(L, G, N)]
+    dt = softplus(np.asarray(dt_raw, dtype=np.float64) + np.asarray(dt_bias, dtype=np.float64))
+    return tuple(outs) + (dt,)
+
+
+def gated_rmsnorm(y, z, w, eps: float, group: int):
+    """Mamba2's gated RMS norm after the scan: g = y * silu(z), then every
+    row's channels in groups of ``group`` are divided by their root mean
+    square (plus eps inside the root) and multiplied by the weight w.
+    y, z [rows, dim]; w [dim]."""
+    g = np.asarray(y, dtype=np.float64) * silu(z)
+    rows, dim = g.shape
+    gg = g.reshape(rows, dim // group, group)
+    r = np.sqrt((gg * gg).mean(axis=-1, keepdims=True) + eps)
+    return (gg / r).reshape(rows, dim) * np.asarray(w, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
 # The whole mixer.
 # --------------------------------------------------------------------------
 

@@ -345,6 +345,60 @@ def te_backward(args, mate, torch):
     return 0
 
 
+def block_steps(args, mate, torch):
+    """The steps either side of the scan on the workload (lingen_ma_prep:
+    scan-order causal convolution + SiLU for both directions and softplus dt;
+    lingen_gated_rmsnorm: SiLU(z) gate and RMS norm), each timed with events
+    on the launch stream, scan order = step mod 4, against the algorithmic
+    bytes each must move; and the per-direction scan they feed."""
+    from mate_inputs import CONFIGS, CONFIG_NOTES, make_block_inputs, make_inputs
+
+    s = CONFIGS[args.config]
+    inp = make_block_inputs(s, args.config)
+    names = ("xbc", "dt_raw", "conv_w_f", "conv_b_f", "conv_w_b", "conv_b_b", "dt_bias", "y", "z", "norm_w")
+    d = {n: inp.torch(n, "cuda") for n in names}
+    ad = make_inputs(s, args.config, tensors=["A", "D"])
+    A, D = ad.torch("A", "cuda"), ad.torch("D", "cuda")
+    outs = mate.lingen_ma_prep(d["xbc"], d["dt_raw"], (d["conv_w_f"], d["conv_b_f"]), (d["conv_w_b"], d["conv_b_b"]),
+                               d["dt_bias"], 0, s)
+    y_ma = torch.empty((s.batch, s.L, s.d_inner), dtype=outs[0].dtype, device="cuda")
+    normed = torch.empty_like(d["y"])
+    ws = torch.empty(max(mate.lingen_mate_workspace_bytes(s), 16), dtype=torch.uint8, device="cuda")
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    prep_ms = timed(lambda i: mate.lingen_ma_prep(
+        d["xbc"], d["dt_raw"], (d["conv_w_f"], d["conv_b_f"]), (d["conv_w_b"], d["conv_b_b"]), d["dt_bias"], i % 4, s,
+        outs=outs))
+    norm_ms = timed(lambda i: mate.lingen_gated_rmsnorm(d["y"], d["z"], d["norm_w"], 1e-5, s.d_inner // s.ngroups,
+                                                        out=normed))
+    xf, Bf, Cf, xb, Bb, Cb, dt = outs
+    dirs_ms = timed(lambda i: mate.lingen_ma_fwd_dirs((xf, dt, A, Bf, Cf, D), (xb, dt, A, Bb, Cb, D), i % 4, s,
+                                                      out=y_ma, workspace=ws))
+    e = s.elem_bytes
+    ch = s.d_inner + 2 * s.ngroups * s.d_state
+    prep_bytes = 3 * s.L * ch * e + 2 * s.L * s.ssd_heads * 4      # xbc in, both directions out; dt_raw in, dt out
+    norm_bytes = 3 * s.L * s.d_inner * e                           # y, z in; out
+    out = {"workload": CONFIG_NOTES[args.config], "steps": args.steps, "conv_k": 4, "channels": ch}
+    for name, ms, nbytes in (("ma_prep", prep_ms, prep_bytes), ("gated_rmsnorm", norm_ms, norm_bytes)):
+        out[name] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "GB/s": round(nbytes / ms / 1e6, 1),
+                     "hbm_frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    out["ma_fwd_dirs_ms"] = round(dirs_ms, 4)
+    out["block_ms"] = round(prep_ms + dirs_ms + norm_ms, 4)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def dense_compare(args, mate, torch):
     """The quadratic mixer MATE replaces, at the workload's L, heads and head
     size: dense softmax attention over all tokens (lingen_dense_attn_fwd)
@@ -431,6 +485,9 @@ def main(argv=None):
                          "tensors, as context for the dense kernel")
     ap.add_argument("--te-bwd", action="store_true",
                     help="instead of the benchmark line, time the TE branch's backward pass against its forward")
+    ap.add_argument("--block", action="store_true",
+                    help="instead of the benchmark line, time the steps either side of the scan (convolution + "
+                         "SiLU + softplus, gated RMS norm) and the per-direction scan they feed")
     ap.add_argument("--dense", action="store_true",
                     help="instead of the benchmark line, time dense softmax attention over all tokens (the "
                          "quadratic mixer MATE replaces) against the MATE forward on the workload")
@@ -462,6 +519,8 @@ def main(argv=None):
         return dense_compare(args, mate, torch)
     if args.te_bwd:
         return te_backward(args, mate, torch)
+    if args.block:
+        return block_steps(args, mate, torch)
     s = CONFIGS[args.config]
     workload = CONFIG_NOTES[args.config]
     print(f"[bench] generating inputs: {workload}, {s.L} tokens", file=sys.stderr, flush=True)

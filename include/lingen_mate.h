@@ -261,6 +261,61 @@ int lingen_dense_attn_fwd(const void* q, const void* k, const void* v, void* o,
                           int32_t batch, int32_t L, int32_t heads, int32_t head_dim,
                           int32_t dtype, hipStream_t stream);
 
+/* ----------------------------------------------------------------------------
+ * Steps around the scan.  The MA branch is a bidirectional Mamba2 block (page
+ * "视频生成模子太贵太慢如何办？", section 要领：线性复杂度的 MATE 模块); these two
+ * calls carry out the elementwise steps of that block either side of the
+ * scan, in the layout of the Mamba-2 architecture (Dao & Gu 2024, section 7:
+ * a short depthwise causal convolution with SiLU on the x, B, C channels and
+ * a softplus on dt before the scan, a SiLU(z) gate with a grouped RMS norm
+ * after it).  Where the pages leave the step open, the readings taken are:
+ * the convolution is causal along the order the scan visits the tokens (so
+ * each direction of the scan convolves along its own order, with its own
+ * weights), and dt is shared by both directions.
+ * ------------------------------------------------------------------------- */
+
+/* Before the scan, for RMS order `mode` (0..3):
+ *   x_f | B_f | C_f = silu(conv_f(xbc)) along the scan order of `mode`,
+ *   x_b | B_b | C_b = silu(conv_b(xbc)) along the reversed order,
+ *   dt[b, l, i]     = softplus(dt_raw[b, l, i] + dt_bias[i]),
+ * where for the token at scan position s (taps before the first position
+ * are zero), channel c and K = conv_k taps,
+ *   conv(u)[order[s], c] = bias[c] + sum_{k<K} w[c, k] u[order[s-K+1+k], c].
+ *   xbc:          device, [batch, L, Hs*P + 2*G*N], shape->dtype, canonical
+ *                 token order; channels x (Hs*P, head-major) then B (G*N)
+ *                 then C (G*N).
+ *   dt_raw:       device, [batch, L, Hs] fp32.      dt_bias: device, [Hs] fp32.
+ *   conv_w_f/_b:  device, [Hs*P + 2*G*N, K] fp32.   conv_b_f/_b: device,
+ *                 [Hs*P + 2*G*N] fp32 (forward / backward direction).
+ *   x_f, x_b:     device outputs, layout of x;  B_f, C_f, B_b, C_b: layout
+ *                 of B;  dt: device output, layout of dt.  These are the
+ *                 inputs lingen_ma_fwd_dirs takes.
+ * The shape must pass lingen_mate_validate.  Errors: those of
+ * lingen_mate_validate; LINGEN_ERR_SHAPE for mode outside 0..3, conv_k
+ * outside 1..4, or Hs*P or G*N not a multiple of 16 bytes of elements;
+ * LINGEN_ERR_NULL / _ALIGN for a pointer. */
+int lingen_ma_prep(const void* xbc, const float* dt_raw, const float* conv_w_f,
+                   const float* conv_b_f, const float* conv_w_b, const float* conv_b_b,
+                   const float* dt_bias, int32_t conv_k, int32_t mode,
+                   const lingen_mate_shape* shape, void* x_f, void* B_f, void* C_f,
+                   void* x_b, void* B_b, void* C_b, float* dt, hipStream_t stream);
+
+/* After the scan: for every row r of `rows` and channel c of `dim`,
+ *   g[r, c]   = y[r, c] * silu(z[r, c]),
+ *   out[r, c] = g[r, c] / sqrt(mean_{c' in group(c)} g[r, c']^2 + eps) * weight[c],
+ * the groups being `group` consecutive channels.
+ *   y, z, out: device, [rows, dim], dtype (LINGEN_F32 or LINGEN_BF16); the
+ *              arithmetic is fp32, out rounded once.  out may not alias y, z.
+ *   weight:    device, [dim] fp32.
+ * rows = 0 is a no-op that does not look at the pointers.  Errors:
+ * LINGEN_ERR_DTYPE; LINGEN_ERR_SHAPE for rows < 0 or >= 2^31, dim < 1,
+ * group < 1, group not dividing dim, group not a multiple of 16 bytes of
+ * elements (8 bf16, 4 fp32), dim above 8192 (bf16) / 4096 (fp32), or eps < 0;
+ * LINGEN_ERR_NULL / _ALIGN for a pointer. */
+int lingen_gated_rmsnorm(const void* y, const void* z, const float* weight, float eps,
+                         int64_t rows, int32_t dim, int32_t group, int32_t dtype,
+                         void* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

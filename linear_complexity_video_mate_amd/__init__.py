@@ -14,6 +14,8 @@ from .binding import (
     STATUS_NAMES,
     lib,
     lingen_dense_attn_fwd,
+    lingen_ma_prep,
+    lingen_gated_rmsnorm,
     lingen_ma_fwd,
     lingen_ma_fwd_dirs,
     lingen_mate_fwd,
@@ -40,6 +42,8 @@ __all__ = [
     "STATUS_NAMES",
     "lib",
     "lingen_dense_attn_fwd",
+    "lingen_ma_prep",
+    "lingen_gated_rmsnorm",
     "lingen_ma_fwd",
     "lingen_ma_fwd_dirs",
     "lingen_mate_fwd",

@@ -46,6 +46,8 @@ EXPORTS = (
     "lingen_mate_fwd",
     "lingen_mate_fwd_events",
     "lingen_dense_attn_fwd",
+    "lingen_ma_prep",
+    "lingen_gated_rmsnorm",
 )
 
 
@@ -92,6 +94,8 @@ def lib() -> ctypes.CDLL:
         "lingen_mate_fwd": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_mate_fwd_events": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P, P], ctypes.c_int),
         "lingen_dense_attn_fwd": ([P, P, P, P, I32, I32, I32, I32, I32, P], ctypes.c_int),
+        "lingen_ma_prep": ([P] * 7 + [I32, I32, SP] + [P] * 7 + [P], ctypes.c_int),
+        "lingen_gated_rmsnorm": ([P, P, P, ctypes.c_float, I64, I32, I32, I32, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -396,4 +400,59 @@ def lingen_dense_attn_fwd(q, k, v, out=None):
         out = torch.empty_like(q)
     args = [_need(t, name, q.dtype, q.numel()) for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
     _check("lingen_dense_attn_fwd", lib().lingen_dense_attn_fwd(*args, batch, L, heads, d, code, _stream()))
+    return out
+
+
+def lingen_ma_prep(xbc, dt_raw, conv_f, conv_b, dt_bias, mode: int, shape, outs=None):
+    """The steps before the scan: ``xbc`` [batch, L, Hs*P + 2*G*N] (x, B, C
+    channels, canonical token order) is convolved along the scan order of
+    ``mode`` and along its reverse with the (weight [Ch, K], bias [Ch]) pairs
+    ``conv_f`` and ``conv_b``, then SiLU; dt = softplus(dt_raw + dt_bias).
+    Returns (x_f, B_f, C_f, x_b, B_b, C_b, dt) shaped for lingen_ma_fwd_dirs."""
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    L = shape.T * shape.H * shape.W
+    d, gn = shape.ssd_heads * shape.headdim, shape.ngroups * shape.d_state
+    ch = d + 2 * gn
+    (wf, bf), (wb, bb) = conv_f, conv_b
+    if wf.dim() != 2 or wf.shape[0] != ch or wb.shape != wf.shape:
+        raise ValueError(f"convolution weights must be [{ch}, K] tensors of one shape")
+    K = int(wf.shape[1])
+    if outs is None:
+        outs = tuple(torch.empty((shape.batch, L, w), dtype=td, device="cuda") for w in (d, gn, gn, d, gn, gn)) + (
+            torch.empty((shape.batch, L, shape.ssd_heads), dtype=torch.float32, device="cuda"),)
+    f32 = torch.float32
+    args = [_need(xbc, "xbc", td, shape.batch * L * ch), _need(dt_raw, "dt_raw", f32, n["dt"]),
+            _need(wf, "conv_w_f", f32, ch * K), _need(bf, "conv_b_f", f32, ch),
+            _need(wb, "conv_w_b", f32, ch * K), _need(bb, "conv_b_b", f32, ch),
+            _need(dt_bias, "dt_bias", f32, shape.ssd_heads)]
+    names = ("x_f", "B_f", "C_f", "x_b", "B_b", "C_b")
+    sizes = (n["x"], n["B"], n["B"], n["x"], n["B"], n["B"])
+    po = [_need(t, nm, td, sz) for t, nm, sz in zip(outs[:6], names, sizes)]
+    po.append(_need(outs[6], "dt", f32, n["dt"]))
+    _check("lingen_ma_prep", lib().lingen_ma_prep(*args, K, int(mode), ctypes.byref(cs), *po, _stream()))
+    return tuple(outs)
+
+
+def lingen_gated_rmsnorm(y, z, weight, eps: float, group: int, out=None):
+    """Gated RMS norm after the scan: for y, z [..., dim] (bf16 or fp32, one
+    dtype) and weight [dim] fp32, g = y * silu(z) and each group of ``group``
+    channels is divided by sqrt(mean(g^2) + eps) and multiplied by the
+    weight.  Returns a tensor shaped like y."""
+    torch = _torch()
+    if z.shape != y.shape or y.dim() < 1:
+        raise ValueError("y and z must be tensors of one shape")
+    if y.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"y must be bfloat16 or float32 (got {y.dtype})")
+    dim = int(y.shape[-1])
+    rows = y.numel() // dim if dim else 0
+    code = LINGEN_BF16 if y.dtype == torch.bfloat16 else LINGEN_F32
+    if out is None:
+        out = torch.empty_like(y)
+    py, pz, po = (_need(t, nm, y.dtype, y.numel()) for t, nm in ((y, "y"), (z, "z"), (out, "out")))
+    pw = _need(weight, "weight", torch.float32, dim)
+    _check("lingen_gated_rmsnorm", lib().lingen_gated_rmsnorm(py, pz, pw, float(eps), rows, dim, int(group), code, po,
+                                                              _stream()))
     return out

@@ -22,7 +22,7 @@ LIB_NAME = "liblingen_mate.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = os.environ.get("LINGEN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["lingen_host.cpp", "lingen_kernels.hip", "dense_attn.hip", "tesa_bwd.hip"]
+SOURCES = ["lingen_host.cpp", "lingen_kernels.hip", "dense_attn.hip", "tesa_bwd.hip", "block_steps.hip"]
 
 COMMON_FLAGS = [
     "-O3",

@@ -9,6 +9,8 @@ from .configs import MateShape, CONFIGS, config_shape, CONFIG_NOTES
 from .generate import (
     MateInputs,
     make_inputs,
+    make_block_inputs,
+    BLOCK_TENSOR_IDS,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
     TENSOR_IDS,
@@ -21,6 +23,8 @@ __all__ = [
     "config_shape",
     "MateInputs",
     "make_inputs",
+    "make_block_inputs",
+    "BLOCK_TENSOR_IDS",
     "bf16_bits_from_f32",
     "f32_from_bf16_bits",
     "TENSOR_IDS",

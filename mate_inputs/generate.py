@@ -24,6 +24,9 @@ import numpy as np
 from .configs import MateShape
 
 TENSOR_IDS = {"x": 0, "dt": 1, "A": 2, "B": 3, "C": 4, "D": 5, "q": 6, "k": 7, "v": 8}
+# Tensors of the steps around the scan (make_block_inputs).
+BLOCK_TENSOR_IDS = {"xbc": 9, "dt_raw": 10, "dt_bias": 11, "conv_w_f": 12, "conv_b_f": 13, "conv_w_b": 14,
+                    "conv_b_b": 15, "z": 16, "y": 17, "norm_w": 18}
 DEFAULT_SEED = 20241212
 
 
@@ -43,7 +46,8 @@ def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
 
 
 def _rng(seed: int, cfg_id: int, tensor: str, head: int) -> np.random.Generator:
-    ss = np.random.SeedSequence([seed, cfg_id, TENSOR_IDS[tensor], head])
+    tid = TENSOR_IDS[tensor] if tensor in TENSOR_IDS else BLOCK_TENSOR_IDS[tensor]
+    ss = np.random.SeedSequence([seed, cfg_id, tid, head])
     return np.random.Generator(np.random.PCG64(ss))
 
 
@@ -168,4 +172,51 @@ def make_inputs(shape: MateShape, cfg_id: int, seed: int = DEFAULT_SEED,
     else:
         for f, j, h in jobs:
             f(j, h)
+    return out
+
+
+def make_block_inputs(shape: MateShape, cfg_id: int, seed: int = DEFAULT_SEED, conv_k: int = 4,
+                      rows: Optional[int] = None, tensors: Optional[Sequence[str]] = None) -> MateInputs:
+    """Inputs of the steps either side of the scan, for one batch element,
+    following the Mamba-2 block's initialisation:
+      xbc [L, Hs*P + 2*G*N] ~ N(0, 1) (the projected x, B, C channels);
+      conv_w_f, conv_w_b [Ch, K], conv_b_f, conv_b_b [Ch] ~ U(-1/sqrt(K), 1/sqrt(K))
+        (a depthwise convolution's default fan-in bound);
+      dt_raw [L, Hs] ~ N(0, 0.5^2); dt_bias [Hs] = log(expm1(dt0)), dt0
+        log-uniform in [1e-3, 1e-1] (the inverse softplus of Mamba's dt range);
+      y, z [rows, Hs*P] ~ N(0, 1) (scan output and gate; rows defaults to L);
+      norm_w [Hs*P] ~ 1 + 0.1 N(0, 1).
+    xbc, y, z are rounded to bf16 in bf16 configurations; the rest is fp32.
+    Each tensor draws from its own stream; ``tensors`` restricts which are
+    produced.
+    """
+    L, Hs = shape.L, shape.ssd_heads
+    d = Hs * shape.headdim
+    ch = d + 2 * shape.ngroups * shape.d_state
+    rows = L if rows is None else rows
+    bf16 = shape.dtype == "bf16"
+
+    def finish(a32):
+        return bf16_bits_from_f32(a32) if bf16 else a32
+
+    out = MateInputs(shape=shape, cfg_id=cfg_id, seed=seed, heads=list(range(Hs)))
+    st = out.store
+    want = set(tensors) if tensors is not None else set(BLOCK_TENSOR_IDS)
+    if "xbc" in want:
+        st["xbc"] = finish(_normal(seed, cfg_id, "xbc", 0, L * ch).reshape(L, ch))
+    bound = 1.0 / math.sqrt(conv_k)
+    for name, n in (("conv_w_f", ch * conv_k), ("conv_b_f", ch), ("conv_w_b", ch * conv_k), ("conv_b_b", ch)):
+        if name in want:
+            a = _rng(seed, cfg_id, name, 0).uniform(-bound, bound, n).astype(np.float32)
+            st[name] = a.reshape(ch, conv_k) if name.startswith("conv_w") else a
+    if "dt_raw" in want:
+        st["dt_raw"] = _normal(seed, cfg_id, "dt_raw", 0, L * Hs, 0.5).reshape(L, Hs)
+    if "dt_bias" in want:
+        dt0 = np.exp(_rng(seed, cfg_id, "dt_bias", 0).uniform(math.log(1e-3), math.log(1e-1), Hs))
+        st["dt_bias"] = np.log(np.expm1(dt0)).astype(np.float32)
+    for name in ("y", "z"):
+        if name in want:
+            st[name] = finish(_normal(seed, cfg_id, name, 0, rows * d).reshape(rows, d))
+    if "norm_w" in want:
+        st["norm_w"] = (1.0 + 0.1 * _normal(seed, cfg_id, "norm_w", 0, d)).astype(np.float32)
     return out

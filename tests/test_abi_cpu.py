@@ -237,6 +237,48 @@ def test_dense_attention_rejects_before_launch(L):
     assert call(F, F, F, F, 1, 64, 0, 64, 1, None) == 0
 
 
+def test_ma_prep_rejects_before_launch(L):
+    F = ctypes.c_void_p(FAKE)
+    Z = ctypes.c_void_p(0)
+    M = ctypes.c_void_p(MISALIGNED)
+    call = L.lingen_ma_prep
+    for cfg in (CONFIGS[0], CONFIGS[1]):
+        cs = mate.to_c_shape(cfg)
+        for K, mode in ((0, 0), (5, 0), (4, -1), (4, 4)):
+            assert call(*[F] * 7, K, mode, ctypes.byref(cs), *[F] * 7, None) == -2, (K, mode)
+        for i in range(14):
+            p = [F] * 14
+            p[i] = Z
+            assert call(*p[:7], 4, 1, ctypes.byref(cs), *p[7:], None) == -1, i
+            p[i] = M
+            assert call(*p[:7], 4, 1, ctypes.byref(cs), *p[7:], None) == -4, i
+    assert call(*[F] * 7, 4, 0, None, *[F] * 7, None) == -1
+    bad = mate.to_c_shape(CONFIGS[1].with_(dtype=5))
+    assert call(*[F] * 7, 4, 0, ctypes.byref(bad), *[F] * 7, None) == -3
+
+
+def test_gated_rmsnorm_rejects_before_launch(L):
+    F = ctypes.c_void_p(FAKE)
+    Z = ctypes.c_void_p(0)
+    M = ctypes.c_void_p(MISALIGNED)
+    call = L.lingen_gated_rmsnorm
+    assert call(F, F, F, 1e-5, 4, 64, 64, 2, F, None) == -3
+    for rows, dim, group, dt, eps in ((-1, 64, 64, 1, 1e-5), (1 << 31, 64, 64, 1, 1e-5), (4, 0, 8, 1, 1e-5),
+                                      (4, 64, 0, 1, 1e-5), (4, 64, 48, 1, 1e-5), (4, 64, 4, 1, 1e-5),
+                                      (4, 64, 2, 0, 1e-5), (4, 8200, 8, 1, 1e-5), (4, 4100, 4, 0, 1e-5),
+                                      (4, 64, 64, 1, -1.0), (4, 64, 64, 1, float("nan"))):
+        assert call(F, F, F, eps, rows, dim, group, dt, F, None) == -2, (rows, dim, group, dt, eps)
+    for i in range(4):
+        p = [F] * 4
+        p[i] = Z
+        assert call(*p[:3], 1e-5, 4, 64, 64, 1, p[3], None) == -1, i
+        p[i] = M
+        assert call(*p[:3], 1e-5, 4, 64, 64, 1, p[3], None) == -4, i
+    # the largest compiled rows are accepted; zero rows is a no-op
+    assert call(Z, Z, Z, 1e-5, 0, 8192, 8192, 1, Z, None) == 0
+    assert call(Z, Z, Z, 1e-5, 0, 4096, 64, 0, Z, None) == 0
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     import linear_complexity_video_mate_amd.binding as b
     monkeypatch.setattr(b, "_lib", None)

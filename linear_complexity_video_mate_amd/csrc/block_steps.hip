@@ -38,12 +38,20 @@ struct ScanOrder {
   }
 };
 
-__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+// v * sigmoid(v) with the hardware exp and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
 
 // 16 bytes of channels: 8 bf16 or 4 fp32, widened to fp32 in registers.
 template <typename TS> struct Unit16;
 template <> struct Unit16<__bf16> {
   static constexpr int n = 8;
+  using raw = bf16x8;
+  __device__ static raw load_raw(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  __device__ static raw zero_raw() { return raw{}; }
+  __device__ static void widen(const raw& u, float (&v)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(u[e]);
+  }
   __device__ static void load(const __bf16* p, float (&v)[8]) {
     const bf16x8 u = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
@@ -58,6 +66,10 @@ template <> struct Unit16<__bf16> {
 };
 template <> struct Unit16<float> {
   static constexpr int n = 4;
+  using raw = float4;
+  __device__ static raw load_raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static raw zero_raw() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ static void widen(const raw& u, float (&v)[4]) { v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w; }
   __device__ static void load(const float* p, float (&v)[4]) {
     const float4 u = *reinterpret_cast<const float4*>(p);
     v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
@@ -67,36 +79,107 @@ template <> struct Unit16<float> {
   }
 };
 
+// s_waitcnt immediate waiting for at most n outstanding vector-memory
+// operations (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt left
+// at their maxima, i.e. not waited for).
+constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+
 struct PrepOut {
   void* x[2];   // [L][d] per direction (forward, backward)
   void* b[2];   // [L][gn]
   void* c[2];   // [L][gn]
 };
 
-// One thread per (run of S consecutive scan positions, 16-byte unit of
-// channels); consecutive threads take consecutive units of the same rows, so
-// every row is read and written in whole coalesced lines.  For scan position
-// s and channel c, with K taps,
+constexpr int kConvMaxTaps = 4;
+constexpr int kConvSegMax = 128;  // scan positions per wave, at most
+
+// Four 16-byte LDS reads at addr, addr + 1 KiB, + 2 KiB, + 3 KiB, waited for
+// inside the same statement.  Written as one asm statement so that the
+// compiler, which cannot tell the ring buffers apart from the LDS targets of
+// loads still in flight, does not add a wait for every outstanding global
+// load before them; the waits the data needs are issued explicitly.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_read4x16(unsigned addr, i32x4& a, i32x4& b, i32x4& c, i32x4& d) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+      : "v"(addr)
+      : "memory");
+}
+
+// One wave per (segment of consecutive scan positions, tile of 64 16-byte
+// channel units): lane l owns unit 64*tile + l, so every row access of the
+// wave is one contiguous KiB.  For scan position s and channel c, K taps,
 //   forward:  silu(bf[c] + sum_k wf[c][k] in[canon(s - K + 1 + k)][c])
 //   backward: silu(bb[c] + sum_k wb[c][k] in[canon(s + K - 1 - k)][c])
 // (the backward direction is the same convolution along the reversed order),
-// taps outside [0, L) read as zero.  Each thread loads the S + 2(K-1) rows its
-// outputs touch once, and its 2*K*V weights once.
-template <typename TS, int K, int S>
+// taps outside [0, L) read as zero.  The wave walks its segment 4 positions
+// per step, keeping rows s-K+1 .. s+K+2 in registers; the 4 new rows of each
+// step arrive by direct global-to-LDS loads issued D steps earlier into a
+// ring of D+1 LDS buffers (read back with lds_read4x16), which keeps 4*D KiB
+// per wave in flight without holding registers for it.  Each row is fetched once per segment, plus
+// 2(K-1) halo rows; weights once per segment.  The scan map of every
+// position the segment touches is computed once, one position per lane, and
+// broadcast from its lane when needed.
+//
+// Wait accounting (vector-memory operations of one wave complete in issue
+// order): step s issues the 4 loads of step s+D, then its own loads' data is
+// complete once at most 4*D + 8*min(s, D) newer operations are pending -- the
+// later loads and the 8 stores of every step in between.  Every step issues
+// exactly 4 loads and 8 stores (L and the segment length are multiples of 4,
+// and the loads of the D steps past the end re-read a valid row), so the
+// count is exact; the first D steps use the smaller bound 4*D.
+template <typename TS, int K, int D>
 __global__ __launch_bounds__(256) void scan_conv_silu_kernel(const TS* __restrict__ in, const float* __restrict__ wf,
                                                              const float* __restrict__ bf,
                                                              const float* __restrict__ wb,
                                                              const float* __restrict__ bb, ScanOrder so, int L,
-                                                             int ch, int d, int gn, PrepOut out) {
+                                                             int seg, int ch, int d, int gn, PrepOut out) {
   using U = Unit16<TS>;
+  using Raw = typename U::raw;
   constexpr int V = U::n;
-  const int units = ch / V;
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t runs = (int64_t(L) + S - 1) / S;
-  if (i >= runs * units) return;
-  const int s0 = int(i / units) * S, c0 = int(i % units) * V;
+  constexpr int R = 4;                    // positions per step (the four-row LDS read)
+  constexpr int H = 2 * (K - 1);          // halo rows carried from step to step
+  constexpr int NW = H + R;               // window rows
+  constexpr int NB = D + 1;               // LDS ring buffers
+  static_assert(K >= 1 && K <= kConvMaxTaps && NB >= 2 && NB <= 4, "compiled tap counts and ring depths");
+  static_assert(3 * R * D <= 63, "vmcnt field");
+  static_assert(kConvSegMax + 2 * (kConvMaxTaps - 1) <= 192, "three positions per lane in the token table");
+  constexpr int WBUF = R * 64 * 16;       // bytes per wave and buffer: R rows x 64 lanes x 16 B
+  __shared__ __attribute__((aligned(16))) char ring[NB][4][WBUF];
 
-  float w_f[V][K], w_b[V][K];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int units = ch / V, tiles = (units + 63) / 64;
+  const int64_t item = int64_t(blockIdx.x) * 4 + wave;
+  const int64_t nseg = (int64_t(L) + seg - 1) / seg;
+  if (item >= nseg * tiles) return;
+  const int s_begin = int(item / tiles) * seg, tile = int(item % tiles);
+  const int s_end = min(L, s_begin + seg);
+  const int nsteps = (s_end - s_begin) / R;
+  const int u = tile * 64 + lane;
+  const bool valid = u < units;
+  const int c0 = min(u, units - 1) * V;   // lanes past the last unit load the last unit and store nothing
+
+  // Stream row j sits at scan position s_begin - (K-1) + j (rows outside
+  // [0, L) are loaded clamped; their data is replaced by zeros); its token
+  // is held by lane j % 64 in tok0, tok1 or tok2 (j / 64).
+  const int p0 = s_begin - (K - 1) + lane;
+  const int tok0 = so.canon(min(max(p0, 0), L - 1));
+  const int tok1 = so.canon(min(max(p0 + 64, 0), L - 1));
+  const int tok2 = so.canon(min(max(p0 + 128, 0), L - 1));
+  auto token = [&](int j) -> int {   // j is the same in every lane
+    const int a = __builtin_amdgcn_readlane(tok0, j & 63);
+    const int b = __builtin_amdgcn_readlane(tok1, j & 63);
+    const int c = __builtin_amdgcn_readlane(tok2, j & 63);
+    return j < 64 ? a : (j < 128 ? b : c);
+  };
+
+  float w_f[V][K], w_b[V][K], b_f[V], b_b[V];
   {
     const float4* pf = reinterpret_cast<const float4*>(wf + int64_t(c0) * K);
     const float4* pb = reinterpret_cast<const float4*>(wb + int64_t(c0) * K);
@@ -110,52 +193,87 @@ __global__ __launch_bounds__(256) void scan_conv_silu_kernel(const TS* __restric
         w_b[(4 * q + r) / K][(4 * q + r) % K] = bv[r];
       }
     }
+#pragma unroll
+    for (int e = 0; e < V; ++e) { b_f[e] = bf[c0 + e]; b_b[e] = bb[c0 + e]; }
   }
-  float acc_f[S][V], acc_b[S][V];
+  const TS* src = in + c0;
+  const int last_row = s_end - s_begin + H - 1;   // last stream row the segment needs
+  // Loads of step `step` into ring buffer step % NB.
+  auto issue = [&](int step) {
+    char* base = ring[step % NB][wave];
 #pragma unroll
-  for (int e = 0; e < V; ++e) {
-    const float b0 = bf[c0 + e], b1 = bb[c0 + e];
+    for (int r = 0; r < R; ++r)
+      lds_load16(src + int64_t(token(min(H + step * R + r, last_row))) * ch, base + r * 1024);
+  };
+  // Channel unit -> destination tensor (x: first d channels, then B, then C).
+  int col, width;
+  void *pf_, *pb_;
+  if (c0 < d) { col = c0; width = d; pf_ = out.x[0]; pb_ = out.x[1]; }
+  else if (c0 < d + gn) { col = c0 - d; width = gn; pf_ = out.b[0]; pb_ = out.b[1]; }
+  else { col = c0 - d - gn; width = gn; pf_ = out.c[0]; pb_ = out.c[1]; }
+  TS* df = static_cast<TS*>(pf_) + col;
+  TS* db = static_cast<TS*>(pb_) + col;
+
+  // win[r] holds stream row s*R + r during step s.
+  float win[NW][V];
+  {
+    Raw first[H > 0 ? H : 1];
 #pragma unroll
-    for (int j = 0; j < S; ++j) { acc_f[j][e] = b0; acc_b[j][e] = b1; }
+    for (int j = 0; j < H; ++j) first[j] = *reinterpret_cast<const Raw*>(src + int64_t(token(j)) * ch);
+#pragma unroll
+    for (int t = 0; t < D; ++t) issue(t);
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      U::widen(first[j], win[R + j]);
+      const int q = s_begin - (K - 1) + j;
+      if (q < 0 || q >= L)
+#pragma unroll
+        for (int e = 0; e < V; ++e) win[R + j][e] = 0.f;
+    }
   }
-  // Row at scan position s0 + r feeds forward output j with tap
-  // k = r - j + K - 1 and backward output j with tap k = j - r + K - 1.
+  for (int s = 0; s < nsteps; ++s) {
+    issue(s + D);
+    if (s < D) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R * D));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * R * D));
 #pragma unroll
-  for (int r = -(K - 1); r < S + K - 1; ++r) {
-    const int p = s0 + r;
-    if (p < 0 || p >= L) continue;
-    float v[V];
-    U::load(in + int64_t(so.canon(p)) * ch + c0, v);
+    for (int r = 0; r < H; ++r)
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-      const int kf = r - j + K - 1, kb = j - r + K - 1;
-      if (kf >= 0 && kf < K) {
+      for (int e = 0; e < V; ++e) win[r][e] = win[r + R][e];
+    {
+      const unsigned addr = unsigned(reinterpret_cast<uintptr_t>(ring[s % NB][wave])) + unsigned(lane * 16);
+      i32x4 raw[R];
+      lds_read4x16(addr, raw[0], raw[1], raw[2], raw[3]);
 #pragma unroll
-        for (int e = 0; e < V; ++e) acc_f[j][e] = fmaf(w_f[e][kf], v[e], acc_f[j][e]);
+      for (int r = 0; r < R; ++r) {
+        U::widen(__builtin_bit_cast(Raw, raw[r]), win[H + r]);
+        const int q = s_begin - (K - 1) + H + s * R + r;
+        if (q >= L)
+#pragma unroll
+          for (int e = 0; e < V; ++e) win[H + r][e] = 0.f;
       }
-      if (kb >= 0 && kb < K) {
+    }
 #pragma unroll
-        for (int e = 0; e < V; ++e) acc_b[j][e] = fmaf(w_b[e][kb], v[e], acc_b[j][e]);
+    for (int j = 0; j < R; ++j) {
+      float o_f[V], o_b[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        float af = b_f[e], ab = b_b[e];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          af = fmaf(w_f[e][k], win[j + k][e], af);
+          ab = fmaf(w_b[e][k], win[j + H - k][e], ab);
+        }
+        o_f[e] = silu(af);
+        o_b[e] = silu(ab);
+      }
+      const int64_t off = int64_t(token(K - 1 + s * R + j)) * width;
+      if (valid) {
+        U::store(df + off, o_f);
+        U::store(db + off, o_b);
       }
     }
   }
-  // Channel unit -> destination tensor (x: first d channels, then B, then C).
-  int sec, col, width;
-  if (c0 < d) { sec = 0; col = c0; width = d; }
-  else if (c0 < d + gn) { sec = 1; col = c0 - d; width = gn; }
-  else { sec = 2; col = c0 - d - gn; width = gn; }
-  TS* df = static_cast<TS*>(sec == 0 ? out.x[0] : sec == 1 ? out.b[0] : out.c[0]);
-  TS* db = static_cast<TS*>(sec == 0 ? out.x[1] : sec == 1 ? out.b[1] : out.c[1]);
-#pragma unroll
-  for (int j = 0; j < S; ++j) {
-    const int p = s0 + j;
-    if (p >= L) break;
-    const int64_t tok = so.canon(p);
-#pragma unroll
-    for (int e = 0; e < V; ++e) { acc_f[j][e] = silu(acc_f[j][e]); acc_b[j][e] = silu(acc_b[j][e]); }
-    U::store(df + tok * width + col, acc_f[j]);
-    U::store(db + tok * width + col, acc_b[j]);
-  }
+  wait_vmem();   // the loads issued past the end are still landing in LDS
 }
 
 // dt = softplus(dt_raw + dt_bias[head]) in the overflow-safe form
@@ -234,14 +352,23 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(const TS* _
   }
 }
 
-constexpr int kConvRun = 4;   // scan positions per thread
+constexpr int kConvStep = 4;      // scan positions per step of a wave
+constexpr int kConvAhead = 2;     // steps of loads in flight per wave
 
 template <typename TS, int K>
 int launch_conv(const TS* in, const float* wf, const float* bf, const float* wb, const float* bb, ScanOrder so,
                 int L, int ch, int d, int gn, PrepOut o, hipStream_t st) {
-  const int64_t threads = (int64_t(L) + kConvRun - 1) / kConvRun * (ch / Unit16<TS>::n);
-  scan_conv_silu_kernel<TS, K, kConvRun><<<unsigned((threads + 255) / 256), 256, 0, st>>>(in, wf, bf, wb, bb, so, L,
-                                                                                          ch, d, gn, o);
+  const int64_t tiles = (ch / Unit16<TS>::n + 63) / 64;
+  // Longest segment that still gives every compute unit several waves per
+  // SIMD: long segments load fewer halo rows and weights, short ones fill the
+  // chip.
+  const int cus = compute_units();
+  const int64_t want_waves = 32LL * (cus > 0 ? cus : 256);
+  int seg = kConvSegMax;
+  while (seg > kConvStep && ((int64_t(L) + seg - 1) / seg) * tiles < want_waves) seg /= 2;
+  const int64_t waves = ((int64_t(L) + seg - 1) / seg) * tiles;
+  scan_conv_silu_kernel<TS, K, kConvAhead><<<unsigned((waves + 3) / 4), 256, 0, st>>>(in, wf, bf, wb, bb, so, L, seg,
+                                                                                      ch, d, gn, o);
   return hipGetLastError() == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
 }
 
@@ -288,6 +415,9 @@ extern "C" int lingen_ma_prep(const void* xbc, const float* dt_raw, const float*
   const int v = shape->dtype == LINGEN_BF16 ? 8 : 4;
   if (mode < 0 || mode > 3 || conv_k < 1 || conv_k > 4) return LINGEN_ERR_SHAPE;
   if ((shape->ssd_heads * shape->headdim) % v || (shape->ngroups * shape->d_state) % v) return LINGEN_ERR_SHAPE;
+  // the convolution walks whole steps of kConvStep positions (every compiled
+  // chunk length is a multiple of it, so every valid shape passes)
+  if (tokens(shape) % kConvStep) return LINGEN_ERR_SHAPE;
   const void* ptrs[] = {xbc, dt_raw, conv_w_f, conv_b_f, conv_w_b, conv_b_b, dt_bias, x_f, B_f, C_f, x_b, B_b, C_b, dt};
   for (const void* p : ptrs)
     if (int rc = check_ptr(p)) return rc;

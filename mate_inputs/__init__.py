@@ -10,6 +10,7 @@ from .generate import (
     MateInputs,
     make_inputs,
     make_block_inputs,
+    make_block_weights,
     BLOCK_TENSOR_IDS,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
@@ -24,6 +25,7 @@ __all__ = [
     "MateInputs",
     "make_inputs",
     "make_block_inputs",
+    "make_block_weights",
     "BLOCK_TENSOR_IDS",
     "bf16_bits_from_f32",
     "f32_from_bf16_bits",

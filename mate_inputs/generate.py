@@ -26,7 +26,9 @@ from .configs import MateShape
 TENSOR_IDS = {"x": 0, "dt": 1, "A": 2, "B": 3, "C": 4, "D": 5, "q": 6, "k": 7, "v": 8}
 # Tensors of the steps around the scan (make_block_inputs).
 BLOCK_TENSOR_IDS = {"xbc": 9, "dt_raw": 10, "dt_bias": 11, "conv_w_f": 12, "conv_b_f": 13, "conv_w_b": 14,
-                    "conv_b_b": 15, "z": 16, "y": 17, "norm_w": 18}
+                    "conv_b_b": 15, "z": 16, "y": 17, "norm_w": 18, "u": 19, "w_z": 20, "w_xbc": 21, "w_dt": 22,
+                    "w_out_ma": 23, "w_q": 24, "w_k": 25, "w_v": 26, "w_o": 27, "A_f": 28, "A_b": 29, "D_f": 30,
+                    "D_b": 31}
 DEFAULT_SEED = 20241212
 
 
@@ -219,4 +221,41 @@ def make_block_inputs(shape: MateShape, cfg_id: int, seed: int = DEFAULT_SEED, c
             st[name] = finish(_normal(seed, cfg_id, name, 0, rows * d).reshape(rows, d))
     if "norm_w" in want:
         st["norm_w"] = (1.0 + 0.1 * _normal(seed, cfg_id, "norm_w", 0, d)).astype(np.float32)
+    return out
+
+
+def make_block_weights(shape: MateShape, cfg_id: int, d_model: int, seed: int = DEFAULT_SEED,
+                       conv_k: int = 4) -> MateInputs:
+    """Input u [L, d_model] and every weight of one MATE block (the names of
+    the library's block weights):
+      u ~ N(0, 1);
+      projections w_z [d, Dm], w_xbc [d + 2GN, Dm], w_dt [Hs, Dm],
+        w_out_ma [Dm, d], w_q, w_k, w_v [d, Dm], w_o [Dm, d] ~ U(-1/sqrt(in),
+        1/sqrt(in)) (a linear layer's default bound, no bias);
+      A_f, A_b = -exp(U(0, ln 16)) per head; D_f, D_b ~ 1 + 0.1 N(0, 1);
+      conv weights and biases, dt_bias and norm_w as in make_block_inputs.
+    u and the projections are rounded to bf16 in bf16 configurations.
+    """
+    d = shape.ssd_heads * shape.headdim
+    ch = d + 2 * shape.ngroups * shape.d_state
+    hs = shape.ssd_heads
+    bf16 = shape.dtype == "bf16"
+
+    def finish(a32):
+        return bf16_bits_from_f32(a32) if bf16 else a32
+
+    out = make_block_inputs(shape, cfg_id, seed, conv_k,
+                            tensors=("conv_w_f", "conv_b_f", "conv_w_b", "conv_b_b", "dt_bias", "norm_w"))
+    st = out.store
+    st["u"] = finish(_normal(seed, cfg_id, "u", 0, shape.L * d_model).reshape(shape.L, d_model))
+    for name, rows, cols in (("w_z", d, d_model), ("w_xbc", ch, d_model), ("w_dt", hs, d_model),
+                             ("w_out_ma", d_model, d), ("w_q", d, d_model), ("w_k", d, d_model),
+                             ("w_v", d, d_model), ("w_o", d_model, d)):
+        bound = 1.0 / math.sqrt(cols)
+        a = _rng(seed, cfg_id, name, 0).uniform(-bound, bound, rows * cols).astype(np.float32)
+        st[name] = finish(a.reshape(rows, cols))
+    for name in ("A_f", "A_b"):
+        st[name] = (-np.exp(_rng(seed, cfg_id, name, 0).uniform(0.0, math.log(16.0), hs))).astype(np.float32)
+    for name in ("D_f", "D_b"):
+        st[name] = (1.0 + 0.1 * _normal(seed, cfg_id, name, 0, hs)).astype(np.float32)
     return out

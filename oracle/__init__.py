@@ -46,6 +46,7 @@ from .mate_oracle import (
     dense_attention_for_queries,
     mate_fwd,
     ma_fwd,
+    mate_block,
 )
 
 __all__ = [
@@ -70,5 +71,6 @@ __all__ = [
     "softplus",
     "dense_attention_for_queries",
     "mate_fwd",
+    "mate_block",
     "ma_fwd",
 ]

@@ -523,3 +523,45 @@ def mate_fwd(x, dt, A, B, C, D, q, k, v, layer_idx: int, T: int, H: int, W: int,
     o = tesa(q, k, v, T, H, W, win, shift, stats=stats)
     L = T * H * W
     return y_ma.reshape(L, -1) + o.reshape(L, -1)
+
+
+# --------------------------------------------------------------------------
+# The whole block around the mixer.
+# --------------------------------------------------------------------------
+
+
+def mate_block(u, w, layer_idx: int, T: int, H: int, W: int, Hs: int, P: int, G: int, N: int, Ha: int,
+               win, eps: float = 1e-5):
+    """The MATE block on u [L, Dm] (canonical token order): the MA branch
+    and the TE branch, each with its projections, outputs summed.
+
+    [ART] 要领: the block is an MA branch plus a TE branch in place of the
+    self-attention.  Readings for what the pages leave open (the same as the
+    library's): the MA branch follows the Mamba-2 block layout of [SSD]
+    (section 7) -- z, xBC and dt_raw are projections of u, then ``ma_prep``,
+    the per-direction scan ``ssd_dirs``, ``gated_rmsnorm`` with one group per
+    B/C group, and an output projection; the TE branch projects q, k, v,
+    applies ``tesa`` and projects its output.  No projection has a bias.
+    ``w`` maps names to arrays: w_z [d, Dm], w_xbc [d + 2GN, Dm], w_dt
+    [Hs, Dm], conv_w_f, conv_w_b [Ch, K], conv_b_f, conv_b_b [Ch], dt_bias,
+    A_f, D_f, A_b, D_b [Hs], norm_w [d], w_out_ma [Dm, d], w_q, w_k, w_v
+    [d, Dm], w_o [Dm, d], with d = Hs*P = Ha*(attention head size).
+    """
+    f = {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
+    u = np.asarray(u, dtype=np.float64)
+    L = T * H * W
+    d = Hs * P
+    mode = rms_mode(layer_idx)
+    order = rms_scan_order(mode, T, H, W)
+    z = u @ f["w_z"].T
+    xbc = u @ f["w_xbc"].T
+    dt_raw = u @ f["w_dt"].T
+    xf, Bf, Cf, xb, Bb, Cb, dt = ma_prep(xbc, dt_raw, f["conv_w_f"], f["conv_b_f"], f["conv_w_b"], f["conv_b_b"],
+                                         f["dt_bias"], order, Hs, P, G, N)
+    y = ssd_dirs((xf, dt, f["A_f"], Bf, Cf, f["D_f"]), (xb, dt, f["A_b"], Bb, Cb, f["D_b"]), order)
+    yn = gated_rmsnorm(y.reshape(L, d), z, f["norm_w"], eps, d // G)
+    out = yn @ f["w_out_ma"].T
+    dh = d // Ha
+    q, k, v = ((u @ f[n].T).reshape(L, Ha, dh) for n in ("w_q", "w_k", "w_v"))
+    o = tesa(q, k, v, T, H, W, win, tesa_shift(layer_idx, win))
+    return out + o.reshape(L, d) @ f["w_o"].T

@@ -91,3 +91,99 @@ def test_gated_rmsnorm_loops_and_invariants():
     a = oracle.gated_rmsnorm(y, z, np.ones(dim), 0.0, group)
     np.testing.assert_allclose(oracle.gated_rmsnorm(3.5 * y, z, np.ones(dim), 0.0, group), a, rtol=1e-13)
     np.testing.assert_allclose(np.sqrt((a.reshape(rows, -1, group) ** 2).mean(-1)), 1.0, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# The whole block (projections around the mixer): wiring pins.
+# ---------------------------------------------------------------------------
+
+def _block_weights(rng, Dm, Hs, P, G, N, K):
+    d = Hs * P
+    ch = d + 2 * G * N
+    w = {
+        "w_z": rng.standard_normal((d, Dm)) / np.sqrt(Dm),
+        "w_xbc": rng.standard_normal((ch, Dm)) / np.sqrt(Dm),
+        "w_dt": rng.standard_normal((Hs, Dm)) / np.sqrt(Dm),
+        "conv_w_f": rng.standard_normal((ch, K)), "conv_b_f": rng.standard_normal(ch),
+        "conv_w_b": rng.standard_normal((ch, K)), "conv_b_b": rng.standard_normal(ch),
+        "dt_bias": rng.standard_normal(Hs), "A_f": -rng.uniform(1, 4, Hs), "A_b": -rng.uniform(1, 4, Hs),
+        "D_f": rng.standard_normal(Hs), "D_b": rng.standard_normal(Hs), "norm_w": 1 + 0.1 * rng.standard_normal(d),
+        "w_out_ma": rng.standard_normal((Dm, d)) / np.sqrt(d),
+        "w_q": rng.standard_normal((d, Dm)), "w_k": rng.standard_normal((d, Dm)),
+        "w_v": rng.standard_normal((d, Dm)), "w_o": rng.standard_normal((Dm, d)) / np.sqrt(d),
+    }
+    return w
+
+
+def test_block_te_branch_one_window_is_dense_attention():
+    """With the MA output projection zeroed and one window over the whole
+    grid, the block is textbook softmax attention of the projected q, k, v,
+    projected by w_o (scipy's softmax, no oracle helper)."""
+    from scipy.special import softmax
+
+    rng = np.random.default_rng(41)
+    T, H, W, Hs, P, G, N, Dm = 2, 2, 3, 2, 3, 1, 2, 5
+    w = _block_weights(rng, Dm, Hs, P, G, N, 4)
+    w["w_out_ma"] = np.zeros_like(w["w_out_ma"])
+    u = rng.standard_normal((T * H * W, Dm))
+    got = oracle.mate_block(u, w, 0, T, H, W, Hs, P, G, N, Hs, (T, H, W))
+    q, k, v = ((u @ w[n].T).reshape(-1, Hs, P) for n in ("w_q", "w_k", "w_v"))
+    o = np.empty_like(q)
+    for h in range(Hs):
+        a = softmax(q[:, h] @ k[:, h].T / np.sqrt(P), axis=1)
+        o[:, h] = a @ v[:, h]
+    np.testing.assert_allclose(got, o.reshape(len(u), -1) @ w["w_o"].T, rtol=1e-12, atol=1e-12)
+
+
+def test_block_ma_branch_infinite_decay_closed_form():
+    """With w_o zeroed, one-tap convolutions and a decay that empties the
+    state at every token, each direction's scan output is (dt B.C + D) x at
+    the token itself, so the MA branch has a closed form: written out here
+    with numpy alone (logaddexp for softplus, x * sigmoid for SiLU), with
+    different weights per direction, two B/C groups and two norm groups."""
+    rng = np.random.default_rng(42)
+    T, H, W, Hs, P, G, N, Dm = 2, 2, 2, 4, 2, 2, 3, 6
+    d, L = Hs * P, T * H * W
+    w = _block_weights(rng, Dm, Hs, P, G, N, 1)
+    w["w_o"] = np.zeros_like(w["w_o"])
+    w["A_f"] = np.full(Hs, -1e6)
+    w["A_b"] = np.full(Hs, -1e6)
+    w["dt_bias"] = np.full(Hs, 2.0)          # dt >= softplus(2 - |raw|), far above 1e6^-1
+    u = rng.standard_normal((L, Dm)) * 0.5
+    sig = lambda a: 1 / (1 + np.exp(-a))
+    xbc = u @ w["w_xbc"].T
+    z = u @ w["w_z"].T
+    dt = np.logaddexp(0.0, u @ w["w_dt"].T + w["dt_bias"])
+    y = np.zeros((L, Hs, P))
+    for tag in ("f", "b"):
+        c = xbc * w["conv_w_" + tag][:, 0] + w["conv_b_" + tag]
+        c = c * sig(c)
+        x = c[:, :d].reshape(L, Hs, P)
+        Bm = c[:, d:d + G * N].reshape(L, G, N)
+        Cm = c[:, d + G * N:].reshape(L, G, N)
+        for h in range(Hs):
+            g = h // (Hs // G)
+            bc = np.sum(Bm[:, g] * Cm[:, g], axis=1)
+            y[:, h] += (dt[:, h] * bc + w["D_" + tag][h])[:, None] * x[:, h]
+    gte = y.reshape(L, d) * z * sig(z)
+    grp = gte.reshape(L, G, d // G)
+    yn = (grp / np.sqrt((grp ** 2).mean(axis=2, keepdims=True) + 1e-5)).reshape(L, d) * w["norm_w"]
+    want = yn @ w["w_out_ma"].T
+    for layer in (0, 1, 2, 3):       # every scan order: the decay leaves no neighbour term
+        got = oracle.mate_block(u, w, layer, T, H, W, Hs, P, G, N, Hs, (2, 2, 2))
+        np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-12)
+
+
+def test_block_branches_add_and_layers_repeat():
+    rng = np.random.default_rng(43)
+    T, H, W, Hs, P, G, N, Dm = 2, 4, 4, 2, 4, 1, 4, 7
+    w = _block_weights(rng, Dm, Hs, P, G, N, 4)
+    u = rng.standard_normal((T * H * W, Dm))
+    args = (T, H, W, Hs, P, G, N, Hs, (2, 2, 2))
+    full = oracle.mate_block(u, w, 1, *args)
+    ma = oracle.mate_block(u, dict(w, w_o=np.zeros_like(w["w_o"])), 1, *args)
+    te = oracle.mate_block(u, dict(w, w_out_ma=np.zeros_like(w["w_out_ma"])), 1, *args)
+    np.testing.assert_allclose(full, ma + te, rtol=1e-12, atol=1e-12)
+    # scan orders repeat every 4 layers, window phases every 2
+    np.testing.assert_allclose(oracle.mate_block(u, w, 5, *args), full, rtol=1e-12, atol=1e-12)
+    assert np.abs(oracle.mate_block(u, w, 3, *args) - full).max() > 1e-3

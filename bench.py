@@ -399,6 +399,71 @@ def block_steps(args, mate, torch):
     return 0
 
 
+def mate_block(args, mate, torch):
+    """The whole MATE block (lingen_mate_block_fwd) on the workload at model
+    width d_model = Hs*P: rocBLAS projections around the library's kernels.
+    Times the block (layer_idx = step mod 4) and, on the same intermediates,
+    the library's own steps alone (convolution + softplus, per-direction
+    scan, gated norm, window attention); the projections' share is the
+    difference."""
+    from mate_inputs import CONFIGS, CONFIG_NOTES, make_block_weights
+
+    s = CONFIGS[args.config]
+    dm = s.d_inner
+    inp = make_block_weights(s, args.config, dm)
+    w = {n: inp.torch(n, "cuda") for n in mate.BLOCK_WEIGHTS}
+    u = inp.torch("u", "cuda").reshape(s.batch, s.L, dm)
+    out = torch.empty_like(u)
+    ws = torch.empty(mate.lingen_mate_block_workspace_bytes(s, dm), dtype=torch.uint8, device="cuda")
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    block_ms = timed(lambda i: mate.lingen_mate_block_fwd(u, w, i % 4, s, out=out, workspace=ws))
+    # the library's steps alone, on tensors of the block's intermediate shapes
+    td = u.dtype
+    d, gn, ch = s.d_inner, s.ngroups * s.d_state, s.d_inner + 2 * s.ngroups * s.d_state
+    xbc = torch.empty((s.batch, s.L, ch), dtype=td, device="cuda").normal_()
+    dt_raw = torch.empty((s.batch, s.L, s.ssd_heads), dtype=torch.float32, device="cuda").normal_()
+    outs = mate.lingen_ma_prep(xbc, dt_raw, (w["conv_w_f"], w["conv_b_f"]), (w["conv_w_b"], w["conv_b_b"]),
+                               w["dt_bias"], 0, s)
+    prep_ms = timed(lambda i: mate.lingen_ma_prep(xbc, dt_raw, (w["conv_w_f"], w["conv_b_f"]),
+                                                  (w["conv_w_b"], w["conv_b_b"]), w["dt_bias"], i % 4, s, outs=outs))
+    xf, Bf, Cf, xb, Bb, Cb, dt = outs
+    y = torch.empty((s.batch, s.L, d), dtype=td, device="cuda")
+    sws = torch.empty(max(mate.lingen_mate_workspace_bytes(s), 16), dtype=torch.uint8, device="cuda")
+    dirs_ms = timed(lambda i: mate.lingen_ma_fwd_dirs((xf, dt, w["A_f"], Bf, Cf, w["D_f"]),
+                                                      (xb, dt, w["A_b"], Bb, Cb, w["D_b"]), i % 4, s, out=y,
+                                                      workspace=sws))
+    z = torch.empty_like(y).normal_()
+    yn = torch.empty_like(y)
+    norm_ms = timed(lambda i: mate.lingen_gated_rmsnorm(y, z, w["norm_w"], 1e-5, d // s.ngroups, out=yn))
+    q, k, v = (torch.empty((s.batch, s.L, d), dtype=td, device="cuda").normal_() for _ in range(3))
+    te_ms = timed(lambda i: mate.lingen_te_fwd(q, k, v, i % 2, s, out=yn))
+    own = prep_ms + dirs_ms + norm_ms + te_ms
+    rows = s.batch * s.L
+    gemm_flops = 2 * rows * dm * (d + ch + s.ssd_heads + 3 * d) + 2 * rows * d * dm * 2
+    gemm_ms = block_ms - own
+    res = {"workload": CONFIG_NOTES[args.config], "d_model": dm, "steps": args.steps,
+           "block_ms": round(block_ms, 4), "tokens_per_s": round(rows / (block_ms / 1e3), 1),
+           "library_kernels_ms": {"ma_prep": round(prep_ms, 4), "ma_fwd_dirs": round(dirs_ms, 4),
+                                  "gated_rmsnorm": round(norm_ms, 4), "te_fwd": round(te_ms, 4),
+                                  "sum": round(own, 4)},
+           "projections": {"gemm_flops": gemm_flops, "ms_by_difference": round(gemm_ms, 4),
+                           "TFLOP/s": round(gemm_flops / gemm_ms / 1e9, 1) if gemm_ms > 0 else None}}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def dense_compare(args, mate, torch):
     """The quadratic mixer MATE replaces, at the workload's L, heads and head
     size: dense softmax attention over all tokens (lingen_dense_attn_fwd)
@@ -488,6 +553,9 @@ def main(argv=None):
     ap.add_argument("--block", action="store_true",
                     help="instead of the benchmark line, time the steps either side of the scan (convolution + "
                          "SiLU + softplus, gated RMS norm) and the per-direction scan they feed")
+    ap.add_argument("--mate-block", action="store_true",
+                    help="instead of the benchmark line, time the whole MATE block (projections around the "
+                         "mixer) and the library's own steps inside it")
     ap.add_argument("--dense", action="store_true",
                     help="instead of the benchmark line, time dense softmax attention over all tokens (the "
                          "quadratic mixer MATE replaces) against the MATE forward on the workload")
@@ -521,6 +589,8 @@ def main(argv=None):
         return te_backward(args, mate, torch)
     if args.block:
         return block_steps(args, mate, torch)
+    if args.mate_block:
+        return mate_block(args, mate, torch)
     s = CONFIGS[args.config]
     workload = CONFIG_NOTES[args.config]
     print(f"[bench] generating inputs: {workload}, {s.L} tokens", file=sys.stderr, flush=True)

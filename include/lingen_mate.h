@@ -16,9 +16,10 @@
  *       windows, the window grid shifted by half a window on odd layers
  *       (same pages, sections 要领 and 关键算法创新 > TESA).
  *
- * and y = y_MA + y_TE.  The projections around the mixer are the caller's:
- * this library takes the projected tensors (x, dt, B, C for the scan and
- * q, k, v for the attention) and returns the mixed tokens.
+ * and y = y_MA + y_TE.  lingen_mate_fwd takes the projected tensors (x, dt,
+ * B, C for the scan and q, k, v for the attention) and returns the mixed
+ * tokens; lingen_mate_block_fwd (at the end of this header) adds the steps
+ * and projections of the whole block around it.
  *
  * The scan uses Mamba2's scalar-A recurrence (Dao & Gu 2024): per head, with
  * state h in R^{P x N},
@@ -49,8 +50,9 @@
  *   Device work is enqueued on `stream` and the call returns without waiting;
  *   a launch failure is reported as LINGEN_ERR_HIP.  The only state the
  *   library keeps is a per-device cache of the compute-unit count (it sizes
- *   the persistent attention grid); concurrent calls on different streams
- *   are safe if they use different outputs and workspaces.
+ *   the persistent attention grid) and, for lingen_mate_block_fwd, one
+ *   rocBLAS handle per device; concurrent calls on different streams are
+ *   safe if they use different outputs and workspaces.
  */
 #ifndef LINGEN_MATE_H
 #define LINGEN_MATE_H
@@ -315,6 +317,73 @@ int lingen_ma_prep(const void* xbc, const float* dt_raw, const float* conv_w_f,
 int lingen_gated_rmsnorm(const void* y, const void* z, const float* weight, float eps,
                          int64_t rows, int32_t dim, int32_t group, int32_t dtype,
                          void* out, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------
+ * The whole MATE block: the mixer with the projections around both branches
+ * (page "视频生成模子太贵太慢如何办？", section 要领：线性复杂度的 MATE 模块: an MA
+ * branch and a TE branch replace the block's self-attention).  Readings where
+ * the pages are silent: the MA branch is laid out as a Mamba-2 block (Dao &
+ * Gu 2024, section 7) with one input projection per product (z, xBC, dt),
+ * the convolution of lingen_ma_prep, the per-direction scan of
+ * lingen_ma_fwd_dirs, the gated norm of lingen_gated_rmsnorm with one norm
+ * group per B/C group, and an output projection; the TE branch projects q,
+ * k, v, attends as lingen_te_fwd and projects its output; the block returns
+ * the sum of the two projected outputs.  The projections carry no bias.
+ * ------------------------------------------------------------------------- */
+
+/* Weights of one block, all device pointers owned by the caller, 16-byte
+ * aligned.  Projection matrices are row-major [out, in] in the shape dtype
+ * (y = u W^T); Dm = d_model, d = Hs*P = Ha*d_head, Ch = d + 2*G*N. */
+typedef struct {
+  const void* w_z;          /* [d, Dm]  gate z                                   */
+  const void* w_xbc;        /* [Ch, Dm] x, B, C channels                         */
+  const void* w_dt;         /* [Hs, Dm] dt_raw (product kept in fp32)            */
+  const float* conv_w_f;    /* [Ch, K] fp32, forward direction                   */
+  const float* conv_b_f;    /* [Ch]                                              */
+  const float* conv_w_b;    /* [Ch, K] fp32, backward direction                  */
+  const float* conv_b_b;    /* [Ch]                                              */
+  const float* dt_bias;     /* [Hs]                                              */
+  const float* A_f;         /* [Hs] <= 0, forward scan                           */
+  const float* D_f;         /* [Hs]                                              */
+  const float* A_b;         /* [Hs] <= 0, backward scan                          */
+  const float* D_b;         /* [Hs]                                              */
+  const float* norm_w;      /* [d] gated-norm weight                             */
+  const void* w_out_ma;     /* [Dm, d] MA output projection                      */
+  const void* w_q;          /* [d, Dm]                                           */
+  const void* w_k;          /* [d, Dm]                                           */
+  const void* w_v;          /* [d, Dm]                                           */
+  const void* w_o;          /* [Dm, d] TE output projection                      */
+} lingen_mate_block_weights;
+
+/* Workspace size of lingen_mate_block_fwd for `shape` and `d_model`.
+ * Errors as lingen_mate_block_fwd's shape checks; LINGEN_ERR_NULL for a NULL
+ * `bytes`. */
+int lingen_mate_block_workspace_bytes(const lingen_mate_shape* shape, int32_t d_model,
+                                      size_t* bytes);
+
+/* out = MA(u) + TE(u) for u [batch, L, d_model] (canonical token order,
+ * shape dtype), RMS mode = layer_idx mod 4 and shifted windows on odd
+ * layer_idx as in lingen_mate_fwd; conv_k taps (1..4); norm_eps >= 0.
+ *   out:       device, [batch, L, d_model], shape dtype; must not alias u.
+ *   workspace: device, at least lingen_mate_block_workspace_bytes bytes,
+ *              16-byte aligned; its contents on return are unspecified.
+ * The projections run as rocBLAS GEMMs (fp32 accumulation) on `stream`; the
+ * library keeps one rocBLAS handle per device for them, created at the first
+ * call on that device, and serialises its use with a lock.  Intermediates
+ * (z, xBC, q, k, v, the scan output and the normed output) are stored in the
+ * shape dtype; dt_raw and dt in fp32.
+ * Errors, all found before anything is enqueued: those of
+ * lingen_mate_validate; LINGEN_ERR_SHAPE for d_model outside 1..65536,
+ * batch*L of 2^31 or more, layer_idx < 0, conv_k outside 1..4, eps < 0, or
+ * d, G*N or d/G not a multiple of 16 bytes of elements or d above 8192
+ * (bf16) / 4096 (fp32); LINGEN_ERR_UNSUPPORTED for review tokens;
+ * LINGEN_ERR_NULL / _ALIGN for a pointer (weights included);
+ * LINGEN_ERR_WORKSPACE.  A failing rocBLAS call is reported as
+ * LINGEN_ERR_HIP, with the earlier steps already enqueued. */
+int lingen_mate_block_fwd(const void* u, const lingen_mate_block_weights* w, int32_t d_model,
+                          int32_t conv_k, float norm_eps, int32_t layer_idx,
+                          const lingen_mate_shape* shape, void* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -48,7 +48,12 @@ EXPORTS = (
     "lingen_dense_attn_fwd",
     "lingen_ma_prep",
     "lingen_gated_rmsnorm",
+    "lingen_mate_block_workspace_bytes",
+    "lingen_mate_block_fwd",
 )
+
+BLOCK_WEIGHTS = ("w_z", "w_xbc", "w_dt", "conv_w_f", "conv_b_f", "conv_w_b", "conv_b_b", "dt_bias", "A_f", "D_f",
+                 "A_b", "D_b", "norm_w", "w_out_ma", "w_q", "w_k", "w_v", "w_o")
 
 
 class LingenError(RuntimeError):
@@ -62,6 +67,10 @@ class lingen_mate_shape(ctypes.Structure):
         "batch", "T", "H", "W", "ssd_heads", "headdim", "d_state", "ngroups", "chunk",
         "attn_heads", "attn_headdim", "win_t", "win_h", "win_w", "dtype", "n_review",
         "rpool_t", "rpool_h", "rpool_w", "rgrid_t", "rgrid_h", "rgrid_w")]
+
+
+class lingen_mate_block_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_WEIGHTS]
 
 
 _lib = None
@@ -96,6 +105,9 @@ def lib() -> ctypes.CDLL:
         "lingen_dense_attn_fwd": ([P, P, P, P, I32, I32, I32, I32, I32, P], ctypes.c_int),
         "lingen_ma_prep": ([P] * 7 + [I32, I32, SP] + [P] * 7 + [P], ctypes.c_int),
         "lingen_gated_rmsnorm": ([P, P, P, ctypes.c_float, I64, I32, I32, I32, P, P], ctypes.c_int),
+        "lingen_mate_block_workspace_bytes": ([SP, I32, ctypes.POINTER(SZ)], ctypes.c_int),
+        "lingen_mate_block_fwd": ([P, ctypes.POINTER(lingen_mate_block_weights), I32, I32, ctypes.c_float, I32, SP,
+                                   P, P, SZ, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -455,4 +467,53 @@ def lingen_gated_rmsnorm(y, z, weight, eps: float, group: int, out=None):
     pw = _need(weight, "weight", torch.float32, dim)
     _check("lingen_gated_rmsnorm", lib().lingen_gated_rmsnorm(py, pz, pw, float(eps), rows, dim, int(group), code, po,
                                                               _stream()))
+    return out
+
+
+def lingen_mate_block_workspace_bytes(shape, d_model: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("lingen_mate_block_workspace_bytes",
+           lib().lingen_mate_block_workspace_bytes(ctypes.byref(to_c_shape(shape)), int(d_model), ctypes.byref(n)))
+    return n.value
+
+
+def block_weight_sizes(shape, d_model: int, conv_k: int = 4):
+    """Element counts of every block weight (see lingen_mate_block_weights)."""
+    d = shape.ssd_heads * shape.headdim
+    ch = d + 2 * shape.ngroups * shape.d_state
+    hs = shape.ssd_heads
+    return dict(w_z=d * d_model, w_xbc=ch * d_model, w_dt=hs * d_model, conv_w_f=ch * conv_k, conv_b_f=ch,
+                conv_w_b=ch * conv_k, conv_b_b=ch, dt_bias=hs, A_f=hs, D_f=hs, A_b=hs, D_b=hs, norm_w=d,
+                w_out_ma=d_model * d, w_q=d * d_model, w_k=d * d_model, w_v=d * d_model, w_o=d_model * d)
+
+
+def lingen_mate_block_fwd(u, weights, layer_idx: int, shape, conv_k: int = 4, norm_eps: float = 1e-5, out=None,
+                          workspace=None):
+    """The whole MATE block on u [batch, L, d_model]: ``weights`` maps every
+    name of BLOCK_WEIGHTS to a GPU tensor (projections in the shape dtype,
+    the rest fp32).  Returns out [batch, L, d_model]."""
+    torch = _torch()
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    L = shape.T * shape.H * shape.W
+    if u.dim() != 3 or u.shape[0] != shape.batch or u.shape[1] != L:
+        raise ValueError(f"u must be [{shape.batch}, {L}, d_model]")
+    d_model = int(u.shape[2])
+    sizes = block_weight_sizes(shape, d_model, conv_k)
+    w = lingen_mate_block_weights()
+    for name in BLOCK_WEIGHTS:
+        dtype = td if name.startswith("w_") else torch.float32
+        setattr(w, name, _need(weights[name], name, dtype, sizes[name]).value)
+    if out is None:
+        out = torch.empty_like(u)
+    pu = _need(u, "u", td, u.numel())
+    po = _need(out, "out", td, u.numel())
+    need = lingen_mate_block_workspace_bytes(shape, d_model)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    pw = ctypes.c_void_p(workspace.data_ptr())
+    nw = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    _check("lingen_mate_block_fwd", lib().lingen_mate_block_fwd(pu, ctypes.byref(w), d_model, int(conv_k),
+                                                                float(norm_eps), int(layer_idx), ctypes.byref(cs),
+                                                                po, pw, nw, _stream()))
     return out

@@ -22,7 +22,11 @@ LIB_NAME = "liblingen_mate.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = os.environ.get("LINGEN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["lingen_host.cpp", "lingen_kernels.hip", "dense_attn.hip", "tesa_bwd.hip", "block_steps.hip"]
+SOURCES = ["lingen_host.cpp", "lingen_kernels.hip", "dense_attn.hip", "tesa_bwd.hip", "block_steps.hip",
+           "lingen_block.cpp"]
+# The block's projections are plain GEMMs, left to rocBLAS.
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+LINK_FLAGS = [f"-L{ROCM}/lib", "-lrocblas", f"-Wl,-rpath,{ROCM}/lib"]
 
 COMMON_FLAGS = [
     "-O3",
@@ -73,7 +77,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *LINK_FLAGS]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -279,6 +279,61 @@ def test_gated_rmsnorm_rejects_before_launch(L):
     assert call(Z, Z, Z, 1e-5, 0, 4096, 64, 0, Z, None) == 0
 
 
+def test_mate_block_rejects_before_launch(L):
+    F = ctypes.c_void_p(FAKE)
+    Z = ctypes.c_void_p(0)
+    M = ctypes.c_void_p(MISALIGNED)
+    call = L.lingen_mate_block_fwd
+    cs = mate.to_c_shape(CONFIGS[1])
+    n = mate.lingen_mate_block_workspace_bytes(CONFIGS[1], 1024)
+    W = mate.binding.lingen_mate_block_weights
+
+    def weights(bad=None, value=None):
+        w = W()
+        for name in mate.BLOCK_WEIGHTS:
+            setattr(w, name, FAKE)
+        if bad is not None:
+            setattr(w, bad, value)
+        return w
+
+    good = weights()   # every call below is rejected before anything is enqueued
+    for dm, k, eps, layer in ((0, 4, 1e-5, 0), (70000, 4, 1e-5, 0), (1024, 0, 1e-5, 0), (1024, 5, 1e-5, 0),
+                              (1024, 4, -1.0, 0), (1024, 4, 1e-5, -1)):
+        assert call(F, ctypes.byref(good), dm, k, eps, layer, ctypes.byref(cs), F, F, n, None) == -2, (dm, k, eps)
+    for name in mate.BLOCK_WEIGHTS:
+        for value, code in ((0, -1), (MISALIGNED, -4)):
+            w = weights(name, value)
+            assert call(F, ctypes.byref(w), 1024, 4, 1e-5, 0, ctypes.byref(cs), F, F, n, None) == code, name
+    assert call(F, None, 1024, 4, 1e-5, 0, ctypes.byref(cs), F, F, n, None) == -1
+    for i in range(3):
+        p = [F, F, F]
+        p[i] = Z
+        assert call(p[0], ctypes.byref(good), 1024, 4, 1e-5, 0, ctypes.byref(cs), p[1], p[2], n, None) == -1
+        p[i] = M
+        assert call(p[0], ctypes.byref(good), 1024, 4, 1e-5, 0, ctypes.byref(cs), p[1], p[2], n, None) == -4
+    assert call(F, ctypes.byref(good), 1024, 4, 1e-5, 0, ctypes.byref(cs), F, F, n - 1, None) == -5
+    # review tokens are not supported by the per-direction scan the block uses
+    rv = mate.to_c_shape(CONFIGS[1].with_(n_review=64, rpool=(2, 4, 4), rgrid=(4, 4, 4)))
+    assert call(F, ctypes.byref(good), 1024, 4, 1e-5, 0, ctypes.byref(rv), F, F, n, None) == -7
+    size = ctypes.c_size_t(0)
+    assert L.lingen_mate_block_workspace_bytes(ctypes.byref(rv), 1024, ctypes.byref(size)) == -7
+    assert L.lingen_mate_block_workspace_bytes(ctypes.byref(cs), 1024, None) == -1
+    assert L.lingen_mate_block_workspace_bytes(None, 1024, ctypes.byref(size)) == -1
+
+
+def test_mate_block_workspace_formula():
+    """Workspace = the block's intermediates (aligned to 256 bytes) plus the
+    scan's own workspace."""
+    for cfg, dm in ((CONFIGS[0], 96), (CONFIGS[1], 1024), (CONFIGS[2], 2048)):
+        rows, e = cfg.batch * cfg.L, cfg.elem_bytes
+        d, gn, hs = cfg.ssd_heads * cfg.headdim, cfg.ngroups * cfg.d_state, cfg.ssd_heads
+        al = lambda b: (b + 255) // 256 * 256
+        parts = [rows * d * e, rows * (d + 2 * gn) * e, rows * hs * 4, rows * d * e, rows * gn * e, rows * gn * e,
+                 rows * d * e, rows * gn * e, rows * gn * e, rows * hs * 4, rows * d * e, rows * d * e, rows * d * e,
+                 rows * d * e, mate.lingen_mate_workspace_bytes(cfg)]
+        assert mate.lingen_mate_block_workspace_bytes(cfg, dm) == sum(al(b) for b in parts)
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     import linear_complexity_video_mate_amd.binding as b
     monkeypatch.setattr(b, "_lib", None)

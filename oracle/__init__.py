@@ -31,6 +31,8 @@ from .mate_oracle import (
     ssd_scan,
     ssd_bidir,
     ssd_dirs,
+    ssd_scan_backward,
+    ssd_bidir_backward,
     review_tokens,
     review_state,
     tesa_window_keys,
@@ -57,6 +59,8 @@ __all__ = [
     "ssd_scan",
     "ssd_bidir",
     "ssd_dirs",
+    "ssd_scan_backward",
+    "ssd_bidir_backward",
     "review_tokens",
     "review_state",
     "tesa_window_keys",

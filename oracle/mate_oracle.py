@@ -167,6 +167,97 @@ def ssd_bidir(x, dt, A, B, C, D, perm: np.ndarray, h0=None, stats=None):
     return y_f + y_b
 
 
+def _fold_groups(d_per_head, like) -> np.ndarray:
+    """Sum a per-head gradient [L, Hs, N] over the heads of each group, into
+    the layout of ``like`` ([L, N] for one group, [L, G, N] for several)."""
+    like = np.asarray(like)
+    L, Hs, N = d_per_head.shape
+    if like.ndim == 2:
+        return d_per_head.sum(axis=1)
+    G = like.shape[1]
+    return d_per_head.reshape(L, G, Hs // G, N).sum(axis=2)
+
+
+def ssd_scan_backward(x, dt, A, B, C, D, dy, order: Sequence[int], h0=None, segment: int = 64):
+    """Gradients of sum(dy * y) for y = ssd_scan(x, dt, A, B, C, D, order)[0]
+    with respect to x, dt, A, B, C, D: (dx, ddt, dA, dB, dC, dD), each in
+    the layout of its input.
+
+    The adjoint of the recurrence in ``ssd_scan``, walked backwards over the
+    visited tokens: with g the adjoint of the state after token c (g <- dy_c
+    C_c^T + exp(dt_next A) g_next),
+        dx_c  = dt_c g B_c + D dy_c          dB_c = dt_c g^T x_c
+        dC_c  = h_c^T dy_c                   dD  += dy_c . x_c
+        ddt_c = x_c^T g B_c + A exp(dt_c A) <h_prev, g>
+        dA   += dt_c exp(dt_c A) <h_prev, g>
+    per head (dB, dC summed over the heads of a group).  The states h are
+    kept every ``segment`` tokens and recomputed within a segment.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dt = np.asarray(dt, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    D = np.asarray(D, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    Hs, P = x.shape[1], x.shape[2]
+    Bh = _per_head(B, Hs)
+    Ch = _per_head(C, Hs)
+    N = Bh.shape[2]
+    order = np.asarray(order)
+    n = len(order)
+
+    def absorb(h, c):
+        a = np.exp(dt[c] * A)
+        return a[:, None, None] * h + (dt[c][:, None] * x[c])[:, :, None] * Bh[c][:, None, :]
+
+    h = np.zeros((Hs, P, N)) if h0 is None else np.array(h0, dtype=np.float64, copy=True)
+    ckpt = {}
+    for i, c in enumerate(order):
+        if i % segment == 0:
+            ckpt[i] = h.copy()                  # state before token i
+        h = absorb(h, c)
+
+    dx = np.zeros_like(x)
+    ddt = np.zeros_like(dt)
+    dA = np.zeros(Hs)
+    dBh = np.zeros((x.shape[0], Hs, N))
+    dCh = np.zeros((x.shape[0], Hs, N))
+    dD = np.zeros(Hs)
+    g = np.zeros((Hs, P, N))                    # adjoint of the state after the token being visited
+    for start in reversed(range(0, n, segment)):
+        idx = order[start:start + segment]
+        states = []
+        h = ckpt[start].copy()
+        for c in idx:
+            h = absorb(h, c)
+            states.append(h)
+        for j in reversed(range(len(idx))):
+            c = idx[j]
+            h_t = states[j]
+            h_prev = states[j - 1] if j > 0 else ckpt[start]
+            g = g + dy[c][:, :, None] * Ch[c][:, None, :]
+            dCh[c] += np.einsum("hpn,hp->hn", h_t, dy[c])
+            dx[c] += D[:, None] * dy[c]
+            dD += np.sum(dy[c] * x[c], axis=1)
+            a = np.exp(dt[c] * A)
+            gB = np.einsum("hpn,hn->hp", g, Bh[c])
+            dx[c] += dt[c][:, None] * gB
+            dBh[c] += dt[c][:, None] * np.einsum("hpn,hp->hn", g, x[c])
+            cross = np.sum(g * h_prev, axis=(1, 2))
+            ddt[c] += np.sum(x[c] * gB, axis=1) + A * a * cross
+            dA += dt[c] * a * cross
+            g = a[:, None, None] * g
+    return dx, ddt, dA, _fold_groups(dBh, B), _fold_groups(dCh, C), dD
+
+
+def ssd_bidir_backward(x, dt, A, B, C, D, dy, perm: np.ndarray):
+    """Gradients of sum(dy * y) for the shared-parameter bidirectional scan
+    ``ssd_bidir`` (no review state): the two directions' gradients summed."""
+    perm = np.asarray(perm)
+    f = ssd_scan_backward(x, dt, A, B, C, D, dy, perm)
+    b = ssd_scan_backward(x, dt, A, B, C, D, dy, perm[::-1])
+    return tuple(u + v for u, v in zip(f, b))
+
+
 def ssd_dirs(fwd, bwd, perm: np.ndarray):
     """Bidirectional scan with a parameter set per direction: the scan of
     ``fwd`` = (x, dt, A, B, C, D) along ``perm`` plus the scan of ``bwd`` along

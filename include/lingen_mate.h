@@ -263,6 +263,34 @@ int lingen_dense_attn_fwd(const void* q, const void* k, const void* v, void* o,
                           int32_t batch, int32_t L, int32_t heads, int32_t head_dim,
                           int32_t dtype, hipStream_t stream);
 
+/* Backward pass of the MA branch: the gradients of sum(dy * y_ma) for y_ma =
+ * lingen_ma_fwd(x, dt, A, B, C, D, mode) without review tokens (the
+ * shared-parameter bidirectional scan; [SSD] recurrence, page
+ * "视频生成模子太贵太慢如何办？", section 要领：线性复杂度的 MATE 模块), with
+ * respect to every input:
+ *   dx:  [batch, L, Hs, P] fp32      ddt: [batch, L, Hs] fp32
+ *   dB, dC: [batch, L, G, N] fp32 (summed over the heads of each group)
+ *   dA, dD: [Hs] fp32 (summed over tokens and batch elements)
+ * all device, caller-owned, overwritten.  dy has the layout and dtype of y.
+ * The gradients are assembled from the library's scans run with transformed
+ * operands (transposed scans with dt moved by one scan position, the scan
+ * of x' = dy exp(dt A) / dt for the adjoint chunk states, scans with B as
+ * values and x, dy as per-head keys and queries) and per-chunk sums for ddt
+ * and dA; see the source for the derivation.  Supported: bf16 storage with
+ * P = 64 and N a multiple of 64 (the compiled families (BF16, 64, 64, 64)
+ * and (BF16, 64, 128, 128)); anything else that passes lingen_mate_validate
+ * returns LINGEN_ERR_UNSUPPORTED, as do review tokens.
+ * workspace: device, lingen_ma_bwd_workspace_bytes (chunk states of two
+ * scans in fp32, plus the transformed operands and the scans' outputs).
+ * Errors: those of lingen_mate_validate; LINGEN_ERR_UNSUPPORTED as above;
+ * LINGEN_ERR_SHAPE for mode outside 0..3; LINGEN_ERR_NULL / _ALIGN for a
+ * pointer; LINGEN_ERR_WORKSPACE. */
+int lingen_ma_bwd_workspace_bytes(const lingen_mate_shape* shape, size_t* bytes);
+int lingen_ma_bwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                  const float* D, const void* dy, int32_t mode, const lingen_mate_shape* shape,
+                  float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ----------------------------------------------------------------------------
  * Steps around the scan.  The MA branch is a bidirectional Mamba2 block (page
  * "视频生成模子太贵太慢如何办？", section 要领：线性复杂度的 MATE 模块); these two

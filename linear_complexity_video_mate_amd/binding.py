@@ -50,6 +50,8 @@ EXPORTS = (
     "lingen_gated_rmsnorm",
     "lingen_mate_block_workspace_bytes",
     "lingen_mate_block_fwd",
+    "lingen_ma_bwd_workspace_bytes",
+    "lingen_ma_bwd",
 )
 
 BLOCK_WEIGHTS = ("w_z", "w_xbc", "w_dt", "conv_w_f", "conv_b_f", "conv_w_b", "conv_b_b", "dt_bias", "A_f", "D_f",
@@ -106,6 +108,8 @@ def lib() -> ctypes.CDLL:
         "lingen_ma_prep": ([P] * 7 + [I32, I32, SP] + [P] * 7 + [P], ctypes.c_int),
         "lingen_gated_rmsnorm": ([P, P, P, ctypes.c_float, I64, I32, I32, I32, P, P], ctypes.c_int),
         "lingen_mate_block_workspace_bytes": ([SP, I32, ctypes.POINTER(SZ)], ctypes.c_int),
+        "lingen_ma_bwd_workspace_bytes": ([SP, ctypes.POINTER(SZ)], ctypes.c_int),
+        "lingen_ma_bwd": ([P] * 7 + [I32, SP] + [P] * 7 + [SZ, P], ctypes.c_int),
         "lingen_mate_block_fwd": ([P, ctypes.POINTER(lingen_mate_block_weights), I32, I32, ctypes.c_float, I32, SP,
                                    P, P, SZ, P], ctypes.c_int),
     }
@@ -517,3 +521,41 @@ def lingen_mate_block_fwd(u, weights, layer_idx: int, shape, conv_k: int = 4, no
                                                                 float(norm_eps), int(layer_idx), ctypes.byref(cs),
                                                                 po, pw, nw, _stream()))
     return out
+
+
+def lingen_ma_bwd_workspace_bytes(shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check("lingen_ma_bwd_workspace_bytes",
+           lib().lingen_ma_bwd_workspace_bytes(ctypes.byref(to_c_shape(shape)), ctypes.byref(n)))
+    return n.value
+
+
+def lingen_ma_bwd(x, dt, A, B, C, D, dy, mode: int, shape, grads=None, workspace=None):
+    """Gradients (dx, ddt, dA, dB, dC, dD) of sum(dy * y_ma) for the MA
+    branch of lingen_ma_fwd (no review tokens), all fp32 GPU tensors."""
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    L = shape.T * shape.H * shape.W
+    f32 = torch.float32
+    args = [_need(x, "x", td, n["x"]), _need(dt, "dt", f32, n["dt"]), _need(A, "A", f32, n["A"]),
+            _need(B, "B", td, n["B"]), _need(C, "C", td, n["B"]), _need(D, "D", f32, n["D"]),
+            _need(dy, "dy", td, n["y"])]
+    if grads is None:
+        dev = "cuda"
+        grads = (torch.empty((shape.batch, L, shape.ssd_heads, shape.headdim), dtype=f32, device=dev),
+                 torch.empty((shape.batch, L, shape.ssd_heads), dtype=f32, device=dev),
+                 torch.empty(shape.ssd_heads, dtype=f32, device=dev),
+                 torch.empty((shape.batch, L, shape.ngroups, shape.d_state), dtype=f32, device=dev),
+                 torch.empty((shape.batch, L, shape.ngroups, shape.d_state), dtype=f32, device=dev),
+                 torch.empty(shape.ssd_heads, dtype=f32, device=dev))
+    sizes = (n["x"], n["dt"], n["A"], n["B"], n["B"], n["D"])
+    pg = [_need(g, name, f32, sz) for g, name, sz in zip(grads, ("dx", "ddt", "dA", "dB", "dC", "dD"), sizes)]
+    need = lingen_ma_bwd_workspace_bytes(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    pw = ctypes.c_void_p(workspace.data_ptr())
+    nw = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    _check("lingen_ma_bwd", lib().lingen_ma_bwd(*args, int(mode), ctypes.byref(cs), *pg, pw, nw, _stream()))
+    return grads

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = os.environ.get("LINGEN_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["lingen_host.cpp", "lingen_kernels.hip", "dense_attn.hip", "tesa_bwd.hip", "block_steps.hip",
-           "lingen_block.cpp"]
+           "lingen_block.cpp", "ma_bwd.hip"]
 # The block's projections are plain GEMMs, left to rocBLAS.
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 LINK_FLAGS = [f"-L{ROCM}/lib", "-lrocblas", f"-Wl,-rpath,{ROCM}/lib"]

@@ -16,27 +16,11 @@
 
 #include "lingen_device.h"
 #include "lingen_internal.h"
+#include "lingen_scan_map.h"
 
 namespace lingen {
 
 namespace {
-
-// Scan position -> canonical token for the four Rotary Major Scan orders
-// (t-major 0, h-fastest 1, t-fastest w-major 2, t-fastest h-major 3; the same
-// four maps the scan kernels use).
-struct ScanOrder {
-  int mode, T, H, W;
-  __device__ __forceinline__ int canon(int s) const {
-    int t, h, w;
-    switch (mode) {
-      case 0: return s;
-      case 1: { h = s % H; const int r = s / H; w = r % W; t = r / W; break; }
-      case 2: { t = s % T; const int r = s / T; w = r % W; h = r / W; break; }
-      default: { t = s % T; const int r = s / T; h = r % H; w = r / H; break; }
-    }
-    return (t * H + h) * W + w;
-  }
-};
 
 // v * sigmoid(v) with the hardware exp and reciprocal (about 1 ulp each).
 __device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }

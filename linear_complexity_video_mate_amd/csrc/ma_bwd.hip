@@ -1,0 +1,690 @@
+// Backward pass of the MA branch: gradients of sum(dy * y_MA) for the
+// shared-parameter bidirectional scan (Mamba2's scalar-A recurrence, "Transformers
+// are SSMs", Dao & Gu 2024; run along the Rotary Major Scan order and its
+// reverse, page "视频生成模子太贵太慢如何办？", section 要领：线性复杂度的 MATE 模块)
+// with respect to x, dt, A, B, C and D.
+//
+// Per direction write M for the scan's matrix (y = M x), L_ts for the decay
+// product between scan positions and W_ts = M_ts (dy_t . x_s).  Every
+// gradient is built from scans the library already runs, with transformed
+// operands, plus the kernels of this file:
+//   * M^T of one direction is the opposite direction's scan with dt moved
+//     by one scan position (so the decays cover the right tokens), the input
+//     divided by that moved dt and B, C exchanged: dx = dt (M_f^T + M_b^T) dy
+//     / dt + 2 D dy, and dB likewise with C as the values and dy, x as keys
+//     and queries (one group per head);
+//   * dC is the forward bidirectional scan with B as the values, x as the
+//     keys and dy as the queries (one group per head);
+//   * the chunk-boundary adjoint states are chunk states of the scan of
+//     x' = dy exp(dt A) / dt with C in place of B;
+//   * ddt and dA need, at every position r, the crossing sum
+//     R_r = sum_{s < r <= t} W_ts.  Within a chunk it is the suffix sum of
+//     dy_t . ytilde_t - dt_t x_t . yhat_t (ytilde: the direction's output,
+//     yhat: its transposed output before the dt factor) plus one constant,
+//     the inner product of the state entering the next chunk and the adjoint
+//     state leaving this one; ddt = x . (yhat_f + yhat_b) + A (R_f + R_b),
+//     dA = sum dt (R_f + R_b).
+// All sums are formed chunk by chunk, so no cancellation runs over the
+// whole sequence.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "lingen_device.h"
+#include "lingen_internal.h"
+#include "lingen_scan_map.h"
+
+namespace lingen {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kHalf = 64;   // value columns per auxiliary scan (its compiled head size)
+
+unsigned blocks_for(int64_t n) { return unsigned((n + kThreads - 1) / kThreads); }
+
+__device__ __forceinline__ void load8(const __bf16* p, float (&v)[8]) {
+  const bf16x8 u = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(u[e]);
+}
+__device__ __forceinline__ void store8(__bf16* p, const float (&v)[8]) {
+  bf16x8 u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) u[e] = static_cast<__bf16>(v[e]);
+  *reinterpret_cast<bf16x8*>(p) = u;
+}
+
+// Zero n16 16-byte units (a kernel, not a memset, so that the sequence can
+// be captured in a graph).
+__global__ __launch_bounds__(kThreads) void zero16_kernel(uint4* __restrict__ p, int64_t n16) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n16) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Zero three arrays of n floats each (the accumulated gradients dA, dD and a
+// zero D for the auxiliary scans).
+__global__ __launch_bounds__(kThreads) void zero_floats_kernel(float* __restrict__ a, float* __restrict__ b,
+                                                               float* __restrict__ c, int n) {
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    a[i] = 0.f;
+    b[i] = 0.f;
+    c[i] = 0.f;
+  }
+}
+
+// x' = dy * exp(dt A) / dt, for rows of Hs heads x P (P a multiple of 8).
+__global__ __launch_bounds__(kThreads) void adjoint_input_kernel(const __bf16* __restrict__ dy,
+                                                                 const float* __restrict__ dt,
+                                                                 const float* __restrict__ A, int64_t rows, int Hs,
+                                                                 int P, __bf16* __restrict__ out) {
+  const int upr = P / 8;
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= rows * Hs * upr) return;
+  const int64_t rh = i / upr;              // row * Hs + head
+  const int h = int(rh % Hs);
+  const float d = dt[rh];
+  const float s = __expf(d * A[h]) / d;
+  float v[8];
+  load8(dy + i * 8, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] *= s;
+  store8(out + i * 8, v);
+}
+
+// dt moved by one scan position each way, and dy divided by it:
+//   dt_next at the token of scan position r = dt at position r+1 (the last
+//   position keeps its own), dt_prev = dt at position r-1 (the first keeps
+//   its own); dy_next = dy / dt_next, dy_prev = dy / dt_prev.
+// One thread per (batch, scan position, head, 8 elements of P).
+__global__ __launch_bounds__(kThreads) void shifted_dt_kernel(const __bf16* __restrict__ dy,
+                                                              const float* __restrict__ dt, ScanOrder so, int L,
+                                                              int Hs, int P, int64_t total,
+                                                              float* __restrict__ dt_next,
+                                                              float* __restrict__ dt_prev,
+                                                              __bf16* __restrict__ dy_next,
+                                                              __bf16* __restrict__ dy_prev) {
+  const int upr = P / 8;
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= total) return;
+  const int unit = int(i % upr);
+  const int h = int((i / upr) % Hs);
+  const int64_t br = i / (int64_t(upr) * Hs);   // batch * L + scan position
+  const int r = int(br % L);
+  const int64_t base = br - r;                  // batch * L
+  const int64_t c = base + so.canon(r);
+  const int64_t cn = base + so.canon(r + 1 < L ? r + 1 : r);
+  const int64_t cp = base + so.canon(r > 0 ? r - 1 : r);
+  const float dn = dt[cn * Hs + h], dp = dt[cp * Hs + h];
+  if (unit == 0) {
+    dt_next[c * Hs + h] = dn;
+    dt_prev[c * Hs + h] = dp;
+  }
+  const int64_t off = (c * Hs + h) * P + unit * 8;
+  float v[8], a[8], b[8];
+  load8(dy + off, v);
+  const float rn = 1.f / dn, rp = 1.f / dp;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { a[e] = v[e] * rn; b[e] = v[e] * rp; }
+  store8(dy_next + off, a);
+  store8(dy_prev + off, b);
+}
+
+// Per-head values from columns [col0, col0 + 64) of a grouped tensor
+// src [rows, G, N]: out[row, h, j] = src[row, g(h), col0 + j] (/ scale[row, h]).
+__global__ __launch_bounds__(kThreads) void head_values_kernel(const __bf16* __restrict__ src, int G, int N,
+                                                               int col0, const float* __restrict__ scale, int Hs,
+                                                               int64_t rows, __bf16* __restrict__ out) {
+  constexpr int upr = kHalf / 8;
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= rows * Hs * upr) return;
+  const int unit = int(i % upr);
+  const int64_t rh = i / upr;
+  const int h = int(rh % Hs);
+  const int64_t row = rh / Hs;
+  const int g = h / (Hs / G);
+  float v[8];
+  load8(src + (row * G + g) * N + col0 + unit * 8, v);
+  if (scale != nullptr) {
+    const float r = 1.f / scale[rh];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= r;
+  }
+  store8(out + i * 8, v);
+}
+
+// dst[row, g, col0 + j] = sum over the heads h of group g of w[row, h] *
+// src[row, h, j] (w = 1 when NULL), fp32.  One thread per (row, group, 4 j).
+__global__ __launch_bounds__(kThreads) void group_sum_kernel(const __bf16* __restrict__ src,
+                                                             const float* __restrict__ w, int Hs, int G, int N,
+                                                             int col0, int64_t rows, float* __restrict__ dst) {
+  constexpr int upr = kHalf / 4;
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= rows * G * upr) return;
+  const int unit = int(i % upr);
+  const int g = int((i / upr) % G);
+  const int64_t row = i / (int64_t(upr) * G);
+  const int hpg = Hs / G;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const float s = w != nullptr ? w[row * Hs + h] : 1.f;
+    const bf16x4 u = *reinterpret_cast<const bf16x4*>(src + (row * Hs + h) * kHalf + unit * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(s, static_cast<float>(u[e]), acc[e]);
+  }
+  *reinterpret_cast<float4*>(dst + (row * G + g) * N + col0 + unit * 4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+}
+
+constexpr int kCrossThreads = 512;
+
+// Block-wide sum over the 512 threads of a workgroup.
+__device__ __forceinline__ float block_sum512(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCrossThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+__device__ __forceinline__ float bf(const bf16x8& u, int e) { return static_cast<float>(u[e]); }
+
+// The crossing sums R_r of both directions for one (chunk, head, batch
+// element), head size 64, written to R [batch, L, Hs] fp32.  With cs the
+// chunk-local inclusive cumulative sum of dt*A along the scan order and csx
+// its exclusive form, V_ts = dt_s (C_t . B_s)(dy_t . x_s):
+//   forward pairs s < t:  W_ts = exp(cs_t - cs_s) V_ts,   crossing s < r <= t
+//   backward pairs s > t: W_ts = exp(csx_s - csx_t) V_ts, crossing t <= r < s
+// R_r = (pairs inside the chunk: suffix / prefix sums of row minus column
+// sums of W) + (pairs with one end outside: the boundary terms below, from
+// the chunk states) + (pairs with both ends outside: a constant).  Boundary
+// terms, with hf1 = forward state entering the chunk, hb1 = reverse state
+// entering it from the right, hf2 / hb2 = the adjoint states of the reverse /
+// forward scan (chunk states of x' = dy exp(dt A) / dt against C):
+//   U_f(t) = exp(cs_t) dy_t . (hf1 C_t)               (s before the chunk)
+//   V_f(s) = dt_s exp(cs_last - cs_s) x_s . (hb2 B_s) (t after the chunk)
+//   U_b(t) = exp(cs_last - csx_t) dy_t . (hb1 C_t)    (s after the chunk)
+//   V_b(s) = dt_s exp(csx_s) x_s . (hf2 B_s)          (t before the chunk)
+//   K = exp(cs_last) (<hf1, hb2> + <hb1, hf2>)
+// R_r = suffix_{t >= r}(d_f + U_f + V_b) + prefix_{t <= r}(d_b + U_b + V_f)
+//       - V_f(r) - V_b(r) + K.
+// Every product is formed in fp32 from the bf16 inputs and the fp32 states,
+// chunk by chunk, so no sum runs across the sequence.  512 threads; thread
+// (tid / 16, tid % 16) owns a (Q/32) x (Q/16) tile of the Q x Q products and
+// a (Q/32) x (N/16) tile of the Q x N ones.
+template <int Q, int N>
+__global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
+    const __bf16* __restrict__ x, const __bf16* __restrict__ dy, const float* __restrict__ dt,
+    const float* __restrict__ A, const __bf16* __restrict__ B, const __bf16* __restrict__ C,
+    const float* __restrict__ hf1, const float* __restrict__ hb1, const float* __restrict__ hf2,
+    const float* __restrict__ hb2, ScanOrder so, int L, int Hs, int G, float* __restrict__ R) {
+  constexpr int P = 64, NT = kCrossThreads;
+  constexpr int LDB = N + 8, LDX = P + 8;     // padded bf16 row strides
+  constexpr int TR = Q / 32, TC = Q / 16, TCN = N / 16;
+  static_assert(Q % 32 == 0 && Q <= NT && N % 16 == 0, "tiles");
+  __shared__ __attribute__((aligned(16))) __bf16 sB[Q * LDB], sC[Q * LDB], sX[Q * LDX], sDY[Q * LDX];
+  __shared__ __attribute__((aligned(16))) float sM[P * N];
+  __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], red[NT / 64];
+  __shared__ int s_tok[Q];
+
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nc = L / Q;
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  const int g = h / (Hs / G);
+  const float a_h = A[h];
+  const int64_t bl = int64_t(b) * L;
+
+  for (int i = tid; i < Q; i += NT) {
+    const int tok = so.canon(c * Q + i);
+    s_tok[i] = tok;
+    s_dt[i] = dt[(bl + tok) * Hs + h];
+    s_fw[i] = 0.f;
+    s_bw[i] = 0.f;
+    s_sub[i] = 0.f;
+  }
+  __syncthreads();
+  for (int i = tid; i < Q * (N / 8); i += NT) {
+    const int row = i / (N / 8), k8 = (i % (N / 8)) * 8;
+    const int64_t src = ((bl + s_tok[row]) * G + g) * N + k8;
+    *reinterpret_cast<bf16x8*>(sB + row * LDB + k8) = *reinterpret_cast<const bf16x8*>(B + src);
+    *reinterpret_cast<bf16x8*>(sC + row * LDB + k8) = *reinterpret_cast<const bf16x8*>(C + src);
+  }
+  for (int i = tid; i < Q * (P / 8); i += NT) {
+    const int row = i / (P / 8), k8 = (i % (P / 8)) * 8;
+    const int64_t src = ((bl + s_tok[row]) * Hs + h) * P + k8;
+    *reinterpret_cast<bf16x8*>(sX + row * LDX + k8) = *reinterpret_cast<const bf16x8*>(x + src);
+    *reinterpret_cast<bf16x8*>(sDY + row * LDX + k8) = *reinterpret_cast<const bf16x8*>(dy + src);
+  }
+  // chunk-local cumulative sums of dt*A (inclusive in s_cs)
+  for (int i = tid; i < Q; i += NT) s_cs[i] = s_dt[i] * a_h;
+  __syncthreads();
+  for (int off = 1; off < Q; off <<= 1) {
+    float v = 0.f;
+    if (tid < Q && tid >= off) v = s_cs[tid - off];
+    __syncthreads();
+    if (tid < Q) s_cs[tid] += v;
+    __syncthreads();
+  }
+  for (int i = tid; i < Q; i += NT) s_csx[i] = s_cs[i] - s_dt[i] * a_h;
+  __syncthreads();
+  const float cs_last = s_cs[Q - 1];
+
+  // pairs inside the chunk
+  {
+    float cb[TR][TC], dx[TR][TC];
+#pragma unroll
+    for (int i = 0; i < TR; ++i)
+#pragma unroll
+      for (int j = 0; j < TC; ++j) { cb[i][j] = 0.f; dx[i][j] = 0.f; }
+    const int t0 = ty * TR, s0 = tx * TC;
+#pragma unroll 2
+    for (int k = 0; k < N; k += 8) {
+      bf16x8 ct[TR], bs[TC];
+#pragma unroll
+      for (int i = 0; i < TR; ++i) ct[i] = *reinterpret_cast<const bf16x8*>(sC + (t0 + i) * LDB + k);
+#pragma unroll
+      for (int j = 0; j < TC; ++j) bs[j] = *reinterpret_cast<const bf16x8*>(sB + (s0 + j) * LDB + k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < TR; ++i) {
+          const float cv = bf(ct[i], e);
+#pragma unroll
+          for (int j = 0; j < TC; ++j) cb[i][j] = fmaf(cv, bf(bs[j], e), cb[i][j]);
+        }
+    }
+#pragma unroll 2
+    for (int k = 0; k < P; k += 8) {
+      bf16x8 yt[TR], xs[TC];
+#pragma unroll
+      for (int i = 0; i < TR; ++i) yt[i] = *reinterpret_cast<const bf16x8*>(sDY + (t0 + i) * LDX + k);
+#pragma unroll
+      for (int j = 0; j < TC; ++j) xs[j] = *reinterpret_cast<const bf16x8*>(sX + (s0 + j) * LDX + k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < TR; ++i) {
+          const float yv = bf(yt[i], e);
+#pragma unroll
+          for (int j = 0; j < TC; ++j) dx[i][j] = fmaf(yv, bf(xs[j], e), dx[i][j]);
+        }
+    }
+    float rf[TR], rbk[TR], cf[TC], cbk[TC];
+#pragma unroll
+    for (int i = 0; i < TR; ++i) { rf[i] = 0.f; rbk[i] = 0.f; }
+#pragma unroll
+    for (int j = 0; j < TC; ++j) { cf[j] = 0.f; cbk[j] = 0.f; }
+#pragma unroll
+    for (int i = 0; i < TR; ++i) {
+      const int t = t0 + i;
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        const int s2 = s0 + j;
+        const float v = s_dt[s2] * cb[i][j] * dx[i][j];
+        if (s2 < t) {
+          const float w = __expf(s_cs[t] - s_cs[s2]) * v;
+          rf[i] += w;
+          cf[j] += w;
+        } else if (s2 > t) {
+          const float w = __expf(s_csx[s2] - s_csx[t]) * v;
+          rbk[i] += w;
+          cbk[j] += w;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TR; ++i) {
+      atomicAdd(s_fw + t0 + i, rf[i]);
+      atomicAdd(s_bw + t0 + i, rbk[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < TC; ++j) {
+      atomicAdd(s_fw + s0 + j, -cf[j]);
+      atomicAdd(s_bw + s0 + j, -cbk[j]);
+    }
+  }
+
+  // pairs with one end outside the chunk: a_t . (M b_t) for the four states
+  const int64_t st_off = ((int64_t(b) * nc + c) * Hs + h) * int64_t(P) * N;
+  const float* mats[4] = {hf1 + st_off, hb2 + st_off, hb1 + st_off, hf2 + st_off};
+#pragma unroll 1
+  for (int term = 0; term < 4; ++term) {
+    __syncthreads();   // sM is free, and the pair sums above have landed
+    for (int i = tid; i < P * N / 4; i += NT)
+      reinterpret_cast<float4*>(sM)[i] = reinterpret_cast<const float4*>(mats[term])[i];
+    __syncthreads();
+    const bool is_u = (term == 0 || term == 2);          // U terms: dy and C; V terms: x and B
+    const __bf16* sa = is_u ? sDY : sX;
+    const __bf16* sv = is_u ? sC : sB;
+    const int t0 = ty * TR, n0 = tx * TCN;
+    float acc[TR][TCN];
+#pragma unroll
+    for (int i = 0; i < TR; ++i)
+#pragma unroll
+      for (int j = 0; j < TCN; ++j) acc[i][j] = 0.f;
+#pragma unroll 2
+    for (int p = 0; p < P; p += 8) {
+      bf16x8 av[TR];
+#pragma unroll
+      for (int i = 0; i < TR; ++i) av[i] = *reinterpret_cast<const bf16x8*>(sa + (t0 + i) * LDX + p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float mv[TCN];
+#pragma unroll
+        for (int j = 0; j < TCN; ++j) mv[j] = sM[(p + e) * N + n0 + j];
+#pragma unroll
+        for (int i = 0; i < TR; ++i) {
+          const float a = bf(av[i], e);
+#pragma unroll
+          for (int j = 0; j < TCN; ++j) acc[i][j] = fmaf(a, mv[j], acc[i][j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TR; ++i) {
+      const int t = t0 + i;
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < TCN; ++j) sum = fmaf(acc[i][j], static_cast<float>(sv[t * LDB + n0 + j]), sum);
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
+      if (tx == 0) {
+        if (term == 0) {
+          s_fw[t] += __expf(s_cs[t]) * sum;                          // U_f
+        } else if (term == 1) {
+          const float v = s_dt[t] * __expf(cs_last - s_cs[t]) * sum;  // V_f
+          s_bw[t] += v;
+          s_sub[t] += v;
+        } else if (term == 2) {
+          s_bw[t] += __expf(cs_last - s_csx[t]) * sum;               // U_b
+        } else {
+          const float v = s_dt[t] * __expf(s_csx[t]) * sum;          // V_b
+          s_fw[t] += v;
+          s_sub[t] += v;
+        }
+      }
+    }
+  }
+
+  // pairs with both ends outside
+  float k = 0.f;
+  for (int e = tid * 4; e < P * N; e += NT * 4) {
+    const float4 u1 = *reinterpret_cast<const float4*>(mats[0] + e), v1 = *reinterpret_cast<const float4*>(mats[1] + e);
+    const float4 u2 = *reinterpret_cast<const float4*>(mats[2] + e), v2 = *reinterpret_cast<const float4*>(mats[3] + e);
+    k += u1.x * v1.x + u1.y * v1.y + u1.z * v1.z + u1.w * v1.w + u2.x * v2.x + u2.y * v2.y + u2.z * v2.z + u2.w * v2.w;
+  }
+  k = __expf(cs_last) * block_sum512(k, red);   // its barriers also order the boundary terms before the scans
+
+  // suffix sums of s_fw, prefix sums of s_bw
+  for (int off = 1; off < Q; off <<= 1) {
+    float f = 0.f, bk = 0.f;
+    if (tid < Q) {
+      if (tid + off < Q) f = s_fw[tid + off];
+      if (tid >= off) bk = s_bw[tid - off];
+    }
+    __syncthreads();
+    if (tid < Q) {
+      s_fw[tid] += f;
+      s_bw[tid] += bk;
+    }
+    __syncthreads();
+  }
+  if (tid < Q) R[(bl + s_tok[tid]) * Hs + h] = s_fw[tid] + s_bw[tid] - s_sub[tid] + k;
+}
+
+// Per (chunk, head, batch element), one thread per scan position of the
+// chunk (Q <= 128), head size 64: dx = dt (yhat_f + yhat_b) + 2 D dy, ddt =
+// x . (yhat_f + yhat_b) + A R, and this chunk's share of dA = sum dt R and
+// dD = 2 sum dy . x.  yhat_f, yhat_b: the transposed outputs M_f^T dy / dt,
+// M_b^T dy / dt; R: the crossing sums.
+__global__ __launch_bounds__(128) void ma_bwd_chunk_kernel(
+    const __bf16* __restrict__ x, const __bf16* __restrict__ dy, const float* __restrict__ dt,
+    const float* __restrict__ A, const float* __restrict__ D, const __bf16* __restrict__ yh_f,
+    const __bf16* __restrict__ yh_b, const float* __restrict__ R, ScanOrder so, int L, int Q, int Hs,
+    float* __restrict__ dx, float* __restrict__ ddt, float* __restrict__ dA, float* __restrict__ dD) {
+  constexpr int P = 64;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int i = threadIdx.x;
+  float da = 0.f, dd = 0.f;
+  if (i < Q) {
+    const int64_t t = int64_t(b) * L + so.canon(c * Q + i);
+    const int64_t rh = t * Hs + h;
+    const float d = dt[rh], r = R[rh];
+    const int64_t off = rh * P;
+    float xyh = 0.f, dyx = 0.f;
+    const float two_d = 2.f * D[h];
+    for (int u = 0; u < P; u += 8) {
+      float vx[8], vdy[8], vhf[8], vhb[8], gx[8];
+      load8(x + off + u, vx);
+      load8(dy + off + u, vdy);
+      load8(yh_f + off + u, vhf);
+      load8(yh_b + off + u, vhb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float s2 = vhf[e] + vhb[e];
+        xyh = fmaf(vx[e], s2, xyh);
+        dyx = fmaf(vdy[e], vx[e], dyx);
+        gx[e] = fmaf(d, s2, two_d * vdy[e]);
+      }
+      float4* o = reinterpret_cast<float4*>(dx + off + u);
+      o[0] = make_float4(gx[0], gx[1], gx[2], gx[3]);
+      o[1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
+    }
+    ddt[rh] = xyh + A[h] * r;
+    da = d * r;
+    dd = 2.f * dyx;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    da += __shfl_xor(da, off, 64);
+    dd += __shfl_xor(dd, off, 64);
+  }
+  if ((i & 63) == 0) {
+    atomicAdd(dA + h, da);
+    atomicAdd(dD + h, dd);
+  }
+}
+
+// Byte offsets inside the caller's workspace.
+struct BwdWs {
+  size_t hf1, hb1, hf2, hb2, scan, xprime, zero, dzero, dt_next, dt_prev, dy_next, dy_prev, R, yh_f, yh_b,
+      val_a, val_b, out, total;
+};
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+lingen_mate_shape aux_shape(const lingen_mate_shape* s) {
+  // the scans whose keys and queries are per-head P-vectors: one group per
+  // head, key size P, 64 value columns per call, chunk 64
+  lingen_mate_shape a = *s;
+  a.headdim = kHalf;
+  a.d_state = s->headdim;
+  a.ngroups = s->ssd_heads;
+  a.chunk = 64;
+  a.attn_heads = s->ssd_heads;
+  a.attn_headdim = kHalf;
+  a.n_review = 0;
+  return a;
+}
+
+int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
+  const size_t rows = size_t(s->batch) * size_t(tokens(s));
+  const size_t hs = size_t(s->ssd_heads), P = size_t(s->headdim), N = size_t(s->d_state);
+  const size_t nc = size_t(tokens(s)) / size_t(s->chunk);
+  const lingen_mate_shape a = aux_shape(s);
+  size_t ws_main = 0, ws_aux = 0;
+  if (int rc = lingen_mate_workspace_bytes(s, &ws_main)) return rc;
+  if (int rc = lingen_mate_workspace_bytes(&a, &ws_aux)) return rc;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+  const size_t states = size_t(s->batch) * nc * hs * P * N * 4;
+  w->hf1 = take(states);
+  w->hb1 = take(states);
+  w->hf2 = take(states);
+  w->hb2 = take(states);
+  w->scan = take(ws_main > ws_aux ? ws_main : ws_aux);
+  w->xprime = take(rows * hs * P * 2);
+  w->zero = take(rows * hs * P * 2);
+  w->dzero = take(hs * 4);
+  w->dt_next = take(rows * hs * 4);
+  w->dt_prev = take(rows * hs * 4);
+  w->dy_next = take(rows * hs * P * 2);
+  w->dy_prev = take(rows * hs * P * 2);
+  w->R = take(rows * hs * 4);
+  w->yh_f = take(rows * hs * P * 2);
+  w->yh_b = take(rows * hs * P * 2);
+  w->val_a = take(rows * hs * kHalf * 2);
+  w->val_b = take(rows * hs * kHalf * 2);
+  w->out = take(rows * hs * kHalf * 2);
+  w->total = off;
+  return LINGEN_OK;
+}
+
+int check_bwd_shape(const lingen_mate_shape* s) {
+  if (int rc = validate_shape(s)) return rc;
+  if (s->n_review != 0) return LINGEN_ERR_UNSUPPORTED;
+  // the transposed scans run in the bf16 family whose key size is the head
+  // size: bf16 storage, P = 64, N a multiple of 64
+  if (s->dtype != LINGEN_BF16 || s->headdim != 64 || s->d_state % kHalf) return LINGEN_ERR_UNSUPPORTED;
+  // the crossing-sum kernel is compiled for the two bf16 scan families with P = 64
+  if (!((s->chunk == 64 && s->d_state == 64) || (s->chunk == 128 && s->d_state == 128))) return LINGEN_ERR_UNSUPPORTED;
+  const lingen_mate_shape a = aux_shape(s);
+  return validate_shape(&a);
+}
+
+int zero_fill(void* p, size_t bytes, hipStream_t st) {
+  const int64_t n16 = int64_t(bytes / 16);
+  if (n16 == 0) return LINGEN_OK;
+  zero16_kernel<<<blocks_for(n16), kThreads, 0, st>>>(static_cast<uint4*>(p), n16);
+  return hipGetLastError() == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace lingen
+
+using namespace lingen;
+
+extern "C" int lingen_ma_bwd_workspace_bytes(const lingen_mate_shape* shape, size_t* bytes) {
+  if (bytes == nullptr) return LINGEN_ERR_NULL;
+  if (int rc = check_bwd_shape(shape)) return rc;
+  BwdWs w{};
+  if (int rc = bwd_layout(shape, &w)) return rc;
+  *bytes = w.total;
+  return LINGEN_OK;
+}
+
+extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                             const float* D, const void* dy, int32_t mode, const lingen_mate_shape* shape,
+                             float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (int rc = check_bwd_shape(shape)) return rc;
+  if (mode < 0 || mode > 3) return LINGEN_ERR_SHAPE;
+  const void* ptrs[] = {x, dt, A, B, C, D, dy, dx, ddt, dA, dB, dC, dD, workspace};
+  for (const void* p : ptrs)
+    if (int rc = check_ptr(p)) return rc;
+  BwdWs w{};
+  if (int rc = bwd_layout(shape, &w)) return rc;
+  if (workspace_bytes < w.total) return LINGEN_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+  auto atf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const int L = int(tokens(shape)), Hs = shape->ssd_heads, P = shape->headdim, N = shape->d_state;
+  const int G = shape->ngroups, Q = shape->chunk, nc = L / Q;
+  const int64_t rows = int64_t(shape->batch) * L;
+  const size_t scan_bytes = w.xprime - w.scan;
+  const ScanOrder so{mode, shape->T, shape->H, shape->W};
+  const lingen_mate_shape aux = aux_shape(shape);
+  const __bf16* xb = static_cast<const __bf16*>(x);
+  const __bf16* dyb = static_cast<const __bf16*>(dy);
+  int rc;
+#define LINGEN_TRY(expr)                          \
+  do {                                            \
+    if ((rc = (expr)) != LINGEN_OK) return rc;    \
+  } while (0)
+#define LINGEN_LAUNCHED()                                             \
+  do {                                                                \
+    if (hipGetLastError() != hipSuccess) return LINGEN_ERR_HIP;       \
+  } while (0)
+
+  LINGEN_TRY(zero_fill(at(w.zero), rows * Hs * P * 2, stream));
+  zero_floats_kernel<<<1, kThreads, 0, stream>>>(atf(w.dzero), dA, dD, Hs);   // D = 0 for the auxiliary scans; dA, dD
+  LINGEN_LAUNCHED();
+  const float* dz = atf(w.dzero);
+  const void* zx = at(w.zero);
+
+  // forward states of (x, B) and adjoint states of (x', C)
+  LINGEN_TRY(lingen_ssd_chunk_states(x, dt, A, B, mode, shape, atf(w.hf1), atf(w.hb1), at(w.scan), scan_bytes,
+                                     stream));
+  adjoint_input_kernel<<<blocks_for(rows * Hs * (P / 8)), kThreads, 0, stream>>>(
+      dyb, dt, A, rows, Hs, P, static_cast<__bf16*>(at(w.xprime)));
+  LINGEN_LAUNCHED();
+  LINGEN_TRY(lingen_ssd_chunk_states(at(w.xprime), dt, A, C, mode, shape, atf(w.hf2), atf(w.hb2), at(w.scan),
+                                     scan_bytes, stream));
+
+  // transposed outputs: M_b^T dy / dt is the forward scan with dt_prev, M_f^T dy / dt the reverse scan with
+  // dt_next, inputs dy / (moved dt), B and C exchanged
+  {
+    const int64_t total = rows * Hs * (P / 8);
+    shifted_dt_kernel<<<blocks_for(total), kThreads, 0, stream>>>(
+        dyb, dt, so, L, Hs, P, total, atf(w.dt_next), atf(w.dt_prev), static_cast<__bf16*>(at(w.dy_next)),
+        static_cast<__bf16*>(at(w.dy_prev)));
+    LINGEN_LAUNCHED();
+  }
+  const float* dtn = atf(w.dt_next);
+  const float* dtp = atf(w.dt_prev);
+  LINGEN_TRY(lingen_ma_fwd_dirs(at(w.dy_prev), dtp, A, C, B, dz, zx, dtp, A, C, B, dz, mode, shape, at(w.yh_b),
+                                at(w.scan), scan_bytes, stream));
+  LINGEN_TRY(lingen_ma_fwd_dirs(zx, dtn, A, C, B, dz, at(w.dy_next), dtn, A, C, B, dz, mode, shape, at(w.yh_f),
+                                at(w.scan), scan_bytes, stream));
+
+  // dC and dB, 64 value columns at a time, keys and queries per head
+  for (int col0 = 0; col0 < N; col0 += kHalf) {
+    head_values_kernel<<<blocks_for(rows * Hs * (kHalf / 8)), kThreads, 0, stream>>>(
+        static_cast<const __bf16*>(B), G, N, col0, nullptr, Hs, rows, static_cast<__bf16*>(at(w.val_a)));
+    LINGEN_LAUNCHED();
+    LINGEN_TRY(lingen_ma_fwd(at(w.val_a), dt, A, x, dy, dz, mode, &aux, at(w.out), at(w.scan), scan_bytes, stream));
+    group_sum_kernel<<<blocks_for(rows * G * (kHalf / 4)), kThreads, 0, stream>>>(
+        static_cast<const __bf16*>(at(w.out)), nullptr, Hs, G, N, col0, rows, dC);
+    LINGEN_LAUNCHED();
+
+    head_values_kernel<<<blocks_for(rows * Hs * (kHalf / 8)), kThreads, 0, stream>>>(
+        static_cast<const __bf16*>(C), G, N, col0, dtp, Hs, rows, static_cast<__bf16*>(at(w.val_a)));
+    LINGEN_LAUNCHED();
+    head_values_kernel<<<blocks_for(rows * Hs * (kHalf / 8)), kThreads, 0, stream>>>(
+        static_cast<const __bf16*>(C), G, N, col0, dtn, Hs, rows, static_cast<__bf16*>(at(w.val_b)));
+    LINGEN_LAUNCHED();
+    LINGEN_TRY(lingen_ma_fwd_dirs(at(w.val_a), dtp, A, dy, x, dz, at(w.val_b), dtn, A, dy, x, dz, mode, &aux,
+                                  at(w.out), at(w.scan), scan_bytes, stream));
+    group_sum_kernel<<<blocks_for(rows * G * (kHalf / 4)), kThreads, 0, stream>>>(
+        static_cast<const __bf16*>(at(w.out)), dt, Hs, G, N, col0, rows, dB);
+    LINGEN_LAUNCHED();
+  }
+
+  // crossing sums, then ddt, dx, dA, dD
+  {
+    const dim3 grid{unsigned(nc), unsigned(Hs), unsigned(shape->batch)};
+    const __bf16* bb = static_cast<const __bf16*>(B);
+    const __bf16* cc = static_cast<const __bf16*>(C);
+    if (Q == 128 && N == 128)
+      ma_bwd_cross_kernel<128, 128><<<grid, kCrossThreads, 0, stream>>>(
+          xb, dyb, dt, A, bb, cc, atf(w.hf1), atf(w.hb1), atf(w.hf2), atf(w.hb2), so, L, Hs, G, atf(w.R));
+    else if (Q == 64 && N == 64)
+      ma_bwd_cross_kernel<64, 64><<<grid, kCrossThreads, 0, stream>>>(
+          xb, dyb, dt, A, bb, cc, atf(w.hf1), atf(w.hb1), atf(w.hf2), atf(w.hb2), so, L, Hs, G, atf(w.R));
+    else
+      return LINGEN_ERR_UNSUPPORTED;
+    LINGEN_LAUNCHED();
+    ma_bwd_chunk_kernel<<<grid, 128, 0, stream>>>(xb, dyb, dt, A, D, static_cast<const __bf16*>(at(w.yh_f)),
+                                                 static_cast<const __bf16*>(at(w.yh_b)), atf(w.R), so, L, Q, Hs,
+                                                 dx, ddt, dA, dD);
+    LINGEN_LAUNCHED();
+  }
+#undef LINGEN_TRY
+#undef LINGEN_LAUNCHED
+  return LINGEN_OK;
+}

@@ -334,6 +334,32 @@ def test_mate_block_workspace_formula():
         assert mate.lingen_mate_block_workspace_bytes(cfg, dm) == sum(al(b) for b in parts)
 
 
+def test_ma_bwd_rejects_before_launch(L):
+    F = ctypes.c_void_p(FAKE)
+    Z = ctypes.c_void_p(0)
+    M = ctypes.c_void_p(MISALIGNED)
+    call = L.lingen_ma_bwd
+    cs = mate.to_c_shape(CONFIGS[1])
+    n = mate.lingen_ma_bwd_workspace_bytes(CONFIGS[1])
+    for bad in (-1, 4):
+        assert call(*[F] * 7, bad, ctypes.byref(cs), *[F] * 7, n, None) == -2
+    for i in range(14):
+        p = [F] * 14
+        p[i] = Z
+        assert call(*p[:7], 0, ctypes.byref(cs), *p[7:], n, None) == -1, i
+        p[i] = M
+        assert call(*p[:7], 0, ctypes.byref(cs), *p[7:], n, None) == -4, i
+    assert call(*[F] * 7, 0, ctypes.byref(cs), *[F] * 7, n - 1, None) == -5
+    # fp32 storage, review tokens, a head size other than 64: not supported
+    for shape in (CONFIGS[0], CONFIGS[1].with_(n_review=64, rpool=(2, 4, 4), rgrid=(4, 4, 4))):
+        c = mate.to_c_shape(shape)
+        assert call(*[F] * 7, 0, ctypes.byref(c), *[F] * 7, n, None) == -7
+        size = ctypes.c_size_t(0)
+        assert L.lingen_ma_bwd_workspace_bytes(ctypes.byref(c), ctypes.byref(size)) == -7
+    assert call(*[F] * 7, 0, None, *[F] * 7, n, None) == -1
+    assert L.lingen_ma_bwd_workspace_bytes(ctypes.byref(cs), None) == -1
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     import linear_complexity_video_mate_amd.binding as b
     monkeypatch.setattr(b, "_lib", None)

@@ -464,6 +464,49 @@ def mate_block(args, mate, torch):
     return 0
 
 
+def ma_backward(args, mate, torch):
+    """The MA branch's backward pass (lingen_ma_bwd) on the workload against
+    its forward (lingen_ma_fwd), both timed with events on the launch stream,
+    scan order = step mod 4."""
+    from mate_inputs import CONFIGS, CONFIG_NOTES, make_inputs
+
+    s = CONFIGS[args.config]
+    inp = make_inputs(s, args.config, tensors=["x", "dt", "A", "B", "C", "D"], threads=16)
+    d = {n: inp.torch(n, "cuda") for n in ("x", "dt", "A", "B", "C", "D")}
+    dy = torch.empty((s.batch, s.L, s.d_inner), dtype=d["x"].dtype, device="cuda").normal_()
+    grads = mate.lingen_ma_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], dy, 0, s)
+    ws = torch.empty(mate.lingen_ma_bwd_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    y = torch.empty((s.batch, s.L, s.d_inner), dtype=d["x"].dtype, device="cuda")
+    fws = torch.empty(max(mate.lingen_mate_workspace_bytes(s), 16), dtype=torch.uint8, device="cuda")
+    args_f = [d[n] for n in ("x", "dt", "A", "B", "C", "D")]
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    bwd_ms = timed(lambda i: mate.lingen_ma_bwd(*args_f, dy, i % 4, s, grads=grads, workspace=ws))
+    fwd_ms = timed(lambda i: mate.lingen_ma_fwd(*args_f, i % 4, s, out=y, workspace=fws))
+    e = s.elem_bytes
+    rows = s.batch * s.L
+    G, N, Hs, P = s.ngroups, s.d_state, s.ssd_heads, s.headdim
+    # inputs read once (x, dy, B, C, dt), gradients written once (dx, ddt, dB, dC in fp32)
+    nbytes = rows * (2 * Hs * P * e + 2 * G * N * e + Hs * 4) + rows * (Hs * P * 4 + Hs * 4 + 2 * G * N * 4)
+    out = {"kernel": "ma_bwd", "workload": CONFIG_NOTES[args.config], "steps": args.steps,
+           "bwd_ms": round(bwd_ms, 4), "fwd_ms": round(fwd_ms, 4), "bwd_over_fwd": round(bwd_ms / fwd_ms, 2),
+           "compulsory_bytes": nbytes, "compulsory_GB/s": round(nbytes / bwd_ms / 1e6, 1),
+           "workspace_GiB": round(ws.numel() / 2 ** 30, 2)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def dense_compare(args, mate, torch):
     """The quadratic mixer MATE replaces, at the workload's L, heads and head
     size: dense softmax attention over all tokens (lingen_dense_attn_fwd)
@@ -556,6 +599,8 @@ def main(argv=None):
     ap.add_argument("--mate-block", action="store_true",
                     help="instead of the benchmark line, time the whole MATE block (projections around the "
                          "mixer) and the library's own steps inside it")
+    ap.add_argument("--ma-bwd", action="store_true",
+                    help="instead of the benchmark line, time the MA branch's backward pass against its forward")
     ap.add_argument("--dense", action="store_true",
                     help="instead of the benchmark line, time dense softmax attention over all tokens (the "
                          "quadratic mixer MATE replaces) against the MATE forward on the workload")
@@ -591,6 +636,8 @@ def main(argv=None):
         return block_steps(args, mate, torch)
     if args.mate_block:
         return mate_block(args, mate, torch)
+    if args.ma_bwd:
+        return ma_backward(args, mate, torch)
     s = CONFIGS[args.config]
     workload = CONFIG_NOTES[args.config]
     print(f"[bench] generating inputs: {workload}, {s.L} tokens", file=sys.stderr, flush=True)

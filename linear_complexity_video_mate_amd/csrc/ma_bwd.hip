@@ -55,13 +55,6 @@ __device__ __forceinline__ void store8(__bf16* p, const float (&v)[8]) {
   *reinterpret_cast<bf16x8*>(p) = u;
 }
 
-// Zero n16 16-byte units (a kernel, not a memset, so that the sequence can
-// be captured in a graph).
-__global__ __launch_bounds__(kThreads) void zero16_kernel(uint4* __restrict__ p, int64_t n16) {
-  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (i < n16) p[i] = make_uint4(0u, 0u, 0u, 0u);
-}
-
 // Zero three arrays of n floats each (the accumulated gradients dA, dD and a
 // zero D for the auxiliary scans).
 __global__ __launch_bounds__(kThreads) void zero_floats_kernel(float* __restrict__ a, float* __restrict__ b,
@@ -191,8 +184,6 @@ __device__ __forceinline__ float block_sum512(float v, float* red) {
   return t;
 }
 
-__device__ __forceinline__ float bf(const bf16x8& u, int e) { return static_cast<float>(u[e]); }
-
 // The crossing sums R_r of both directions for one (chunk, head, batch
 // element), head size 64, written to R [batch, L, Hs] fp32.  With cs the
 // chunk-local inclusive cumulative sum of dt*A along the scan order and csx
@@ -212,28 +203,29 @@ __device__ __forceinline__ float bf(const bf16x8& u, int e) { return static_cast
 //   K = exp(cs_last) (<hf1, hb2> + <hb1, hf2>)
 // R_r = suffix_{t >= r}(d_f + U_f + V_b) + prefix_{t <= r}(d_b + U_b + V_f)
 //       - V_f(r) - V_b(r) + K.
-// Every product is formed in fp32 from the bf16 inputs and the fp32 states,
-// chunk by chunk, so no sum runs across the sequence.  512 threads; thread
-// (tid / 16, tid % 16) owns a (Q/32) x (Q/16) tile of the Q x Q products and
-// a (Q/32) x (N/16) tile of the Q x N ones.
+// The products C B^T, dy x^T (Q x Q) and dy M, x M (Q x N, M a state as
+// bf16) run on 16x16x32 bf16 MFMA tiles from padded LDS rows, accumulated in
+// fp32; everything after them is fp32, chunk by chunk, so no sum runs across
+// the sequence.  512 threads (8 waves).
 template <int Q, int N>
 __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ dy, const float* __restrict__ dt,
     const float* __restrict__ A, const __bf16* __restrict__ B, const __bf16* __restrict__ C,
     const float* __restrict__ hf1, const float* __restrict__ hb1, const float* __restrict__ hf2,
     const float* __restrict__ hb2, ScanOrder so, int L, int Hs, int G, float* __restrict__ R) {
-  constexpr int P = 64, NT = kCrossThreads;
-  constexpr int LDB = N + 8, LDX = P + 8;     // padded bf16 row strides
-  constexpr int TR = Q / 32, TC = Q / 16, TCN = N / 16;
-  static_assert(Q % 32 == 0 && Q <= NT && N % 16 == 0, "tiles");
+  constexpr int P = 64, NT = kCrossThreads, NW = NT / 64;
+  constexpr int LDB = N + 8, LDX = P + 8;     // padded bf16 row strides (conflict-free 16-byte fragment reads)
+  constexpr int QT = Q / 16, NTL = N / 16;    // 16-row tiles
+  static_assert(Q % 32 == 0 && Q <= NT && N % 32 == 0, "tiles");
   __shared__ __attribute__((aligned(16))) __bf16 sB[Q * LDB], sC[Q * LDB], sX[Q * LDX], sDY[Q * LDX];
-  __shared__ __attribute__((aligned(16))) float sM[P * N];
-  __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], red[NT / 64];
+  __shared__ __attribute__((aligned(16))) __bf16 sMT[N * LDX];   // a state, transposed: row n holds M[0..P)[n]
+  __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], red[NW];
   __shared__ int s_tok[Q];
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int nc = L / Q;
-  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;   // fragment row / lane group
   const int g = h / (Hs / G);
   const float a_h = A[h];
   const int64_t bl = int64_t(b) * L;
@@ -273,78 +265,62 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   __syncthreads();
   const float cs_last = s_cs[Q - 1];
 
-  // pairs inside the chunk
-  {
-    float cb[TR][TC], dx[TR][TC];
+  // pairs inside the chunk: one 16x16 tile of C B^T and dy x^T per step
+  for (int tile = wave; tile < QT * QT; tile += NW) {
+    const int t0 = (tile / QT) * 16, s0 = (tile % QT) * 16;
+    f32x4 cb = {0.f, 0.f, 0.f, 0.f}, dx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < TR; ++i)
-#pragma unroll
-      for (int j = 0; j < TC; ++j) { cb[i][j] = 0.f; dx[i][j] = 0.f; }
-    const int t0 = ty * TR, s0 = tx * TC;
-#pragma unroll 2
-    for (int k = 0; k < N; k += 8) {
-      bf16x8 ct[TR], bs[TC];
-#pragma unroll
-      for (int i = 0; i < TR; ++i) ct[i] = *reinterpret_cast<const bf16x8*>(sC + (t0 + i) * LDB + k);
-#pragma unroll
-      for (int j = 0; j < TC; ++j) bs[j] = *reinterpret_cast<const bf16x8*>(sB + (s0 + j) * LDB + k);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int i = 0; i < TR; ++i) {
-          const float cv = bf(ct[i], e);
-#pragma unroll
-          for (int j = 0; j < TC; ++j) cb[i][j] = fmaf(cv, bf(bs[j], e), cb[i][j]);
-        }
+    for (int k = 0; k < N; k += 32) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sC + (t0 + lr) * LDB + k + 8 * lg);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(sB + (s0 + lr) * LDB + k + 8 * lg);
+      cb = mma(a, v, cb);
     }
-#pragma unroll 2
-    for (int k = 0; k < P; k += 8) {
-      bf16x8 yt[TR], xs[TC];
 #pragma unroll
-      for (int i = 0; i < TR; ++i) yt[i] = *reinterpret_cast<const bf16x8*>(sDY + (t0 + i) * LDX + k);
-#pragma unroll
-      for (int j = 0; j < TC; ++j) xs[j] = *reinterpret_cast<const bf16x8*>(sX + (s0 + j) * LDX + k);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int i = 0; i < TR; ++i) {
-          const float yv = bf(yt[i], e);
-#pragma unroll
-          for (int j = 0; j < TC; ++j) dx[i][j] = fmaf(yv, bf(xs[j], e), dx[i][j]);
-        }
+    for (int k = 0; k < P; k += 32) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sDY + (t0 + lr) * LDX + k + 8 * lg);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(sX + (s0 + lr) * LDX + k + 8 * lg);
+      dx = mma(a, v, dx);
     }
-    float rf[TR], rbk[TR], cf[TC], cbk[TC];
+    // lane holds rows t0 + 4 lg + r, column s0 + lr
+    const int s2 = s0 + lr;
+    const float ds = s_dt[s2], cs_s = s_cs[s2], csx_s = s_csx[s2];
+    float rf[4], rb[4], cf = 0.f, cbk = 0.f;
 #pragma unroll
-    for (int i = 0; i < TR; ++i) { rf[i] = 0.f; rbk[i] = 0.f; }
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 4 * lg + r;
+      const float v = ds * cb[r] * dx[r];
+      float wf = 0.f, wb = 0.f;
+      if (s2 < t) wf = __expf(s_cs[t] - cs_s) * v;
+      else if (s2 > t) wb = __expf(csx_s - s_csx[t]) * v;
+      rf[r] = wf;
+      rb[r] = wb;
+      cf += wf;
+      cbk += wb;
+    }
 #pragma unroll
-    for (int j = 0; j < TC; ++j) { cf[j] = 0.f; cbk[j] = 0.f; }
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int i = 0; i < TR; ++i) {
-      const int t = t0 + i;
-#pragma unroll
-      for (int j = 0; j < TC; ++j) {
-        const int s2 = s0 + j;
-        const float v = s_dt[s2] * cb[i][j] * dx[i][j];
-        if (s2 < t) {
-          const float w = __expf(s_cs[t] - s_cs[s2]) * v;
-          rf[i] += w;
-          cf[j] += w;
-        } else if (s2 > t) {
-          const float w = __expf(s_csx[s2] - s_csx[t]) * v;
-          rbk[i] += w;
-          cbk[j] += w;
-        }
+      for (int m = 8; m > 0; m >>= 1) {
+        rf[r] += __shfl_xor(rf[r], m, 16);
+        rb[r] += __shfl_xor(rb[r], m, 16);
       }
-    }
 #pragma unroll
-    for (int i = 0; i < TR; ++i) {
-      atomicAdd(s_fw + t0 + i, rf[i]);
-      atomicAdd(s_bw + t0 + i, rbk[i]);
+    for (int m = 16; m < 64; m <<= 1) {
+      cf += __shfl_xor(cf, m, 64);
+      cbk += __shfl_xor(cbk, m, 64);
     }
+    if (lr < 4) {   // lane lr of each group adds row t0 + 4 lg + lr
+      const int t = t0 + 4 * lg + lr;
+      float f = rf[0], bk = rb[0];
 #pragma unroll
-    for (int j = 0; j < TC; ++j) {
-      atomicAdd(s_fw + s0 + j, -cf[j]);
-      atomicAdd(s_bw + s0 + j, -cbk[j]);
+      for (int r = 1; r < 4; ++r)
+        if (lr == r) { f = rf[r]; bk = rb[r]; }
+      atomicAdd(s_fw + t, f);
+      atomicAdd(s_bw + t, bk);
+    }
+    if (lg == 0) {
+      atomicAdd(s_fw + s2, -cf);
+      atomicAdd(s_bw + s2, -cbk);
     }
   }
 
@@ -353,46 +329,46 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   const float* mats[4] = {hf1 + st_off, hb2 + st_off, hb1 + st_off, hf2 + st_off};
 #pragma unroll 1
   for (int term = 0; term < 4; ++term) {
-    __syncthreads();   // sM is free, and the pair sums above have landed
-    for (int i = tid; i < P * N / 4; i += NT)
-      reinterpret_cast<float4*>(sM)[i] = reinterpret_cast<const float4*>(mats[term])[i];
+    __syncthreads();   // sMT is free, and the pair sums above have landed
+    for (int i = tid; i < P * N / 4; i += NT) {
+      const float4 m4 = reinterpret_cast<const float4*>(mats[term])[i];
+      const int p = (i * 4) / N, n = (i * 4) % N;
+      sMT[(n + 0) * LDX + p] = static_cast<__bf16>(m4.x);
+      sMT[(n + 1) * LDX + p] = static_cast<__bf16>(m4.y);
+      sMT[(n + 2) * LDX + p] = static_cast<__bf16>(m4.z);
+      sMT[(n + 3) * LDX + p] = static_cast<__bf16>(m4.w);
+    }
     __syncthreads();
     const bool is_u = (term == 0 || term == 2);          // U terms: dy and C; V terms: x and B
     const __bf16* sa = is_u ? sDY : sX;
     const __bf16* sv = is_u ? sC : sB;
-    const int t0 = ty * TR, n0 = tx * TCN;
-    float acc[TR][TCN];
+    for (int tb = wave; tb < QT; tb += NW) {
+      const int t0 = tb * 16;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      bf16x8 af[P / 32];
 #pragma unroll
-    for (int i = 0; i < TR; ++i)
+      for (int kk = 0; kk < P / 32; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(sa + (t0 + lr) * LDX + 32 * kk + 8 * lg);
+      for (int nt = 0; nt < NTL; ++nt) {
+        const int n0 = nt * 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < TCN; ++j) acc[i][j] = 0.f;
-#pragma unroll 2
-    for (int p = 0; p < P; p += 8) {
-      bf16x8 av[TR];
-#pragma unroll
-      for (int i = 0; i < TR; ++i) av[i] = *reinterpret_cast<const bf16x8*>(sa + (t0 + i) * LDX + p);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float mv[TCN];
-#pragma unroll
-        for (int j = 0; j < TCN; ++j) mv[j] = sM[(p + e) * N + n0 + j];
-#pragma unroll
-        for (int i = 0; i < TR; ++i) {
-          const float a = bf(av[i], e);
-#pragma unroll
-          for (int j = 0; j < TCN; ++j) acc[i][j] = fmaf(a, mv[j], acc[i][j]);
+        for (int kk = 0; kk < P / 32; ++kk) {
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(sMT + (n0 + lr) * LDX + 32 * kk + 8 * lg);
+          acc = mma(af[kk], v, acc);
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[r] = fmaf(acc[r], static_cast<float>(sv[(t0 + 4 * lg + r) * LDB + n0 + lr]), part[r]);
       }
-    }
 #pragma unroll
-    for (int i = 0; i < TR; ++i) {
-      const int t = t0 + i;
-      float sum = 0.f;
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int j = 0; j < TCN; ++j) sum = fmaf(acc[i][j], static_cast<float>(sv[t * LDB + n0 + j]), sum);
+        for (int m = 8; m > 0; m >>= 1) part[r] += __shfl_xor(part[r], m, 16);
+      if (lr < 4) {
+        const int t = t0 + 4 * lg + lr;
+        float sum = part[0];
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
-      if (tx == 0) {
+        for (int r = 1; r < 4; ++r)
+          if (lr == r) sum = part[r];
         if (term == 0) {
           s_fw[t] += __expf(s_cs[t]) * sum;                          // U_f
         } else if (term == 1) {
@@ -436,62 +412,72 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   if (tid < Q) R[(bl + s_tok[tid]) * Hs + h] = s_fw[tid] + s_bw[tid] - s_sub[tid] + k;
 }
 
-// Per (chunk, head, batch element), one thread per scan position of the
-// chunk (Q <= 128), head size 64: dx = dt (yhat_f + yhat_b) + 2 D dy, ddt =
-// x . (yhat_f + yhat_b) + A R, and this chunk's share of dA = sum dt R and
-// dD = 2 sum dy . x.  yhat_f, yhat_b: the transposed outputs M_f^T dy / dt,
-// M_b^T dy / dt; R: the crossing sums.
-__global__ __launch_bounds__(128) void ma_bwd_chunk_kernel(
+// Per (chunk, head, batch element), head size 64: dx = dt yhat + 2 D dy,
+// ddt = x . yhat + A R, and this chunk's share of dA = sum dt R and dD =
+// 2 sum dy . x, with yhat = (M_f^T + M_b^T) dy / dt and R the crossing sums.
+// Eight lanes share a token's 128-byte rows (16 bytes each), so every load
+// and store of a wave covers eight whole rows; 256 threads take 32 scan
+// positions per pass.
+__global__ __launch_bounds__(256) void ma_bwd_chunk_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ dy, const float* __restrict__ dt,
-    const float* __restrict__ A, const float* __restrict__ D, const __bf16* __restrict__ yh_f,
-    const __bf16* __restrict__ yh_b, const float* __restrict__ R, ScanOrder so, int L, int Q, int Hs,
-    float* __restrict__ dx, float* __restrict__ ddt, float* __restrict__ dA, float* __restrict__ dD) {
+    const float* __restrict__ A, const float* __restrict__ D, const __bf16* __restrict__ yh,
+    const float* __restrict__ R, ScanOrder so, int L, int Q, int Hs, float* __restrict__ dx,
+    float* __restrict__ ddt, float* __restrict__ dA, float* __restrict__ dD) {
   constexpr int P = 64;
+  __shared__ float red[8][2];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int i = threadIdx.x;
+  const int sub = threadIdx.x & 7, slot = threadIdx.x >> 3;
+  const float two_d = 2.f * D[h], a_h = A[h];
   float da = 0.f, dd = 0.f;
-  if (i < Q) {
-    const int64_t t = int64_t(b) * L + so.canon(c * Q + i);
-    const int64_t rh = t * Hs + h;
-    const float d = dt[rh], r = R[rh];
-    const int64_t off = rh * P;
+  for (int i = slot; i < Q; i += 32) {
+    const int64_t rh = (int64_t(b) * L + so.canon(c * Q + i)) * Hs + h;
+    const float d = dt[rh];
+    const int64_t off = rh * P + sub * 8;
+    float vx[8], vdy[8], vh[8], gx[8];
+    load8(x + off, vx);
+    load8(dy + off, vdy);
+    load8(yh + off, vh);
     float xyh = 0.f, dyx = 0.f;
-    const float two_d = 2.f * D[h];
-    for (int u = 0; u < P; u += 8) {
-      float vx[8], vdy[8], vhf[8], vhb[8], gx[8];
-      load8(x + off + u, vx);
-      load8(dy + off + u, vdy);
-      load8(yh_f + off + u, vhf);
-      load8(yh_b + off + u, vhb);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float s2 = vhf[e] + vhb[e];
-        xyh = fmaf(vx[e], s2, xyh);
-        dyx = fmaf(vdy[e], vx[e], dyx);
-        gx[e] = fmaf(d, s2, two_d * vdy[e]);
-      }
-      float4* o = reinterpret_cast<float4*>(dx + off + u);
-      o[0] = make_float4(gx[0], gx[1], gx[2], gx[3]);
-      o[1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
+    for (int e = 0; e < 8; ++e) {
+      xyh = fmaf(vx[e], vh[e], xyh);
+      dyx = fmaf(vdy[e], vx[e], dyx);
+      gx[e] = fmaf(d, vh[e], two_d * vdy[e]);
     }
-    ddt[rh] = xyh + A[h] * r;
-    da = d * r;
-    dd = 2.f * dyx;
+    float4* o = reinterpret_cast<float4*>(dx + off);
+    o[0] = make_float4(gx[0], gx[1], gx[2], gx[3]);
+    o[1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
+#pragma unroll
+    for (int m = 4; m > 0; m >>= 1) {
+      xyh += __shfl_xor(xyh, m, 8);
+      dyx += __shfl_xor(dyx, m, 8);
+    }
+    if (sub == 0) {
+      const float r = R[rh];
+      ddt[rh] = xyh + a_h * r;
+      da += d * r;
+      dd += 2.f * dyx;
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     da += __shfl_xor(da, off, 64);
     dd += __shfl_xor(dd, off, 64);
   }
-  if ((i & 63) == 0) {
-    atomicAdd(dA + h, da);
-    atomicAdd(dD + h, dd);
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6][0] = da;
+    red[threadIdx.x >> 6][1] = dd;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicAdd(dA + h, red[0][0] + red[1][0] + red[2][0] + red[3][0]);
+    atomicAdd(dD + h, red[0][1] + red[1][1] + red[2][1] + red[3][1]);
   }
 }
 
 // Byte offsets inside the caller's workspace.
 struct BwdWs {
-  size_t hf1, hb1, hf2, hb2, scan, xprime, zero, dzero, dt_next, dt_prev, dy_next, dy_prev, R, yh_f, yh_b,
+  size_t hf1, hb1, hf2, hb2, scan, xprime, dzero, dt_next, dt_prev, dy_next, dy_prev, R, yh,
       val_a, val_b, out, total;
 };
 
@@ -528,15 +514,13 @@ int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   w->hb2 = take(states);
   w->scan = take(ws_main > ws_aux ? ws_main : ws_aux);
   w->xprime = take(rows * hs * P * 2);
-  w->zero = take(rows * hs * P * 2);
   w->dzero = take(hs * 4);
   w->dt_next = take(rows * hs * 4);
   w->dt_prev = take(rows * hs * 4);
   w->dy_next = take(rows * hs * P * 2);
   w->dy_prev = take(rows * hs * P * 2);
   w->R = take(rows * hs * 4);
-  w->yh_f = take(rows * hs * P * 2);
-  w->yh_b = take(rows * hs * P * 2);
+  w->yh = take(rows * hs * P * 2);
   w->val_a = take(rows * hs * kHalf * 2);
   w->val_b = take(rows * hs * kHalf * 2);
   w->out = take(rows * hs * kHalf * 2);
@@ -556,12 +540,6 @@ int check_bwd_shape(const lingen_mate_shape* s) {
   return validate_shape(&a);
 }
 
-int zero_fill(void* p, size_t bytes, hipStream_t st) {
-  const int64_t n16 = int64_t(bytes / 16);
-  if (n16 == 0) return LINGEN_OK;
-  zero16_kernel<<<blocks_for(n16), kThreads, 0, st>>>(static_cast<uint4*>(p), n16);
-  return hipGetLastError() == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
-}
 
 }  // namespace
 }  // namespace lingen
@@ -611,11 +589,10 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
     if (hipGetLastError() != hipSuccess) return LINGEN_ERR_HIP;       \
   } while (0)
 
-  LINGEN_TRY(zero_fill(at(w.zero), rows * Hs * P * 2, stream));
-  zero_floats_kernel<<<1, kThreads, 0, stream>>>(atf(w.dzero), dA, dD, Hs);   // D = 0 for the auxiliary scans; dA, dD
+  // a zero D for the auxiliary scans; dA and dD accumulate from zero
+  zero_floats_kernel<<<1, kThreads, 0, stream>>>(atf(w.dzero), dA, dD, Hs);
   LINGEN_LAUNCHED();
   const float* dz = atf(w.dzero);
-  const void* zx = at(w.zero);
 
   // forward states of (x, B) and adjoint states of (x', C)
   LINGEN_TRY(lingen_ssd_chunk_states(x, dt, A, B, mode, shape, atf(w.hf1), atf(w.hb1), at(w.scan), scan_bytes,
@@ -637,10 +614,10 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   }
   const float* dtn = atf(w.dt_next);
   const float* dtp = atf(w.dt_prev);
-  LINGEN_TRY(lingen_ma_fwd_dirs(at(w.dy_prev), dtp, A, C, B, dz, zx, dtp, A, C, B, dz, mode, shape, at(w.yh_b),
-                                at(w.scan), scan_bytes, stream));
-  LINGEN_TRY(lingen_ma_fwd_dirs(zx, dtn, A, C, B, dz, at(w.dy_next), dtn, A, C, B, dz, mode, shape, at(w.yh_f),
-                                at(w.scan), scan_bytes, stream));
+  // (M_b^T + M_f^T) dy / dt in one per-direction call: the forward scan with dt_prev and the reverse scan
+  // with dt_next
+  LINGEN_TRY(lingen_ma_fwd_dirs(at(w.dy_prev), dtp, A, C, B, dz, at(w.dy_next), dtn, A, C, B, dz, mode, shape,
+                                at(w.yh), at(w.scan), scan_bytes, stream));
 
   // dC and dB, 64 value columns at a time, keys and queries per head
   for (int col0 = 0; col0 < N; col0 += kHalf) {
@@ -679,9 +656,8 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
     else
       return LINGEN_ERR_UNSUPPORTED;
     LINGEN_LAUNCHED();
-    ma_bwd_chunk_kernel<<<grid, 128, 0, stream>>>(xb, dyb, dt, A, D, static_cast<const __bf16*>(at(w.yh_f)),
-                                                 static_cast<const __bf16*>(at(w.yh_b)), atf(w.R), so, L, Q, Hs,
-                                                 dx, ddt, dA, dD);
+    ma_bwd_chunk_kernel<<<grid, 256, 0, stream>>>(xb, dyb, dt, A, D, static_cast<const __bf16*>(at(w.yh)), atf(w.R),
+                                                 so, L, Q, Hs, dx, ddt, dA, dD);
     LINGEN_LAUNCHED();
   }
 #undef LINGEN_TRY

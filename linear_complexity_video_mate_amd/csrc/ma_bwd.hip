@@ -11,10 +11,10 @@
 //   * M^T of one direction is the opposite direction's scan with dt moved
 //     by one scan position (so the decays cover the right tokens), the input
 //     divided by that moved dt and B, C exchanged: dx = dt (M_f^T + M_b^T) dy
-//     / dt + 2 D dy, and dB likewise with C as the values and dy, x as keys
-//     and queries (one group per head);
-//   * dC is the forward bidirectional scan with B as the values, x as the
-//     keys and dy as the queries (one group per head);
+//     / dt + 2 D dy;
+//   * dB and dC are, per chunk, products of the same chunk-local matrices the
+//     crossing sums need (E = dt (dy x^T) weighted by the decays) with C and
+//     B, plus products of the chunk-boundary states with x and dy;
 //   * the chunk-boundary adjoint states are chunk states of the scan of
 //     x' = dy exp(dt A) / dt with C in place of B;
 //   * ddt and dA need, at every position r, the crossing sum
@@ -39,7 +39,6 @@ namespace lingen {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kHalf = 64;   // value columns per auxiliary scan (its compiled head size)
 
 unsigned blocks_for(int64_t n) { return unsigned((n + kThreads - 1) / kThreads); }
 
@@ -56,7 +55,7 @@ __device__ __forceinline__ void store8(__bf16* p, const float (&v)[8]) {
 }
 
 // Zero three arrays of n floats each (the accumulated gradients dA, dD and a
-// zero D for the auxiliary scans).
+// zero D for the transposed scans).
 __global__ __launch_bounds__(kThreads) void zero_floats_kernel(float* __restrict__ a, float* __restrict__ b,
                                                                float* __restrict__ c, int n) {
   for (int i = threadIdx.x; i < n; i += kThreads) {
@@ -123,52 +122,6 @@ __global__ __launch_bounds__(kThreads) void shifted_dt_kernel(const __bf16* __re
   store8(dy_prev + off, b);
 }
 
-// Per-head values from columns [col0, col0 + 64) of a grouped tensor
-// src [rows, G, N]: out[row, h, j] = src[row, g(h), col0 + j] (/ scale[row, h]).
-__global__ __launch_bounds__(kThreads) void head_values_kernel(const __bf16* __restrict__ src, int G, int N,
-                                                               int col0, const float* __restrict__ scale, int Hs,
-                                                               int64_t rows, __bf16* __restrict__ out) {
-  constexpr int upr = kHalf / 8;
-  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= rows * Hs * upr) return;
-  const int unit = int(i % upr);
-  const int64_t rh = i / upr;
-  const int h = int(rh % Hs);
-  const int64_t row = rh / Hs;
-  const int g = h / (Hs / G);
-  float v[8];
-  load8(src + (row * G + g) * N + col0 + unit * 8, v);
-  if (scale != nullptr) {
-    const float r = 1.f / scale[rh];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= r;
-  }
-  store8(out + i * 8, v);
-}
-
-// dst[row, g, col0 + j] = sum over the heads h of group g of w[row, h] *
-// src[row, h, j] (w = 1 when NULL), fp32.  One thread per (row, group, 4 j).
-__global__ __launch_bounds__(kThreads) void group_sum_kernel(const __bf16* __restrict__ src,
-                                                             const float* __restrict__ w, int Hs, int G, int N,
-                                                             int col0, int64_t rows, float* __restrict__ dst) {
-  constexpr int upr = kHalf / 4;
-  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= rows * G * upr) return;
-  const int unit = int(i % upr);
-  const int g = int((i / upr) % G);
-  const int64_t row = i / (int64_t(upr) * G);
-  const int hpg = Hs / G;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int hh = 0; hh < hpg; ++hh) {
-    const int h = g * hpg + hh;
-    const float s = w != nullptr ? w[row * Hs + h] : 1.f;
-    const bf16x4 u = *reinterpret_cast<const bf16x4*>(src + (row * Hs + h) * kHalf + unit * 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = fmaf(s, static_cast<float>(u[e]), acc[e]);
-  }
-  *reinterpret_cast<float4*>(dst + (row * G + g) * N + col0 + unit * 4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-}
-
 constexpr int kCrossThreads = 512;
 
 // Block-wide sum over the 512 threads of a workgroup.
@@ -184,60 +137,79 @@ __device__ __forceinline__ float block_sum512(float v, float* red) {
   return t;
 }
 
-// The crossing sums R_r of both directions for one (chunk, head, batch
-// element), head size 64, written to R [batch, L, Hs] fp32.  With cs the
-// chunk-local inclusive cumulative sum of dt*A along the scan order and csx
-// its exclusive form, V_ts = dt_s (C_t . B_s)(dy_t . x_s):
-//   forward pairs s < t:  W_ts = exp(cs_t - cs_s) V_ts,   crossing s < r <= t
-//   backward pairs s > t: W_ts = exp(csx_s - csx_t) V_ts, crossing t <= r < s
-// R_r = (pairs inside the chunk: suffix / prefix sums of row minus column
-// sums of W) + (pairs with one end outside: the boundary terms below, from
-// the chunk states) + (pairs with both ends outside: a constant).  Boundary
-// terms, with hf1 = forward state entering the chunk, hb1 = reverse state
-// entering it from the right, hf2 / hb2 = the adjoint states of the reverse /
-// forward scan (chunk states of x' = dy exp(dt A) / dt against C):
-//   U_f(t) = exp(cs_t) dy_t . (hf1 C_t)               (s before the chunk)
-//   V_f(s) = dt_s exp(cs_last - cs_s) x_s . (hb2 B_s) (t after the chunk)
-//   U_b(t) = exp(cs_last - csx_t) dy_t . (hb1 C_t)    (s after the chunk)
-//   V_b(s) = dt_s exp(csx_s) x_s . (hf2 B_s)          (t before the chunk)
+// Two 4-element transposing LDS reads (rows k and k + 16 of a row-major
+// bf16 tile, 16 columns from `col`), giving lane group g the contraction
+// indices {4g..4g+3, 16+4g..16+4g+3} of a 32-block for column (lane & 15):
+// the operand order of the 16x16x32 MFMA with its k axis permuted.
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16* tile, int ld, int k0, int col0, int lane) {
+  const int r16 = lane & 15, grp = lane >> 4;
+  lds_bf16* p = (lds_bf16*)(tile + (k0 + 4 * grp + (r16 >> 2)) * ld + col0 + 4 * (r16 & 3));
+  const bf16x4 lo = lds_read_tr(p);
+  const bf16x4 hi = lds_read_tr(p + 16 * ld);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// The matching operand from a k-contiguous row: k = {4g..4g+3, 16+4g..16+4g+3}.
+__device__ __forceinline__ bf16x8 perm_frag(const __bf16* row, int k0, int lane) {
+  const int grp = lane >> 4;
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + k0 + 4 * grp);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + k0 + 16 + 4 * grp);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Per (chunk, group, batch element), looping over the group's heads (head
+// size 64): the crossing sums R_r behind ddt and dA, written to R [batch, L,
+// Hs], and the gradients dB, dC of the chunk's tokens, written to [batch, L,
+// G, N] fp32.  With cs the chunk-local inclusive cumulative sum of dt*A
+// along the scan order and csx its exclusive form:
+//   forward pairs s <= t:  decay exp(cs_t - cs_s),   backward pairs s >= t:
+//   decay exp(csx_s - csx_t); E_ts = dt_s (dy_t . x_s) (sum of the decays that
+//   apply); W_ts = E_ts (C_t . B_s) split by direction (s = t excluded).
+// Crossing sums (forward: s < r <= t; backward: t <= r < s):
+//   R_r = suffix_{t >= r}(d_f + U_f + V_b) + prefix_{t <= r}(d_b + U_b + V_f)
+//         - V_f(r) - V_b(r) + K,
+// d_f, d_b the row minus column sums of W per direction, and the pairs with
+// an end outside the chunk from the four chunk-boundary states (hf1: forward
+// state entering the chunk; hb1: reverse state entering it from the right;
+// hf2, hb2: adjoint states of the reverse / forward scan):
+//   U_f(t) = exp(cs_t) dy_t . (hf1 C_t)      V_f(s) = dt_s exp(cs_last - cs_s) x_s . (hb2 B_s)
+//   U_b(t) = exp(cs_last - csx_t) dy_t . (hb1 C_t)   V_b(s) = dt_s exp(csx_s) x_s . (hf2 B_s)
 //   K = exp(cs_last) (<hf1, hb2> + <hb1, hf2>)
-// R_r = suffix_{t >= r}(d_f + U_f + V_b) + prefix_{t <= r}(d_b + U_b + V_f)
-//       - V_f(r) - V_b(r) + K.
-// The products C B^T, dy x^T (Q x Q) and dy M, x M (Q x N, M a state as
-// bf16) run on 16x16x32 bf16 MFMA tiles from padded LDS rows, accumulated in
-// fp32; everything after them is fp32, chunk by chunk, so no sum runs across
-// the sequence.  512 threads (8 waves).
+// and, summed over the heads of the group,
+//   dC_t = sum_s E_ts B_s + exp(cs_t) hf1^T dy_t + exp(cs_last - csx_t) hb1^T dy_t
+//   dB_s = sum_t E_ts C_t + dt_s exp(cs_last - cs_s) hb2^T x_s + dt_s exp(csx_s) hf2^T x_s.
+// Products on 16x16x32 bf16 MFMA tiles from padded LDS rows (C B^T, dy x^T,
+// E B, E^T C and the state products, per head), fp32 everywhere after them;
+// no sum runs across the sequence.  512
+// threads (8 waves); wave w owns row block w of every Q x N result.
 template <int Q, int N>
 __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ dy, const float* __restrict__ dt,
     const float* __restrict__ A, const __bf16* __restrict__ B, const __bf16* __restrict__ C,
     const float* __restrict__ hf1, const float* __restrict__ hb1, const float* __restrict__ hf2,
-    const float* __restrict__ hb2, ScanOrder so, int L, int Hs, int G, float* __restrict__ R) {
+    const float* __restrict__ hb2, ScanOrder so, int L, int Hs, int G, float* __restrict__ R,
+    float* __restrict__ dB, float* __restrict__ dC) {
   constexpr int P = 64, NT = kCrossThreads, NW = NT / 64;
-  constexpr int LDB = N + 8, LDX = P + 8;     // padded bf16 row strides (conflict-free 16-byte fragment reads)
-  constexpr int QT = Q / 16, NTL = N / 16;    // 16-row tiles
-  static_assert(Q % 32 == 0 && Q <= NT && N % 32 == 0, "tiles");
+  constexpr int LDB = N + 8, LDX = P + 8, LDE = Q + 8;   // padded bf16 row strides
+  constexpr int QT = Q / 16, NTL = N / 16;
+  constexpr int CBT = (QT * QT + NW - 1) / NW;           // Q x Q tiles per wave
+  constexpr int MT_ELEMS = N * LDX, E_ELEMS = Q * LDE;
+  constexpr int U_ELEMS = MT_ELEMS > E_ELEMS ? MT_ELEMS : E_ELEMS;
+  constexpr int SPT = P * N / NT;                        // state elements per thread
+  static_assert(Q % 32 == 0 && Q <= NT && N % 32 == 0 && QT <= NW && (P * N) % (4 * NT) == 0, "tiles");
   __shared__ __attribute__((aligned(16))) __bf16 sB[Q * LDB], sC[Q * LDB], sX[Q * LDX], sDY[Q * LDX];
-  __shared__ __attribute__((aligned(16))) __bf16 sMT[N * LDX];   // a state, transposed: row n holds M[0..P)[n]
+  __shared__ __attribute__((aligned(16))) __bf16 sU[U_ELEMS];   // E (Q x Q), then a state transposed (N x P)
   __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], red[NW];
   __shared__ int s_tok[Q];
+  __bf16* const sE = sU;
+  __bf16* const sMT = sU;
 
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int nc = L / Q;
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int nc = L / Q, hpg = Hs / G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;   // fragment row / lane group
-  const int g = h / (Hs / G);
-  const float a_h = A[h];
+  const int lr = lane & 15, lg = lane >> 4;
   const int64_t bl = int64_t(b) * L;
 
-  for (int i = tid; i < Q; i += NT) {
-    const int tok = so.canon(c * Q + i);
-    s_tok[i] = tok;
-    s_dt[i] = dt[(bl + tok) * Hs + h];
-    s_fw[i] = 0.f;
-    s_bw[i] = 0.f;
-    s_sub[i] = 0.f;
-  }
+  for (int i = tid; i < Q; i += NT) s_tok[i] = so.canon(c * Q + i);
   __syncthreads();
   for (int i = tid; i < Q * (N / 8); i += NT) {
     const int row = i / (N / 8), k8 = (i % (N / 8)) * 8;
@@ -245,109 +217,164 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     *reinterpret_cast<bf16x8*>(sB + row * LDB + k8) = *reinterpret_cast<const bf16x8*>(B + src);
     *reinterpret_cast<bf16x8*>(sC + row * LDB + k8) = *reinterpret_cast<const bf16x8*>(C + src);
   }
-  for (int i = tid; i < Q * (P / 8); i += NT) {
-    const int row = i / (P / 8), k8 = (i % (P / 8)) * 8;
-    const int64_t src = ((bl + s_tok[row]) * Hs + h) * P + k8;
-    *reinterpret_cast<bf16x8*>(sX + row * LDX + k8) = *reinterpret_cast<const bf16x8*>(x + src);
-    *reinterpret_cast<bf16x8*>(sDY + row * LDX + k8) = *reinterpret_cast<const bf16x8*>(dy + src);
-  }
-  // chunk-local cumulative sums of dt*A (inclusive in s_cs)
-  for (int i = tid; i < Q; i += NT) s_cs[i] = s_dt[i] * a_h;
   __syncthreads();
-  for (int off = 1; off < Q; off <<= 1) {
-    float v = 0.f;
-    if (tid < Q && tid >= off) v = s_cs[tid - off];
-    __syncthreads();
-    if (tid < Q) s_cs[tid] += v;
-    __syncthreads();
-  }
-  for (int i = tid; i < Q; i += NT) s_csx[i] = s_cs[i] - s_dt[i] * a_h;
-  __syncthreads();
-  const float cs_last = s_cs[Q - 1];
+  f32x4 gC[NTL], gB[NTL];   // dC, dB of row block `wave`, summed over the group's heads
+#pragma unroll
+  for (int j = 0; j < NTL; ++j) { gC[j] = f32x4{0.f, 0.f, 0.f, 0.f}; gB[j] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  const bool owns_rows = wave < QT;
+  const int r0 = wave * 16;   // the row block this wave owns in the Q x N results
 
-  // pairs inside the chunk: one 16x16 tile of C B^T and dy x^T per step
-  for (int tile = wave; tile < QT * QT; tile += NW) {
-    const int t0 = (tile / QT) * 16, s0 = (tile % QT) * 16;
-    f32x4 cb = {0.f, 0.f, 0.f, 0.f}, dx = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < N; k += 32) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sC + (t0 + lr) * LDB + k + 8 * lg);
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(sB + (s0 + lr) * LDB + k + 8 * lg);
-      cb = mma(a, v, cb);
+#pragma unroll 1
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const float a_h = A[h];
+    __syncthreads();   // the previous head is done with every shared array
+    for (int i = tid; i < Q; i += NT) {
+      s_dt[i] = dt[(bl + s_tok[i]) * Hs + h];
+      s_fw[i] = 0.f;
+      s_bw[i] = 0.f;
+      s_sub[i] = 0.f;
     }
-#pragma unroll
-    for (int k = 0; k < P; k += 32) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sDY + (t0 + lr) * LDX + k + 8 * lg);
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(sX + (s0 + lr) * LDX + k + 8 * lg);
-      dx = mma(a, v, dx);
+    for (int i = tid; i < Q * (P / 8); i += NT) {
+      const int row = i / (P / 8), k8 = (i % (P / 8)) * 8;
+      const int64_t src = ((bl + s_tok[row]) * Hs + h) * P + k8;
+      *reinterpret_cast<bf16x8*>(sX + row * LDX + k8) = *reinterpret_cast<const bf16x8*>(x + src);
+      *reinterpret_cast<bf16x8*>(sDY + row * LDX + k8) = *reinterpret_cast<const bf16x8*>(dy + src);
     }
-    // lane holds rows t0 + 4 lg + r, column s0 + lr
-    const int s2 = s0 + lr;
-    const float ds = s_dt[s2], cs_s = s_cs[s2], csx_s = s_csx[s2];
-    float rf[4], rb[4], cf = 0.f, cbk = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + 4 * lg + r;
-      const float v = ds * cb[r] * dx[r];
-      float wf = 0.f, wb = 0.f;
-      if (s2 < t) wf = __expf(s_cs[t] - cs_s) * v;
-      else if (s2 > t) wb = __expf(csx_s - s_csx[t]) * v;
-      rf[r] = wf;
-      rb[r] = wb;
-      cf += wf;
-      cbk += wb;
+    __syncthreads();
+    for (int i = tid; i < Q; i += NT) s_cs[i] = s_dt[i] * a_h;
+    __syncthreads();
+    for (int off = 1; off < Q; off <<= 1) {
+      float v = 0.f;
+      if (tid < Q && tid >= off) v = s_cs[tid - off];
+      __syncthreads();
+      if (tid < Q) s_cs[tid] += v;
+      __syncthreads();
     }
+    for (int i = tid; i < Q; i += NT) s_csx[i] = s_cs[i] - s_dt[i] * a_h;
+    __syncthreads();
+    const float cs_last = s_cs[Q - 1];
+
+    // pairs inside the chunk: dy x^T tiles -> W (crossing sums) and E (dB, dC weights)
+#pragma unroll 1
+    for (int q = 0; q < CBT; ++q) {
+      const int tile = wave + q * NW;
+      if (tile >= QT * QT) break;
+      const int t0 = (tile / QT) * 16, s0 = (tile % QT) * 16;
+      f32x4 cb = {0.f, 0.f, 0.f, 0.f}, dx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int m = 8; m > 0; m >>= 1) {
-        rf[r] += __shfl_xor(rf[r], m, 16);
-        rb[r] += __shfl_xor(rb[r], m, 16);
+      for (int k = 0; k < N; k += 32) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sC + (t0 + lr) * LDB + k + 8 * lg);
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(sB + (s0 + lr) * LDB + k + 8 * lg);
+        cb = mma(a, v, cb);
       }
 #pragma unroll
-    for (int m = 16; m < 64; m <<= 1) {
-      cf += __shfl_xor(cf, m, 64);
-      cbk += __shfl_xor(cbk, m, 64);
-    }
-    if (lr < 4) {   // lane lr of each group adds row t0 + 4 lg + lr
-      const int t = t0 + 4 * lg + lr;
-      float f = rf[0], bk = rb[0];
+      for (int k = 0; k < P; k += 32) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sDY + (t0 + lr) * LDX + k + 8 * lg);
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(sX + (s0 + lr) * LDX + k + 8 * lg);
+        dx = mma(a, v, dx);
+      }
+      const int s2 = s0 + lr;
+      const float ds = s_dt[s2], cs_s = s_cs[s2], csx_s = s_csx[s2];
+      float rf[4], rb[4], cf = 0.f, cbk = 0.f;
 #pragma unroll
-      for (int r = 1; r < 4; ++r)
-        if (lr == r) { f = rf[r]; bk = rb[r]; }
-      atomicAdd(s_fw + t, f);
-      atomicAdd(s_bw + t, bk);
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 4 * lg + r;
+        const float df = s2 <= t ? __expf(s_cs[t] - cs_s) : 0.f;
+        const float db = s2 >= t ? __expf(csx_s - s_csx[t]) : 0.f;
+        const float e = ds * dx[r];
+        sE[t * LDE + s2] = static_cast<__bf16>(e * (df + db));
+        const float v = e * cb[r];
+        const float wf = s2 < t ? df * v : 0.f;
+        const float wb = s2 > t ? db * v : 0.f;
+        rf[r] = wf;
+        rb[r] = wb;
+        cf += wf;
+        cbk += wb;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int m = 8; m > 0; m >>= 1) {
+          rf[r] += __shfl_xor(rf[r], m, 16);
+          rb[r] += __shfl_xor(rb[r], m, 16);
+        }
+#pragma unroll
+      for (int m = 16; m < 64; m <<= 1) {
+        cf += __shfl_xor(cf, m, 64);
+        cbk += __shfl_xor(cbk, m, 64);
+      }
+      if (lr < 4) {
+        float f = rf[0], bk = rb[0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r)
+          if (lr == r) { f = rf[r]; bk = rb[r]; }
+        atomicAdd(s_fw + t0 + 4 * lg + lr, f);
+        atomicAdd(s_bw + t0 + 4 * lg + lr, bk);
+      }
+      if (lg == 0) {
+        atomicAdd(s_fw + s2, -cf);
+        atomicAdd(s_bw + s2, -cbk);
+      }
     }
-    if (lg == 0) {
-      atomicAdd(s_fw + s2, -cf);
-      atomicAdd(s_bw + s2, -cbk);
-    }
-  }
-
-  // pairs with one end outside the chunk: a_t . (M b_t) for the four states
-  const int64_t st_off = ((int64_t(b) * nc + c) * Hs + h) * int64_t(P) * N;
-  const float* mats[4] = {hf1 + st_off, hb2 + st_off, hb1 + st_off, hf2 + st_off};
+    __syncthreads();   // E is complete
+    // dC += E B (rows t = row block), dB += E^T C (rows s = row block)
+    if (owns_rows) {
 #pragma unroll 1
-  for (int term = 0; term < 4; ++term) {
-    __syncthreads();   // sMT is free, and the pair sums above have landed
-    for (int i = tid; i < P * N / 4; i += NT) {
-      const float4 m4 = reinterpret_cast<const float4*>(mats[term])[i];
-      const int p = (i * 4) / N, n = (i * 4) % N;
-      sMT[(n + 0) * LDX + p] = static_cast<__bf16>(m4.x);
-      sMT[(n + 1) * LDX + p] = static_cast<__bf16>(m4.y);
-      sMT[(n + 2) * LDX + p] = static_cast<__bf16>(m4.z);
-      sMT[(n + 3) * LDX + p] = static_cast<__bf16>(m4.w);
+      for (int kb = 0; kb < Q; kb += 32) {
+        const bf16x8 ea = perm_frag(sE + (r0 + lr) * LDE, kb, lane);     // E rows r0.., k = s
+        const bf16x8 et = tr_frag(sE, LDE, kb, r0, lane);                  // E^T rows r0.., k = t
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) {
+          gC[j] = mma(ea, tr_frag(sB, LDB, kb, 16 * j, lane), gC[j]);
+          gB[j] = mma(et, tr_frag(sC, LDB, kb, 16 * j, lane), gB[j]);
+        }
+      }
     }
-    __syncthreads();
-    const bool is_u = (term == 0 || term == 2);          // U terms: dy and C; V terms: x and B
-    const __bf16* sa = is_u ? sDY : sX;
-    const __bf16* sv = is_u ? sC : sB;
-    for (int tb = wave; tb < QT; tb += NW) {
-      const int t0 = tb * 16;
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
+
+    // pairs with one end outside the chunk, and their share of dC, dB
+    const int64_t st_off = ((int64_t(b) * nc + c) * Hs + h) * int64_t(P) * N;
+    const float* mats[4] = {hf1 + st_off, hb2 + st_off, hb1 + st_off, hf2 + st_off};
+    float keep[SPT];
+    float k = 0.f;
+#pragma unroll 1
+    for (int term = 0; term < 4; ++term) {
+      __syncthreads();   // E (and the previous state) is no longer read; the pair sums have landed
+#pragma unroll
+      for (int q = 0; q < SPT / 4; ++q) {
+        const int i = tid + q * NT;
+        const float4 m4 = reinterpret_cast<const float4*>(mats[term])[i];
+        if (term == 0 || term == 2) {
+          keep[4 * q] = m4.x; keep[4 * q + 1] = m4.y; keep[4 * q + 2] = m4.z; keep[4 * q + 3] = m4.w;
+        } else {
+          k += keep[4 * q] * m4.x + keep[4 * q + 1] * m4.y + keep[4 * q + 2] * m4.z + keep[4 * q + 3] * m4.w;
+        }
+        const int pp = (i * 4) / N, n = (i * 4) % N;
+        sMT[(n + 0) * LDX + pp] = static_cast<__bf16>(m4.x);
+        sMT[(n + 1) * LDX + pp] = static_cast<__bf16>(m4.y);
+        sMT[(n + 2) * LDX + pp] = static_cast<__bf16>(m4.z);
+        sMT[(n + 3) * LDX + pp] = static_cast<__bf16>(m4.w);
+      }
+      __syncthreads();
+      if (!owns_rows) continue;
+      const bool is_u = (term == 0 || term == 2);          // U terms: dy, C, dC; V terms: x, B, dB
+      const __bf16* sa = is_u ? sDY : sX;
+      const __bf16* sv = is_u ? sC : sB;
       bf16x8 af[P / 32];
 #pragma unroll
-      for (int kk = 0; kk < P / 32; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(sa + (t0 + lr) * LDX + 32 * kk + 8 * lg);
+      for (int kk = 0; kk < P / 32; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(sa + (r0 + lr) * LDX + 32 * kk + 8 * lg);
+      // row scales of this term (rows r0 + 4 lg + r)
+      float scale[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = r0 + 4 * lg + r;
+        scale[r] = term == 0 ? __expf(s_cs[t])
+                 : term == 1 ? s_dt[t] * __expf(cs_last - s_cs[t])
+                 : term == 2 ? __expf(cs_last - s_csx[t])
+                             : s_dt[t] * __expf(s_csx[t]);
+      }
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
       for (int nt = 0; nt < NTL; ++nt) {
         const int n0 = nt * 16;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -357,59 +384,60 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
           acc = mma(af[kk], v, acc);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part[r] = fmaf(acc[r], static_cast<float>(sv[(t0 + 4 * lg + r) * LDB + n0 + lr]), part[r]);
+        for (int r = 0; r < 4; ++r) {
+          part[r] = fmaf(acc[r], static_cast<float>(sv[(r0 + 4 * lg + r) * LDB + n0 + lr]), part[r]);
+          if (is_u) gC[nt][r] = fmaf(scale[r], acc[r], gC[nt][r]);
+          else gB[nt][r] = fmaf(scale[r], acc[r], gB[nt][r]);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int m = 8; m > 0; m >>= 1) part[r] += __shfl_xor(part[r], m, 16);
       if (lr < 4) {
-        const int t = t0 + 4 * lg + lr;
-        float sum = part[0];
+        const int t = r0 + 4 * lg + lr;
+        float sum = part[0], sc = scale[0];
 #pragma unroll
         for (int r = 1; r < 4; ++r)
-          if (lr == r) sum = part[r];
-        if (term == 0) {
-          s_fw[t] += __expf(s_cs[t]) * sum;                          // U_f
-        } else if (term == 1) {
-          const float v = s_dt[t] * __expf(cs_last - s_cs[t]) * sum;  // V_f
-          s_bw[t] += v;
-          s_sub[t] += v;
-        } else if (term == 2) {
-          s_bw[t] += __expf(cs_last - s_csx[t]) * sum;               // U_b
-        } else {
-          const float v = s_dt[t] * __expf(s_csx[t]) * sum;          // V_b
-          s_fw[t] += v;
-          s_sub[t] += v;
-        }
+          if (lr == r) { sum = part[r]; sc = scale[r]; }
+        const float v = sc * sum;
+        if (term == 0) s_fw[t] += v;                       // U_f
+        else if (term == 1) { s_bw[t] += v; s_sub[t] += v; }  // V_f
+        else if (term == 2) s_bw[t] += v;                  // U_b
+        else { s_fw[t] += v; s_sub[t] += v; }              // V_b
+      }
+    }
+    k = __expf(cs_last) * block_sum512(k, red);   // its barriers also order the boundary terms before the scans
+
+    // suffix sums of s_fw, prefix sums of s_bw
+    for (int off = 1; off < Q; off <<= 1) {
+      float f = 0.f, bk = 0.f;
+      if (tid < Q) {
+        if (tid + off < Q) f = s_fw[tid + off];
+        if (tid >= off) bk = s_bw[tid - off];
+      }
+      __syncthreads();
+      if (tid < Q) {
+        s_fw[tid] += f;
+        s_bw[tid] += bk;
+      }
+      __syncthreads();
+    }
+    if (tid < Q) R[(bl + s_tok[tid]) * Hs + h] = s_fw[tid] + s_bw[tid] - s_sub[tid] + k;
+  }
+
+  // dB, dC of the chunk's tokens (rows r0 + 4 lg + r, columns 16 j + lr)
+  if (owns_rows) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = ((bl + s_tok[r0 + 4 * lg + r]) * G + g) * N;
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) {
+        dC[row + 16 * j + lr] = gC[j][r];
+        dB[row + 16 * j + lr] = gB[j][r];
       }
     }
   }
-
-  // pairs with both ends outside
-  float k = 0.f;
-  for (int e = tid * 4; e < P * N; e += NT * 4) {
-    const float4 u1 = *reinterpret_cast<const float4*>(mats[0] + e), v1 = *reinterpret_cast<const float4*>(mats[1] + e);
-    const float4 u2 = *reinterpret_cast<const float4*>(mats[2] + e), v2 = *reinterpret_cast<const float4*>(mats[3] + e);
-    k += u1.x * v1.x + u1.y * v1.y + u1.z * v1.z + u1.w * v1.w + u2.x * v2.x + u2.y * v2.y + u2.z * v2.z + u2.w * v2.w;
-  }
-  k = __expf(cs_last) * block_sum512(k, red);   // its barriers also order the boundary terms before the scans
-
-  // suffix sums of s_fw, prefix sums of s_bw
-  for (int off = 1; off < Q; off <<= 1) {
-    float f = 0.f, bk = 0.f;
-    if (tid < Q) {
-      if (tid + off < Q) f = s_fw[tid + off];
-      if (tid >= off) bk = s_bw[tid - off];
-    }
-    __syncthreads();
-    if (tid < Q) {
-      s_fw[tid] += f;
-      s_bw[tid] += bk;
-    }
-    __syncthreads();
-  }
-  if (tid < Q) R[(bl + s_tok[tid]) * Hs + h] = s_fw[tid] + s_bw[tid] - s_sub[tid] + k;
 }
 
 // Per (chunk, head, batch element), head size 64: dx = dt yhat + 2 D dy,
@@ -478,33 +506,18 @@ __global__ __launch_bounds__(256) void ma_bwd_chunk_kernel(
 // Byte offsets inside the caller's workspace.
 struct BwdWs {
   size_t hf1, hb1, hf2, hb2, scan, xprime, dzero, dt_next, dt_prev, dy_next, dy_prev, R, yh,
-      val_a, val_b, out, total;
+ total;
 };
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-lingen_mate_shape aux_shape(const lingen_mate_shape* s) {
-  // the scans whose keys and queries are per-head P-vectors: one group per
-  // head, key size P, 64 value columns per call, chunk 64
-  lingen_mate_shape a = *s;
-  a.headdim = kHalf;
-  a.d_state = s->headdim;
-  a.ngroups = s->ssd_heads;
-  a.chunk = 64;
-  a.attn_heads = s->ssd_heads;
-  a.attn_headdim = kHalf;
-  a.n_review = 0;
-  return a;
-}
 
 int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   const size_t rows = size_t(s->batch) * size_t(tokens(s));
   const size_t hs = size_t(s->ssd_heads), P = size_t(s->headdim), N = size_t(s->d_state);
   const size_t nc = size_t(tokens(s)) / size_t(s->chunk);
-  const lingen_mate_shape a = aux_shape(s);
-  size_t ws_main = 0, ws_aux = 0;
+  size_t ws_main = 0;
   if (int rc = lingen_mate_workspace_bytes(s, &ws_main)) return rc;
-  if (int rc = lingen_mate_workspace_bytes(&a, &ws_aux)) return rc;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
   const size_t states = size_t(s->batch) * nc * hs * P * N * 4;
@@ -512,7 +525,7 @@ int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   w->hb1 = take(states);
   w->hf2 = take(states);
   w->hb2 = take(states);
-  w->scan = take(ws_main > ws_aux ? ws_main : ws_aux);
+  w->scan = take(ws_main);
   w->xprime = take(rows * hs * P * 2);
   w->dzero = take(hs * 4);
   w->dt_next = take(rows * hs * 4);
@@ -521,9 +534,6 @@ int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   w->dy_prev = take(rows * hs * P * 2);
   w->R = take(rows * hs * 4);
   w->yh = take(rows * hs * P * 2);
-  w->val_a = take(rows * hs * kHalf * 2);
-  w->val_b = take(rows * hs * kHalf * 2);
-  w->out = take(rows * hs * kHalf * 2);
   w->total = off;
   return LINGEN_OK;
 }
@@ -531,13 +541,11 @@ int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
 int check_bwd_shape(const lingen_mate_shape* s) {
   if (int rc = validate_shape(s)) return rc;
   if (s->n_review != 0) return LINGEN_ERR_UNSUPPORTED;
-  // the transposed scans run in the bf16 family whose key size is the head
-  // size: bf16 storage, P = 64, N a multiple of 64
-  if (s->dtype != LINGEN_BF16 || s->headdim != 64 || s->d_state % kHalf) return LINGEN_ERR_UNSUPPORTED;
+  // the crossing-sum kernel takes bf16 storage with head size 64
+  if (s->dtype != LINGEN_BF16 || s->headdim != 64) return LINGEN_ERR_UNSUPPORTED;
   // the crossing-sum kernel is compiled for the two bf16 scan families with P = 64
   if (!((s->chunk == 64 && s->d_state == 64) || (s->chunk == 128 && s->d_state == 128))) return LINGEN_ERR_UNSUPPORTED;
-  const lingen_mate_shape a = aux_shape(s);
-  return validate_shape(&a);
+  return LINGEN_OK;
 }
 
 
@@ -576,7 +584,6 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   const int64_t rows = int64_t(shape->batch) * L;
   const size_t scan_bytes = w.xprime - w.scan;
   const ScanOrder so{mode, shape->T, shape->H, shape->W};
-  const lingen_mate_shape aux = aux_shape(shape);
   const __bf16* xb = static_cast<const __bf16*>(x);
   const __bf16* dyb = static_cast<const __bf16*>(dy);
   int rc;
@@ -589,7 +596,7 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
     if (hipGetLastError() != hipSuccess) return LINGEN_ERR_HIP;       \
   } while (0)
 
-  // a zero D for the auxiliary scans; dA and dD accumulate from zero
+  // a zero D for the transposed scans; dA and dD accumulate from zero
   zero_floats_kernel<<<1, kThreads, 0, stream>>>(atf(w.dzero), dA, dD, Hs);
   LINGEN_LAUNCHED();
   const float* dz = atf(w.dzero);
@@ -619,40 +626,18 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   LINGEN_TRY(lingen_ma_fwd_dirs(at(w.dy_prev), dtp, A, C, B, dz, at(w.dy_next), dtn, A, C, B, dz, mode, shape,
                                 at(w.yh), at(w.scan), scan_bytes, stream));
 
-  // dC and dB, 64 value columns at a time, keys and queries per head
-  for (int col0 = 0; col0 < N; col0 += kHalf) {
-    head_values_kernel<<<blocks_for(rows * Hs * (kHalf / 8)), kThreads, 0, stream>>>(
-        static_cast<const __bf16*>(B), G, N, col0, nullptr, Hs, rows, static_cast<__bf16*>(at(w.val_a)));
-    LINGEN_LAUNCHED();
-    LINGEN_TRY(lingen_ma_fwd(at(w.val_a), dt, A, x, dy, dz, mode, &aux, at(w.out), at(w.scan), scan_bytes, stream));
-    group_sum_kernel<<<blocks_for(rows * G * (kHalf / 4)), kThreads, 0, stream>>>(
-        static_cast<const __bf16*>(at(w.out)), nullptr, Hs, G, N, col0, rows, dC);
-    LINGEN_LAUNCHED();
-
-    head_values_kernel<<<blocks_for(rows * Hs * (kHalf / 8)), kThreads, 0, stream>>>(
-        static_cast<const __bf16*>(C), G, N, col0, dtp, Hs, rows, static_cast<__bf16*>(at(w.val_a)));
-    LINGEN_LAUNCHED();
-    head_values_kernel<<<blocks_for(rows * Hs * (kHalf / 8)), kThreads, 0, stream>>>(
-        static_cast<const __bf16*>(C), G, N, col0, dtn, Hs, rows, static_cast<__bf16*>(at(w.val_b)));
-    LINGEN_LAUNCHED();
-    LINGEN_TRY(lingen_ma_fwd_dirs(at(w.val_a), dtp, A, dy, x, dz, at(w.val_b), dtn, A, dy, x, dz, mode, &aux,
-                                  at(w.out), at(w.scan), scan_bytes, stream));
-    group_sum_kernel<<<blocks_for(rows * G * (kHalf / 4)), kThreads, 0, stream>>>(
-        static_cast<const __bf16*>(at(w.out)), dt, Hs, G, N, col0, rows, dB);
-    LINGEN_LAUNCHED();
-  }
-
   // crossing sums, then ddt, dx, dA, dD
   {
+    const dim3 cgrid{unsigned(nc), unsigned(G), unsigned(shape->batch)};
     const dim3 grid{unsigned(nc), unsigned(Hs), unsigned(shape->batch)};
     const __bf16* bb = static_cast<const __bf16*>(B);
     const __bf16* cc = static_cast<const __bf16*>(C);
     if (Q == 128 && N == 128)
-      ma_bwd_cross_kernel<128, 128><<<grid, kCrossThreads, 0, stream>>>(
-          xb, dyb, dt, A, bb, cc, atf(w.hf1), atf(w.hb1), atf(w.hf2), atf(w.hb2), so, L, Hs, G, atf(w.R));
+      ma_bwd_cross_kernel<128, 128><<<cgrid, kCrossThreads, 0, stream>>>(
+          xb, dyb, dt, A, bb, cc, atf(w.hf1), atf(w.hb1), atf(w.hf2), atf(w.hb2), so, L, Hs, G, atf(w.R), dB, dC);
     else if (Q == 64 && N == 64)
-      ma_bwd_cross_kernel<64, 64><<<grid, kCrossThreads, 0, stream>>>(
-          xb, dyb, dt, A, bb, cc, atf(w.hf1), atf(w.hb1), atf(w.hf2), atf(w.hb2), so, L, Hs, G, atf(w.R));
+      ma_bwd_cross_kernel<64, 64><<<cgrid, kCrossThreads, 0, stream>>>(
+          xb, dyb, dt, A, bb, cc, atf(w.hf1), atf(w.hb1), atf(w.hf2), atf(w.hb2), so, L, Hs, G, atf(w.R), dB, dC);
     else
       return LINGEN_ERR_UNSUPPORTED;
     LINGEN_LAUNCHED();

@@ -33,5 +33,11 @@ ScanFamily scan_family(const lingen_mate_shape* s);
 AttnFamily attn_family(const lingen_mate_shape* s);
 int check_ptr(const void* p);                      // NULL / alignment check
 int compute_units();                               // of the current device (cached per device), -1 on error
+// Chunk states and scan states of one batch element (x, dt, B of that
+// element) into the workspace, at ws_layout(s).states in the storage dtype:
+// [2][n_chunks][Hs][P][N], the state entering each chunk of the forward scan
+// and then of the reverse scan.  lingen_status.
+int scan_states_one(const lingen_mate_shape* s, int mode, const void* xb, const float* dtb, const float* A,
+                    const void* Bb, void* workspace, hipStream_t stream);
 
 }  // namespace lingen

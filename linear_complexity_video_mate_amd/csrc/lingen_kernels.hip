@@ -1566,6 +1566,29 @@ int check_ws(const lingen_mate_shape* s, const void* ws, size_t ws_bytes) {
 
 using namespace lingen;
 
+namespace lingen {
+// Chunk states and scan states of one batch element into the workspace (at
+// ws_layout().states, [2][n_chunks][Hs][P][N] in the storage dtype: the
+// state entering each chunk of the forward scan, then of the reverse scan).
+int scan_states_one(const lingen_mate_shape* s, int mode, const void* xb, const float* dtb, const float* A,
+                    const void* Bb, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  switch (scan_family(s)) {
+    case SCAN_F32_P32_N16_Q16:
+      return launch_states<float, 32, 16, 16>(s, mode, static_cast<const float*>(xb), dtb, A,
+                                              static_cast<const float*>(Bb), ws, stream);
+    case SCAN_BF16_P64_N64_Q64:
+      return launch_states<__bf16, 64, 64, 64>(s, mode, static_cast<const __bf16*>(xb), dtb, A,
+                                               static_cast<const __bf16*>(Bb), ws, stream);
+    case SCAN_BF16_P64_N128_Q128:
+      return launch_states<__bf16, 64, 128, 128>(s, mode, static_cast<const __bf16*>(xb), dtb, A,
+                                                 static_cast<const __bf16*>(Bb), ws, stream);
+    default:
+      return LINGEN_ERR_UNSUPPORTED;
+  }
+}
+}  // namespace lingen
+
 extern "C" {
 
 int lingen_rms_index_device(int32_t mode, int32_t T, int32_t H, int32_t W, int32_t* perm_dev, hipStream_t stream) {
@@ -1610,23 +1633,7 @@ int lingen_ssd_chunk_states(const void* x, const float* dt, const float* A, cons
     const char* xb = static_cast<const char*>(x) + b * L * Hs * P * eb;
     const float* dtb = dt + b * L * Hs;
     const char* Bb = static_cast<const char*>(B) + b * L * s->ngroups * N * eb;
-    int rc = LINGEN_ERR_UNSUPPORTED;
-    switch (scan_family(s)) {
-      case SCAN_F32_P32_N16_Q16:
-        rc = launch_states<float, 32, 16, 16>(s, mode, reinterpret_cast<const float*>(xb), dtb, A,
-                                              reinterpret_cast<const float*>(Bb), ws, stream);
-        break;
-      case SCAN_BF16_P64_N64_Q64:
-        rc = launch_states<__bf16, 64, 64, 64>(s, mode, reinterpret_cast<const __bf16*>(xb), dtb, A,
-                                               reinterpret_cast<const __bf16*>(Bb), ws, stream);
-        break;
-      case SCAN_BF16_P64_N128_Q128:
-        rc = launch_states<__bf16, 64, 128, 128>(s, mode, reinterpret_cast<const __bf16*>(xb), dtb, A,
-                                                 reinterpret_cast<const __bf16*>(Bb), ws, stream);
-        break;
-      default: break;
-    }
-    if (rc) return rc;
+    if (int rc = scan_states_one(s, mode, xb, dtb, A, Bb, ws, stream)) return rc;
     const unsigned blocks = unsigned((per + 255) / 256);
     if (s->dtype == LINGEN_BF16) {
       const __bf16* st = reinterpret_cast<const __bf16*>(ws + lay.states);

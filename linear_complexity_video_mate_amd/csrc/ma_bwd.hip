@@ -15,8 +15,9 @@
 //   * dB and dC are, per chunk, products of the same chunk-local matrices the
 //     crossing sums need (E = dt (dy x^T) weighted by the decays) with C and
 //     B, plus products of the chunk-boundary states with x and dy;
-//   * the chunk-boundary adjoint states are chunk states of the scan of
-//     x' = dy exp(dt A) / dt with C in place of B;
+//   * the chunk-boundary adjoint states are the scan states of x' = dy
+//     exp(dt A) / dt with C in place of B (read in bf16 from the chunk-state
+//     pass's workspace, one batch element at a time);
 //   * ddt and dA need, at every position r, the crossing sum
 //     R_r = sum_{s < r <= t} W_ts.  Within a chunk it is the suffix sum of
 //     dy_t . ytilde_t - dt_t x_t . yhat_t (ytilde: the direction's output,
@@ -179,32 +180,34 @@ __device__ __forceinline__ bf16x8 perm_frag(const __bf16* row, int k0, int lane)
 //   dB_s = sum_t E_ts C_t + dt_s exp(cs_last - cs_s) hb2^T x_s + dt_s exp(csx_s) hf2^T x_s.
 // Products on 16x16x32 bf16 MFMA tiles from padded LDS rows (C B^T, dy x^T,
 // E B, E^T C and the state products, per head), fp32 everywhere after them;
-// no sum runs across the sequence.  512
+// no sum runs across the sequence.  The states are the bf16 scan states the
+// chunk-state pass leaves in its workspace (st1: of (x, B); st2: of
+// (dy exp(dt A) / dt, C); each [2][n_chunks][Hs][P][N], forward then reverse),
+// for batch element b.  512
 // threads (8 waves); wave w owns row block w of every Q x N result.
 template <int Q, int N>
 __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ dy, const float* __restrict__ dt,
     const float* __restrict__ A, const __bf16* __restrict__ B, const __bf16* __restrict__ C,
-    const float* __restrict__ hf1, const float* __restrict__ hb1, const float* __restrict__ hf2,
-    const float* __restrict__ hb2, ScanOrder so, int L, int Hs, int G, float* __restrict__ R,
-    float* __restrict__ dB, float* __restrict__ dC) {
+    const __bf16* __restrict__ st1, const __bf16* __restrict__ st2, int64_t per, ScanOrder so, int L, int Hs,
+    int G, int b, float* __restrict__ R, float* __restrict__ dB, float* __restrict__ dC) {
   constexpr int P = 64, NT = kCrossThreads, NW = NT / 64;
   constexpr int LDB = N + 8, LDX = P + 8, LDE = Q + 8;   // padded bf16 row strides
   constexpr int QT = Q / 16, NTL = N / 16;
   constexpr int CBT = (QT * QT + NW - 1) / NW;           // Q x Q tiles per wave
-  constexpr int MT_ELEMS = N * LDX, E_ELEMS = Q * LDE;
-  constexpr int U_ELEMS = MT_ELEMS > E_ELEMS ? MT_ELEMS : E_ELEMS;
-  constexpr int SPT = P * N / NT;                        // state elements per thread
-  static_assert(Q % 32 == 0 && Q <= NT && N % 32 == 0 && QT <= NW && (P * N) % (4 * NT) == 0, "tiles");
+  constexpr int M_ELEMS = P * LDB, E_ELEMS = Q * LDE;
+  constexpr int U_ELEMS = M_ELEMS > E_ELEMS ? M_ELEMS : E_ELEMS;
+  constexpr int SCH = P * N / 8 / NT;                    // 16-byte state chunks per thread
+  static_assert(Q % 32 == 0 && Q <= NT && N % 32 == 0 && QT <= NW && (P * N) % (8 * NT) == 0, "tiles");
   __shared__ __attribute__((aligned(16))) __bf16 sB[Q * LDB], sC[Q * LDB], sX[Q * LDX], sDY[Q * LDX];
-  __shared__ __attribute__((aligned(16))) __bf16 sU[U_ELEMS];   // E (Q x Q), then a state transposed (N x P)
+  __shared__ __attribute__((aligned(16))) __bf16 sU[U_ELEMS];   // E (Q x Q), then a state (P x N rows)
   __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], red[NW];
   __shared__ int s_tok[Q];
   __bf16* const sE = sU;
-  __bf16* const sMT = sU;
+  __bf16* const sM = sU;
 
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int nc = L / Q, hpg = Hs / G;
+  const int c = blockIdx.x, g = blockIdx.y;
+  const int hpg = Hs / G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int64_t bl = int64_t(b) * L;
@@ -333,27 +336,25 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     }
 
     // pairs with one end outside the chunk, and their share of dC, dB
-    const int64_t st_off = ((int64_t(b) * nc + c) * Hs + h) * int64_t(P) * N;
-    const float* mats[4] = {hf1 + st_off, hb2 + st_off, hb1 + st_off, hf2 + st_off};
-    float keep[SPT];
+    const int64_t st_off = (int64_t(c) * Hs + h) * int64_t(P) * N;
+    const __bf16* mats[4] = {st1 + st_off, st2 + per + st_off, st1 + per + st_off, st2 + st_off};   // hf1 hb2 hb1 hf2
+    bf16x8 keep[SCH];
     float k = 0.f;
 #pragma unroll 1
     for (int term = 0; term < 4; ++term) {
       __syncthreads();   // E (and the previous state) is no longer read; the pair sums have landed
 #pragma unroll
-      for (int q = 0; q < SPT / 4; ++q) {
+      for (int q = 0; q < SCH; ++q) {
         const int i = tid + q * NT;
-        const float4 m4 = reinterpret_cast<const float4*>(mats[term])[i];
+        const bf16x8 m8 = reinterpret_cast<const bf16x8*>(mats[term])[i];
         if (term == 0 || term == 2) {
-          keep[4 * q] = m4.x; keep[4 * q + 1] = m4.y; keep[4 * q + 2] = m4.z; keep[4 * q + 3] = m4.w;
+          keep[q] = m8;
         } else {
-          k += keep[4 * q] * m4.x + keep[4 * q + 1] * m4.y + keep[4 * q + 2] * m4.z + keep[4 * q + 3] * m4.w;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) k = fmaf(static_cast<float>(keep[q][e]), static_cast<float>(m8[e]), k);
         }
-        const int pp = (i * 4) / N, n = (i * 4) % N;
-        sMT[(n + 0) * LDX + pp] = static_cast<__bf16>(m4.x);
-        sMT[(n + 1) * LDX + pp] = static_cast<__bf16>(m4.y);
-        sMT[(n + 2) * LDX + pp] = static_cast<__bf16>(m4.z);
-        sMT[(n + 3) * LDX + pp] = static_cast<__bf16>(m4.w);
+        const int pp = (i * 8) / N, n = (i * 8) % N;
+        *reinterpret_cast<bf16x8*>(sM + pp * LDB + n) = m8;
       }
       __syncthreads();
       if (!owns_rows) continue;
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       const __bf16* sv = is_u ? sC : sB;
       bf16x8 af[P / 32];
 #pragma unroll
-      for (int kk = 0; kk < P / 32; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(sa + (r0 + lr) * LDX + 32 * kk + 8 * lg);
+      for (int kk = 0; kk < P / 32; ++kk) af[kk] = perm_frag(sa + (r0 + lr) * LDX, 32 * kk, lane);
       // row scales of this term (rows r0 + 4 lg + r)
       float scale[4];
 #pragma unroll
@@ -379,10 +380,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         const int n0 = nt * 16;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < P / 32; ++kk) {
-          const bf16x8 v = *reinterpret_cast<const bf16x8*>(sMT + (n0 + lr) * LDX + 32 * kk + 8 * lg);
-          acc = mma(af[kk], v, acc);
-        }
+        for (int kk = 0; kk < P / 32; ++kk) acc = mma(af[kk], tr_frag(sM, LDB, 32 * kk, n0, lane), acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           part[r] = fmaf(acc[r], static_cast<float>(sv[(r0 + 4 * lg + r) * LDB + n0 + lr]), part[r]);
@@ -505,27 +503,21 @@ __global__ __launch_bounds__(256) void ma_bwd_chunk_kernel(
 
 // Byte offsets inside the caller's workspace.
 struct BwdWs {
-  size_t hf1, hb1, hf2, hb2, scan, xprime, dzero, dt_next, dt_prev, dy_next, dy_prev, R, yh,
+  size_t scan1, scan2, xprime, dzero, dt_next, dt_prev, dy_next, dy_prev, R, yh,
  total;
 };
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-
 int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   const size_t rows = size_t(s->batch) * size_t(tokens(s));
-  const size_t hs = size_t(s->ssd_heads), P = size_t(s->headdim), N = size_t(s->d_state);
-  const size_t nc = size_t(tokens(s)) / size_t(s->chunk);
+  const size_t hs = size_t(s->ssd_heads), P = size_t(s->headdim);
   size_t ws_main = 0;
   if (int rc = lingen_mate_workspace_bytes(s, &ws_main)) return rc;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
-  const size_t states = size_t(s->batch) * nc * hs * P * N * 4;
-  w->hf1 = take(states);
-  w->hb1 = take(states);
-  w->hf2 = take(states);
-  w->hb2 = take(states);
-  w->scan = take(ws_main);
+  w->scan1 = take(ws_main);
+  w->scan2 = take(ws_main);
   w->xprime = take(rows * hs * P * 2);
   w->dzero = take(hs * 4);
   w->dt_next = take(rows * hs * 4);
@@ -582,7 +574,7 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   const int L = int(tokens(shape)), Hs = shape->ssd_heads, P = shape->headdim, N = shape->d_state;
   const int G = shape->ngroups, Q = shape->chunk, nc = L / Q;
   const int64_t rows = int64_t(shape->batch) * L;
-  const size_t scan_bytes = w.xprime - w.scan;
+  const size_t scan_bytes = w.scan2 - w.scan1;
   const ScanOrder so{mode, shape->T, shape->H, shape->W};
   const __bf16* xb = static_cast<const __bf16*>(x);
   const __bf16* dyb = static_cast<const __bf16*>(dy);
@@ -601,14 +593,9 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   LINGEN_LAUNCHED();
   const float* dz = atf(w.dzero);
 
-  // forward states of (x, B) and adjoint states of (x', C)
-  LINGEN_TRY(lingen_ssd_chunk_states(x, dt, A, B, mode, shape, atf(w.hf1), atf(w.hb1), at(w.scan), scan_bytes,
-                                     stream));
   adjoint_input_kernel<<<blocks_for(rows * Hs * (P / 8)), kThreads, 0, stream>>>(
       dyb, dt, A, rows, Hs, P, static_cast<__bf16*>(at(w.xprime)));
   LINGEN_LAUNCHED();
-  LINGEN_TRY(lingen_ssd_chunk_states(at(w.xprime), dt, A, C, mode, shape, atf(w.hf2), atf(w.hb2), at(w.scan),
-                                     scan_bytes, stream));
 
   // transposed outputs: M_b^T dy / dt is the forward scan with dt_prev, M_f^T dy / dt the reverse scan with
   // dt_next, inputs dy / (moved dt), B and C exchanged
@@ -624,23 +611,36 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   // (M_b^T + M_f^T) dy / dt in one per-direction call: the forward scan with dt_prev and the reverse scan
   // with dt_next
   LINGEN_TRY(lingen_ma_fwd_dirs(at(w.dy_prev), dtp, A, C, B, dz, at(w.dy_next), dtn, A, C, B, dz, mode, shape,
-                                at(w.yh), at(w.scan), scan_bytes, stream));
+                                at(w.yh), at(w.scan1), scan_bytes, stream));
 
   // crossing sums, then ddt, dx, dA, dD
   {
-    const dim3 cgrid{unsigned(nc), unsigned(G), unsigned(shape->batch)};
+    const dim3 cgrid{unsigned(nc), unsigned(G), 1u};
     const dim3 grid{unsigned(nc), unsigned(Hs), unsigned(shape->batch)};
-    const __bf16* bb = static_cast<const __bf16*>(B);
-    const __bf16* cc = static_cast<const __bf16*>(C);
-    if (Q == 128 && N == 128)
-      ma_bwd_cross_kernel<128, 128><<<cgrid, kCrossThreads, 0, stream>>>(
-          xb, dyb, dt, A, bb, cc, atf(w.hf1), atf(w.hb1), atf(w.hf2), atf(w.hb2), so, L, Hs, G, atf(w.R), dB, dC);
-    else if (Q == 64 && N == 64)
-      ma_bwd_cross_kernel<64, 64><<<cgrid, kCrossThreads, 0, stream>>>(
-          xb, dyb, dt, A, bb, cc, atf(w.hf1), atf(w.hb1), atf(w.hf2), atf(w.hb2), so, L, Hs, G, atf(w.R), dB, dC);
-    else
-      return LINGEN_ERR_UNSUPPORTED;
-    LINGEN_LAUNCHED();
+    const WsLayout lay = ws_layout(shape);
+    const int64_t per = int64_t(nc) * Hs * P * N;   // one direction's scan states
+    const __bf16* st1 = reinterpret_cast<const __bf16*>(ws + w.scan1 + lay.states);
+    const __bf16* st2 = reinterpret_cast<const __bf16*>(ws + w.scan2 + lay.states);
+    const int64_t eb = 2;
+    for (int bi = 0; bi < shape->batch; ++bi) {
+      // forward / reverse states of (x, B) and of (x', C) for this batch element, left in the two workspaces
+      const int64_t xo = int64_t(bi) * L * Hs * P * eb, bo = int64_t(bi) * L * G * N * eb;
+      LINGEN_TRY(scan_states_one(shape, mode, static_cast<const char*>(x) + xo, dt + int64_t(bi) * L * Hs, A,
+                                 static_cast<const char*>(B) + bo, ws + w.scan1, stream));
+      LINGEN_TRY(scan_states_one(shape, mode, static_cast<const char*>(at(w.xprime)) + xo, dt + int64_t(bi) * L * Hs,
+                                 A, static_cast<const char*>(C) + bo, ws + w.scan2, stream));
+      if (Q == 128 && N == 128)
+        ma_bwd_cross_kernel<128, 128><<<cgrid, kCrossThreads, 0, stream>>>(
+            xb, dyb, dt, A, static_cast<const __bf16*>(B), static_cast<const __bf16*>(C), st1, st2, per, so, L, Hs,
+            G, bi, atf(w.R), dB, dC);
+      else if (Q == 64 && N == 64)
+        ma_bwd_cross_kernel<64, 64><<<cgrid, kCrossThreads, 0, stream>>>(
+            xb, dyb, dt, A, static_cast<const __bf16*>(B), static_cast<const __bf16*>(C), st1, st2, per, so, L, Hs,
+            G, bi, atf(w.R), dB, dC);
+      else
+        return LINGEN_ERR_UNSUPPORTED;
+      LINGEN_LAUNCHED();
+    }
     ma_bwd_chunk_kernel<<<grid, 256, 0, stream>>>(xb, dyb, dt, A, D, static_cast<const __bf16*>(at(w.yh)), atf(w.R),
                                                  so, L, Q, Hs, dx, ddt, dA, dD);
     LINGEN_LAUNCHED();

@@ -273,15 +273,16 @@ int lingen_dense_attn_fwd(const void* q, const void* k, const void* v, void* o,
  *   dA, dD: [Hs] fp32 (summed over tokens and batch elements)
  * all device, caller-owned, overwritten.  dy has the layout and dtype of y.
  * The gradients are assembled from the library's scans run with transformed
- * operands (transposed scans with dt moved by one scan position, the scan
- * of x' = dy exp(dt A) / dt for the adjoint chunk states, scans with B as
- * values and x, dy as per-head keys and queries) and per-chunk sums for ddt
- * and dA; see the source for the derivation.  Supported: bf16 storage with
- * P = 64 and N a multiple of 64 (the compiled families (BF16, 64, 64, 64)
- * and (BF16, 64, 128, 128)); anything else that passes lingen_mate_validate
- * returns LINGEN_ERR_UNSUPPORTED, as do review tokens.
- * workspace: device, lingen_ma_bwd_workspace_bytes (chunk states of two
- * scans in fp32, plus the transformed operands and the scans' outputs).
+ * operands (the transposed scans, with dt moved by one scan position, for
+ * dx; the chunk-state pass of x' = dy exp(dt A) / dt against C for the
+ * adjoint states) and a per-chunk MFMA kernel for the crossing sums behind
+ * ddt and dA and for dB and dC; see the source for the derivation.
+ * Supported: bf16 storage with P = 64 in the compiled families
+ * (BF16, 64, 64, 64) and (BF16, 64, 128, 128); anything else that passes
+ * lingen_mate_validate returns LINGEN_ERR_UNSUPPORTED, as do review tokens.
+ * workspace: device, lingen_ma_bwd_workspace_bytes (two scan workspaces,
+ * whose bf16 chunk states the kernel reads, plus the transformed operands
+ * and the transposed scan's output).
  * Errors: those of lingen_mate_validate; LINGEN_ERR_UNSUPPORTED as above;
  * LINGEN_ERR_SHAPE for mode outside 0..3; LINGEN_ERR_NULL / _ALIGN for a
  * pointer; LINGEN_ERR_WORKSPACE. */

@@ -138,6 +138,23 @@ __device__ __forceinline__ float block_sum512(float v, float* red) {
   return t;
 }
 
+// Inclusive prefix sums of Q = 64 V values held V per lane (lane l holds
+// positions V l .. V l + V - 1), within one wave, by shuffles.
+template <int V>
+__device__ __forceinline__ void wave_prefix(float (&v)[V], int lane) {
+#pragma unroll
+  for (int e = 1; e < V; ++e) v[e] += v[e - 1];
+  float run = v[V - 1];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float o = __shfl_up(run, d, 64);
+    if (lane >= d) run += o;
+  }
+  const float before = run - v[V - 1];
+#pragma unroll
+  for (int e = 0; e < V; ++e) v[e] += before;
+}
+
 // Two 4-element transposing LDS reads (rows k and k + 16 of a row-major
 // bf16 tile, 16 columns from `col`), giving lane group g the contraction
 // indices {4g..4g+3, 16+4g..16+4g+3} of a 32-block for column (lane & 15):
@@ -245,18 +262,28 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       *reinterpret_cast<bf16x8*>(sDY + row * LDX + k8) = *reinterpret_cast<const bf16x8*>(dy + src);
     }
     __syncthreads();
-    for (int i = tid; i < Q; i += NT) s_cs[i] = s_dt[i] * a_h;
-    __syncthreads();
-    for (int off = 1; off < Q; off <<= 1) {
-      float v = 0.f;
-      if (tid < Q && tid >= off) v = s_cs[tid - off];
-      __syncthreads();
-      if (tid < Q) s_cs[tid] += v;
-      __syncthreads();
+    if (wave == 0) {   // chunk-local cumulative sums of dt*A, inclusive and exclusive
+      constexpr int V = Q / 64;
+      float v[V], d0[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) { d0[e] = s_dt[V * lane + e] * a_h; v[e] = d0[e]; }
+      wave_prefix<V>(v, lane);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        s_cs[V * lane + e] = v[e];
+        s_csx[V * lane + e] = v[e] - d0[e];
+      }
     }
-    for (int i = tid; i < Q; i += NT) s_csx[i] = s_cs[i] - s_dt[i] * a_h;
     __syncthreads();
     const float cs_last = s_cs[Q - 1];
+
+    // the four chunk-boundary states of this head (hf1, hb2, hb1, hf2); the
+    // first one is fetched now, each next one while the previous is in use
+    const int64_t st_off = (int64_t(c) * Hs + h) * int64_t(P) * N;
+    const __bf16* mats[4] = {st1 + st_off, st2 + per + st_off, st1 + per + st_off, st2 + st_off};
+    bf16x8 cur[SCH];
+#pragma unroll
+    for (int q = 0; q < SCH; ++q) cur[q] = reinterpret_cast<const bf16x8*>(mats[0])[tid + q * NT];
 
     // pairs inside the chunk: dy x^T tiles -> W (crossing sums) and E (dB, dC weights)
 #pragma unroll 1
@@ -336,8 +363,6 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     }
 
     // pairs with one end outside the chunk, and their share of dC, dB
-    const int64_t st_off = (int64_t(c) * Hs + h) * int64_t(P) * N;
-    const __bf16* mats[4] = {st1 + st_off, st2 + per + st_off, st1 + per + st_off, st2 + st_off};   // hf1 hb2 hb1 hf2
     bf16x8 keep[SCH];
     float k = 0.f;
 #pragma unroll 1
@@ -346,7 +371,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
 #pragma unroll
       for (int q = 0; q < SCH; ++q) {
         const int i = tid + q * NT;
-        const bf16x8 m8 = reinterpret_cast<const bf16x8*>(mats[term])[i];
+        const bf16x8 m8 = cur[q];
         if (term == 0 || term == 2) {
           keep[q] = m8;
         } else {
@@ -355,6 +380,10 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         }
         const int pp = (i * 8) / N, n = (i * 8) % N;
         *reinterpret_cast<bf16x8*>(sM + pp * LDB + n) = m8;
+      }
+      if (term < 3) {
+#pragma unroll
+        for (int q = 0; q < SCH; ++q) cur[q] = reinterpret_cast<const bf16x8*>(mats[term + 1])[tid + q * NT];
       }
       __syncthreads();
       if (!owns_rows) continue;
@@ -407,20 +436,26 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     }
     k = __expf(cs_last) * block_sum512(k, red);   // its barriers also order the boundary terms before the scans
 
-    // suffix sums of s_fw, prefix sums of s_bw
-    for (int off = 1; off < Q; off <<= 1) {
-      float f = 0.f, bk = 0.f;
-      if (tid < Q) {
-        if (tid + off < Q) f = s_fw[tid + off];
-        if (tid >= off) bk = s_bw[tid - off];
+    // suffix sums of s_fw, prefix sums of s_bw, by wave 0 (the suffix sums as
+    // prefix sums of the reversed order)
+    if (wave == 0) {
+      constexpr int V = Q / 64;
+      float f[V], bk[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        f[e] = s_fw[Q - 1 - (V * lane + e)];
+        bk[e] = s_bw[V * lane + e];
       }
-      __syncthreads();
-      if (tid < Q) {
-        s_fw[tid] += f;
-        s_bw[tid] += bk;
+      wave_prefix<V>(f, lane);
+      wave_prefix<V>(bk, lane);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const int rf = Q - 1 - (V * lane + e), rb = V * lane + e;
+        s_fw[rf] = f[e];
+        s_bw[rb] = bk[e];
       }
-      __syncthreads();
     }
+    __syncthreads();
     if (tid < Q) R[(bl + s_tok[tid]) * Hs + h] = s_fw[tid] + s_bw[tid] - s_sub[tid] + k;
   }
 

@@ -19,14 +19,16 @@
 //     exp(dt A) / dt with C in place of B (read in bf16 from the chunk-state
 //     pass's workspace, one batch element at a time);
 //   * ddt and dA need, at every position r, the crossing sum
-//     R_r = sum_{s < r <= t} W_ts.  Within a chunk it is the suffix sum of
-//     dy_t . ytilde_t - dt_t x_t . yhat_t (ytilde: the direction's output,
-//     yhat: its transposed output before the dt factor) plus one constant,
-//     the inner product of the state entering the next chunk and the adjoint
-//     state leaving this one; ddt = x . (yhat_f + yhat_b) + A (R_f + R_b),
-//     dA = sum dt (R_f + R_b).
-// All sums are formed chunk by chunk, so no cancellation runs over the
-// whole sequence.
+//     R_r = sum_{s < r <= t} W_ts: the pairs inside r's chunk come from the
+//     chunk's W (row minus column sums, then a suffix sum), the pairs with
+//     one end outside from products of the chunk-boundary states with the
+//     chunk's rows, the pairs with both ends outside from one inner product
+//     of states; ddt = x . (yhat_f + yhat_b) + A (R_f + R_b) with yhat the
+//     transposed outputs before the dt factor, dA = sum dt (R_f + R_b).
+//     (Forming the in-chunk part instead from the difference of the bf16
+//     forward and transposed outputs cancels, and loses dA.)
+// All sums are formed chunk by chunk, in fp32 from the bf16 inputs, so no
+// sum runs over the whole sequence.
 
 #include <hip/hip_runtime.h>
 

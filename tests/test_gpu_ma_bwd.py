@@ -1,10 +1,11 @@
 """GPU parity of the MA branch's backward (lingen_ma_bwd) against the fp64
 oracle's ssd_bidir_backward: the 16k-token bf16 workload in several scan
 orders with one and two B/C groups, a batch of two, and the 512p-like
-workload in its launch configuration with dy nonzero on one head only (the
-gradients are linear in dy, so every gradient -- dB and dC included -- is
-that head's, which the oracle computes over all 131,072 tokens; the other
-heads' dx, ddt, dA, dD must be zero).  Bar: relative L2 error at most 2e-2
+workload in its launch configuration and the minute-length workload
+(524,288 tokens) with dy nonzero on one head only (the gradients are linear
+in dy, so every gradient -- dB and dC included -- is that head's, which the
+oracle computes over all tokens; the other heads' dx, ddt, dA, dD must be
+zero).  Bar: relative L2 error at most 2e-2
 per gradient (bf16 storage)."""
 import numpy as np
 import pytest
@@ -108,4 +109,31 @@ def test_ma_bwd_512p_one_head():
     ref = oracle.ssd_bidir_backward(hx["x"], hx["dt"], hx["A"], inp.f64("B"), inp.f64("C"), hx["D"], dy64,
                                     oracle.rms_scan_order(mode, s.T, s.H, s.W))
     got_head = (dx[0][:, [head]], ddt[0][:, [head]], dA[[head]], dB[0], dC[0], dD[[head]])
+    _check(got_head, ref, f"head {head}")
+
+
+def test_ma_bwd_minute_length_one_head():
+    """The largest workload (128x64x64 = 524,288 tokens; 4096 chunks, about
+    10^9 state elements per direction), dy on one head, scan order 1."""
+    torch, mate = need_gpu()
+    from mate_inputs import f32_from_bf16_bits
+    s, cfg_id, head, mode = CONFIGS[3], 3, 5, 1
+    inp = make_inputs(s, cfg_id, seed=151, tensors=list(SCAN), threads=16)
+    dy_bits = _dy(s, cfg_id, 152)
+    dy_bits[:, :head] = 0
+    dy_bits[:, head + 1:] = 0
+    say(f"ma_bwd minute-length mode{mode}, dy on head {head} only")
+    d = {n: inp.torch(n, "cuda") for n in SCAN}
+    dy = torch.from_numpy(dy_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    got = mate.lingen_ma_bwd(*(d[n] for n in SCAN), dy, mode, s)
+    torch.cuda.synchronize()
+    dx, ddt, dA, dB, dC, dD = got
+    got_head = (dx[0][:, [head]].clone(), ddt[0][:, [head]].clone(), dA[[head]].clone(), dB[0].clone(), dC[0].clone(),
+                dD[[head]].clone())
+    del got, dx, ddt, d, dy
+    say("  oracle over all tokens (one head)")
+    hx = {n: head_f64(inp, n, head) for n in ("x", "dt", "A", "D")}
+    dy64 = f32_from_bf16_bits(dy_bits[:, [head]]).astype(np.float64)
+    ref = oracle.ssd_bidir_backward(hx["x"], hx["dt"], hx["A"], inp.f64("B"), inp.f64("C"), hx["D"], dy64,
+                                    oracle.rms_scan_order(mode, s.T, s.H, s.W))
     _check(got_head, ref, f"head {head}")

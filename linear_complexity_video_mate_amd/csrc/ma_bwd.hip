@@ -127,31 +127,67 @@ __global__ __launch_bounds__(kThreads) void shifted_dt_kernel(const __bf16* __re
 
 constexpr int kCrossThreads = 512;
 
+// Cross-lane sums without LDS traffic (every lane of the wave active).
+// DPP quad permutations swap neighbours and pairs inside each quad, the
+// half-row mirror pairs the two quads of an 8-lane half-row and the row
+// mirror the two halves of a 16-lane row; v_permlane16_swap and
+// v_permlane32_swap exchange whole rows (lane l with l ^ 16, l ^ 32).
+template <int CTRL>
+__device__ __forceinline__ float dpp_plus(float v) {
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over each aligned group of 8 lanes, in every lane of the group
+__device__ __forceinline__ float sum8(float v) {
+  v = dpp_plus<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_plus<0x4E>(v);    // quad_perm [2,3,0,1]
+  return dpp_plus<0x141>(v);   // row_half_mirror
+}
+// sum over each 16-lane row, in every lane of the row
+__device__ __forceinline__ float sum16(float v) { return dpp_plus<0x140>(sum8(v));   /* row_mirror */ }
+// sum over the four rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float sum_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float sum64(float v) { return sum_rows(sum16(v)); }
+
 // Block-wide sum over the 512 threads of a workgroup.
 __device__ __forceinline__ float block_sum512(float v, float* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  __syncthreads();
+  v = sum64(v);
+  lds_barrier();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
+  lds_barrier();
   float t = 0.f;
 #pragma unroll
   for (int w = 0; w < kCrossThreads / 64; ++w) t += red[w];
   return t;
 }
 
+// v + the value of the lane the DPP control names (0 where it names none,
+// and in rows the row mask leaves out).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_shifted_plus(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
 // Inclusive prefix sums of Q = 64 V values held V per lane (lane l holds
-// positions V l .. V l + V - 1), within one wave, by shuffles.
+// positions V l .. V l + V - 1), within one wave (all lanes active): row
+// shifts by 1, 2, 4, 8 scan each 16-lane row, then the last lane of row 0
+// and of row 2 is broadcast into the next row, and the last lane of row 1
+// into rows 2 and 3.
 template <int V>
 __device__ __forceinline__ void wave_prefix(float (&v)[V], int lane) {
 #pragma unroll
   for (int e = 1; e < V; ++e) v[e] += v[e - 1];
   float run = v[V - 1];
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float o = __shfl_up(run, d, 64);
-    if (lane >= d) run += o;
-  }
+  run = dpp_shifted_plus<0x111, 0xF>(run);   // row_shr:1
+  run = dpp_shifted_plus<0x112, 0xF>(run);   // row_shr:2
+  run = dpp_shifted_plus<0x114, 0xF>(run);   // row_shr:4
+  run = dpp_shifted_plus<0x118, 0xF>(run);   // row_shr:8
+  run = dpp_shifted_plus<0x142, 0xA>(run);   // row_bcast:15 into rows 1, 3
+  run = dpp_shifted_plus<0x143, 0xC>(run);   // row_bcast:31 into rows 2, 3
   const float before = run - v[V - 1];
 #pragma unroll
   for (int e = 0; e < V; ++e) v[e] += before;
@@ -217,7 +253,8 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   constexpr int M_ELEMS = P * LDB, E_ELEMS = Q * LDE;
   constexpr int U_ELEMS = M_ELEMS > E_ELEMS ? M_ELEMS : E_ELEMS;
   constexpr int SCH = P * N / 8 / NT;                    // 16-byte state chunks per thread
-  static_assert(Q % 32 == 0 && Q <= NT && N % 32 == 0 && QT <= NW && (P * N) % (8 * NT) == 0, "tiles");
+  static_assert(Q % 32 == 0 && Q <= NT && N % 32 == 0 && QT <= NW && (P * N) % (8 * NT) == 0 &&
+                (Q * P) % (8 * NT) == 0 && (Q * N) % (8 * NT) == 0, "tiles");
   __shared__ __attribute__((aligned(16))) __bf16 sB[Q * LDB], sC[Q * LDB], sX[Q * LDX], sDY[Q * LDX];
   __shared__ __attribute__((aligned(16))) __bf16 sU[U_ELEMS];   // E (Q x Q), then a state (P x N rows)
   __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], red[NW];
@@ -232,14 +269,26 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   const int64_t bl = int64_t(b) * L;
 
   for (int i = tid; i < Q; i += NT) s_tok[i] = so.canon(c * Q + i);
-  __syncthreads();
-  for (int i = tid; i < Q * (N / 8); i += NT) {
-    const int row = i / (N / 8), k8 = (i % (N / 8)) * 8;
-    const int64_t src = ((bl + s_tok[row]) * G + g) * N + k8;
-    *reinterpret_cast<bf16x8*>(sB + row * LDB + k8) = *reinterpret_cast<const bf16x8*>(B + src);
-    *reinterpret_cast<bf16x8*>(sC + row * LDB + k8) = *reinterpret_cast<const bf16x8*>(C + src);
+  lds_barrier();
+  {
+    // every load is issued before the first LDS store
+    constexpr int UB = Q * (N / 8) / NT;
+    bf16x8 vb[UB], vc[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int i = tid + u * NT, row = i / (N / 8), k8 = (i % (N / 8)) * 8;
+      const int64_t src = ((bl + s_tok[row]) * G + g) * N + k8;
+      vb[u] = *reinterpret_cast<const bf16x8*>(B + src);
+      vc[u] = *reinterpret_cast<const bf16x8*>(C + src);
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int i = tid + u * NT, row = i / (N / 8), k8 = (i % (N / 8)) * 8;
+      *reinterpret_cast<bf16x8*>(sB + row * LDB + k8) = vb[u];
+      *reinterpret_cast<bf16x8*>(sC + row * LDB + k8) = vc[u];
+    }
   }
-  __syncthreads();
+  lds_barrier();
   f32x4 gC[NTL], gB[NTL];   // dC, dB of row block `wave`, summed over the group's heads
 #pragma unroll
   for (int j = 0; j < NTL; ++j) { gC[j] = f32x4{0.f, 0.f, 0.f, 0.f}; gB[j] = f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -250,20 +299,33 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
     const float a_h = A[h];
-    __syncthreads();   // the previous head is done with every shared array
-    for (int i = tid; i < Q; i += NT) {
-      s_dt[i] = dt[(bl + s_tok[i]) * Hs + h];
-      s_fw[i] = 0.f;
-      s_bw[i] = 0.f;
-      s_sub[i] = 0.f;
+    lds_barrier();   // the previous head is done with every shared array
+    {
+      // dt, x and dy rows: every load is issued before the first LDS store
+      constexpr int UX = Q * (P / 8) / NT;
+      const float dt_i = tid < Q ? dt[(bl + s_tok[tid]) * Hs + h] : 0.f;
+      bf16x8 vx[UX], vd[UX];
+#pragma unroll
+      for (int u = 0; u < UX; ++u) {
+        const int i = tid + u * NT, row = i / (P / 8), k8 = (i % (P / 8)) * 8;
+        const int64_t src = ((bl + s_tok[row]) * Hs + h) * P + k8;
+        vx[u] = *reinterpret_cast<const bf16x8*>(x + src);
+        vd[u] = *reinterpret_cast<const bf16x8*>(dy + src);
+      }
+      if (tid < Q) {
+        s_dt[tid] = dt_i;
+        s_fw[tid] = 0.f;
+        s_bw[tid] = 0.f;
+        s_sub[tid] = 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < UX; ++u) {
+        const int i = tid + u * NT, row = i / (P / 8), k8 = (i % (P / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(sX + row * LDX + k8) = vx[u];
+        *reinterpret_cast<bf16x8*>(sDY + row * LDX + k8) = vd[u];
+      }
     }
-    for (int i = tid; i < Q * (P / 8); i += NT) {
-      const int row = i / (P / 8), k8 = (i % (P / 8)) * 8;
-      const int64_t src = ((bl + s_tok[row]) * Hs + h) * P + k8;
-      *reinterpret_cast<bf16x8*>(sX + row * LDX + k8) = *reinterpret_cast<const bf16x8*>(x + src);
-      *reinterpret_cast<bf16x8*>(sDY + row * LDX + k8) = *reinterpret_cast<const bf16x8*>(dy + src);
-    }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {   // chunk-local cumulative sums of dt*A, inclusive and exclusive
       constexpr int V = Q / 64;
       float v[V], d0[V];
@@ -276,16 +338,21 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         s_csx[V * lane + e] = v[e] - d0[e];
       }
     }
-    __syncthreads();
+    lds_barrier();
     const float cs_last = s_cs[Q - 1];
 
     // the four chunk-boundary states of this head (hf1, hb2, hb1, hf2); the
     // first one is fetched now, each next one while the previous is in use
     const int64_t st_off = (int64_t(c) * Hs + h) * int64_t(P) * N;
-    const __bf16* mats[4] = {st1 + st_off, st2 + per + st_off, st1 + per + st_off, st2 + st_off};
+    // (chosen by selects on the kernel's own pointers, so the loads stay
+    // global loads rather than generic ones, which the LDS waits would drain)
+    auto state = [&](int term) {
+      const __bf16* base = (term == 0 || term == 2) ? st1 : st2;
+      return reinterpret_cast<const bf16x8*>(base + ((term == 1 || term == 2) ? per : 0) + st_off);
+    };
     bf16x8 cur[SCH];
 #pragma unroll
-    for (int q = 0; q < SCH; ++q) cur[q] = reinterpret_cast<const bf16x8*>(mats[0])[tid + q * NT];
+    for (int q = 0; q < SCH; ++q) cur[q] = state(0)[tid + q * NT];
 
     // pairs inside the chunk: dy x^T tiles -> W (crossing sums) and E (dB, dC weights)
 #pragma unroll 1
@@ -325,17 +392,12 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         cbk += wb;
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int m = 8; m > 0; m >>= 1) {
-          rf[r] += __shfl_xor(rf[r], m, 16);
-          rb[r] += __shfl_xor(rb[r], m, 16);
-        }
-#pragma unroll
-      for (int m = 16; m < 64; m <<= 1) {
-        cf += __shfl_xor(cf, m, 64);
-        cbk += __shfl_xor(cbk, m, 64);
+      for (int r = 0; r < 4; ++r) {
+        rf[r] = sum16(rf[r]);
+        rb[r] = sum16(rb[r]);
       }
+      cf = sum_rows(cf);
+      cbk = sum_rows(cbk);
       if (lr < 4) {
         float f = rf[0], bk = rb[0];
 #pragma unroll
@@ -349,7 +411,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         atomicAdd(s_bw + s2, -cbk);
       }
     }
-    __syncthreads();   // E is complete
+    lds_barrier();   // E is complete
     // dC += E B (rows t = row block), dB += E^T C (rows s = row block)
     if (owns_rows) {
 #pragma unroll 1
@@ -369,7 +431,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     float k = 0.f;
 #pragma unroll 1
     for (int term = 0; term < 4; ++term) {
-      __syncthreads();   // E (and the previous state) is no longer read; the pair sums have landed
+      lds_barrier();   // E (and the previous state) is no longer read; the pair sums have landed
 #pragma unroll
       for (int q = 0; q < SCH; ++q) {
         const int i = tid + q * NT;
@@ -385,9 +447,9 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       }
       if (term < 3) {
 #pragma unroll
-        for (int q = 0; q < SCH; ++q) cur[q] = reinterpret_cast<const bf16x8*>(mats[term + 1])[tid + q * NT];
+        for (int q = 0; q < SCH; ++q) cur[q] = state(term + 1)[tid + q * NT];
       }
-      __syncthreads();
+      lds_barrier();
       if (!owns_rows) continue;
       const bool is_u = (term == 0 || term == 2);          // U terms: dy, C, dC; V terms: x, B, dB
       const __bf16* sa = is_u ? sDY : sX;
@@ -420,9 +482,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int m = 8; m > 0; m >>= 1) part[r] += __shfl_xor(part[r], m, 16);
+      for (int r = 0; r < 4; ++r) part[r] = sum16(part[r]);
       if (lr < 4) {
         const int t = r0 + 4 * lg + lr;
         float sum = part[0], sc = scale[0];
@@ -457,7 +517,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         s_bw[rb] = bk[e];
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < Q) R[(bl + s_tok[tid]) * Hs + h] = s_fw[tid] + s_bw[tid] - s_sub[tid] + k;
   }
 
@@ -492,41 +552,45 @@ __global__ __launch_bounds__(256) void ma_bwd_chunk_kernel(
   const int sub = threadIdx.x & 7, slot = threadIdx.x >> 3;
   const float two_d = 2.f * D[h], a_h = A[h];
   float da = 0.f, dd = 0.f;
-  for (int i = slot; i < Q; i += 32) {
-    const int64_t rh = (int64_t(b) * L + so.canon(c * Q + i)) * Hs + h;
-    const float d = dt[rh];
-    const int64_t off = rh * P + sub * 8;
-    float vx[8], vdy[8], vh[8], gx[8];
-    load8(x + off, vx);
-    load8(dy + off, vdy);
-    load8(yh + off, vh);
-    float xyh = 0.f, dyx = 0.f;
+  // Q / 32 passes (2 or 4: the chunk is 64 or 128 positions), taken two at a
+  // time with every load of both issued before either is used.
+  for (int i0 = slot; i0 < Q; i0 += 64) {
+    int64_t rh[2];
+    float d[2], r[2], vx[2][8], vdy[2][8], vh[2][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      xyh = fmaf(vx[e], vh[e], xyh);
-      dyx = fmaf(vdy[e], vx[e], dyx);
-      gx[e] = fmaf(d, vh[e], two_d * vdy[e]);
-    }
-    float4* o = reinterpret_cast<float4*>(dx + off);
-    o[0] = make_float4(gx[0], gx[1], gx[2], gx[3]);
-    o[1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
+    for (int u = 0; u < 2; ++u) rh[u] = (int64_t(b) * L + so.canon(c * Q + i0 + 32 * u)) * Hs + h;
 #pragma unroll
-    for (int m = 4; m > 0; m >>= 1) {
-      xyh += __shfl_xor(xyh, m, 8);
-      dyx += __shfl_xor(dyx, m, 8);
+    for (int u = 0; u < 2; ++u) {
+      d[u] = dt[rh[u]];
+      r[u] = sub == 0 ? R[rh[u]] : 0.f;
+      const int64_t off = rh[u] * P + sub * 8;
+      load8(x + off, vx[u]);
+      load8(dy + off, vdy[u]);
+      load8(yh + off, vh[u]);
     }
-    if (sub == 0) {
-      const float r = R[rh];
-      ddt[rh] = xyh + a_h * r;
-      da += d * r;
-      dd += 2.f * dyx;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float gx[8], xyh = 0.f, dyx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xyh = fmaf(vx[u][e], vh[u][e], xyh);
+        dyx = fmaf(vdy[u][e], vx[u][e], dyx);
+        gx[e] = fmaf(d[u], vh[u][e], two_d * vdy[u][e]);
+      }
+      float4* o = reinterpret_cast<float4*>(dx + rh[u] * P + sub * 8);
+      o[0] = make_float4(gx[0], gx[1], gx[2], gx[3]);
+      o[1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
+      xyh = sum8(xyh);
+      dyx = sum8(dyx);
+      if (sub == 0) {
+        ddt[rh[u]] = xyh + a_h * r[u];
+        da += d[u] * r[u];
+        dd += 2.f * dyx;
+      }
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    da += __shfl_xor(da, off, 64);
-    dd += __shfl_xor(dd, off, 64);
-  }
+  da = sum64(da);
+  dd = sum64(dd);
   if ((threadIdx.x & 63) == 0) {
     red[threadIdx.x >> 6][0] = da;
     red[threadIdx.x >> 6][1] = dd;

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   constexpr int QT = Q / 16, NTL = N / 16;
   constexpr int CBT = (QT * QT + NW - 1) / NW;           // Q x Q tiles per wave
   constexpr int M_ELEMS = P * LDB, E_ELEMS = Q * LDE;
-  constexpr int U_ELEMS = M_ELEMS > E_ELEMS ? M_ELEMS : E_ELEMS;
+  constexpr int U_ELEMS = 2 * M_ELEMS > E_ELEMS ? 2 * M_ELEMS : E_ELEMS;
   constexpr int SCH = P * N / 8 / NT;                    // 16-byte state chunks per thread
   static_assert(Q % 32 == 0 && Q <= NT && N % 32 == 0 && QT <= NW && (P * N) % (8 * NT) == 0 &&
                 (Q * P) % (8 * NT) == 0 && (Q * N) % (8 * NT) == 0, "tiles");
@@ -260,7 +260,8 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], red[NW];
   __shared__ int s_tok[Q];
   __bf16* const sE = sU;
-  __bf16* const sM = sU;
+  __bf16* const sM0 = sU;
+  __bf16* const sM1 = sU + M_ELEMS;
 
   const int c = blockIdx.x, g = blockIdx.y;
   const int hpg = Hs / G;
@@ -350,9 +351,12 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       const __bf16* base = (term == 0 || term == 2) ? st1 : st2;
       return reinterpret_cast<const bf16x8*>(base + ((term == 1 || term == 2) ? per : 0) + st_off);
     };
-    bf16x8 cur[SCH];
+    bf16x8 cur0[SCH], cur1[SCH];
 #pragma unroll
-    for (int q = 0; q < SCH; ++q) cur[q] = state(0)[tid + q * NT];
+    for (int q = 0; q < SCH; ++q) {
+      cur0[q] = state(0)[tid + q * NT];
+      cur1[q] = state(1)[tid + q * NT];
+    }
 
     // pairs inside the chunk: dy x^T tiles -> W (crossing sums) and E (dB, dC weights)
 #pragma unroll 1
@@ -426,31 +430,11 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       }
     }
 
-    // pairs with one end outside the chunk, and their share of dC, dB
-    bf16x8 keep[SCH];
+    // pairs with one end outside the chunk, and their share of dC, dB: the
+    // four terms in two rounds, each round the two states whose inner
+    // product enters K ((hf1, hb2), then (hb1, hf2)), staged side by side
     float k = 0.f;
-#pragma unroll 1
-    for (int term = 0; term < 4; ++term) {
-      lds_barrier();   // E (and the previous state) is no longer read; the pair sums have landed
-#pragma unroll
-      for (int q = 0; q < SCH; ++q) {
-        const int i = tid + q * NT;
-        const bf16x8 m8 = cur[q];
-        if (term == 0 || term == 2) {
-          keep[q] = m8;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) k = fmaf(static_cast<float>(keep[q][e]), static_cast<float>(m8[e]), k);
-        }
-        const int pp = (i * 8) / N, n = (i * 8) % N;
-        *reinterpret_cast<bf16x8*>(sM + pp * LDB + n) = m8;
-      }
-      if (term < 3) {
-#pragma unroll
-        for (int q = 0; q < SCH; ++q) cur[q] = state(term + 1)[tid + q * NT];
-      }
-      lds_barrier();
-      if (!owns_rows) continue;
+    auto do_term = [&](int term, const __bf16* sMt) {
       const bool is_u = (term == 0 || term == 2);          // U terms: dy, C, dC; V terms: x, B, dB
       const __bf16* sa = is_u ? sDY : sX;
       const __bf16* sv = is_u ? sC : sB;
@@ -473,7 +457,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         const int n0 = nt * 16;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < P / 32; ++kk) acc = mma(af[kk], tr_frag(sM, LDB, 32 * kk, n0, lane), acc);
+        for (int kk = 0; kk < P / 32; ++kk) acc = mma(af[kk], tr_frag(sMt, LDB, 32 * kk, n0, lane), acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           part[r] = fmaf(acc[r], static_cast<float>(sv[(r0 + 4 * lg + r) * LDB + n0 + lr]), part[r]);
@@ -495,6 +479,30 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         else if (term == 2) s_bw[t] += v;                  // U_b
         else { s_fw[t] += v; s_sub[t] += v; }              // V_b
       }
+    };
+#pragma unroll 1
+    for (int round = 0; round < 2; ++round) {
+      lds_barrier();   // E (and the previous states) are no longer read; the pair sums have landed
+#pragma unroll
+      for (int q = 0; q < SCH; ++q) {
+        const int i = tid + q * NT;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k = fmaf(static_cast<float>(cur0[q][e]), static_cast<float>(cur1[q][e]), k);
+        const int pp = (i * 8) / N, n = (i * 8) % N;
+        *reinterpret_cast<bf16x8*>(sM0 + pp * LDB + n) = cur0[q];
+        *reinterpret_cast<bf16x8*>(sM1 + pp * LDB + n) = cur1[q];
+      }
+      if (round == 0) {
+#pragma unroll
+        for (int q = 0; q < SCH; ++q) {
+          cur0[q] = state(2)[tid + q * NT];
+          cur1[q] = state(3)[tid + q * NT];
+        }
+      }
+      lds_barrier();
+      if (!owns_rows) continue;
+      do_term(2 * round, sM0);
+      do_term(2 * round + 1, sM1);
     }
     k = __expf(cs_last) * block_sum512(k, red);   // its barriers also order the boundary terms before the scans
 

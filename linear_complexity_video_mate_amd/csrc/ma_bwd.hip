@@ -358,50 +358,67 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       cur1[q] = state(1)[tid + q * NT];
     }
 
-    // pairs inside the chunk: dy x^T tiles -> W (crossing sums) and E (dB, dC weights)
-#pragma unroll 1
-    for (int q = 0; q < CBT; ++q) {
-      const int tile = wave + q * NW;
-      if (tile >= QT * QT) break;
-      const int t0 = (tile / QT) * 16, s0 = (tile % QT) * 16;
-      f32x4 cb = {0.f, 0.f, 0.f, 0.f}, dx = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < N; k += 32) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sC + (t0 + lr) * LDB + k + 8 * lg);
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(sB + (s0 + lr) * LDB + k + 8 * lg);
-        cb = mma(a, v, cb);
-      }
-#pragma unroll
-      for (int k = 0; k < P; k += 32) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sDY + (t0 + lr) * LDX + k + 8 * lg);
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(sX + (s0 + lr) * LDX + k + 8 * lg);
-        dx = mma(a, v, dx);
-      }
-      const int s2 = s0 + lr;
-      const float ds = s_dt[s2], cs_s = s_cs[s2], csx_s = s_csx[s2];
-      float rf[4], rb[4], cf = 0.f, cbk = 0.f;
+    // pairs inside the chunk: dy x^T tiles -> W (crossing sums) and E (dB, dC
+    // weights).  Wave w keeps the t rows of tile w mod QT, so its row sums of
+    // W stay in registers until the end; it walks the s tiles from a start
+    // that differs from the other waves', so their column sums land on
+    // different LDS words at any one time.
+    {
+      const int t0 = (wave % QT) * 16;
+      float cs_t[4], csx_t[4], rf[4] = {0.f, 0.f, 0.f, 0.f}, rb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 4 * lg + r;
-        const float df = s2 <= t ? __expf(s_cs[t] - cs_s) : 0.f;
-        const float db = s2 >= t ? __expf(csx_s - s_csx[t]) : 0.f;
-        const float e = ds * dx[r];
-        sE[t * LDE + s2] = static_cast<__bf16>(e * (df + db));
-        const float v = e * cb[r];
-        const float wf = s2 < t ? df * v : 0.f;
-        const float wb = s2 > t ? db * v : 0.f;
-        rf[r] = wf;
-        rb[r] = wb;
-        cf += wf;
-        cbk += wb;
+        cs_t[r] = s_cs[t0 + 4 * lg + r];
+        csx_t[r] = s_csx[t0 + 4 * lg + r];
+      }
+#pragma unroll 1
+      for (int q = 0; q < CBT; ++q) {
+        const int tile = wave + q * NW;
+        if (tile >= QT * QT) break;
+        const int s0 = ((tile / QT + wave % QT) % QT) * 16;
+        f32x4 cb = {0.f, 0.f, 0.f, 0.f}, dx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < N; k += 32) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sC + (t0 + lr) * LDB + k + 8 * lg);
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(sB + (s0 + lr) * LDB + k + 8 * lg);
+          cb = mma(a, v, cb);
+        }
+#pragma unroll
+        for (int k = 0; k < P; k += 32) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sDY + (t0 + lr) * LDX + k + 8 * lg);
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(sX + (s0 + lr) * LDX + k + 8 * lg);
+          dx = mma(a, v, dx);
+        }
+        const int s2 = s0 + lr;
+        const float ds = s_dt[s2], cs_s = s_cs[s2], csx_s = s_csx[s2];
+        float cf = 0.f, cbk = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + 4 * lg + r;
+          const float df = s2 <= t ? __expf(cs_t[r] - cs_s) : 0.f;
+          const float db = s2 >= t ? __expf(csx_s - csx_t[r]) : 0.f;
+          const float e = ds * dx[r];
+          sE[t * LDE + s2] = static_cast<__bf16>(e * (df + db));
+          const float v = e * cb[r];
+          const float wf = s2 < t ? df * v : 0.f;
+          const float wb = s2 > t ? db * v : 0.f;
+          rf[r] += wf;
+          rb[r] += wb;
+          cf += wf;
+          cbk += wb;
+        }
+        cf = sum_rows(cf);
+        cbk = sum_rows(cbk);
+        if (lg == 0) {
+          atomicAdd(s_fw + s2, -cf);
+          atomicAdd(s_bw + s2, -cbk);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         rf[r] = sum16(rf[r]);
         rb[r] = sum16(rb[r]);
       }
-      cf = sum_rows(cf);
-      cbk = sum_rows(cbk);
       if (lr < 4) {
         float f = rf[0], bk = rb[0];
 #pragma unroll
@@ -409,10 +426,6 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
           if (lr == r) { f = rf[r]; bk = rb[r]; }
         atomicAdd(s_fw + t0 + 4 * lg + lr, f);
         atomicAdd(s_bw + t0 + 4 * lg + lr, bk);
-      }
-      if (lg == 0) {
-        atomicAdd(s_fw + s2, -cf);
-        atomicAdd(s_bw + s2, -cbk);
       }
     }
     lds_barrier();   // E is complete

@@ -556,70 +556,79 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   }
 }
 
-// Per (chunk, head, batch element), head size 64: dx = dt yhat + 2 D dy,
-// ddt = x . yhat + A R, and this chunk's share of dA = sum dt R and dD =
-// 2 sum dy . x, with yhat = (M_f^T + M_b^T) dy / dt and R the crossing sums.
-// Eight lanes share a token's 128-byte rows (16 bytes each), so every load
-// and store of a wave covers eight whole rows; 256 threads take 32 scan
-// positions per pass.
-__global__ __launch_bounds__(256) void ma_bwd_chunk_kernel(
+// Per token and head (head size 64), in canonical order (nothing here
+// depends on the scan order or the chunks):
+//   dx = dt yhat + 2 D dy,  ddt = x . yhat + A R,
+// and the shares of dA = sum dt R and dD = 2 sum dy . x, with yhat =
+// (M_f^T + M_b^T) dy / dt and R the crossing sums.  A workgroup takes
+// kTokRows consecutive token rows and a slice of 32 heads: eight lanes share
+// a head's 128-byte row (16 bytes each), so with 32 heads or more the
+// workgroup reads 4 KiB of contiguous row per token.  A lane's head is
+// fixed, so its dA, dD shares stay in registers until one atomic per head
+// and workgroup.  kTokUnroll tokens' loads are issued before any is used.
+constexpr int kTokRows = 64, kTokUnroll = 4;
+__global__ __launch_bounds__(256) void ma_bwd_token_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ dy, const float* __restrict__ dt,
     const float* __restrict__ A, const float* __restrict__ D, const __bf16* __restrict__ yh,
-    const float* __restrict__ R, ScanOrder so, int L, int Q, int Hs, float* __restrict__ dx,
-    float* __restrict__ ddt, float* __restrict__ dA, float* __restrict__ dD) {
-  constexpr int P = 64;
-  __shared__ float red[8][2];
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int sub = threadIdx.x & 7, slot = threadIdx.x >> 3;
-  const float two_d = 2.f * D[h], a_h = A[h];
+    const float* __restrict__ R, int64_t rows, int Hs, float* __restrict__ dx, float* __restrict__ ddt,
+    float* __restrict__ dA, float* __restrict__ dD) {
+  constexpr int P = 64, U = kTokUnroll;
+  const int sub = threadIdx.x & 7;
+  const int h = int(blockIdx.y) * 32 + int(threadIdx.x >> 3);
+  const bool active = h < Hs;   // whole groups of eight lanes
+  const int hc = active ? h : 0;
+  const float two_d = 2.f * D[hc], a_h = A[hc];
+  const int64_t r0 = int64_t(blockIdx.x) * kTokRows;
+  const int nr = int(rows - r0 < kTokRows ? rows - r0 : kTokRows);
   float da = 0.f, dd = 0.f;
-  // Q / 32 passes (2 or 4: the chunk is 64 or 128 positions), taken two at a
-  // time with every load of both issued before either is used.
-  for (int i0 = slot; i0 < Q; i0 += 64) {
-    int64_t rh[2];
-    float d[2], r[2], vx[2][8], vdy[2][8], vh[2][8];
+  for (int i0 = 0; i0 < nr; i0 += U) {
+    int64_t rh[U];
+    bool ok[U];
+    float d[U], r[U];
+    bf16x8 bx[U], bdy[U], bh[U];   // kept in bf16 until used
 #pragma unroll
-    for (int u = 0; u < 2; ++u) rh[u] = (int64_t(b) * L + so.canon(c * Q + i0 + 32 * u)) * Hs + h;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      d[u] = dt[rh[u]];
-      r[u] = sub == 0 ? R[rh[u]] : 0.f;
-      const int64_t off = rh[u] * P + sub * 8;
-      load8(x + off, vx[u]);
-      load8(dy + off, vdy[u]);
-      load8(yh + off, vh[u]);
+    for (int u = 0; u < U; ++u) {
+      ok[u] = active && i0 + u < nr;
+      rh[u] = (r0 + i0 + u) * Hs + hc;
+      d[u] = r[u] = 0.f;
+      bx[u] = bdy[u] = bh[u] = bf16x8{};
+      if (ok[u]) {
+        d[u] = dt[rh[u]];
+        r[u] = R[rh[u]];
+        const int64_t off = rh[u] * P + sub * 8;
+        bx[u] = *reinterpret_cast<const bf16x8*>(x + off);
+        bdy[u] = *reinterpret_cast<const bf16x8*>(dy + off);
+        bh[u] = *reinterpret_cast<const bf16x8*>(yh + off);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < U; ++u) {
       float gx[8], xyh = 0.f, dyx = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        xyh = fmaf(vx[u][e], vh[u][e], xyh);
-        dyx = fmaf(vdy[u][e], vx[u][e], dyx);
-        gx[e] = fmaf(d[u], vh[u][e], two_d * vdy[u][e]);
+        const float vx = static_cast<float>(bx[u][e]), vdy = static_cast<float>(bdy[u][e]),
+                    vh = static_cast<float>(bh[u][e]);
+        xyh = fmaf(vx, vh, xyh);
+        dyx = fmaf(vdy, vx, dyx);
+        gx[e] = fmaf(d[u], vh, two_d * vdy);
       }
-      float4* o = reinterpret_cast<float4*>(dx + rh[u] * P + sub * 8);
-      o[0] = make_float4(gx[0], gx[1], gx[2], gx[3]);
-      o[1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
+      if (ok[u]) {
+        float4* o = reinterpret_cast<float4*>(dx + rh[u] * P + sub * 8);
+        o[0] = make_float4(gx[0], gx[1], gx[2], gx[3]);
+        o[1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
+      }
       xyh = sum8(xyh);
       dyx = sum8(dyx);
-      if (sub == 0) {
+      if (ok[u] && sub == 0) {
         ddt[rh[u]] = xyh + a_h * r[u];
         da += d[u] * r[u];
         dd += 2.f * dyx;
       }
     }
   }
-  da = sum64(da);
-  dd = sum64(dd);
-  if ((threadIdx.x & 63) == 0) {
-    red[threadIdx.x >> 6][0] = da;
-    red[threadIdx.x >> 6][1] = dd;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    atomicAdd(dA + h, red[0][0] + red[1][0] + red[2][0] + red[3][0]);
-    atomicAdd(dD + h, red[0][1] + red[1][1] + red[2][1] + red[3][1]);
+  if (active && sub == 0) {
+    atomicAdd(dA + h, da);
+    atomicAdd(dD + h, dd);
   }
 }
 
@@ -738,7 +747,6 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   // crossing sums, then ddt, dx, dA, dD
   {
     const dim3 cgrid{unsigned(nc), unsigned(G), 1u};
-    const dim3 grid{unsigned(nc), unsigned(Hs), unsigned(shape->batch)};
     const WsLayout lay = ws_layout(shape);
     const int64_t per = int64_t(nc) * Hs * P * N;   // one direction's scan states
     const __bf16* st1 = reinterpret_cast<const __bf16*>(ws + w.scan1 + lay.states);
@@ -763,8 +771,9 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
         return LINGEN_ERR_UNSUPPORTED;
       LINGEN_LAUNCHED();
     }
-    ma_bwd_chunk_kernel<<<grid, 256, 0, stream>>>(xb, dyb, dt, A, D, static_cast<const __bf16*>(at(w.yh)), atf(w.R),
-                                                 so, L, Q, Hs, dx, ddt, dA, dD);
+    const dim3 tgrid{unsigned((rows + kTokRows - 1) / kTokRows), unsigned((Hs + 31) / 32), 1u};
+    ma_bwd_token_kernel<<<tgrid, 256, 0, stream>>>(xb, dyb, dt, A, D, static_cast<const __bf16*>(at(w.yh)), atf(w.R),
+                                                   rows, Hs, dx, ddt, dA, dD);
     LINGEN_LAUNCHED();
   }
 #undef LINGEN_TRY

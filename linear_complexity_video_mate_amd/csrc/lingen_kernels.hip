@@ -450,7 +450,7 @@ struct StateCfg {
 constexpr int kLptX = 2, kLptB = 2;
 // BIDIR = false: the forward direction's chunk states only (a scan whose
 // backward direction has parameters of its own).
-template <typename TS, int P, int N, int Q, bool BIDIR = true>
+template <typename TS, int P, int N, int Q, bool BIDIR = true, int WM = kWeightDt>
 __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
                                                               const float* __restrict__ A, const TS* __restrict__ B,
                                                               RmsMap rms, int Hs, int G, int hg, int n_chunks,
@@ -509,11 +509,18 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
     const int h = h0 + hh;
     const float cum_end = cs.cum[hh][Q - 1];
     const float a2 = A[h] * kLog2e;
+    // token weights by WeightMode (the weighted x^T of each direction)
     for (int i = tid; i < Q; i += NTHR) {
       const float d = cs.dt[hh][i];
       const float cum_i = cs.cum[hh][i];
-      sW[0][i] = fast_exp2(cum_end - cum_i) * d;
-      sW[1][i] = fast_exp2(cum_i - d * a2) * d;     // exc_i = cum_i - a_i
+      if constexpr (WM == kWeightAdjoint) {
+        sW[0][i] = fast_exp2(cum_end - cum_i + d * a2);   // e^{cum_end - exc_i}
+        sW[1][i] = fast_exp2(cum_i);                      // e^{exc_i + a_i}
+      } else {
+        const float w = WM == kWeightUnit ? 1.f : d;
+        sW[0][i] = fast_exp2(cum_end - cum_i) * w;
+        sW[1][i] = fast_exp2(cum_i - d * a2) * w;     // exc_i = cum_i - a_i
+      }
     }
     if (tid == 0) decay[int64_t(c) * Hs + h] = fast_exp2(cum_end);
     lds_barrier();
@@ -672,7 +679,9 @@ struct OutCfg {
 // BIDIR = false: the forward direction alone (lower triangle and diagonal
 // weight 1, the forward inter-chunk term, D x once), for a scan whose
 // backward direction has parameters of its own; ACC adds the result to y.
-template <typename TS, int P, int N, int Q, bool BIDIR = true, bool ACC = false>
+// UNIT: the input is already dt x (kWeightUnit): no dt factor on the
+// tokens, and no skip term (D is not read).
+template <typename TS, int P, int N, int Q, bool BIDIR = true, bool ACC = false, bool UNIT = false>
 __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_kernel(
     const TS* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const TS* __restrict__ B,
     const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int G, int hg, int n_chunks,
@@ -793,8 +802,9 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       const float ref_lo = exc[ts], ref_hi = cum[te];
       for (int s = lane; s < Q; s += 64) {
         float vs = 0.f;
-        if (s < ts) vs = fast_exp2(ref_lo - cum[s]) * cs.dt[hh][s];
-        else if (s > te) vs = fast_exp2(exc[s] - ref_hi) * cs.dt[hh][s];
+        const float w = UNIT ? 1.f : cs.dt[hh][s];
+        if (s < ts) vs = fast_exp2(ref_lo - cum[s]) * w;
+        else if (s > te) vs = fast_exp2(exc[s] - ref_hi) * w;
         sV[wave][s] = vs;
       }
     }
@@ -825,7 +835,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
           const int s = sb + r;
           const float arg = s < t ? cum_t - cv[r] : xv[r] - exc_t;
           const float lam = s == t ? (BIDIR ? 2.f : 1.f) : (BIDIR || s < t ? fast_exp2(arg) : 0.f);
-          mv[r] = to_f32(g[st][r]) * lam * dv[r];
+          mv[r] = to_f32(g[st][r]) * lam * (UNIT ? 1.f : dv[r]);
         }
       } else {
         const float4 v4 = *reinterpret_cast<const float4*>(&sV[wave][sb]);
@@ -886,7 +896,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 
     // Inter-chunk terms, the skip, and the store.
     const float ef = fast_exp2(cum_t), eb = BIDIR ? fast_exp2(cum[Q - 1] - exc_t) : 0.f;
-    const float twoD = (BIDIR ? 2.f : 1.f) * D[h];
+    const float twoD = UNIT ? 0.f : (BIDIR ? 2.f : 1.f) * D[h];
     // bf16 rows of 64 owned by one wave: the four p-tiles are stored together
     // in 16-byte pieces (see below).
     constexpr bool kP16 = kBf16 && Cfg::PT == 4 && Cfg::P_PER == 4 && Cfg::WPW == 1;
@@ -1382,7 +1392,7 @@ int launch_review(const lingen_mate_shape* s, const TS* x, const float* dt, cons
 
 // Phase A + state pass (+ review state) for one batch element.  BIDIR =
 // false: the forward direction of the (possibly reversed, rev = 1) order only.
-template <typename TS, int P, int N, int Q, bool BIDIR = true>
+template <typename TS, int P, int N, int Q, bool BIDIR = true, int WM = kWeightDt>
 int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float* dt, const float* A, const TS* B,
                   char* ws, hipStream_t st, const hipEvent_t* ev = nullptr, int rev = 0) {
   const WsLayout lay = ws_layout(s);
@@ -1399,7 +1409,7 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
     h0 = reinterpret_cast<const float*>(ws + lay.review_h);
   }
   if (int rc = mark(ev, 1, st)) return rc;
-  ssd_chunk_state_kernel<TS, P, N, Q, BIDIR><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(
+  ssd_chunk_state_kernel<TS, P, N, Q, BIDIR, WM><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(
       x, dt, A, B, make_rms(s, mode, rev), Hs, s->ngroups, hg, nc, states, decay);
   if (hip_status()) return LINGEN_ERR_HIP;
   if (int rc = mark(ev, 2, st)) return rc;
@@ -1444,8 +1454,9 @@ int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char
 
 // MA branch with a parameter set per direction: the forward direction of
 // the scan order with af, then the forward direction of the reversed order
-// (the backward scan) with ab, added to the first result.
-template <typename TS, int P, int N, int Q>
+// (the backward scan) with ab, added to the first result.  UNIT: the inputs
+// already carry their dt factor (kWeightUnit; no skip term).
+template <typename TS, int P, int N, int Q, bool UNIT = false>
 int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const Args& ab, void* y, char* ws,
                    hipStream_t st) {
   const int L = int(tokens(s));
@@ -1464,13 +1475,14 @@ int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const A
       const int64_t bc = int64_t(b) * L * s->ngroups * N * eb;
       const TS* B = reinterpret_cast<const TS*>(static_cast<const char*>(a.B) + bc);
       const TS* C = reinterpret_cast<const TS*>(static_cast<const char*>(a.C) + bc);
-      if (int rc = launch_states<TS, P, N, Q, false>(s, mode, x, dt, a.A, B, ws, st, nullptr, dir)) return rc;
+      constexpr int WM = UNIT ? kWeightUnit : kWeightDt;
+      if (int rc = launch_states<TS, P, N, Q, false, WM>(s, mode, x, dt, a.A, B, ws, st, nullptr, dir)) return rc;
       const TS* states = reinterpret_cast<const TS*>(ws + lay.states);
       if (dir == 0)
-        ssd_chunk_out_kernel<TS, P, N, Q, false, false><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
+        ssd_chunk_out_kernel<TS, P, N, Q, false, false, UNIT><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
             x, dt, a.A, B, C, a.D, make_rms(s, mode, 0), Hs, s->ngroups, hg, nc, states, yb);
       else
-        ssd_chunk_out_kernel<TS, P, N, Q, false, true><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
+        ssd_chunk_out_kernel<TS, P, N, Q, false, true, UNIT><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
             x, dt, a.A, B, C, a.D, make_rms(s, mode, 1), Hs, s->ngroups, hg, nc, states, yb);
       if (hip_status()) return LINGEN_ERR_HIP;
     }
@@ -1478,12 +1490,13 @@ int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const A
   return LINGEN_OK;
 }
 
+template <bool UNIT>
 int dispatch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const Args& ab, void* y, char* ws,
                      hipStream_t st) {
   switch (scan_family(s)) {
-    case SCAN_F32_P32_N16_Q16: return launch_ma_dirs<float, 32, 16, 16>(s, mode, af, ab, y, ws, st);
-    case SCAN_BF16_P64_N64_Q64: return launch_ma_dirs<__bf16, 64, 64, 64>(s, mode, af, ab, y, ws, st);
-    case SCAN_BF16_P64_N128_Q128: return launch_ma_dirs<__bf16, 64, 128, 128>(s, mode, af, ab, y, ws, st);
+    case SCAN_F32_P32_N16_Q16: return launch_ma_dirs<float, 32, 16, 16, UNIT>(s, mode, af, ab, y, ws, st);
+    case SCAN_BF16_P64_N64_Q64: return launch_ma_dirs<__bf16, 64, 64, 64, UNIT>(s, mode, af, ab, y, ws, st);
+    case SCAN_BF16_P64_N128_Q128: return launch_ma_dirs<__bf16, 64, 128, 128, UNIT>(s, mode, af, ab, y, ws, st);
     default: return LINGEN_ERR_UNSUPPORTED;
   }
 }
@@ -1570,22 +1583,43 @@ namespace lingen {
 // Chunk states and scan states of one batch element into the workspace (at
 // ws_layout().states, [2][n_chunks][Hs][P][N] in the storage dtype: the
 // state entering each chunk of the forward scan, then of the reverse scan).
+// wmode: kWeightDt or kWeightAdjoint.
 int scan_states_one(const lingen_mate_shape* s, int mode, const void* xb, const float* dtb, const float* A,
-                    const void* Bb, void* workspace, hipStream_t stream) {
+                    const void* Bb, void* workspace, hipStream_t stream, int wmode) {
   char* ws = static_cast<char*>(workspace);
+  if (wmode != kWeightDt && wmode != kWeightAdjoint) return LINGEN_ERR_UNSUPPORTED;
+  const bool adj = wmode == kWeightAdjoint;
   switch (scan_family(s)) {
-    case SCAN_F32_P32_N16_Q16:
-      return launch_states<float, 32, 16, 16>(s, mode, static_cast<const float*>(xb), dtb, A,
-                                              static_cast<const float*>(Bb), ws, stream);
-    case SCAN_BF16_P64_N64_Q64:
-      return launch_states<__bf16, 64, 64, 64>(s, mode, static_cast<const __bf16*>(xb), dtb, A,
-                                               static_cast<const __bf16*>(Bb), ws, stream);
-    case SCAN_BF16_P64_N128_Q128:
-      return launch_states<__bf16, 64, 128, 128>(s, mode, static_cast<const __bf16*>(xb), dtb, A,
-                                                 static_cast<const __bf16*>(Bb), ws, stream);
+    case SCAN_F32_P32_N16_Q16: {
+      const float* x = static_cast<const float*>(xb);
+      const float* B = static_cast<const float*>(Bb);
+      return adj ? launch_states<float, 32, 16, 16, true, kWeightAdjoint>(s, mode, x, dtb, A, B, ws, stream)
+                 : launch_states<float, 32, 16, 16>(s, mode, x, dtb, A, B, ws, stream);
+    }
+    case SCAN_BF16_P64_N64_Q64: {
+      const __bf16* x = static_cast<const __bf16*>(xb);
+      const __bf16* B = static_cast<const __bf16*>(Bb);
+      return adj ? launch_states<__bf16, 64, 64, 64, true, kWeightAdjoint>(s, mode, x, dtb, A, B, ws, stream)
+                 : launch_states<__bf16, 64, 64, 64>(s, mode, x, dtb, A, B, ws, stream);
+    }
+    case SCAN_BF16_P64_N128_Q128: {
+      const __bf16* x = static_cast<const __bf16*>(xb);
+      const __bf16* B = static_cast<const __bf16*>(Bb);
+      return adj ? launch_states<__bf16, 64, 128, 128, true, kWeightAdjoint>(s, mode, x, dtb, A, B, ws, stream)
+                 : launch_states<__bf16, 64, 128, 128>(s, mode, x, dtb, A, B, ws, stream);
+    }
     default:
       return LINGEN_ERR_UNSUPPORTED;
   }
+}
+
+int ma_fwd_dirs_unit(const lingen_mate_shape* s, int mode, const void* u_f, const float* dt_f, const void* B_f,
+                     const void* C_f, const void* u_b, const float* dt_b, const void* B_b, const void* C_b,
+                     const float* A, void* y, void* workspace, hipStream_t stream) {
+  if (s->n_review != 0) return LINGEN_ERR_UNSUPPORTED;
+  Args af{u_f, dt_f, A, B_f, C_f, nullptr, nullptr, nullptr, nullptr};
+  Args ab{u_b, dt_b, A, B_b, C_b, nullptr, nullptr, nullptr, nullptr};
+  return dispatch_ma_dirs<true>(s, mode, af, ab, y, static_cast<char*>(workspace), stream);
 }
 }  // namespace lingen
 
@@ -1633,7 +1667,7 @@ int lingen_ssd_chunk_states(const void* x, const float* dt, const float* A, cons
     const char* xb = static_cast<const char*>(x) + b * L * Hs * P * eb;
     const float* dtb = dt + b * L * Hs;
     const char* Bb = static_cast<const char*>(B) + b * L * s->ngroups * N * eb;
-    if (int rc = scan_states_one(s, mode, xb, dtb, A, Bb, ws, stream)) return rc;
+    if (int rc = scan_states_one(s, mode, xb, dtb, A, Bb, ws, stream, kWeightDt)) return rc;
     const unsigned blocks = unsigned((per + 255) / 256);
     if (s->dtype == LINGEN_BF16) {
       const __bf16* st = reinterpret_cast<const __bf16*>(ws + lay.states);
@@ -1671,7 +1705,7 @@ int lingen_ma_fwd_dirs(const void* x_f, const float* dt_f, const float* A_f, con
   if (shape->n_review != 0) return LINGEN_ERR_UNSUPPORTED;
   Args af{x_f, dt_f, A_f, B_f, C_f, D_f, nullptr, nullptr, nullptr};
   Args ab{x_b, dt_b, A_b, B_b, C_b, D_b, nullptr, nullptr, nullptr};
-  return dispatch_ma_dirs(shape, mode, af, ab, y_ma, static_cast<char*>(workspace), stream);
+  return dispatch_ma_dirs<false>(shape, mode, af, ab, y_ma, static_cast<char*>(workspace), stream);
 }
 
 int lingen_te_fwd(const void* q, const void* k, const void* v, int32_t shifted, const lingen_mate_shape* shape,

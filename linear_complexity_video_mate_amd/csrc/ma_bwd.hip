@@ -9,15 +9,17 @@
 // gradient is built from scans the library already runs, with transformed
 // operands, plus the kernels of this file:
 //   * M^T of one direction is the opposite direction's scan with dt moved
-//     by one scan position (so the decays cover the right tokens), the input
-//     divided by that moved dt and B, C exchanged: dx = dt (M_f^T + M_b^T) dy
-//     / dt + 2 D dy;
+//     by one scan position (so the decays cover the right tokens) and B, C
+//     exchanged, fed dy as an input that already carries its dt factor:
+//     dx = dt (M_f^T + M_b^T) dy / dt + 2 D dy;
 //   * dB and dC are, per chunk, products of the same chunk-local matrices the
 //     crossing sums need (E = dt (dy x^T) weighted by the decays) with C and
 //     B, plus products of the chunk-boundary states with x and dy;
 //   * the chunk-boundary adjoint states are the scan states of x' = dy
-//     exp(dt A) / dt with C in place of B (read in bf16 from the chunk-state
-//     pass's workspace, one batch element at a time);
+//     exp(dt A) / dt with C in place of B, taken from dy with the token
+//     weights exp(dt A) in place of dt (x' itself is never formed; read in
+//     bf16 from the chunk-state pass's workspace, one batch element at a
+//     time);
 //   * ddt and dA need, at every position r, the crossing sum
 //     R_r = sum_{s < r <= t} W_ts: the pairs inside r's chunk come from the
 //     chunk's W (row minus column sums, then a suffix sum), the pairs with
@@ -45,84 +47,32 @@ constexpr int kThreads = 256;
 
 unsigned blocks_for(int64_t n) { return unsigned((n + kThreads - 1) / kThreads); }
 
-__device__ __forceinline__ void load8(const __bf16* p, float (&v)[8]) {
-  const bf16x8 u = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(u[e]);
-}
-__device__ __forceinline__ void store8(__bf16* p, const float (&v)[8]) {
-  bf16x8 u;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) u[e] = static_cast<__bf16>(v[e]);
-  *reinterpret_cast<bf16x8*>(p) = u;
-}
-
-// Zero three arrays of n floats each (the accumulated gradients dA, dD and a
-// zero D for the transposed scans).
-__global__ __launch_bounds__(kThreads) void zero_floats_kernel(float* __restrict__ a, float* __restrict__ b,
-                                                               float* __restrict__ c, int n) {
+// Zero two arrays of n floats each (the accumulated gradients dA, dD).
+__global__ __launch_bounds__(kThreads) void zero_floats_kernel(float* __restrict__ a, float* __restrict__ b, int n) {
   for (int i = threadIdx.x; i < n; i += kThreads) {
     a[i] = 0.f;
     b[i] = 0.f;
-    c[i] = 0.f;
   }
 }
 
-// x' = dy * exp(dt A) / dt, for rows of Hs heads x P (P a multiple of 8).
-__global__ __launch_bounds__(kThreads) void adjoint_input_kernel(const __bf16* __restrict__ dy,
-                                                                 const float* __restrict__ dt,
-                                                                 const float* __restrict__ A, int64_t rows, int Hs,
-                                                                 int P, __bf16* __restrict__ out) {
-  const int upr = P / 8;
-  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= rows * Hs * upr) return;
-  const int64_t rh = i / upr;              // row * Hs + head
-  const int h = int(rh % Hs);
-  const float d = dt[rh];
-  const float s = __expf(d * A[h]) / d;
-  float v[8];
-  load8(dy + i * 8, v);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] *= s;
-  store8(out + i * 8, v);
-}
-
-// dt moved by one scan position each way, and dy divided by it:
-//   dt_next at the token of scan position r = dt at position r+1 (the last
-//   position keeps its own), dt_prev = dt at position r-1 (the first keeps
-//   its own); dy_next = dy / dt_next, dy_prev = dy / dt_prev.
-// One thread per (batch, scan position, head, 8 elements of P).
-__global__ __launch_bounds__(kThreads) void shifted_dt_kernel(const __bf16* __restrict__ dy,
-                                                              const float* __restrict__ dt, ScanOrder so, int L,
-                                                              int Hs, int P, int64_t total,
-                                                              float* __restrict__ dt_next,
-                                                              float* __restrict__ dt_prev,
-                                                              __bf16* __restrict__ dy_next,
-                                                              __bf16* __restrict__ dy_prev) {
-  const int upr = P / 8;
+// dt moved by one scan position each way: dt_next at the token of scan
+// position r = dt at position r+1 (the last position keeps its own),
+// dt_prev = dt at position r-1 (the first keeps its own).  One thread per
+// (batch, scan position, head).
+__global__ __launch_bounds__(kThreads) void shifted_dt_kernel(const float* __restrict__ dt, ScanOrder so, int L,
+                                                              int Hs, int64_t total, float* __restrict__ dt_next,
+                                                              float* __restrict__ dt_prev) {
   const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= total) return;
-  const int unit = int(i % upr);
-  const int h = int((i / upr) % Hs);
-  const int64_t br = i / (int64_t(upr) * Hs);   // batch * L + scan position
+  const int h = int(i % Hs);
+  const int64_t br = i / Hs;                    // batch * L + scan position
   const int r = int(br % L);
   const int64_t base = br - r;                  // batch * L
   const int64_t c = base + so.canon(r);
   const int64_t cn = base + so.canon(r + 1 < L ? r + 1 : r);
   const int64_t cp = base + so.canon(r > 0 ? r - 1 : r);
-  const float dn = dt[cn * Hs + h], dp = dt[cp * Hs + h];
-  if (unit == 0) {
-    dt_next[c * Hs + h] = dn;
-    dt_prev[c * Hs + h] = dp;
-  }
-  const int64_t off = (c * Hs + h) * P + unit * 8;
-  float v[8], a[8], b[8];
-  load8(dy + off, v);
-  const float rn = 1.f / dn, rp = 1.f / dp;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) { a[e] = v[e] * rn; b[e] = v[e] * rp; }
-  store8(dy_next + off, a);
-  store8(dy_prev + off, b);
+  dt_next[c * Hs + h] = dt[cn * Hs + h];
+  dt_prev[c * Hs + h] = dt[cp * Hs + h];
 }
 
 constexpr int kCrossThreads = 512;
@@ -634,8 +584,7 @@ __global__ __launch_bounds__(256) void ma_bwd_token_kernel(
 
 // Byte offsets inside the caller's workspace.
 struct BwdWs {
-  size_t scan1, scan2, xprime, dzero, dt_next, dt_prev, dy_next, dy_prev, R, yh,
- total;
+  size_t scan1, scan2, dt_next, dt_prev, R, yh, total;
 };
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
@@ -649,12 +598,8 @@ int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
   w->scan1 = take(ws_main);
   w->scan2 = take(ws_main);
-  w->xprime = take(rows * hs * P * 2);
-  w->dzero = take(hs * 4);
   w->dt_next = take(rows * hs * 4);
   w->dt_prev = take(rows * hs * 4);
-  w->dy_next = take(rows * hs * P * 2);
-  w->dy_prev = take(rows * hs * P * 2);
   w->R = take(rows * hs * 4);
   w->yh = take(rows * hs * P * 2);
   w->total = off;
@@ -705,7 +650,6 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   const int L = int(tokens(shape)), Hs = shape->ssd_heads, P = shape->headdim, N = shape->d_state;
   const int G = shape->ngroups, Q = shape->chunk, nc = L / Q;
   const int64_t rows = int64_t(shape->batch) * L;
-  const size_t scan_bytes = w.scan2 - w.scan1;
   const ScanOrder so{mode, shape->T, shape->H, shape->W};
   const __bf16* xb = static_cast<const __bf16*>(x);
   const __bf16* dyb = static_cast<const __bf16*>(dy);
@@ -719,30 +663,20 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
     if (hipGetLastError() != hipSuccess) return LINGEN_ERR_HIP;       \
   } while (0)
 
-  // a zero D for the transposed scans; dA and dD accumulate from zero
-  zero_floats_kernel<<<1, kThreads, 0, stream>>>(atf(w.dzero), dA, dD, Hs);
-  LINGEN_LAUNCHED();
-  const float* dz = atf(w.dzero);
-
-  adjoint_input_kernel<<<blocks_for(rows * Hs * (P / 8)), kThreads, 0, stream>>>(
-      dyb, dt, A, rows, Hs, P, static_cast<__bf16*>(at(w.xprime)));
+  // dA and dD accumulate from zero
+  zero_floats_kernel<<<1, kThreads, 0, stream>>>(dA, dD, Hs);
   LINGEN_LAUNCHED();
 
   // transposed outputs: M_b^T dy / dt is the forward scan with dt_prev, M_f^T dy / dt the reverse scan with
-  // dt_next, inputs dy / (moved dt), B and C exchanged
+  // dt_next, both fed dy as an input that carries its dt factor, B and C exchanged
   {
-    const int64_t total = rows * Hs * (P / 8);
-    shifted_dt_kernel<<<blocks_for(total), kThreads, 0, stream>>>(
-        dyb, dt, so, L, Hs, P, total, atf(w.dt_next), atf(w.dt_prev), static_cast<__bf16*>(at(w.dy_next)),
-        static_cast<__bf16*>(at(w.dy_prev)));
+    const int64_t total = rows * Hs;
+    shifted_dt_kernel<<<blocks_for(total), kThreads, 0, stream>>>(dt, so, L, Hs, total, atf(w.dt_next),
+                                                                 atf(w.dt_prev));
     LINGEN_LAUNCHED();
   }
-  const float* dtn = atf(w.dt_next);
-  const float* dtp = atf(w.dt_prev);
-  // (M_b^T + M_f^T) dy / dt in one per-direction call: the forward scan with dt_prev and the reverse scan
-  // with dt_next
-  LINGEN_TRY(lingen_ma_fwd_dirs(at(w.dy_prev), dtp, A, C, B, dz, at(w.dy_next), dtn, A, C, B, dz, mode, shape,
-                                at(w.yh), at(w.scan1), scan_bytes, stream));
+  LINGEN_TRY(ma_fwd_dirs_unit(shape, mode, dy, atf(w.dt_prev), C, B, dy, atf(w.dt_next), C, B, A, at(w.yh),
+                              at(w.scan1), stream));
 
   // crossing sums, then ddt, dx, dA, dD
   {
@@ -756,9 +690,9 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
       // forward / reverse states of (x, B) and of (x', C) for this batch element, left in the two workspaces
       const int64_t xo = int64_t(bi) * L * Hs * P * eb, bo = int64_t(bi) * L * G * N * eb;
       LINGEN_TRY(scan_states_one(shape, mode, static_cast<const char*>(x) + xo, dt + int64_t(bi) * L * Hs, A,
-                                 static_cast<const char*>(B) + bo, ws + w.scan1, stream));
-      LINGEN_TRY(scan_states_one(shape, mode, static_cast<const char*>(at(w.xprime)) + xo, dt + int64_t(bi) * L * Hs,
-                                 A, static_cast<const char*>(C) + bo, ws + w.scan2, stream));
+                                 static_cast<const char*>(B) + bo, ws + w.scan1, stream, kWeightDt));
+      LINGEN_TRY(scan_states_one(shape, mode, static_cast<const char*>(dy) + xo, dt + int64_t(bi) * L * Hs, A,
+                                 static_cast<const char*>(C) + bo, ws + w.scan2, stream, kWeightAdjoint));
       if (Q == 128 && N == 128)
         ma_bwd_cross_kernel<128, 128><<<cgrid, kCrossThreads, 0, stream>>>(
             xb, dyb, dt, A, static_cast<const __bf16*>(B), static_cast<const __bf16*>(C), st1, st2, per, so, L, Hs,

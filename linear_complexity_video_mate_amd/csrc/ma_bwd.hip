@@ -240,7 +240,9 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     }
   }
   lds_barrier();
-  f32x4 gC[NTL], gB[NTL];   // dC, dB of row block `wave`, summed over the group's heads
+  // dC, dB of row block `wave`, summed over the group's heads, transposed:
+  // the lane holds columns 16 j + 4 lg + r of row r0 + lr
+  f32x4 gC[NTL], gB[NTL];
 #pragma unroll
   for (int j = 0; j < NTL; ++j) { gC[j] = f32x4{0.f, 0.f, 0.f, 0.f}; gB[j] = f32x4{0.f, 0.f, 0.f, 0.f}; }
   const bool owns_rows = wave < QT;
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       }
     }
     lds_barrier();   // E is complete
-    // dC += E B (rows t = row block), dB += E^T C (rows s = row block)
+    // dC^T += B^T E^T (columns t = row block), dB^T += C^T E (columns s = row block)
     if (owns_rows) {
 #pragma unroll 1
       for (int kb = 0; kb < Q; kb += 32) {
@@ -387,8 +389,8 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         const bf16x8 et = tr_frag(sE, LDE, kb, r0, lane);                  // E^T rows r0.., k = t
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
-          gC[j] = mma(ea, tr_frag(sB, LDB, kb, 16 * j, lane), gC[j]);
-          gB[j] = mma(et, tr_frag(sC, LDB, kb, 16 * j, lane), gB[j]);
+          gC[j] = mma(tr_frag(sB, LDB, kb, 16 * j, lane), ea, gC[j]);
+          gB[j] = mma(tr_frag(sC, LDB, kb, 16 * j, lane), et, gB[j]);
         }
       }
     }
@@ -401,42 +403,36 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       const bool is_u = (term == 0 || term == 2);          // U terms: dy, C, dC; V terms: x, B, dB
       const __bf16* sa = is_u ? sDY : sX;
       const __bf16* sv = is_u ? sC : sB;
+      // rows of the term's operand (dy or x) as the MFMA's columns, k = p
       bf16x8 af[P / 32];
 #pragma unroll
       for (int kk = 0; kk < P / 32; ++kk) af[kk] = perm_frag(sa + (r0 + lr) * LDX, 32 * kk, lane);
-      // row scales of this term (rows r0 + 4 lg + r)
-      float scale[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = r0 + 4 * lg + r;
-        scale[r] = term == 0 ? __expf(s_cs[t])
-                 : term == 1 ? s_dt[t] * __expf(cs_last - s_cs[t])
-                 : term == 2 ? __expf(cs_last - s_csx[t])
-                             : s_dt[t] * __expf(s_csx[t]);
-      }
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      // the row scale of this term for the lane's row t
+      const int t = r0 + lr;
+      const float scale = term == 0 ? __expf(s_cs[t])
+                        : term == 1 ? s_dt[t] * __expf(cs_last - s_cs[t])
+                        : term == 2 ? __expf(cs_last - s_csx[t])
+                                    : s_dt[t] * __expf(s_csx[t]);
+      const __bf16* svr = sv + t * LDB + 4 * lg;
+      float part = 0.f;
 #pragma unroll
       for (int nt = 0; nt < NTL; ++nt) {
         const int n0 = nt * 16;
+        // (state^T a^T)[n][t] for n = n0 + 4 lg + r
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < P / 32; ++kk) acc = mma(af[kk], tr_frag(sMt, LDB, 32 * kk, n0, lane), acc);
+        for (int kk = 0; kk < P / 32; ++kk) acc = mma(tr_frag(sMt, LDB, 32 * kk, n0, lane), af[kk], acc);
+        const bf16x4 v4 = *reinterpret_cast<const bf16x4*>(svr + n0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          part[r] = fmaf(acc[r], static_cast<float>(sv[(r0 + 4 * lg + r) * LDB + n0 + lr]), part[r]);
-          if (is_u) gC[nt][r] = fmaf(scale[r], acc[r], gC[nt][r]);
-          else gB[nt][r] = fmaf(scale[r], acc[r], gB[nt][r]);
+          part = fmaf(acc[r], static_cast<float>(v4[r]), part);
+          if (is_u) gC[nt][r] = fmaf(scale, acc[r], gC[nt][r]);
+          else gB[nt][r] = fmaf(scale, acc[r], gB[nt][r]);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part[r] = sum16(part[r]);
-      if (lr < 4) {
-        const int t = r0 + 4 * lg + lr;
-        float sum = part[0], sc = scale[0];
-#pragma unroll
-        for (int r = 1; r < 4; ++r)
-          if (lr == r) { sum = part[r]; sc = scale[r]; }
-        const float v = sc * sum;
+      part = sum_rows(part);
+      if (lg == 0) {
+        const float v = scale * part;
         if (term == 0) s_fw[t] += v;                       // U_f
         else if (term == 1) { s_bw[t] += v; s_sub[t] += v; }  // V_f
         else if (term == 2) s_bw[t] += v;                  // U_b
@@ -492,16 +488,13 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     if (tid < Q) R[(bl + s_tok[tid]) * Hs + h] = s_fw[tid] + s_bw[tid] - s_sub[tid] + k;
   }
 
-  // dB, dC of the chunk's tokens (rows r0 + 4 lg + r, columns 16 j + lr)
+  // dB, dC of the chunk's tokens (row r0 + lr, columns 16 j + 4 lg .. + 3)
   if (owns_rows) {
+    const int64_t row = ((bl + s_tok[r0 + lr]) * G + g) * N;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = ((bl + s_tok[r0 + 4 * lg + r]) * G + g) * N;
-#pragma unroll
-      for (int j = 0; j < NTL; ++j) {
-        dC[row + 16 * j + lr] = gC[j][r];
-        dB[row + 16 * j + lr] = gB[j][r];
-      }
+    for (int j = 0; j < NTL; ++j) {
+      *reinterpret_cast<float4*>(dC + row + 16 * j + 4 * lg) = make_float4(gC[j][0], gC[j][1], gC[j][2], gC[j][3]);
+      *reinterpret_cast<float4*>(dB + row + 16 * j + 4 * lg) = make_float4(gB[j][0], gB[j][1], gB[j][2], gB[j][3]);
     }
   }
 }

@@ -311,8 +311,7 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(const TS* _
   for (int gi = wave; gi < ngroups; gi += kNormThreads / 64) {
     float ss = 0.f;
     for (int u = gi * upg + lane; u < (gi + 1) * upg; u += 64) ss += part[u];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    ss = sum64(ss);
     if (lane == 0) inv[gi] = rsqrtf(ss / float(group) + eps);
   }
   __syncthreads();

@@ -166,8 +166,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dense_attn_kernel(const __bf16* __
       float bm = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) bm = fmaxf(bm, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
-      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      bm = max_rows(bm);
       const float mnew = fmaxf(m[qt], bm * sc);
       // Rescale the running output only when some query's maximum grew.
       if (__ballot(mnew > m[qt])) {

@@ -1,7 +1,8 @@
 // Device helpers shared by the HIP kernels of the library (gfx950 / CDNA4):
 // vector types, the MFMA 16x16 tiles and their operand fragments, the
 // swizzled 128-byte-row LDS tile with its transposing read, direct
-// global-to-LDS loads and the LDS-only workgroup barrier.
+// global-to-LDS loads, the LDS-only workgroup barrier and cross-lane
+// reductions and scans.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,6 +28,56 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Cross-lane sums, maxima and scans without LDS traffic (every lane of the
+// wave active).  DPP quad permutations swap neighbours and pairs inside each
+// quad, the half-row mirror pairs the two quads of an 8-lane half-row and
+// the row mirror the two halves of a 16-lane row; v_permlane16_swap and
+// v_permlane32_swap exchange whole rows (lane l with l ^ 16, l ^ 32).
+template <int CTRL>
+__device__ __forceinline__ float dpp_plus(float v) {
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over each aligned group of 8 lanes, in every lane of the group
+__device__ __forceinline__ float sum8(float v) {
+  v = dpp_plus<0xB1>(v);       // quad_perm [1,0,3,2]
+  v = dpp_plus<0x4E>(v);       // quad_perm [2,3,0,1]
+  return dpp_plus<0x141>(v);   // row_half_mirror
+}
+// sum over each 16-lane row, in every lane of the row
+__device__ __forceinline__ float sum16(float v) { return dpp_plus<0x140>(sum8(v)); /* row_mirror */ }
+// sum and maximum over the four rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float sum_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float max_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum64(float v) { return sum_rows(sum16(v)); }
+
+// v + the value of the lane the DPP control names (0 where it names none,
+// and in rows the row mask leaves out).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_shifted_plus(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+// Inclusive prefix sum over the 64 lanes of the wave: row shifts by 1, 2, 4,
+// 8 scan each 16-lane row, then the last lane of rows 0 and 2 is broadcast
+// into the next row and the last lane of row 1 into rows 2 and 3.
+__device__ __forceinline__ float wave_scan_incl(float v) {
+  v = dpp_shifted_plus<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_shifted_plus<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_shifted_plus<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_shifted_plus<0x118, 0xF>(v);   // row_shr:8
+  v = dpp_shifted_plus<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+  return dpp_shifted_plus<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
 }
 
 __device__ __forceinline__ float to_f32(float v) { return v; }

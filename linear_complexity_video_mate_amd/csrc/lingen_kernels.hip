@@ -212,13 +212,7 @@ __device__ __forceinline__ void wave_chunk_prefix(const float* sdt, float Ah, fl
     v[e] = idx < Q ? sdt[idx] * a2 : 0.f;
     run += v[e];
   }
-  float incl = run;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  float base = incl - run;
+  float base = wave_scan_incl(run) - run;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int idx = lane * E + e;
@@ -1228,8 +1222,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
         for (int sb = 0; sb < SB; ++sb)
           bm = fmaxf(bm, fmaxf(fmaxf(fmaxf(s[sb][0][0], s[sb][0][1]), fmaxf(s[sb][0][2], s[sb][0][3])),
                                fmaxf(fmaxf(s[sb][1][0], s[sb][1][1]), fmaxf(s[sb][1][2], s[sb][1][3]))));
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        bm = max_rows(bm);
         const float mnew = fmaxf(msc[qi], bm * sc);
         const float mref = mnew == -INFINITY ? 0.f : mnew;
         const float alpha = fast_exp2(msc[qi] - mref);
@@ -1284,8 +1277,7 @@ __global__ __launch_bounds__((AttnCfg<TS, DH, NWIN>::NWAVE * 64)) void tesa_wind
 #pragma unroll
     for (int qi = 0; qi < QTP; ++qi) {
       float lt = l[qi];
-      lt += __shfl_xor(lt, 16, 64);
-      lt += __shfl_xor(lt, 32, 64);
+      lt = sum_rows(lt);
       const float inv = __builtin_amdgcn_rcpf(lt);
       if (kPadded && (wave + qi * Cfg::NWAVE) * 16 + r16 >= NVALID) continue;   // padding slot
       TS* yrow = y + int64_t(cur.tokq[qi]) * rowstride + int64_t(h) * DH;

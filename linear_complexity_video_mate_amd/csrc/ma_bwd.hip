@@ -77,32 +77,6 @@ __global__ __launch_bounds__(kThreads) void shifted_dt_kernel(const float* __res
 
 constexpr int kCrossThreads = 512;
 
-// Cross-lane sums without LDS traffic (every lane of the wave active).
-// DPP quad permutations swap neighbours and pairs inside each quad, the
-// half-row mirror pairs the two quads of an 8-lane half-row and the row
-// mirror the two halves of a 16-lane row; v_permlane16_swap and
-// v_permlane32_swap exchange whole rows (lane l with l ^ 16, l ^ 32).
-template <int CTRL>
-__device__ __forceinline__ float dpp_plus(float v) {
-  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-// sum over each aligned group of 8 lanes, in every lane of the group
-__device__ __forceinline__ float sum8(float v) {
-  v = dpp_plus<0xB1>(v);    // quad_perm [1,0,3,2]
-  v = dpp_plus<0x4E>(v);    // quad_perm [2,3,0,1]
-  return dpp_plus<0x141>(v);   // row_half_mirror
-}
-// sum over each 16-lane row, in every lane of the row
-__device__ __forceinline__ float sum16(float v) { return dpp_plus<0x140>(sum8(v));   /* row_mirror */ }
-// sum over the four rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
-__device__ __forceinline__ float sum_rows(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-__device__ __forceinline__ float sum64(float v) { return sum_rows(sum16(v)); }
-
 // Block-wide sum over the 512 threads of a workgroup.
 __device__ __forceinline__ float block_sum512(float v, float* red) {
   v = sum64(v);
@@ -115,29 +89,13 @@ __device__ __forceinline__ float block_sum512(float v, float* red) {
   return t;
 }
 
-// v + the value of the lane the DPP control names (0 where it names none,
-// and in rows the row mask leaves out).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_shifted_plus(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
-}
-
 // Inclusive prefix sums of Q = 64 V values held V per lane (lane l holds
-// positions V l .. V l + V - 1), within one wave (all lanes active): row
-// shifts by 1, 2, 4, 8 scan each 16-lane row, then the last lane of row 0
-// and of row 2 is broadcast into the next row, and the last lane of row 1
-// into rows 2 and 3.
+// positions V l .. V l + V - 1), within one wave (all lanes active).
 template <int V>
-__device__ __forceinline__ void wave_prefix(float (&v)[V], int lane) {
+__device__ __forceinline__ void wave_prefix(float (&v)[V]) {
 #pragma unroll
   for (int e = 1; e < V; ++e) v[e] += v[e - 1];
-  float run = v[V - 1];
-  run = dpp_shifted_plus<0x111, 0xF>(run);   // row_shr:1
-  run = dpp_shifted_plus<0x112, 0xF>(run);   // row_shr:2
-  run = dpp_shifted_plus<0x114, 0xF>(run);   // row_shr:4
-  run = dpp_shifted_plus<0x118, 0xF>(run);   // row_shr:8
-  run = dpp_shifted_plus<0x142, 0xA>(run);   // row_bcast:15 into rows 1, 3
-  run = dpp_shifted_plus<0x143, 0xC>(run);   // row_bcast:31 into rows 2, 3
+  const float run = wave_scan_incl(v[V - 1]);
   const float before = run - v[V - 1];
 #pragma unroll
   for (int e = 0; e < V; ++e) v[e] += before;
@@ -284,7 +242,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       float v[V], d0[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) { d0[e] = s_dt[V * lane + e] * a_h; v[e] = d0[e]; }
-      wave_prefix<V>(v, lane);
+      wave_prefix<V>(v);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         s_cs[V * lane + e] = v[e];
@@ -475,8 +433,8 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         f[e] = s_fw[Q - 1 - (V * lane + e)];
         bk[e] = s_bw[V * lane + e];
       }
-      wave_prefix<V>(f, lane);
-      wave_prefix<V>(bk, lane);
+      wave_prefix<V>(f);
+      wave_prefix<V>(bk);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const int rf = Q - 1 - (V * lane + e), rb = V * lane + e;

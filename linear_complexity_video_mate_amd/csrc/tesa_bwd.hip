@@ -193,8 +193,7 @@ __global__ __launch_bounds__(64 * 16 / QT) void tesa_bwd_kernel(const __bf16* __
         }
         float bm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        bm = max_rows(bm);
         const float mnew = fmaxf(m[qt], bm * sc);
         const float mref = mnew == -INFINITY ? 0.f : mnew;
         const float alpha = fast_exp2(m[qt] - mref);
@@ -222,8 +221,7 @@ __global__ __launch_bounds__(64 * 16 / QT) void tesa_bwd_kernel(const __bf16* __
     for (int qt = 0; qt < QT; ++qt) {
       const int i0 = (wave * QT + qt) * 16;
       float lt = l[qt];
-      lt += __shfl_xor(lt, 16, 64);
-      lt += __shfl_xor(lt, 32, 64);
+      lt = sum_rows(lt);
       const float inv = 1.f / lt;
       // D_i = sum_d dO_i[d] o_i[d]: the lane holds o for d = et*16 + 4g + r.
       float ds_ = 0.f;
@@ -233,8 +231,7 @@ __global__ __launch_bounds__(64 * 16 / QT) void tesa_bwd_kernel(const __bf16* __
 #pragma unroll
         for (int r = 0; r < 4; ++r) ds_ = fmaf(static_cast<float>(g4[r]), o[qt][et][r] * inv, ds_);
       }
-      ds_ += __shfl_xor(ds_, 16, 64);
-      ds_ += __shfl_xor(ds_, 32, 64);
+      ds_ = sum_rows(ds_);
       dsum[qt] = ds_;
       lse[qt] = m[qt] + log2f(lt);
       if (grp == 0) {

@@ -1405,13 +1405,16 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
       x, dt, A, B, make_rms(s, mode, rev), Hs, s->ngroups, hg, nc, states, decay);
   if (hip_status()) return LINGEN_ERR_HIP;
   if (int rc = mark(ev, 2, st)) return rc;
-  // P*N/8 threads per head, in blocks of up to 256 (P*N/8 is 64, 512 or
-  // 1024 in the compiled families).
-  constexpr int E = 8, BS = 256;
+  // P*N/E threads per head, in blocks of up to 256.  Both directions: E = 8
+  // elements per thread, 8 chunks' loads in flight.  One direction has half
+  // the work, so it takes E = 4 (twice the threads) with 16 chunks in flight
+  // (measured: 0.25 -> 0.21 ms per one-direction pass at the 512p-like
+  // workload; 16 in flight slows the two-direction pass).
+  constexpr int E = BIDIR ? 8 : 4, U = BIDIR ? 8 : 16, BS = 256;
   static_assert((P * N / E) % 64 == 0 && ((P * N / E) < BS || (P * N / E) % BS == 0), "state pass blocking");
   const int bs = (P * N / E) < BS ? (P * N / E) : BS;
   const int64_t thr = int64_t(Hs) * P * N / E;
-  ssd_state_pass_kernel<TS, 8, E><<<dim3(unsigned(thr / bs), BIDIR ? 2 : 1), bs, 0, st>>>(states, decay, h0, Hs,
+  ssd_state_pass_kernel<TS, U, E><<<dim3(unsigned(thr / bs), BIDIR ? 2 : 1), bs, 0, st>>>(states, decay, h0, Hs,
                                                                                            P * N, nc);
   if (hip_status()) return LINGEN_ERR_HIP;
   return mark(ev, 3, st);

@@ -33,13 +33,13 @@ ScanFamily scan_family(const lingen_mate_shape* s);
 AttnFamily attn_family(const lingen_mate_shape* s);
 int check_ptr(const void* p);                      // NULL / alignment check
 int compute_units();                               // of the current device (cached per device), -1 on error
-// How a token's input enters the chunked scan, with a = dt A its log decay:
+// How a token's input enters the chunked scan's states, with a = dt A its
+// log decay:
 //   kWeightDt       the SSD recurrence: token s contributes dt_s x_s (with B_s);
-//   kWeightUnit     the input is already dt x (dt then sets the decays only);
 //   kWeightAdjoint  token s contributes e^{a_s} x_s, the recurrence of the
 //                   input x e^{a} / dt (the adjoint states of the backward
 //                   pass) without forming that input.
-enum WeightMode { kWeightDt = 0, kWeightUnit = 1, kWeightAdjoint = 2 };
+enum WeightMode { kWeightDt = 0, kWeightAdjoint = 2 };
 
 // Chunk states and scan states of one batch element (x, dt, B of that
 // element) into the workspace, at ws_layout(s).states in the storage dtype:
@@ -48,13 +48,15 @@ enum WeightMode { kWeightDt = 0, kWeightUnit = 1, kWeightAdjoint = 2 };
 // lingen_status.
 int scan_states_one(const lingen_mate_shape* s, int mode, const void* xb, const float* dtb, const float* A,
                     const void* Bb, void* workspace, hipStream_t stream, int wmode);
-// The per-direction MA branch of lingen_ma_fwd_dirs (forward direction with
-// the _f operands, the reverse one with the _b operands, one A) for inputs
-// u that already carry their dt factor (u = dt x; dt sets the decays only),
-// without the skip term.  No review tokens.  Shapes and pointers are the
-// caller's to validate.  lingen_status.
-int ma_fwd_dirs_unit(const lingen_mate_shape* s, int mode, const void* u_f, const float* dt_f, const void* B_f,
-                     const void* C_f, const void* u_b, const float* dt_b, const void* B_b, const void* C_b,
-                     const float* A, void* y, void* workspace, hipStream_t stream);
+// The transposed bidirectional scan of one batch element, y = (M_f^T +
+// M_b^T) u / dt, with M_f, M_b the matrices of the two directions of the
+// shared-parameter SSD scan with dt, A, B, C (y_MA = (M_f + M_b) x + 2 D x;
+// the division removes M's dt factor, so no dt enters y): the chunk states
+// must be those that
+// scan_states_one(s, mode, u, dt, A, C, workspace, ..., kWeightAdjoint) left
+// in `workspace`.  bf16 families only; no review tokens.  Shapes and
+// pointers are the caller's to validate.  lingen_status.
+int ma_transposed_one(const lingen_mate_shape* s, int mode, const void* ub, const float* dtb, const float* A,
+                      const void* Bb, const void* Cb, const void* workspace, void* yb, hipStream_t stream);
 
 }  // namespace lingen

@@ -511,9 +511,8 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
         sW[0][i] = fast_exp2(cum_end - cum_i + d * a2);   // e^{cum_end - exc_i}
         sW[1][i] = fast_exp2(cum_i);                      // e^{exc_i + a_i}
       } else {
-        const float w = WM == kWeightUnit ? 1.f : d;
-        sW[0][i] = fast_exp2(cum_end - cum_i) * w;
-        sW[1][i] = fast_exp2(cum_i - d * a2) * w;     // exc_i = cum_i - a_i
+        sW[0][i] = fast_exp2(cum_end - cum_i) * d;
+        sW[1][i] = fast_exp2(cum_i - d * a2) * d;     // exc_i = cum_i - a_i
       }
     }
     if (tid == 0) decay[int64_t(c) * Hs + h] = fast_exp2(cum_end);
@@ -673,9 +672,18 @@ struct OutCfg {
 // BIDIR = false: the forward direction alone (lower triangle and diagonal
 // weight 1, the forward inter-chunk term, D x once), for a scan whose
 // backward direction has parameters of its own; ACC adds the result to y.
-// UNIT: the input is already dt x (kWeightUnit): no dt factor on the
-// tokens, and no skip term (D is not read).
-template <typename TS, int P, int N, int Q, bool BIDIR = true, bool ACC = false, bool UNIT = false>
+// UNIT: no dt factor on the tokens (the input carries its own token
+// weights), and no skip term (D is not read).
+// TRANS (with BIDIR and UNIT): the transposed scan (M_f^T + M_b^T) u of the
+// bidirectional one, which the backward pass needs: pairs s < t decay by
+// e^{exc_t - exc_s} and pairs s > t by e^{cum_s - cum_t} (the roles of the
+// inclusive and exclusive prefix sums exchanged), the entering states apply
+// e^{exc_t} and e^{cum_end - cum_t}, and the caller exchanges B and C and
+// passes the states of u with the adjoint token weights (kWeightAdjoint),
+// whose chunk-local weights e^{cum_end - exc_s} and e^{cum_s} are exactly
+// the transposed scan's.
+template <typename TS, int P, int N, int Q, bool BIDIR = true, bool ACC = false, bool UNIT = false,
+          bool TRANS = false>
 __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_kernel(
     const TS* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const TS* __restrict__ B,
     const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int G, int hg, int n_chunks,
@@ -683,6 +691,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   using MT = TS;
   using F = Frag<MT>;
   using Cfg = OutCfg<TS, P, N, Q>;
+  static_assert(!TRANS || (BIDIR && UNIT), "the transposed scan is bidirectional with unit token weights");
   constexpr int NTHR = Cfg::NW * 64;
   constexpr int KI = F::K;
   using TN = Tile<MT, N>;     // rows of N: B rows and the entering states
@@ -797,8 +806,9 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       for (int s = lane; s < Q; s += 64) {
         float vs = 0.f;
         const float w = UNIT ? 1.f : cs.dt[hh][s];
-        if (s < ts) vs = fast_exp2(ref_lo - cum[s]) * w;
-        else if (s > te) vs = fast_exp2(exc[s] - ref_hi) * w;
+        // (TRANS: the same references, the other prefix sum at s)
+        if (s < ts) vs = fast_exp2(ref_lo - (TRANS ? exc[s] : cum[s])) * w;
+        else if (s > te) vs = fast_exp2((TRANS ? cum[s] : exc[s]) - ref_hi) * w;
         sV[wave][s] = vs;
       }
     }
@@ -809,8 +819,8 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
     const float* exc = cs.exc[hh];
     const float* dth = cs.dt[hh];
     const float cum_t = cum[t], exc_t = exc[t];
-    const float fac_lo = fast_exp2(cum_t - exc[wt * 16]);          // t-side factor, s before the tile
-    const float fac_hi = fast_exp2(cum[wt * 16 + 15] - exc_t);     // t-side factor, s after the tile
+    const float fac_lo = fast_exp2((TRANS ? exc_t : cum_t) - exc[wt * 16]);   // t-side factor, s before the tile
+    const float fac_hi = fast_exp2(cum[wt * 16 + 15] - (TRANS ? cum_t : exc_t));   // t-side factor, s after the tile
 
     // M^T values of this lane for s-tile st (s = 16*st + 4*grp + r).  On the
     // diagonal tile: s < t forward decay e^{cum_t - cum_s}, s > t backward
@@ -827,7 +837,7 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int s = sb + r;
-          const float arg = s < t ? cum_t - cv[r] : xv[r] - exc_t;
+          const float arg = TRANS ? (s < t ? exc_t - xv[r] : cv[r] - cum_t) : (s < t ? cum_t - cv[r] : xv[r] - exc_t);
           const float lam = s == t ? (BIDIR ? 2.f : 1.f) : (BIDIR || s < t ? fast_exp2(arg) : 0.f);
           mv[r] = to_f32(g[st][r]) * lam * (UNIT ? 1.f : dv[r]);
         }
@@ -889,7 +899,8 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
     }
 
     // Inter-chunk terms, the skip, and the store.
-    const float ef = fast_exp2(cum_t), eb = BIDIR ? fast_exp2(cum[Q - 1] - exc_t) : 0.f;
+    const float ef = fast_exp2(TRANS ? exc_t : cum_t);
+    const float eb = BIDIR ? fast_exp2(cum[Q - 1] - (TRANS ? cum_t : exc_t)) : 0.f;
     const float twoD = UNIT ? 0.f : (BIDIR ? 2.f : 1.f) * D[h];
     // bf16 rows of 64 owned by one wave: the four p-tiles are stored together
     // in 16-byte pieces (see below).
@@ -1449,9 +1460,8 @@ int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char
 
 // MA branch with a parameter set per direction: the forward direction of
 // the scan order with af, then the forward direction of the reversed order
-// (the backward scan) with ab, added to the first result.  UNIT: the inputs
-// already carry their dt factor (kWeightUnit; no skip term).
-template <typename TS, int P, int N, int Q, bool UNIT = false>
+// (the backward scan) with ab, added to the first result.
+template <typename TS, int P, int N, int Q>
 int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const Args& ab, void* y, char* ws,
                    hipStream_t st) {
   const int L = int(tokens(s));
@@ -1470,14 +1480,13 @@ int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const A
       const int64_t bc = int64_t(b) * L * s->ngroups * N * eb;
       const TS* B = reinterpret_cast<const TS*>(static_cast<const char*>(a.B) + bc);
       const TS* C = reinterpret_cast<const TS*>(static_cast<const char*>(a.C) + bc);
-      constexpr int WM = UNIT ? kWeightUnit : kWeightDt;
-      if (int rc = launch_states<TS, P, N, Q, false, WM>(s, mode, x, dt, a.A, B, ws, st, nullptr, dir)) return rc;
+      if (int rc = launch_states<TS, P, N, Q, false>(s, mode, x, dt, a.A, B, ws, st, nullptr, dir)) return rc;
       const TS* states = reinterpret_cast<const TS*>(ws + lay.states);
       if (dir == 0)
-        ssd_chunk_out_kernel<TS, P, N, Q, false, false, UNIT><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
+        ssd_chunk_out_kernel<TS, P, N, Q, false, false><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
             x, dt, a.A, B, C, a.D, make_rms(s, mode, 0), Hs, s->ngroups, hg, nc, states, yb);
       else
-        ssd_chunk_out_kernel<TS, P, N, Q, false, true, UNIT><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
+        ssd_chunk_out_kernel<TS, P, N, Q, false, true><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
             x, dt, a.A, B, C, a.D, make_rms(s, mode, 1), Hs, s->ngroups, hg, nc, states, yb);
       if (hip_status()) return LINGEN_ERR_HIP;
     }
@@ -1485,15 +1494,31 @@ int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const A
   return LINGEN_OK;
 }
 
-template <bool UNIT>
 int dispatch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const Args& ab, void* y, char* ws,
                      hipStream_t st) {
   switch (scan_family(s)) {
-    case SCAN_F32_P32_N16_Q16: return launch_ma_dirs<float, 32, 16, 16, UNIT>(s, mode, af, ab, y, ws, st);
-    case SCAN_BF16_P64_N64_Q64: return launch_ma_dirs<__bf16, 64, 64, 64, UNIT>(s, mode, af, ab, y, ws, st);
-    case SCAN_BF16_P64_N128_Q128: return launch_ma_dirs<__bf16, 64, 128, 128, UNIT>(s, mode, af, ab, y, ws, st);
+    case SCAN_F32_P32_N16_Q16: return launch_ma_dirs<float, 32, 16, 16>(s, mode, af, ab, y, ws, st);
+    case SCAN_BF16_P64_N64_Q64: return launch_ma_dirs<__bf16, 64, 64, 64>(s, mode, af, ab, y, ws, st);
+    case SCAN_BF16_P64_N128_Q128: return launch_ma_dirs<__bf16, 64, 128, 128>(s, mode, af, ab, y, ws, st);
     default: return LINGEN_ERR_UNSUPPORTED;
   }
+}
+
+// The transposed bidirectional scan of one batch element (TRANS above): the
+// states are those of u against C with the adjoint token weights, left by
+// scan_states_one in `ws`; B and C are exchanged for the output kernel.
+template <typename TS, int P, int N, int Q>
+int launch_transposed(const lingen_mate_shape* s, int mode, const TS* u, const float* dt, const float* A,
+                      const TS* B, const TS* C, const char* ws, TS* y, hipStream_t st) {
+  const int nc = int(tokens(s)) / Q;
+  const int Hs = s->ssd_heads;
+  using Cfg = OutCfg<TS, P, N, Q>;
+  const int hg = head_group(Hs / s->ngroups);
+  const TS* states = reinterpret_cast<const TS*>(ws + ws_layout(s).states);
+  ssd_chunk_out_kernel<TS, P, N, Q, true, false, true, true><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
+      u, dt, A, C, B, nullptr, make_rms(s, mode), Hs, s->ngroups, hg, nc, states, y);
+  if (hip_status()) return LINGEN_ERR_HIP;
+  return LINGEN_OK;
 }
 
 int dispatch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char* ws, hipStream_t st,
@@ -1608,13 +1633,22 @@ int scan_states_one(const lingen_mate_shape* s, int mode, const void* xb, const 
   }
 }
 
-int ma_fwd_dirs_unit(const lingen_mate_shape* s, int mode, const void* u_f, const float* dt_f, const void* B_f,
-                     const void* C_f, const void* u_b, const float* dt_b, const void* B_b, const void* C_b,
-                     const float* A, void* y, void* workspace, hipStream_t stream) {
+int ma_transposed_one(const lingen_mate_shape* s, int mode, const void* ub, const float* dtb, const float* A,
+                      const void* Bb, const void* Cb, const void* workspace, void* yb, hipStream_t stream) {
   if (s->n_review != 0) return LINGEN_ERR_UNSUPPORTED;
-  Args af{u_f, dt_f, A, B_f, C_f, nullptr, nullptr, nullptr, nullptr};
-  Args ab{u_b, dt_b, A, B_b, C_b, nullptr, nullptr, nullptr, nullptr};
-  return dispatch_ma_dirs<true>(s, mode, af, ab, y, static_cast<char*>(workspace), stream);
+  const char* ws = static_cast<const char*>(workspace);
+  switch (scan_family(s)) {
+    case SCAN_BF16_P64_N64_Q64:
+      return launch_transposed<__bf16, 64, 64, 64>(s, mode, static_cast<const __bf16*>(ub), dtb, A,
+                                                   static_cast<const __bf16*>(Bb), static_cast<const __bf16*>(Cb), ws,
+                                                   static_cast<__bf16*>(yb), stream);
+    case SCAN_BF16_P64_N128_Q128:
+      return launch_transposed<__bf16, 64, 128, 128>(s, mode, static_cast<const __bf16*>(ub), dtb, A,
+                                                     static_cast<const __bf16*>(Bb), static_cast<const __bf16*>(Cb),
+                                                     ws, static_cast<__bf16*>(yb), stream);
+    default:
+      return LINGEN_ERR_UNSUPPORTED;
+  }
 }
 }  // namespace lingen
 
@@ -1700,7 +1734,7 @@ int lingen_ma_fwd_dirs(const void* x_f, const float* dt_f, const float* A_f, con
   if (shape->n_review != 0) return LINGEN_ERR_UNSUPPORTED;
   Args af{x_f, dt_f, A_f, B_f, C_f, D_f, nullptr, nullptr, nullptr};
   Args ab{x_b, dt_b, A_b, B_b, C_b, D_b, nullptr, nullptr, nullptr};
-  return dispatch_ma_dirs<false>(shape, mode, af, ab, y_ma, static_cast<char*>(workspace), stream);
+  return dispatch_ma_dirs(shape, mode, af, ab, y_ma, static_cast<char*>(workspace), stream);
 }
 
 int lingen_te_fwd(const void* q, const void* k, const void* v, int32_t shifted, const lingen_mate_shape* shape,

@@ -8,10 +8,12 @@
 // product between scan positions and W_ts = M_ts (dy_t . x_s).  Every
 // gradient is built from scans the library already runs, with transformed
 // operands, plus the kernels of this file:
-//   * M^T of one direction is the opposite direction's scan with dt moved
-//     by one scan position (so the decays cover the right tokens) and B, C
-//     exchanged, fed dy as an input that already carries its dt factor:
-//     dx = dt (M_f^T + M_b^T) dy / dt + 2 D dy;
+//   * dx = dt yhat + 2 D dy with yhat = (M_f^T + M_b^T) dy / dt.  Inside a
+//     chunk, M_f^T + M_b^T is the bidirectional scan with B and C exchanged,
+//     unit token weights and the inclusive and exclusive prefix sums of
+//     dt A trading places in the decays; its chunk states are those of dy
+//     against C with the token weights exp(dt A), i.e. the adjoint states
+//     below, so yhat is one output-kernel launch over them;
 //   * dB and dC are, per chunk, products of the same chunk-local matrices the
 //     crossing sums need (E = dt (dy x^T) weighted by the decays) with C and
 //     B, plus products of the chunk-boundary states with x and dy;
@@ -53,26 +55,6 @@ __global__ __launch_bounds__(kThreads) void zero_floats_kernel(float* __restrict
     a[i] = 0.f;
     b[i] = 0.f;
   }
-}
-
-// dt moved by one scan position each way: dt_next at the token of scan
-// position r = dt at position r+1 (the last position keeps its own),
-// dt_prev = dt at position r-1 (the first keeps its own).  One thread per
-// (batch, scan position, head).
-__global__ __launch_bounds__(kThreads) void shifted_dt_kernel(const float* __restrict__ dt, ScanOrder so, int L,
-                                                              int Hs, int64_t total, float* __restrict__ dt_next,
-                                                              float* __restrict__ dt_prev) {
-  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= total) return;
-  const int h = int(i % Hs);
-  const int64_t br = i / Hs;                    // batch * L + scan position
-  const int r = int(br % L);
-  const int64_t base = br - r;                  // batch * L
-  const int64_t c = base + so.canon(r);
-  const int64_t cn = base + so.canon(r + 1 < L ? r + 1 : r);
-  const int64_t cp = base + so.canon(r > 0 ? r - 1 : r);
-  dt_next[c * Hs + h] = dt[cn * Hs + h];
-  dt_prev[c * Hs + h] = dt[cp * Hs + h];
 }
 
 constexpr int kCrossThreads = 512;
@@ -535,7 +517,7 @@ __global__ __launch_bounds__(256) void ma_bwd_token_kernel(
 
 // Byte offsets inside the caller's workspace.
 struct BwdWs {
-  size_t scan1, scan2, dt_next, dt_prev, R, yh, total;
+  size_t scan1, scan2, R, yh, total;
 };
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
@@ -549,8 +531,6 @@ int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
   w->scan1 = take(ws_main);
   w->scan2 = take(ws_main);
-  w->dt_next = take(rows * hs * 4);
-  w->dt_prev = take(rows * hs * 4);
   w->R = take(rows * hs * 4);
   w->yh = take(rows * hs * P * 2);
   w->total = off;
@@ -618,17 +598,6 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   zero_floats_kernel<<<1, kThreads, 0, stream>>>(dA, dD, Hs);
   LINGEN_LAUNCHED();
 
-  // transposed outputs: M_b^T dy / dt is the forward scan with dt_prev, M_f^T dy / dt the reverse scan with
-  // dt_next, both fed dy as an input that carries its dt factor, B and C exchanged
-  {
-    const int64_t total = rows * Hs;
-    shifted_dt_kernel<<<blocks_for(total), kThreads, 0, stream>>>(dt, so, L, Hs, total, atf(w.dt_next),
-                                                                 atf(w.dt_prev));
-    LINGEN_LAUNCHED();
-  }
-  LINGEN_TRY(ma_fwd_dirs_unit(shape, mode, dy, atf(w.dt_prev), C, B, dy, atf(w.dt_next), C, B, A, at(w.yh),
-                              at(w.scan1), stream));
-
   // crossing sums, then ddt, dx, dA, dD
   {
     const dim3 cgrid{unsigned(nc), unsigned(G), 1u};
@@ -644,6 +613,10 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
                                  static_cast<const char*>(B) + bo, ws + w.scan1, stream, kWeightDt));
       LINGEN_TRY(scan_states_one(shape, mode, static_cast<const char*>(dy) + xo, dt + int64_t(bi) * L * Hs, A,
                                  static_cast<const char*>(C) + bo, ws + w.scan2, stream, kWeightAdjoint));
+      // the transposed outputs yhat = (M_f^T + M_b^T) dy / dt from the same adjoint states
+      LINGEN_TRY(ma_transposed_one(shape, mode, static_cast<const char*>(dy) + xo, dt + int64_t(bi) * L * Hs, A,
+                                   static_cast<const char*>(B) + bo, static_cast<const char*>(C) + bo, ws + w.scan2,
+                                   static_cast<char*>(at(w.yh)) + xo, stream));
       if (Q == 128 && N == 128)
         ma_bwd_cross_kernel<128, 128><<<cgrid, kCrossThreads, 0, stream>>>(
             xb, dyb, dt, A, static_cast<const __bf16*>(B), static_cast<const __bf16*>(C), st1, st2, per, so, L, Hs,

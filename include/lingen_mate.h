@@ -272,19 +272,19 @@ int lingen_dense_attn_fwd(const void* q, const void* k, const void* v, void* o,
  *   dB, dC: [batch, L, G, N] fp32 (summed over the heads of each group)
  *   dA, dD: [Hs] fp32 (summed over tokens and batch elements)
  * all device, caller-owned, overwritten.  dy has the layout and dtype of y.
- * The gradients are assembled from the library's scans run on dy with other
- * token weights (the transposed scans, with dt moved by one scan position
- * and dy taken as an input that carries its dt factor, for dx; the
- * chunk-state pass of dy against C with the token weights e^{dt A}, i.e.
- * the states of dy e^{dt A} / dt, for the adjoint states) and a per-chunk
- * MFMA kernel for the crossing sums behind ddt and dA and for dB and dC;
- * see the source for the derivation.
+ * The gradients are assembled from the library's scan kernels run on dy
+ * with other token weights (the chunk-state pass of dy against C with the
+ * token weights e^{dt A}, i.e. the states of dy e^{dt A} / dt: the adjoint
+ * states; the output kernel in its transposed form over those states for
+ * (M_f^T + M_b^T) dy / dt, behind dx) and a per-chunk MFMA kernel for the
+ * crossing sums behind ddt and dA and for dB and dC; see the source for the
+ * derivation.
  * Supported: bf16 storage with P = 64 in the compiled families
  * (BF16, 64, 64, 64) and (BF16, 64, 128, 128); anything else that passes
  * lingen_mate_validate returns LINGEN_ERR_UNSUPPORTED, as do review tokens.
  * workspace: device, lingen_ma_bwd_workspace_bytes (two scan workspaces,
- * whose bf16 chunk states the kernel reads, plus the moved dt arrays, the
- * crossing sums and the transposed scan's output).
+ * whose bf16 chunk states the kernels read, plus the crossing sums and the
+ * transposed outputs).
  * Errors: those of lingen_mate_validate; LINGEN_ERR_UNSUPPORTED as above;
  * LINGEN_ERR_SHAPE for mode outside 0..3; LINGEN_ERR_NULL / _ALIGN for a
  * pointer; LINGEN_ERR_WORKSPACE. */

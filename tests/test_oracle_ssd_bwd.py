@@ -77,3 +77,61 @@ def test_checkpoint_spacing_does_not_matter_and_skip_gradient():
     # y carries D x once per direction: dD = 2 sum dy . x for the bidirectional scan
     full = oracle.ssd_bidir_backward(*params, dy, order)
     np.testing.assert_allclose(full[5], 2 * np.sum(dy * params[0], axis=(0, 2)), rtol=1e-12)
+
+
+def test_transposed_scan_identity_in_chunks():
+    """The identity behind the GPU backward's dx: yhat = (dx - 2 D dy) / dt of
+    the oracle equals the bidirectional scan with B and C exchanged, unit
+    token weights and the prefix sums trading places (pairs i < o decay by
+    e^{exc_o - exc_i}, pairs i > o by e^{cum_i - cum_o}, weight 2 on the
+    diagonal), evaluated chunk by chunk: within a chunk densely, across
+    chunks through states that carry the chunk-local weights e^{cum_end -
+    exc_i} (forward) and e^{cum_i} (reverse), i.e. the states of dy e^{dt A}
+    / dt against C, with the factors e^{exc_o} and e^{cum_end - cum_o} on the
+    output side."""
+    rng = np.random.default_rng(71)
+    T, H, W, Hs, P, N, Q = 2, 2, 4, 2, 3, 2, 4
+    L = T * H * W
+    params, dy = _inputs(rng, L, Hs, P, N, 1)
+    x, dt, A, B, C, D = params
+    perm = oracle.rms_scan_order(1, T, H, W)
+    dx = oracle.ssd_bidir_backward(*params, dy, perm)[0]
+    yhat_oracle = (dx - 2.0 * D[None, :, None] * dy) / dt[:, :, None]
+    nc = L // Q
+    yhat = np.zeros_like(dy)
+    for h in range(Hs):
+        a = dt[perm, h] * A[h]                      # scan order
+        Bs, Cs, us = B[perm], C[perm], dy[perm, h]  # [L, N], [L, N], [L, P]
+        cum = np.zeros(L)
+        exc = np.zeros(L)
+        for c in range(nc):                         # chunk-local prefix sums
+            blk = slice(c * Q, (c + 1) * Q)
+            cum[blk] = np.cumsum(a[blk])
+            exc[blk] = cum[blk] - a[blk]
+        g = np.array([np.exp(cum[(c + 1) * Q - 1]) for c in range(nc)])
+        # chunk states of u against C with the adjoint weights
+        sf = np.zeros((nc, N, P))
+        sb = np.zeros((nc, N, P))
+        for c in range(nc):
+            end = (c + 1) * Q - 1
+            for i in range(c * Q, (c + 1) * Q):
+                sf[c] += np.exp(cum[end] - exc[i]) * np.outer(Cs[i], us[i])
+                sb[c] += np.exp(cum[i]) * np.outer(Cs[i], us[i])
+        hf = np.zeros((nc, N, P))
+        hb = np.zeros((nc, N, P))
+        for c in range(1, nc):
+            hf[c] = g[c - 1] * hf[c - 1] + sf[c - 1]
+        for c in range(nc - 2, -1, -1):
+            hb[c] = g[c + 1] * hb[c + 1] + sb[c + 1]
+        out = np.zeros((L, P))
+        for c in range(nc):
+            end = (c + 1) * Q - 1
+            for o in range(c * Q, (c + 1) * Q):
+                acc = np.zeros(P)
+                for i in range(c * Q, (c + 1) * Q):
+                    lam = 2.0 if i == o else (np.exp(exc[o] - exc[i]) if i < o else np.exp(cum[i] - cum[o]))
+                    acc += (Bs[o] @ Cs[i]) * lam * us[i]
+                acc += np.exp(exc[o]) * (Bs[o] @ hf[c]) + np.exp(cum[end] - cum[o]) * (Bs[o] @ hb[c])
+                out[o] = acc
+        yhat[perm, h] = out
+    np.testing.assert_allclose(yhat, yhat_oracle, rtol=1e-10, atol=1e-10)

@@ -1,18 +1,22 @@
 """Benchmark of the MATE mixer forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
 
 One step = one lingen_mate_fwd call over the whole token tensor: both MA
 stages (chunk states, inter-chunk state pass, chunk outputs), windowed
 attention and the branch sum.  Step k uses layer index k mod 4, so the four
 scan orders and both window phases are timed in equal measure.  Inputs are
 the seeded synthetic tensors of the workload, resident in GPU memory before
-timing starts.
+timing starts.  The default workload is the minute-length grid
+(128x64x64 = 524,288 tokens), the largest that is run on one GPU.
 
 Prints one JSON line: whole-job tokens/s, per-stage times from HIP events
 recorded on the launch stream (lingen_mate_fwd_events), the roofline of the
-dominant kernel against MI355X's peak HBM bandwidth, and the fp64 oracle
-timed on host cores over a bounded sample of the same workload.
+dominant kernel (its bound taken from its arithmetic intensity against the
+MFMA/HBM ridge), the linear-scaling check (the same forward on the first
+quarter of the frames, i.e. the 512p-like 32x64x64 grid, timed in the same
+run), and the fp64 oracle timed on host cores over a bounded sample of the
+same workload (a process pool, run before the GPU is initialised).
 """
 from __future__ import annotations
 
@@ -123,62 +127,107 @@ def compulsory_bytes(s):
                 + 3 * s.attn_heads * s.attn_headdim * e)
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` measured with rocprofv3 counters, if a
-    committed measurement exists for the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    if not os.path.exists(path):
-        return None
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def _traffic_records():
+    if not os.path.exists(TRAFFIC_PATH):
+        return {}
     try:
-        rec = json.load(open(path))
+        return json.load(open(TRAFFIC_PATH))
     except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_sha256") != kernel_source_sha256() or rec.get("workload") != workload:
+        return {}
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` measured with rocprofv3
+    counters, if a committed measurement exists for that workload and the
+    current kernel source; else None."""
+    rec = _traffic_records().get("workloads", {}).get(workload)
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the fp64 oracle, as it stands, on a bounded sample
+# CPU baseline: the fp64 oracle, as it stands, on a bounded sample, in a
+# process pool over heads (heads are independent in both branches).  It runs
+# before anything initialises the GPU, so the forked workers hold no device
+# state; they read the inputs copy-on-write from this process.
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(s, inp):
+_CPU_SHARED = {}
+MAX_CPU_WORKERS = 16     # the host share of one GPU
+
+
+def _head_f64(inp, name, h):
     import numpy as np
+
+    from mate_inputs import f32_from_bf16_bits
+
+    a = inp.store[name]
+    sl = a[[h]] if name in ("A", "D") else a[:, [h]]
+    return (f32_from_bf16_bits(sl) if sl.dtype == np.uint16 else sl).astype(np.float64)
+
+
+def _cpu_task(task):
+    """One head of one branch through the oracle, single-threaded; returns its
+    wall time (the extraction of the head's inputs is not timed)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
-    from mate_inputs import f32_from_bf16_bits
 
-    def head(name, h):
-        a = inp.store[name]
-        sl = a[[h]] if name in ("A", "D") else a[:, [h]]
-        return (f32_from_bf16_bits(sl) if sl.dtype == np.uint16 else sl).astype(np.float64)
-
-    B, C = inp.f64("B"), inp.f64("C")
-    review = (s.rpool, s.rgrid) if s.n_review else None
-    ns, na = min(4, s.ssd_heads), min(4, s.attn_heads)   # about 12 s of CPU at the 512p-like workload
-    t_ssd = t_att = 0.0
+    kind, h = task
+    s, inp = _CPU_SHARED["shape"], _CPU_SHARED["inp"]
     with threadpool_limits(limits=1):
-        for h in range(ns):
-            hx = {n: head(n, h) for n in ("x", "dt", "A", "D")}
+        if kind == "ssd":
+            hx = {n: _head_f64(inp, n, h) for n in ("x", "dt", "A", "D")}
+            review = (s.rpool, s.rgrid) if s.n_review else None
             t0 = time.perf_counter()
-            oracle.ma_fwd(hx["x"], hx["dt"], hx["A"], B, C, hx["D"], 0, s.T, s.H, s.W, review=review)
-            t_ssd += time.perf_counter() - t0
-        for h in range(na):
-            hx = {n: head(n, h) for n in ("q", "k", "v")}
+            oracle.ma_fwd(hx["x"], hx["dt"], hx["A"], _CPU_SHARED["B"], _CPU_SHARED["C"], hx["D"], 0,
+                          s.T, s.H, s.W, review=review)
+        else:
+            hx = {n: _head_f64(inp, n, h) for n in ("q", "k", "v")}
             t0 = time.perf_counter()
             oracle.tesa(hx["q"], hx["k"], hx["v"], s.T, s.H, s.W, s.win, (0, 0, 0))
-            t_att += time.perf_counter() - t0
-    est = t_ssd / ns * s.ssd_heads + t_att / na * s.attn_heads
+        return time.perf_counter() - t0
+
+
+def cpu_workers(requested: int = 0) -> int:
+    avail = len(os.sched_getaffinity(0))
+    n = requested if requested > 0 else min(MAX_CPU_WORKERS, avail)
+    return max(1, min(n, avail))
+
+
+def cpu_baseline(s, inp, workers):
+    """Layer 0 (scan order 0, plain windows) of the workload through the fp64
+    oracle: `workers` SSD heads at once over every token (both directions),
+    then `workers` attention heads at once, one head per process.  The whole
+    job's time is each batch's wall time scaled by heads / workers."""
+    import multiprocessing as mp
+
+    _CPU_SHARED.update(shape=s, inp=inp, B=inp.f64("B"), C=inp.f64("C"))
+    ns, na = min(workers, s.ssd_heads), min(workers, s.attn_heads)
+    with mp.get_context("fork").Pool(workers) as pool:
+        t0 = time.perf_counter()
+        per_ssd = pool.map(_cpu_task, [("ssd", h) for h in range(ns)], chunksize=1)
+        w_ssd = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        per_att = pool.map(_cpu_task, [("tesa", h) for h in range(na)], chunksize=1)
+        w_att = time.perf_counter() - t0
+    _CPU_SHARED.clear()
+    est = w_ssd * s.ssd_heads / ns + w_att * s.attn_heads / na
     return {
         "value": s.L / est,
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle, single thread, over all {s.L} tokens: SSD heads 0-{ns - 1} (both "
-                   f"directions, layer 0) {t_ssd:.2f} s and attention heads 0-{na - 1} {t_att:.2f} s; "
-                   f"per-head times scaled by {s.ssd_heads} SSD heads and {s.attn_heads} attention heads"),
+        "sample": (f"fp64 NumPy oracle, {workers} processes of one thread each, layer 0, over all {s.L} tokens: "
+                   f"SSD heads 0-{ns - 1} at once (both directions) {w_ssd:.2f} s wall "
+                   f"(per head {min(per_ssd):.2f}-{max(per_ssd):.2f} s), then attention heads 0-{na - 1} at "
+                   f"once {w_att:.2f} s wall; scaled by {s.ssd_heads}/{ns} SSD and {s.attn_heads}/{na} "
+                   f"attention heads"),
     }
 
 
@@ -211,17 +260,17 @@ def record_traffic(mix_fetch, mix_write, copy_fetch, copy_write, config=2):
         rd, wr = fetch[name] * fcal * 1024, write[name] * wcal * 1024
         kernels[name] = {"read_bytes": round(rd), "write_bytes": round(wr), "bytes_per_launch": round(rd + wr)}
     rec = {
-        "workload": CONFIG_NOTES[config],
         "kernel_source_sha256": kernel_source_sha256(),
         "calibration": {"FETCH_SIZE_scale": round(fcal, 4), "WRITE_SIZE_scale": round(wcal, 4),
                         "copy": "bench.py --copy-gib 1 (1 GiB read + 1 GiB written per launch)"},
         "counters": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, each its own run",
         "kernels": kernels,
     }
-    out = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    with open(out, "w") as f:
-        json.dump(rec, f, indent=1)
-    print(json.dumps(rec))
+    allrec = _traffic_records()
+    allrec.setdefault("workloads", {})[CONFIG_NOTES[config]] = rec
+    with open(TRAFFIC_PATH, "w") as f:
+        json.dump({"workloads": allrec["workloads"]}, f, indent=1)
+    print(json.dumps({CONFIG_NOTES[config]: rec}))
     return 0
 
 
@@ -572,16 +621,61 @@ def dense_compare(args, mate, torch):
 
 # ---------------------------------------------------------------------------
 
+def timed_forward(mate, args_t, s, y, ws, K, W, stream, ev):
+    """W warmup and K timed lingen_mate_fwd steps (layer_idx = step mod 4)
+    bracketed by HIP events on the launch stream; ms per step."""
+    for i in range(W):
+        mate.lingen_mate_fwd(*args_t, i % 4, s, out=y, workspace=ws)
+    a, b = ev.create(), ev.create()
+    import torch
+    torch.cuda.synchronize()
+    ev.record(a, stream)
+    for k in range(K):
+        mate.lingen_mate_fwd(*args_t, k % 4, s, out=y, workspace=ws)
+    ev.record(b, stream)
+    torch.cuda.synchronize()
+    return ev.ms(a, b) / K
+
+
+def roofline_of(work, kernel, ms, workload):
+    """Roofline line of one kernel: its bound is the one its arithmetic
+    intensity (algorithmic flop per algorithmic byte) puts it under, against
+    the ridge of MI355X's dense bf16 MFMA peak over its HBM peak; both
+    fractions are reported."""
+    t = ms / 1e3
+    nbytes, flops = work[kernel]["bytes"], work[kernel]["flops"]
+    gbs, tflops = nbytes / t / 1e9, flops / t / 1e12
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    intensity = flops / nbytes
+    hbm = {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    mfma = {"achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    bound = "mfma" if intensity > ridge else "hbm"
+    main, other = (mfma, hbm) if bound == "mfma" else (hbm, mfma)
+    return {"kernel": kernel, "bound": bound, **main,
+            "traffic": traffic_for(kernel, workload) if bound == "hbm" else None,
+            "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
+            "flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
+            "other_bound": {"bound": "hbm" if bound == "mfma" else "mfma", **other},
+            "avg_launch_ms": round(ms, 4)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes for the CPU baseline (default: the host cores this process may use, "
+                         f"at most {MAX_CPU_WORKERS})")
+    ap.add_argument("--no-scaling", action="store_true",
+                    help="skip the linear-scaling leg (the forward on the first quarter of the frames)")
     ap.add_argument("--record-traffic", nargs=4, metavar=("MIX_FETCH", "MIX_WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="write profiles/hbm_traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs of "
-                         "this benchmark and of the --copy-gib calibration run, then exit")
+                    help="add the --config workload's record to profiles/hbm_traffic.json from rocprofv3 --pmc "
+                         "FETCH_SIZE / WRITE_SIZE CSVs of this benchmark and of the --copy-gib calibration run, "
+                         "then exit")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="instead of the mixer, time a plain device copy of this many GiB (the RMS gather "
                          "kernel in scan mode 0) and print its bandwidth: the HBM calibration point")
@@ -615,10 +709,27 @@ def main(argv=None):
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         return 2
 
+    side = (args.copy_gib > 0 or args.gather or args.dense or args.te_bwd or args.block or args.mate_block
+            or args.ma_bwd)
+    inp = None
+    cpu = None
+    if not side:
+        from mate_inputs import CONFIGS, CONFIG_NOTES, make_inputs
+
+        s = CONFIGS[args.config]
+        workload = CONFIG_NOTES[args.config]
+        print(f"[bench] generating inputs: {workload}, {s.L} tokens", file=sys.stderr, flush=True)
+        inp = make_inputs(s, args.config, threads=16)
+        if not args.no_cpu_baseline:
+            nw = cpu_workers(args.cpu_workers)
+            print(f"[bench] timing the oracle on the host ({nw} processes, bounded sample)", file=sys.stderr,
+                  flush=True)
+            cpu = cpu_baseline(s, inp, nw)
+            print(f"[bench] oracle done: {cpu['value']:.1f} tokens/s", file=sys.stderr, flush=True)
+
     import torch
 
     import linear_complexity_video_mate_amd as mate
-    from mate_inputs import CONFIGS, CONFIG_NOTES, make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -638,11 +749,8 @@ def main(argv=None):
         return mate_block(args, mate, torch)
     if args.ma_bwd:
         return ma_backward(args, mate, torch)
-    s = CONFIGS[args.config]
-    workload = CONFIG_NOTES[args.config]
-    print(f"[bench] generating inputs: {workload}, {s.L} tokens", file=sys.stderr, flush=True)
-    inp = make_inputs(s, args.config, threads=16)
     d = {n: inp.torch(n, "cuda") for n in ("x", "dt", "A", "B", "C", "D", "q", "k", "v")}
+    del inp
     args_t = [d[n] for n in ("x", "dt", "A", "B", "C", "D", "q", "k", "v")]
     ws = torch.empty(mate.lingen_mate_workspace_bytes(s), dtype=torch.uint8, device="cuda")
     y = torch.empty((1, s.L, s.d_inner), dtype=torch.bfloat16 if s.dtype == "bf16" else torch.float32,
@@ -677,7 +785,6 @@ def main(argv=None):
         for i, name in enumerate(STAGES):
             stage_ms[name] += ev.ms(e[i], e[i + 1]) / K
         per_layer[k % 4] += ev.ms(e[0], e[5]) / (K / 4)
-    ev.close()
 
     work = kernel_work(s)
     stages = {}
@@ -693,24 +800,35 @@ def main(argv=None):
             "mfma_frac": round(work[name]["flops"] / t / 1e12 / BF16_PEAK_TFLOPS, 4),
         }
     dom = max((n for n in stages), key=lambda n: stage_ms[n])
-    dom_t = stage_ms[dom] / 1e3
-    achieved = work[dom]["bytes"] / dom_t / 1e9
-    roofline = {
-        "kernel": dom,
-        "bound": "hbm",
-        "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": traffic_for(dom, workload),
-        "algorithmic_bytes_per_launch": work[dom]["bytes"],
-        "avg_launch_ms": round(stage_ms[dom], 4),
-    }
+    roofline = roofline_of(work, dom, stage_ms[dom], workload)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(s, inp)
+    # Linear scaling in T: the same forward on the first quarter of the
+    # frames (a T/4 x H x W grid, a prefix of every canonical-order tensor),
+    # timed the same way in this run.
+    scaling = None
+    if not args.no_scaling and s.T % 4 == 0 and s.n_review == 0 and s.batch == 1:
+        small = s.with_(T=s.T // 4)
+        Ls = small.L
+        sub = [d[n][:Ls] if n not in ("A", "D") else d[n] for n in ("x", "dt", "A", "B", "C", "D", "q", "k", "v")]
+        sws = ws[:mate.lingen_mate_workspace_bytes(small)]
+        sy = y[:, :Ls]
+        print(f"[bench] linear-scaling leg: {Ls} tokens, {K} steps", file=sys.stderr, flush=True)
+        ms_small = timed_forward(mate, sub, small, sy, sws, K, W, stream, ev)
+        wk_small = kernel_work(small)
+        f_big = sum(w["flops"] for w in work.values())
+        f_small = sum(w["flops"] for w in wk_small.values())
+        scaling = {
+            "small_grid_THW": [small.T, small.H, small.W],
+            "small_tokens": Ls,
+            "small_ms_per_step": round(ms_small, 4),
+            "tokens_ratio": round(s.L / Ls, 3),
+            "flop_ratio": round(f_big / f_small, 3),
+            "bytes_ratio": round(sum(w["bytes"] for w in work.values())
+                                 / sum(w["bytes"] for w in wk_small.values()), 3),
+            "time_ratio": round(ms_step / ms_small, 3),
+            "band": [3.6, 4.4],
+        }
+    ev.close()
 
     comp = compulsory_bytes(s)
     out = {
@@ -737,6 +855,7 @@ def main(argv=None):
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "linear_scaling": scaling,
         "stages": stages,
         "per_layer_ms": [round(v, 4) for v in per_layer],
         "path_vs_compulsory_hbm": round(comp / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),

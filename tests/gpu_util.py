@@ -60,3 +60,29 @@ def tol(shape) -> float:
 
 def review_of(shape):
     return (shape.rpool, shape.rgrid) if shape.n_review else None
+
+
+def row_tol(shape) -> float:
+    """Bound on the relative L2 error of every single (token, head) row of y:
+    5e-2 with bf16 storage, 1e-4 with fp32 storage, so that a wrong chunk,
+    window or head cannot hide inside a whole-tensor norm."""
+    return 1e-4 if shape.dtype == "f32" else 5e-2
+
+
+def check_rows(got, ref, width: int, shape, what: str = "y") -> None:
+    """Assert the whole-tensor bound (tol) and the per-row bound (row_tol) on
+    rows of `width` consecutive elements (one head's slice of one token).
+    A row's error is taken relative to its own norm, floored at 1e-3 of the
+    mean row norm (a row of the reference that cancels to nearly zero would
+    otherwise demand an exact result)."""
+    got = np.asarray(got, dtype=np.float64).reshape(-1, width)
+    ref = np.asarray(ref, dtype=np.float64).reshape(-1, width)
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    den = np.maximum(den, 1e-3 * max(float(den.mean()), 1e-300))
+    rows = num / den
+    e = rel_l2(got, ref)
+    worst = int(np.argmax(rows))
+    say(f"  {what}: rel L2 {e:.3e}, worst row {rows[worst]:.3e} (row {worst})")
+    assert e <= tol(shape), f"{what}: relative L2 {e:.3e} > {tol(shape)}"
+    assert rows[worst] <= row_tol(shape), f"{what}: row {worst} relative error {rows[worst]:.3e} > {row_tol(shape)}"

@@ -164,10 +164,13 @@ int lingen_ma_fwd(const void* x, const float* dt, const float* A, const void* B,
  *   y_ma = scan(x_f, dt_f, A_f, B_f, C_f, D_f along the order of `mode`)
  *        + scan(x_b, dt_b, A_b, B_b, C_b, D_b along the reversed order),
  * each scan carrying its own skip D x (so y_ma holds D_f x_f + D_b x_b).
- * Layouts, dtypes and workspace as lingen_ma_fwd, for both sets.  Review
- * tokens are not supported here (shape->n_review must be 0, else
- * LINGEN_ERR_UNSUPPORTED).  The forward scan's result is rounded to the
- * output dtype before the backward scan's is added. */
+ * Layouts, dtypes and workspace as lingen_ma_fwd, for both sets.  With
+ * review tokens (shape->n_review > 0; page "视频生成模子太贵太慢如何办？",
+ * section 要领) each direction pools its review tokens from its own x, dt,
+ * B and scans them with its own A, and starts from the state they leave.
+ * With bf16 storage the forward scan's result reaches the sum with about 16
+ * significant bits (kept as two bf16 halves in the workspace) and the sum
+ * is rounded once. */
 int lingen_ma_fwd_dirs(const void* x_f, const float* dt_f, const float* A_f, const void* B_f,
                        const void* C_f, const float* D_f,
                        const void* x_b, const float* dt_b, const float* A_b, const void* B_b,
@@ -264,10 +267,11 @@ int lingen_dense_attn_fwd(const void* q, const void* k, const void* v, void* o,
                           int32_t dtype, hipStream_t stream);
 
 /* Backward pass of the MA branch: the gradients of sum(dy * y_ma) for y_ma =
- * lingen_ma_fwd(x, dt, A, B, C, D, mode) without review tokens (the
- * shared-parameter bidirectional scan; [SSD] recurrence, page
- * "视频生成模子太贵太慢如何办？", section 要领：线性复杂度的 MATE 模块), with
- * respect to every input:
+ * lingen_ma_fwd(x, dt, A, B, C, D, mode), with review tokens when
+ * shape->n_review > 0 (the shared-parameter bidirectional scan; [SSD]
+ * recurrence, page "视频生成模子太贵太慢如何办？", section 要领：线性复杂度的 MATE
+ * 模块, whose review tokens seed both directions), with respect to every
+ * input:
  *   dx:  [batch, L, Hs, P] fp32      ddt: [batch, L, Hs] fp32
  *   dB, dC: [batch, L, G, N] fp32 (summed over the heads of each group)
  *   dA, dD: [Hs] fp32 (summed over tokens and batch elements)
@@ -278,13 +282,18 @@ int lingen_dense_attn_fwd(const void* q, const void* k, const void* v, void* o,
  * states; the output kernel in its transposed form over those states for
  * (M_f^T + M_b^T) dy / dt, behind dx) and a per-chunk MFMA kernel for the
  * crossing sums behind ddt and dA and for dB and dC; see the source for the
- * derivation.
+ * derivation.  With review tokens the adjoint that reaches the review state
+ * (the sum of the two directions' initial-state adjoints, the final carries
+ * of the adjoint state pass) is walked back through the review tokens' scan
+ * and each pooled token's gradient is spread over its pooling block (dx,
+ * ddt, dB, dA gain these shares; dC and dD do not: the review tokens'
+ * outputs are discarded).
  * Supported: bf16 storage with P = 64 in the compiled families
  * (BF16, 64, 64, 64) and (BF16, 64, 128, 128); anything else that passes
- * lingen_mate_validate returns LINGEN_ERR_UNSUPPORTED, as do review tokens.
+ * lingen_mate_validate returns LINGEN_ERR_UNSUPPORTED.
  * workspace: device, lingen_ma_bwd_workspace_bytes (two scan workspaces,
- * whose bf16 chunk states the kernels read, plus the crossing sums and the
- * transposed outputs).
+ * whose bf16 chunk states the kernels read, plus the crossing sums, the
+ * transposed outputs and, with review tokens, their gradients).
  * Errors: those of lingen_mate_validate; LINGEN_ERR_UNSUPPORTED as above;
  * LINGEN_ERR_SHAPE for mode outside 0..3; LINGEN_ERR_NULL / _ALIGN for a
  * pointer; LINGEN_ERR_WORKSPACE. */
@@ -395,6 +404,9 @@ int lingen_mate_block_workspace_bytes(const lingen_mate_shape* shape, int32_t d_
 /* out = MA(u) + TE(u) for u [batch, L, d_model] (canonical token order,
  * shape dtype), RMS mode = layer_idx mod 4 and shifted windows on odd
  * layer_idx as in lingen_mate_fwd; conv_k taps (1..4); norm_eps >= 0.
+ * Review tokens (shape->n_review > 0) enter the MA branch as in
+ * lingen_ma_fwd_dirs, pooled from each direction's scan inputs (after the
+ * convolution).
  *   out:       device, [batch, L, d_model], shape dtype; must not alias u.
  *   workspace: device, at least lingen_mate_block_workspace_bytes bytes,
  *              16-byte aligned; its contents on return are unspecified.
@@ -407,8 +419,8 @@ int lingen_mate_block_workspace_bytes(const lingen_mate_shape* shape, int32_t d_
  * lingen_mate_validate; LINGEN_ERR_SHAPE for d_model outside 1..65536,
  * batch*L of 2^31 or more, layer_idx < 0, conv_k outside 1..4, eps < 0, or
  * d, G*N or d/G not a multiple of 16 bytes of elements or d above 8192
- * (bf16) / 4096 (fp32); LINGEN_ERR_UNSUPPORTED for review tokens;
- * LINGEN_ERR_NULL / _ALIGN for a pointer (weights included);
+ * (bf16) / 4096 (fp32); LINGEN_ERR_NULL / _ALIGN for a pointer (weights
+ * included);
  * LINGEN_ERR_WORKSPACE.  A failing rocBLAS call is reported as
  * LINGEN_ERR_HIP, with the earlier steps already enqueued. */
 int lingen_mate_block_fwd(const void* u, const lingen_mate_block_weights* w, int32_t d_model,

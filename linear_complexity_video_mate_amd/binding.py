@@ -15,7 +15,10 @@ from typing import Optional, Tuple
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblingen_mate.so")
+# LINGEN_LIB_PATH selects another build of the same library (the host-ASan
+# variant the CPU tests run against); there is no other library and no
+# fallback.
+LIB_PATH = os.environ.get("LINGEN_LIB_PATH") or os.path.join(_PKG, "liblingen_mate.so")
 
 LINGEN_OK = 0
 STATUS_NAMES = {

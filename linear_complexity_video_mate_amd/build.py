@@ -56,9 +56,29 @@ def _hipcc() -> str:
 SOURCE_FLAGS = {"dense_attn.hip": ["-fno-honor-nans"]}
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+# AddressSanitizer on the host code only (the device code is built as
+# usual): the variant that tests/test_abi_cpu.py runs against on the CPU.
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_LIB_PATH = os.path.join(BUILD_DIR, "asan", "liblingen_mate_asan.so")
+
+
+def asan_runtime() -> str:
+    """The shared AddressSanitizer runtime of the ROCm clang that builds the
+    variant (to be preloaded into an uninstrumented Python)."""
+    import glob
+
+    found = sorted(glob.glob(os.path.join(ROCM, "llvm", "lib", "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    if not found:
+        raise RuntimeError("the ROCm clang AddressSanitizer runtime was not found")
+    return found[-1]
+
+
+def _compile(src: str, verbose: bool, asan: bool = False) -> str:
+    out_dir = os.path.join(BUILD_DIR, "asan") if asan else BUILD_DIR
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *(ASAN_FLAGS if asan else []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -72,19 +92,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, asan: bool = False) -> str:
+    """Compile and link the library; with asan, the host-ASan variant at
+    ASAN_LIB_PATH instead of the library at LIB_PATH."""
+    out = ASAN_LIB_PATH if asan else LIB_PATH
+    os.makedirs(os.path.dirname(out) if asan else BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *LINK_FLAGS]
+        objs = list(ex.map(lambda s: _compile(s, verbose, asan), SOURCES))
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *(["-shared-libasan", *ASAN_FLAGS] if asan else []),
+           "-o", tmp, *objs, *LINK_FLAGS]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking {LIB_NAME} failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+        raise RuntimeError(f"linking {os.path.basename(out)} failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

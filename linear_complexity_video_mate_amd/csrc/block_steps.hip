@@ -352,7 +352,7 @@ int launch_conv(const TS* in, const float* wf, const float* bf, const float* wb,
   const int64_t waves = ((int64_t(L) + seg - 1) / seg) * tiles;
   scan_conv_silu_kernel<TS, K, kConvAhead><<<unsigned((waves + 3) / 4), 256, 0, st>>>(in, wf, bf, wb, bb, so, L, seg,
                                                                                       ch, d, gn, o);
-  return hipGetLastError() == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
+  return launch_status(__func__);
 }
 
 template <typename TS>
@@ -382,7 +382,7 @@ int launch_prep(const lingen_mate_shape* s, const void* xbc, const float* dt_raw
   }
   const int64_t n = int64_t(s->batch) * L * s->ssd_heads;
   softplus_bias_kernel<<<unsigned((n + 255) / 256), 256, 0, st>>>(dt_raw, dt_bias, n, s->ssd_heads, dt);
-  return hipGetLastError() == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
+  return launch_status(__func__);
 }
 
 }  // namespace
@@ -431,5 +431,5 @@ extern "C" int lingen_gated_rmsnorm(const void* y, const void* z, const float* w
     gated_rmsnorm_kernel<float><<<unsigned(rows), kNormThreads, 0, stream>>>(
         static_cast<const float*>(y), static_cast<const float*>(z), weight, eps, dim, group,
         static_cast<float*>(out));
-  return hipGetLastError() == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
+  return launch_status(__func__);
 }

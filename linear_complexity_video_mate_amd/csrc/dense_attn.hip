@@ -252,5 +252,5 @@ extern "C" int lingen_dense_attn_fwd(const void* q, const void* k, const void* v
   dense_attn_kernel<64, kDenseWaves, kDenseQTiles><<<grid, kDenseWaves * 64, 0, stream>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), L, heads,
       static_cast<__bf16*>(o));
-  return hipGetLastError() == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
+  return launch_status(__func__);
 }

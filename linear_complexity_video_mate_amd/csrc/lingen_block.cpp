@@ -117,7 +117,6 @@ int check_block_shape(const lingen_mate_shape* s, int32_t d_model) {
   if (int rc = validate_shape(s)) return rc;
   if (d_model < 1 || d_model > 65536) return LINGEN_ERR_SHAPE;
   if (int64_t(s->batch) * tokens(s) > int64_t(0x7fffffff)) return LINGEN_ERR_SHAPE;   // GEMM row count
-  if (s->n_review != 0) return LINGEN_ERR_UNSUPPORTED;   // the per-direction scan takes no review tokens
   return LINGEN_OK;
 }
 

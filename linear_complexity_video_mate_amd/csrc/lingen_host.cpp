@@ -1,8 +1,12 @@
 // Host-side part of the MATE mixer library: argument validation, workspace
-// planning and the host copy of the Rotary Major Scan index maps.  Nothing in
-// this file calls into HIP, so all of it can be exercised without a GPU.
+// planning, the host copy of the Rotary Major Scan index maps and the check
+// after each kernel launch.  Nothing in this file launches a kernel, and the
+// validation and planning functions touch no GPU, so they can be exercised
+// without one.
 #include <atomic>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "lingen_internal.h"
@@ -50,6 +54,25 @@ int compute_units() {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
   if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+// LINGEN_DEBUG set to anything but "" or "0": after every kernel launch the
+// library waits for the device and checks for errors, and reports a failure
+// with the launching function's name on stderr.  Read once per process.
+bool debug_sync() {
+  static const bool on = [] {
+    const char* v = std::getenv("LINGEN_DEBUG");
+    return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+int launch_status(const char* where) {
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && debug_sync()) e = hipDeviceSynchronize();
+  if (e == hipSuccess) return LINGEN_OK;
+  if (debug_sync()) std::fprintf(stderr, "lingen: kernel launched by %s failed: %s\n", where, hipGetErrorString(e));
+  return LINGEN_ERR_HIP;
 }
 
 int check_ptr(const void* p) {

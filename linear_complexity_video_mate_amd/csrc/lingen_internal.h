@@ -32,6 +32,12 @@ WsLayout ws_layout(const lingen_mate_shape* s);
 ScanFamily scan_family(const lingen_mate_shape* s);
 AttnFamily attn_family(const lingen_mate_shape* s);
 int check_ptr(const void* p);                      // NULL / alignment check
+// After a kernel launch: LINGEN_OK, or LINGEN_ERR_HIP if the launch failed.
+// With the environment variable LINGEN_DEBUG set (not "0"), it also waits for
+// the device and reports any error on stderr naming `where`: a sync-and-check
+// mode for debugging (not for use under graph capture).
+int launch_status(const char* where);
+bool debug_sync();
 int compute_units();                               // of the current device (cached per device), -1 on error
 // How a token's input enters the chunked scan's states, with a = dt A its
 // log decay:
@@ -44,10 +50,15 @@ enum WeightMode { kWeightDt = 0, kWeightAdjoint = 2 };
 // Chunk states and scan states of one batch element (x, dt, B of that
 // element) into the workspace, at ws_layout(s).states in the storage dtype:
 // [2][n_chunks][Hs][P][N], the state entering each chunk of the forward scan
-// and then of the reverse scan.  wmode: kWeightDt or kWeightAdjoint.
+// and then of the reverse scan.  With s->n_review > 0 the review tokens of
+// (x, dt, B) are pooled and scanned first (into the workspace's review
+// buffers) and their state starts both walks; pass a shape with n_review = 0
+// for a scan without them.  wmode: kWeightDt or kWeightAdjoint.  h_last
+// (optional, fp32 [2][Hs][P][N]): the state each walk carries out of its
+// last chunk (the upward walk's first, then the downward walk's).
 // lingen_status.
 int scan_states_one(const lingen_mate_shape* s, int mode, const void* xb, const float* dtb, const float* A,
-                    const void* Bb, void* workspace, hipStream_t stream, int wmode);
+                    const void* Bb, void* workspace, hipStream_t stream, int wmode, float* h_last);
 // The transposed bidirectional scan of one batch element, y = (M_f^T +
 // M_b^T) u / dt, with M_f, M_b the matrices of the two directions of the
 // shared-parameter SSD scan with dt, A, B, C (y_MA = (M_f + M_b) x + 2 D x;

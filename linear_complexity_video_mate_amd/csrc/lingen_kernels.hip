@@ -587,13 +587,16 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
 // State pass: turns chunk states into the state entering each chunk, in
 // place.  dir 0 walks chunks upward, dir 1 downward; h0 (review state, fp32,
 // or zero) starts both walks.  Each thread owns 8 elements of one head's
-// P x N state and carries them in fp32.
+// P x N state and carries them in fp32.  h_last (optional, fp32
+// [dir][Hs][P][N]) receives the state each walk carries out of its last
+// chunk: for the adjoint states of the backward pass, the adjoints of the
+// two directions' initial states.
 // ---------------------------------------------------------------------------
 
 template <typename TS, int U, int E>
 __global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ states, const float* __restrict__ decay,
                                                              const float* __restrict__ h0, int Hs, int PN,
-                                                             int n_chunks) {
+                                                             int n_chunks, float* __restrict__ h_last) {
   // E elements per thread (16-byte accesses for bf16 at E = 8), U chunks'
   // loads in flight.  A block (blockDim.x threads, dividing PN/E) covers
   // consecutive elements of one head, so the head index and its chunk
@@ -636,6 +639,10 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(TS* __restrict__ st
       }
     }
   }
+  if (h_last) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) h_last[int64_t(dir) * Hs * PN + ev * E + e] = hv[e];
+  }
 }
 
 // Scan states in the workspace -> fp32 output (lingen_ssd_chunk_states).
@@ -672,6 +679,12 @@ struct OutCfg {
 // BIDIR = false: the forward direction alone (lower triangle and diagonal
 // weight 1, the forward inter-chunk term, D x once), for a scan whose
 // backward direction has parameters of its own; ACC adds the result to y.
+// With bf16 storage the one-direction passes also use ylo (laid out like y):
+// the first pass (ACC = false) writes its fp32 result v as y = bf16(v) and
+// ylo = bf16(v - y), and the second pass (ACC = true) adds y + ylo, so the
+// first direction's result reaches the sum with about 16 significant bits
+// instead of 8 (where the two directions nearly cancel, a rounded first
+// term would dominate the error of the row).
 // UNIT: no dt factor on the tokens (the input carries its own token
 // weights), and no skip term (D is not read).
 // TRANS (with BIDIR and UNIT): the transposed scan (M_f^T + M_b^T) u of the
@@ -687,7 +700,7 @@ template <typename TS, int P, int N, int Q, bool BIDIR = true, bool ACC = false,
 __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_kernel(
     const TS* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const TS* __restrict__ B,
     const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int G, int hg, int n_chunks,
-    const TS* __restrict__ states, TS* __restrict__ y) {
+    const TS* __restrict__ states, TS* __restrict__ y, TS* __restrict__ ylo) {
   using MT = TS;
   using F = Frag<MT>;
   using Cfg = OutCfg<TS, P, N, Q>;
@@ -905,6 +918,8 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
     // bf16 rows of 64 owned by one wave: the four p-tiles are stored together
     // in 16-byte pieces (see below).
     constexpr bool kP16 = kBf16 && Cfg::PT == 4 && Cfg::P_PER == 4 && Cfg::WPW == 1;
+    constexpr bool kSplit = kBf16 && !BIDIR;   // hi / lo halves of the one-direction passes (ylo)
+    static_assert(!kSplit || kP16, "the split sum is stored in 16-byte pieces");
     float ob[4][4];
 #pragma unroll
     for (int pj = 0; pj < Cfg::P_PER; ++pj) {
@@ -953,25 +968,36 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
       // lane groups g and g ^ 1 (v_permlane16_swap): the lane then holds
       // p0 .. p0 + 7, p0 = 32 r1 + 16 (g & 1) + 8 (g >> 1), and a wave's
       // 16-byte stores cover 64 contiguous bytes of each row.
-      TS* row = y + tok_t * (int64_t(Hs) * P) + int64_t(h) * P + 16 * (grp & 1) + 8 * (grp >> 1);
+      const int64_t roff = tok_t * (int64_t(Hs) * P) + int64_t(h) * P + 16 * (grp & 1) + 8 * (grp >> 1);
+      TS* row = y + roff;
 #pragma unroll
       for (int r1 = 0; r1 < 2; ++r1) {
-        bf16x8 old;
+        bf16x8 old, oldlo;
         if constexpr (ACC) old = *reinterpret_cast<const bf16x8*>(row + 32 * r1);
-        bf16x8 res;
+        if constexpr (ACC && kSplit) oldlo = *reinterpret_cast<const bf16x8*>(ylo + roff + 32 * r1);
+        float v[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(ob[2 * r1][r]),
                                                            __float_as_uint(ob[2 * r1 + 1][r]), false, false);
-          float lo = __uint_as_float(sw[0]), hi = __uint_as_float(sw[1]);
-          if constexpr (ACC) {
-            lo += static_cast<float>(old[r]);
-            hi += static_cast<float>(old[4 + r]);
+          v[r] = __uint_as_float(sw[0]);
+          v[4 + r] = __uint_as_float(sw[1]);
+        }
+        if constexpr (ACC) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v[e] += static_cast<float>(old[e]);
+            if constexpr (kSplit) v[e] += static_cast<float>(oldlo[e]);
           }
-          res[r] = static_cast<__bf16>(lo);
-          res[4 + r] = static_cast<__bf16>(hi);
+        }
+        bf16x8 res, rlo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          res[e] = static_cast<__bf16>(v[e]);
+          rlo[e] = static_cast<__bf16>(v[e] - static_cast<float>(res[e]));
         }
         *reinterpret_cast<bf16x8*>(row + 32 * r1) = res;
+        if constexpr (kSplit && !ACC) *reinterpret_cast<bf16x8*>(ylo + roff + 32 * r1) = rlo;
       }
     }
     lds_barrier();   // staging buffers free for the next head
@@ -1352,10 +1378,7 @@ struct Args {
 
 int64_t elem_bytes(const lingen_mate_shape* s) { return s->dtype == LINGEN_BF16 ? 2 : 4; }
 
-int hip_status() {
-  const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? LINGEN_OK : LINGEN_ERR_HIP;
-}
+
 
 RmsMap make_rms(const lingen_mate_shape* s, int mode, int rev = 0) { return RmsMap{mode, s->T, s->H, s->W, rev}; }
 
@@ -1387,17 +1410,17 @@ int launch_review(const lingen_mate_shape* s, const TS* x, const float* dt, cons
   float* hR = reinterpret_cast<float*>(ws + lay.review_h);
   review_pool_kernel<TS><<<dim3(s->n_review, s->ssd_heads + s->ngroups), 256, 0, st>>>(
       x, dt, B, s->T, s->H, s->W, s->ssd_heads, s->headdim, s->d_state, s->ngroups, g, rx, rdt, rb);
-  if (hip_status()) return LINGEN_ERR_HIP;
+  if (launch_status(__func__)) return LINGEN_ERR_HIP;
   review_state_kernel<<<dim3(s->ssd_heads, (s->headdim * s->d_state + 1023) / 1024), 256, 0, st>>>(rx, rdt, rb, A, s->n_review, s->ssd_heads, s->headdim,
                                                     s->d_state, s->ngroups, hR);
-  return hip_status();
+  return launch_status(__func__);
 }
 
 // Phase A + state pass (+ review state) for one batch element.  BIDIR =
 // false: the forward direction of the (possibly reversed, rev = 1) order only.
 template <typename TS, int P, int N, int Q, bool BIDIR = true, int WM = kWeightDt>
 int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float* dt, const float* A, const TS* B,
-                  char* ws, hipStream_t st, const hipEvent_t* ev = nullptr, int rev = 0) {
+                  char* ws, hipStream_t st, const hipEvent_t* ev = nullptr, int rev = 0, float* h_last = nullptr) {
   const WsLayout lay = ws_layout(s);
   const int L = int(tokens(s));
   const int nc = L / Q;
@@ -1414,7 +1437,7 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
   if (int rc = mark(ev, 1, st)) return rc;
   ssd_chunk_state_kernel<TS, P, N, Q, BIDIR, WM><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(
       x, dt, A, B, make_rms(s, mode, rev), Hs, s->ngroups, hg, nc, states, decay);
-  if (hip_status()) return LINGEN_ERR_HIP;
+  if (launch_status(__func__)) return LINGEN_ERR_HIP;
   if (int rc = mark(ev, 2, st)) return rc;
   // P*N/E threads per head, in blocks of up to 256.  Both directions: E = 8
   // elements per thread, 8 chunks' loads in flight.  One direction has half
@@ -1426,8 +1449,8 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
   const int bs = (P * N / E) < BS ? (P * N / E) : BS;
   const int64_t thr = int64_t(Hs) * P * N / E;
   ssd_state_pass_kernel<TS, U, E><<<dim3(unsigned(thr / bs), BIDIR ? 2 : 1), bs, 0, st>>>(states, decay, h0, Hs,
-                                                                                           P * N, nc);
-  if (hip_status()) return LINGEN_ERR_HIP;
+                                                                                           P * N, nc, h_last);
+  if (launch_status(__func__)) return LINGEN_ERR_HIP;
   return mark(ev, 3, st);
 }
 
@@ -1451,8 +1474,8 @@ int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char
     const int hg = head_group(Hs / s->ngroups);   // a divisor of the heads per B, C group
     ssd_chunk_out_kernel<TS, P, N, Q><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
         x, dt, a.A, B, C, a.D, make_rms(s, mode), Hs, s->ngroups, hg, nc, reinterpret_cast<const TS*>(ws + lay.states),
-        yb);
-    if (hip_status()) return LINGEN_ERR_HIP;
+        yb, nullptr);
+    if (launch_status(__func__)) return LINGEN_ERR_HIP;
     if (int rc = mark(ev, 4, st)) return rc;
   }
   return LINGEN_OK;
@@ -1482,13 +1505,20 @@ int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const A
       const TS* C = reinterpret_cast<const TS*>(static_cast<const char*>(a.C) + bc);
       if (int rc = launch_states<TS, P, N, Q, false>(s, mode, x, dt, a.A, B, ws, st, nullptr, dir)) return rc;
       const TS* states = reinterpret_cast<const TS*>(ws + lay.states);
+      // The one-direction passes fill only the first half of the states
+      // region; the second half (nc*Hs*P*N elements, at least L*Hs*P since
+      // N >= Q in the bf16 families) holds the low half of the first
+      // direction's result for the second pass.
+      static_assert(std::is_same<TS, float>::value || N >= Q, "room for the low half of y");
+      TS* ylo = std::is_same<TS, float>::value ? nullptr
+                                               : reinterpret_cast<TS*>(ws + lay.states) + int64_t(nc) * Hs * P * N;
       if (dir == 0)
         ssd_chunk_out_kernel<TS, P, N, Q, false, false><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
-            x, dt, a.A, B, C, a.D, make_rms(s, mode, 0), Hs, s->ngroups, hg, nc, states, yb);
+            x, dt, a.A, B, C, a.D, make_rms(s, mode, 0), Hs, s->ngroups, hg, nc, states, yb, ylo);
       else
         ssd_chunk_out_kernel<TS, P, N, Q, false, true><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
-            x, dt, a.A, B, C, a.D, make_rms(s, mode, 1), Hs, s->ngroups, hg, nc, states, yb);
-      if (hip_status()) return LINGEN_ERR_HIP;
+            x, dt, a.A, B, C, a.D, make_rms(s, mode, 1), Hs, s->ngroups, hg, nc, states, yb, ylo);
+      if (launch_status(__func__)) return LINGEN_ERR_HIP;
     }
   }
   return LINGEN_OK;
@@ -1516,8 +1546,8 @@ int launch_transposed(const lingen_mate_shape* s, int mode, const TS* u, const f
   const int hg = head_group(Hs / s->ngroups);
   const TS* states = reinterpret_cast<const TS*>(ws + ws_layout(s).states);
   ssd_chunk_out_kernel<TS, P, N, Q, true, false, true, true><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
-      u, dt, A, C, B, nullptr, make_rms(s, mode), Hs, s->ngroups, hg, nc, states, y);
-  if (hip_status()) return LINGEN_ERR_HIP;
+      u, dt, A, C, B, nullptr, make_rms(s, mode), Hs, s->ngroups, hg, nc, states, y, nullptr);
+  if (launch_status(__func__)) return LINGEN_ERR_HIP;
   return LINGEN_OK;
 }
 
@@ -1558,7 +1588,7 @@ int launch_te(const lingen_mate_shape* s, const int shift[3], int masked, const 
     else
       tesa_window_kernel<TS, DH, NWIN, NVALID, false><<<grid, Cfg::NWAVE * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads,
                                                                                        items, yb);
-    if (hip_status()) return LINGEN_ERR_HIP;
+    if (launch_status(__func__)) return LINGEN_ERR_HIP;
   }
   return LINGEN_OK;
 }
@@ -1605,7 +1635,7 @@ namespace lingen {
 // state entering each chunk of the forward scan, then of the reverse scan).
 // wmode: kWeightDt or kWeightAdjoint.
 int scan_states_one(const lingen_mate_shape* s, int mode, const void* xb, const float* dtb, const float* A,
-                    const void* Bb, void* workspace, hipStream_t stream, int wmode) {
+                    const void* Bb, void* workspace, hipStream_t stream, int wmode, float* h_last) {
   char* ws = static_cast<char*>(workspace);
   if (wmode != kWeightDt && wmode != kWeightAdjoint) return LINGEN_ERR_UNSUPPORTED;
   const bool adj = wmode == kWeightAdjoint;
@@ -1613,20 +1643,23 @@ int scan_states_one(const lingen_mate_shape* s, int mode, const void* xb, const 
     case SCAN_F32_P32_N16_Q16: {
       const float* x = static_cast<const float*>(xb);
       const float* B = static_cast<const float*>(Bb);
-      return adj ? launch_states<float, 32, 16, 16, true, kWeightAdjoint>(s, mode, x, dtb, A, B, ws, stream)
-                 : launch_states<float, 32, 16, 16>(s, mode, x, dtb, A, B, ws, stream);
+      return adj ? launch_states<float, 32, 16, 16, true, kWeightAdjoint>(s, mode, x, dtb, A, B, ws, stream, nullptr,
+                                                                          0, h_last)
+                 : launch_states<float, 32, 16, 16>(s, mode, x, dtb, A, B, ws, stream, nullptr, 0, h_last);
     }
     case SCAN_BF16_P64_N64_Q64: {
       const __bf16* x = static_cast<const __bf16*>(xb);
       const __bf16* B = static_cast<const __bf16*>(Bb);
-      return adj ? launch_states<__bf16, 64, 64, 64, true, kWeightAdjoint>(s, mode, x, dtb, A, B, ws, stream)
-                 : launch_states<__bf16, 64, 64, 64>(s, mode, x, dtb, A, B, ws, stream);
+      return adj ? launch_states<__bf16, 64, 64, 64, true, kWeightAdjoint>(s, mode, x, dtb, A, B, ws, stream, nullptr,
+                                                                           0, h_last)
+                 : launch_states<__bf16, 64, 64, 64>(s, mode, x, dtb, A, B, ws, stream, nullptr, 0, h_last);
     }
     case SCAN_BF16_P64_N128_Q128: {
       const __bf16* x = static_cast<const __bf16*>(xb);
       const __bf16* B = static_cast<const __bf16*>(Bb);
-      return adj ? launch_states<__bf16, 64, 128, 128, true, kWeightAdjoint>(s, mode, x, dtb, A, B, ws, stream)
-                 : launch_states<__bf16, 64, 128, 128>(s, mode, x, dtb, A, B, ws, stream);
+      return adj ? launch_states<__bf16, 64, 128, 128, true, kWeightAdjoint>(s, mode, x, dtb, A, B, ws, stream,
+                                                                             nullptr, 0, h_last)
+                 : launch_states<__bf16, 64, 128, 128>(s, mode, x, dtb, A, B, ws, stream, nullptr, 0, h_last);
     }
     default:
       return LINGEN_ERR_UNSUPPORTED;
@@ -1660,7 +1693,7 @@ int lingen_rms_index_device(int32_t mode, int32_t T, int32_t H, int32_t W, int32
   if (L > (int64_t(1) << 31) - 1) return LINGEN_ERR_SHAPE;
   if (int rc = check_ptr(perm_dev)) return rc;
   rms_index_kernel<<<unsigned((L + 255) / 256), 256, 0, stream>>>(RmsMap{mode, T, H, W}, int(L), perm_dev);
-  return hip_status();
+  return launch_status(__func__);
 }
 
 int lingen_rms_gather(const void* src, int64_t row_bytes, int32_t mode, int32_t T, int32_t H, int32_t W, void* dst,
@@ -1675,7 +1708,7 @@ int lingen_rms_gather(const void* src, int64_t row_bytes, int32_t mode, int32_t 
   if ((units + 255) / 256 > int64_t(0x7fffffff)) return LINGEN_ERR_SHAPE;
   rms_gather_kernel<<<unsigned((units + 255) / 256), 256, 0, stream>>>(
       static_cast<const uint4*>(src), row16, RmsMap{mode, T, H, W}, units, static_cast<uint4*>(dst));
-  return hip_status();
+  return launch_status(__func__);
 }
 
 int lingen_ssd_chunk_states(const void* x, const float* dt, const float* A, const void* B, int32_t mode,
@@ -1696,7 +1729,7 @@ int lingen_ssd_chunk_states(const void* x, const float* dt, const float* A, cons
     const char* xb = static_cast<const char*>(x) + b * L * Hs * P * eb;
     const float* dtb = dt + b * L * Hs;
     const char* Bb = static_cast<const char*>(B) + b * L * s->ngroups * N * eb;
-    if (int rc = scan_states_one(s, mode, xb, dtb, A, Bb, ws, stream, kWeightDt)) return rc;
+    if (int rc = scan_states_one(s, mode, xb, dtb, A, Bb, ws, stream, kWeightDt, nullptr)) return rc;
     const unsigned blocks = unsigned((per + 255) / 256);
     if (s->dtype == LINGEN_BF16) {
       const __bf16* st = reinterpret_cast<const __bf16*>(ws + lay.states);
@@ -1707,7 +1740,7 @@ int lingen_ssd_chunk_states(const void* x, const float* dt, const float* A, cons
       states_to_f32_kernel<float><<<blocks, 256, 0, stream>>>(st, h_fwd + b * per, per);
       states_to_f32_kernel<float><<<blocks, 256, 0, stream>>>(st + per, h_bwd + b * per, per);
     }
-    if (hip_status()) return LINGEN_ERR_HIP;
+    if (launch_status(__func__)) return LINGEN_ERR_HIP;
   }
   return LINGEN_OK;
 }
@@ -1731,7 +1764,6 @@ int lingen_ma_fwd_dirs(const void* x_f, const float* dt_f, const float* A_f, con
   if (mode < 0 || mode > 3) return LINGEN_ERR_SHAPE;
   if (int rc = check_all({x_f, dt_f, A_f, B_f, C_f, D_f, x_b, dt_b, A_b, B_b, C_b, D_b, y_ma})) return rc;
   if (int rc = check_ws(shape, workspace, workspace_bytes)) return rc;
-  if (shape->n_review != 0) return LINGEN_ERR_UNSUPPORTED;
   Args af{x_f, dt_f, A_f, B_f, C_f, D_f, nullptr, nullptr, nullptr};
   Args ab{x_b, dt_b, A_b, B_b, C_b, D_b, nullptr, nullptr, nullptr};
   return dispatch_ma_dirs(shape, mode, af, ab, y_ma, static_cast<char*>(workspace), stream);

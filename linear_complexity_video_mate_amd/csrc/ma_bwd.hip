@@ -515,9 +515,131 @@ __global__ __launch_bounds__(256) void ma_bwd_token_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Review tokens.  The review state h_R (the state the pooled review tokens
+// leave, scanned once from zero in canonical order, their outputs
+// discarded) starts both directions, so the adjoint reaching it is the sum
+// of the two directions' initial-state adjoints, dhR: the final carries of
+// the adjoint state pass (the upward walk's carry is the reverse
+// direction's, the downward walk's the forward direction's).  Walking the
+// review scan backwards from dhR with no output adjoint gives, per head,
+// with w_r = exp(A sum_{r' > r} dt_r') and K_r = <dhR, x_r B_r^T>:
+//   dx_r  = w_r dt_r dhR B_r,        dB_r = w_r dt_r dhR^T x_r (over the group's heads),
+//   ddt_r = w_r K_r + A sum_{r' < r} w_r' dt_r' K_r',
+//   dA   += sum_r w_r dt_r K_r sum_{r' > r} dt_r'.
+// Each pooled value is a block mean, so its gradient is then spread evenly
+// over the tokens of its pooling block.
+// ---------------------------------------------------------------------------
+
+constexpr int kRevMaxP = 64, kRevMaxN = 128, kRevMaxR = 256;
+
+// Zero n floats (grid-stride).
+__global__ __launch_bounds__(kThreads) void zero_kernel(float* __restrict__ a, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += int64_t(gridDim.x) * kThreads) a[i] = 0.f;
+}
+
+// One workgroup per head.  h_last: fp32 [2][Hs][P][N]; rx [R][Hs][P], rdt
+// [R][Hs], rb [R][G][N] (the pooled review tokens); gx, gdt like rx, rdt;
+// gb like rb, zeroed by the caller (heads of a group add into it).
+__global__ __launch_bounds__(kThreads) void review_bwd_kernel(const float* __restrict__ h_last,
+                                                             const float* __restrict__ rx,
+                                                             const float* __restrict__ rdt,
+                                                             const float* __restrict__ rb,
+                                                             const float* __restrict__ A, int R, int Hs, int P, int N,
+                                                             int G, float* __restrict__ gx, float* __restrict__ gdt,
+                                                             float* __restrict__ gb, float* __restrict__ dA) {
+  // dhR rows padded by one float: the threads of the first product walk a
+  // column (stride N + 1), those of the second a row.
+  __shared__ float dh[kRevMaxP * (kRevMaxN + 1)];
+  __shared__ float sx[kRevMaxP], sb[kRevMaxN], su[kRevMaxP];
+  __shared__ float sw[kRevMaxR], sK[kRevMaxR];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int grp = h / (Hs / G);
+  const int64_t PN = int64_t(P) * N;
+  for (int i = tid; i < P * N; i += kThreads)
+    dh[(i / N) * (N + 1) + i % N] = h_last[int64_t(h) * PN + i] + h_last[(int64_t(Hs) + h) * PN + i];
+  if (tid == 0) {
+    float suf = 0.f;
+    for (int r = R - 1; r >= 0; --r) {
+      sw[r] = expf(A[h] * suf);
+      suf += rdt[int64_t(r) * Hs + h];
+    }
+  }
+  lds_barrier();
+  for (int r = 0; r < R; ++r) {
+    for (int p = tid; p < P; p += kThreads) sx[p] = rx[(int64_t(r) * Hs + h) * P + p];
+    for (int n = tid; n < N; n += kThreads) sb[n] = rb[(int64_t(r) * G + grp) * N + n];
+    lds_barrier();
+    const float wd = sw[r] * rdt[int64_t(r) * Hs + h];
+    for (int p = tid; p < P; p += kThreads) {
+      float u = 0.f;
+      for (int n = 0; n < N; ++n) u = fmaf(dh[p * (N + 1) + n], sb[n], u);
+      su[p] = u;
+      gx[(int64_t(r) * Hs + h) * P + p] = wd * u;
+    }
+    for (int n = tid; n < N; n += kThreads) {
+      float v = 0.f;
+      for (int p = 0; p < P; ++p) v = fmaf(dh[p * (N + 1) + n], sx[p], v);
+      atomicAdd(&gb[(int64_t(r) * G + grp) * N + n], wd * v);
+    }
+    lds_barrier();
+    if (tid < 64) {
+      float k = 0.f;
+      for (int p = tid; p < P; p += 64) k = fmaf(sx[p], su[p], k);
+      k = sum64(k);
+      if (tid == 0) sK[r] = k;
+    }
+    lds_barrier();
+  }
+  if (tid == 0) {
+    float pre = 0.f;   // sum_{r' < r} w_r' dt_r' K_r'
+    for (int r = 0; r < R; ++r) {
+      const float d = rdt[int64_t(r) * Hs + h];
+      gdt[int64_t(r) * Hs + h] = sw[r] * sK[r] + A[h] * pre;
+      pre += sw[r] * d * sK[r];
+    }
+    float suf = 0.f, da = 0.f;   // suf = sum_{r' > r} dt_r'
+    for (int r = R - 1; r >= 0; --r) {
+      const float d = rdt[int64_t(r) * Hs + h];
+      da += sw[r] * d * sK[r] * suf;
+      suf += d;
+    }
+    atomicAdd(dA + h, da);
+  }
+}
+
+// Review block geometry: pooling block, points per axis and the stride
+// between sampled blocks (in blocks).
+struct RevGeom {
+  int pt, ph, pw, rt, rh, rw, st, sh, sw;
+};
+
+// Adds 1/|block| of review token r's gradients (gx, gdt, gb of batch
+// element blockIdx.z) to every token of its pooling block.  Grid (R,
+// tokens per block, batch); blocks are disjoint, so no two workgroups touch
+// one token.
+__global__ __launch_bounds__(kThreads) void review_scatter_kernel(const float* __restrict__ gx,
+                                                                 const float* __restrict__ gdt,
+                                                                 const float* __restrict__ gb, RevGeom g, int R,
+                                                                 int T, int H, int W, int Hs, int P, int G, int N,
+                                                                 float* __restrict__ dx, float* __restrict__ ddt,
+                                                                 float* __restrict__ dB) {
+  const int r = blockIdx.x, tl = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int i = r / (g.rh * g.rw), j = (r / g.rw) % g.rh, k = r % g.rw;
+  const int a = tl / (g.ph * g.pw), bb = (tl / g.pw) % g.ph, c = tl % g.pw;
+  const int64_t L = int64_t(T) * H * W;
+  const int64_t tok = int64_t(b) * L +
+                      ((int64_t(i * g.st * g.pt + a) * H + (j * g.sh * g.ph + bb)) * W + (k * g.sw * g.pw + c));
+  const float inv = 1.f / float(g.pt * g.ph * g.pw);
+  const int64_t rr = int64_t(b) * R + r;
+  for (int e = tid; e < Hs * P; e += kThreads) dx[tok * Hs * P + e] += gx[rr * Hs * P + e] * inv;
+  for (int e = tid; e < Hs; e += kThreads) ddt[tok * Hs + e] += gdt[rr * Hs + e] * inv;
+  for (int e = tid; e < G * N; e += kThreads) dB[tok * G * N + e] += gb[rr * G * N + e] * inv;
+}
+
 // Byte offsets inside the caller's workspace.
 struct BwdWs {
-  size_t scan1, scan2, R, yh, total;
+  size_t scan1, scan2, R, yh, hlast, gx, gdt, gb, total;
 };
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
@@ -533,13 +655,19 @@ int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   w->scan2 = take(ws_main);
   w->R = take(rows * hs * 4);
   w->yh = take(rows * hs * P * 2);
+  // review tokens: the adjoint states' final carries (one batch element at
+  // a time) and the pooled tokens' gradients of every batch element
+  const size_t nr = size_t(s->batch) * size_t(s->n_review);
+  w->hlast = take(s->n_review ? 2 * hs * P * size_t(s->d_state) * 4 : 0);
+  w->gx = take(nr * hs * P * 4);
+  w->gdt = take(nr * hs * 4);
+  w->gb = take(nr * size_t(s->ngroups) * size_t(s->d_state) * 4);
   w->total = off;
   return LINGEN_OK;
 }
 
 int check_bwd_shape(const lingen_mate_shape* s) {
   if (int rc = validate_shape(s)) return rc;
-  if (s->n_review != 0) return LINGEN_ERR_UNSUPPORTED;
   // the crossing-sum kernel takes bf16 storage with head size 64
   if (s->dtype != LINGEN_BF16 || s->headdim != 64) return LINGEN_ERR_UNSUPPORTED;
   // the crossing-sum kernel is compiled for the two bf16 scan families with P = 64
@@ -591,12 +719,20 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   } while (0)
 #define LINGEN_LAUNCHED()                                             \
   do {                                                                \
-    if (hipGetLastError() != hipSuccess) return LINGEN_ERR_HIP;       \
+    if (launch_status(__func__) != LINGEN_OK) return LINGEN_ERR_HIP;       \
   } while (0)
 
   // dA and dD accumulate from zero
   zero_floats_kernel<<<1, kThreads, 0, stream>>>(dA, dD, Hs);
   LINGEN_LAUNCHED();
+  const int R = shape->n_review;
+  lingen_mate_shape plain = *shape;   // the same scan without review tokens
+  plain.n_review = 0;
+  if (R) {
+    const int64_t nb = int64_t(shape->batch) * R * G * N;   // the pooled B gradients add over heads
+    zero_kernel<<<blocks_for(nb) < 1024 ? blocks_for(nb) : 1024, kThreads, 0, stream>>>(atf(w.gb), nb);
+    LINGEN_LAUNCHED();
+  }
 
   // crossing sums, then ddt, dx, dA, dD
   {
@@ -609,14 +745,28 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
     for (int bi = 0; bi < shape->batch; ++bi) {
       // forward / reverse states of (x, B) and of (x', C) for this batch element, left in the two workspaces
       const int64_t xo = int64_t(bi) * L * Hs * P * eb, bo = int64_t(bi) * L * G * N * eb;
+      // with review tokens, this pass also pools them (into scan1's review
+      // buffers) and starts both walks from their state
       LINGEN_TRY(scan_states_one(shape, mode, static_cast<const char*>(x) + xo, dt + int64_t(bi) * L * Hs, A,
-                                 static_cast<const char*>(B) + bo, ws + w.scan1, stream, kWeightDt));
-      LINGEN_TRY(scan_states_one(shape, mode, static_cast<const char*>(dy) + xo, dt + int64_t(bi) * L * Hs, A,
-                                 static_cast<const char*>(C) + bo, ws + w.scan2, stream, kWeightAdjoint));
+                                 static_cast<const char*>(B) + bo, ws + w.scan1, stream, kWeightDt, nullptr));
+      // the adjoint scan has no review state; its final carries are the
+      // adjoints of the two directions' initial states
+      LINGEN_TRY(scan_states_one(&plain, mode, static_cast<const char*>(dy) + xo, dt + int64_t(bi) * L * Hs, A,
+                                 static_cast<const char*>(C) + bo, ws + w.scan2, stream, kWeightAdjoint,
+                                 R ? atf(w.hlast) : nullptr));
       // the transposed outputs yhat = (M_f^T + M_b^T) dy / dt from the same adjoint states
-      LINGEN_TRY(ma_transposed_one(shape, mode, static_cast<const char*>(dy) + xo, dt + int64_t(bi) * L * Hs, A,
+      LINGEN_TRY(ma_transposed_one(&plain, mode, static_cast<const char*>(dy) + xo, dt + int64_t(bi) * L * Hs, A,
                                    static_cast<const char*>(B) + bo, static_cast<const char*>(C) + bo, ws + w.scan2,
                                    static_cast<char*>(at(w.yh)) + xo, stream));
+      if (R) {
+        const WsLayout rl = ws_layout(shape);
+        const float* s1 = reinterpret_cast<const float*>(ws + w.scan1);
+        review_bwd_kernel<<<Hs, kThreads, 0, stream>>>(
+            atf(w.hlast), s1 + rl.review_x / 4, s1 + rl.review_dt / 4, s1 + rl.review_b / 4, A, R, Hs, P, N, G,
+            atf(w.gx) + int64_t(bi) * R * Hs * P, atf(w.gdt) + int64_t(bi) * R * Hs,
+            atf(w.gb) + int64_t(bi) * R * G * N, dA);
+        LINGEN_LAUNCHED();
+      }
       if (Q == 128 && N == 128)
         ma_bwd_cross_kernel<128, 128><<<cgrid, kCrossThreads, 0, stream>>>(
             xb, dyb, dt, A, static_cast<const __bf16*>(B), static_cast<const __bf16*>(C), st1, st2, per, so, L, Hs,
@@ -633,6 +783,16 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
     ma_bwd_token_kernel<<<tgrid, 256, 0, stream>>>(xb, dyb, dt, A, D, static_cast<const __bf16*>(at(w.yh)), atf(w.R),
                                                    rows, Hs, dx, ddt, dA, dD);
     LINGEN_LAUNCHED();
+    if (R) {
+      RevGeom g;
+      g.pt = shape->rpool_t; g.ph = shape->rpool_h; g.pw = shape->rpool_w;
+      g.rt = shape->rgrid_t; g.rh = shape->rgrid_h; g.rw = shape->rgrid_w;
+      g.st = (shape->T / g.pt) / g.rt; g.sh = (shape->H / g.ph) / g.rh; g.sw = (shape->W / g.pw) / g.rw;
+      const dim3 sgrid{unsigned(R), unsigned(g.pt * g.ph * g.pw), unsigned(shape->batch)};
+      review_scatter_kernel<<<sgrid, kThreads, 0, stream>>>(atf(w.gx), atf(w.gdt), atf(w.gb), g, R, shape->T,
+                                                           shape->H, shape->W, Hs, P, G, N, dx, ddt, dB);
+      LINGEN_LAUNCHED();
+    }
   }
 #undef LINGEN_TRY
 #undef LINGEN_LAUNCHED

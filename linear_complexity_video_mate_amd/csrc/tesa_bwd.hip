@@ -389,7 +389,7 @@ extern "C" int lingen_te_bwd(const void* q, const void* k, const void* v, const 
         static_cast<const __bf16*>(q) + off, static_cast<const __bf16*>(k) + off, static_cast<const __bf16*>(v) + off,
         static_cast<const __bf16*>(d_out) + off, g, shape->attn_heads, static_cast<__bf16*>(dq) + off,
         static_cast<__bf16*>(dk) + off, static_cast<__bf16*>(dv) + off);
-    if (hipGetLastError() != hipSuccess) return LINGEN_ERR_HIP;
+    if (launch_status(__func__) != LINGEN_OK) return LINGEN_ERR_HIP;
   }
   return LINGEN_OK;
 }

@@ -48,6 +48,7 @@ from .mate_oracle import (
     dense_attention_for_queries,
     mate_fwd,
     ma_fwd,
+    ma_bwd,
     mate_block,
 )
 
@@ -77,4 +78,5 @@ __all__ = [
     "mate_fwd",
     "mate_block",
     "ma_fwd",
+    "ma_bwd",
 ]

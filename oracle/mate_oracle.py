@@ -178,7 +178,8 @@ def _fold_groups(d_per_head, like) -> np.ndarray:
     return d_per_head.reshape(L, G, Hs // G, N).sum(axis=2)
 
 
-def ssd_scan_backward(x, dt, A, B, C, D, dy, order: Sequence[int], h0=None, segment: int = 64):
+def ssd_scan_backward(x, dt, A, B, C, D, dy, order: Sequence[int], h0=None, segment: int = 64,
+                      g_final=None, return_dh0: bool = False):
     """Gradients of sum(dy * y) for y = ssd_scan(x, dt, A, B, C, D, order)[0]
     with respect to x, dt, A, B, C, D: (dx, ddt, dA, dB, dC, dD), each in
     the layout of its input.
@@ -192,6 +193,12 @@ def ssd_scan_backward(x, dt, A, B, C, D, dy, order: Sequence[int], h0=None, segm
         dA   += dt_c exp(dt_c A) <h_prev, g>
     per head (dB, dC summed over the heads of a group).  The states h are
     kept every ``segment`` tokens and recomputed within a segment.
+
+    ``g_final`` [Hs, P, N]: the adjoint of the state after the last visited
+    token (the scan's final state feeds something else: the review tokens'
+    state feeds the main scan), zero by default.  With ``return_dh0`` the
+    adjoint of the initial state h0, i.e. g after the walk has passed the
+    first token, is returned as a seventh value.
     """
     x = np.asarray(x, dtype=np.float64)
     dt = np.asarray(dt, dtype=np.float64)
@@ -222,7 +229,8 @@ def ssd_scan_backward(x, dt, A, B, C, D, dy, order: Sequence[int], h0=None, segm
     dBh = np.zeros((x.shape[0], Hs, N))
     dCh = np.zeros((x.shape[0], Hs, N))
     dD = np.zeros(Hs)
-    g = np.zeros((Hs, P, N))                    # adjoint of the state after the token being visited
+    # adjoint of the state after the token being visited
+    g = np.zeros((Hs, P, N)) if g_final is None else np.array(g_final, dtype=np.float64, copy=True)
     for start in reversed(range(0, n, segment)):
         idx = order[start:start + segment]
         states = []
@@ -246,7 +254,8 @@ def ssd_scan_backward(x, dt, A, B, C, D, dy, order: Sequence[int], h0=None, segm
             ddt[c] += np.sum(x[c] * gB, axis=1) + A * a * cross
             dA += dt[c] * a * cross
             g = a[:, None, None] * g
-    return dx, ddt, dA, _fold_groups(dBh, B), _fold_groups(dCh, C), dD
+    grads = (dx, ddt, dA, _fold_groups(dBh, B), _fold_groups(dCh, C), dD)
+    return grads + (g,) if return_dh0 else grads
 
 
 def ssd_bidir_backward(x, dt, A, B, C, D, dy, perm: np.ndarray):
@@ -258,7 +267,55 @@ def ssd_bidir_backward(x, dt, A, B, C, D, dy, perm: np.ndarray):
     return tuple(u + v for u, v in zip(f, b))
 
 
-def ssd_dirs(fwd, bwd, perm: np.ndarray):
+def ma_bwd(x, dt, A, B, C, D, dy, mode: int, T: int, H: int, W: int, review=None):
+    """Gradients of sum(dy * y_MA) for y_MA = ``ma_fwd(x, dt, A, B, C, D,
+    mode, T, H, W, review)``: (dx, ddt, dA, dB, dC, dD) in the layouts of
+    the inputs.
+
+    Without review tokens this is ``ssd_bidir_backward``.  With them, the
+    review state h_R starts both directions, so the adjoints that reach the
+    initial state of the two directions add up to dh_R; h_R is the final
+    state of the scan over the review tokens, whose outputs are discarded, so
+    that scan is walked backwards from dh_R with no output adjoint, giving
+    the gradients of the pooled review x, dt and B and a share of dA; each
+    pooled value is a block mean, so its gradient is spread evenly over the
+    tokens of its pooling block (``review_tokens``).
+    """
+    perm = rms_scan_order(mode, T, H, W)
+    if review is None:
+        return ssd_bidir_backward(x, dt, A, B, C, D, dy, perm)
+    rpool, rgrid = review
+    h0 = review_state(x, dt, A, B, C, T, H, W, rpool, rgrid)
+    f = ssd_scan_backward(x, dt, A, B, C, D, dy, perm, h0=h0, return_dh0=True)
+    b = ssd_scan_backward(x, dt, A, B, C, D, dy, perm[::-1], h0=h0, return_dh0=True)
+    dx, ddt, dA, dB, dC, dD = (u + v for u, v in zip(f[:6], b[:6]))
+    dhR = f[6] + b[6]
+    xr, dtr, Br, Cr = review_tokens(x, dt, B, C, T, H, W, rpool, rgrid)
+    R = xr.shape[0]
+    zero_D = np.zeros(np.shape(A))
+    rg = ssd_scan_backward(xr, dtr, A, Br, Cr, zero_D, np.zeros(xr.shape), np.arange(R), g_final=dhR)
+    dxr, ddtr, dAr, dBr = rg[0], rg[1], rg[2], rg[3]
+    dA = dA + dAr
+    # spread each review token's gradient over its pooling block
+    pt, ph, pw = rpool
+    gt, gh, gw = T // pt, H // ph, W // pw
+    rt, rh, rw = rgrid
+    st, sh, sw = gt // rt, gh // rh, gw // rw
+    cnt = pt * ph * pw
+    grid_views = [a.reshape((T, H, W) + a.shape[1:]) for a in (dx, ddt, dB)]
+    r = 0
+    for i in range(rt):
+        for j in range(rh):
+            for k in range(rw):
+                t0, h0_, w0 = i * st * pt, j * sh * ph, k * sw * pw
+                blk = (slice(t0, t0 + pt), slice(h0_, h0_ + ph), slice(w0, w0 + pw))
+                for view, g in zip(grid_views, (dxr, ddtr, dBr)):
+                    view[blk] += g[r] / cnt
+                r += 1
+    return dx, ddt, dA, dB, dC, dD
+
+
+def ssd_dirs(fwd, bwd, perm: np.ndarray, review=None, grid=None):
     """Bidirectional scan with a parameter set per direction: the scan of
     ``fwd`` = (x, dt, A, B, C, D) along ``perm`` plus the scan of ``bwd`` along
     the reversed order, summed per token; each direction carries its own D
@@ -267,10 +324,24 @@ def ssd_dirs(fwd, bwd, perm: np.ndarray):
     [ABS] names a bidirectional Mamba2 block without saying whether the two
     directions share weights; this is the reading in which they do not (the
     mixer's default, ``ssd_bidir``, shares them).
+
+    ``review`` = (rpool, rgrid) with ``grid`` = (T, H, W): review tokens
+    ([ART] 要领).  Reading taken with a parameter set per direction: each
+    direction forms its review tokens from its own inputs (its x, dt, B, C)
+    and scans them with its own A, so each direction starts from the state
+    its own review tokens leave (``review_state``).
     """
     perm = np.asarray(perm)
-    y_f, _, _ = ssd_scan(*fwd, perm)
-    y_b, _, _ = ssd_scan(*bwd, perm[::-1])
+    h0_f = h0_b = None
+    if review is not None:
+        rpool, rgrid = review
+        T, H, W = grid
+        xf, dtf, Af, Bf, Cf, _ = fwd
+        xb, dtb, Ab, Bb, Cb, _ = bwd
+        h0_f = review_state(xf, dtf, Af, Bf, Cf, T, H, W, rpool, rgrid)
+        h0_b = review_state(xb, dtb, Ab, Bb, Cb, T, H, W, rpool, rgrid)
+    y_f, _, _ = ssd_scan(*fwd, perm, h0=h0_f)
+    y_b, _, _ = ssd_scan(*bwd, perm[::-1], h0=h0_b)
     return y_f + y_b
 
 
@@ -622,7 +693,7 @@ def mate_fwd(x, dt, A, B, C, D, q, k, v, layer_idx: int, T: int, H: int, W: int,
 
 
 def mate_block(u, w, layer_idx: int, T: int, H: int, W: int, Hs: int, P: int, G: int, N: int, Ha: int,
-               win, eps: float = 1e-5):
+               win, eps: float = 1e-5, review=None):
     """The MATE block on u [L, Dm] (canonical token order): the MA branch
     and the TE branch, each with its projections, outputs summed.
 
@@ -637,6 +708,8 @@ def mate_block(u, w, layer_idx: int, T: int, H: int, W: int, Hs: int, P: int, G:
     [Hs, Dm], conv_w_f, conv_w_b [Ch, K], conv_b_f, conv_b_b [Ch], dt_bias,
     A_f, D_f, A_b, D_b [Hs], norm_w [d], w_out_ma [Dm, d], w_q, w_k, w_v
     [d, Dm], w_o [Dm, d], with d = Hs*P = Ha*(attention head size).
+    ``review`` = (rpool, rgrid): review tokens in the MA branch, formed by
+    ``ssd_dirs`` from each direction's scan inputs (after the convolution).
     """
     f = {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
     u = np.asarray(u, dtype=np.float64)
@@ -649,7 +722,8 @@ def mate_block(u, w, layer_idx: int, T: int, H: int, W: int, Hs: int, P: int, G:
     dt_raw = u @ f["w_dt"].T
     xf, Bf, Cf, xb, Bb, Cb, dt = ma_prep(xbc, dt_raw, f["conv_w_f"], f["conv_b_f"], f["conv_w_b"], f["conv_b_b"],
                                          f["dt_bias"], order, Hs, P, G, N)
-    y = ssd_dirs((xf, dt, f["A_f"], Bf, Cf, f["D_f"]), (xb, dt, f["A_b"], Bb, Cb, f["D_b"]), order)
+    y = ssd_dirs((xf, dt, f["A_f"], Bf, Cf, f["D_f"]), (xb, dt, f["A_b"], Bb, Cb, f["D_b"]), order,
+                 review=review, grid=(T, H, W))
     yn = gated_rmsnorm(y.reshape(L, d), z, f["norm_w"], eps, d // G)
     out = yn @ f["w_out_ma"].T
     dh = d // Ha

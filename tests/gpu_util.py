@@ -69,17 +69,25 @@ def row_tol(shape) -> float:
     return 1e-4 if shape.dtype == "f32" else 5e-2
 
 
+ROW_FLOOR = 0.1
+
+
 def check_rows(got, ref, width: int, shape, what: str = "y") -> None:
     """Assert the whole-tensor bound (tol) and the per-row bound (row_tol) on
     rows of `width` consecutive elements (one head's slice of one token).
-    A row's error is taken relative to its own norm, floored at 1e-3 of the
-    mean row norm (a row of the reference that cancels to nearly zero would
-    otherwise demand an exact result)."""
+    A row's error is taken relative to its own norm, floored at ROW_FLOOR of
+    the mean row norm: the arithmetic's error is relative to the size of the
+    terms that add up to a row (the state read-out, the skip term, the
+    attention output), and in rare rows those terms cancel to a small
+    fraction of that size (seen: 0.5% of the mean row norm, the read-out
+    cancelling the skip term), where a bound relative to the row alone would
+    ask for more than bf16 storage carries.  A wrong chunk, window or head
+    leaves errors of the order of the mean row norm, far above the floor."""
     got = np.asarray(got, dtype=np.float64).reshape(-1, width)
     ref = np.asarray(ref, dtype=np.float64).reshape(-1, width)
     num = np.linalg.norm(got - ref, axis=1)
     den = np.linalg.norm(ref, axis=1)
-    den = np.maximum(den, 1e-3 * max(float(den.mean()), 1e-300))
+    den = np.maximum(den, ROW_FLOOR * max(float(den.mean()), 1e-300))
     rows = num / den
     e = rel_l2(got, ref)
     worst = int(np.argmax(rows))

@@ -312,11 +312,14 @@ def test_mate_block_rejects_before_launch(L):
         p[i] = M
         assert call(p[0], ctypes.byref(good), 1024, 4, 1e-5, 0, ctypes.byref(cs), p[1], p[2], n, None) == -4
     assert call(F, ctypes.byref(good), 1024, 4, 1e-5, 0, ctypes.byref(cs), F, F, n - 1, None) == -5
-    # review tokens are not supported by the per-direction scan the block uses
-    rv = mate.to_c_shape(CONFIGS[1].with_(n_review=64, rpool=(2, 4, 4), rgrid=(4, 4, 4)))
-    assert call(F, ctypes.byref(good), 1024, 4, 1e-5, 0, ctypes.byref(rv), F, F, n, None) == -7
+    # review tokens: the per-direction scan the block uses takes them; the
+    # workspace grows by the scan's review buffers
+    rs = CONFIGS[1].with_(n_review=64, rpool=(2, 4, 4), rgrid=(4, 4, 4))
+    rv = mate.to_c_shape(rs)
     size = ctypes.c_size_t(0)
-    assert L.lingen_mate_block_workspace_bytes(ctypes.byref(rv), 1024, ctypes.byref(size)) == -7
+    assert L.lingen_mate_block_workspace_bytes(ctypes.byref(rv), 1024, ctypes.byref(size)) == 0
+    assert size.value - int(n) == mate.lingen_mate_workspace_bytes(rs) - mate.lingen_mate_workspace_bytes(CONFIGS[1])
+    assert call(F, ctypes.byref(good), 1024, 4, 1e-5, 0, ctypes.byref(rv), F, F, n, None) == -5
     assert L.lingen_mate_block_workspace_bytes(ctypes.byref(cs), 1024, None) == -1
     assert L.lingen_mate_block_workspace_bytes(None, 1024, ctypes.byref(size)) == -1
 
@@ -350,12 +353,23 @@ def test_ma_bwd_rejects_before_launch(L):
         p[i] = M
         assert call(*p[:7], 0, ctypes.byref(cs), *p[7:], n, None) == -4, i
     assert call(*[F] * 7, 0, ctypes.byref(cs), *[F] * 7, n - 1, None) == -5
-    # fp32 storage, review tokens, a head size other than 64: not supported
-    for shape in (CONFIGS[0], CONFIGS[1].with_(n_review=64, rpool=(2, 4, 4), rgrid=(4, 4, 4))):
+    # fp32 storage, a head size other than 64: not supported
+    for shape in (CONFIGS[0],):
         c = mate.to_c_shape(shape)
         assert call(*[F] * 7, 0, ctypes.byref(c), *[F] * 7, n, None) == -7
         size = ctypes.c_size_t(0)
         assert L.lingen_ma_bwd_workspace_bytes(ctypes.byref(c), ctypes.byref(size)) == -7
+    # review tokens: supported; the workspace grows by the review buffers of
+    # both scan workspaces, the adjoint states' final carries and the
+    # pooled tokens' gradients
+    rs = CONFIGS[1].with_(n_review=64, rpool=(2, 4, 4), rgrid=(4, 4, 4))
+    R, Hs, P, N, G = 64, rs.ssd_heads, rs.headdim, rs.d_state, rs.ngroups
+    al = lambda b: (b + 255) // 256 * 256
+    grow = (2 * (mate.lingen_mate_workspace_bytes(rs) - mate.lingen_mate_workspace_bytes(CONFIGS[1]))
+            + al(2 * Hs * P * N * 4) + al(R * Hs * P * 4) + al(R * Hs * 4) + al(R * G * N * 4))
+    assert mate.lingen_ma_bwd_workspace_bytes(rs) == n + grow
+    c = mate.to_c_shape(rs)
+    assert call(*[F] * 7, 0, ctypes.byref(c), *[F] * 7, n + grow - 1, None) == -5
     assert call(*[F] * 7, 0, None, *[F] * 7, n, None) == -1
     assert L.lingen_ma_bwd_workspace_bytes(ctypes.byref(cs), None) == -1
 

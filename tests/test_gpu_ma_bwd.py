@@ -5,8 +5,11 @@ workload in its launch configuration and the minute-length workload
 (524,288 tokens) with dy nonzero on one head only (the gradients are linear
 in dy, so every gradient -- dB and dC included -- is that head's, which the
 oracle computes over all tokens; the other heads' dx, ddt, dA, dD must be
-zero).  Bar: relative L2 error at most 2e-2
-per gradient (bf16 storage)."""
+zero); and review tokens (the 16k-token workload with 64 review tokens,
+and the 768p-like workload with its 64 review tokens, dy on one head),
+against the oracle's ma_bwd, whose review path is pinned by finite
+differences.  Bar: relative L2 error at most 2e-2 per gradient (bf16
+storage)."""
 import numpy as np
 import pytest
 
@@ -137,3 +140,88 @@ def test_ma_bwd_minute_length_one_head():
     ref = oracle.ssd_bidir_backward(hx["x"], hx["dt"], hx["A"], inp.f64("B"), inp.f64("C"), hx["D"], dy64,
                                     oracle.rms_scan_order(mode, s.T, s.H, s.W))
     _check(got_head, ref, f"head {head}")
+
+
+@pytest.mark.parametrize("mode,G", [(0, 1), (2, 2)])
+def test_ma_bwd_review_parity(mode, G):
+    torch, mate = need_gpu()
+    from mate_inputs import f32_from_bf16_bits
+    rv = ((2, 4, 4), (4, 4, 4))
+    s = CONFIGS[1].with_(ngroups=G, n_review=64, rpool=rv[0], rgrid=rv[1])
+    inp = make_inputs(s, 1, seed=161, tensors=list(SCAN))
+    dy_bits = _dy(s, 1, 162)
+    say(f"ma_bwd {s.T}x{s.H}x{s.W} bf16 groups={G} mode{mode} review={s.n_review}")
+    d = {n: inp.torch(n, "cuda") for n in SCAN}
+    dy = torch.from_numpy(dy_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    got = mate.lingen_ma_bwd(*(d[n] for n in SCAN), dy, mode, s)
+    torch.cuda.synchronize()
+    f = {n: inp.f64(n) for n in SCAN}
+    dy64 = f32_from_bf16_bits(dy_bits).astype(np.float64)
+    ref = oracle.ma_bwd(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], dy64, mode, s.T, s.H, s.W, review=rv)
+    _check(got, ref, "")
+
+
+def test_ma_bwd_768p_review_one_head():
+    """The 768p-like workload (32x96x96 = 294,912 tokens) with its 64 review
+    tokens, dy on one head, scan order 2: the review state's adjoint
+    reaches the pooled x, dt and B of that head (and B of all)."""
+    torch, mate = need_gpu()
+    from mate_inputs import f32_from_bf16_bits
+    s, cfg_id, head, mode = CONFIGS[4], 4, 21, 2
+    inp = make_inputs(s, cfg_id, seed=171, tensors=list(SCAN), threads=16)
+    dy_bits = _dy(s, cfg_id, 172)
+    dy_bits[:, :head] = 0
+    dy_bits[:, head + 1:] = 0
+    say(f"ma_bwd 768p-like + review mode{mode}, dy on head {head} only")
+    d = {n: inp.torch(n, "cuda") for n in SCAN}
+    dy = torch.from_numpy(dy_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    got = mate.lingen_ma_bwd(*(d[n] for n in SCAN), dy, mode, s)
+    torch.cuda.synchronize()
+    dx, ddt, dA, dB, dC, dD = got
+    others = [h for h in range(s.ssd_heads) if h != head]
+    assert float(dx[0][:, others].abs().max()) == 0.0
+    assert float(ddt[0][:, others].abs().max()) == 0.0
+    assert float(dA[others].abs().max()) == 0.0 and float(dD[others].abs().max()) == 0.0
+    got_head = (dx[0][:, [head]].clone(), ddt[0][:, [head]].clone(), dA[[head]].clone(), dB[0].clone(), dC[0].clone(),
+                dD[[head]].clone())
+    del got, dx, ddt, d, dy
+    say("  oracle over all tokens (one head)")
+    hx = {n: head_f64(inp, n, head) for n in ("x", "dt", "A", "D")}
+    dy64 = f32_from_bf16_bits(dy_bits[:, [head]]).astype(np.float64)
+    ref = oracle.ma_bwd(hx["x"], hx["dt"], hx["A"], inp.f64("B"), inp.f64("C"), hx["D"], dy64, mode, s.T, s.H, s.W,
+                        review=(s.rpool, s.rgrid))
+    _check(got_head, ref, f"head {head}")
+
+
+def test_ma_bwd_review_path_isolated():
+    """The review tokens' share of the gradients is small at these decays
+    (1e-5 of dx, 3e-4 of dB), below what a bf16 bar sees in the whole
+    gradient, so it is checked on its own: dx and dB take nothing from the
+    review state on the main path (dx from the adjoint alone, dB from the
+    adjoint and x), so the difference between the gradients with and
+    without review tokens is exactly the review tokens' share, in fp32 on
+    both sides; it must match the oracle's difference."""
+    torch, mate = need_gpu()
+    from mate_inputs import f32_from_bf16_bits
+    rv = ((2, 4, 4), (4, 4, 4))
+    plain = CONFIGS[1].with_(T=8)
+    s = plain.with_(n_review=64, rpool=rv[0], rgrid=rv[1])
+    mode = 3
+    inp = make_inputs(s, 1, seed=181, tensors=list(SCAN))
+    dy_bits = _dy(s, 1, 182)
+    say(f"ma_bwd review share {s.T}x{s.H}x{s.W} mode{mode}: with minus without review tokens")
+    d = {n: inp.torch(n, "cuda") for n in SCAN}
+    dy = torch.from_numpy(dy_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    got_r = [g.clone() for g in mate.lingen_ma_bwd(*(d[n] for n in SCAN), dy, mode, s)]
+    got_p = mate.lingen_ma_bwd(*(d[n] for n in SCAN), dy, mode, plain)
+    torch.cuda.synchronize()
+    f = [inp.f64(n) for n in SCAN]
+    dy64 = f32_from_bf16_bits(dy_bits).astype(np.float64)
+    ref_r = oracle.ma_bwd(*f, dy64, mode, s.T, s.H, s.W, review=rv)
+    ref_p = oracle.ma_bwd(*f, dy64, mode, s.T, s.H, s.W)
+    for i, name in ((0, "dx"), (3, "dB")):
+        dg = to_np(got_r[i]).reshape(np.shape(ref_r[i])) - to_np(got_p[i]).reshape(np.shape(ref_p[i]))
+        dr = ref_r[i] - ref_p[i]
+        e = rel_l2(dg, dr)
+        say(f"  review share of {name}: rel L2 {e:.3e} (share {rel_l2(ref_r[i], ref_p[i]):.2e} of the gradient)")
+        assert e <= TOL, name

@@ -265,6 +265,38 @@ def test_repeatable_nan_workspace_and_canary():
     assert not bool(torch.isnan(y1.float()).any())
 
 
+def test_debug_sync_mode_same_results():
+    # LINGEN_DEBUG=1 (sync and check after every launch), in a child process
+    # since the variable is read once per process: the mixer's results are
+    # unchanged and every launch reports success
+    import os
+    import subprocess
+    import sys
+
+    need_gpu()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import torch, numpy as np, oracle, linear_complexity_video_mate_amd as mate\n"
+        "from mate_inputs import CONFIGS, make_inputs\n"
+        "s = CONFIGS[0].with_(n_review=4, rpool=(2, 2, 2), rgrid=(1, 2, 2)); inp = make_inputs(s, 0)\n"
+        "d = [inp.torch(n, 'cuda') for n in ('x', 'dt', 'A', 'B', 'C', 'D', 'q', 'k', 'v')]\n"
+        "f = [inp.f64(n) for n in ('x', 'dt', 'A', 'B', 'C', 'D', 'q', 'k', 'v')]\n"
+        "for layer in range(4):\n"
+        "    y = mate.lingen_mate_fwd(*d, layer, s).double().cpu().numpy().reshape(s.L, -1)\n"
+        "    ref = oracle.mate_fwd(*f, layer, s.T, s.H, s.W, s.win, review=(s.rpool, s.rgrid))\n"
+        "    e = np.linalg.norm(y - ref) / np.linalg.norm(ref)\n"
+        "    print(layer, e, flush=True)\n"
+        "    assert e <= 1e-5\n"
+    ) % root
+    say("LINGEN_DEBUG=1 child process: tiny fp32 mixer with review tokens, layers 0-3")
+    r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, LINGEN_DEBUG="1"), capture_output=True,
+                       text=True, timeout=180)
+    say(r.stdout.strip())
+    assert r.returncode == 0, r.stderr[-3000:]
+    assert "lingen:" not in r.stderr
+
+
 def test_rejects_bad_tensors():
     torch, mate = need_gpu()
     s = CONFIGS[0]

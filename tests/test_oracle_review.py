@@ -99,3 +99,44 @@ def test_mate_is_sum_of_branches():
         ym = oracle.ma_fwd(x, dt, A, B, C, D, layer % 4, Tt, Hh, Ww)
         o = oracle.tesa(q, k, v, Tt, Hh, Ww, (2, 4, 4), (1, 2, 2) if layer % 2 else (0, 0, 0))
         np.testing.assert_allclose(y, ym.reshape(-1, Hs * P) + o.reshape(-1, Hs * P), rtol=0, atol=0)
+
+
+def _prepend_scan(x, dt, A, B, C, D, order, R):
+    """Scan [review tokens, main tokens] as one sequence (review tokens first,
+    in canonical order, then the main tokens along ``order``) and return the
+    main tokens' outputs: the review tokens written out as a prefix, with no
+    initial state."""
+    xr, dtr, Br, Cr = oracle.review_tokens(x, dt, B, C, T, H, W, RPOOL, RGRID)
+    cat = lambda a, b: np.concatenate([a, b], axis=0)
+    X, DT, BB, CC = cat(xr, x), cat(dtr, dt), cat(Br, B), cat(Cr, C)
+    y, _, _ = oracle.ssd_scan(X, DT, A, BB, CC, D, np.concatenate([np.arange(R), R + np.asarray(order)]))
+    return y[R:]
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_dirs_review_equals_prepending_own_tokens(mode):
+    # Per-direction parameters: each direction prepends review tokens pooled
+    # from its own inputs and scans them with its own A; two B/C groups.
+    rng = np.random.default_rng(6 + mode)
+    G = 2
+    f = _case(rng, T, H, W, 4, 3, 5)
+    b = _case(rng, T, H, W, 4, 3, 5)
+    L = T * H * W
+    fwd = (f[0], f[1], f[2], rng.standard_normal((L, G, 5)) / 2, rng.standard_normal((L, G, 5)) / 2, f[5])
+    bwd = (b[0], b[1], b[2], rng.standard_normal((L, G, 5)) / 2, rng.standard_normal((L, G, 5)) / 2, b[5])
+    perm = oracle.rms_scan_order(mode, T, H, W)
+    R = int(np.prod(RGRID))
+    y = oracle.ssd_dirs(fwd, bwd, perm, review=(RPOOL, RGRID), grid=(T, H, W))
+    want = _prepend_scan(*fwd, perm, R) + _prepend_scan(*bwd, perm[::-1], R)
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-13)
+    # and the review state does change the result
+    assert np.abs(y - oracle.ssd_dirs(fwd, bwd, perm)).max() > 1e-3
+
+
+def test_dirs_review_with_shared_sets_is_the_mixer_branch():
+    # the same set in both directions reduces to the shared-parameter branch
+    rng = np.random.default_rng(9)
+    s = _case(rng, T, H, W, 2, 3, 4)
+    perm = oracle.rms_scan_order(1, T, H, W)
+    y = oracle.ssd_dirs(s, s, perm, review=(RPOOL, RGRID), grid=(T, H, W))
+    np.testing.assert_allclose(y, oracle.ma_fwd(*s, 1, T, H, W, review=(RPOOL, RGRID)), rtol=1e-13, atol=1e-14)

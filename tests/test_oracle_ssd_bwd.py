@@ -1,8 +1,8 @@
 """Pins for the oracle's backward of the MA branch (ssd_scan_backward,
-ssd_bidir_backward): every gradient against central finite differences of
-the pinned forward scan, per input tensor, with one and two B/C groups and
-every scan order; independence from the checkpoint spacing; the closed-form
-skip gradient."""
+ssd_bidir_backward, ma_bwd): every gradient against central finite
+differences of the pinned forward scan, per input tensor, with one and two
+B/C groups and every scan order, with and without review tokens;
+independence from the checkpoint spacing; the closed-form skip gradient."""
 import numpy as np
 import pytest
 
@@ -135,3 +135,74 @@ def test_transposed_scan_identity_in_chunks():
                 out[o] = acc
         yhat[perm, h] = out
     np.testing.assert_allclose(yhat, yhat_oracle, rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("G,mode", [(1, 0), (2, 3)])
+def test_review_backward_matches_finite_differences(G, mode):
+    """ma_bwd with review tokens: the review state starts both directions and
+    depends on pooled x, dt, B and on A, so every input but C gets a share
+    through it; central finite differences of the pinned forward
+    (oracle.ma_fwd with review) check every gradient."""
+    rng = np.random.default_rng(90 + G + mode)
+    T, H, W, Hs, P, N = 4, 6, 6, 2, 3, 4
+    review = ((2, 3, 3), (2, 2, 2))          # pooled grid 2x2x2, every block sampled
+    params, dy = _inputs(rng, T * H * W, Hs, P, N, G)
+    grads = oracle.ma_bwd(*params, dy, mode, T, H, W, review=review)
+
+    def loss(ps):
+        return float(np.sum(dy * oracle.ma_fwd(*ps, mode, T, H, W, review=review)))
+
+    eps = 1e-6
+    for i, name in enumerate(("x", "dt", "A", "B", "C", "D")):
+        assert grads[i].shape == np.shape(params[i]), name
+        v = rng.standard_normal(np.shape(params[i]))
+        plus = [p.copy() for p in params]
+        minus = [p.copy() for p in params]
+        plus[i] = plus[i] + eps * v
+        minus[i] = minus[i] - eps * v
+        fd = (loss(plus) - loss(minus)) / (2 * eps)
+        an = float(np.sum(grads[i] * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (name, fd, an)
+    # the review path changes the gradients (it is not a no-op)
+    plain = oracle.ma_bwd(*params, dy, mode, T, H, W)
+    assert np.abs(plain[0] - grads[0]).max() > 1e-3
+
+
+def test_review_backward_without_review_is_bidir_backward():
+    rng = np.random.default_rng(95)
+    T, H, W = 2, 2, 3
+    params, dy = _inputs(rng, T * H * W, 2, 3, 2, 1)
+    a = oracle.ma_bwd(*params, dy, 1, T, H, W)
+    b = oracle.ssd_bidir_backward(*params, dy, oracle.rms_scan_order(1, T, H, W))
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_initial_state_adjoint_matches_finite_differences():
+    """return_dh0: the adjoint of the initial state, and g_final: an adjoint
+    on the final state, against finite differences of sum(dy * y) +
+    <gf, h_final> in h0."""
+    rng = np.random.default_rng(96)
+    L, Hs, P, N = 7, 2, 3, 2
+    params, dy = _inputs(rng, L, Hs, P, N, 1)
+    order = rng.permutation(L)
+    h0 = rng.standard_normal((Hs, P, N))
+    gf = rng.standard_normal((Hs, P, N))
+    out = oracle.ssd_scan_backward(*params, dy, order, h0=h0, g_final=gf, return_dh0=True, segment=3)
+
+    def loss(h, ps=params):
+        y, hf, _ = oracle.ssd_scan(*ps, order, h0=h)
+        return float(np.sum(dy * y) + np.sum(gf * hf))
+
+    eps = 1e-6
+    v = rng.standard_normal(h0.shape)
+    fd = (loss(h0 + eps * v) - loss(h0 - eps * v)) / (2 * eps)
+    assert abs(fd - float(np.sum(out[6] * v))) <= 1e-6 * max(1.0, abs(fd))
+    for i in range(6):
+        w = rng.standard_normal(np.shape(params[i]))
+        plus = [p.copy() for p in params]
+        minus = [p.copy() for p in params]
+        plus[i] = plus[i] + eps * w
+        minus[i] = minus[i] - eps * w
+        fd = (loss(h0, plus) - loss(h0, minus)) / (2 * eps)
+        assert abs(fd - float(np.sum(out[i] * w))) <= 1e-6 * max(1.0, abs(fd)), i

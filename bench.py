@@ -38,7 +38,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 STAGES = ("review", "ssd_chunk_state", "ssd_state_pass", "ssd_chunk_out", "tesa_window")
 # Sources that define the mixer's kernels (a traffic record is valid only for them as they stand).
 KERNEL_SRCS = [os.path.join(ROOT, "linear_complexity_video_mate_amd", "csrc", n)
-               for n in ("lingen_kernels.hip", "lingen_device.h", "lingen_window.h")]
+               for n in ("lingen_kernels.hip", "lingen_device.h", "lingen_window.h", "tesa_window.hip")]
 
 
 def kernel_source_sha256() -> str:

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = os.environ.get("LINGEN_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["lingen_host.cpp", "lingen_kernels.hip", "dense_attn.hip", "tesa_bwd.hip", "block_steps.hip",
-           "lingen_block.cpp", "ma_bwd.hip"]
+           "lingen_block.cpp", "ma_bwd.hip", "tesa_window.hip"]
 # The block's projections are plain GEMMs, left to rocBLAS.
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 LINK_FLAGS = [f"-L{ROCM}/lib", "-lrocblas", f"-Wl,-rpath,{ROCM}/lib"]
@@ -49,11 +49,11 @@ def _hipcc() -> str:
     return path
 
 
-# Per-source additions.  The dense attention kernel never produces or
-# consumes NaN (masked scores are -inf, exp2(-inf) = 0), so it is built
-# without NaN semantics: its running maxima then need no NaN-quieting
+# Per-source additions.  The dense and windowed attention kernels never
+# produce or consume NaN (masked scores are -inf, exp2(-inf) = 0), so they
+# are built without NaN semantics: their maxima then need no NaN-quieting
 # instructions around v_max.
-SOURCE_FLAGS = {"dense_attn.hip": ["-fno-honor-nans"]}
+SOURCE_FLAGS = {"dense_attn.hip": ["-fno-honor-nans"], "tesa_window.hip": ["-fno-honor-nans"]}
 
 
 # AddressSanitizer on the host code only (the device code is built as

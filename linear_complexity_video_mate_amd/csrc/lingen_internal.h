@@ -70,4 +70,11 @@ int scan_states_one(const lingen_mate_shape* s, int mode, const void* xb, const 
 int ma_transposed_one(const lingen_mate_shape* s, int mode, const void* ub, const float* dtb, const float* A,
                       const void* Bb, const void* Cb, const void* workspace, void* yb, hipStream_t stream);
 
+// The TE branch for the (bf16, d = 64, 256-token window) family
+// (tesa_window.hip): y = o (accumulate = 0) or y += o (accumulate = 1), one
+// batch element after another.  Shapes and pointers are the caller's to
+// validate.  lingen_status.
+int launch_te_win256(const lingen_mate_shape* s, const int shift[3], int masked, const void* q, const void* k,
+                     const void* v, void* y, int accumulate, hipStream_t st);
+
 }  // namespace lingen

@@ -1599,7 +1599,7 @@ int dispatch_te(const lingen_mate_shape* s, const int shift[3], int masked, cons
                 const void* v, void* y, int accumulate, hipStream_t st) {
   switch (attn_family(s)) {
     case ATTN_F32_D32_W32: return launch_te<float, 32, 32, 32>(s, shift, masked, q, k, v, y, accumulate, st);
-    case ATTN_BF16_D64_W256: return launch_te<__bf16, 64, 256, 256>(s, shift, masked, q, k, v, y, accumulate, st);
+    case ATTN_BF16_D64_W256: return launch_te_win256(s, shift, masked, q, k, v, y, accumulate, st);
     case ATTN_BF16_D64_W27: return launch_te<__bf16, 64, 32, 27>(s, shift, masked, q, k, v, y, accumulate, st);
     default: return LINGEN_ERR_UNSUPPORTED;
   }

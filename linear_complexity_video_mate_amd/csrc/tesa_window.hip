@@ -1,0 +1,365 @@
+// TEmporal Swin Attention over 256-token windows (4x8x8 at the workloads'
+// shapes), bf16 storage, head size 64, on gfx950: softmax attention inside
+// each (possibly shifted) 3D window, plus the fused branch sum y = y_MA + o
+// (page "LinGen：基于Mamba机制的线性复杂度高清长视频生成框架", section 关键算法创新
+// > TESA: fixed small windows, plain and shifted partitions alternating by
+// layer; page "Towards High-Resolution Minute-Length Text-to-Video Generation
+// with Linear Computational Complexity", abstract: MATE = MA branch + TE
+// branch).
+//
+// A window holds only 256 keys, so a wave takes its 16 queries' scores in
+// two halves of 128 keys, each half's scores in registers (8 MFMA result
+// tiles, 32 VGPRs), and the exact maximum of a half before any exponential:
+// one exp2 per score and a single rescale of the output per item (when the
+// second half raises a query's maximum), instead of a running maximum per
+// key block.  Per (window, head) item and wave, per half:
+//   S^T[j][i] = K_j . Q_i        (MFMA; K from LDS, Q fragments in registers)
+//   m_i = max(m_i, max_j S[i][j]) (masked scores are -inf)
+//   P^T = 2^(S^T sc - m sc),  sc = log2(e)/sqrt(d), rounded to bf16
+//   O^T += V^T P^T               (MFMA; V^T by transposing LDS reads)
+//   l_i = sum_j P^T[j][i]        (MFMA against an all-ones operand, from the
+//                                 same rounded weights as the output)
+//   y_i = y_MA_i + O_i / l_i
+// The kernel is persistent (one 16-wave workgroup per compute unit, one
+// 16-query tile per wave).  While an item is computed, the next item's K and
+// V stream into the second of two LDS buffer pairs (direct global-to-LDS
+// loads) and its Q fragments into registers.  The shift is index
+// arithmetic: windows are enumerated on the offset grid, wrapping around each
+// axis, and a wrap class per slot masks scores between tokens that the cut
+// partition separates.
+//
+// Built without NaN semantics: scores are finite or -inf, and the maxima
+// then take v_max3 without NaN-quieting instructions.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "lingen_device.h"
+#include "lingen_internal.h"
+#include "lingen_window.h"
+
+namespace lingen {
+
+namespace {
+
+constexpr int kW256Waves = 16;  // one workgroup per compute unit, four waves per SIMD
+constexpr int kW256QTiles = 1;  // 16-query tiles per wave
+constexpr int kW256KBlocks = 2; // key blocks per item: 128 keys' scores per query tile live at a time
+
+template <bool ACCUMULATE>
+__global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_kernel(const __bf16* __restrict__ q,
+                                                                      const __bf16* __restrict__ k,
+                                                                      const __bf16* __restrict__ v, WinGeom wg,
+                                                                      int Ha, int n_items, int contiguous,
+                                                                      __bf16* __restrict__ y) {
+  constexpr int DH = 64, NWIN = 256, NWAVE = kW256Waves, QT = kW256QTiles, KB = kW256KBlocks;
+  constexpr int BKEYS = NWIN / KB;                 // keys per block
+  constexpr int NTHR = NWAVE * 64;
+  constexpr int KT16 = NWIN / 16;                  // 16-key tiles of S^T
+  constexpr int SUBS = NWIN / 32;                  // 32-key blocks of the P V product
+  constexpr int CPR = DH / 8;                      // 16-byte chunks per K / V row
+  constexpr int DMA = NWIN * CPR / NTHR;           // direct loads per lane and tile
+  static_assert(NWIN * CPR % NTHR == 0 && NWIN / 16 == NWAVE * QT, "query tiles cover the window");
+  static_assert(NWIN <= NTHR, "one window slot per thread");
+  using KT = KvTile<__bf16, DH>;
+  __shared__ __attribute__((aligned(16))) __bf16 sK0[NWIN * DH];
+  __shared__ __attribute__((aligned(16))) __bf16 sK1[NWIN * DH];
+  __shared__ __attribute__((aligned(16))) __bf16 sV0[NWIN * DH];
+  __shared__ __attribute__((aligned(16))) __bf16 sV1[NWIN * DH];
+  __shared__ int sTok[2][NWIN];   // token of each window slot (item parity)
+  __shared__ __attribute__((aligned(16))) int sCls[3][NWIN];   // wrap class of each slot (item mod 3)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int64_t rowstride = int64_t(Ha) * DH;
+  const int nwin_hw = wg.nwh * wg.nww;
+  const float sc = kLog2e * 0.125f;   // log2(e) / sqrt(64)
+
+  // Items (window, head), item = window * Ha + head.  A workgroup walks
+  // either every gridDim-th item (strided) or a contiguous range of items
+  // (contiguous: the heads of one window one after another).
+  int it_begin, it_end, it_step;
+  if (contiguous) {
+    it_begin = int(int64_t(blockIdx.x) * n_items / gridDim.x);
+    it_end = int(int64_t(blockIdx.x + 1) * n_items / gridDim.x);
+    it_step = 1;
+  } else {
+    it_begin = int(blockIdx.x);
+    it_end = n_items;
+    it_step = int(gridDim.x);
+  }
+  struct ItemPos { int item, h, wi, wj, wk; };
+  auto decompose = [&](int it) {
+    const int win = it / Ha;
+    return ItemPos{it, it % Ha, win / nwin_hw, (win / wg.nww) % wg.nwh, win % wg.nww};
+  };
+  const ItemPos step_pos = decompose(it_step);
+  auto advance = [&](ItemPos p) {   // p + it_step in mixed radix (head, wk, wj, wi)
+    p.item += it_step;
+    p.h += step_pos.h;
+    int c = p.h >= Ha;
+    if (c) p.h -= Ha;
+    p.wk += step_pos.wk + c;
+    c = p.wk >= wg.nww;
+    if (c) p.wk -= wg.nww;
+    p.wj += step_pos.wj + c;
+    c = p.wj >= wg.nwh;
+    if (c) p.wj -= wg.nwh;
+    p.wi += step_pos.wi + c;
+    return p;
+  };
+  // This thread's window slot (tid < NWIN).
+  const int slot_a = tid / (wg.wh * wg.ww), slot_b = (tid / wg.ww) % wg.wh, slot_c = tid % wg.ww;
+  auto item_tokens = [&](const ItemPos& p, int* tok, int* cls) {
+    if (tid < NWIN) {
+      int cl;
+      tok[tid] = window_token(wg, p.wi, p.wj, p.wk, slot_a, slot_b, slot_c, cl);
+      cls[tid] = wg.masked ? cl : 0;
+    }
+  };
+  // Direct global-to-LDS loads of an item's K and V tiles: 64 chunks (8
+  // rows) per instruction, each lane fetching the chunk that lands in its
+  // slot of the swizzled tile.
+  auto issue_kv = [&](__bf16* dK, __bf16* dV, const int* tok, int h) {
+#pragma unroll
+    for (int d = 0; d < DMA; ++d) {
+      const int base = (wave * DMA + d) * 64;
+      const int u = base + lane, row = u / CPR, ch = (u % CPR) ^ (row & 7);
+      const int64_t goff = int64_t(tok[row]) * rowstride + int64_t(h) * DH + ch * 8;
+      lds_load16(k + goff, dK + base * 8);
+      lds_load16(v + goff, dV + base * 8);
+    }
+  };
+  // y is read and written in 16-byte pieces: after the exchange in the
+  // epilogue a lane holds d0 .. d0 + 7 of the two 32-wide halves of its row.
+  const int y16_off = 16 * (grp & 1) + 8 * (grp >> 1);
+  // Per-lane registers of an item, loaded one item ahead: the wave's query
+  // tiles (Q fragments, the B operand of S^T = K Q^T) and their tokens.
+  struct QState {
+    bf16x8 qf[QT][2];
+    int tokq[QT];
+  };
+  auto load_q = [&](QState& qs, const int* tok, int h) {
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      qs.tokq[qi] = tok[(wave + qi * NWAVE) * 16 + r16];
+      const __bf16* qrow = q + int64_t(qs.tokq[qi]) * rowstride + int64_t(h) * DH;
+      qs.qf[qi][0] = Frag<__bf16>::load(qrow, lane);
+      qs.qf[qi][1] = Frag<__bf16>::load(qrow + 32, lane);
+    }
+  };
+
+  if (it_begin >= it_end) return;
+  ItemPos pos = decompose(it_begin);
+  item_tokens(pos, sTok[0], sCls[0]);
+  lds_barrier();
+  QState nxt;
+  issue_kv(sK0, sV0, sTok[0], pos.h);
+  load_q(nxt, sTok[0], pos.h);
+
+  // Per-lane LDS offsets of the operand fragments in rows 0..15 of a tile;
+  // a fragment 16 rows further down is 16*DH elements further on.
+  const int offk0 = KT::at(r16, grp * 8), offk1 = KT::at(r16, 32 + grp * 8);
+  int offv[4];
+#pragma unroll
+  for (int et = 0; et < 4; ++et) offv[et] = KT::at(4 * grp + (r16 >> 2), et * 16 + 4 * (r16 & 3));
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.f);
+
+  auto step = [&](int n, const __bf16* cK, const __bf16* cV, __bf16* nK, __bf16* nV) -> bool {
+    const int h = pos.h;
+    const ItemPos npos = advance(pos);
+    const bool has_next = npos.item < it_end;
+    if (has_next) item_tokens(npos, sTok[(n + 1) & 1], sCls[(n + 1) % 3]);
+    wait_vmem();     // this wave's loads of the item (and its earlier stores) are done
+    lds_barrier();   // ... and every wave's; the other buffer pair is free
+    const QState cur = nxt;
+    if (has_next) {
+      issue_kv(nK, nV, sTok[(n + 1) & 1], npos.h);
+      load_q(nxt, sTok[(n + 1) & 1], npos.h);
+    }
+    // The MA output this item adds to arrives while the products run.
+    bf16x8 ya[QT][2];
+    if constexpr (ACCUMULATE) {
+#pragma unroll
+      for (int qi = 0; qi < QT; ++qi) {
+        const __bf16* yrow = y + int64_t(cur.tokq[qi]) * rowstride + int64_t(h) * DH + y16_off;
+        ya[qi][0] = *reinterpret_cast<const bf16x8*>(yrow);
+        ya[qi][1] = *reinterpret_cast<const bf16x8*>(yrow + 32);
+      }
+    }
+    const bool wrapped = wg.masked && window_wrapped(wg, pos.wi, pos.wj, pos.wk);
+    const int* cls = sCls[n % 3];
+    int qcls[QT];
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) qcls[qi] = cls[(wave + qi * NWAVE) * 16 + r16];
+
+    // The keys in KB blocks: the scores of one block for the wave's query
+    // tiles stay in registers (lane (grp, r16) holds keys
+    // BKEYS hf + 16 kt + 4 grp + r of query r16 in s[qi][kt][r]), their
+    // maximum is taken before any exponential, and the output so far is
+    // rescaled when a later block raises a query's maximum.  Every K and V
+    // fragment read from LDS serves all of the wave's query tiles.
+    f32x4 o[QT][4], den[QT];
+    float m[QT];
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      den[qi] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m[qi] = -INFINITY;   // running maximum, scaled units
+#pragma unroll
+      for (int et = 0; et < 4; ++et) o[qi][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    lds_bf16* vb = (lds_bf16*)(cV);
+#pragma unroll
+    for (int hf = 0; hf < KB; ++hf) {
+      f32x4 s[QT][BKEYS / 16];
+#pragma unroll
+      for (int kt = 0; kt < BKEYS / 16; ++kt) {
+        const int row = hf * BKEYS + kt * 16;
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(cK + offk0 + row * DH);
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(cK + offk1 + row * DH);
+#pragma unroll
+        for (int qi = 0; qi < QT; ++qi)
+          s[qi][kt] = mma(k1, cur.qf[qi][1], mma(k0, cur.qf[qi][0], f32x4{0.f, 0.f, 0.f, 0.f}));
+      }
+      if (wrapped) {
+#pragma unroll
+        for (int kt = 0; kt < BKEYS / 16; ++kt) {
+          const int4 kc = *reinterpret_cast<const int4*>(&cls[hf * BKEYS + kt * 16 + grp * 4]);
+#pragma unroll
+          for (int qi = 0; qi < QT; ++qi) {
+            s[qi][kt][0] = kc.x != qcls[qi] ? -INFINITY : s[qi][kt][0];
+            s[qi][kt][1] = kc.y != qcls[qi] ? -INFINITY : s[qi][kt][1];
+            s[qi][kt][2] = kc.z != qcls[qi] ? -INFINITY : s[qi][kt][2];
+            s[qi][kt][3] = kc.w != qcls[qi] ? -INFINITY : s[qi][kt][3];
+          }
+        }
+      }
+      float mref[QT];
+#pragma unroll
+      for (int qi = 0; qi < QT; ++qi) {
+        float mx = fmaxf(fmaxf(s[qi][0][0], s[qi][0][1]), fmaxf(s[qi][0][2], s[qi][0][3]));
+#pragma unroll
+        for (int kt = 1; kt < BKEYS / 16; ++kt)
+          mx = fmaxf(fmaxf(mx, fmaxf(s[qi][kt][0], s[qi][kt][1])), fmaxf(s[qi][kt][2], s[qi][kt][3]));
+        const float mnew = fmaxf(m[qi], max_rows(mx) * sc);
+        // A query whose keys so far are all masked (possible in the first
+        // blocks of a cut window) keeps a zero output: its weights are
+        // exp2(-inf - 0) = 0.  Its own key is always present, so the final
+        // maximum is finite.
+        mref[qi] = mnew == -INFINITY ? 0.f : mnew;
+        if (hf) {
+          const float alpha = fast_exp2(m[qi] - mref[qi]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) den[qi][r] *= alpha;
+#pragma unroll
+          for (int et = 0; et < 4; ++et)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[qi][et][r] *= alpha;
+        }
+        m[qi] = mnew;
+      }
+#pragma unroll
+      for (int sb = 0; sb < BKEYS / 32; ++sb) {
+        const int row = hf * BKEYS + 32 * sb;
+        // P^T operands of keys BKEYS hf + 32 sb .. + 31: lane group g brings
+        // keys 4g .. 4g+3 of both 16-key tiles (the k order of the V^T reads).
+        bf16x8 pb[QT];
+#pragma unroll
+        for (int qi = 0; qi < QT; ++qi) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pb[qi][r] = static_cast<__bf16>(fast_exp2(fmaf(s[qi][2 * sb][r], sc, -mref[qi])));
+            pb[qi][4 + r] = static_cast<__bf16>(fast_exp2(fmaf(s[qi][2 * sb + 1][r], sc, -mref[qi])));
+          }
+          den[qi] = mma(ones, pb[qi], den[qi]);
+        }
+#pragma unroll
+        for (int et = 0; et < 4; ++et) {
+          const bf16x4 lo = lds_read_tr(vb + offv[et] + row * DH);
+          const bf16x4 hi = lds_read_tr(vb + offv[et] + (row + 16) * DH);
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int qi = 0; qi < QT; ++qi) o[qi][et] = mma(vf, pb[qi], o[qi][et]);
+        }
+      }
+    }
+
+    // O^T[e][i]: the lane holds e = 16 et + 4 grp + r of query r16.  One
+    // v_permlane16_swap per register pair exchanges the 4-element pieces of
+    // d-tiles 2 r1 and 2 r1 + 1 between lane groups g and g ^ 1, so that the
+    // lane holds 8 consecutive values and y moves in 16-byte pieces.
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      const float inv = __builtin_amdgcn_rcpf(den[qi][0]);
+#pragma unroll
+      for (int r1 = 0; r1 < 2; ++r1) {
+        float ov[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(o[qi][2 * r1][r]),
+                                                           __float_as_uint(o[qi][2 * r1 + 1][r]), false, false);
+          ov[r] = __uint_as_float(sw[0]);
+          ov[4 + r] = __uint_as_float(sw[1]);
+        }
+        bf16x8 res;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float val = ov[e] * inv;
+          res[e] = static_cast<__bf16>(ACCUMULATE ? static_cast<float>(ya[qi][r1][e]) + val : val);
+        }
+        __bf16* yrow = y + int64_t(cur.tokq[qi]) * rowstride + int64_t(h) * DH + y16_off;
+        *reinterpret_cast<bf16x8*>(yrow + 32 * r1) = res;
+      }
+    }
+    pos = npos;
+    return has_next;
+  };
+
+#pragma unroll 1
+  for (int n = 0;; n += 2) {
+    if (!step(n, sK0, sV0, sK1, sV1)) break;
+    if (!step(n + 1, sK1, sV1, sK0, sV0)) break;
+  }
+}
+
+}  // namespace
+
+// The TE branch for the (bf16, d 64, 256-token window) family, one batch
+// element after another; persistent grid of one workgroup per compute unit.
+int launch_te_win256(const lingen_mate_shape* s, const int shift[3], int masked, const void* q, const void* k,
+                     const void* v, void* y, int accumulate, hipStream_t st) {
+  const WinGeom g = make_wingeom(s, shift, masked);
+  const int64_t L = tokens(s);
+  const int nwin = g.nwt * g.nwh * g.nww;
+  const int64_t per = L * s->attn_heads * 64 * 2;
+  const int ncu = compute_units();
+  if (ncu < 1) return LINGEN_ERR_HIP;
+  for (int b = 0; b < s->batch; ++b) {
+    const int64_t off = int64_t(b) * per;
+    const __bf16* qb = reinterpret_cast<const __bf16*>(static_cast<const char*>(q) + off);
+    const __bf16* kb = reinterpret_cast<const __bf16*>(static_cast<const char*>(k) + off);
+    const __bf16* vb = reinterpret_cast<const __bf16*>(static_cast<const char*>(v) + off);
+    __bf16* yb = reinterpret_cast<__bf16*>(static_cast<char*>(y) + off);
+    const int items = nwin * s->attn_heads;
+    const int grid = items < ncu ? items : ncu;
+    // Item order: a contiguous range per workgroup (the heads of a window
+    // one after another) once a workgroup has at least 128 items; measured
+    // at 256 and 144 items per workgroup (the minute-length and 768p-like
+    // workloads: 2.43 against 2.71 ms and 1.30 against 1.46 ms), while at 64
+    // (the 512p-like workload) the strided order is 2% faster.
+    const int contiguous = items >= 128 * grid ? 1 : 0;
+    if (accumulate)
+      tesa_win256_kernel<true><<<grid, kW256Waves * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, items, contiguous,
+                                                                 yb);
+    else
+      tesa_win256_kernel<false><<<grid, kW256Waves * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, items, contiguous,
+                                                                  yb);
+    if (launch_status(__func__) != LINGEN_OK) return LINGEN_ERR_HIP;
+  }
+  return LINGEN_OK;
+}
+
+}  // namespace lingen

@@ -73,7 +73,9 @@ typedef enum {
   LINGEN_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned          */
   LINGEN_ERR_WORKSPACE = -5,   /* workspace smaller than lingen_mate_workspace_bytes */
   LINGEN_ERR_HIP = -6,         /* a HIP call or kernel launch failed               */
-  LINGEN_ERR_UNSUPPORTED = -7  /* valid shape, but no compiled kernel for it       */
+  LINGEN_ERR_UNSUPPORTED = -7, /* valid shape, but no compiled kernel for it       */
+  LINGEN_ERR_SCRATCH = -8      /* shape needs more workspace than the fixed scratch
+                                  array of lingen_mate_fwd_noalloc holds          */
 } lingen_status;
 
 typedef enum { LINGEN_F32 = 0, LINGEN_BF16 = 1 } lingen_dtype;
@@ -245,6 +247,31 @@ int lingen_mate_fwd_events(const void* x, const float* dt, const float* A, const
                            int32_t layer_idx, const lingen_mate_shape* shape, void* y,
                            void* workspace, size_t workspace_bytes, hipStream_t stream,
                            hipEvent_t* events);
+
+/* Bytes of the device scratch array behind lingen_mate_fwd_noalloc: one
+ * copy per GPU the library runs on, held until the process ends. */
+#define LINGEN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* lingen_mate_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The workspace is a file-scope device array of LINGEN_NOALLOC_SCRATCH_BYTES
+ * (256 MiB) per GPU instead of a caller-provided buffer; the call allocates
+ * and frees nothing, and the caller still passes inputs and the output y.
+ * Shapes whose lingen_mate_workspace_bytes exceeds that size (with the
+ * 512p-like dimensions, more than about 32k tokens) return
+ * LINGEN_ERR_SCRATCH before anything is enqueued; every 16,384-token shape
+ * fits.  Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents (the mixer writes all of it that it reads, so nothing
+ * carries over): calls that overlap on one GPU, on different streams or from
+ * different threads, race on it and must be serialised by the caller.  The
+ * first call on a device looks up the array's device address (the HIP
+ * runtime loads the library's code object for that device if it has not yet
+ * done so).  Arguments, results and other errors as lingen_mate_fwd. */
+int lingen_mate_fwd_noalloc(const void* x, const float* dt, const float* A, const void* B,
+                            const void* C, const float* D,
+                            const void* q, const void* k, const void* v,
+                            int32_t layer_idx, const lingen_mate_shape* shape, void* y,
+                            hipStream_t stream);
 
 /* Dense softmax attention over all L tokens of each sequence, per head:
  *     o_i = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j,   j = 0 .. L-1,

@@ -30,6 +30,7 @@ STATUS_NAMES = {
     -5: "LINGEN_ERR_WORKSPACE",
     -6: "LINGEN_ERR_HIP",
     -7: "LINGEN_ERR_UNSUPPORTED",
+    -8: "LINGEN_ERR_SCRATCH",
 }
 LINGEN_F32, LINGEN_BF16 = 0, 1
 
@@ -48,6 +49,7 @@ EXPORTS = (
     "lingen_te_bwd",
     "lingen_mate_fwd",
     "lingen_mate_fwd_events",
+    "lingen_mate_fwd_noalloc",
     "lingen_dense_attn_fwd",
     "lingen_ma_prep",
     "lingen_gated_rmsnorm",
@@ -107,6 +109,7 @@ def lib() -> ctypes.CDLL:
         "lingen_te_bwd": ([P, P, P, P, I32, I32, I32, I32, SP, P, P, P, P], ctypes.c_int),
         "lingen_mate_fwd": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_mate_fwd_events": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P, P], ctypes.c_int),
+        "lingen_mate_fwd_noalloc": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P], ctypes.c_int),
         "lingen_dense_attn_fwd": ([P, P, P, P, I32, I32, I32, I32, I32, P], ctypes.c_int),
         "lingen_ma_prep": ([P] * 7 + [I32, I32, SP] + [P] * 7 + [P], ctypes.c_int),
         "lingen_gated_rmsnorm": ([P, P, P, ctypes.c_float, I64, I32, I32, I32, P, P], ctypes.c_int),
@@ -378,6 +381,26 @@ def lingen_mate_fwd(x, dt, A, B, C, D, q, k, v, layer_idx: int, shape, out=None,
     py = _need(out, "out", td, n["y"])
     workspace, pw, nw = _workspace(shape, workspace)
     _check("lingen_mate_fwd", lib().lingen_mate_fwd(*args, int(layer_idx), ctypes.byref(cs), py, pw, nw, _stream()))
+    return out
+
+
+def lingen_mate_fwd_noalloc(x, dt, A, B, C, D, q, k, v, layer_idx: int, shape, out=None):
+    """The MATE mixer with the library's fixed device scratch array as its
+    workspace (no allocation inside the call); returns y [batch, L, Hs*P]."""
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    L = shape.T * shape.H * shape.W
+    if out is None:
+        out = torch.empty((shape.batch, L, shape.ssd_heads * shape.headdim), dtype=td, device="cuda")
+    args = [_need(x, "x", td, n["x"]), _need(dt, "dt", torch.float32, n["dt"]),
+            _need(A, "A", torch.float32, n["A"]), _need(B, "B", td, n["B"]), _need(C, "C", td, n["B"]),
+            _need(D, "D", torch.float32, n["D"]), _need(q, "q", td, n["q"]), _need(k, "k", td, n["q"]),
+            _need(v, "v", td, n["q"])]
+    py = _need(out, "out", td, n["y"])
+    _check("lingen_mate_fwd_noalloc", lib().lingen_mate_fwd_noalloc(*args, int(layer_idx), ctypes.byref(cs), py,
+                                                                    _stream()))
     return out
 
 

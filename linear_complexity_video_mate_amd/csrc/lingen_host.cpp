@@ -152,6 +152,7 @@ const char* lingen_status_str(int status) {
     case LINGEN_ERR_WORKSPACE: return "workspace too small";
     case LINGEN_ERR_HIP: return "HIP error";
     case LINGEN_ERR_UNSUPPORTED: return "no compiled kernel for this shape";
+    case LINGEN_ERR_SCRATCH: return "shape needs more workspace than the no-allocation scratch array holds";
     default: return "unknown status";
   }
 }

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert mate.status_str(code) and mate.status_str(code) != "unknown status"
     assert mate.status_str(5) == "unknown status"
 

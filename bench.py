@@ -231,18 +231,24 @@ def cpu_baseline(s, inp, workers):
     }
 
 
+# Kernel (mangled-name fragment) -> the stage name bench.py reports it under.
+KERNEL_STAGE = (("tesa_win256_kernel", "tesa_window"), ("tesa_window_kernel", "tesa_window"),
+                ("ssd_chunk_state_kernel", "ssd_chunk_state"), ("ssd_state_pass_kernel", "ssd_state_pass"),
+                ("ssd_chunk_out_kernel", "ssd_chunk_out"), ("review_pool_kernel", "review"),
+                ("review_state_kernel", "review"), ("rms_gather_kernel", "rms_gather"))
+
+
 def _pmc_means(path):
-    """Mean counter value per kernel (short name) from a rocprofv3 counter CSV."""
+    """Mean counter value per launch of each stage from a rocprofv3 counter
+    CSV (the review stage's two kernels summed per launch)."""
     import csv
-    import re
     acc = {}
     for r in csv.DictReader(open(path)):
-        m = re.search(r"lingen(?:::|\d+)?([a-z_]+?)_kernel", r["Kernel_Name"])
-        if not m:
-            continue
-        name = re.sub(r"^\d+", "", m.group(1))
-        acc.setdefault(name, []).append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+        for frag, stage in KERNEL_STAGE:
+            if frag in r["Kernel_Name"]:
+                acc.setdefault(stage, {}).setdefault(frag, []).append(float(r["Counter_Value"]))
+                break
+    return {stage: sum(sum(v) / len(v) for v in per.values()) for stage, per in acc.items()}
 
 
 def record_traffic(mix_fetch, mix_write, copy_fetch, copy_write, config=2):

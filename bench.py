@@ -327,6 +327,9 @@ def gather_modes(args, mate, torch):
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / args.steps
+        perm, _ = mate.lingen_rms_index(mode, s.T, s.H, s.W)
+        assert torch.equal(dst.view(-1, s.d_inner).view(torch.int16),
+                           src[torch.from_numpy(perm).long().cuda()].view(torch.int16)), f"gather mode {mode}"
         out["modes"][mode] = {"ms": round(ms, 4), "GB/s_read+write": round(2 * nbytes / ms / 1e6, 1),
                               "hbm_frac": round(2 * nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
     print(json.dumps(out), flush=True)
@@ -786,10 +789,13 @@ def main(argv=None):
 
     stage_ms = {name: 0.0 for name in STAGES}
     per_layer = [0.0] * 4
+    per_layer_stage = [{name: 0.0 for name in STAGES} for _ in range(4)]
     for k in range(K):
         e = step_events[k]
         for i, name in enumerate(STAGES):
-            stage_ms[name] += ev.ms(e[i], e[i + 1]) / K
+            t = ev.ms(e[i], e[i + 1])
+            stage_ms[name] += t / K
+            per_layer_stage[k % 4][name] += t / (K / 4)
         per_layer[k % 4] += ev.ms(e[0], e[5]) / (K / 4)
 
     work = kernel_work(s)
@@ -864,6 +870,7 @@ def main(argv=None):
         "linear_scaling": scaling,
         "stages": stages,
         "per_layer_ms": [round(v, 4) for v in per_layer],
+        "per_layer_stage_ms": [{n: round(v, 4) for n, v in d.items() if n in stages} for d in per_layer_stage],
         "path_vs_compulsory_hbm": round(comp / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "wall_s_timed_region": round(wall, 3),
     }

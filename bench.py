@@ -443,6 +443,11 @@ def block_steps(args, mate, torch):
     xf, Bf, Cf, xb, Bb, Cb, dt = outs
     dirs_ms = timed(lambda i: mate.lingen_ma_fwd_dirs((xf, dt, A, Bf, Cf, D), (xb, dt, A, Bb, Cb, D), i % 4, s,
                                                       out=y_ma, workspace=ws))
+    fused_ms = None
+    if s.dtype == "bf16" and not s.n_review:
+        fused_ms = timed(lambda i: mate.lingen_ma_fwd_dirs_conv(
+            d["xbc"], d["dt_raw"], (d["conv_w_f"], d["conv_b_f"]), (d["conv_w_b"], d["conv_b_b"]), d["dt_bias"],
+            A, D, A, D, i % 4, s, out=y_ma, workspace=ws))
     e = s.elem_bytes
     ch = s.d_inner + 2 * s.ngroups * s.d_state
     prep_bytes = 3 * s.L * ch * e + 2 * s.L * s.ssd_heads * 4      # xbc in, both directions out; dt_raw in, dt out
@@ -453,6 +458,9 @@ def block_steps(args, mate, torch):
                      "hbm_frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
     out["ma_fwd_dirs_ms"] = round(dirs_ms, 4)
     out["block_ms"] = round(prep_ms + dirs_ms + norm_ms, 4)
+    if fused_ms is not None:   # the convolution and softplus inside the scan kernels
+        out["ma_fwd_dirs_conv_ms"] = round(fused_ms, 4)
+        out["block_fused_ms"] = round(fused_ms + norm_ms, 4)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -502,6 +510,13 @@ def mate_block(args, mate, torch):
     dirs_ms = timed(lambda i: mate.lingen_ma_fwd_dirs((xf, dt, w["A_f"], Bf, Cf, w["D_f"]),
                                                       (xb, dt, w["A_b"], Bb, Cb, w["D_b"]), i % 4, s, out=y,
                                                       workspace=sws))
+    # The fused form (convolution and softplus inside the scan kernels) is
+    # timed beside the two-call form the block takes.
+    fused = s.dtype == "bf16" and not s.n_review
+    if fused:
+        conv_ms = timed(lambda i: mate.lingen_ma_fwd_dirs_conv(
+            xbc, dt_raw, (w["conv_w_f"], w["conv_b_f"]), (w["conv_w_b"], w["conv_b_b"]), w["dt_bias"], w["A_f"],
+            w["D_f"], w["A_b"], w["D_b"], i % 4, s, out=y, workspace=sws))
     z = torch.empty_like(y).normal_()
     yn = torch.empty_like(y)
     norm_ms = timed(lambda i: mate.lingen_gated_rmsnorm(y, z, w["norm_w"], 1e-5, d // s.ngroups, out=yn))
@@ -514,8 +529,9 @@ def mate_block(args, mate, torch):
     res = {"workload": CONFIG_NOTES[args.config], "d_model": dm, "steps": args.steps,
            "block_ms": round(block_ms, 4), "tokens_per_s": round(rows / (block_ms / 1e3), 1),
            "library_kernels_ms": {"ma_prep": round(prep_ms, 4), "ma_fwd_dirs": round(dirs_ms, 4),
+                                  "ma_fwd_dirs_conv": round(conv_ms, 4) if fused else None,
                                   "gated_rmsnorm": round(norm_ms, 4), "te_fwd": round(te_ms, 4),
-                                  "sum": round(own, 4)},
+                                  "sum_of_the_blocks_own_steps": round(own, 4)},
            "projections": {"gemm_flops": gemm_flops, "ms_by_difference": round(gemm_ms, 4),
                            "TFLOP/s": round(gemm_flops / gemm_ms / 1e9, 1) if gemm_ms > 0 else None}}
     print(json.dumps(res), flush=True)

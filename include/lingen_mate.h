@@ -369,6 +369,31 @@ int lingen_ma_prep(const void* xbc, const float* dt_raw, const float* conv_w_f,
                    const lingen_mate_shape* shape, void* x_f, void* B_f, void* C_f,
                    void* x_b, void* B_b, void* C_b, float* dt, hipStream_t stream);
 
+/* lingen_ma_prep followed by lingen_ma_fwd_dirs in one pass per direction:
+ * the convolution, SiLU and softplus are taken inside the scan kernels, on
+ * the rows the scan reads (each chunk also reads the conv_k - 1 positions
+ * before it), and none of x_f .. C_b or dt is written to memory.  Results
+ * equal those of the two calls: every value is formed with the same
+ * operations in the same order.
+ *   xbc, dt_raw, dt_bias, conv_w_f/_b, conv_b_f/_b, conv_k, mode: as
+ *                 lingen_ma_prep.   A_f, D_f, A_b, D_b: as lingen_ma_fwd_dirs
+ *                 (the dt of both directions is softplus(dt_raw + dt_bias)).
+ *   y_ma:         device output, layout of y.
+ *   workspace:    device, lingen_mate_workspace_bytes(shape) bytes.
+ * It reads xBC twice per direction instead of writing and reading the six
+ * convolved tensors, but forms the convolution in both scan kernels of each
+ * direction; lingen_mate_block_fwd takes the two calls, the faster form on
+ * MI355X at the benchmark workloads.
+ * Errors: those of lingen_ma_prep and lingen_ma_fwd_dirs;
+ * LINGEN_ERR_UNSUPPORTED for fp32 storage or review tokens
+ * (shape->n_review > 0), which take the two calls instead. */
+int lingen_ma_fwd_dirs_conv(const void* xbc, const float* dt_raw, const float* dt_bias,
+                            int32_t conv_k, const float* conv_w_f, const float* conv_b_f,
+                            const float* A_f, const float* D_f, const float* conv_w_b,
+                            const float* conv_b_b, const float* A_b, const float* D_b,
+                            int32_t mode, const lingen_mate_shape* shape, void* y_ma,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* After the scan: for every row r of `rows` and channel c of `dim`,
  *   g[r, c]   = y[r, c] * silu(z[r, c]),
  *   out[r, c] = g[r, c] / sqrt(mean_{c' in group(c)} g[r, c']^2 + eps) * weight[c],

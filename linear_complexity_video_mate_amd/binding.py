@@ -52,6 +52,7 @@ EXPORTS = (
     "lingen_mate_fwd_noalloc",
     "lingen_dense_attn_fwd",
     "lingen_ma_prep",
+    "lingen_ma_fwd_dirs_conv",
     "lingen_gated_rmsnorm",
     "lingen_mate_block_workspace_bytes",
     "lingen_mate_block_fwd",
@@ -112,6 +113,7 @@ def lib() -> ctypes.CDLL:
         "lingen_mate_fwd_noalloc": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P], ctypes.c_int),
         "lingen_dense_attn_fwd": ([P, P, P, P, I32, I32, I32, I32, I32, P], ctypes.c_int),
         "lingen_ma_prep": ([P] * 7 + [I32, I32, SP] + [P] * 7 + [P], ctypes.c_int),
+        "lingen_ma_fwd_dirs_conv": ([P, P, P, I32] + [P] * 8 + [I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_gated_rmsnorm": ([P, P, P, ctypes.c_float, I64, I32, I32, I32, P, P], ctypes.c_int),
         "lingen_mate_block_workspace_bytes": ([SP, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "lingen_ma_bwd_workspace_bytes": ([SP, ctypes.POINTER(SZ)], ctypes.c_int),
@@ -476,6 +478,38 @@ def lingen_ma_prep(xbc, dt_raw, conv_f, conv_b, dt_bias, mode: int, shape, outs=
     po.append(_need(outs[6], "dt", f32, n["dt"]))
     _check("lingen_ma_prep", lib().lingen_ma_prep(*args, K, int(mode), ctypes.byref(cs), *po, _stream()))
     return tuple(outs)
+
+
+def lingen_ma_fwd_dirs_conv(xbc, dt_raw, conv_f, conv_b, dt_bias, A_f, D_f, A_b, D_b, mode: int, shape, out=None,
+                            workspace=None):
+    """lingen_ma_prep and lingen_ma_fwd_dirs in one pass per direction (the
+    convolution, SiLU and softplus taken inside the scan kernels): arguments
+    as those two calls; returns y_ma [batch, L, Hs*P]."""
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    L = shape.T * shape.H * shape.W
+    d, gn = shape.ssd_heads * shape.headdim, shape.ngroups * shape.d_state
+    ch = d + 2 * gn
+    (wf, bf), (wb, bb) = conv_f, conv_b
+    if wf.dim() != 2 or wf.shape[0] != ch or wb.shape != wf.shape:
+        raise ValueError(f"convolution weights must be [{ch}, K] tensors of one shape")
+    K = int(wf.shape[1])
+    if out is None:
+        out = torch.empty((shape.batch, L, d), dtype=td, device="cuda")
+    f32 = torch.float32
+    args = [_need(xbc, "xbc", td, shape.batch * L * ch), _need(dt_raw, "dt_raw", f32, n["dt"]),
+            _need(dt_bias, "dt_bias", f32, shape.ssd_heads), K,
+            _need(wf, "conv_w_f", f32, ch * K), _need(bf, "conv_b_f", f32, ch),
+            _need(A_f, "A_f", f32, n["A"]), _need(D_f, "D_f", f32, n["D"]),
+            _need(wb, "conv_w_b", f32, ch * K), _need(bb, "conv_b_b", f32, ch),
+            _need(A_b, "A_b", f32, n["A"]), _need(D_b, "D_b", f32, n["D"])]
+    py = _need(out, "out", td, n["y"])
+    workspace, pw, nw = _workspace(shape, workspace)
+    _check("lingen_ma_fwd_dirs_conv",
+           lib().lingen_ma_fwd_dirs_conv(*args, int(mode), ctypes.byref(cs), py, pw, nw, _stream()))
+    return out
 
 
 def lingen_gated_rmsnorm(y, z, weight, eps: float, group: int, out=None):

@@ -22,9 +22,6 @@ namespace lingen {
 
 namespace {
 
-// v * sigmoid(v) with the hardware exp and reciprocal (about 1 ulp each).
-__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
-
 // 16 bytes of channels: 8 bf16 or 4 fp32, widened to fp32 in registers.
 template <typename TS> struct Unit16;
 template <> struct Unit16<__bf16> {
@@ -267,8 +264,7 @@ __global__ __launch_bounds__(256) void softplus_bias_kernel(const float* __restr
                                                             float* __restrict__ out) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n) return;
-  const float a = raw[i] + bias[i % heads];
-  out[i] = fmaxf(a, 0.f) + log1pf(expf(-fabsf(a)));
+  out[i] = softplus(raw[i] + bias[i % heads]);
 }
 
 constexpr int kNormThreads = 256;

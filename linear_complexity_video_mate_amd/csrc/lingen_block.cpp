@@ -159,14 +159,19 @@ extern "C" int lingen_mate_block_fwd(const void* u, const lingen_mate_block_weig
   if ((rc = gemm_rows(stream, et, et, rows, ch, d_model, u, w->w_xbc, ws + L.xbc, 0.f))) return rc;
   if ((rc = gemm_rows(stream, et, rocblas_datatype_f32_r, rows, hs, d_model, u, w->w_dt, ws + L.dt_raw, 0.f)))
     return rc;
+  // The convolution, SiLU and softplus as a pass of their own, then the
+  // per-direction scan.  (lingen_ma_fwd_dirs_conv takes the three steps
+  // inside the scan kernels with identical results, but on this GPU it is
+  // the slower form: the convolution is formed again by both scan kernels of
+  // each direction, and their vector-ALU time outgrows the pass it saves.)
+  const float* dt_raw = reinterpret_cast<const float*>(ws + L.dt_raw);
   float* dt = reinterpret_cast<float*>(ws + L.dt);
-  if ((rc = lingen_ma_prep(ws + L.xbc, reinterpret_cast<const float*>(ws + L.dt_raw), w->conv_w_f, w->conv_b_f,
-                           w->conv_w_b, w->conv_b_b, w->dt_bias, conv_k, mode, shape, ws + L.xf, ws + L.bf,
-                           ws + L.cf, ws + L.xb, ws + L.bb, ws + L.cb, dt, stream)))
+  if ((rc = lingen_ma_prep(ws + L.xbc, dt_raw, w->conv_w_f, w->conv_b_f, w->conv_w_b, w->conv_b_b, w->dt_bias,
+                           conv_k, mode, shape, ws + L.xf, ws + L.bf, ws + L.cf, ws + L.xb, ws + L.bb, ws + L.cb, dt,
+                           stream)))
     return rc;
-  if ((rc = lingen_ma_fwd_dirs(ws + L.xf, dt, w->A_f, ws + L.bf, ws + L.cf, w->D_f, ws + L.xb, dt, w->A_b,
-                               ws + L.bb, ws + L.cb, w->D_b, mode, shape, ws + L.y, ws + L.scan,
-                               L.total - L.scan, stream)))
+  if ((rc = lingen_ma_fwd_dirs(ws + L.xf, dt, w->A_f, ws + L.bf, ws + L.cf, w->D_f, ws + L.xb, dt, w->A_b, ws + L.bb,
+                               ws + L.cb, w->D_b, mode, shape, ws + L.y, ws + L.scan, L.total - L.scan, stream)))
     return rc;
   // gated norm into the xBC buffer (no longer needed), one group per B/C group
   if ((rc = lingen_gated_rmsnorm(ws + L.y, ws + L.z, w->norm_w, norm_eps, rows, d, d / shape->ngroups,

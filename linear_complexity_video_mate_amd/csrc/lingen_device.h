@@ -20,6 +20,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 // denormal, which is far below every tolerance the callers work to.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// v * sigmoid(v) with the hardware exp and reciprocal (about 1 ulp each): the
+// activation after the scan-order convolution of the MA branch.  The
+// standalone convolution and the one fused into the scan kernels share it, so
+// the two paths round alike.
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
+
+// softplus(a) = log(1 + e^a), written so that neither term overflows.
+__device__ __forceinline__ float softplus(float a) { return fmaxf(a, 0.f) + log1pf(expf(-fabsf(a))); }
+
 // Workgroup barrier for LDS traffic only.  The waves of a workgroup exchange
 // data through LDS alone (never through global memory), so the barrier waits
 // for this wave's LDS accesses but leaves its global loads and stores in

@@ -257,10 +257,11 @@ struct __attribute__((aligned(16))) ChunkSched {
   float exc[WITH_EXC ? HGM : 1][WITH_EXC ? Q : 4];   // exc = cum - a when not kept
 };
 
+// dt_bias (when not null): the schedule takes softplus(dt + dt_bias[h]).
 template <int Q, int NTHR, int HGM, bool WITH_EXC>
 __device__ __forceinline__ void load_chunk_schedule(ChunkSched<Q, HGM, WITH_EXC>& cs, const float* __restrict__ dt,
                                                     const float* __restrict__ A, RmsMap rms, int c, int Hs, int h0,
-                                                    int hg) {
+                                                    int hg, const float* __restrict__ dt_bias = nullptr) {
   const int tid = threadIdx.x, wave = tid >> 6;
   constexpr int nwave = NTHR / 64;
   for (int i = tid; i < Q; i += NTHR) cs.tok[i] = rms.canon(c * Q + i);
@@ -275,7 +276,7 @@ __device__ __forceinline__ void load_chunk_schedule(ChunkSched<Q, HGM, WITH_EXC>
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int u = tid + it * NTHR;
-    if (u < Q * hg) cs.dt[u % hg][u / hg] = v[it];
+    if (u < Q * hg) cs.dt[u % hg][u / hg] = dt_bias ? softplus(v[it] + dt_bias[h0 + u % hg]) : v[it];
   }
   lds_barrier();
   for (int j = wave; j < hg; j += nwave) wave_chunk_prefix<Q, WITH_EXC>(cs.dt[j], A[h0 + j], cs.cum[j], cs.exc[WITH_EXC ? j : 0]);
@@ -474,13 +475,191 @@ struct StateCfg {
 // consecutive tokens far apart, while the transposed LDS stores stay
 // spread over the banks.
 constexpr int kLptX = 2, kLptB = 2;
+
+// ---------------------------------------------------------------------------
+// The Mamba-2 steps between the input projection and the scan, fused into the
+// scan kernels of a scan with a parameter set per direction (page
+// "视频生成模子太贵太慢如何办？", section 要领: the MA branch is a
+// bidirectional Mamba2 block).  x, B and C are SiLU of a causal depthwise
+// convolution of the xBC channels along the scan order of the direction, and
+// dt = softplus(dt_raw + dt_bias).  A chunk's Q positions read the
+// kConvTaps - 1 positions before it as well (its halo).  Fewer taps than
+// kConvTaps run as kConvTaps with leading zero weights: fma(0, v, a) = a for
+// the finite inputs here, so every tap count takes the same roundings as the
+// standalone convolution (bias first, then the taps oldest first, SiLU,
+// rounding to the storage type).
+// ---------------------------------------------------------------------------
+constexpr int kConvTaps = 4;
+constexpr int kConvHalo = kConvTaps - 1;
+constexpr int kConvW = kConvTaps + 1;   // rows of a weight table: the padded taps, then the bias
+
+// The thread index through an empty asm statement: values formed from it
+// inside a loop are formed again on every pass instead of being kept in
+// registers across the loop (the fused kernels' per-head staging addresses
+// otherwise outgrow the register budget and spill).
+__device__ __forceinline__ int fresh_tid() {
+  int t = int(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+struct ConvIn {
+  const float* w = nullptr;        // [ch][K] taps per channel
+  const float* b = nullptr;        // [ch] biases
+  const float* dt_bias = nullptr;  // [Hs]; null: dt is taken as given
+  int K = 0;                       // taps, 1 .. kConvTaps
+  int ch = 0;                      // channels of an xBC row (its stride in elements)
+  int coff_b = 0, coff_c = 0;      // first channel of B and of C (x starts at 0)
+};
+
+// Token of row j of a chunk's raw rows: rows 0 .. kConvHalo - 1 are the halo
+// (scan positions c*Q - kConvHalo + j), the others the chunk's own
+// positions.  Halo rows before the sequence (chunk 0 only) give the chunk's
+// first token instead, a valid row whose data the staging replaces by
+// zeros: every load is then issued unconditionally (no branch around a
+// load, which would make the wait counters drain at the join).
+// The halo's tokens are formed once per chunk (halo_tokens, before the
+// schedule's barrier) and read from LDS with the chunk's own.
+template <int Q>
+__device__ __forceinline__ void halo_tokens(int* htok, const RmsMap& m, int c) {
+  const int j = int(threadIdx.x);
+  if (j < kConvHalo) htok[j] = m.canon(c > 0 ? c * Q - kConvHalo + j : 0);
+}
+template <typename Sched>
+__device__ __forceinline__ int raw_row_token(const Sched& cs, const int* htok, int j) {
+  return j >= kConvHalo ? cs.tok[j - kConvHalo] : htok[j];
+}
+
+// Conv weights of COLS channels from channel c0, as [kConvW][COLS] (the taps
+// padded at the front, then the bias): fetched into registers, then written
+// to LDS by the caller's workgroup of NTHR threads.
+template <int COLS, int NTHR>
+struct ConvWeights {
+  static constexpr int PER = COLS * kConvW;
+  static constexpr int IT = (PER + NTHR - 1) / NTHR;
+  float w[IT], b[IT];
+  int pad;   // taps of the table before the caller's first
+  // Both candidates are loaded from clamped, valid indices and the entry is
+  // chosen when it is stored (no branch around a load).
+  __device__ __forceinline__ void load(const ConvIn& cv, int c0) {
+    const int t = fresh_tid();
+    pad = kConvTaps - cv.K;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = PER % NTHR == 0 ? t + it * NTHR : min(t + it * NTHR, PER - 1);
+      const int k = i / COLS, col = i % COLS;
+      w[it] = cv.w[int64_t(c0 + col) * cv.K + min(max(k - pad, 0), cv.K - 1)];
+      b[it] = cv.b[c0 + col];
+    }
+  }
+  __device__ __forceinline__ void store(float* dst) const {
+    const int t = fresh_tid();
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = t + it * NTHR, k = i / COLS;
+      if (PER % NTHR == 0 || i < PER) dst[i] = k == kConvTaps ? b[it] : (k < pad ? 0.f : w[it]);
+    }
+  }
+};
+
+// A chunk's raw rows (halo first) of COLS channels, each row from `row(j)`,
+// staged through registers: the chunk's own rows go to `main` (tile layout
+// TL), the halo rows to `halo` ([kConvHalo][COLS]), as zeros when zero_halo
+// (chunk 0: the halo lies before the sequence).  Lanes past the last piece
+// load the last piece again and store nothing.
+template <typename TS, int Q, int COLS, int NTHR>
+struct RawRows {
+  static constexpr int VEC = Vec16<TS>::n, PR = COLS / VEC;
+  static constexpr int TOTAL = (Q + kConvHalo) * PR;
+  static constexpr int IT = (TOTAL + NTHR - 1) / NTHR;
+  uint4 v[IT];
+  template <typename Row>
+  __device__ __forceinline__ void load(Row row) {
+    const int t = fresh_tid();
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int u = TOTAL % NTHR == 0 ? t + it * NTHR : min(t + it * NTHR, TOTAL - 1);
+      v[it] = *reinterpret_cast<const uint4*>(row(u / PR) + (u % PR) * VEC);
+    }
+  }
+  template <typename TL>
+  __device__ __forceinline__ void store(TS* main, TS* halo, bool zero_halo) const {
+    const int t = fresh_tid();
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int u = t + it * NTHR;
+      if (TOTAL % NTHR == 0 || u < TOTAL) {
+        const int j = u / PR, col = (u % PR) * VEC;
+        if (j < kConvHalo) *reinterpret_cast<uint4*>(&halo[j * COLS + col]) = zero_halo ? uint4{0u, 0u, 0u, 0u} : v[it];
+        else *reinterpret_cast<uint4*>(&main[TL::at(j - kConvHalo, col)]) = v[it];
+      }
+    }
+  }
+};
+
+// 16 bytes of raw row r (0 .. Q + kConvHalo - 1) at column col, widened.
+template <typename TS, typename TL, int COLS>
+__device__ __forceinline__ void raw_read(const TS* main, const TS* halo, int r, int col, float (&v)[Vec16<TS>::n]) {
+  Vec16<TS> u;
+  u.u = *reinterpret_cast<const uint4*>(r < kConvHalo ? &halo[r * COLS + col] : &main[TL::at(r - kConvHalo, col)]);
+#pragma unroll
+  for (int e = 0; e < Vec16<TS>::n; ++e) v[e] = to_f32(u.e[e]);
+}
+
+// Convolution + SiLU of R consecutive positions s0 .. s0 + R - 1 of the
+// chunk for the VEC channels at column col (raw rows s0 .. s0 + R + 2), with
+// the weights wt ([kConvW][COLS] in LDS); out in the storage type.  Taps
+// outermost, so one tap's weights are live at a time.
+template <typename TS, typename TL, int COLS, int R>
+__device__ __forceinline__ void conv_rows(const TS* main, const TS* halo, const float* wt, int s0, int col,
+                                          TS (&out)[R][Vec16<TS>::n]) {
+  constexpr int V = Vec16<TS>::n;
+  static_assert(V % 4 == 0, "whole float4 pieces of the weight rows");
+  auto weights = [&](int k, float (&w)[V]) {
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      const float4 a = *reinterpret_cast<const float4*>(&wt[k * COLS + col + 4 * q]);
+      w[4 * q + 0] = a.x; w[4 * q + 1] = a.y; w[4 * q + 2] = a.z; w[4 * q + 3] = a.w;
+    }
+  };
+  float acc[R][V];
+  {
+    float bias[V];
+    weights(kConvTaps, bias);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[r][e] = bias[e];
+  }
+#pragma unroll
+  for (int k = 0; k < kConvTaps; ++k) {
+    float w[V];
+    weights(k, w);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float v[V];
+      raw_read<TS, TL, COLS>(main, halo, s0 + r + k, col, v);   // tap k of position s0 + r
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[r][e] = fmaf(w[e], v[e], acc[r][e]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < V; ++e) out[r][e] = from_f32<TS>(silu(acc[r][e]));
+}
+
 // BIDIR = false: the forward direction's chunk states only (a scan whose
 // backward direction has parameters of its own).
-template <typename TS, int P, int N, int Q, bool BIDIR = true, int WM = kWeightDt>
-__global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
+// CONV: x and B are the convolved xBC channels (the fused steps above): x
+// and B both point at the xBC rows, cv gives the convolution and dt_bias.
+// Two workgroups share a compute unit (at most 128 VGPRs).
+template <typename TS, int P, int N, int Q, bool BIDIR = true, int WM = kWeightDt, bool CONV = false>
+__global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64), 4) void ssd_chunk_state_kernel(const TS* __restrict__ x, const float* __restrict__ dt,
                                                               const float* __restrict__ A, const TS* __restrict__ B,
                                                               RmsMap rms, int Hs, int G, int hg, int n_chunks,
-                                                              TS* __restrict__ states, float* __restrict__ decay) {
+                                                              TS* __restrict__ states, float* __restrict__ decay,
+                                                              ConvIn cv) {
   using MT = TS;
   using F = Frag<MT>;
   constexpr int KI = F::K;
@@ -501,27 +680,76 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
   TS* sOut = reinterpret_cast<TS*>(sU);
   using SC = StateCfg<P, N>;
   constexpr int NTHR = SC::NWAVE * 64;
+  // CONV: the raw rows of B (chunk rows in sU, before any x staging) and of
+  // each head's x (chunk rows in the second half of sU, unused by one
+  // direction), the halo rows and the weight table.
+  static_assert(!CONV || (!BIDIR && WM == kWeightDt && sizeof(TS) == 2), "fused steps: one direction, bf16");
+  static_assert(!CONV || Q * N * int(sizeof(TS)) <= UBYTES, "raw B rows fit the x / output staging");
+  constexpr int CW = N > P ? N : P;
+  __shared__ __attribute__((aligned(16))) MT sHalo[CONV ? kConvHalo * CW : 1];
+  __shared__ __attribute__((aligned(16))) float sCw[CONV ? kConvW * CW : 1];
+  __shared__ int sHtok[kConvHalo];
+  using TRB = Tile<MT, N>;
+  using TRX = Tile<MT, P>;
 
   const int ngrp = Hs / hg;
   const int work = xcd_work_id(blockIdx.x, gridDim.x);
   const int c = chunk_order<Q>(rms, work / ngrp), h0 = (work % ngrp) * hg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t xstride = CONV ? cv.ch : int64_t(Hs) * P;   // elements per token row of x
 
-  load_chunk_schedule<Q, NTHR>(cs, dt, A, rms, c, Hs, h0, hg);
-  {
-    // the hg heads of the workgroup share one B group
-    const TS* Bg = B + int64_t(h0 / (Hs / G)) * N;
-    StageT<TS, Q, N, NTHR, kLptB> bs;
-    bs.load([&](int s) { return Bg + int64_t(cs.tok[s]) * G * N; });
-    bs.use([&](int s0, int n0, const Vec16<TS>& va, const Vec16<TS>& vb) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) st_pair(&sBt[TQ::at(n0 + e, s0)], va.e[e], vb.e[e]);
-    });
-  }
+  if constexpr (CONV) halo_tokens<Q>(sHtok, rms, c);
+  load_chunk_schedule<Q, NTHR>(cs, dt, A, rms, c, Hs, h0, hg, CONV ? cv.dt_bias : nullptr);
   // x of the next head is loaded while the current head is computed.
   StageT<TS, Q, P, NTHR, kLptX> xs;
-  auto load_x = [&](int h) { xs.load([&](int s) { return x + (int64_t(cs.tok[s]) * Hs + h) * P; }); };
-  load_x(h0);
+  RawRows<TS, Q, P, NTHR> xr;
+  ConvWeights<P, NTHR> xw;
+  auto load_x = [&](int h) {
+    if constexpr (CONV) {
+      xr.load([&](int j) { return x + int64_t(raw_row_token(cs, sHtok, j)) * xstride + int64_t(h) * P; });
+      xw.load(cv, h * P);
+    } else {
+      xs.load([&](int s) { return x + int64_t(cs.tok[s]) * xstride + int64_t(h) * P; });
+    }
+  };
+  {
+    // the hg heads of the workgroup share one B group
+    const int g = h0 / (Hs / G);
+    if constexpr (CONV) {
+      RawRows<TS, Q, N, NTHR> br;
+      ConvWeights<N, NTHR> bw;
+      const TS* Bg = x + cv.coff_b + int64_t(g) * N;
+      br.load([&](int j) { return Bg + int64_t(raw_row_token(cs, sHtok, j)) * cv.ch; });
+      bw.load(cv, cv.coff_b + g * N);
+      load_x(h0);
+      MT* rawB = reinterpret_cast<MT*>(sU);
+      br.template store<TRB>(rawB, sHalo, c == 0);
+      bw.store(sCw);
+      lds_barrier();
+      // B^T of the chunk, two positions (a token pair) per unit, the units
+      // spread over pairs as in the unfused staging (transposed stores to
+      // distinct banks)
+      constexpr int UNITS = (Q / 2) * (N / VEC);
+#pragma unroll 1
+      for (int u = tid; u < UNITS; u += NTHR) {
+        const int i = (u / kLptB) % (Q / 2), n0 = ((u / kLptB) / (Q / 2) * kLptB + u % kLptB) * VEC;
+        TS o[2][VEC];
+        conv_rows<TS, TRB, N, 2>(rawB, sHalo, sCw, 2 * i, n0, o);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) st_pair(&sBt[TQ::at(n0 + e, 2 * i)], o[0][e], o[1][e]);
+      }
+      lds_barrier();   // the raw rows and the weight table are free for x
+    } else {
+      const TS* Bg = B + int64_t(g) * N;
+      StageT<TS, Q, N, NTHR, kLptB> bs;
+      bs.load([&](int s) { return Bg + int64_t(cs.tok[s]) * G * N; });
+      bs.use([&](int s0, int n0, const Vec16<TS>& va, const Vec16<TS>& vb) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) st_pair(&sBt[TQ::at(n0 + e, s0)], va.e[e], vb.e[e]);
+      });
+      load_x(h0);
+    }
+  }
 
   constexpr int NT = SC::NT, WP = SC::WP, WN = SC::WN, PT_PER = SC::PT_PER, NT_PER = SC::NT_PER;
   const int wp = wave % WP, wn = wave / WP;
@@ -536,7 +764,7 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
     const float cum_end = cs.cum[hh][Q - 1];
     const float a2 = A[h] * kLog2e;
     // token weights by WeightMode (the weighted x^T of each direction)
-    for (int i = tid; i < Q; i += NTHR) {
+    for (int i = CONV ? fresh_tid() : tid; i < Q; i += NTHR) {
       const float d = cs.dt[hh][i];
       const float cum_i = cs.cum[hh][i];
       if constexpr (WM == kWeightAdjoint) {
@@ -548,16 +776,36 @@ __global__ __launch_bounds__((StateCfg<P, N>::NWAVE * 64)) void ssd_chunk_state_
       }
     }
     if (tid == 0) decay[int64_t(c) * Hs + h] = fast_exp2(cum_end);
+    if constexpr (CONV) {
+      // raw rows of x_h into the second half of sU (free with one direction)
+      xr.template store<TRX>(sXb, sHalo, c == 0);
+      xw.store(sCw);
+    }
     lds_barrier();
-    xs.use([&](int s0, int p0, const Vec16<TS>& va, const Vec16<TS>& vb) {
-      const float wf0 = sW[0][s0], wf1 = sW[0][s0 + 1], wb0 = sW[1][s0], wb1 = sW[1][s0 + 1];
+    if constexpr (CONV) {
+      const int u0 = fresh_tid();
+      constexpr int UNITS = (Q / 2) * (P / VEC);
+#pragma unroll 1
+      for (int u = u0; u < UNITS; u += NTHR) {
+        const int i = (u / kLptX) % (Q / 2), p0 = ((u / kLptX) / (Q / 2) * kLptX + u % kLptX) * VEC, s0 = 2 * i;
+        TS o[2][VEC];
+        conv_rows<TS, TRX, P, 2>(sXb, sHalo, sCw, s0, p0, o);
+        const float wf0 = sW[0][s0], wf1 = sW[0][s0 + 1];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float x0 = to_f32(va.e[e]), x1 = to_f32(vb.e[e]);
-        st_pair_f32(&sXf[TQ::at(p0 + e, s0)], x0 * wf0, x1 * wf1);
-        if constexpr (BIDIR) st_pair_f32(&sXb[TQ::at(p0 + e, s0)], x0 * wb0, x1 * wb1);
+        for (int e = 0; e < VEC; ++e)
+          st_pair_f32(&sXf[TQ::at(p0 + e, s0)], to_f32(o[0][e]) * wf0, to_f32(o[1][e]) * wf1);
       }
-    });
+    } else {
+      xs.use([&](int s0, int p0, const Vec16<TS>& va, const Vec16<TS>& vb) {
+        const float wf0 = sW[0][s0], wf1 = sW[0][s0 + 1], wb0 = sW[1][s0], wb1 = sW[1][s0 + 1];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float x0 = to_f32(va.e[e]), x1 = to_f32(vb.e[e]);
+          st_pair_f32(&sXf[TQ::at(p0 + e, s0)], x0 * wf0, x1 * wf1);
+          if constexpr (BIDIR) st_pair_f32(&sXb[TQ::at(p0 + e, s0)], x0 * wb0, x1 * wb1);
+        }
+      });
+    }
     lds_barrier();
     if (hh + 1 < hg) load_x(h + 1);
     f32x4 accf[PT_PER][NT_PER], accb[PT_PER][NT_PER];
@@ -727,12 +975,14 @@ struct OutCfg {
 // passes the states of u with the adjoint token weights (kWeightAdjoint),
 // whose chunk-local weights e^{cum_end - exc_s} and e^{cum_s} are exactly
 // the transposed scan's.
+// CONV (one direction): x, B and C are the convolved xBC channels (x, B and
+// C all point at the xBC rows; cv gives the convolution and dt_bias).
 template <typename TS, int P, int N, int Q, bool BIDIR = true, bool ACC = false, bool UNIT = false,
-          bool TRANS = false>
+          bool TRANS = false, bool CONV = false>
 __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_kernel(
     const TS* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const TS* __restrict__ B,
     const TS* __restrict__ C, const float* __restrict__ D, RmsMap rms, int Hs, int G, int hg, int n_chunks,
-    const TS* __restrict__ states, TS* __restrict__ y, TS* __restrict__ ylo) {
+    const TS* __restrict__ states, TS* __restrict__ y, TS* __restrict__ ylo, ConvIn cv) {
   using MT = TS;
   using F = Frag<MT>;
   using Cfg = OutCfg<TS, P, N, Q>;
@@ -757,20 +1007,38 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   MT* sBr = sU;
   __shared__ ChunkSched<Q> cs;
   __shared__ __attribute__((aligned(16))) float sV[Cfg::NW][Q];   // per-wave decay factors of s
+  // CONV: raw rows of the chunk (B, then C, then each head's x), the halo
+  // rows and the weight table.
+  static_assert(!CONV || (!BIDIR && !UNIT && !TRANS && kBf16), "fused steps: one direction, bf16");
+  constexpr int CW = N > P ? N : P;
+  __shared__ __attribute__((aligned(16))) MT sRaw[CONV ? Q * CW : 1];
+  __shared__ __attribute__((aligned(16))) MT sHalo[CONV ? kConvHalo * CW : 1];
+  __shared__ __attribute__((aligned(16))) float sCw[CONV ? kConvW * CW : 1];
+  __shared__ int sHtok[kConvHalo];
+  using TRN = Tile<MT, N>;   // raw B and C rows
+  using TRX = Tile<MT, P>;   // raw x rows
+  constexpr int RB = Q * (N / VEC) / NTHR, RX = Q * (P / VEC) / NTHR;   // conv rows per thread
+  static_assert(!CONV || (RB * NTHR == Q * (N / VEC) && RX * NTHR == Q * (P / VEC) && NTHR % (N / VEC) == 0 &&
+                          NTHR % (P / VEC) == 0), "conv rows tile the chunk");
 
   const int ngrp = Hs / hg;
   const int work = xcd_work_id(blockIdx.x, gridDim.x);
   const int c = chunk_order<Q>(rms, work / ngrp), h0 = (work % ngrp) * hg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, grp = lane >> 4;
+  const int64_t xstride = CONV ? cv.ch : int64_t(Hs) * P;   // elements per token row of x
+  const int64_t bstride = CONV ? cv.ch : int64_t(G) * N;    // ... of B and C
 
-  load_chunk_schedule<Q, NTHR>(cs, dt, A, rms, c, Hs, h0, hg);
+  if constexpr (CONV) halo_tokens<Q>(sHtok, rms, c);
+  load_chunk_schedule<Q, NTHR>(cs, dt, A, rms, c, Hs, h0, hg, CONV ? cv.dt_bias : nullptr);
 
   // x and the two entering states of the next head are loaded while the
   // current head is computed.
   const int64_t per = int64_t(P) * N;
   struct HeadBuf {
     Stage16<Q * (P / VEC), NTHR> xs;
+    RawRows<TS, Q, P, NTHR> xr;
+    ConvWeights<P, NTHR> xw;
     Stage16<P * (N / VEC), NTHR> hfs, hbs;
   };
   HeadBuf buf0;
@@ -778,9 +1046,15 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
     // Consecutive lanes take consecutive 16-byte pieces of one token row, so
     // one load instruction touches few rows (and pages) even when the scan
     // order puts consecutive tokens far apart.
-    hb_.xs.load([&](int u) {
-      return *reinterpret_cast<const uint4*>(x + (int64_t(cs.tok[u / (P / VEC)]) * Hs + h) * P + (u % (P / VEC)) * VEC);
-    });
+    if constexpr (CONV) {
+      hb_.xr.load([&](int j) { return x + int64_t(raw_row_token(cs, sHtok, j)) * xstride + int64_t(h) * P; });
+      hb_.xw.load(cv, h * P);
+    } else {
+      hb_.xs.load([&](int u) {
+        return *reinterpret_cast<const uint4*>(x + int64_t(cs.tok[u / (P / VEC)]) * xstride + int64_t(h) * P +
+                                               (u % (P / VEC)) * VEC);
+      });
+    }
     const uint4* hf = reinterpret_cast<const uint4*>(states + (int64_t(c) * Hs + h) * per);
     const uint4* hb = reinterpret_cast<const uint4*>(states + ((int64_t(n_chunks) + c) * Hs + h) * per);
     hb_.hfs.load([&](int u) { return hf[u]; });
@@ -792,21 +1066,63 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   const int t = wt * 16 + r16;            // this lane's output position
   const int64_t tok_t = cs.tok[t];
   // the hg heads of the workgroup share one B, C group
-  const TS* Bg = B + int64_t(h0 / (Hs / G)) * N;
-  const TS* Cg = C + int64_t(h0 / (Hs / G)) * N;
+  const int grp_bc = h0 / (Hs / G);
+  const TS* Bg = (CONV ? x + cv.coff_b : B) + int64_t(grp_bc) * N;
+  const TS* Cg = (CONV ? x + cv.coff_c : C) + int64_t(grp_bc) * N;
   // C_t fragments (B operand, k = n) for the inter-chunk terms, and G^T.
   typename F::type cfr[N / KI];
-#pragma unroll
-  for (int ks = 0; ks < N / KI; ++ks) cfr[ks] = F::load(Cg + tok_t * G * N + ks * KI, lane);
   // G^T is accumulated in fp32 and kept in the operand type (bf16 for bf16
   // data: the M^T values built from it are rounded to bf16 anyway).
   using GT = typename std::conditional<kBf16, bf16x4, f32x4>::type;
   // The B rows of the chunk are staged once (coalesced, row-major) and every
   // wave reads its MFMA fragments from LDS.
-  {
+  if constexpr (CONV) {
+    // Raw B and C rows (with the halo) and their weights are fetched
+    // together; B is convolved into sBr by whole tiles (each thread one
+    // column piece over RB consecutive rows), C straight into each lane's
+    // fragments.
+    RawRows<TS, Q, N, NTHR> br, cr;
+    ConvWeights<N, NTHR> bw, cw;
+    auto rows_of = [&](const TS* base) {
+      return [&, base](int j) { return base + int64_t(raw_row_token(cs, sHtok, j)) * bstride; };
+    };
+    br.load(rows_of(Bg));
+    bw.load(cv, cv.coff_b + grp_bc * N);
+    cr.load(rows_of(Cg));
+    cw.load(cv, cv.coff_c + grp_bc * N);
+    br.template store<TRN>(sRaw, sHalo, c == 0);
+    bw.store(sCw);
+    lds_barrier();
+    {
+      constexpr int PR = N / VEC;
+      const int col = (tid % PR) * VEC, s0 = (tid / PR) * RB;
+      TS o[RB][VEC];
+      conv_rows<TS, TRN, N, RB>(sRaw, sHalo, sCw, s0, col, o);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        Vec16<TS> v;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v.e[e] = o[r][e];
+        *reinterpret_cast<uint4*>(&sBr[TN::at(s0 + r, col)]) = v.u;
+      }
+    }
+    lds_barrier();
+    cr.template store<TRN>(sRaw, sHalo, c == 0);
+    cw.store(sCw);
+    lds_barrier();
+#pragma unroll
+    for (int ks = 0; ks < N / KI; ++ks) {
+      TS o[1][VEC];
+      conv_rows<TS, TRN, N, 1>(sRaw, sHalo, sCw, t, ks * KI + (lane >> 4) * VEC, o);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) cfr[ks][e] = o[0][e];
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < N / KI; ++ks) cfr[ks] = F::load(Cg + tok_t * bstride + ks * KI, lane);
     Stage16<Q * (N / VEC), NTHR> bs;
     bs.load([&](int u) {
-      return *reinterpret_cast<const uint4*>(Bg + int64_t(cs.tok[u / (N / VEC)]) * G * N + (u % (N / VEC)) * VEC);
+      return *reinterpret_cast<const uint4*>(Bg + int64_t(cs.tok[u / (N / VEC)]) * bstride + (u % (N / VEC)) * VEC);
     });
     bs.use([&](int u, uint4 raw) {
       *reinterpret_cast<uint4*>(&sBr[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
@@ -827,9 +1143,14 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   auto do_head = [&](int hh, HeadBuf& buf) {
     const int h = h0 + hh;
     // Stage x_h and the two entering states of this head.
-    buf.xs.use([&](int u, uint4 raw) {
-      *reinterpret_cast<uint4*>(&sX[TX::at(u / (P / VEC), (u % (P / VEC)) * VEC)]) = raw;
-    });
+    if constexpr (CONV) {
+      buf.xr.template store<TRX>(sRaw, sHalo, c == 0);
+      buf.xw.store(sCw);
+    } else {
+      buf.xs.use([&](int u, uint4 raw) {
+        *reinterpret_cast<uint4*>(&sX[TX::at(u / (P / VEC), (u % (P / VEC)) * VEC)]) = raw;
+      });
+    }
     buf.hfs.use([&](int u, uint4 raw) {
       *reinterpret_cast<uint4*>(&sHf[TN::at(u / (N / VEC), (u % (N / VEC)) * VEC)]) = raw;
     });
@@ -859,6 +1180,23 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
     }
     lds_barrier();
     if (hh + 1 < hg) load_head(buf, h + 1);
+    if constexpr (CONV) {
+      // x_h from its raw rows: each thread one column piece over RX
+      // consecutive rows
+      constexpr int PR = P / VEC;
+      const int u0 = fresh_tid();
+      const int col = (u0 % PR) * VEC, s0 = (u0 / PR) * RX;
+      TS o[RX][VEC];
+      conv_rows<TS, TRX, P, RX>(sRaw, sHalo, sCw, s0, col, o);
+#pragma unroll
+      for (int r = 0; r < RX; ++r) {
+        Vec16<TS> v;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v.e[e] = o[r][e];
+        *reinterpret_cast<uint4*>(&sX[TX::at(s0 + r, col)]) = v.u;
+      }
+      lds_barrier();
+    }
 
     const float* cum = cs.cum[hh];
     const float* exc = cs.exc[hh];
@@ -1450,9 +1788,11 @@ int launch_review(const lingen_mate_shape* s, const TS* x, const float* dt, cons
 
 // Phase A + state pass (+ review state) for one batch element.  BIDIR =
 // false: the forward direction of the (possibly reversed, rev = 1) order only.
-template <typename TS, int P, int N, int Q, bool BIDIR = true, int WM = kWeightDt>
+// CONV: x is the xBC rows and the convolution of cv is fused (no review).
+template <typename TS, int P, int N, int Q, bool BIDIR = true, int WM = kWeightDt, bool CONV = false>
 int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float* dt, const float* A, const TS* B,
-                  char* ws, hipStream_t st, const hipEvent_t* ev = nullptr, int rev = 0, float* h_last = nullptr) {
+                  char* ws, hipStream_t st, const hipEvent_t* ev = nullptr, int rev = 0, float* h_last = nullptr,
+                  const ConvIn& cv = ConvIn{}) {
   const WsLayout lay = ws_layout(s);
   const int L = int(tokens(s));
   const int nc = L / Q;
@@ -1463,12 +1803,13 @@ int launch_states(const lingen_mate_shape* s, int mode, const TS* x, const float
   const int hg = head_group(Hs / s->ngroups, kStateHeadGroup);
   const float* h0 = nullptr;
   if (s->n_review > 0) {
+    if (CONV) return LINGEN_ERR_UNSUPPORTED;
     if (int rc = launch_review<TS>(s, x, dt, A, B, ws, lay, st)) return rc;
     h0 = reinterpret_cast<const float*>(ws + lay.review_h);
   }
   if (int rc = mark(ev, 1, st)) return rc;
-  ssd_chunk_state_kernel<TS, P, N, Q, BIDIR, WM><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(
-      x, dt, A, B, make_rms(s, mode, rev), Hs, s->ngroups, hg, nc, states, decay);
+  ssd_chunk_state_kernel<TS, P, N, Q, BIDIR, WM, CONV><<<nc * (Hs / hg), StateCfg<P, N>::NWAVE * 64, 0, st>>>(
+      x, dt, A, B, make_rms(s, mode, rev), Hs, s->ngroups, hg, nc, states, decay, cv);
   if (launch_status(__func__)) return LINGEN_ERR_HIP;
   if (int rc = mark(ev, 2, st)) return rc;
   // P*N/E threads per head, in blocks of up to 256.  Both directions: E = 8
@@ -1506,7 +1847,7 @@ int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char
     const int hg = head_group(Hs / s->ngroups);   // a divisor of the heads per B, C group
     ssd_chunk_out_kernel<TS, P, N, Q><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
         x, dt, a.A, B, C, a.D, make_rms(s, mode), Hs, s->ngroups, hg, nc, reinterpret_cast<const TS*>(ws + lay.states),
-        yb, nullptr);
+        yb, nullptr, ConvIn{});
     if (launch_status(__func__)) return LINGEN_ERR_HIP;
     if (int rc = mark(ev, 4, st)) return rc;
   }
@@ -1515,10 +1856,12 @@ int launch_ma(const lingen_mate_shape* s, int mode, const Args& a, void* y, char
 
 // MA branch with a parameter set per direction: the forward direction of
 // the scan order with af, then the forward direction of the reversed order
-// (the backward scan) with ab, added to the first result.
-template <typename TS, int P, int N, int Q>
+// (the backward scan) with ab, added to the first result.  CONV: both
+// directions read the xBC rows (a.x; a.B and a.C unused) and dt_raw (a.dt),
+// with the convolution and dt bias of cv[dir] fused into their kernels.
+template <typename TS, int P, int N, int Q, bool CONV = false>
 int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const Args& ab, void* y, char* ws,
-                   hipStream_t st) {
+                   hipStream_t st, const ConvIn* cv = nullptr) {
   const int L = int(tokens(s));
   const int nc = L / Q;
   const int Hs = s->ssd_heads;
@@ -1526,16 +1869,21 @@ int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const A
   const int64_t eb = elem_bytes(s);
   using Cfg = OutCfg<TS, P, N, Q>;
   const int hg = head_group(Hs / s->ngroups);
+  // elements per token row of x and of B, C
+  const int64_t xrow = CONV ? cv[0].ch : int64_t(Hs) * P, brow = CONV ? cv[0].ch : int64_t(s->ngroups) * N;
   for (int b = 0; b < s->batch; ++b) {
     TS* yb = reinterpret_cast<TS*>(static_cast<char*>(y) + int64_t(b) * L * Hs * P * eb);
     for (int dir = 0; dir < 2; ++dir) {
       const Args& a = dir ? ab : af;
-      const TS* x = reinterpret_cast<const TS*>(static_cast<const char*>(a.x) + int64_t(b) * L * Hs * P * eb);
+      const ConvIn cvd = CONV ? cv[dir] : ConvIn{};
+      const TS* x = reinterpret_cast<const TS*>(static_cast<const char*>(a.x) + int64_t(b) * L * xrow * eb);
       const float* dt = a.dt + int64_t(b) * L * Hs;
-      const int64_t bc = int64_t(b) * L * s->ngroups * N * eb;
-      const TS* B = reinterpret_cast<const TS*>(static_cast<const char*>(a.B) + bc);
-      const TS* C = reinterpret_cast<const TS*>(static_cast<const char*>(a.C) + bc);
-      if (int rc = launch_states<TS, P, N, Q, false>(s, mode, x, dt, a.A, B, ws, st, nullptr, dir)) return rc;
+      const int64_t bc = int64_t(b) * L * brow * eb;
+      const TS* B = CONV ? x : reinterpret_cast<const TS*>(static_cast<const char*>(a.B) + bc);
+      const TS* C = CONV ? x : reinterpret_cast<const TS*>(static_cast<const char*>(a.C) + bc);
+      if (int rc = launch_states<TS, P, N, Q, false, kWeightDt, CONV>(s, mode, x, dt, a.A, B, ws, st, nullptr, dir,
+                                                                      nullptr, cvd))
+        return rc;
       const TS* states = reinterpret_cast<const TS*>(ws + lay.states);
       // The one-direction passes fill only the first half of the states
       // region; the second half (nc*Hs*P*N elements, at least L*Hs*P since
@@ -1545,11 +1893,11 @@ int launch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const A
       TS* ylo = std::is_same<TS, float>::value ? nullptr
                                                : reinterpret_cast<TS*>(ws + lay.states) + int64_t(nc) * Hs * P * N;
       if (dir == 0)
-        ssd_chunk_out_kernel<TS, P, N, Q, false, false><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
-            x, dt, a.A, B, C, a.D, make_rms(s, mode, 0), Hs, s->ngroups, hg, nc, states, yb, ylo);
+        ssd_chunk_out_kernel<TS, P, N, Q, false, false, false, false, CONV><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
+            x, dt, a.A, B, C, a.D, make_rms(s, mode, 0), Hs, s->ngroups, hg, nc, states, yb, ylo, cvd);
       else
-        ssd_chunk_out_kernel<TS, P, N, Q, false, true><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
-            x, dt, a.A, B, C, a.D, make_rms(s, mode, 1), Hs, s->ngroups, hg, nc, states, yb, ylo);
+        ssd_chunk_out_kernel<TS, P, N, Q, false, true, false, false, CONV><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
+            x, dt, a.A, B, C, a.D, make_rms(s, mode, 1), Hs, s->ngroups, hg, nc, states, yb, ylo, cvd);
       if (launch_status(__func__)) return LINGEN_ERR_HIP;
     }
   }
@@ -1566,6 +1914,17 @@ int dispatch_ma_dirs(const lingen_mate_shape* s, int mode, const Args& af, const
   }
 }
 
+// The fused form: bf16 families only (the fp32 family runs the standalone
+// steps and then dispatch_ma_dirs).
+int dispatch_ma_dirs_conv(const lingen_mate_shape* s, int mode, const Args& af, const Args& ab, const ConvIn* cv,
+                          void* y, char* ws, hipStream_t st) {
+  switch (scan_family(s)) {
+    case SCAN_BF16_P64_N64_Q64: return launch_ma_dirs<__bf16, 64, 64, 64, true>(s, mode, af, ab, y, ws, st, cv);
+    case SCAN_BF16_P64_N128_Q128: return launch_ma_dirs<__bf16, 64, 128, 128, true>(s, mode, af, ab, y, ws, st, cv);
+    default: return LINGEN_ERR_UNSUPPORTED;
+  }
+}
+
 // The transposed bidirectional scan of one batch element (TRANS above): the
 // states are those of u against C with the adjoint token weights, left by
 // scan_states_one in `ws`; B and C are exchanged for the output kernel.
@@ -1578,7 +1937,7 @@ int launch_transposed(const lingen_mate_shape* s, int mode, const TS* u, const f
   const int hg = head_group(Hs / s->ngroups);
   const TS* states = reinterpret_cast<const TS*>(ws + ws_layout(s).states);
   ssd_chunk_out_kernel<TS, P, N, Q, true, false, true, true><<<nc * (Hs / hg), Cfg::NW * 64, 0, st>>>(
-      u, dt, A, C, B, nullptr, make_rms(s, mode), Hs, s->ngroups, hg, nc, states, y, nullptr);
+      u, dt, A, C, B, nullptr, make_rms(s, mode), Hs, s->ngroups, hg, nc, states, y, nullptr, ConvIn{});
   if (launch_status(__func__)) return LINGEN_ERR_HIP;
   return LINGEN_OK;
 }
@@ -1797,6 +2156,28 @@ int lingen_ma_fwd_dirs(const void* x_f, const float* dt_f, const float* A_f, con
   Args af{x_f, dt_f, A_f, B_f, C_f, D_f, nullptr, nullptr, nullptr};
   Args ab{x_b, dt_b, A_b, B_b, C_b, D_b, nullptr, nullptr, nullptr};
   return dispatch_ma_dirs(shape, mode, af, ab, y_ma, static_cast<char*>(workspace), stream);
+}
+
+int lingen_ma_fwd_dirs_conv(const void* xbc, const float* dt_raw, const float* dt_bias, int32_t conv_k,
+                            const float* conv_w_f, const float* conv_b_f, const float* A_f, const float* D_f,
+                            const float* conv_w_b, const float* conv_b_b, const float* A_b, const float* D_b,
+                            int32_t mode, const lingen_mate_shape* shape, void* y_ma, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (int rc = validate_shape(shape)) return rc;
+  if (mode < 0 || mode > 3 || conv_k < 1 || conv_k > kConvTaps) return LINGEN_ERR_SHAPE;
+  if (int rc = check_all({xbc, dt_raw, dt_bias, conv_w_f, conv_b_f, A_f, D_f, conv_w_b, conv_b_b, A_b, D_b, y_ma}))
+    return rc;
+  if (int rc = check_ws(shape, workspace, workspace_bytes)) return rc;
+  if (shape->dtype != LINGEN_BF16 || shape->n_review > 0) return LINGEN_ERR_UNSUPPORTED;
+  const int d = shape->ssd_heads * shape->headdim, gn = shape->ngroups * shape->d_state;
+  // 16-byte pieces of every row: x, B, C all start on a piece
+  if (d % 8 || gn % 8) return LINGEN_ERR_SHAPE;
+  ConvIn cv[2];
+  cv[0] = ConvIn{conv_w_f, conv_b_f, dt_bias, conv_k, d + 2 * gn, d, d + gn};
+  cv[1] = ConvIn{conv_w_b, conv_b_b, dt_bias, conv_k, d + 2 * gn, d, d + gn};
+  Args af{xbc, dt_raw, A_f, xbc, xbc, D_f, nullptr, nullptr, nullptr};
+  Args ab{xbc, dt_raw, A_b, xbc, xbc, D_b, nullptr, nullptr, nullptr};
+  return dispatch_ma_dirs_conv(shape, mode, af, ab, cv, y_ma, static_cast<char*>(workspace), stream);
 }
 
 int lingen_te_fwd(const void* q, const void* k, const void* v, int32_t shifted, const lingen_mate_shape* shape,

@@ -215,9 +215,11 @@ int lingen_te_fwd_shift(const void* q, const void* k, const void* v,
  *                    the gradient of its output);
  *   dq, dk, dv:      device, [batch, L, Ha, d] dtype, written in full; they
  *                    must not alias the inputs or each other.
- * Offsets and masking as lingen_te_fwd_shift.  Compiled for BF16 with d = 64
- * and 4x8x8-token windows (256 tokens); other valid shapes return
- * LINGEN_ERR_UNSUPPORTED.  Errors as lingen_te_fwd_shift. */
+ * Offsets and masking as lingen_te_fwd_shift.  Compiled for the forward's
+ * three families: BF16 with d = 64 and 256-token windows (MFMA tiles), BF16
+ * with d = 64 and 3x3x3-token windows, FP32 with d = 32 and 32-token windows
+ * (fp32 loops); other valid shapes return LINGEN_ERR_UNSUPPORTED.  Errors as
+ * lingen_te_fwd_shift. */
 int lingen_te_bwd(const void* q, const void* k, const void* v, const void* d_out,
                   int32_t shift_t, int32_t shift_h, int32_t shift_w, int32_t masked,
                   const lingen_mate_shape* shape, void* dq, void* dk, void* dv,

@@ -363,6 +363,114 @@ __global__ __launch_bounds__(64 * 16 / QT) void tesa_bwd_kernel(const __bf16* __
   }
 }
 
+
+// Small windows (at most 32 slots: the 3x3x3 and 2x4x4 windows), any
+// element type: one workgroup of 256 threads per (window, head) item.  The
+// item's q, k, v and dO rows sit in LDS as fp32 (rows padded by one element,
+// so that threads stepping along a row's neighbours hit distinct banks); the
+// scores, the softmax weights P and dS = P * (dP - D) are dense NW x NW fp32
+// tiles, and every product is a plain fp32 loop: an item is a few tens of
+// thousands of multiply-adds, far below what an MFMA tiling would pay back.
+// Masked pairs (slots of different wrap classes in a cut window) get P = 0.
+template <typename TS, int DH, int NW>
+__global__ __launch_bounds__(256) void tesa_bwd_small_kernel(const TS* __restrict__ q, const TS* __restrict__ k,
+                                                             const TS* __restrict__ v, const TS* __restrict__ dO,
+                                                             WinGeom wg, int Ha, TS* __restrict__ dq,
+                                                             TS* __restrict__ dk, TS* __restrict__ dv) {
+  static_assert(NW <= 32, "one thread per softmax row");
+  constexpr int NTHR = 256, LD = DH + 1, LP = NW + 1;
+  __shared__ float sQ[NW * LD], sK[NW * LD], sV[NW * LD], sG[NW * LD];
+  __shared__ float sP[NW * LP], sD[NW * LP];
+  __shared__ int sTok[NW], sCls[NW];
+  const int tid = threadIdx.x;
+  const int item = blockIdx.x, h = item % Ha, win = item / Ha;
+  const int nwin_hw = wg.nwh * wg.nww;
+  const int wi = win / nwin_hw, wj = (win / wg.nww) % wg.nwh, wk = win % wg.nww;
+  const int64_t rowstride = int64_t(Ha) * DH, hoff = int64_t(h) * DH;
+  const float scale = rsqrtf(float(DH));
+  if (tid < NW) {
+    int cl;
+    sTok[tid] = window_token(wg, wi, wj, wk, tid / (wg.wh * wg.ww), (tid / wg.ww) % wg.wh, tid % wg.ww, cl);
+    sCls[tid] = wg.masked ? cl : 0;
+  }
+  __syncthreads();
+  for (int u = tid; u < NW * DH; u += NTHR) {
+    const int i = u / DH, d = u % DH;
+    const int64_t g = int64_t(sTok[i]) * rowstride + hoff + d;
+    sQ[i * LD + d] = to_f32(q[g]);
+    sK[i * LD + d] = to_f32(k[g]);
+    sV[i * LD + d] = to_f32(v[g]);
+    sG[i * LD + d] = to_f32(dO[g]);
+  }
+  __syncthreads();
+  // scaled scores and dP = dO v^T
+  for (int u = tid; u < NW * NW; u += NTHR) {
+    const int i = u / NW, j = u % NW;
+    float sc = 0.f, dp = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < DH; ++d) {
+      sc = fmaf(sQ[i * LD + d], sK[j * LD + d], sc);
+      dp = fmaf(sG[i * LD + d], sV[j * LD + d], dp);
+    }
+    sP[i * LP + j] = sCls[i] == sCls[j] ? sc * scale : -INFINITY;
+    sD[i * LP + j] = dp;
+  }
+  __syncthreads();
+  // P = softmax of each row, D_i = sum_j P_ij dP_ij, dS = P (dP - D)
+  if (tid < NW) {
+    float* pr = &sP[tid * LP];
+    float* dr = &sD[tid * LP];
+    float m = -INFINITY;
+    for (int j = 0; j < NW; ++j) m = fmaxf(m, pr[j]);   // the slot's own key is never masked
+    float l = 0.f;
+    for (int j = 0; j < NW; ++j) {
+      const float e = expf(pr[j] - m);
+      pr[j] = e;
+      l += e;
+    }
+    const float inv = 1.f / l;
+    float dsum = 0.f;
+    for (int j = 0; j < NW; ++j) {
+      pr[j] *= inv;
+      dsum = fmaf(pr[j], dr[j], dsum);
+    }
+    for (int j = 0; j < NW; ++j) dr[j] = pr[j] * (dr[j] - dsum);
+  }
+  __syncthreads();
+  // dq_i = scale sum_j dS_ij k_j;  dk_i = scale sum_j dS_ji q_j;  dv_i = sum_j P_ji dO_j
+  for (int u = tid; u < NW * DH; u += NTHR) {
+    const int i = u / DH, d = u % DH;
+    float a = 0.f, b = 0.f, c = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < NW; ++j) {
+      a = fmaf(sD[i * LP + j], sK[j * LD + d], a);
+      b = fmaf(sD[j * LP + i], sQ[j * LD + d], b);
+      c = fmaf(sP[j * LP + i], sG[j * LD + d], c);
+    }
+    const int64_t g = int64_t(sTok[i]) * rowstride + hoff + d;
+    dq[g] = from_f32<TS>(a * scale);
+    dk[g] = from_f32<TS>(b * scale);
+    dv[g] = from_f32<TS>(c);
+  }
+}
+
+template <typename TS, int DH, int NW>
+int launch_te_bwd_small(const lingen_mate_shape* s, const WinGeom& g, const void* q, const void* k, const void* v,
+                        const void* d_out, void* dq, void* dk, void* dv, hipStream_t st) {
+  const int64_t L = tokens(s);
+  const int items = g.nwt * g.nwh * g.nww * s->attn_heads;
+  const int64_t per = L * s->attn_heads * DH;
+  for (int b = 0; b < s->batch; ++b) {
+    const int64_t off = int64_t(b) * per;
+    tesa_bwd_small_kernel<TS, DH, NW><<<items, 256, 0, st>>>(
+        static_cast<const TS*>(q) + off, static_cast<const TS*>(k) + off, static_cast<const TS*>(v) + off,
+        static_cast<const TS*>(d_out) + off, g, s->attn_heads, static_cast<TS*>(dq) + off,
+        static_cast<TS*>(dk) + off, static_cast<TS*>(dv) + off);
+    if (launch_status(__func__) != LINGEN_OK) return LINGEN_ERR_HIP;
+  }
+  return LINGEN_OK;
+}
+
 }  // namespace lingen
 
 using namespace lingen;
@@ -377,9 +485,14 @@ extern "C" int lingen_te_bwd(const void* q, const void* k, const void* v, const 
   for (const void* p : {q, k, v, d_out, static_cast<const void*>(dq), static_cast<const void*>(dk),
                         static_cast<const void*>(dv)})
     if (int rc = check_ptr(p)) return rc;
-  if (attn_family(shape) != ATTN_BF16_D64_W256) return LINGEN_ERR_UNSUPPORTED;
   const int shift[3] = {shift_t, shift_h, shift_w};
   const WinGeom g = make_wingeom(shape, shift, masked);
+  switch (attn_family(shape)) {
+    case ATTN_BF16_D64_W256: break;
+    case ATTN_BF16_D64_W27: return launch_te_bwd_small<__bf16, 64, 27>(shape, g, q, k, v, d_out, dq, dk, dv, stream);
+    case ATTN_F32_D32_W32: return launch_te_bwd_small<float, 32, 32>(shape, g, q, k, v, d_out, dq, dk, dv, stream);
+    default: return LINGEN_ERR_UNSUPPORTED;
+  }
   const int64_t L = tokens(shape);
   const int items = g.nwt * g.nwh * g.nww * shape->attn_heads;
   const int64_t per = L * shape->attn_heads * kBwdDim;   // elements per batch element

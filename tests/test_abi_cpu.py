@@ -198,9 +198,10 @@ def test_te_bwd_rejects_before_launch(L):
         assert call(*p[:4], 2, 4, 4, 1, ctypes.byref(cs1), *p[4:], None) == -1, i
         p[i] = ctypes.c_void_p(MISALIGNED)
         assert call(*p[:4], 2, 4, 4, 1, ctypes.byref(cs1), *p[4:], None) == -4, i
-    # only the bf16 / d 64 / 256-token window family has a backward kernel
-    cs0 = mate.to_c_shape(CONFIGS[0])
-    assert call(F, F, F, F, 1, 2, 2, 1, ctypes.byref(cs0), F, F, F, None) == -7
+    # the backward has the forward's families; a window no family covers
+    # (bf16, d 64, 2x4x4 windows) is refused before anything is launched
+    csn = mate.to_c_shape(CONFIGS[1].with_(win=(2, 4, 4)))
+    assert call(F, F, F, F, 1, 2, 2, 1, ctypes.byref(csn), F, F, F, None) == -7
     assert call(F, F, F, F, 1, 2, 2, 1, None, F, F, F, None) == -1
 
 

@@ -1,7 +1,8 @@
 """GPU parity of the TE-branch backward pass (lingen_te_bwd) through the C
 ABI against the fp64 oracle's tesa_backward on the same inputs: plain,
 shifted (cut border windows), cyclic and uneven offsets, batch 2, and sampled
-heads at the 512p-like workload in the benchmark's launch configuration.
+heads at the 512p-like workload in the benchmark's launch configuration;
+the odd 3x3x3 window (bf16) and the fp32 family of the smallest grid.
 
 Bar (bf16 storage, fp32 accumulation, bf16 rounding of P and dS as MFMA
 operands): relative L2 error at most 2e-2 for each of dq, dk and dv, and
@@ -81,3 +82,48 @@ def test_te_bwd_512p_sampled_heads(shift):
         ref = oracle.tesa_backward(f["q"], f["k"], f["v"], g[:, [h]].double().numpy(), s.T, s.H, s.W, s.win, shift)
         for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
             _check(got[:, [h]].double().cpu().numpy(), want, f"head {h} {name}")
+
+
+# The small-window families (fp32 loops, one workgroup per window and head):
+# the odd 3x3x3 window with bf16 storage (the bars above), and the fp32
+# family of the 4x8x8 grid (2x4x4 windows, d = 32), where fp32 arithmetic
+# from fp32 inputs leaves relative errors of order 1e-6: bar 1e-5.
+ODD = CONFIGS[1].with_(T=12, H=12, W=12, win=(3, 3, 3))
+
+
+@pytest.mark.parametrize("shift,masked", [((0, 0, 0), 1), ((1, 1, 1), 1), ((1, 2, 1), 0), ((2, 1, 0), 1)])
+def test_te_bwd_odd_window(shift, masked):
+    torch, mate = need_gpu()
+    s = ODD
+    inp = make_inputs(s, 1, tensors=["q", "k", "v"])
+    shape = (s.L, s.attn_heads, s.attn_headdim)
+    d = {n: inp.torch(n, "cuda") for n in ("q", "k", "v")}
+    g = _grad_out(torch, shape, 53)
+    say(f"te_bwd 3x3x3 windows {s.T}x{s.H}x{s.W} shift{shift} masked{masked}")
+    dq, dk, dv = mate.lingen_te_bwd(d["q"], d["k"], d["v"], g.cuda(), shift, masked, s)
+    torch.cuda.synchronize()
+    f = {n: inp.f64(n) for n in ("q", "k", "v")}
+    ref = oracle.tesa_backward(f["q"], f["k"], f["v"], g.double().numpy(), s.T, s.H, s.W, s.win, shift,
+                               cyclic=not masked)
+    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        _check(got.double().cpu().numpy().reshape(want.shape), want, name)
+
+
+@pytest.mark.parametrize("shift,masked", [((0, 0, 0), 1), ((1, 2, 2), 1), ((1, 2, 2), 0), ((1, 1, 3), 1)])
+def test_te_bwd_fp32(shift, masked):
+    torch, mate = need_gpu()
+    s = CONFIGS[0].with_(batch=2)
+    rng = np.random.default_rng(54)
+    shape = (2, s.L, s.attn_heads, s.attn_headdim)
+    q, k, v, g = (torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)) for _ in range(4))
+    say(f"te_bwd fp32 {s.T}x{s.H}x{s.W} windows {s.win} shift{shift} masked{masked}, batch 2")
+    dq, dk, dv = mate.lingen_te_bwd(q.cuda(), k.cuda(), v.cuda(), g.cuda(), shift, masked, s)
+    torch.cuda.synchronize()
+    for b in range(2):
+        ref = oracle.tesa_backward(q[b].double().numpy(), k[b].double().numpy(), v[b].double().numpy(),
+                                   g[b].double().numpy(), s.T, s.H, s.W, s.win, shift, cyclic=not masked)
+        for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            got = got[b].double().cpu().numpy()
+            e = rel_l2(got, want)
+            say(f"  batch {b} {name}: rel L2 {e:.3e}")
+            assert e <= 1e-5, (name, e)

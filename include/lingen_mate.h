@@ -317,9 +317,10 @@ int lingen_dense_attn_fwd(const void* q, const void* k, const void* v, void* o,
  * and each pooled token's gradient is spread over its pooling block (dx,
  * ddt, dB, dA gain these shares; dC and dD do not: the review tokens'
  * outputs are discarded).
- * Supported: bf16 storage with P = 64 in the compiled families
- * (BF16, 64, 64, 64) and (BF16, 64, 128, 128); anything else that passes
- * lingen_mate_validate returns LINGEN_ERR_UNSUPPORTED.
+ * Supported: the three compiled scan families (BF16, 64, 64, 64) and
+ * (BF16, 64, 128, 128) (MFMA tiles), and (F32, 32, 16, 16) (fp32 loops);
+ * anything else that passes lingen_mate_validate returns
+ * LINGEN_ERR_UNSUPPORTED.
  * workspace: device, lingen_ma_bwd_workspace_bytes (two scan workspaces,
  * whose bf16 chunk states the kernels read, plus the crossing sums, the
  * transposed outputs and, with review tokens, their gradients).

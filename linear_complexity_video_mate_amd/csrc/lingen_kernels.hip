@@ -2062,6 +2062,10 @@ int ma_transposed_one(const lingen_mate_shape* s, int mode, const void* ub, cons
   if (s->n_review != 0) return LINGEN_ERR_UNSUPPORTED;
   const char* ws = static_cast<const char*>(workspace);
   switch (scan_family(s)) {
+    case SCAN_F32_P32_N16_Q16:
+      return launch_transposed<float, 32, 16, 16>(s, mode, static_cast<const float*>(ub), dtb, A,
+                                                  static_cast<const float*>(Bb), static_cast<const float*>(Cb), ws,
+                                                  static_cast<float*>(yb), stream);
     case SCAN_BF16_P64_N64_Q64:
       return launch_transposed<__bf16, 64, 64, 64>(s, mode, static_cast<const __bf16*>(ub), dtb, A,
                                                    static_cast<const __bf16*>(Bb), static_cast<const __bf16*>(Cb), ws,

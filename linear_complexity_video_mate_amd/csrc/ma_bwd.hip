@@ -439,6 +439,159 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   }
 }
 
+
+// The same crossing sums and dB, dC for fp32 storage (the small family: head
+// size 32, N = Q = 16), every product a plain fp32 loop over LDS rows: the
+// chunk's Q x Q pairs and the P x N states are a few thousand
+// multiply-adds per head.  One workgroup of 256 threads per (chunk, group,
+// batch element); the states are the fp32 ones the chunk-state pass leaves.
+template <int Q, int N, int P>
+__global__ __launch_bounds__(256) void ma_bwd_cross_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ dy, const float* __restrict__ dt,
+    const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ C,
+    const float* __restrict__ st1, const float* __restrict__ st2, int64_t per, ScanOrder so, int L, int Hs, int G,
+    int b, float* __restrict__ R, float* __restrict__ dB, float* __restrict__ dC) {
+  constexpr int NT = 256, LQ = Q + 1, LN = N + 1, LP = P + 1;
+  static_assert(Q <= 64 && Q * Q <= 4 * NT, "pairs per thread");
+  __shared__ float sB[Q * LN], sC[Q * LN], sX[Q * LP], sDY[Q * LP], sE[Q * LQ];
+  __shared__ float sS[4][P * LN];   // hf1, hb2, hb1, hf2 of the head
+  __shared__ float gB[Q * LN], gC[Q * LN];
+  __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], s_k;
+  __shared__ int s_tok[Q];
+  const int c = blockIdx.x, g = blockIdx.y;
+  const int hpg = Hs / G;
+  const int tid = threadIdx.x;
+  const int64_t bl = int64_t(b) * L;
+  for (int i = tid; i < Q; i += NT) s_tok[i] = so.canon(c * Q + i);
+  __syncthreads();
+  for (int u = tid; u < Q * N; u += NT) {
+    const int i = u / N, n = u % N;
+    const int64_t src = ((bl + s_tok[i]) * G + g) * N + n;
+    sB[i * LN + n] = B[src];
+    sC[i * LN + n] = C[src];
+    gB[i * LN + n] = 0.f;
+    gC[i * LN + n] = 0.f;
+  }
+#pragma unroll 1
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const float a_h = A[h];
+    __syncthreads();   // the previous head is done with every shared array
+    for (int u = tid; u < Q * P; u += NT) {
+      const int i = u / P, p = u % P;
+      const int64_t src = ((bl + s_tok[i]) * Hs + h) * P + p;
+      sX[i * LP + p] = x[src];
+      sDY[i * LP + p] = dy[src];
+    }
+    const int64_t st_off = (int64_t(c) * Hs + h) * int64_t(P) * N;
+    for (int u = tid; u < P * N; u += NT) {
+      const int p = u / N, n = u % N;
+      sS[0][p * LN + n] = st1[st_off + u];          // hf1: forward state entering the chunk
+      sS[1][p * LN + n] = st2[per + st_off + u];    // hb2: adjoint state of the forward scan
+      sS[2][p * LN + n] = st1[per + st_off + u];    // hb1: reverse state entering from the right
+      sS[3][p * LN + n] = st2[st_off + u];          // hf2: adjoint state of the reverse scan
+    }
+    if (tid < Q) {
+      s_dt[tid] = dt[(bl + s_tok[tid]) * Hs + h];
+      s_fw[tid] = s_bw[tid] = s_sub[tid] = 0.f;
+    }
+    if (tid == 0) s_k = 0.f;
+    __syncthreads();
+    if (tid == 0) {   // chunk-local cumulative sums of dt*A, inclusive and exclusive
+      float run = 0.f;
+      for (int i = 0; i < Q; ++i) {
+        const float a = s_dt[i] * a_h;
+        run += a;
+        s_cs[i] = run;
+        s_csx[i] = run - a;
+      }
+    }
+    __syncthreads();
+    const float cs_last = s_cs[Q - 1];
+    // pairs inside the chunk: E (dB, dC weights) and W's row and column sums
+    for (int u = tid; u < Q * Q; u += NT) {
+      const int t = u / Q, s2 = u % Q;
+      float dx = 0.f, cb = 0.f;
+      for (int p = 0; p < P; ++p) dx = fmaf(sDY[t * LP + p], sX[s2 * LP + p], dx);
+      for (int n = 0; n < N; ++n) cb = fmaf(sC[t * LN + n], sB[s2 * LN + n], cb);
+      const float df = s2 <= t ? __expf(s_cs[t] - s_cs[s2]) : 0.f;
+      const float db = s2 >= t ? __expf(s_csx[s2] - s_csx[t]) : 0.f;
+      const float e = s_dt[s2] * dx;
+      sE[t * LQ + s2] = e * (df + db);
+      const float v = e * cb;
+      const float wf = s2 < t ? df * v : 0.f;
+      const float wb = s2 > t ? db * v : 0.f;
+      atomicAdd(s_fw + t, wf);
+      atomicAdd(s_bw + t, wb);
+      atomicAdd(s_fw + s2, -wf);
+      atomicAdd(s_bw + s2, -wb);
+    }
+    __syncthreads();
+    // dC_t += sum_s E_ts B_s,  dB_s += sum_t E_ts C_t
+    for (int u = tid; u < Q * N; u += NT) {
+      const int i = u / N, n = u % N;
+      float gc = 0.f, gb = 0.f;
+      for (int j = 0; j < Q; ++j) {
+        gc = fmaf(sE[i * LQ + j], sB[j * LN + n], gc);
+        gb = fmaf(sE[j * LQ + i], sC[j * LN + n], gb);
+      }
+      gC[i * LN + n] += gc;
+      gB[i * LN + n] += gb;
+    }
+    __syncthreads();   // before the boundary terms add to gC, gB
+    // pairs with one end outside the chunk: per row t and term, the state
+    // applied to the row's dy (U terms) or x (V terms), its product with the
+    // row's C or B, and its share of dC or dB
+    for (int u = tid; u < 4 * Q; u += NT) {
+      const int term = u / Q, t = u % Q;
+      const bool is_u = (term == 0 || term == 2);
+      const float* a = is_u ? &sDY[t * LP] : &sX[t * LP];
+      const float* vr = is_u ? &sC[t * LN] : &sB[t * LN];
+      const float scale = term == 0 ? __expf(s_cs[t])
+                        : term == 1 ? s_dt[t] * __expf(cs_last - s_cs[t])
+                        : term == 2 ? __expf(cs_last - s_csx[t])
+                                    : s_dt[t] * __expf(s_csx[t]);
+      const float* st = sS[term];
+      float part = 0.f;
+      for (int n = 0; n < N; ++n) {
+        float acc = 0.f;
+        for (int p = 0; p < P; ++p) acc = fmaf(st[p * LN + n], a[p], acc);
+        part = fmaf(acc, vr[n], part);
+        atomicAdd(is_u ? &gC[t * LN + n] : &gB[t * LN + n], scale * acc);
+      }
+      const float v = scale * part;
+      if (term == 0) atomicAdd(s_fw + t, v);                                        // U_f
+      else if (term == 1) { atomicAdd(s_bw + t, v); atomicAdd(s_sub + t, v); }     // V_f
+      else if (term == 2) atomicAdd(s_bw + t, v);                                   // U_b
+      else { atomicAdd(s_fw + t, v); atomicAdd(s_sub + t, v); }                     // V_b
+    }
+    // both ends outside: K = e^{cs_last} (<hf1, hb2> + <hb1, hf2>)
+    float k = 0.f;
+    for (int u = tid; u < P * N; u += NT) {
+      const int p = u / N, n = u % N;
+      k = fmaf(sS[0][p * LN + n], sS[1][p * LN + n], k);
+      k = fmaf(sS[2][p * LN + n], sS[3][p * LN + n], k);
+    }
+    atomicAdd(&s_k, k);
+    __syncthreads();
+    if (tid == 0) {
+      const float kk = s_k * __expf(cs_last);
+      // suffix sums of s_fw, prefix sums of s_bw, then R
+      float suf = 0.f, pre = 0.f;
+      for (int i = Q - 1; i >= 0; --i) { suf += s_fw[i]; s_fw[i] = suf; }
+      for (int i = 0; i < Q; ++i) { pre += s_bw[i]; s_bw[i] = pre; }
+      for (int i = 0; i < Q; ++i) R[(bl + s_tok[i]) * Hs + h] = s_fw[i] + s_bw[i] - s_sub[i] + kk;
+    }
+  }
+  __syncthreads();
+  for (int u = tid; u < Q * N; u += NT) {
+    const int i = u / N, n = u % N;
+    const int64_t row = ((bl + s_tok[i]) * G + g) * N + n;
+    dC[row] = gC[i * LN + n];
+    dB[row] = gB[i * LN + n];
+  }
+}
+
 // Per token and head (head size 64), in canonical order (nothing here
 // depends on the scan order or the chunks):
 //   dx = dt yhat + 2 D dy,  ddt = x . yhat + A R,
@@ -449,13 +602,20 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
 // workgroup reads 4 KiB of contiguous row per token.  A lane's head is
 // fixed, so its dA, dD shares stay in registers until one atomic per head
 // and workgroup.  kTokUnroll tokens' loads are issued before any is used.
+// (fp32 storage: head size 32, eight lanes of four elements per head row.)
 constexpr int kTokRows = 64, kTokUnroll = 4;
+template <typename TS>
+union Piece16 {
+  uint4 u;
+  TS e[16 / sizeof(TS)];
+};
+template <typename TS>
 __global__ __launch_bounds__(256) void ma_bwd_token_kernel(
-    const __bf16* __restrict__ x, const __bf16* __restrict__ dy, const float* __restrict__ dt,
-    const float* __restrict__ A, const float* __restrict__ D, const __bf16* __restrict__ yh,
+    const TS* __restrict__ x, const TS* __restrict__ dy, const float* __restrict__ dt,
+    const float* __restrict__ A, const float* __restrict__ D, const TS* __restrict__ yh,
     const float* __restrict__ R, int64_t rows, int Hs, float* __restrict__ dx, float* __restrict__ ddt,
     float* __restrict__ dA, float* __restrict__ dD) {
-  constexpr int P = 64, U = kTokUnroll;
+  constexpr int V = 16 / int(sizeof(TS)), P = 8 * V, U = kTokUnroll;
   const int sub = threadIdx.x & 7;
   const int h = int(blockIdx.y) * 32 + int(threadIdx.x >> 3);
   const bool active = h < Hs;   // whole groups of eight lanes
@@ -468,37 +628,36 @@ __global__ __launch_bounds__(256) void ma_bwd_token_kernel(
     int64_t rh[U];
     bool ok[U];
     float d[U], r[U];
-    bf16x8 bx[U], bdy[U], bh[U];   // kept in bf16 until used
+    Piece16<TS> bx[U], bdy[U], bh[U];   // kept in the storage type until used
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       ok[u] = active && i0 + u < nr;
       rh[u] = (r0 + i0 + u) * Hs + hc;
       d[u] = r[u] = 0.f;
-      bx[u] = bdy[u] = bh[u] = bf16x8{};
+      bx[u].u = bdy[u].u = bh[u].u = uint4{0u, 0u, 0u, 0u};
       if (ok[u]) {
         d[u] = dt[rh[u]];
         r[u] = R[rh[u]];
-        const int64_t off = rh[u] * P + sub * 8;
-        bx[u] = *reinterpret_cast<const bf16x8*>(x + off);
-        bdy[u] = *reinterpret_cast<const bf16x8*>(dy + off);
-        bh[u] = *reinterpret_cast<const bf16x8*>(yh + off);
+        const int64_t off = rh[u] * P + sub * V;
+        bx[u].u = *reinterpret_cast<const uint4*>(x + off);
+        bdy[u].u = *reinterpret_cast<const uint4*>(dy + off);
+        bh[u].u = *reinterpret_cast<const uint4*>(yh + off);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float gx[8], xyh = 0.f, dyx = 0.f;
+      float gx[V], xyh = 0.f, dyx = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float vx = static_cast<float>(bx[u][e]), vdy = static_cast<float>(bdy[u][e]),
-                    vh = static_cast<float>(bh[u][e]);
+      for (int e = 0; e < V; ++e) {
+        const float vx = to_f32(bx[u].e[e]), vdy = to_f32(bdy[u].e[e]), vh = to_f32(bh[u].e[e]);
         xyh = fmaf(vx, vh, xyh);
         dyx = fmaf(vdy, vx, dyx);
         gx[e] = fmaf(d[u], vh, two_d * vdy);
       }
       if (ok[u]) {
-        float4* o = reinterpret_cast<float4*>(dx + rh[u] * P + sub * 8);
-        o[0] = make_float4(gx[0], gx[1], gx[2], gx[3]);
-        o[1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
+        float4* o = reinterpret_cast<float4*>(dx + rh[u] * P + sub * V);
+#pragma unroll
+        for (int q4 = 0; q4 < V / 4; ++q4) o[q4] = make_float4(gx[4 * q4], gx[4 * q4 + 1], gx[4 * q4 + 2], gx[4 * q4 + 3]);
       }
       xyh = sum8(xyh);
       dyx = sum8(dyx);
@@ -654,7 +813,7 @@ int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   w->scan1 = take(ws_main);
   w->scan2 = take(ws_main);
   w->R = take(rows * hs * 4);
-  w->yh = take(rows * hs * P * 2);
+  w->yh = take(rows * hs * P * (s->dtype == LINGEN_BF16 ? 2 : 4));
   // review tokens: the adjoint states' final carries (one batch element at
   // a time) and the pooled tokens' gradients of every batch element
   const size_t nr = size_t(s->batch) * size_t(s->n_review);
@@ -666,12 +825,17 @@ int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   return LINGEN_OK;
 }
 
+// The crossing-sum kernels are compiled for the three scan families: bf16
+// with P = 64 and N = Q = 64 or 128 (MFMA tiles), fp32 with P = 32 and
+// N = Q = 16 (fp32 loops).
 int check_bwd_shape(const lingen_mate_shape* s) {
   if (int rc = validate_shape(s)) return rc;
-  // the crossing-sum kernel takes bf16 storage with head size 64
-  if (s->dtype != LINGEN_BF16 || s->headdim != 64) return LINGEN_ERR_UNSUPPORTED;
-  // the crossing-sum kernel is compiled for the two bf16 scan families with P = 64
-  if (!((s->chunk == 64 && s->d_state == 64) || (s->chunk == 128 && s->d_state == 128))) return LINGEN_ERR_UNSUPPORTED;
+  if (s->dtype == LINGEN_BF16) {
+    if (s->headdim != 64) return LINGEN_ERR_UNSUPPORTED;
+    if (!((s->chunk == 64 && s->d_state == 64) || (s->chunk == 128 && s->d_state == 128))) return LINGEN_ERR_UNSUPPORTED;
+    return LINGEN_OK;
+  }
+  if (s->headdim != 32 || s->chunk != 16 || s->d_state != 16) return LINGEN_ERR_UNSUPPORTED;
   return LINGEN_OK;
 }
 
@@ -712,6 +876,7 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
   const ScanOrder so{mode, shape->T, shape->H, shape->W};
   const __bf16* xb = static_cast<const __bf16*>(x);
   const __bf16* dyb = static_cast<const __bf16*>(dy);
+  const bool f32 = shape->dtype == LINGEN_F32;
   int rc;
 #define LINGEN_TRY(expr)                          \
   do {                                            \
@@ -741,7 +906,7 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
     const int64_t per = int64_t(nc) * Hs * P * N;   // one direction's scan states
     const __bf16* st1 = reinterpret_cast<const __bf16*>(ws + w.scan1 + lay.states);
     const __bf16* st2 = reinterpret_cast<const __bf16*>(ws + w.scan2 + lay.states);
-    const int64_t eb = 2;
+    const int64_t eb = f32 ? 4 : 2;
     for (int bi = 0; bi < shape->batch; ++bi) {
       // forward / reverse states of (x, B) and of (x', C) for this batch element, left in the two workspaces
       const int64_t xo = int64_t(bi) * L * Hs * P * eb, bo = int64_t(bi) * L * G * N * eb;
@@ -767,7 +932,12 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
             atf(w.gb) + int64_t(bi) * R * G * N, dA);
         LINGEN_LAUNCHED();
       }
-      if (Q == 128 && N == 128)
+      if (f32)
+        ma_bwd_cross_f32_kernel<16, 16, 32><<<cgrid, 256, 0, stream>>>(
+            static_cast<const float*>(x), static_cast<const float*>(dy), dt, A, static_cast<const float*>(B),
+            static_cast<const float*>(C), reinterpret_cast<const float*>(st1), reinterpret_cast<const float*>(st2),
+            per, so, L, Hs, G, bi, atf(w.R), dB, dC);
+      else if (Q == 128 && N == 128)
         ma_bwd_cross_kernel<128, 128><<<cgrid, kCrossThreads, 0, stream>>>(
             xb, dyb, dt, A, static_cast<const __bf16*>(B), static_cast<const __bf16*>(C), st1, st2, per, so, L, Hs,
             G, bi, atf(w.R), dB, dC);
@@ -780,8 +950,14 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
       LINGEN_LAUNCHED();
     }
     const dim3 tgrid{unsigned((rows + kTokRows - 1) / kTokRows), unsigned((Hs + 31) / 32), 1u};
-    ma_bwd_token_kernel<<<tgrid, 256, 0, stream>>>(xb, dyb, dt, A, D, static_cast<const __bf16*>(at(w.yh)), atf(w.R),
-                                                   rows, Hs, dx, ddt, dA, dD);
+    if (f32)
+      ma_bwd_token_kernel<float><<<tgrid, 256, 0, stream>>>(static_cast<const float*>(x),
+                                                            static_cast<const float*>(dy), dt, A, D,
+                                                            static_cast<const float*>(at(w.yh)), atf(w.R), rows, Hs,
+                                                            dx, ddt, dA, dD);
+    else
+      ma_bwd_token_kernel<__bf16><<<tgrid, 256, 0, stream>>>(xb, dyb, dt, A, D, static_cast<const __bf16*>(at(w.yh)),
+                                                             atf(w.R), rows, Hs, dx, ddt, dA, dD);
     LINGEN_LAUNCHED();
     if (R) {
       RevGeom g;

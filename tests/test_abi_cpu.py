@@ -354,12 +354,16 @@ def test_ma_bwd_rejects_before_launch(L):
         p[i] = M
         assert call(*p[:7], 0, ctypes.byref(cs), *p[7:], n, None) == -4, i
     assert call(*[F] * 7, 0, ctypes.byref(cs), *[F] * 7, n - 1, None) == -5
-    # fp32 storage, a head size other than 64: not supported
-    for shape in (CONFIGS[0],):
-        c = mate.to_c_shape(shape)
-        assert call(*[F] * 7, 0, ctypes.byref(c), *[F] * 7, n, None) == -7
-        size = ctypes.c_size_t(0)
-        assert L.lingen_ma_bwd_workspace_bytes(ctypes.byref(c), ctypes.byref(size)) == -7
+    # the fp32 family (head size 32): two scan workspaces, the crossing sums
+    # and the transposed outputs in fp32
+    s0 = CONFIGS[0]
+    c = mate.to_c_shape(s0)
+    size = ctypes.c_size_t(0)
+    assert L.lingen_ma_bwd_workspace_bytes(ctypes.byref(c), ctypes.byref(size)) == 0
+    al0 = lambda b: (b + 255) // 256 * 256
+    rows0 = s0.batch * s0.L
+    assert size.value == (2 * al0(mate.lingen_mate_workspace_bytes(s0)) + al0(rows0 * s0.ssd_heads * 4)
+                          + al0(rows0 * s0.ssd_heads * s0.headdim * 4))
     # review tokens: supported; the workspace grows by the review buffers of
     # both scan workspaces, the adjoint states' final carries and the
     # pooled tokens' gradients

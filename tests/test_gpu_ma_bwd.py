@@ -9,7 +9,8 @@ zero); and review tokens (the 16k-token workload with 64 review tokens,
 and the 768p-like workload with its 64 review tokens, dy on one head),
 against the oracle's ma_bwd, whose review path is pinned by finite
 differences.  Bar: relative L2 error at most 2e-2 per gradient (bf16
-storage)."""
+storage).  The fp32 family (the 4x8x8 grid: every scan order, one and two
+groups, review tokens, a batch of two) at 1e-4."""
 import numpy as np
 import pytest
 
@@ -225,3 +226,68 @@ def test_ma_bwd_review_path_isolated():
         e = rel_l2(dg, dr)
         say(f"  review share of {name}: rel L2 {e:.3e} (share {rel_l2(ref_r[i], ref_p[i]):.2e} of the gradient)")
         assert e <= TOL, name
+
+
+# The fp32 family (4x8x8 grid, 2 heads of 32, N = Q = 16): fp32 storage and
+# fp32 arithmetic throughout (fp32 loops for the crossing sums), so the bar
+# is 1e-4 relative L2 per gradient.
+TOL_F32 = 1e-4
+
+
+def _check_f32(got, ref, what):
+    for name, g, r in zip(NAMES, got, ref):
+        g = to_np(g).reshape(np.shape(r))
+        e = rel_l2(g, r)
+        say(f"  {what} {name}: rel L2 {e:.3e}")
+        assert e <= TOL_F32, (what, name, e)
+
+
+@pytest.mark.parametrize("mode,G,review", [(0, 1, False), (1, 2, False), (2, 1, False), (3, 2, False),
+                                           (1, 1, True), (2, 2, True)])
+def test_ma_bwd_fp32(mode, G, review):
+    torch, mate = need_gpu()
+    rv = ((2, 2, 2), (1, 2, 2))
+    s = CONFIGS[0].with_(ngroups=G)
+    if review:
+        s = s.with_(n_review=4, rpool=rv[0], rgrid=rv[1])
+    inp = make_inputs(s, 0, seed=181, tensors=list(SCAN))
+    dy = _dy(s, 0, 182)
+    say(f"ma_bwd {s.T}x{s.H}x{s.W} fp32 groups={G} mode{mode} review={s.n_review}")
+    d = {n: inp.torch(n, "cuda") for n in SCAN}
+    got = mate.lingen_ma_bwd(*(d[n] for n in SCAN), torch.from_numpy(dy).cuda(), mode, s)
+    torch.cuda.synchronize()
+    f = {n: inp.f64(n) for n in SCAN}
+    ref = oracle.ma_bwd(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], dy.astype(np.float64), mode, s.T, s.H, s.W,
+                        review=rv if review else None)
+    _check_f32(got, ref, "")
+
+
+def test_ma_bwd_fp32_batch_of_two():
+    torch, mate = need_gpu()
+    base = CONFIGS[0]
+    s = base.with_(batch=2)
+    mode = 3
+    parts = [make_inputs(base, 0, seed=191 + b, tensors=list(SCAN)) for b in range(2)]
+    dys = [_dy(base, 0, 193 + b) for b in range(2)]
+    say(f"ma_bwd fp32 batch 2, {base.T}x{base.H}x{base.W} mode{mode}")
+    cat = lambda n: torch.stack([p.torch(n, "cuda") for p in parts])
+    x, dt, B, C = cat("x"), cat("dt"), cat("B"), cat("C")
+    A, D = parts[0].torch("A", "cuda"), parts[0].torch("D", "cuda")
+    dy = torch.stack([torch.from_numpy(v) for v in dys]).cuda()
+    got = mate.lingen_ma_bwd(x, dt, A, B, C, D, dy, mode, s)
+    torch.cuda.synchronize()
+    perm = oracle.rms_scan_order(mode, base.T, base.H, base.W)
+    refs = []
+    for b in range(2):
+        f = {n: parts[b].f64(n) for n in SCAN}
+        refs.append(oracle.ssd_bidir_backward(f["x"], f["dt"], parts[0].f64("A"), f["B"], f["C"],
+                                              parts[0].f64("D"), dys[b].astype(np.float64), perm))
+    for i, name in enumerate(NAMES):
+        g = to_np(got[i])
+        if name in ("dA", "dD"):   # summed over the batch
+            r = refs[0][i] + refs[1][i]
+            e = rel_l2(g.reshape(np.shape(r)), r)
+        else:
+            e = max(rel_l2(g[b].reshape(np.shape(refs[b][i])), refs[b][i]) for b in range(2))
+        say(f"  {name}: rel L2 {e:.3e}")
+        assert e <= TOL_F32, (name, e)

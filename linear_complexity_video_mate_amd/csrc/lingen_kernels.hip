@@ -55,16 +55,19 @@ template <> struct LdsPad<float> { static constexpr int v = 4; };
 // LDS tile with COLS elements per row, read by MFMA fragment loads (16 rows
 // x one 16-byte chunk per lane group).  bf16 rows that are a whole number of
 // 128-byte lines are stored unpadded with the 16-byte chunks of row r
-// permuted as chunk ^ (r mod 16) (mod 8 for 128-byte rows): fragment loads,
-// row-contiguous stores and the 16-row column stores of MFMA results then
-// all touch distinct banks.  Other tiles are padded by LdsPad.
+// permuted as chunk ^ (r mod 16) (mod 8 for 128-byte rows) ^ 4 [bit 3 of r]:
+// fragment loads and row-contiguous stores touch distinct banks, and so do
+// the transposed token-pair stores of the chunk-state kernel, whose 32
+// lanes write rows r and r + 8 at once (with chunk ^ (r mod 16) alone those
+// two rows' chunks meet in the same banks, 128 bytes of banks per cycle).
+// Other tiles are padded by LdsPad.
 template <typename MT, int COLS>
 struct Tile {
   static constexpr bool kSwz = sizeof(MT) == 2 && COLS % 64 == 0;
   static constexpr int LD = kSwz ? COLS : COLS + LdsPad<MT>::v;
   static constexpr int kMask = (COLS / 8 >= 16 ? 16 : COLS / 8) - 1;
   __device__ static __forceinline__ int at(int row, int col) {
-    if constexpr (kSwz) return row * COLS + ((((col >> 3) ^ (row & kMask)) << 3) | (col & 7));
+    if constexpr (kSwz) return row * COLS + ((((col >> 3) ^ (row & kMask) ^ ((row >> 1) & 4)) << 3) | (col & 7));
     else return row * LD + col;
   }
   // Operand fragment of row `row` for k = k0 + the lane group's k values.

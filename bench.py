@@ -232,7 +232,8 @@ def cpu_baseline(s, inp, workers):
 
 
 # Kernel (mangled-name fragment) -> the stage name bench.py reports it under.
-KERNEL_STAGE = (("tesa_win256_kernel", "tesa_window"), ("tesa_window_kernel", "tesa_window"),
+KERNEL_STAGE = (("tesa_win256_pair_kernel", "tesa_window"), ("tesa_win256_kernel", "tesa_window"),
+                ("tesa_window_kernel", "tesa_window"),
                 ("ssd_chunk_state_kernel", "ssd_chunk_state"), ("ssd_state_pass_kernel", "ssd_state_pass"),
                 ("ssd_chunk_out_kernel", "ssd_chunk_out"), ("review_pool_kernel", "review"),
                 ("review_state_kernel", "review"), ("rms_gather_kernel", "rms_gather"))

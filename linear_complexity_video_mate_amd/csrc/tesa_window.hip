@@ -21,9 +21,14 @@
 //                                 same rounded weights as the output)
 //   y_i = y_MA_i + O_i / l_i
 // The kernel is persistent (one 16-wave workgroup per compute unit, one
-// 16-query tile per wave).  While an item is computed, the next item's K and
-// V stream into the second of two LDS buffer pairs (direct global-to-LDS
-// loads) and its Q fragments into registers.  The shift is index
+// 16-query tile per wave).  With an even head count, an item is a window
+// and two heads (tesa_win256_pair_kernel): the two heads' K and V rows,
+// 256 contiguous bytes of each token row, arrive together by direct
+// global-to-LDS loads into a ring of two window halves, each refilled with
+// the next item's half as soon as both heads are done with it.  With an odd
+// head count, an item is one window and head (tesa_win256_kernel): while it
+// is computed, the next item's K and V stream into the second of two LDS
+// buffer pairs and its Q fragments into registers.  The shift is index
 // arithmetic: windows are enumerated on the offset grid, wrapping around each
 // axis, and a wrap class per slot masks scores between tokens that the cut
 // partition separates.
@@ -56,8 +61,6 @@ __global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_kernel(const __bf
   constexpr int DH = 64, NWIN = 256, NWAVE = kW256Waves, QT = kW256QTiles, KB = kW256KBlocks;
   constexpr int BKEYS = NWIN / KB;                 // keys per block
   constexpr int NTHR = NWAVE * 64;
-  constexpr int KT16 = NWIN / 16;                  // 16-key tiles of S^T
-  constexpr int SUBS = NWIN / 32;                  // 32-key blocks of the P V product
   constexpr int CPR = DH / 8;                      // 16-byte chunks per K / V row
   constexpr int DMA = NWIN * CPR / NTHR;           // direct loads per lane and tile
   static_assert(NWIN * CPR % NTHR == 0 && NWIN / 16 == NWAVE * QT, "query tiles cover the window");
@@ -325,6 +328,273 @@ __global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_kernel(const __bf
   }
 }
 
+
+// Two heads per item: item = (window, pair of heads h0 = 2 hp, h0 + 1).  A
+// head's K or V row is 128 bytes of a 4 KiB token row; the two heads' rows
+// are 256 contiguous bytes, and the direct loads fetch them together (four
+// rows of 256 bytes per instruction instead of eight of 128), which the
+// memory system serves faster.  The LDS holds the pair's keys in two slots
+// of one window half each (keys 0..127, 128..255), K and V of both heads
+// interleaved per key row ([row][head][64], 16-byte chunks permuted by
+// row mod 8).  A wave takes its 16 queries through head h0 (half 0, half 1)
+// and then head h1 (half 0, half 1); once every wave is done with h1's half
+// in a slot, that slot is refilled with the next pair's half, which then has
+// one half of compute to land.  Per half the arithmetic is the single-head
+// kernel's: scores of 128 keys in registers, their exact maximum first, one
+// rescale of the output if the second half raises it.
+// s_waitcnt immediate: at most n vector-memory operations outstanding
+// (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt not waited for).
+constexpr int vmcnt_count(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+
+template <bool ACCUMULATE>
+__global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_pair_kernel(const __bf16* __restrict__ q,
+                                                                           const __bf16* __restrict__ k,
+                                                                           const __bf16* __restrict__ v, WinGeom wg,
+                                                                           int Ha, int n_items, int contiguous,
+                                                                           __bf16* __restrict__ y) {
+  constexpr int DH = 64, NWIN = 256, HALF = 128, NWAVE = kW256Waves;
+  constexpr int NTHR = NWAVE * 64;
+  constexpr int KT16 = HALF / 16;                  // 16-key tiles of a half
+  constexpr int CPR = DH / 8;                      // 16-byte chunks per head row
+  constexpr int DMA = HALF * 2 * CPR / NTHR;       // direct loads per lane, per tile and half
+  static_assert(HALF * 2 * CPR % NTHR == 0 && NWIN / 16 == NWAVE, "one 16-query tile per wave");
+  __shared__ __attribute__((aligned(16))) __bf16 sK0[HALF * 2 * DH];
+  __shared__ __attribute__((aligned(16))) __bf16 sK1[HALF * 2 * DH];
+  __shared__ __attribute__((aligned(16))) __bf16 sV0[HALF * 2 * DH];
+  __shared__ __attribute__((aligned(16))) __bf16 sV1[HALF * 2 * DH];
+  __shared__ int sTok[2][NWIN];
+  __shared__ __attribute__((aligned(16))) int sCls[3][NWIN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int64_t rowstride = int64_t(Ha) * DH;
+  const int Hp = Ha / 2;
+  const int nwin_hw = wg.nwh * wg.nww;
+  const float sc = kLog2e * 0.125f;   // log2(e) / sqrt(64)
+
+  int it_begin, it_end, it_step;
+  if (contiguous) {
+    it_begin = int(int64_t(blockIdx.x) * n_items / gridDim.x);
+    it_end = int(int64_t(blockIdx.x + 1) * n_items / gridDim.x);
+    it_step = 1;
+  } else {
+    it_begin = int(blockIdx.x);
+    it_end = n_items;
+    it_step = int(gridDim.x);
+  }
+  struct ItemPos { int item, hp, wi, wj, wk; };
+  auto decompose = [&](int it) {
+    const int win = it / Hp;
+    return ItemPos{it, it % Hp, win / nwin_hw, (win / wg.nww) % wg.nwh, win % wg.nww};
+  };
+  const int slot_a = tid / (wg.wh * wg.ww), slot_b = (tid / wg.ww) % wg.wh, slot_c = tid % wg.ww;
+  auto item_tokens = [&](const ItemPos& p, int* tok, int* cls) {
+    if (tid < NWIN) {
+      int cl;
+      tok[tid] = window_token(wg, p.wi, p.wj, p.wk, slot_a, slot_b, slot_c, cl);
+      cls[tid] = wg.masked ? cl : 0;
+    }
+  };
+  // Direct loads of one half of the pair's K and V: unit u (16 bytes) of the
+  // slot is key row u / 16, head (u / 8) mod 2, permuted chunk u mod 8.
+  auto issue_half = [&](__bf16* dK, __bf16* dV, const int* tok, int hp, int half) {
+#pragma unroll
+    for (int d = 0; d < DMA; ++d) {
+      const int base = (wave * DMA + d) * 64;
+      const int u = base + lane, row = u / 16, e = (u / 8) & 1, ch = (u & 7) ^ (row & 7);
+      const int64_t goff = int64_t(tok[half * HALF + row]) * rowstride + int64_t(2 * hp + e) * DH + ch * 8;
+      lds_load16(k + goff, dK + base * 8);
+      lds_load16(v + goff, dV + base * 8);
+    }
+  };
+  const int y16_off = 16 * (grp & 1) + 8 * (grp >> 1);
+  struct QState {
+    bf16x8 qf[2];
+    int tokq;
+  };
+  auto load_q = [&](QState& qs, const int* tok, int h) {
+    qs.tokq = tok[wave * 16 + r16];
+    const __bf16* qrow = q + int64_t(qs.tokq) * rowstride + int64_t(h) * DH;
+    qs.qf[0] = Frag<__bf16>::load(qrow, lane);
+    qs.qf[1] = Frag<__bf16>::load(qrow + 32, lane);
+  };
+  // Per-lane LDS offsets (elements) in a slot, for head e: K fragments of
+  // key rows r16 (+16 per tile), V transposing reads of rows 4 grp + r16/4.
+  auto k_off = [&](int e, int col) { return (2 * r16 + e) * DH + ((((col >> 3) ^ (r16 & 7)) << 3) | (col & 7)); };
+  int offk[2][2], offv[2][4];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    offk[e][0] = k_off(e, grp * 8);
+    offk[e][1] = k_off(e, 32 + grp * 8);
+#pragma unroll
+    for (int et = 0; et < 4; ++et) {
+      const int row = 4 * grp + (r16 >> 2), col = et * 16 + 4 * (r16 & 3);
+      offv[e][et] = (2 * row + e) * DH + ((((col >> 3) ^ (row & 7)) << 3) | (col & 7));
+    }
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.f);
+
+  if (it_begin >= it_end) return;
+  ItemPos pos = decompose(it_begin);
+  item_tokens(pos, sTok[0], sCls[0]);
+  lds_barrier();
+  QState nxt;
+  issue_half(sK0, sV0, sTok[0], pos.hp, 0);
+  load_q(nxt, sTok[0], 2 * pos.hp);
+  issue_half(sK1, sV1, sTok[0], pos.hp, 1);
+  wait_vmem();
+
+  // One head of the pair over both halves, its output stored at the end;
+  // after_half0 runs between the halves.
+  auto head = [&](const QState& cur, int h, int e, const int* cls, bool wrapped, auto&& after_half0) {
+    // The MA output this head adds to arrives while the products run.
+    bf16x8 ya[2];
+    if constexpr (ACCUMULATE) {
+      const __bf16* yrow = y + int64_t(cur.tokq) * rowstride + int64_t(h) * DH + y16_off;
+      ya[0] = *reinterpret_cast<const bf16x8*>(yrow);
+      ya[1] = *reinterpret_cast<const bf16x8*>(yrow + 32);
+    }
+    const int qcls = cls[wave * 16 + r16];
+    f32x4 o[4], den = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;
+#pragma unroll
+    for (int et = 0; et < 4; ++et) o[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      if (hf == 1) after_half0();
+      const __bf16* cK = hf ? sK1 : sK0;
+      lds_bf16* vb = (lds_bf16*)(hf ? sV1 : sV0);
+      f32x4 s[KT16];
+#pragma unroll
+      for (int kt = 0; kt < KT16; ++kt) {
+        const int rb = kt * 16 * 2 * DH;
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(cK + offk[e][0] + rb);
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(cK + offk[e][1] + rb);
+        s[kt] = mma(k1, cur.qf[1], mma(k0, cur.qf[0], f32x4{0.f, 0.f, 0.f, 0.f}));
+      }
+      if (wrapped) {
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt) {
+          const int4 kc = *reinterpret_cast<const int4*>(&cls[hf * HALF + kt * 16 + grp * 4]);
+          s[kt][0] = kc.x != qcls ? -INFINITY : s[kt][0];
+          s[kt][1] = kc.y != qcls ? -INFINITY : s[kt][1];
+          s[kt][2] = kc.z != qcls ? -INFINITY : s[kt][2];
+          s[kt][3] = kc.w != qcls ? -INFINITY : s[kt][3];
+        }
+      }
+      float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+      for (int kt = 1; kt < KT16; ++kt) mx = fmaxf(fmaxf(mx, fmaxf(s[kt][0], s[kt][1])), fmaxf(s[kt][2], s[kt][3]));
+      const float mnew = fmaxf(m, max_rows(mx) * sc);
+      // all keys of the first half masked (a cut window): zero weights until
+      // the query's own key, which is always present
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      if (hf) {
+        const float alpha = fast_exp2(m - mref);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) den[r] *= alpha;
+#pragma unroll
+        for (int et = 0; et < 4; ++et)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[et][r] *= alpha;
+      }
+      m = mnew;
+#pragma unroll
+      for (int sb = 0; sb < HALF / 32; ++sb) {
+        const int rb = 32 * sb * 2 * DH;
+        bf16x8 pb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pb[r] = static_cast<__bf16>(fast_exp2(fmaf(s[2 * sb][r], sc, -mref)));
+          pb[4 + r] = static_cast<__bf16>(fast_exp2(fmaf(s[2 * sb + 1][r], sc, -mref)));
+        }
+        den = mma(ones, pb, den);
+#pragma unroll
+        for (int et = 0; et < 4; ++et) {
+          const bf16x4 lo = lds_read_tr(vb + offv[e][et] + rb);
+          const bf16x4 hi = lds_read_tr(vb + offv[e][et] + rb + 16 * 2 * DH);
+          o[et] = mma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[et]);
+        }
+      }
+    }
+    const float inv = __builtin_amdgcn_rcpf(den[0]);
+#pragma unroll
+    for (int r1 = 0; r1 < 2; ++r1) {
+      float ov[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(o[2 * r1][r]), __float_as_uint(o[2 * r1 + 1][r]),
+                                                         false, false);
+        ov[r] = __uint_as_float(sw[0]);
+        ov[4 + r] = __uint_as_float(sw[1]);
+      }
+      bf16x8 res;
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const float val = ov[e8] * inv;
+        res[e8] = static_cast<__bf16>(ACCUMULATE ? static_cast<float>(ya[r1][e8]) + val : val);
+      }
+      __bf16* yrow = y + int64_t(cur.tokq) * rowstride + int64_t(h) * DH + y16_off;
+      *reinterpret_cast<bf16x8*>(yrow + 32 * r1) = res;
+    }
+  };
+
+#pragma unroll 1
+  for (int n = 0;; ++n) {
+    const int h0 = 2 * pos.hp;
+    ItemPos npos = pos;
+    npos.item += it_step;
+    const bool has_next = npos.item < it_end;
+    if (has_next) {
+      npos = decompose(npos.item);
+      item_tokens(npos, sTok[(n + 1) & 1], sCls[(n + 1) % 3]);
+    }
+    // This pair's half 0 (issued after the previous pair's h1 half 0) has
+    // landed once at most the operations issued after it are pending: the
+    // next q (2 loads), h1's output stores (2) and half 1 (2 DMA per lane).
+    if (n == 0) wait_vmem();
+    else __builtin_amdgcn_s_waitcnt(vmcnt_count(2 + 2 + 2 * DMA));
+    lds_barrier();
+    const QState cur0 = nxt;
+    // (empty asm with a memory clobber: the counted groups of vector-memory
+    // operations stay in program order)
+    asm volatile("" ::: "memory");
+    load_q(nxt, sTok[n & 1], h0 + 1);
+    asm volatile("" ::: "memory");
+    const bool wrapped = wg.masked && window_wrapped(wg, pos.wi, pos.wj, pos.wk);
+    const int* cls = sCls[n % 3];
+    // head h0; before its half 1, this pair's half 1 must have landed: the
+    // operations after it are this head's MA-output loads (2) and the next
+    // q loads (2).
+    head(cur0, h0, 0, cls, wrapped, [&] {
+      if (n > 0) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_count((ACCUMULATE ? 2 : 0) + 2));
+        lds_barrier();
+      }
+    });
+    const QState cur1 = nxt;
+    head(cur1, h0 + 1, 1, cls, wrapped, [&] {
+      // every wave is done with slot 0: refill it with the next pair's half 0
+      lds_barrier();
+      if (has_next) {
+        asm volatile("" ::: "memory");
+        issue_half(sK0, sV0, sTok[(n + 1) & 1], npos.hp, 0);
+        asm volatile("" ::: "memory");
+        load_q(nxt, sTok[(n + 1) & 1], 2 * npos.hp);
+        asm volatile("" ::: "memory");
+      }
+    });
+    if (!has_next) break;
+    lds_barrier();   // every wave is done with slot 1
+    asm volatile("" ::: "memory");
+    issue_half(sK1, sV1, sTok[(n + 1) & 1], npos.hp, 1);
+    asm volatile("" ::: "memory");
+    pos = npos;
+  }
+}
+
 }  // namespace
 
 // The TE branch for the (bf16, d 64, 256-token window) family, one batch
@@ -344,6 +614,20 @@ int launch_te_win256(const lingen_mate_shape* s, const int shift[3], int masked,
     const __bf16* vb = reinterpret_cast<const __bf16*>(static_cast<const char*>(v) + off);
     __bf16* yb = reinterpret_cast<__bf16*>(static_cast<char*>(y) + off);
     const int items = nwin * s->attn_heads;
+    if (s->attn_heads % 2 == 0) {
+      // two heads per item; the item order as below, judged by head-items
+      const int pairs = nwin * (s->attn_heads / 2);
+      const int pgrid = pairs < ncu ? pairs : ncu;
+      const int pcontig = items >= 128 * pgrid ? 1 : 0;
+      if (accumulate)
+        tesa_win256_pair_kernel<true><<<pgrid, kW256Waves * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, pairs, pcontig,
+                                                                        yb);
+      else
+        tesa_win256_pair_kernel<false><<<pgrid, kW256Waves * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, pairs, pcontig,
+                                                                         yb);
+      if (launch_status(__func__) != LINGEN_OK) return LINGEN_ERR_HIP;
+      continue;
+    }
     const int grid = items < ncu ? items : ncu;
     // Item order: a contiguous range per workgroup (the heads of a window
     // one after another) once a workgroup has at least 128 items; measured

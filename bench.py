@@ -390,7 +390,7 @@ def te_backward(args, mate, torch):
     rows = s.L * s.attn_heads * s.attn_headdim
     nbytes = 7 * rows * e                                # q, k, v, dO read; dq, dk, dv written
     flops = 10 * s.n_w * rows                            # S, dP, dq, dk, dv: five products of 2 n_w d
-    issued = 18 * s.n_w * rows                           # S three times, o, dP twice, dq, dk, dv
+    issued = 29 * s.n_w * rows // 2                      # S twice, o, dP, dq, dk, dv; row sums on a 16-wide ones operand
     out = {
         "kernel": "tesa_bwd", "workload": CONFIG_NOTES[args.config], "steps": args.steps,
         "bwd_ms": round(bwd_ms, 4), "fwd_ms": round(fwd_ms, 4), "bwd_over_fwd": round(bwd_ms / fwd_ms, 2),

@@ -8,16 +8,20 @@
 //
 // One workgroup of 8 waves per (window, head) item; the item's q, k, v and
 // dO tiles (256 x 64 bf16 each) sit in LDS, filled by direct global-to-LDS
-// loads.  Phase 1, each wave owning two 16-query tiles: an online-softmax
-// sweep over 32-key blocks gives the row maximum and sum and the output o
-// (fp32), hence log-sum-exp and D; a second sweep recomputes P, forms
-// dP^T = V dO^T and dS^T, and accumulates dq^T = K^T dS^T.  Phase 2, each
-// wave owning two 16-key tiles, sweeps 32-query blocks: P and dP from Q K^T
-// and dO V^T with the stored per-query statistics, then dv^T = dO^T P and
-// dk^T = Q^T dS.  The fragments a block reads from LDS serve both tiles.
-// Every product is a 16x16x32 bf16 MFMA with fp32 accumulation; the
-// k-permuted register operands and the transposing LDS reads are those of
-// the forward window kernel.
+// loads.  Phase A, each wave owning 32 query rows: an online-softmax sweep
+// over 32-key blocks gives each row's log-sum-exp and its output o (fp32),
+// hence D; the reference maximum of a row moves only when a block exceeds it
+// by more than 2^8 in weight, so most blocks skip the rescaling of o.  Phase
+// B, each wave owning 32 key rows, sweeps 32-query blocks once: S and dP
+// from Q K^T and dO V^T with the stored row statistics give P and dS, then
+// dv^T += dO^T P and dk^T += Q^T dS accumulate in registers.  The same dS
+// block, written key-major to LDS by all eight waves (in the space V no
+// longer needs), gives the block's dq = s dS K: each wave forms one 16x16
+// tile of it over all 256 keys, one block behind, beside the next block's
+// score products; two buffers and one barrier per block keep the writes of
+// a block clear of the reads of the one before.  Every product is a 16x16x32 bf16
+// MFMA with fp32 accumulation; the k-permuted register operands and the
+// transposing LDS reads are those of the forward window kernel.
 
 #include <hip/hip_runtime.h>
 
@@ -31,8 +35,60 @@ namespace lingen {
 
 namespace {
 
-constexpr int kBwdWin = 256, kBwdDim = 64;
-constexpr int kBwdTiles = 2;   // 16-row tiles per wave
+constexpr int kBwdWin = 256, kBwdDim = 64, kBwdWaves = 8;
+constexpr int kDsRow = 48;               // bf16 per key row of a dS block: 32 queries + padding
+constexpr int kDsBuf = kBwdWin * kDsRow; // one 32-query dS block, key-major
+constexpr float kLazy = 8.f;             // log2 of the largest weight before the row maximum moves
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding
+// (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt not waited for).
+constexpr int vmcnt_count(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+
+// Direct global-to-LDS load of 16 bytes per lane (lane i to lds_wave_base +
+// 16 i), issued from inline asm.  The compiler does not see these loads, so
+// it adds no wait of its own for them (it cannot tell which LDS array such a
+// load writes, and would wait for all of them before any LDS read); the
+// kernel waits for them itself with counted vmcnt waits, which also cover the
+// compiler's own vector-memory operations, since those complete in order
+// with these.  The instruction reads no result register.
+__device__ __forceinline__ void lds_load16_counted(const void* src, void* lds_wave_base) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_bf16*)lds_wave_base));
+  // (m0 is saved and restored around the load: the compiler reserves it)
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep)
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Barrier after waiting for this wave's direct global-to-LDS loads (vmcnt):
+// the wave has no LDS stores of its own pending, so the release half of
+// lds_barrier is not needed, and it would wait for every direct load still in
+// flight (they count as the wave's LDS stores), not just the ones waited for.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Maxima of scores (finite or -inf, never NaN) in one instruction each,
+// without the quieting of signalling NaNs that fmaxf adds to every operand.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// maximum over the four rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float vmax_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // 4-element pieces of the 16-wide d-tiles 2 r1 and 2 r1 + 1 exchanged between
 // lane groups g and g ^ 1: the lane then holds d0 .. d0 + 7 of its row,
@@ -55,63 +111,25 @@ __device__ __forceinline__ void store_rows16(__bf16* row, const f32x4 (&acc)[4],
 
 }  // namespace
 
-// QT row tiles of 16 per wave (16 / QT waves): the operand fragments read
-// from LDS for a block are shared by the wave's QT tiles.
-template <int QT>
-__global__ __launch_bounds__(64 * 16 / QT) void tesa_bwd_kernel(const __bf16* __restrict__ q,
-                                                                const __bf16* __restrict__ k,
-                                                                const __bf16* __restrict__ v,
-                                                                const __bf16* __restrict__ dO, WinGeom wg, int Ha,
-                                                                __bf16* __restrict__ dq, __bf16* __restrict__ dk,
-                                                                __bf16* __restrict__ dv) {
-  constexpr int NWIN = kBwdWin, DH = kBwdDim, ET = DH / 16, NKS = DH / 32;
-  constexpr int NW = 16 / QT, NTHR = NW * 64;
-  static_assert(NWIN == 16 * QT * NW, "one 16-row tile per wave and QT");
-  using KT = KvTile<__bf16, DH>;
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[NWIN * DH];
-  __shared__ __attribute__((aligned(16))) __bf16 sK[NWIN * DH];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[NWIN * DH];
-  __shared__ __attribute__((aligned(16))) __bf16 sG[NWIN * DH];   // dO
-  __shared__ __attribute__((aligned(16))) int sTok[NWIN];
-  __shared__ __attribute__((aligned(16))) int sCls[NWIN];
-  __shared__ __attribute__((aligned(16))) float sLse[NWIN];   // log2-sum-exp of the scaled scores
-  __shared__ __attribute__((aligned(16))) float sD[NWIN];     // sum_d dO . o
+// The item's tiles and per-slot tables in LDS.
+struct BwdLds {
+  __bf16 *sQ, *sK, *sG, *sV;   // sV: V, then the two dS blocks of phase B
+  int *sTok, *sCls;
+  float *sLse, *sD;            // log2-sum-exp of the scaled scores; sum_d dO . o
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Phases A and B of one item whose tiles are in LDS.  MASK: a window cut by
+// the grid's border, whose slots of different wrap classes do not attend to
+// each other; the two instantiations keep the loops free of branches.
+template <bool MASK>
+__device__ __forceinline__ void bwd_phases(const BwdLds& S, int lane, int wave, int64_t rowstride, int64_t hoff,
+                                           __bf16* __restrict__ dq, __bf16* __restrict__ dk,
+                                           __bf16* __restrict__ dv) {
+  constexpr int NWIN = kBwdWin, DH = kBwdDim, ET = DH / 16, NKS = DH / 32;
+  using KT = KvTile<__bf16, DH>;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int item = blockIdx.x;
-  const int h = item % Ha, win = item / Ha;
-  const int nwin_hw = wg.nwh * wg.nww;
-  const int wi = win / nwin_hw, wj = (win / wg.nww) % wg.nwh, wk = win % wg.nww;
-  const int64_t rowstride = int64_t(Ha) * DH;
-  const int64_t hoff = int64_t(h) * DH;
   const float sc = kLog2e * rsqrtf(float(DH));   // scores in log2 units
   const float snat = rsqrtf(float(DH));          // 1/sqrt(d)
-
-  for (int u = tid; u < NWIN; u += NTHR) {
-    const int a = u / (wg.wh * wg.ww), b = (u / wg.ww) % wg.wh, c = u % wg.ww;
-    int cl;
-    sTok[u] = window_token(wg, wi, wj, wk, a, b, c, cl);
-    sCls[u] = wg.masked ? cl : 0;
-  }
-  lds_barrier();
-  // Direct loads of the four tiles: 16-byte chunk u of a tile is row u/8,
-  // chunk (u%8) ^ (row%8) of that row (the KvTile permutation).
-  constexpr int PER_WAVE = NWIN * 8 / (NW * 64);   // load instructions per wave and tile
-#pragma unroll
-  for (int d = 0; d < PER_WAVE; ++d) {
-    const int base = (wave * PER_WAVE + d) * 64;
-    const int u = base + lane, row = u / 8, ch = (u % 8) ^ (row & 7);
-    const int64_t goff = int64_t(sTok[row]) * rowstride + hoff + ch * 8;
-    lds_load16(q + goff, sQ + base * 8);
-    lds_load16(k + goff, sK + base * 8);
-    lds_load16(v + goff, sV + base * 8);
-    lds_load16(dO + goff, sG + base * 8);
-  }
-  wait_vmem();
-  lds_barrier();
-
-  const bool wrapped = wg.masked && window_wrapped(wg, wi, wj, wk);
   // Per-lane LDS offsets: row fragments (A operand rows r16, or B operand
   // columns r16) and the transposing reads of a tile (as in the forward).
   int offk[NKS];
@@ -141,226 +159,355 @@ __global__ __launch_bounds__(64 * 16 / QT) void tesa_bwd_kernel(const __bf16* __
     }
     return p;
   };
-  auto mask = [&](f32x4& s, int j0, int c) {
-    const int4 kc = *reinterpret_cast<const int4*>(&sCls[j0 + 4 * grp]);
-    const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = kcv[r] != c ? -INFINITY : s[r];
-  };
 
-  // ---------------- Phase 1: the wave's query tiles -----------------------
+  // ---------------- Phase A: statistics of the wave's query rows ----------
   {
-    int icls[QT];
-    bf16x8 qf[QT][NKS], gf[QT][NKS];
+    int icls[2] = {0, 0};
+    bf16x8 qf[2][NKS];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int i0 = (wave * QT + qt) * 16;
-      icls[qt] = sCls[i0 + r16];
+    for (int qt = 0; qt < 2; ++qt) {
+      const int i0 = (2 * wave + qt) * 16;
+      if (MASK) icls[qt] = S.sCls[i0 + r16];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        qf[qt][ks] = rowfrag(sQ, i0, ks);
-        gf[qt][ks] = rowfrag(sG, i0, ks);
-      }
+      for (int ks = 0; ks < NKS; ++ks) qf[qt][ks] = rowfrag(S.sQ, i0, ks);
     }
-    // Sweep 1: online softmax statistics and the output o, 32 keys a step.
-    float m[QT], l[QT];
-    f32x4 o[QT][ET];
+    // m: the reference maximum of the row's scaled scores (-inf until a
+    // finite score), l: sum of the weights 2^(score - m) as rounded for the
+    // products (a product with a ones operand: every entry holds the row's
+    // sum), o: sum of the weights times v.
+    float m[2];
+    f32x4 l[2], o[2][ET];
+    bf16x8 ones;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
+    for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.f);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
       m[qt] = -INFINITY;
-      l[qt] = 0.f;
+      l[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int et = 0; et < ET; ++et) o[qt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll 1
     for (int jb = 0; jb < NWIN; jb += 32) {
+      if (jb == NWIN / 2) {
+        // the last 128 rows of K and V (every wave's loads of them done)
+        __builtin_amdgcn_s_waitcnt(vmcnt_count(4));
+        dma_barrier();
+      }
       bf16x8 kfr[2][NKS], vtr[ET];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) kfr[t][ks] = rowfrag(sK, jb + 16 * t, ks);
+        for (int ks = 0; ks < NKS; ++ks) kfr[t][ks] = rowfrag(S.sK, jb + 16 * t, ks);
 #pragma unroll
-      for (int et = 0; et < ET; ++et) vtr[et] = trfrag(sV, jb, et);
+      for (int et = 0; et < ET; ++et) vtr[et] = trfrag(S.sV, jb, et);
+      // S^T: the lane holds keys jb + 16 t + 4 g + r of query row r16
+      f32x4 s[2][2];
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        f32x4 s[2];
+      for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          s[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) s[t] = mma(kfr[t][ks], qf[qt][ks], s[t]);
-          if (wrapped) mask(s[t], jb + 16 * t, icls[qt]);
+          for (int ks = 0; ks < NKS; ++ks) s[qt][t] = mma(kfr[t][ks], qf[qt][ks], s[qt][t]);
         }
-        float bm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        bm = max_rows(bm);
-        const float mnew = fmaxf(m[qt], bm * sc);
-        const float mref = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = fast_exp2(m[qt] - mref);
-        m[qt] = mnew;
-        float ls = 0.f;
+      if (MASK) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int4 kc = *reinterpret_cast<const int4*>(&S.sCls[jb + 16 * t + 4 * grp]);
+          const int kcv[4] = {kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[qt][t][r] = kcv[r] != icls[qt] ? -INFINITY : s[qt][t][r];
+        }
+      }
+      float bm[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const f32x4 a = s[qt][0], b = s[qt][1];
+        bm[qt] = vmax_rows(vmax(vmax3(a[0], a[1], a[2]), vmax3(a[3], b[0], vmax3(b[1], b[2], b[3])))) * sc;
+      }
+      // Wave-uniform: move the reference maxima (and rescale) only when some
+      // row's block maximum exceeds its reference by more than kLazy.
+      if (__builtin_amdgcn_ballot_w64(bm[0] > m[0] + kLazy || bm[1] > m[1] + kLazy) != 0) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const float mnew = fmaxf(m[qt], bm[qt]);
+          const float alpha = m[qt] == -INFINITY ? 0.f : fast_exp2(m[qt] - mnew);
+          m[qt] = mnew;
+          l[qt][0] *= alpha;
+#pragma unroll
+          for (int et = 0; et < ET; ++et)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[qt][et][r] *= alpha;
+        }
+      }
+      bf16x8 pb[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        // all keys so far masked (a cut window): zero weights
+        const float mref = m[qt] == -INFINITY ? 0.f : m[qt];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            s[t][r] = fast_exp2(fmaf(s[t][r], sc, -mref));
-            ls += s[t][r];
-          }
-        l[qt] = fmaf(l[qt], alpha, ls);
-        const bf16x8 pb = pack(s[0], s[1]);
+          for (int r = 0; r < 4; ++r) s[qt][t][r] = fast_exp2(fmaf(s[qt][t][r], sc, -mref));
+        pb[qt] = pack(s[qt][0], s[qt][1]);
+      }
 #pragma unroll
-        for (int et = 0; et < ET; ++et) {
+      for (int qt = 0; qt < 2; ++qt) {
+        l[qt] = mma(ones, pb[qt], l[qt]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[qt][et][r] *= alpha;
-          o[qt][et] = mma(vtr[et], pb, o[qt][et]);
-        }
+        for (int et = 0; et < ET; ++et) o[qt][et] = mma(vtr[et], pb[qt], o[qt][et]);
       }
     }
-    float lse[QT], dsum[QT];
+    // dO (every wave's loads of it done)
+    __builtin_amdgcn_s_waitcnt(vmcnt_count(0));
+    dma_barrier();
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int i0 = (wave * QT + qt) * 16;
-      float lt = l[qt];
-      lt = sum_rows(lt);
+    for (int qt = 0; qt < 2; ++qt) {
+      const int i0 = (2 * wave + qt) * 16;
+      const float lt = l[qt][0];
       const float inv = 1.f / lt;
       // D_i = sum_d dO_i[d] o_i[d]: the lane holds o for d = et*16 + 4g + r.
       float ds_ = 0.f;
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
-        const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(sG + KT::at(i0 + r16, et * 16 + 4 * grp));
+        const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(S.sG + KT::at(i0 + r16, et * 16 + 4 * grp));
 #pragma unroll
         for (int r = 0; r < 4; ++r) ds_ = fmaf(static_cast<float>(g4[r]), o[qt][et][r] * inv, ds_);
       }
       ds_ = sum_rows(ds_);
-      dsum[qt] = ds_;
-      lse[qt] = m[qt] + log2f(lt);
       if (grp == 0) {
-        sLse[i0 + r16] = lse[qt];
-        sD[i0 + r16] = ds_;
+        // the query's own key is never masked, so m is finite here
+        S.sLse[i0 + r16] = m[qt] + log2f(lt);
+        S.sD[i0 + r16] = ds_;
       }
-    }
-    // Sweep 2: dS^T and dq^T = K^T dS^T, 32 keys a step.
-    f32x4 gq[QT][ET];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int et = 0; et < ET; ++et) gq[qt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int jb = 0; jb < NWIN; jb += 32) {
-      bf16x8 kfr[2][NKS], vfr[2][NKS], ktr[ET];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          kfr[t][ks] = rowfrag(sK, jb + 16 * t, ks);
-          vfr[t][ks] = rowfrag(sV, jb + 16 * t, ks);
-        }
-#pragma unroll
-      for (int et = 0; et < ET; ++et) ktr[et] = trfrag(sK, jb, et);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        f32x4 ds[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            s = mma(kfr[t][ks], qf[qt][ks], s);
-            dp = mma(vfr[t][ks], gf[qt][ks], dp);
-          }
-          if (wrapped) mask(s, jb + 16 * t, icls[qt]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ds[t][r] = fast_exp2(fmaf(s[r], sc, -lse[qt])) * (dp[r] - dsum[qt]);
-        }
-        const bf16x8 db = pack(ds[0], ds[1]);
-#pragma unroll
-        for (int et = 0; et < ET; ++et) gq[qt][et] = mma(ktr[et], db, gq[qt][et]);
-      }
-    }
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int i = (wave * QT + qt) * 16 + r16;
-      store_rows16(dq + int64_t(sTok[i]) * rowstride + hoff, gq[qt], snat, grp);
     }
   }
   lds_barrier();   // every query's statistics are in LDS
 
-  // ---------------- Phase 2: the wave's key tiles -------------------------
+  // ---------------- Phase B: the wave's key rows ---------------------------
   {
-    int jcls[QT];
-    bf16x8 kf[QT][NKS], vf[QT][NKS];
+    int jcls[2] = {0, 0};
+    bf16x8 kf[2][NKS], vf[2][NKS];
 #pragma unroll
-    for (int kt = 0; kt < QT; ++kt) {
-      const int j0 = (wave * QT + kt) * 16;
-      jcls[kt] = sCls[j0 + r16];
+    for (int kt = 0; kt < 2; ++kt) {
+      const int j0 = (2 * wave + kt) * 16;
+      if (MASK) jcls[kt] = S.sCls[j0 + r16];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        kf[kt][ks] = rowfrag(sK, j0, ks);
-        vf[kt][ks] = rowfrag(sV, j0, ks);
+        kf[kt][ks] = rowfrag(S.sK, j0, ks);
+        vf[kt][ks] = rowfrag(S.sV, j0, ks);
       }
     }
-    f32x4 gk[QT][ET], gv[QT][ET];
+    f32x4 gk[2][ET], gv[2][ET];
 #pragma unroll
-    for (int kt = 0; kt < QT; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
         gk[kt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
         gv[kt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-#pragma unroll 1
-    for (int ib = 0; ib < NWIN; ib += 32) {
+    lds_barrier();   // every wave holds its rows of V: the dS blocks take that space
+    // This wave's tile of each block's dq: d columns 16 eq .., queries 16 qh ..
+    const int eq = wave & 3, qh = wave >> 2;
+    // Offsets of the transposing reads of a dS block (key rows of kDsRow):
+    // lane (r16, g) reads key row 4 g + r16 / 4, queries 16 qh + 4 (r16 % 4) ..
+    const int offd = (4 * grp + (r16 >> 2)) * kDsRow + 16 * qh + 4 * (r16 & 3);
+
+    f32x4 s[2][2], dp[2][2];   // [kt][t]
+    float4 lv[2], dd[2];
+    // S and dP of block ib: the lane holds queries ib + 16 t + 4 g + r of key
+    // row 32 wave + 16 kt + r16.
+    auto scores = [&](int ib) {
       bf16x8 qfr[2][NKS], gfr[2][NKS];
-      float lv[2][4], dv4[2][4];
-      int qc[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int iq = ib + 16 * t;   // score rows iq + 4g + r
+        const int iq = ib + 16 * t;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          qfr[t][ks] = rowfrag(sQ, iq, ks);
-          gfr[t][ks] = rowfrag(sG, iq, ks);
+          qfr[t][ks] = rowfrag(S.sQ, iq, ks);
+          gfr[t][ks] = rowfrag(S.sG, iq, ks);
         }
-        const float4 ls4 = *reinterpret_cast<const float4*>(&sLse[iq + 4 * grp]);
-        const float4 dd = *reinterpret_cast<const float4*>(&sD[iq + 4 * grp]);
-        lv[t][0] = ls4.x; lv[t][1] = ls4.y; lv[t][2] = ls4.z; lv[t][3] = ls4.w;
-        dv4[t][0] = dd.x; dv4[t][1] = dd.y; dv4[t][2] = dd.z; dv4[t][3] = dd.w;
-        const int4 c4 = *reinterpret_cast<const int4*>(&sCls[iq + 4 * grp]);
-        qc[t][0] = c4.x; qc[t][1] = c4.y; qc[t][2] = c4.z; qc[t][3] = c4.w;
+        lv[t] = *reinterpret_cast<const float4*>(&S.sLse[iq + 4 * grp]);
+        dd[t] = *reinterpret_cast<const float4*>(&S.sD[iq + 4 * grp]);
       }
 #pragma unroll
-      for (int kt = 0; kt < QT; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          s[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            s[kt][t] = mma(qfr[t][ks], kf[kt][ks], s[kt][t]);
+            dp[kt][t] = mma(gfr[t][ks], vf[kt][ks], dp[kt][t]);
+          }
+        }
+    };
+    // P and dS of block ib, dv^T += dO^T P and dk^T += Q^T dS, and dS into
+    // the block's LDS buffer: key row 32 wave + 16 kt + r16, queries 16 t + 4 g ..
+    auto grads = [&](int ib, __bf16* ds_blk) {
+      bf16x8 trG[ET], trQ[ET];
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        trG[et] = trfrag(S.sG, ib, et);
+        trQ[et] = trfrag(S.sQ, ib, et);
+      }
+      bf16x8 pb[2], db[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
         f32x4 p[2], ds[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            s = mma(qfr[t][ks], kf[kt][ks], s);
-            dp = mma(gfr[t][ks], vf[kt][ks], dp);
+          const float lvv[4] = {lv[t].x, lv[t].y, lv[t].z, lv[t].w};
+          const float ddv[4] = {dd[t].x, dd[t].y, dd[t].z, dd[t].w};
+          int qcv[4] = {0, 0, 0, 0};
+          if (MASK) {
+            const int4 c4 = *reinterpret_cast<const int4*>(&S.sCls[ib + 16 * t + 4 * grp]);
+            qcv[0] = c4.x; qcv[1] = c4.y; qcv[2] = c4.z; qcv[3] = c4.w;
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float pv = (wrapped && qc[t][r] != jcls[kt]) ? 0.f : fast_exp2(fmaf(s[r], sc, -lv[t][r]));
+            float pv = fast_exp2(fmaf(s[kt][t][r], sc, -lvv[r]));
+            if (MASK) pv = qcv[r] != jcls[kt] ? 0.f : pv;
             p[t][r] = pv;
-            ds[t][r] = pv * (dp[r] - dv4[t][r]);
+            ds[t][r] = pv * (dp[kt][t][r] - ddv[r]);
           }
         }
-        const bf16x8 pb = pack(p[0], p[1]), db = pack(ds[0], ds[1]);
+        pb[kt] = pack(p[0], p[1]);
+        db[kt] = pack(ds[0], ds[1]);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int et = 0; et < ET; ++et) {
-          gv[kt][et] = mma(trfrag(sG, ib, et), pb, gv[kt][et]);
-          gk[kt][et] = mma(trfrag(sQ, ib, et), db, gk[kt][et]);
+          gv[kt][et] = mma(trG[et], pb[kt], gv[kt][et]);
+          gk[kt][et] = mma(trQ[et], db[kt], gk[kt][et]);
         }
-      }
-    }
 #pragma unroll
-    for (int kt = 0; kt < QT; ++kt) {
-      const int j = (wave * QT + kt) * 16 + r16;
-      const int64_t roff = int64_t(sTok[j]) * rowstride + hoff;
+      for (int kt = 0; kt < 2; ++kt) {
+        __bf16* row = ds_blk + (32 * wave + 16 * kt + r16) * kDsRow + 4 * grp;
+        *reinterpret_cast<bf16x4*>(row) = __builtin_shufflevector(db[kt], db[kt], 0, 1, 2, 3);
+        *reinterpret_cast<bf16x4*>(row + 16) = __builtin_shufflevector(db[kt], db[kt], 4, 5, 6, 7);
+      }
+    };
+    // dq of block ib once every wave's dS is in ds_blk: the wave's dq^T tile
+    // = K^T dS^T over the 256 keys, both operands by transposing reads (keys
+    // in the order 4 g .. 4 g + 3, 16 + 4 g ..); two accumulators halve the
+    // dependent chain.
+    auto dq_block = [&](int ib, const __bf16* ds_blk) {
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int b = 0; b < NWIN / 32; ++b) {
+        lds_bf16* t = (lds_bf16*)(ds_blk) + offd + 32 * b * kDsRow;
+        const bf16x4 lo = lds_read_tr(t), hi = lds_read_tr(t + 16 * kDsRow);
+        acc[b & 1] = mma(trfrag(S.sK, 32 * b, eq), __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                         acc[b & 1]);
+      }
+      // the lane holds dq[query ib + 16 qh + r16][d = 16 eq + 4 g + r]
+      bf16x4 out;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[r] = static_cast<__bf16>((acc[0][r] + acc[1][r]) * snat);
+      *reinterpret_cast<bf16x4*>(dq + int64_t(S.sTok[ib + 16 * qh + r16]) * rowstride + hoff + 16 * eq + 4 * grp) =
+          out;
+    };
+
+    // Block n's dq is formed in iteration n + 1, beside block n + 1's score
+    // products; one barrier per block publishes its dS and retires the reads
+    // of the buffer the block writes next.
+    scores(0);
+    grads(0, S.sV);
+#pragma unroll 1
+    for (int n = 1; n < NWIN / 32; ++n) {
+      lds_barrier();
+      scores(32 * n);
+      dq_block(32 * (n - 1), S.sV + ((n - 1) & 1) * kDsBuf);
+      grads(32 * n, S.sV + (n & 1) * kDsBuf);
+    }
+    lds_barrier();
+    dq_block(NWIN - 32, S.sV + ((NWIN / 32 - 1) & 1) * kDsBuf);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int j = (2 * wave + kt) * 16 + r16;
+      const int64_t roff = int64_t(S.sTok[j]) * rowstride + hoff;
       store_rows16(dk + roff, gk[kt], snat, grp);
       store_rows16(dv + roff, gv[kt], 1.f, grp);
     }
   }
+}
+
+__global__ __launch_bounds__(64 * kBwdWaves) void tesa_bwd_kernel(const __bf16* __restrict__ q,
+                                                                  const __bf16* __restrict__ k,
+                                                                  const __bf16* __restrict__ v,
+                                                                  const __bf16* __restrict__ dO, WinGeom wg, int Ha,
+                                                                  __bf16* __restrict__ dq, __bf16* __restrict__ dk,
+                                                                  __bf16* __restrict__ dv) {
+  constexpr int NWIN = kBwdWin, DH = kBwdDim;
+  constexpr int NW = kBwdWaves, NTHR = NW * 64;
+  static_assert(NWIN == 32 * NW, "32 query rows and 32 key rows per wave");
+  static_assert(2 * kDsBuf >= NWIN * DH, "the dS buffers fill the space of V");
+  // The tiles filled by direct loads must lie in the first 128 KiB of LDS,
+  // the range those loads address.  Q, K and dO (the most strictly aligned)
+  // are placed first; V's array follows, its first 32 KiB the V tile, and in
+  // phase B it takes the two dS blocks, which run 16 KiB past that.  Separate
+  // arrays also let the compiler tell the loads' targets apart, so that the
+  // staged waits below are not widened to all loads.
+  constexpr int TILE = NWIN * DH;
+  __shared__ __attribute__((aligned(1024))) __bf16 tQ[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 tK[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 tG[TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 tV[2 * kDsBuf];
+  __shared__ __attribute__((aligned(16))) int tTok[NWIN];
+  __shared__ __attribute__((aligned(16))) int tCls[NWIN];
+  __shared__ __attribute__((aligned(16))) float tLse[NWIN];
+  __shared__ __attribute__((aligned(16))) float tD[NWIN];
+  BwdLds S{tQ, tK, tG, tV, tTok, tCls, tLse, tD};
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int item = blockIdx.x;
+  const int h = item % Ha, win = item / Ha;
+  const int nwin_hw = wg.nwh * wg.nww;
+  const int wi = win / nwin_hw, wj = (win / wg.nww) % wg.nwh, wk = win % wg.nww;
+  const int64_t rowstride = int64_t(Ha) * DH;
+  const int64_t hoff = int64_t(h) * DH;
+
+  for (int u = tid; u < NWIN; u += NTHR) {
+    const int a = u / (wg.wh * wg.ww), b = (u / wg.ww) % wg.wh, c = u % wg.ww;
+    int cl;
+    S.sTok[u] = window_token(wg, wi, wj, wk, a, b, c, cl);
+    S.sCls[u] = wg.masked ? cl : 0;
+  }
+  lds_barrier();
+  // Direct loads of the four tiles in the order phase A needs them: Q, the
+  // first 128 rows of K and V, their last 128 rows (waited for halfway
+  // through phase A), then dO (waited for at its end).  16-byte chunk u of a
+  // tile is row u/8, chunk (u%8) ^ (row%8) of that row (the KvTile
+  // permutation); load d of a wave takes chunks (d * 8 + wave) * 64 .., so
+  // loads 0 and 1 of every wave fill rows 0 .. 127.
+  static_assert(NWIN * 8 == 4 * NW * 64, "four loads per wave and tile");
+  auto issue = [&](const __bf16* src, __bf16* dst, int d) {
+    const int base = (d * NW + wave) * 64;
+    const int u = base + lane, row = u / 8, ch = (u % 8) ^ (row & 7);
+    lds_load16_counted(src + int64_t(S.sTok[row]) * rowstride + hoff + ch * 8, dst + base * 8);
+  };
+#pragma unroll
+  for (int d = 0; d < 4; ++d) issue(q, S.sQ, d);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    issue(k, S.sK, d);
+    issue(v, S.sV, d);
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) issue(dO, S.sG, d);
+  __builtin_amdgcn_s_waitcnt(vmcnt_count(8));   // Q and the first halves of K and V
+  dma_barrier();
+
+  if (wg.masked && window_wrapped(wg, wi, wj, wk))
+    bwd_phases<true>(S, lane, wave, rowstride, hoff, dq, dk, dv);
+  else
+    bwd_phases<false>(S, lane, wave, rowstride, hoff, dq, dk, dv);
 }
 
 
@@ -498,7 +645,7 @@ extern "C" int lingen_te_bwd(const void* q, const void* k, const void* v, const 
   const int64_t per = L * shape->attn_heads * kBwdDim;   // elements per batch element
   for (int b = 0; b < shape->batch; ++b) {
     const int64_t off = int64_t(b) * per;
-    tesa_bwd_kernel<kBwdTiles><<<items, 64 * 16 / kBwdTiles, 0, stream>>>(
+    tesa_bwd_kernel<<<items, 64 * kBwdWaves, 0, stream>>>(
         static_cast<const __bf16*>(q) + off, static_cast<const __bf16*>(k) + off, static_cast<const __bf16*>(v) + off,
         static_cast<const __bf16*>(d_out) + off, g, shape->attn_heads, static_cast<__bf16*>(dq) + off,
         static_cast<__bf16*>(dk) + off, static_cast<__bf16*>(dv) + off);

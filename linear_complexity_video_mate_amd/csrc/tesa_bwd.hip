@@ -50,7 +50,7 @@ constexpr int vmcnt_count(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); 
 // load writes, and would wait for all of them before any LDS read); the
 // kernel waits for them itself with counted vmcnt waits, which also cover the
 // compiler's own vector-memory operations, since those complete in order
-// with these.  The instruction reads no result register.
+// with these.  The instruction has no result register: its data goes to LDS.
 __device__ __forceinline__ void lds_load16_counted(const void* src, void* lds_wave_base) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_bf16*)lds_wave_base));
   // (m0 is saved and restored around the load: the compiler reserves it)

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   static_assert(Q % 32 == 0 && Q <= NT && N % 32 == 0 && QT <= NW && (P * N) % (8 * NT) == 0 &&
                 (Q * P) % (8 * NT) == 0 && (Q * N) % (8 * NT) == 0, "tiles");
   __shared__ __attribute__((aligned(16))) __bf16 sB[Q * LDB], sC[Q * LDB], sX[Q * LDX], sDY[Q * LDX];
-  __shared__ __attribute__((aligned(16))) __bf16 sU[U_ELEMS];   // E (Q x Q), then a state (P x N rows)
+  __shared__ __attribute__((aligned(16))) __bf16 sU[U_ELEMS];   // E^T (Q x Q, row s), then a state (P x N rows)
   __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], red[NW];
   __shared__ int s_tok[Q];
   __bf16* const sE = sU;
@@ -283,28 +283,61 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         }
         const int s2 = s0 + lr;
         const float ds = s_dt[s2], cs_s = s_cs[s2], csx_s = s_csx[s2];
-        float cf = 0.f, cbk = 0.f;
+        bf16x4 e4;
+        // A tile below the diagonal holds forward pairs only (s < t), one
+        // above it backward pairs only: one decay each, and one column sum.
+        if (s0 < t0) {
+          float cf = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t0 + 4 * lg + r;
-          const float df = s2 <= t ? __expf(cs_t[r] - cs_s) : 0.f;
-          const float db = s2 >= t ? __expf(csx_s - csx_t[r]) : 0.f;
-          const float e = ds * dx[r];
-          sE[t * LDE + s2] = static_cast<__bf16>(e * (df + db));
-          const float v = e * cb[r];
-          const float wf = s2 < t ? df * v : 0.f;
-          const float wb = s2 > t ? db * v : 0.f;
-          rf[r] += wf;
-          rb[r] += wb;
-          cf += wf;
-          cbk += wb;
+          for (int r = 0; r < 4; ++r) {
+            const float df = __expf(cs_t[r] - cs_s);
+            const float e = ds * dx[r];
+            e4[r] = static_cast<__bf16>(e * df);
+            const float wf = df * (e * cb[r]);
+            rf[r] += wf;
+            cf += wf;
+          }
+          cf = sum_rows(cf);
+          if (lg == 0) atomicAdd(s_fw + s2, -cf);
+        } else if (s0 > t0) {
+          float cbk = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float db = __expf(csx_s - csx_t[r]);
+            const float e = ds * dx[r];
+            e4[r] = static_cast<__bf16>(e * db);
+            const float wb = db * (e * cb[r]);
+            rb[r] += wb;
+            cbk += wb;
+          }
+          cbk = sum_rows(cbk);
+          if (lg == 0) atomicAdd(s_bw + s2, -cbk);
+        } else {
+          float cf = 0.f, cbk = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * lg + r;
+            const float df = s2 <= t ? __expf(cs_t[r] - cs_s) : 0.f;
+            const float db = s2 >= t ? __expf(csx_s - csx_t[r]) : 0.f;
+            const float e = ds * dx[r];
+            e4[r] = static_cast<__bf16>(e * (df + db));
+            const float v = e * cb[r];
+            const float wf = s2 < t ? df * v : 0.f;
+            const float wb = s2 > t ? db * v : 0.f;
+            rf[r] += wf;
+            rb[r] += wb;
+            cf += wf;
+            cbk += wb;
+          }
+          cf = sum_rows(cf);
+          cbk = sum_rows(cbk);
+          if (lg == 0) {
+            atomicAdd(s_fw + s2, -cf);
+            atomicAdd(s_bw + s2, -cbk);
+          }
         }
-        cf = sum_rows(cf);
-        cbk = sum_rows(cbk);
-        if (lg == 0) {
-          atomicAdd(s_fw + s2, -cf);
-          atomicAdd(s_bw + s2, -cbk);
-        }
+        // E is stored transposed (row s, column t): the lane's four t are one 8-byte piece
+        *reinterpret_cast<bf16x4*>(sE + s2 * LDE + t0 + 4 * lg) = e4;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -325,8 +358,8 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     if (owns_rows) {
 #pragma unroll 1
       for (int kb = 0; kb < Q; kb += 32) {
-        const bf16x8 ea = perm_frag(sE + (r0 + lr) * LDE, kb, lane);     // E rows r0.., k = s
-        const bf16x8 et = tr_frag(sE, LDE, kb, r0, lane);                  // E^T rows r0.., k = t
+        const bf16x8 ea = tr_frag(sE, LDE, kb, r0, lane);                  // E rows r0.., k = s
+        const bf16x8 et = perm_frag(sE + (r0 + lr) * LDE, kb, lane);     // E^T rows r0.., k = t
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
           gC[j] = mma(tr_frag(sB, LDB, kb, 16 * j, lane), ea, gC[j]);

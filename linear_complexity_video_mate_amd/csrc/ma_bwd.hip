@@ -372,47 +372,61 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     // four terms in two rounds, each round the two states whose inner
     // product enters K ((hf1, hb2), then (hb1, hf2)), staged side by side
     float k = 0.f;
-    auto do_term = [&](int term, const __bf16* sMt) {
-      const bool is_u = (term == 0 || term == 2);          // U terms: dy, C, dC; V terms: x, B, dB
-      const __bf16* sa = is_u ? sDY : sX;
-      const __bf16* sv = is_u ? sC : sB;
-      // rows of the term's operand (dy or x) as the MFMA's columns, k = p
-      bf16x8 af[P / 32];
+    // The round's two terms on one loop over the column tiles, so that each
+    // tile carries two independent product chains: a U term (dy, C, into dC)
+    // with the state in sM0 and a V term (x, B, into dB) with the state in
+    // sM1.  Round 0: U_f with hf1, V_f with hb2; round 1: U_b with hb1, V_b
+    // with hf2.
+    auto do_terms = [&](int round) {
+      // rows of dy and x as the MFMA's columns, k = p
+      bf16x8 au[P / 32], av[P / 32];
 #pragma unroll
-      for (int kk = 0; kk < P / 32; ++kk) af[kk] = perm_frag(sa + (r0 + lr) * LDX, 32 * kk, lane);
-      // the row scale of this term for the lane's row t
+      for (int kk = 0; kk < P / 32; ++kk) {
+        au[kk] = perm_frag(sDY + (r0 + lr) * LDX, 32 * kk, lane);
+        av[kk] = perm_frag(sX + (r0 + lr) * LDX, 32 * kk, lane);
+      }
+      // the terms' row scales for the lane's row t
       const int t = r0 + lr;
-      const float scale = term == 0 ? __expf(s_cs[t])
-                        : term == 1 ? s_dt[t] * __expf(cs_last - s_cs[t])
-                        : term == 2 ? __expf(cs_last - s_csx[t])
-                                    : s_dt[t] * __expf(s_csx[t]);
-      const __bf16* svr = sv + t * LDB + 4 * lg;
-      float part = 0.f;
+      const float su = round == 0 ? __expf(s_cs[t]) : __expf(cs_last - s_csx[t]);
+      const float sv = round == 0 ? s_dt[t] * __expf(cs_last - s_cs[t]) : s_dt[t] * __expf(s_csx[t]);
+      const __bf16* crow = sC + t * LDB + 4 * lg;
+      const __bf16* brow = sB + t * LDB + 4 * lg;
+      float pu = 0.f, pv = 0.f;
 #pragma unroll
       for (int nt = 0; nt < NTL; ++nt) {
         const int n0 = nt * 16;
         // (state^T a^T)[n][t] for n = n0 + 4 lg + r
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 accu = {0.f, 0.f, 0.f, 0.f}, accv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < P / 32; ++kk) acc = mma(tr_frag(sMt, LDB, 32 * kk, n0, lane), af[kk], acc);
-        const bf16x4 v4 = *reinterpret_cast<const bf16x4*>(svr + n0);
+        for (int kk = 0; kk < P / 32; ++kk) {
+          accu = mma(tr_frag(sM0, LDB, 32 * kk, n0, lane), au[kk], accu);
+          accv = mma(tr_frag(sM1, LDB, 32 * kk, n0, lane), av[kk], accv);
+        }
+        const bf16x4 c4 = *reinterpret_cast<const bf16x4*>(crow + n0);
+        const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(brow + n0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          part = fmaf(acc[r], static_cast<float>(v4[r]), part);
-          if (is_u) gC[nt][r] = fmaf(scale, acc[r], gC[nt][r]);
-          else gB[nt][r] = fmaf(scale, acc[r], gB[nt][r]);
+          pu = fmaf(accu[r], static_cast<float>(c4[r]), pu);
+          pv = fmaf(accv[r], static_cast<float>(b4[r]), pv);
+          gC[nt][r] = fmaf(su, accu[r], gC[nt][r]);
+          gB[nt][r] = fmaf(sv, accv[r], gB[nt][r]);
         }
       }
-      part = sum_rows(part);
+      pu = sum_rows(pu);
+      pv = sum_rows(pv);
       if (lg == 0) {
-        const float v = scale * part;
-        if (term == 0) s_fw[t] += v;                       // U_f
-        else if (term == 1) { s_bw[t] += v; s_sub[t] += v; }  // V_f
-        else if (term == 2) s_bw[t] += v;                  // U_b
-        else { s_fw[t] += v; s_sub[t] += v; }              // V_b
+        const float vu = su * pu, vv = sv * pv;
+        if (round == 0) {
+          s_fw[t] += vu;    // U_f
+          s_bw[t] += vv;    // V_f
+        } else {
+          s_bw[t] += vu;    // U_b
+          s_fw[t] += vv;    // V_b
+        }
+        s_sub[t] += vv;
       }
     };
-#pragma unroll 1
+#pragma unroll
     for (int round = 0; round < 2; ++round) {
       lds_barrier();   // E (and the previous states) are no longer read; the pair sums have landed
 #pragma unroll
@@ -432,9 +446,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         }
       }
       lds_barrier();
-      if (!owns_rows) continue;
-      do_term(2 * round, sM0);
-      do_term(2 * round + 1, sM1);
+      if (owns_rows) do_terms(round);
     }
     k = __expf(cs_last) * block_sum512(k, red);   // its barriers also order the boundary terms before the scans
 

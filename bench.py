@@ -686,6 +686,53 @@ def roofline_of(work, kernel, ms, workload):
             "avg_launch_ms": round(ms, 4)}
 
 
+def run_config_child(config_id, steps, warmup):
+    """The benchmark line of one workload, from a child process (this
+    process never touches the GPU, so each workload gets a fresh one)."""
+    import subprocess
+
+    cmd = [sys.executable, os.path.abspath(__file__), "--config", str(config_id), "--steps", str(steps),
+           "--warmup", str(warmup), "--no-cpu-baseline", "--no-scaling"]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"bench.py --config {config_id} exited with {res.returncode}")
+    lines = [ln for ln in res.stdout.splitlines() if ln.startswith("{")]
+    if not lines:
+        raise RuntimeError(f"bench.py --config {config_id} printed no result line")
+    return json.loads(lines[-1])
+
+
+def sweep(path, n_configs, run):
+    """One benchmark line per workload appended to `path` (JSON lines, each
+    tagged with its config id).  Workloads already in the file are skipped,
+    so a sweep that was cut short resumes where it stopped; a line that does
+    not parse (a run killed mid-write) counts as not done."""
+    done = set()
+    if os.path.exists(path):
+        with open(path) as f:
+            for line in f:
+                try:
+                    done.add(int(json.loads(line)["config_id"]))
+                except (ValueError, KeyError, TypeError):
+                    continue
+    for cid in range(n_configs):
+        if cid in done:
+            print(f"[bench] sweep: config {cid} already in {path}", file=sys.stderr, flush=True)
+            continue
+        print(f"[bench] sweep: config {cid}", file=sys.stderr, flush=True)
+        rec = dict(run(cid))
+        rec["config_id"] = cid
+        with open(path, "a+") as f:
+            # after a line cut short, start a fresh one
+            if f.tell() > 0:
+                f.seek(f.tell() - 1)
+                if f.read(1) != "\n":
+                    f.write("\n")
+            f.write(json.dumps(rec) + "\n")
+            f.flush()
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -698,6 +745,10 @@ def main(argv=None):
                          f"at most {MAX_CPU_WORKERS})")
     ap.add_argument("--no-scaling", action="store_true",
                     help="skip the linear-scaling leg (the forward on the first quarter of the frames)")
+    ap.add_argument("--sweep", metavar="FILE",
+                    help="run the benchmark line of every workload, each in a child process (no oracle leg, "
+                         "no scaling leg), appending one JSON line per workload to FILE; workloads already "
+                         "in FILE are skipped")
     ap.add_argument("--record-traffic", nargs=4, metavar=("MIX_FETCH", "MIX_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="add the --config workload's record to profiles/hbm_traffic.json from rocprofv3 --pmc "
                          "FETCH_SIZE / WRITE_SIZE CSVs of this benchmark and of the --copy-gib calibration run, "
@@ -726,6 +777,10 @@ def main(argv=None):
                          "quadratic mixer MATE replaces) against the MATE forward on the workload")
     args = ap.parse_args(argv)
 
+    if args.sweep:
+        from mate_inputs import CONFIGS
+
+        return sweep(args.sweep, len(CONFIGS), lambda cid: run_config_child(cid, args.steps, args.warmup))
     if args.record_traffic:
         return record_traffic(*args.record_traffic, config=args.config)
 

@@ -115,7 +115,7 @@ __device__ __forceinline__ void store_rows16(__bf16* row, const f32x4 (&acc)[4],
 struct BwdLds {
   __bf16 *sQ, *sK, *sG, *sV;   // sV: V, then the two dS blocks of phase B
   int *sTok, *sCls;
-  float *sLse, *sD;            // log2-sum-exp of the scaled scores; sum_d dO . o
+  float *sLse, *sD;            // log2-sum-exp of the scaled scores; -sum_d dO . o
 };
 
 // Phases A and B of one item whose tiles are in LDS.  MASK: a window cut by
@@ -281,7 +281,7 @@ __device__ __forceinline__ void bwd_phases(const BwdLds& S, int lane, int wave, 
       if (grp == 0) {
         // the query's own key is never masked, so m is finite here
         S.sLse[i0 + r16] = m[qt] + log2f(lt);
-        S.sD[i0 + r16] = ds_;
+        S.sD[i0 + r16] = -ds_;   // stored negated: it starts phase B's dP accumulators
       }
     }
   }
@@ -317,7 +317,8 @@ __device__ __forceinline__ void bwd_phases(const BwdLds& S, int lane, int wave, 
     const int offd = (4 * grp + (r16 >> 2)) * kDsRow + 16 * qh + 4 * (r16 & 3);
 
     f32x4 s[2][2], dp[2][2];   // [kt][t]
-    float4 lv[2], dd[2];
+    float4 lv[2];
+    f32x4 dd[2];   // -D of the block's rows
     // S and dP of block ib: the lane holds queries ib + 16 t + 4 g + r of key
     // row 32 wave + 16 kt + r16.
     auto scores = [&](int ib) {
@@ -331,14 +332,14 @@ __device__ __forceinline__ void bwd_phases(const BwdLds& S, int lane, int wave, 
           gfr[t][ks] = rowfrag(S.sG, iq, ks);
         }
         lv[t] = *reinterpret_cast<const float4*>(&S.sLse[iq + 4 * grp]);
-        dd[t] = *reinterpret_cast<const float4*>(&S.sD[iq + 4 * grp]);
+        dd[t] = *reinterpret_cast<const f32x4*>(&S.sD[iq + 4 * grp]);
       }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           s[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[kt][t] = dd[t];   // dP - D: the products start from -D of the row
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             s[kt][t] = mma(qfr[t][ks], kf[kt][ks], s[kt][t]);
@@ -362,7 +363,6 @@ __device__ __forceinline__ void bwd_phases(const BwdLds& S, int lane, int wave, 
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const float lvv[4] = {lv[t].x, lv[t].y, lv[t].z, lv[t].w};
-          const float ddv[4] = {dd[t].x, dd[t].y, dd[t].z, dd[t].w};
           int qcv[4] = {0, 0, 0, 0};
           if (MASK) {
             const int4 c4 = *reinterpret_cast<const int4*>(&S.sCls[ib + 16 * t + 4 * grp]);
@@ -373,7 +373,7 @@ __device__ __forceinline__ void bwd_phases(const BwdLds& S, int lane, int wave, 
             float pv = fast_exp2(fmaf(s[kt][t][r], sc, -lvv[r]));
             if (MASK) pv = qcv[r] != jcls[kt] ? 0.f : pv;
             p[t][r] = pv;
-            ds[t][r] = pv * (dp[kt][t][r] - ddv[r]);
+            ds[t][r] = pv * dp[kt][t][r];
           }
         }
         pb[kt] = pack(p[0], p[1]);
@@ -397,13 +397,16 @@ __device__ __forceinline__ void bwd_phases(const BwdLds& S, int lane, int wave, 
     // = K^T dS^T over the 256 keys, both operands by transposing reads (keys
     // in the order 4 g .. 4 g + 3, 16 + 4 g ..); two accumulators halve the
     // dependent chain.
+    bf16x8 kstrip[NWIN / 32];   // K^T rows of the wave's dq columns, all 256 keys
+#pragma unroll
+    for (int b = 0; b < NWIN / 32; ++b) kstrip[b] = trfrag(S.sK, 32 * b, eq);
     auto dq_block = [&](int ib, const __bf16* ds_blk) {
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int b = 0; b < NWIN / 32; ++b) {
         lds_bf16* t = (lds_bf16*)(ds_blk) + offd + 32 * b * kDsRow;
         const bf16x4 lo = lds_read_tr(t), hi = lds_read_tr(t + 16 * kDsRow);
-        acc[b & 1] = mma(trfrag(S.sK, 32 * b, eq), __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+        acc[b & 1] = mma(kstrip[b], __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
                          acc[b & 1]);
       }
       // the lane holds dq[query ib + 16 qh + r16][d = 16 eq + 4 g + r]

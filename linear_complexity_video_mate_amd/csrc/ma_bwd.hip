@@ -188,6 +188,36 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
   const bool owns_rows = wave < QT;
   const int r0 = wave * 16;   // the row block this wave owns in the Q x N results
 
+  // C B^T on the wave's pair tiles (the same for every head of the group),
+  // formed once and kept in registers as bf16, in the order the pair loop
+  // below walks the tiles: that loop takes each tile's four values from the
+  // front of the vector and rotates the next tile's to the front.
+  static_assert(QT * QT == CBT * NW, "every wave walks CBT pair tiles, so the rotation comes full circle");
+  typedef __bf16 bf16xcb __attribute__((ext_vector_type(4 * CBT)));
+  bf16xcb cbq;
+  auto rotate_tiles = [](const bf16xcb& v) {
+    bf16xcb o;
+#pragma unroll
+    for (int i = 0; i < 4 * CBT; ++i) o[i] = v[(i + 4) % (4 * CBT)];
+    return o;
+  };
+#pragma unroll
+  for (int q = 0; q < CBT; ++q) {
+    const int tile = wave + q * NW;
+    const int t0 = (wave % QT) * 16, s0 = ((tile / QT + wave % QT) % QT) * 16;
+    f32x4 cb = {0.f, 0.f, 0.f, 0.f};
+    if (tile < QT * QT) {
+#pragma unroll
+      for (int k = 0; k < N; k += 32) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sC + (t0 + lr) * LDB + k + 8 * lg);
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(sB + (s0 + lr) * LDB + k + 8 * lg);
+        cb = mma(a, v, cb);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cbq[4 * q + r] = static_cast<__bf16>(cb[r]);
+  }
+
 #pragma unroll 1
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
@@ -268,13 +298,10 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
         const int tile = wave + q * NW;
         if (tile >= QT * QT) break;
         const int s0 = ((tile / QT + wave % QT) % QT) * 16;
-        f32x4 cb = {0.f, 0.f, 0.f, 0.f}, dx = {0.f, 0.f, 0.f, 0.f};
+        f32x4 cb, dx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < N; k += 32) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sC + (t0 + lr) * LDB + k + 8 * lg);
-          const bf16x8 v = *reinterpret_cast<const bf16x8*>(sB + (s0 + lr) * LDB + k + 8 * lg);
-          cb = mma(a, v, cb);
-        }
+        for (int r = 0; r < 4; ++r) cb[r] = static_cast<float>(cbq[r]);
+        cbq = rotate_tiles(cbq);
 #pragma unroll
         for (int k = 0; k < P; k += 32) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(sDY + (t0 + lr) * LDX + k + 8 * lg);

@@ -451,21 +451,22 @@ __global__ __launch_bounds__(64 * kBwdWaves) void tesa_bwd_kernel(const __bf16* 
   constexpr int NW = kBwdWaves, NTHR = NW * 64;
   static_assert(NWIN == 32 * NW, "32 query rows and 32 key rows per wave");
   static_assert(2 * kDsBuf >= NWIN * DH, "the dS buffers fill the space of V");
-  // The tiles filled by direct loads must lie in the first 128 KiB of LDS,
-  // the range those loads address.  Q, K and dO (the most strictly aligned)
-  // are placed first; V's array follows, its first 32 KiB the V tile, and in
-  // phase B it takes the two dS blocks, which run 16 KiB past that.  Separate
-  // arrays also let the compiler tell the loads' targets apart, so that the
-  // staged waits below are not widened to all loads.
+  // One LDS array (the kernel's only one, so it starts at LDS address 0):
+  // the four tiles filled by direct loads lie in its first 128 KiB, the
+  // range those loads address, and V's 32 KiB, the last of them, take the
+  // two dS blocks in phase B, which run 16 KiB past it; the per-slot tables
+  // follow.
   constexpr int TILE = NWIN * DH;
-  __shared__ __attribute__((aligned(1024))) __bf16 tQ[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 tK[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 tG[TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 tV[2 * kDsBuf];
-  __shared__ __attribute__((aligned(16))) int tTok[NWIN];
-  __shared__ __attribute__((aligned(16))) int tCls[NWIN];
-  __shared__ __attribute__((aligned(16))) float tLse[NWIN];
-  __shared__ __attribute__((aligned(16))) float tD[NWIN];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[(3 * TILE + 2 * kDsBuf) * 2 + 4 * NWIN * 4];
+  static_assert(4 * TILE * 2 <= 128 * 1024, "direct-load targets below 128 KiB");
+  __bf16* const tQ = reinterpret_cast<__bf16*>(smem);
+  __bf16* const tK = tQ + TILE;
+  __bf16* const tG = tQ + 2 * TILE;
+  __bf16* const tV = tQ + 3 * TILE;
+  int* const tTok = reinterpret_cast<int*>(tV + 2 * kDsBuf);
+  int* const tCls = tTok + NWIN;
+  float* const tLse = reinterpret_cast<float*>(tCls + NWIN);
+  float* const tD = tLse + NWIN;
   BwdLds S{tQ, tK, tG, tV, tTok, tCls, tLse, tD};
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

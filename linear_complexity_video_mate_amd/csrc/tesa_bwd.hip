@@ -8,7 +8,8 @@
 //
 // One workgroup of 8 waves per (window, head) item; the item's q, k, v and
 // dO tiles (256 x 64 bf16 each) sit in LDS, filled by direct global-to-LDS
-// loads.  Phase A, each wave owning 32 query rows: an online-softmax sweep
+// loads in the order phase A needs them (Q and the first half of K and V
+// before it starts, the rest waited for inside it).  Phase A, each wave owning 32 query rows: an online-softmax sweep
 // over 32-key blocks gives each row's log-sum-exp and its output o (fp32),
 // hence D; the reference maximum of a row moves only when a block exceeds it
 // by more than 2^8 in weight, so most blocks skip the rescaling of o.  Phase
@@ -453,9 +454,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void tesa_bwd_kernel(const __bf16* 
   static_assert(2 * kDsBuf >= NWIN * DH, "the dS buffers fill the space of V");
   // One LDS array (the kernel's only one, so it starts at LDS address 0):
   // the four tiles filled by direct loads lie in its first 128 KiB, the
-  // range those loads address, and V's 32 KiB, the last of them, take the
-  // two dS blocks in phase B, which run 16 KiB past it; the per-slot tables
-  // follow.
+  // range those loads address, and V's 32 KiB, the last of them, take (with
+  // the 16 KiB after them) the two dS blocks of phase B; the per-slot
+  // tables follow.
   constexpr int TILE = NWIN * DH;
   __shared__ __attribute__((aligned(16))) unsigned char smem[(3 * TILE + 2 * kDsBuf) * 2 + 4 * NWIN * 4];
   static_assert(4 * TILE * 2 <= 128 * 1024, "direct-load targets below 128 KiB");

@@ -542,7 +542,9 @@ def mate_block(args, mate, torch):
 def ma_backward(args, mate, torch):
     """The MA branch's backward pass (lingen_ma_bwd) on the workload against
     its forward (lingen_ma_fwd), both timed with events on the launch stream,
-    scan order = step mod 4."""
+    scan order = step mod 4; and the saved-state pair (lingen_ma_fwd_saved,
+    then lingen_ma_bwd_saved reading the scan states that forward kept, one
+    saved buffer per scan order)."""
     from mate_inputs import CONFIGS, CONFIG_NOTES, make_inputs
 
     s = CONFIGS[args.config]
@@ -569,6 +571,12 @@ def ma_backward(args, mate, torch):
 
     bwd_ms = timed(lambda i: mate.lingen_ma_bwd(*args_f, dy, i % 4, s, grads=grads, workspace=ws))
     fwd_ms = timed(lambda i: mate.lingen_ma_fwd(*args_f, i % 4, s, out=y, workspace=fws))
+    del ws
+    saved = [mate.lingen_ma_fwd_saved(*args_f, m, s, out=y)[1] for m in range(4)]
+    ws_s = torch.empty(mate.lingen_ma_bwd_saved_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    fwd_saved_ms = timed(lambda i: mate.lingen_ma_fwd_saved(*args_f, i % 4, s, out=y, saved=saved[i % 4]))
+    bwd_saved_ms = timed(lambda i: mate.lingen_ma_bwd_saved(*args_f, dy, saved[i % 4], i % 4, s, grads=grads,
+                                                             workspace=ws_s))
     e = s.elem_bytes
     rows = s.batch * s.L
     G, N, Hs, P = s.ngroups, s.d_state, s.ssd_heads, s.headdim
@@ -577,7 +585,11 @@ def ma_backward(args, mate, torch):
     out = {"kernel": "ma_bwd", "workload": CONFIG_NOTES[args.config], "steps": args.steps,
            "bwd_ms": round(bwd_ms, 4), "fwd_ms": round(fwd_ms, 4), "bwd_over_fwd": round(bwd_ms / fwd_ms, 2),
            "compulsory_bytes": nbytes, "compulsory_GB/s": round(nbytes / bwd_ms / 1e6, 1),
-           "workspace_GiB": round(ws.numel() / 2 ** 30, 2)}
+           "workspace_GiB": round(mate.lingen_ma_bwd_workspace_bytes(s) / 2 ** 30, 2),
+           "saved": {"fwd_ms": round(fwd_saved_ms, 4), "bwd_ms": round(bwd_saved_ms, 4),
+                     "bwd_over_fwd": round(bwd_saved_ms / fwd_saved_ms, 2),
+                     "saved_GiB": round(saved[0].numel() / 2 ** 30, 2),
+                     "workspace_GiB": round(ws_s.numel() / 2 ** 30, 2)}}
     print(json.dumps(out), flush=True)
     return 0
 

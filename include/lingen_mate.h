@@ -333,6 +333,39 @@ int lingen_ma_bwd(const void* x, const float* dt, const float* A, const void* B,
                   float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The same backward pass with the forward scan states saved by the forward
+ * instead of computed again (memory traded for time, as a training step
+ * keeps activations for its backward pass): lingen_ma_fwd_saved computes
+ * y_ma exactly as lingen_ma_fwd does and leaves, per batch element, the
+ * chunk states of both scan directions (and, with review tokens, the pooled
+ * review tokens) in `saved`; lingen_ma_bwd_saved then reads them in place
+ * of its first chunk-state pass (a chunk-state launch and a two-direction
+ * state pass per batch element).  The kernels and their order are those of
+ * lingen_ma_fwd and lingen_ma_bwd: y_ma (no atomic sums) and dx equal
+ * theirs bit for bit, the other gradients up to the order in which their
+ * floating-point atomic sums land.
+ *   saved:  device, caller-owned, lingen_ma_saved_bytes (per batch
+ *           element, the scan workspace lingen_ma_fwd runs in: mostly its
+ *           chunk states, 2 * (L / chunk) * Hs * P * N storage elements);
+ *           written by lingen_ma_fwd_saved, read by
+ *           lingen_ma_bwd_saved, which must be given the same x, dt, A, B,
+ *           mode and shape (nothing checks that it was).
+ *   workspace of lingen_ma_bwd_saved: lingen_ma_bwd_saved_workspace_bytes
+ *           (lingen_ma_bwd's without its first scan workspace).
+ * Other arguments, supported families and errors: those of lingen_ma_fwd
+ * and lingen_ma_bwd; LINGEN_ERR_WORKSPACE also when saved_bytes is below
+ * lingen_ma_saved_bytes. */
+int lingen_ma_saved_bytes(const lingen_mate_shape* shape, size_t* bytes);
+int lingen_ma_fwd_saved(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                        const float* D, int32_t mode, const lingen_mate_shape* shape, void* y_ma,
+                        void* saved, size_t saved_bytes, hipStream_t stream);
+int lingen_ma_bwd_saved_workspace_bytes(const lingen_mate_shape* shape, size_t* bytes);
+int lingen_ma_bwd_saved(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                        const float* D, const void* dy, const void* saved, size_t saved_bytes,
+                        int32_t mode, const lingen_mate_shape* shape, float* dx, float* ddt, float* dA,
+                        float* dB, float* dC, float* dD, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
 /* ----------------------------------------------------------------------------
  * Steps around the scan.  The MA branch is a bidirectional Mamba2 block (page
  * "视频生成模子太贵太慢如何办？", section 要领：线性复杂度的 MATE 模块); these two

@@ -58,6 +58,10 @@ EXPORTS = (
     "lingen_mate_block_fwd",
     "lingen_ma_bwd_workspace_bytes",
     "lingen_ma_bwd",
+    "lingen_ma_saved_bytes",
+    "lingen_ma_fwd_saved",
+    "lingen_ma_bwd_saved_workspace_bytes",
+    "lingen_ma_bwd_saved",
 )
 
 BLOCK_WEIGHTS = ("w_z", "w_xbc", "w_dt", "conv_w_f", "conv_b_f", "conv_w_b", "conv_b_b", "dt_bias", "A_f", "D_f",
@@ -118,6 +122,10 @@ def lib() -> ctypes.CDLL:
         "lingen_mate_block_workspace_bytes": ([SP, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "lingen_ma_bwd_workspace_bytes": ([SP, ctypes.POINTER(SZ)], ctypes.c_int),
         "lingen_ma_bwd": ([P] * 7 + [I32, SP] + [P] * 7 + [SZ, P], ctypes.c_int),
+        "lingen_ma_saved_bytes": ([SP, ctypes.POINTER(SZ)], ctypes.c_int),
+        "lingen_ma_fwd_saved": ([P] * 6 + [I32, SP, P, P, SZ, P], ctypes.c_int),
+        "lingen_ma_bwd_saved_workspace_bytes": ([SP, ctypes.POINTER(SZ)], ctypes.c_int),
+        "lingen_ma_bwd_saved": ([P] * 8 + [SZ, I32, SP] + [P] * 7 + [SZ, P], ctypes.c_int),
         "lingen_mate_block_fwd": ([P, ctypes.POINTER(lingen_mate_block_weights), I32, I32, ctypes.c_float, I32, SP,
                                    P, P, SZ, P], ctypes.c_int),
     }
@@ -590,18 +598,11 @@ def lingen_ma_bwd_workspace_bytes(shape) -> int:
     return n.value
 
 
-def lingen_ma_bwd(x, dt, A, B, C, D, dy, mode: int, shape, grads=None, workspace=None):
-    """Gradients (dx, ddt, dA, dB, dC, dD) of sum(dy * y_ma) for the MA
-    branch of lingen_ma_fwd (no review tokens), all fp32 GPU tensors."""
+def _ma_grads(shape, grads):
     torch = _torch()
     n = _sizes(shape)
-    td = _tdtype(shape)
-    cs = to_c_shape(shape)
     L = shape.T * shape.H * shape.W
     f32 = torch.float32
-    args = [_need(x, "x", td, n["x"]), _need(dt, "dt", f32, n["dt"]), _need(A, "A", f32, n["A"]),
-            _need(B, "B", td, n["B"]), _need(C, "C", td, n["B"]), _need(D, "D", f32, n["D"]),
-            _need(dy, "dy", td, n["y"])]
     if grads is None:
         dev = "cuda"
         grads = (torch.empty((shape.batch, L, shape.ssd_heads, shape.headdim), dtype=f32, device=dev),
@@ -612,10 +613,77 @@ def lingen_ma_bwd(x, dt, A, B, C, D, dy, mode: int, shape, grads=None, workspace
                  torch.empty(shape.ssd_heads, dtype=f32, device=dev))
     sizes = (n["x"], n["dt"], n["A"], n["B"], n["B"], n["D"])
     pg = [_need(g, name, f32, sz) for g, name, sz in zip(grads, ("dx", "ddt", "dA", "dB", "dC", "dD"), sizes)]
-    need = lingen_ma_bwd_workspace_bytes(shape)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-    pw = ctypes.c_void_p(workspace.data_ptr())
-    nw = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    return grads, pg
+
+
+def _ma_bwd_inputs(shape, x, dt, A, B, C, D, dy):
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    f32 = torch.float32
+    return [_need(x, "x", td, n["x"]), _need(dt, "dt", f32, n["dt"]), _need(A, "A", f32, n["A"]),
+            _need(B, "B", td, n["B"]), _need(C, "C", td, n["B"]), _need(D, "D", f32, n["D"]),
+            _need(dy, "dy", td, n["y"])]
+
+
+def _device_buffer(need, buf):
+    torch = _torch()
+    if buf is None:
+        buf = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    return buf, ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(buf.numel() * buf.element_size())
+
+
+def lingen_ma_bwd(x, dt, A, B, C, D, dy, mode: int, shape, grads=None, workspace=None):
+    """Gradients (dx, ddt, dA, dB, dC, dD) of sum(dy * y_ma) for the MA
+    branch of lingen_ma_fwd, all fp32 GPU tensors."""
+    args = _ma_bwd_inputs(shape, x, dt, A, B, C, D, dy)
+    grads, pg = _ma_grads(shape, grads)
+    workspace, pw, nw = _device_buffer(lingen_ma_bwd_workspace_bytes(shape), workspace)
+    cs = to_c_shape(shape)
     _check("lingen_ma_bwd", lib().lingen_ma_bwd(*args, int(mode), ctypes.byref(cs), *pg, pw, nw, _stream()))
+    return grads
+
+
+def lingen_ma_saved_bytes(shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check("lingen_ma_saved_bytes", lib().lingen_ma_saved_bytes(ctypes.byref(to_c_shape(shape)), ctypes.byref(n)))
+    return n.value
+
+
+def lingen_ma_bwd_saved_workspace_bytes(shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check("lingen_ma_bwd_saved_workspace_bytes",
+           lib().lingen_ma_bwd_saved_workspace_bytes(ctypes.byref(to_c_shape(shape)), ctypes.byref(n)))
+    return n.value
+
+
+def lingen_ma_fwd_saved(x, dt, A, B, C, D, mode: int, shape, out=None, saved=None):
+    """lingen_ma_fwd that keeps its scan states for lingen_ma_bwd_saved;
+    returns (y_ma [batch, L, Hs*P], saved uint8 buffer)."""
+    torch = _torch()
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    L = shape.T * shape.H * shape.W
+    if out is None:
+        out = torch.empty((shape.batch, L, shape.ssd_heads * shape.headdim), dtype=td, device="cuda")
+    args = [_need(x, "x", td, n["x"]), _need(dt, "dt", torch.float32, n["dt"]),
+            _need(A, "A", torch.float32, n["A"]), _need(B, "B", td, n["B"]), _need(C, "C", td, n["B"]),
+            _need(D, "D", torch.float32, n["D"])]
+    py = _need(out, "out", td, n["y"])
+    saved, ps, ns = _device_buffer(lingen_ma_saved_bytes(shape), saved)
+    cs = to_c_shape(shape)
+    _check("lingen_ma_fwd_saved", lib().lingen_ma_fwd_saved(*args, int(mode), ctypes.byref(cs), py, ps, ns, _stream()))
+    return out, saved
+
+
+def lingen_ma_bwd_saved(x, dt, A, B, C, D, dy, saved, mode: int, shape, grads=None, workspace=None):
+    """lingen_ma_bwd from the scan states lingen_ma_fwd_saved left in
+    ``saved`` (same inputs and mode); the same gradients."""
+    args = _ma_bwd_inputs(shape, x, dt, A, B, C, D, dy)
+    grads, pg = _ma_grads(shape, grads)
+    _, ps, ns = _device_buffer(0, saved)
+    workspace, pw, nw = _device_buffer(lingen_ma_bwd_saved_workspace_bytes(shape), workspace)
+    cs = to_c_shape(shape)
+    _check("lingen_ma_bwd_saved", lib().lingen_ma_bwd_saved(*args, ps, ns, int(mode), ctypes.byref(cs), *pg, pw, nw,
+                                                            _stream()))
     return grads

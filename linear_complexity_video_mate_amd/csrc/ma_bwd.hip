@@ -875,14 +875,16 @@ struct BwdWs {
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
+// saved: the forward scan states come from the caller's saved buffer (no
+// first scan workspace).
+int bwd_layout(const lingen_mate_shape* s, BwdWs* w, bool saved = false) {
   const size_t rows = size_t(s->batch) * size_t(tokens(s));
   const size_t hs = size_t(s->ssd_heads), P = size_t(s->headdim);
   size_t ws_main = 0;
   if (int rc = lingen_mate_workspace_bytes(s, &ws_main)) return rc;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
-  w->scan1 = take(ws_main);
+  w->scan1 = take(saved ? 0 : ws_main);
   w->scan2 = take(ws_main);
   w->R = take(rows * hs * 4);
   w->yh = take(rows * hs * P * (s->dtype == LINGEN_BF16 ? 2 : 4));
@@ -896,6 +898,11 @@ int bwd_layout(const lingen_mate_shape* s, BwdWs* w) {
   w->total = off;
   return LINGEN_OK;
 }
+
+// The saved buffer of lingen_ma_fwd_saved: per batch element one forward
+// workspace (ws_layout), which keeps that element's chunk states (and, with
+// review tokens, the pooled review tokens) after the forward.
+size_t saved_stride(const lingen_mate_shape* s) { return align256(ws_layout(s).total); }
 
 // The crossing-sum kernels are compiled for the three scan families: bf16
 // with P = 64 and N = Q = 64 or 128 (MFMA tiles), fp32 with P = 32 and
@@ -926,17 +933,23 @@ extern "C" int lingen_ma_bwd_workspace_bytes(const lingen_mate_shape* shape, siz
   return LINGEN_OK;
 }
 
-extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
-                             const float* D, const void* dy, int32_t mode, const lingen_mate_shape* shape,
-                             float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+namespace lingen {
+namespace {
+// The backward pass; saved (nullable) holds the forward scan states of every
+// batch element as lingen_ma_fwd_saved left them, which replaces the first
+// of the two chunk-state passes.
+int ma_bwd_impl(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                const void* dy, const void* saved, size_t saved_bytes, int32_t mode, const lingen_mate_shape* shape,
+                float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
   if (int rc = check_bwd_shape(shape)) return rc;
   if (mode < 0 || mode > 3) return LINGEN_ERR_SHAPE;
   const void* ptrs[] = {x, dt, A, B, C, D, dy, dx, ddt, dA, dB, dC, dD, workspace};
   for (const void* p : ptrs)
     if (int rc = check_ptr(p)) return rc;
+  if (saved != nullptr && saved_bytes < size_t(shape->batch) * saved_stride(shape)) return LINGEN_ERR_WORKSPACE;
   BwdWs w{};
-  if (int rc = bwd_layout(shape, &w)) return rc;
+  if (int rc = bwd_layout(shape, &w, saved != nullptr)) return rc;
   if (workspace_bytes < w.total) return LINGEN_ERR_WORKSPACE;
 
   char* ws = static_cast<char*>(workspace);
@@ -976,16 +989,19 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
     const dim3 cgrid{unsigned(nc), unsigned(G), 1u};
     const WsLayout lay = ws_layout(shape);
     const int64_t per = int64_t(nc) * Hs * P * N;   // one direction's scan states
-    const __bf16* st1 = reinterpret_cast<const __bf16*>(ws + w.scan1 + lay.states);
     const __bf16* st2 = reinterpret_cast<const __bf16*>(ws + w.scan2 + lay.states);
     const int64_t eb = f32 ? 4 : 2;
     for (int bi = 0; bi < shape->batch; ++bi) {
       // forward / reverse states of (x, B) and of (x', C) for this batch element, left in the two workspaces
+      // (the first one saved by the forward, when given)
       const int64_t xo = int64_t(bi) * L * Hs * P * eb, bo = int64_t(bi) * L * G * N * eb;
+      const char* scan1 = saved ? static_cast<const char*>(saved) + size_t(bi) * saved_stride(shape) : ws + w.scan1;
+      const __bf16* st1 = reinterpret_cast<const __bf16*>(scan1 + lay.states);
       // with review tokens, this pass also pools them (into scan1's review
       // buffers) and starts both walks from their state
-      LINGEN_TRY(scan_states_one(shape, mode, static_cast<const char*>(x) + xo, dt + int64_t(bi) * L * Hs, A,
-                                 static_cast<const char*>(B) + bo, ws + w.scan1, stream, kWeightDt, nullptr));
+      if (!saved)
+        LINGEN_TRY(scan_states_one(shape, mode, static_cast<const char*>(x) + xo, dt + int64_t(bi) * L * Hs, A,
+                                   static_cast<const char*>(B) + bo, ws + w.scan1, stream, kWeightDt, nullptr));
       // the adjoint scan has no review state; its final carries are the
       // adjoints of the two directions' initial states
       LINGEN_TRY(scan_states_one(&plain, mode, static_cast<const char*>(dy) + xo, dt + int64_t(bi) * L * Hs, A,
@@ -997,7 +1013,7 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
                                    static_cast<char*>(at(w.yh)) + xo, stream));
       if (R) {
         const WsLayout rl = ws_layout(shape);
-        const float* s1 = reinterpret_cast<const float*>(ws + w.scan1);
+        const float* s1 = reinterpret_cast<const float*>(scan1);
         review_bwd_kernel<<<Hs, kThreads, 0, stream>>>(
             atf(w.hlast), s1 + rl.review_x / 4, s1 + rl.review_dt / 4, s1 + rl.review_b / 4, A, R, Hs, P, N, G,
             atf(w.gx) + int64_t(bi) * R * Hs * P, atf(w.gdt) + int64_t(bi) * R * Hs,
@@ -1045,4 +1061,68 @@ extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, con
 #undef LINGEN_TRY
 #undef LINGEN_LAUNCHED
   return LINGEN_OK;
+}
+}  // namespace
+}  // namespace lingen
+
+extern "C" int lingen_ma_bwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                             const float* D, const void* dy, int32_t mode, const lingen_mate_shape* shape,
+                             float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return ma_bwd_impl(x, dt, A, B, C, D, dy, nullptr, 0, mode, shape, dx, ddt, dA, dB, dC, dD, workspace,
+                     workspace_bytes, stream);
+}
+
+extern "C" int lingen_ma_saved_bytes(const lingen_mate_shape* shape, size_t* bytes) {
+  if (bytes == nullptr) return LINGEN_ERR_NULL;
+  if (int rc = check_bwd_shape(shape)) return rc;
+  *bytes = size_t(shape->batch) * saved_stride(shape);
+  return LINGEN_OK;
+}
+
+extern "C" int lingen_ma_fwd_saved(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                                   const float* D, int32_t mode, const lingen_mate_shape* shape, void* y_ma,
+                                   void* saved, size_t saved_bytes, hipStream_t stream) {
+  if (int rc = check_bwd_shape(shape)) return rc;
+  if (mode < 0 || mode > 3) return LINGEN_ERR_SHAPE;
+  const void* ptrs[] = {x, dt, A, B, C, D, y_ma, saved};
+  for (const void* p : ptrs)
+    if (int rc = check_ptr(p)) return rc;
+  const size_t stride = saved_stride(shape);
+  if (saved_bytes < size_t(shape->batch) * stride) return LINGEN_ERR_WORKSPACE;
+  // one batch element at a time, each with its own slice of the saved
+  // buffer as the forward's workspace
+  lingen_mate_shape one = *shape;
+  one.batch = 1;
+  const int64_t L = tokens(shape), Hs = shape->ssd_heads, P = shape->headdim;
+  const int64_t bn = int64_t(shape->ngroups) * shape->d_state;
+  const int64_t eb = shape->dtype == LINGEN_F32 ? 4 : 2;
+  for (int bi = 0; bi < shape->batch; ++bi) {
+    const int64_t xo = bi * L * Hs * P * eb, bo = bi * L * bn * eb;
+    if (int rc = lingen_ma_fwd(static_cast<const char*>(x) + xo, dt + bi * L * Hs, A,
+                               static_cast<const char*>(B) + bo, static_cast<const char*>(C) + bo, D, mode, &one,
+                               static_cast<char*>(y_ma) + xo, static_cast<char*>(saved) + size_t(bi) * stride,
+                               stride, stream))
+      return rc;
+  }
+  return LINGEN_OK;
+}
+
+extern "C" int lingen_ma_bwd_saved_workspace_bytes(const lingen_mate_shape* shape, size_t* bytes) {
+  if (bytes == nullptr) return LINGEN_ERR_NULL;
+  if (int rc = check_bwd_shape(shape)) return rc;
+  BwdWs w{};
+  if (int rc = bwd_layout(shape, &w, true)) return rc;
+  *bytes = w.total;
+  return LINGEN_OK;
+}
+
+extern "C" int lingen_ma_bwd_saved(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                                   const float* D, const void* dy, const void* saved, size_t saved_bytes,
+                                   int32_t mode, const lingen_mate_shape* shape, float* dx, float* ddt, float* dA,
+                                   float* dB, float* dC, float* dD, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  if (int rc = check_ptr(saved)) return rc;
+  return ma_bwd_impl(x, dt, A, B, C, D, dy, saved, saved_bytes, mode, shape, dx, ddt, dA, dB, dC, dD, workspace,
+                     workspace_bytes, stream);
 }

@@ -379,6 +379,52 @@ def test_ma_bwd_rejects_before_launch(L):
     assert L.lingen_ma_bwd_workspace_bytes(ctypes.byref(cs), None) == -1
 
 
+def test_ma_saved_rejects_before_launch(L):
+    """The saved-state forward and backward: sizes and the checks that
+    return before any launch."""
+    F = ctypes.c_void_p(FAKE)
+    Z = ctypes.c_void_p(0)
+    M = ctypes.c_void_p(MISALIGNED)
+    al = lambda b: (b + 255) // 256 * 256
+    for s in (CONFIGS[0], CONFIGS[1], CONFIGS[1].with_(batch=3),
+              CONFIGS[1].with_(n_review=64, rpool=(2, 4, 4), rgrid=(4, 4, 4))):
+        # per batch element one scan workspace of the forward
+        assert mate.lingen_ma_saved_bytes(s) == s.batch * al(mate.lingen_mate_workspace_bytes(s))
+        # the backward's workspace without its first scan workspace
+        assert (mate.lingen_ma_bwd_saved_workspace_bytes(s)
+                == mate.lingen_ma_bwd_workspace_bytes(s) - al(mate.lingen_mate_workspace_bytes(s)))
+    s = CONFIGS[1].with_(batch=2)
+    cs = mate.to_c_shape(s)
+    ns = mate.lingen_ma_saved_bytes(s)
+    nw = mate.lingen_ma_bwd_saved_workspace_bytes(s)
+    fwd, bwd = L.lingen_ma_fwd_saved, L.lingen_ma_bwd_saved
+    for bad in (-1, 4):
+        assert fwd(*[F] * 6, bad, ctypes.byref(cs), F, F, ns, None) == -2
+        assert bwd(*[F] * 8, ns, bad, ctypes.byref(cs), *[F] * 7, nw, None) == -2
+    for i in range(8):   # x, dt, A, B, C, D, y_ma, saved
+        p = [F] * 8
+        p[i] = Z
+        assert fwd(*p[:6], 0, ctypes.byref(cs), p[6], p[7], ns, None) == -1, i
+        p[i] = M
+        assert fwd(*p[:6], 0, ctypes.byref(cs), p[6], p[7], ns, None) == -4, i
+    for i in range(15):   # x, dt, A, B, C, D, dy, saved, six gradients, workspace
+        p = [F] * 15
+        p[i] = Z
+        assert bwd(*p[:8], ns, 0, ctypes.byref(cs), *p[8:], nw, None) == -1, i
+        p[i] = M
+        assert bwd(*p[:8], ns, 0, ctypes.byref(cs), *p[8:], nw, None) == -4, i
+    assert fwd(*[F] * 6, 0, ctypes.byref(cs), F, F, ns - 1, None) == -5
+    assert bwd(*[F] * 8, ns - 1, 0, ctypes.byref(cs), *[F] * 7, nw, None) == -5
+    assert bwd(*[F] * 8, ns, 0, ctypes.byref(cs), *[F] * 7, nw - 1, None) == -5
+    # a scan with no compiled kernels
+    c = mate.to_c_shape(CONFIGS[1].with_(d_state=32))
+    size = ctypes.c_size_t(0)
+    assert L.lingen_ma_saved_bytes(ctypes.byref(c), ctypes.byref(size)) == -7
+    assert fwd(*[F] * 6, 0, ctypes.byref(c), F, F, ns, None) == -7
+    assert L.lingen_ma_saved_bytes(ctypes.byref(cs), None) == -1
+    assert L.lingen_ma_bwd_saved_workspace_bytes(ctypes.byref(cs), None) == -1
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     import linear_complexity_video_mate_amd.binding as b
     monkeypatch.setattr(b, "_lib", None)

@@ -10,7 +10,10 @@ and the 768p-like workload with its 64 review tokens, dy on one head),
 against the oracle's ma_bwd, whose review path is pinned by finite
 differences.  Bar: relative L2 error at most 2e-2 per gradient (bf16
 storage).  The fp32 family (the 4x8x8 grid: every scan order, one and two
-groups, review tokens, a batch of two) at 1e-4."""
+groups, review tokens, a batch of two) at 1e-4.  The saved-state pair
+(lingen_ma_fwd_saved, lingen_ma_bwd_saved) against lingen_ma_fwd and
+lingen_ma_bwd on the same inputs: y_ma and dx bit for bit, the other
+gradients to 1e-6 (the order of float atomic sums)."""
 import numpy as np
 import pytest
 
@@ -291,3 +294,48 @@ def test_ma_bwd_fp32_batch_of_two():
             e = max(rel_l2(g[b].reshape(np.shape(refs[b][i])), refs[b][i]) for b in range(2))
         say(f"  {name}: rel L2 {e:.3e}")
         assert e <= TOL_F32, (name, e)
+
+
+# The saved-state pair: same kernels as lingen_ma_fwd + lingen_ma_bwd, with
+# the forward's scan states kept instead of computed again.
+SAVED_CASES = {
+    "bf16-16k-g2-mode1": dict(cfg=1, kw=dict(ngroups=2), mode=1, batch=1),
+    "bf16-16k-batch2-mode2": dict(cfg=1, kw=dict(T=4), mode=2, batch=2),
+    "bf16-16k-review-mode3": dict(cfg=1, kw=dict(n_review=64, rpool=(2, 4, 4), rgrid=(4, 4, 4)), mode=3, batch=1),
+    "bf16-512p-like-mode3": dict(cfg=2, kw={}, mode=3, batch=1),
+    "fp32-review-g2-mode2": dict(cfg=0, kw=dict(ngroups=2, n_review=4, rpool=(2, 2, 2), rgrid=(1, 2, 2)), mode=2,
+                                 batch=1),
+    "fp32-batch2-mode0": dict(cfg=0, kw={}, mode=0, batch=2),
+}
+
+
+@pytest.mark.parametrize("case", list(SAVED_CASES))
+def test_ma_saved_matches_recompute(case):
+    torch, mate = need_gpu()
+    c = SAVED_CASES[case]
+    base = CONFIGS[c["cfg"]].with_(**c["kw"])
+    s = base.with_(batch=c["batch"])
+    mode = c["mode"]
+    parts = [make_inputs(base, c["cfg"], seed=201 + b, tensors=list(SCAN), threads=16) for b in range(c["batch"])]
+    dys = [_dy(base, c["cfg"], 211 + b) for b in range(c["batch"])]
+    say(f"ma saved vs recompute: {case} ({s.T}x{s.H}x{s.W} batch {s.batch} {s.dtype} mode{mode})")
+    cat = lambda n: torch.stack([p.torch(n, "cuda") for p in parts])
+    x, dt, B, C = cat("x"), cat("dt"), cat("B"), cat("C")
+    A, D = parts[0].torch("A", "cuda"), parts[0].torch("D", "cuda")
+    if s.dtype == "bf16":
+        dy = torch.stack([torch.from_numpy(v.view(np.int16)).view(torch.bfloat16) for v in dys]).cuda()
+    else:
+        dy = torch.stack([torch.from_numpy(v) for v in dys]).cuda()
+    y_ref = mate.lingen_ma_fwd(x, dt, A, B, C, D, mode, s)
+    ref = [g.clone() for g in mate.lingen_ma_bwd(x, dt, A, B, C, D, dy, mode, s)]
+    y, saved = mate.lingen_ma_fwd_saved(x, dt, A, B, C, D, mode, s)
+    got = mate.lingen_ma_bwd_saved(x, dt, A, B, C, D, dy, saved, mode, s)
+    torch.cuda.synchronize()
+    assert saved.numel() == mate.lingen_ma_saved_bytes(s)
+    assert torch.equal(y.view(torch.int16 if s.dtype == "bf16" else torch.int32),
+                       y_ref.view(torch.int16 if s.dtype == "bf16" else torch.int32)), "y_ma"
+    assert torch.equal(got[0], ref[0]), "dx"
+    for name, g, r in zip(NAMES, got, ref):
+        e = rel_l2(to_np(g), to_np(r))
+        say(f"  {name}: rel L2 to the recomputing backward {e:.2e}")
+        assert e <= 1e-6, name

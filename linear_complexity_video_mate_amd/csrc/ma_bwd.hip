@@ -103,9 +103,12 @@ __device__ __forceinline__ bf16x8 perm_frag(const __bf16* row, int k0, int lane)
 }
 
 // Per (chunk, group, batch element), looping over the group's heads (head
-// size 64): the crossing sums R_r behind ddt and dA, written to R [batch, L,
-// Hs], and the gradients dB, dC of the chunk's tokens, written to [batch, L,
-// G, N] fp32.  With cs the chunk-local inclusive cumulative sum of dt*A
+// size 64): the crossing sums R_r behind ddt and dA, and from them and the
+// transposed outputs yhat = (M_f^T + M_b^T) dy / dt the per-token gradients
+//   dx = dt yhat + 2 D dy,   ddt = x . yhat + A R,   dA += dt R,   dD += 2 dy . x
+// (dx [batch, L, Hs, P], ddt [batch, L, Hs]; dA and dD [Hs], added to), and
+// the gradients dB, dC of the chunk's tokens, written to [batch, L, G, N]
+// fp32.  With cs the chunk-local inclusive cumulative sum of dt*A
 // along the scan order and csx its exclusive form:
 //   forward pairs s <= t:  decay exp(cs_t - cs_s),   backward pairs s >= t:
 //   decay exp(csx_s - csx_t); E_ts = dt_s (dy_t . x_s) (sum of the decays that
@@ -135,7 +138,9 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ dy, const float* __restrict__ dt,
     const float* __restrict__ A, const __bf16* __restrict__ B, const __bf16* __restrict__ C,
     const __bf16* __restrict__ st1, const __bf16* __restrict__ st2, int64_t per, ScanOrder so, int L, int Hs,
-    int G, int b, float* __restrict__ R, float* __restrict__ dB, float* __restrict__ dC) {
+    int G, int b, const __bf16* __restrict__ yh, const float* __restrict__ D, float* __restrict__ dx,
+    float* __restrict__ ddt, float* __restrict__ dA, float* __restrict__ dD, float* __restrict__ dB,
+    float* __restrict__ dC) {
   constexpr int P = 64, NT = kCrossThreads, NW = NT / 64;
   constexpr int LDB = N + 8, LDX = P + 8, LDE = Q + 8;   // padded bf16 row strides
   constexpr int QT = Q / 16, NTL = N / 16;
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
                 (Q * P) % (8 * NT) == 0 && (Q * N) % (8 * NT) == 0, "tiles");
   __shared__ __attribute__((aligned(16))) __bf16 sB[Q * LDB], sC[Q * LDB], sX[Q * LDX], sDY[Q * LDX];
   __shared__ __attribute__((aligned(16))) __bf16 sU[U_ELEMS];   // E^T (Q x Q, row s), then a state (P x N rows)
-  __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], red[NW];
+  __shared__ float s_cs[Q], s_csx[Q], s_dt[Q], s_fw[Q], s_bw[Q], s_sub[Q], red[NW], s_hsum[2];
   __shared__ int s_tok[Q];
   __bf16* const sE = sU;
   __bf16* const sM0 = sU;
@@ -223,6 +228,14 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
     const int h = g * hpg + hh;
     const float a_h = A[h];
     lds_barrier();   // the previous head is done with every shared array
+    if (tid == 0) {   // the previous head's dA, dD shares of this chunk
+      if (hh > 0) {
+        atomicAdd(dA + h - 1, s_hsum[0]);
+        atomicAdd(dD + h - 1, s_hsum[1]);
+      }
+      s_hsum[0] = 0.f;
+      s_hsum[1] = 0.f;
+    }
     {
       // dt, x and dy rows: every load is issued before the first LDS store
       constexpr int UX = Q * (P / 8) / NT;
@@ -475,6 +488,18 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       lds_barrier();
       if (owns_rows) do_terms(round);
     }
+    // this head's yhat rows, used at the end of the head.  The thread index
+    // goes through an empty asm statement, so the addresses of this part are
+    // formed anew in every head rather than kept in registers across the loop.
+    constexpr int UT = Q * (P / 8) / NT;
+    int tidh = tid;
+    asm volatile("" : "+v"(tidh));
+    bf16x8 yv[UT];
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      const int i = tidh + u * NT, row = i / (P / 8), k8 = (i % (P / 8)) * 8;
+      yv[u] = *reinterpret_cast<const bf16x8*>(yh + ((bl + s_tok[row]) * Hs + h) * P + k8);
+    }
     k = __expf(cs_last) * block_sum512(k, red);   // its barriers also order the boundary terms before the scans
 
     // suffix sums of s_fw, prefix sums of s_bw, by wave 0 (the suffix sums as
@@ -497,7 +522,50 @@ __global__ __launch_bounds__(kCrossThreads) void ma_bwd_cross_kernel(
       }
     }
     lds_barrier();
-    if (tid < Q) R[(bl + s_tok[tid]) * Hs + h] = s_fw[tid] + s_bw[tid] - s_sub[tid] + k;
+    // the per-token gradients of this head: eight lanes per token row
+    {
+      const float two_d = 2.f * D[h];
+      float da = 0.f, dd = 0.f;
+#pragma unroll
+      for (int u = 0; u < UT; ++u) {
+        const int i = tidh + u * NT, row = i / (P / 8), k8 = (i % (P / 8)) * 8;
+        const float dtr = s_dt[row];
+        const float r = s_fw[row] + s_bw[row] - s_sub[row] + k;
+        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(sX + row * LDX + k8);
+        const bf16x8 dv = *reinterpret_cast<const bf16x8*>(sDY + row * LDX + k8);
+        float gx[8], xyh = 0.f, dyx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float vx = static_cast<float>(xv[e]), vd = static_cast<float>(dv[e]);
+          const float vh = static_cast<float>(yv[u][e]);
+          xyh = fmaf(vx, vh, xyh);
+          dyx = fmaf(vd, vx, dyx);
+          gx[e] = fmaf(dtr, vh, two_d * vd);
+        }
+        const int64_t rh = (bl + s_tok[row]) * Hs + h;
+        float4* o = reinterpret_cast<float4*>(dx + rh * P + k8);
+        o[0] = make_float4(gx[0], gx[1], gx[2], gx[3]);
+        o[1] = make_float4(gx[4], gx[5], gx[6], gx[7]);
+        xyh = sum8(xyh);
+        dyx = sum8(dyx);
+        if (k8 == 0) {
+          ddt[rh] = xyh + a_h * r;
+          da += dtr * r;
+          dd += 2.f * dyx;
+        }
+      }
+      da = sum64(da);
+      dd = sum64(dd);
+      if (lane == 0) {
+        atomicAdd(&s_hsum[0], da);
+        atomicAdd(&s_hsum[1], dd);
+      }
+    }
+  }
+  lds_barrier();
+  if (tid == 0) {   // the last head's dA, dD shares
+    atomicAdd(dA + g * hpg + hpg - 1, s_hsum[0]);
+    atomicAdd(dD + g * hpg + hpg - 1, s_hsum[1]);
   }
 
   // dB, dC of the chunk's tokens (row r0 + lr, columns 16 j + 4 lg .. + 3)
@@ -1028,25 +1096,24 @@ int ma_bwd_impl(const void* x, const float* dt, const float* A, const void* B, c
       else if (Q == 128 && N == 128)
         ma_bwd_cross_kernel<128, 128><<<cgrid, kCrossThreads, 0, stream>>>(
             xb, dyb, dt, A, static_cast<const __bf16*>(B), static_cast<const __bf16*>(C), st1, st2, per, so, L, Hs,
-            G, bi, atf(w.R), dB, dC);
+            G, bi, static_cast<const __bf16*>(at(w.yh)), D, dx, ddt, dA, dD, dB, dC);
       else if (Q == 64 && N == 64)
         ma_bwd_cross_kernel<64, 64><<<cgrid, kCrossThreads, 0, stream>>>(
             xb, dyb, dt, A, static_cast<const __bf16*>(B), static_cast<const __bf16*>(C), st1, st2, per, so, L, Hs,
-            G, bi, atf(w.R), dB, dC);
+            G, bi, static_cast<const __bf16*>(at(w.yh)), D, dx, ddt, dA, dD, dB, dC);
       else
         return LINGEN_ERR_UNSUPPORTED;
       LINGEN_LAUNCHED();
     }
-    const dim3 tgrid{unsigned((rows + kTokRows - 1) / kTokRows), unsigned((Hs + 31) / 32), 1u};
-    if (f32)
+    // (the bf16 crossing-sum kernels form the per-token gradients themselves)
+    if (f32) {
+      const dim3 tgrid{unsigned((rows + kTokRows - 1) / kTokRows), unsigned((Hs + 31) / 32), 1u};
       ma_bwd_token_kernel<float><<<tgrid, 256, 0, stream>>>(static_cast<const float*>(x),
                                                             static_cast<const float*>(dy), dt, A, D,
                                                             static_cast<const float*>(at(w.yh)), atf(w.R), rows, Hs,
                                                             dx, ddt, dA, dD);
-    else
-      ma_bwd_token_kernel<__bf16><<<tgrid, 256, 0, stream>>>(xb, dyb, dt, A, D, static_cast<const __bf16*>(at(w.yh)),
-                                                             atf(w.R), rows, Hs, dx, ddt, dA, dD);
-    LINGEN_LAUNCHED();
+      LINGEN_LAUNCHED();
+    }
     if (R) {
       RevGeom g;
       g.pt = shape->rpool_t; g.ph = shape->rpool_h; g.pw = shape->rpool_w;

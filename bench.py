@@ -362,7 +362,10 @@ def library_attention(torch, qkv, steps, flops, timed):
 def te_backward(args, mate, torch):
     """The TE branch's backward pass (lingen_te_bwd) on the workload against
     its forward (lingen_te_fwd), both timed with events on the launch stream,
-    plain and shifted windows alternating by step as in the mixer."""
+    plain and shifted windows alternating by step as in the mixer; and the
+    saved-statistics pair (lingen_te_fwd_saved, then lingen_te_bwd_saved
+    reading that forward's output and log2 softmax denominators, one saved
+    set per window offset)."""
     from mate_inputs import CONFIGS, CONFIG_NOTES, make_inputs
 
     s = CONFIGS[args.config]
@@ -386,6 +389,11 @@ def te_backward(args, mate, torch):
 
     bwd_ms = timed(lambda i: mate.lingen_te_bwd(q, k, v, g, half if i % 2 else (0, 0, 0), 1, s, dq=dq, dk=dk, dv=dv))
     fwd_ms = timed(lambda i: mate.lingen_te_fwd(q, k, v, i % 2, s, out=y))
+    saved = [mate.lingen_te_fwd_saved(q, k, v, sh, 1, s) for sh in ((0, 0, 0), half)]
+    fwd_saved_ms = timed(lambda i: mate.lingen_te_fwd_saved(q, k, v, half if i % 2 else (0, 0, 0), 1, s, out=y,
+                                                            lse=saved[0][1]))
+    bwd_saved_ms = timed(lambda i: mate.lingen_te_bwd_saved(q, k, v, saved[i % 2][0], g, saved[i % 2][1],
+                                                            half if i % 2 else (0, 0, 0), 1, s, dq=dq, dk=dk, dv=dv))
     e = s.elem_bytes
     rows = s.L * s.attn_heads * s.attn_headdim
     nbytes = 7 * rows * e                                # q, k, v, dO read; dq, dk, dv written
@@ -399,6 +407,9 @@ def te_backward(args, mate, torch):
         "algorithmic_flops": flops, "TFLOP/s": round(flops / bwd_ms / 1e9, 1),
         "mfma_frac": round(flops / bwd_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
         "issued_mfma_TFLOP/s": round(issued / bwd_ms / 1e9, 1),
+        "saved": {"fwd_ms": round(fwd_saved_ms, 4), "bwd_ms": round(bwd_saved_ms, 4),
+                  "bwd_over_fwd": round(bwd_saved_ms / fwd_saved_ms, 2),
+                  "lse_MiB": round(saved[0][1].numel() * 4 / 2 ** 20, 1)},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -225,6 +225,36 @@ int lingen_te_bwd(const void* q, const void* k, const void* v, const void* d_out
                   const lingen_mate_shape* shape, void* dq, void* dk, void* dv,
                   hipStream_t stream);
 
+/* The same forward and backward with the row statistics saved instead of
+ * formed twice (memory traded for time, as a training step keeps
+ * activations for its backward pass; the backward itself is the chain rule
+ * through the attention of page "LinGen：基于Mamba机制的线性复杂度高清长视频生成框架",
+ * section 关键算法创新 > TESA, as for lingen_te_bwd):
+ *   lingen_te_fwd_saved writes y_te exactly as lingen_te_fwd_shift does (the
+ *   same kernel, bit for bit) and, per query token and head, the base-2 log
+ *   of its softmax denominator,
+ *       lse[b, l, h] = log2 sum_j exp(q_l . k_j / sqrt(d))
+ *   over the keys j of l's window (masked pairs excluded), [batch, L, Ha]
+ *   fp32, device, caller-owned, overwritten;
+ *   lingen_te_bwd_saved takes that y_te as o and that lse and forms
+ *   D_l = sum_e d_out[l, e] o[l, e] from them instead of recomputing the
+ *   forward inside every window first; the gradients are lingen_te_bwd's up
+ *   to the rounding of o to the storage type.  The caller must pass the
+ *   backward the q, k, v, offsets and masking its saved forward ran with.
+ * Supported: BF16 with d = 64 and 256-token windows, for the forward with
+ * an even head count (its kernel takes two heads per item); other valid
+ * shapes return LINGEN_ERR_UNSUPPORTED.  Other arguments and errors as
+ * lingen_te_fwd_shift and lingen_te_bwd. */
+int lingen_te_fwd_saved(const void* q, const void* k, const void* v,
+                        int32_t shift_t, int32_t shift_h, int32_t shift_w, int32_t masked,
+                        const lingen_mate_shape* shape, void* y_te, float* lse,
+                        hipStream_t stream);
+int lingen_te_bwd_saved(const void* q, const void* k, const void* v, const void* o,
+                        const void* d_out, const float* lse,
+                        int32_t shift_t, int32_t shift_h, int32_t shift_w, int32_t masked,
+                        const lingen_mate_shape* shape, void* dq, void* dk, void* dv,
+                        hipStream_t stream);
+
 /* The mixer: y = MA(mode = layer_idx mod 4) + TE(shifted = layer_idx odd).
  * layer_idx >= 0.  y: device, [batch, L, Hs*P] dtype; it is also used as the
  * staging buffer of the MA branch, so its contents on entry are ignored. */

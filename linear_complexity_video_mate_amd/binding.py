@@ -47,6 +47,8 @@ EXPORTS = (
     "lingen_te_fwd",
     "lingen_te_fwd_shift",
     "lingen_te_bwd",
+    "lingen_te_fwd_saved",
+    "lingen_te_bwd_saved",
     "lingen_mate_fwd",
     "lingen_mate_fwd_events",
     "lingen_mate_fwd_noalloc",
@@ -112,6 +114,8 @@ def lib() -> ctypes.CDLL:
         "lingen_te_fwd": ([P, P, P, I32, SP, P, P], ctypes.c_int),
         "lingen_te_fwd_shift": ([P, P, P, I32, I32, I32, I32, SP, P, P], ctypes.c_int),
         "lingen_te_bwd": ([P, P, P, P, I32, I32, I32, I32, SP, P, P, P, P], ctypes.c_int),
+        "lingen_te_fwd_saved": ([P, P, P, I32, I32, I32, I32, SP, P, P, P], ctypes.c_int),
+        "lingen_te_bwd_saved": ([P] * 6 + [I32, I32, I32, I32, SP, P, P, P, P], ctypes.c_int),
         "lingen_mate_fwd": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P], ctypes.c_int),
         "lingen_mate_fwd_events": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P, SZ, P, P], ctypes.c_int),
         "lingen_mate_fwd_noalloc": ([P, P, P, P, P, P, P, P, P, I32, SP, P, P], ctypes.c_int),
@@ -372,6 +376,46 @@ def lingen_te_bwd(q, k, v, d_out, shift, masked: int, shape, dq=None, dk=None, d
     pouts = [_need(t, name, td, n["q"]) for t, name in zip(outs, ("dq", "dk", "dv"))]
     st, sh, sw = (int(a) for a in shift)
     _check("lingen_te_bwd", lib().lingen_te_bwd(*args, st, sh, sw, int(masked), ctypes.byref(cs), *pouts, _stream()))
+    return tuple(outs)
+
+
+def lingen_te_fwd_saved(q, k, v, shift, masked: int, shape, out=None, lse=None):
+    """lingen_te_fwd_shift that also keeps each query's log2 softmax
+    denominator; returns (y_te, lse [batch, L, Ha] fp32)."""
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    torch = _torch()
+    L = shape.T * shape.H * shape.W
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((shape.batch, L, shape.attn_heads), dtype=torch.float32, device="cuda")
+    args = [_need(q, "q", td, n["q"]), _need(k, "k", td, n["q"]), _need(v, "v", td, n["q"])]
+    po = _need(out, "out", td, n["q"])
+    pl = _need(lse, "lse", torch.float32, shape.batch * L * shape.attn_heads)
+    st, sh, sw = (int(a) for a in shift)
+    _check("lingen_te_fwd_saved", lib().lingen_te_fwd_saved(*args, st, sh, sw, int(masked), ctypes.byref(cs), po, pl,
+                                                            _stream()))
+    return out, lse
+
+
+def lingen_te_bwd_saved(q, k, v, o, d_out, lse, shift, masked: int, shape, dq=None, dk=None, dv=None):
+    """lingen_te_bwd from the output ``o`` and statistics ``lse`` that
+    lingen_te_fwd_saved returned for the same inputs and offsets."""
+    n = _sizes(shape)
+    td = _tdtype(shape)
+    cs = to_c_shape(shape)
+    torch = _torch()
+    L = shape.T * shape.H * shape.W
+    outs = [t if t is not None else torch.empty_like(q) for t in (dq, dk, dv)]
+    args = [_need(q, "q", td, n["q"]), _need(k, "k", td, n["q"]), _need(v, "v", td, n["q"]),
+            _need(o, "o", td, n["q"]), _need(d_out, "d_out", td, n["q"]),
+            _need(lse, "lse", torch.float32, shape.batch * L * shape.attn_heads)]
+    pouts = [_need(t, name, td, n["q"]) for t, name in zip(outs, ("dq", "dk", "dv"))]
+    st, sh, sw = (int(a) for a in shift)
+    _check("lingen_te_bwd_saved", lib().lingen_te_bwd_saved(*args, st, sh, sw, int(masked), ctypes.byref(cs), *pouts,
+                                                            _stream()))
     return tuple(outs)
 
 

@@ -72,9 +72,11 @@ int ma_transposed_one(const lingen_mate_shape* s, int mode, const void* ub, cons
 
 // The TE branch for the (bf16, d = 64, 256-token window) family
 // (tesa_window.hip): y = o (accumulate = 0) or y += o (accumulate = 1), one
-// batch element after another.  Shapes and pointers are the caller's to
-// validate.  lingen_status.
+// batch element after another; lse (with accumulate = 0 and an even head
+// count only): also each query's log2-sum-exp of its scaled scores,
+// [batch, L, Ha] fp32.  Shapes and pointers are the caller's to validate.
+// lingen_status.
 int launch_te_win256(const lingen_mate_shape* s, const int shift[3], int masked, const void* q, const void* k,
-                     const void* v, void* y, int accumulate, hipStream_t st);
+                     const void* v, void* y, int accumulate, hipStream_t st, float* lse = nullptr);
 
 }  // namespace lingen

@@ -1027,7 +1027,10 @@ __global__ __launch_bounds__((OutCfg<TS, P, N, Q>::NW * 64)) void ssd_chunk_out_
   const int ngrp = Hs / hg;
   const int work = xcd_work_id(blockIdx.x, gridDim.x);
   const int c = chunk_order<Q>(rms, work / ngrp), h0 = (work % ngrp) * hg;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index as a scalar in [0, NW): the tests on the wave's t-tile
+  // (the diagonal M^T tile, the p-tiles it owns) are then branches of the
+  // whole wave rather than per-lane masks.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (Cfg::NW - 1);
   const int r16 = lane & 15, grp = lane >> 4;
   const int64_t xstride = CONV ? cv.ch : int64_t(Hs) * P;   // elements per token row of x
   const int64_t bstride = CONV ? cv.ch : int64_t(G) * N;    // ... of B and C

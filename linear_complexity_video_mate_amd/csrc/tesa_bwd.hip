@@ -122,7 +122,10 @@ struct BwdLds {
 // Phases A and B of one item whose tiles are in LDS.  MASK: a window cut by
 // the grid's border, whose slots of different wrap classes do not attend to
 // each other; the two instantiations keep the loops free of branches.
-template <bool MASK>
+// SAVED: the statistics come from the forward (its log2-sum-exp and its
+// output o, from which D is formed before this function), so phase A is
+// skipped.
+template <bool MASK, bool SAVED>
 __device__ __forceinline__ void bwd_phases(const BwdLds& S, int lane, int wave, int64_t rowstride, int64_t hoff,
                                            __bf16* __restrict__ dq, __bf16* __restrict__ dk,
                                            __bf16* __restrict__ dv) {
@@ -162,7 +165,7 @@ __device__ __forceinline__ void bwd_phases(const BwdLds& S, int lane, int wave, 
   };
 
   // ---------------- Phase A: statistics of the wave's query rows ----------
-  {
+  if constexpr (!SAVED) {
     int icls[2] = {0, 0};
     bf16x8 qf[2][NKS];
 #pragma unroll
@@ -442,12 +445,16 @@ __device__ __forceinline__ void bwd_phases(const BwdLds& S, int lane, int wave, 
   }
 }
 
+// SAVED: o (the forward's output, layout of q) and lse (its log2-sum-exp of
+// the scaled scores per query and head, [L][Ha] fp32) replace phase A.
+template <bool SAVED>
 __global__ __launch_bounds__(64 * kBwdWaves) void tesa_bwd_kernel(const __bf16* __restrict__ q,
                                                                   const __bf16* __restrict__ k,
                                                                   const __bf16* __restrict__ v,
                                                                   const __bf16* __restrict__ dO, WinGeom wg, int Ha,
                                                                   __bf16* __restrict__ dq, __bf16* __restrict__ dk,
-                                                                  __bf16* __restrict__ dv) {
+                                                                  __bf16* __restrict__ dv, const __bf16* __restrict__ o,
+                                                                  const float* __restrict__ lse) {
   constexpr int NWIN = kBwdWin, DH = kBwdDim;
   constexpr int NW = kBwdWaves, NTHR = NW * 64;
   static_assert(NWIN == 32 * NW, "32 query rows and 32 key rows per wave");
@@ -506,13 +513,48 @@ __global__ __launch_bounds__(64 * kBwdWaves) void tesa_bwd_kernel(const __bf16* 
   }
 #pragma unroll
   for (int d = 0; d < 4; ++d) issue(dO, S.sG, d);
-  __builtin_amdgcn_s_waitcnt(vmcnt_count(8));   // Q and the first halves of K and V
-  dma_barrier();
+  if constexpr (SAVED) {
+    // D_i = sum_d dO_i[d] o_i[d] and the saved statistics of the wave's 32
+    // query rows: lane group g takes d = 16 g .. 16 g + 15 of row r16
+    using KT = KvTile<__bf16, DH>;
+    const int r16 = lane & 15, grp = lane >> 4;
+    bf16x8 ov[2][2];
+    float lv[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int tok = S.sTok[(2 * wave + qt) * 16 + r16];
+      const __bf16* orow = o + int64_t(tok) * rowstride + hoff + 16 * grp;
+      ov[qt][0] = *reinterpret_cast<const bf16x8*>(orow);
+      ov[qt][1] = *reinterpret_cast<const bf16x8*>(orow + 8);
+      lv[qt] = lse[int64_t(tok) * Ha + h];
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_count(0));   // every tile, o and the statistics
+    dma_barrier();
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int i = (2 * wave + qt) * 16 + r16;
+      float ds_ = 0.f;
+#pragma unroll
+      for (int c8 = 0; c8 < 2; ++c8) {
+        const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(S.sG + KT::at(i, 16 * grp + 8 * c8));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ds_ = fmaf(static_cast<float>(g8[e]), static_cast<float>(ov[qt][c8][e]), ds_);
+      }
+      ds_ = sum_rows(ds_);
+      if (grp == 0) {
+        S.sLse[i] = lv[qt];
+        S.sD[i] = -ds_;   // stored negated: it starts phase B's dP accumulators
+      }
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_count(8));   // Q and the first halves of K and V
+    dma_barrier();
+  }
 
   if (wg.masked && window_wrapped(wg, wi, wj, wk))
-    bwd_phases<true>(S, lane, wave, rowstride, hoff, dq, dk, dv);
+    bwd_phases<true, SAVED>(S, lane, wave, rowstride, hoff, dq, dk, dv);
   else
-    bwd_phases<false>(S, lane, wave, rowstride, hoff, dq, dk, dv);
+    bwd_phases<false, SAVED>(S, lane, wave, rowstride, hoff, dq, dk, dv);
 }
 
 
@@ -627,9 +669,12 @@ int launch_te_bwd_small(const lingen_mate_shape* s, const WinGeom& g, const void
 
 using namespace lingen;
 
-extern "C" int lingen_te_bwd(const void* q, const void* k, const void* v, const void* d_out, int32_t shift_t,
-                             int32_t shift_h, int32_t shift_w, int32_t masked, const lingen_mate_shape* shape,
-                             void* dq, void* dk, void* dv, hipStream_t stream) {
+namespace lingen {
+namespace {
+// o, lse: null for the backward that forms the statistics itself
+int te_bwd_impl(const void* q, const void* k, const void* v, const void* d_out, const void* o, const float* lse,
+                int32_t shift_t, int32_t shift_h, int32_t shift_w, int32_t masked, const lingen_mate_shape* shape,
+                void* dq, void* dk, void* dv, hipStream_t stream) {
   if (int rc = validate_shape(shape)) return rc;
   if (shift_t < 0 || shift_t >= shape->win_t || shift_h < 0 || shift_h >= shape->win_h || shift_w < 0 ||
       shift_w >= shape->win_w || (masked != 0 && masked != 1))
@@ -637,6 +682,12 @@ extern "C" int lingen_te_bwd(const void* q, const void* k, const void* v, const 
   for (const void* p : {q, k, v, d_out, static_cast<const void*>(dq), static_cast<const void*>(dk),
                         static_cast<const void*>(dv)})
     if (int rc = check_ptr(p)) return rc;
+  const bool saved = o != nullptr;
+  if (saved) {
+    if (attn_family(shape) != ATTN_BF16_D64_W256) return LINGEN_ERR_UNSUPPORTED;
+    for (const void* p : {o, static_cast<const void*>(lse)})
+      if (int rc = check_ptr(p)) return rc;
+  }
   const int shift[3] = {shift_t, shift_h, shift_w};
   const WinGeom g = make_wingeom(shape, shift, masked);
   switch (attn_family(shape)) {
@@ -650,11 +701,38 @@ extern "C" int lingen_te_bwd(const void* q, const void* k, const void* v, const 
   const int64_t per = L * shape->attn_heads * kBwdDim;   // elements per batch element
   for (int b = 0; b < shape->batch; ++b) {
     const int64_t off = int64_t(b) * per;
-    tesa_bwd_kernel<<<items, 64 * kBwdWaves, 0, stream>>>(
-        static_cast<const __bf16*>(q) + off, static_cast<const __bf16*>(k) + off, static_cast<const __bf16*>(v) + off,
-        static_cast<const __bf16*>(d_out) + off, g, shape->attn_heads, static_cast<__bf16*>(dq) + off,
-        static_cast<__bf16*>(dk) + off, static_cast<__bf16*>(dv) + off);
+    const __bf16* qb = static_cast<const __bf16*>(q) + off;
+    const __bf16* kb = static_cast<const __bf16*>(k) + off;
+    const __bf16* vb = static_cast<const __bf16*>(v) + off;
+    const __bf16* gb = static_cast<const __bf16*>(d_out) + off;
+    __bf16* dqb = static_cast<__bf16*>(dq) + off;
+    __bf16* dkb = static_cast<__bf16*>(dk) + off;
+    __bf16* dvb = static_cast<__bf16*>(dv) + off;
+    if (saved)
+      tesa_bwd_kernel<true><<<items, 64 * kBwdWaves, 0, stream>>>(
+          qb, kb, vb, gb, g, shape->attn_heads, dqb, dkb, dvb, static_cast<const __bf16*>(o) + off,
+          lse + int64_t(b) * L * shape->attn_heads);
+    else
+      tesa_bwd_kernel<false><<<items, 64 * kBwdWaves, 0, stream>>>(qb, kb, vb, gb, g, shape->attn_heads, dqb, dkb,
+                                                                   dvb, nullptr, nullptr);
     if (launch_status(__func__) != LINGEN_OK) return LINGEN_ERR_HIP;
   }
   return LINGEN_OK;
+}
+}  // namespace
+}  // namespace lingen
+
+extern "C" int lingen_te_bwd(const void* q, const void* k, const void* v, const void* d_out, int32_t shift_t,
+                             int32_t shift_h, int32_t shift_w, int32_t masked, const lingen_mate_shape* shape,
+                             void* dq, void* dk, void* dv, hipStream_t stream) {
+  return te_bwd_impl(q, k, v, d_out, nullptr, nullptr, shift_t, shift_h, shift_w, masked, shape, dq, dk, dv, stream);
+}
+
+extern "C" int lingen_te_bwd_saved(const void* q, const void* k, const void* v, const void* o, const void* d_out,
+                                   const float* lse, int32_t shift_t, int32_t shift_h, int32_t shift_w,
+                                   int32_t masked, const lingen_mate_shape* shape, void* dq, void* dk, void* dv,
+                                   hipStream_t stream) {
+  for (const void* p : {o, static_cast<const void*>(lse)})
+    if (int rc = check_ptr(p)) return rc;
+  return te_bwd_impl(q, k, v, d_out, o, lse, shift_t, shift_h, shift_w, masked, shape, dq, dk, dv, stream);
 }

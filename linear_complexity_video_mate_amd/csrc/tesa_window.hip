@@ -346,12 +346,17 @@ __global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_kernel(const __bf
 // (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt not waited for).
 constexpr int vmcnt_count(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 
-template <bool ACCUMULATE>
+// SAVE_LSE: also write each query's log2-sum-exp of its scaled scores,
+// lse[token][head] = m + log2(l) (m the row's maximum, l its sum of 2^(s - m),
+// s = q.k log2(e) / sqrt(d)), which the backward pass reads instead of
+// forming the row statistics again.
+template <bool ACCUMULATE, bool SAVE_LSE = false>
 __global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_pair_kernel(const __bf16* __restrict__ q,
                                                                            const __bf16* __restrict__ k,
                                                                            const __bf16* __restrict__ v, WinGeom wg,
                                                                            int Ha, int n_items, int contiguous,
-                                                                           __bf16* __restrict__ y) {
+                                                                           __bf16* __restrict__ y,
+                                                                           float* __restrict__ lse = nullptr) {
   constexpr int DH = 64, NWIN = 256, HALF = 128, NWAVE = kW256Waves;
   constexpr int NTHR = NWAVE * 64;
   constexpr int KT16 = HALF / 16;                  // 16-key tiles of a half
@@ -447,7 +452,9 @@ __global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_pair_kernel(const
   wait_vmem();
 
   // One head of the pair over both halves, its output stored at the end;
-  // after_half0 runs between the halves.
+  // after_half0 runs between the halves.  (SAVE_LSE: head h0's statistic
+  // waits in lse0 and leaves with head h1's as one 8-byte store.)
+  float lse0 = 0.f;
   auto head = [&](const QState& cur, int h, int e, const int* cls, bool wrapped, auto&& after_half0) {
     // The MA output this head adds to arrives while the products run.
     bf16x8 ya[2];
@@ -520,6 +527,12 @@ __global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_pair_kernel(const
       }
     }
     const float inv = __builtin_amdgcn_rcpf(den[0]);
+    if constexpr (SAVE_LSE) {
+      // the query's own key is never masked, so m is finite here
+      const float lv = m + log2f(den[0]);
+      if (e == 0) lse0 = lv;
+      else if (grp == 0) *reinterpret_cast<float2*>(lse + int64_t(cur.tokq) * Ha + h - 1) = make_float2(lse0, lv);
+    }
 #pragma unroll
     for (int r1 = 0; r1 < 2; ++r1) {
       float ov[8];
@@ -600,7 +613,7 @@ __global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_pair_kernel(const
 // The TE branch for the (bf16, d 64, 256-token window) family, one batch
 // element after another; persistent grid of one workgroup per compute unit.
 int launch_te_win256(const lingen_mate_shape* s, const int shift[3], int masked, const void* q, const void* k,
-                     const void* v, void* y, int accumulate, hipStream_t st) {
+                     const void* v, void* y, int accumulate, hipStream_t st, float* lse) {
   const WinGeom g = make_wingeom(s, shift, masked);
   const int64_t L = tokens(s);
   const int nwin = g.nwt * g.nwh * g.nww;
@@ -614,12 +627,16 @@ int launch_te_win256(const lingen_mate_shape* s, const int shift[3], int masked,
     const __bf16* vb = reinterpret_cast<const __bf16*>(static_cast<const char*>(v) + off);
     __bf16* yb = reinterpret_cast<__bf16*>(static_cast<char*>(y) + off);
     const int items = nwin * s->attn_heads;
+    if (lse != nullptr && s->attn_heads % 2) return LINGEN_ERR_UNSUPPORTED;
     if (s->attn_heads % 2 == 0) {
       // two heads per item; the item order as below, judged by head-items
       const int pairs = nwin * (s->attn_heads / 2);
       const int pgrid = pairs < ncu ? pairs : ncu;
       const int pcontig = items >= 128 * pgrid ? 1 : 0;
-      if (accumulate)
+      if (lse != nullptr)
+        tesa_win256_pair_kernel<false, true><<<pgrid, kW256Waves * 64, 0, st>>>(
+            qb, kb, vb, g, s->attn_heads, pairs, pcontig, yb, lse + int64_t(b) * L * s->attn_heads);
+      else if (accumulate)
         tesa_win256_pair_kernel<true><<<pgrid, kW256Waves * 64, 0, st>>>(qb, kb, vb, g, s->attn_heads, pairs, pcontig,
                                                                         yb);
       else
@@ -647,3 +664,19 @@ int launch_te_win256(const lingen_mate_shape* s, const int shift[3], int masked,
 }
 
 }  // namespace lingen
+
+using namespace lingen;
+
+extern "C" int lingen_te_fwd_saved(const void* q, const void* k, const void* v, int32_t shift_t, int32_t shift_h,
+                                   int32_t shift_w, int32_t masked, const lingen_mate_shape* shape, void* y_te,
+                                   float* lse, hipStream_t stream) {
+  if (int rc = validate_shape(shape)) return rc;
+  if (shift_t < 0 || shift_t >= shape->win_t || shift_h < 0 || shift_h >= shape->win_h || shift_w < 0 ||
+      shift_w >= shape->win_w || (masked != 0 && masked != 1))
+    return LINGEN_ERR_SHAPE;
+  for (const void* p : {q, k, v, static_cast<const void*>(y_te), static_cast<const void*>(lse)})
+    if (int rc = check_ptr(p)) return rc;
+  if (attn_family(shape) != ATTN_BF16_D64_W256 || shape->attn_heads % 2) return LINGEN_ERR_UNSUPPORTED;
+  const int shift[3] = {shift_t, shift_h, shift_w};
+  return launch_te_win256(shape, shift, masked, q, k, v, y_te, 0, stream, lse);
+}

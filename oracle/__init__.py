@@ -39,6 +39,7 @@ from .mate_oracle import (
     tesa,
     tesa_for_queries,
     tesa_backward,
+    tesa_lse,
     dense_attention,
     scan_conv_silu,
     ma_prep,
@@ -68,6 +69,7 @@ __all__ = [
     "tesa",
     "tesa_for_queries",
     "tesa_backward",
+    "tesa_lse",
     "dense_attention",
     "scan_conv_silu",
     "ma_prep",

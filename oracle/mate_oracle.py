@@ -468,6 +468,31 @@ def tesa(q, k, v, T: int, H: int, W: int, win, shift, stats: Optional[Dict] = No
     return o
 
 
+def tesa_lse(q, k, T: int, H: int, W: int, win, shift, cyclic: bool = False) -> np.ndarray:
+    """Per query and head, the base-2 log of the softmax denominator of its
+    window, lse_i = log2 sum_j exp(q_i . k_j / sqrt(d)) over the tokens j in
+    i's window (``tesa_window_keys``); returns [L, Ha].  The softmax weights
+    of ``tesa`` are then 2^(q_i . k_j log2(e) / sqrt(d) - lse_i), the
+    statistic the backward pass reuses instead of forming it again."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    d = q.shape[-1]
+    keys = tesa_window_keys(T, H, W, win, shift, cyclic)
+    _, order, counts = _groups(keys)
+    lse = np.empty(q.shape[:2], dtype=np.float64)
+    start = 0
+    for n in counts:
+        idx = order[start:start + n]
+        start += n
+        qh = q[idx].transpose(1, 0, 2)
+        kh = k[idx].transpose(1, 0, 2)
+        s = (qh @ kh.transpose(0, 2, 1)) / math.sqrt(d)     # [Ha, n, n]
+        mx = s.max(axis=-1, keepdims=True)
+        ln = mx[..., 0] + np.log(np.exp(s - mx).sum(axis=-1))
+        lse[idx] = (ln / math.log(2.0)).T
+    return lse
+
+
 def tesa_backward(q, k, v, dO, T: int, H: int, W: int, win, shift, cyclic: bool = False):
     """Gradients of TESA, (dq, dk, dv), each [L, Ha, d], for an upstream
     gradient dO of the output: the chain rule through o = softmax(q k^T /

@@ -205,6 +205,38 @@ def test_te_bwd_rejects_before_launch(L):
     assert call(F, F, F, F, 1, 2, 2, 1, None, F, F, F, None) == -1
 
 
+def test_te_saved_rejects_before_launch(L):
+    F = ctypes.c_void_p(FAKE)
+    Z = ctypes.c_void_p(0)
+    M = ctypes.c_void_p(MISALIGNED)
+    fwd, bwd = L.lingen_te_fwd_saved, L.lingen_te_bwd_saved
+    cs1 = mate.to_c_shape(CONFIGS[1])
+    for st, sh, sw, masked in ((4, 0, 0, 1), (0, -1, 0, 1), (0, 0, 8, 0), (0, 0, 0, 3)):
+        assert fwd(F, F, F, st, sh, sw, masked, ctypes.byref(cs1), F, F, None) == -2
+        assert bwd(*[F] * 6, st, sh, sw, masked, ctypes.byref(cs1), F, F, F, None) == -2
+    for i in range(5):   # q, k, v, y_te, lse
+        p = [F] * 5
+        p[i] = Z
+        assert fwd(*p[:3], 2, 4, 4, 1, ctypes.byref(cs1), *p[3:], None) == -1, i
+        p[i] = M
+        assert fwd(*p[:3], 2, 4, 4, 1, ctypes.byref(cs1), *p[3:], None) == -4, i
+    for i in range(9):   # q, k, v, o, d_out, lse, dq, dk, dv
+        p = [F] * 9
+        p[i] = Z
+        assert bwd(*p[:6], 2, 4, 4, 1, ctypes.byref(cs1), *p[6:], None) == -1, i
+        p[i] = M
+        assert bwd(*p[:6], 2, 4, 4, 1, ctypes.byref(cs1), *p[6:], None) == -4, i
+    # only the 256-token bf16 windows, and for the forward an even head count
+    # (its kernel takes two heads per item)
+    c = mate.to_c_shape(CONFIGS[0])
+    assert fwd(F, F, F, 0, 0, 0, 1, ctypes.byref(c), F, F, None) == -7
+    assert bwd(*[F] * 6, 0, 0, 0, 1, ctypes.byref(c), F, F, F, None) == -7
+    c = mate.to_c_shape(CONFIGS[1].with_(ssd_heads=15, attn_heads=15))
+    assert L.lingen_mate_validate(ctypes.byref(c)) == 0
+    assert fwd(F, F, F, 0, 0, 0, 1, ctypes.byref(c), F, F, None) == -7
+    assert fwd(F, F, F, 0, 0, 0, 1, None, F, F, None) == -1
+
+
 def test_odd_window_shapes_validate(L):
     for T in (12, 24):
         s = CONFIGS[1].with_(T=T, H=T, W=T, win=(3, 3, 3))

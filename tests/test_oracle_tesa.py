@@ -234,3 +234,61 @@ def test_swin_roll_and_mask_agrees_odd_and_uneven(win, shift):
     got = oracle.tesa(q, k, v, T, H, W, win, shift)
     want = _swin_roll_mask(q, k, v, T, H, W, win, shift)
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+# Pins of the softmax denominator the backward pass reuses (oracle.tesa_lse).
+def test_lse_two_keys_closed_form():
+    # d = 1, two tokens in one window, keys 0 and ln 3: sum exp = 1 + 3
+    q = np.ones((2, 1, 1))
+    k = np.array([0.0, math.log(3.0)]).reshape(2, 1, 1)
+    got = oracle.tesa_lse(q, k, 1, 1, 2, (1, 1, 2), (0, 0, 0))
+    np.testing.assert_allclose(got, np.full((2, 1), 2.0), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("shift", [(0, 0, 0), (1, 2, 1)])
+def test_lse_zero_keys_counts_the_window(shift):
+    # every score 0: lse = log2 of the size of the query's window, with the
+    # window sizes counted by brute force over the grid (cut border windows)
+    T, H, W, win = 3, 5, 4, (2, 4, 2)
+    L, Ha = T * H * W, 2
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((L, Ha, 3))
+    k = np.zeros((L, Ha, 3))
+    got = oracle.tesa_lse(q, k, T, H, W, win, shift)
+    coords = [(t, h, w) for t in range(T) for h in range(H) for w in range(W)]
+    def cell(c):
+        return tuple((c[a] - shift[a]) // win[a] for a in range(3))
+    for i, c in enumerate(coords):
+        n = sum(1 for c2 in coords if cell(c2) == cell(c))
+        np.testing.assert_allclose(got[i], math.log2(n), rtol=0, atol=1e-12)
+
+
+def test_lse_one_window_is_logsumexp():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(8)
+    T, H, W, Ha, d = 2, 3, 4, 2, 5
+    L = T * H * W
+    q, k, _ = _qkv(rng, L, Ha, d, scale=2.0)
+    got = oracle.tesa_lse(q, k, T, H, W, (T, H, W), (0, 0, 0))
+    for h in range(Ha):
+        ref = logsumexp(q[:, h] @ k[:, h].T / math.sqrt(d), axis=1) / math.log(2.0)
+        np.testing.assert_allclose(got[:, h], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_lse_gives_the_tesa_weights():
+    # 2^(s log2(e) - lse) are the softmax weights: with them, sum_j w_ij v_j
+    # is the pinned tesa output, on a shifted (cut) partition
+    rng = np.random.default_rng(9)
+    T, H, W, Ha, d, win, shift = 4, 4, 4, 2, 8, (2, 2, 4), (1, 1, 2)
+    L = T * H * W
+    q, k, v = _qkv(rng, L, Ha, d)
+    lse = oracle.tesa_lse(q, k, T, H, W, win, shift)
+    ref = oracle.tesa(q, k, v, T, H, W, win, shift)
+    keys = oracle.tesa_window_keys(T, H, W, win, shift)
+    for i in range(0, L, 5):
+        same = np.all(keys == keys[i], axis=1)
+        for h in range(Ha):
+            s = k[same, h] @ q[i, h] / math.sqrt(d)
+            w = np.exp2(s * math.log2(math.e) - lse[i, h])
+            assert abs(w.sum() - 1.0) < 1e-12
+            np.testing.assert_allclose(w @ v[same, h], ref[i, h], rtol=1e-11, atol=1e-12)

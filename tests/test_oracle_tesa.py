@@ -176,13 +176,14 @@ def test_oracle_time_grows_linearly_in_T():
         x = rng.standard_normal((L, 1, 4))
         q = rng.standard_normal((L, 1, 4))
         best = float("inf")
-        for _ in range(3):
+        for _ in range(7):   # best of several: a timing under a loaded host
             t0 = time.perf_counter()
             oracle.mate_fwd(x, np.full((L, 1), 0.1), -np.ones(1), rng.standard_normal((L, 4)),
                             rng.standard_normal((L, 4)), np.ones(1), q, q, q, 1, T, H, W, (2, 2, 2))
             best = min(best, time.perf_counter() - t0)
         return best
 
+    run(16)   # warm the code paths before either measurement
     t1, t4 = run(16), run(64)
     assert 2.0 < t4 / t1 < 8.0, (t1, t4)
 

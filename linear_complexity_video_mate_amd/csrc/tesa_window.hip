@@ -350,6 +350,12 @@ constexpr int vmcnt_count(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); 
 // lse[token][head] = m + log2(l) (m the row's maximum, l its sum of 2^(s - m),
 // s = q.k log2(e) / sqrt(d)), which the backward pass reads instead of
 // forming the row statistics again.
+// The pair kernel's K and V rows are read once per launch: its direct loads
+// are non-temporal.
+__device__ __forceinline__ void lds_load16_nt(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 2);
+}
+
 template <bool ACCUMULATE, bool SAVE_LSE = false>
 __global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_pair_kernel(const __bf16* __restrict__ q,
                                                                            const __bf16* __restrict__ k,
@@ -408,8 +414,8 @@ __global__ __launch_bounds__(kW256Waves * 64) void tesa_win256_pair_kernel(const
       const int base = (wave * DMA + d) * 64;
       const int u = base + lane, row = u / 16, e = (u / 8) & 1, ch = (u & 7) ^ (row & 7);
       const int64_t goff = int64_t(tok[half * HALF + row]) * rowstride + int64_t(2 * hp + e) * DH + ch * 8;
-      lds_load16(k + goff, dK + base * 8);
-      lds_load16(v + goff, dV + base * 8);
+      lds_load16_nt(k + goff, dK + base * 8);
+      lds_load16_nt(v + goff, dV + base * 8);
     }
   };
   const int y16_off = 16 * (grp & 1) + 8 * (grp >> 1);
